@@ -1,0 +1,334 @@
+"""The oracle: a plain CPU definition of every FP8/FP4 quantization recipe.
+
+TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package. The GPU library does not import,
+link or call it, and it shares no code with the GPU library.
+
+The arithmetic lives in orc.c (built into liborc.so by oracle/build.py);
+this module only marshals numpy arrays through ctypes.
+
+Inputs are numpy arrays: float32 for fp32 tensors, uint16 holding the bit
+patterns for bf16 tensors. Outputs are numpy arrays of uint8 codes and
+float32 scales.
+
+Sources (short labels used across the oracle):
+  [MP] "混合精度训练：fp16 到 fp8" (garden.houmin.site)
+  [CS] "FP8 Current Scaling：量化、缩放与精度边界" (notes.kuangjux.top)
+  [LP] "从 BF16 到 FP8/FP4：大语言模型低精度训练与混合精度预训练" (r00kie-liu.github.io)
+
+What pins each function (tests/test_oracle_*.py):
+  decode / encode      all codes against the pages' format facts and against
+                       torch's float8 casts; brute-force nearest search;
+                       the E2M1 value list of [MP] "NVFP4".
+  current / with_amax  the worked example, error and underflow examples and
+                       the sharded all-gather example of [CS]; the
+                       amax-to-Fmax invariant; the error bound.
+  delayed              closed forms: a repeated input equals current scaling
+                       on the next step; the window expiry step.
+  block                per-tile amax-to-448 invariant, error bound, 2-D
+                       transpose invariance, brute force on tiny tensors.
+  mx                   closed form code = max(E(a)-8, 0) from the fp32 bits,
+                       power-of-two scale, brute force on tiny tensors.
+  nvfp4                structure (block holding the tensor amax gets the
+                       E4M3 code of 448 and a +-6 element), brute force on
+                       tiny tensors. The fp32 association of the two-level
+                       scale is a reading of the pages: parity unpinned at
+                       the last-ulp level of that association.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+E4M3, E5M2, E2M1 = 0, 1, 2
+IN_F32, IN_BF16 = 0, 1
+ROWWISE, COLWISE = 1, 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liborc.so")
+_lib = None
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_u32 = ctypes.c_uint32
+_f32 = ctypes.c_float
+_fp = ctypes.POINTER(ctypes.c_float)
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _b
+        _b.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    sig = {
+        "orc_max_code": (_u32, [ctypes.c_int]),
+        "orc_decode": (ctypes.c_double, [ctypes.c_int, _u32]),
+        "orc_decode_e8m0": (ctypes.c_double, [_u32]),
+        "orc_fmax": (_f32, [ctypes.c_int]),
+        "orc_encode": (_u32, [ctypes.c_int, _f32]),
+        "orc_encode_array": (None, [ctypes.c_int, _p, _i64, _p]),
+        "orc_amax": (_f32, [_p, ctypes.c_int, _i64]),
+        "orc_tensor_scales": (None, [_f32, _f32, _fp, _fp]),
+        "orc_mx_code": (_u32, [_f32]),
+        "orc_transpose_u8": (None, [_p, _i64, _i64, _p]),
+        "orc_quantize_with_amax": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, ctypes.c_int, _u32, _f32,
+                                                  _p, _p, _fp]),
+        "orc_quantize_current": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, ctypes.c_int, _u32,
+                                                _p, _p, _fp, _fp]),
+        "orc_quantize_delayed": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, ctypes.c_int, _u32,
+                                                _p, _i32, _fp, _fp, _i64, _p, _p, _fp]),
+        "orc_quantize_block": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, ctypes.c_int, ctypes.c_int, _u32,
+                                              _p, _p, _p, _p]),
+        "orc_quantize_mx": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, _u32, _p, _p, _p, _p]),
+        "orc_quantize_nvfp4": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, ctypes.c_int, ctypes.c_int, _u32,
+                                              _p, _p, _p, _p, _fp, _fp]),
+        "orc_dequant_tensor": (None, [_p, _i64, ctypes.c_int, _f32, _p]),
+        "orc_dequant_block": (None, [_p, _p, _i64, _i64, ctypes.c_int, ctypes.c_int, _p]),
+        "orc_dequant_mx": (None, [_p, _p, _i64, _i64, _p]),
+        "orc_dequant_nvfp4": (None, [_p, _p, _f32, _i64, _i64, ctypes.c_int, ctypes.c_int, _p]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise OracleError(f"{what}: oracle rejected the input (code {rc})")
+
+
+def _in(x):
+    """(pointer, dtype code, array kept alive) for an input array."""
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.float32:
+        return x.ctypes.data, IN_F32, x
+    if x.dtype == np.uint16:
+        return x.ctypes.data, IN_BF16, x
+    raise TypeError("oracle inputs are float32 or uint16 (bf16 bits)")
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _shape2(x, shape):
+    if shape is not None:
+        return int(shape[0]), int(shape[1])
+    if x.ndim == 1:
+        return 1, int(x.shape[0])
+    return int(x.shape[0]), int(x.shape[1])
+
+
+# ---------------------------------------------------------------- codecs
+def max_code(fmt):
+    return int(_load().orc_max_code(fmt))
+
+
+def decode(fmt, code):
+    return float(_load().orc_decode(fmt, int(code)))
+
+
+def decode_e8m0(code):
+    return float(_load().orc_decode_e8m0(int(code)))
+
+
+def fmax(fmt):
+    return float(_load().orc_fmax(fmt))
+
+
+def encode(fmt, y):
+    return int(_load().orc_encode(fmt, float(np.float32(y))))
+
+
+def encode_array(fmt, y):
+    """Element-wise encode of a float32 array."""
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    q = np.empty(y.shape, np.uint8)
+    _load().orc_encode_array(fmt, y.ctypes.data, y.size, q.ctypes.data)
+    return q
+
+
+def mx_code(a):
+    return int(_load().orc_mx_code(float(np.float32(a))))
+
+
+def tensor_scales(a, fmax_value):
+    al, s = ctypes.c_float(), ctypes.c_float()
+    _load().orc_tensor_scales(float(np.float32(a)), float(np.float32(fmax_value)), ctypes.byref(al), ctypes.byref(s))
+    return np.float32(al.value), np.float32(s.value)
+
+
+def amax(x):
+    p, dt, keep = _in(x)
+    return np.float32(_load().orc_amax(p, dt, keep.size))
+
+
+# ---------------------------------------------------------------- recipes
+def quantize_current(x, fmt, outputs=ROWWISE, shape=None):
+    """Per-tensor current scaling. Returns dict(q_row, q_col, s, amax)."""
+    p, dt, keep = _in(x)
+    R, C = _shape2(keep, shape)
+    q_row = np.empty(R * C, np.uint8)
+    q_col = np.empty(R * C, np.uint8) if outputs & COLWISE else None
+    s, a = ctypes.c_float(), ctypes.c_float()
+    _check(_load().orc_quantize_current(p, dt, R, C, fmt, outputs, _ptr(q_row), _ptr(q_col),
+                                        ctypes.byref(s), ctypes.byref(a)), "quantize_current")
+    return dict(q_row=q_row.reshape(R, C), q_col=None if q_col is None else q_col.reshape(C, R),
+                s=np.float32(s.value), amax=np.float32(a.value))
+
+
+def quantize_with_amax(x, fmt, amax_value, outputs=ROWWISE, shape=None):
+    """Per-tensor scaling with a given (e.g. all-reduced) amax."""
+    p, dt, keep = _in(x)
+    R, C = _shape2(keep, shape)
+    q_row = np.empty(R * C, np.uint8)
+    q_col = np.empty(R * C, np.uint8) if outputs & COLWISE else None
+    s = ctypes.c_float()
+    _check(_load().orc_quantize_with_amax(p, dt, R, C, fmt, outputs, float(np.float32(amax_value)),
+                                          _ptr(q_row), _ptr(q_col), ctypes.byref(s)), "quantize_with_amax")
+    return dict(q_row=q_row.reshape(R, C), q_col=None if q_col is None else q_col.reshape(C, R),
+                s=np.float32(s.value))
+
+
+class DelayedState:
+    """Delayed-scaling state: amax window, alpha and s (all fp32)."""
+
+    def __init__(self, history_len=1024):
+        self.hist = np.zeros(history_len, np.float32)
+        self.alpha = np.float32(1.0)
+        self.s = np.float32(1.0)
+        self.step = 0
+
+    def copy(self):
+        c = DelayedState(len(self.hist))
+        c.hist[:] = self.hist
+        c.alpha, c.s, c.step = self.alpha, self.s, self.step
+        return c
+
+
+def quantize_delayed(x, fmt, state, outputs=ROWWISE, shape=None):
+    """One delayed-scaling step; updates `state` (and advances its step)."""
+    p, dt, keep = _in(x)
+    R, C = _shape2(keep, shape)
+    q_row = np.empty(R * C, np.uint8)
+    q_col = np.empty(R * C, np.uint8) if outputs & COLWISE else None
+    al, s, a = ctypes.c_float(float(state.alpha)), ctypes.c_float(float(state.s)), ctypes.c_float()
+    _check(_load().orc_quantize_delayed(p, dt, R, C, fmt, outputs, state.hist.ctypes.data, len(state.hist),
+                                        ctypes.byref(al), ctypes.byref(s), int(state.step),
+                                        _ptr(q_row), _ptr(q_col), ctypes.byref(a)), "quantize_delayed")
+    state.alpha, state.s = np.float32(al.value), np.float32(s.value)
+    state.step += 1
+    return dict(q_row=q_row.reshape(R, C), q_col=None if q_col is None else q_col.reshape(C, R),
+                amax=np.float32(a.value))
+
+
+def quantize_block(x, block, outputs=ROWWISE, shape=None):
+    """Blockwise E4M3 with fp32 tile scales; block is (1,128) or (128,128)."""
+    p, dt, keep = _in(x)
+    R, C = _shape2(keep, shape)
+    br, bc = block
+    out = {}
+    q_row = np.empty(R * C, np.uint8) if outputs & ROWWISE else None
+    s_row = np.empty((R // br) * (C // bc), np.float32) if outputs & ROWWISE else None
+    q_col = np.empty(R * C, np.uint8) if outputs & COLWISE else None
+    s_col = None
+    if outputs & COLWISE:
+        s_col = np.empty(C * (R // bc) if br == 1 else (C // bc) * (R // br), np.float32)
+    _check(_load().orc_quantize_block(p, dt, R, C, br, bc, outputs, _ptr(q_row), _ptr(s_row), _ptr(q_col),
+                                      _ptr(s_col)), "quantize_block")
+    out["q_row"] = None if q_row is None else q_row.reshape(R, C)
+    out["s_row"] = None if s_row is None else s_row.reshape(R // br, C // bc)
+    out["q_col"] = None if q_col is None else q_col.reshape(C, R)
+    if s_col is not None:
+        out["s_col"] = s_col.reshape(C, R // bc) if br == 1 else s_col.reshape(C // bc, R // br)
+    else:
+        out["s_col"] = None
+    return out
+
+
+def quantize_mx(x, outputs=ROWWISE | COLWISE, shape=None):
+    """MXFP8 E4M3 with E8M0 codes; rowwise 1x32 and colwise 32x1 (transposed)."""
+    p, dt, keep = _in(x)
+    R, C = _shape2(keep, shape)
+    q_row = np.empty(R * C, np.uint8) if outputs & ROWWISE else None
+    e_row = np.empty(R * (C // 32), np.uint8) if outputs & ROWWISE else None
+    q_col = np.empty(R * C, np.uint8) if outputs & COLWISE else None
+    e_col = np.empty(C * (R // 32), np.uint8) if outputs & COLWISE else None
+    _check(_load().orc_quantize_mx(p, dt, R, C, outputs, _ptr(q_row), _ptr(e_row), _ptr(q_col), _ptr(e_col)),
+           "quantize_mx")
+    return dict(q_row=None if q_row is None else q_row.reshape(R, C),
+                e_row=None if e_row is None else e_row.reshape(R, C // 32),
+                q_col=None if q_col is None else q_col.reshape(C, R),
+                e_col=None if e_col is None else e_col.reshape(C, R // 32))
+
+
+def quantize_nvfp4(x, block, outputs=ROWWISE, shape=None):
+    """NVFP4: packed E2M1 pairs, E4M3 block codes and the fp32 tensor scale S."""
+    p, dt, keep = _in(x)
+    R, C = _shape2(keep, shape)
+    br, bc = block
+    p_row = np.empty(R * C // 2, np.uint8) if outputs & ROWWISE else None
+    c_row = np.empty((R // br) * (C // bc), np.uint8) if outputs & ROWWISE else None
+    p_col = np.empty(R * C // 2, np.uint8) if outputs & COLWISE else None
+    c_col = None
+    if outputs & COLWISE:
+        c_col = np.empty(C * (R // 16) if br == 1 else (C // 16) * (R // 16), np.uint8)
+    S, A = ctypes.c_float(), ctypes.c_float()
+    _check(_load().orc_quantize_nvfp4(p, dt, R, C, br, bc, outputs, _ptr(p_row), _ptr(c_row), _ptr(p_col),
+                                      _ptr(c_col), ctypes.byref(S), ctypes.byref(A)), "quantize_nvfp4")
+    out = dict(p_row=None if p_row is None else p_row.reshape(R, C // 2),
+               c_row=None if c_row is None else c_row.reshape(R // br, C // bc),
+               p_col=None if p_col is None else p_col.reshape(C, R // 2),
+               S=np.float32(S.value), amax=np.float32(A.value))
+    if c_col is not None:
+        out["c_col"] = c_col.reshape(C, R // 16) if br == 1 else c_col.reshape(C // 16, R // 16)
+    else:
+        out["c_col"] = None
+    return out
+
+
+# ---------------------------------------------------------------- dequantize
+def dequant_tensor(q, fmt, s):
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    y = np.empty(q.size, np.float32)
+    _load().orc_dequant_tensor(q.ctypes.data, q.size, fmt, float(np.float32(s)), y.ctypes.data)
+    return y.reshape(q.shape)
+
+
+def dequant_block(q, s, block):
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    R, C = q.shape
+    y = np.empty(R * C, np.float32)
+    _load().orc_dequant_block(q.ctypes.data, s.ctypes.data, R, C, block[0], block[1], y.ctypes.data)
+    return y.reshape(R, C)
+
+
+def dequant_mx(q, codes):
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    R, C = q.shape
+    y = np.empty(R * C, np.float32)
+    _load().orc_dequant_mx(q.ctypes.data, codes.ctypes.data, R, C, y.ctypes.data)
+    return y.reshape(R, C)
+
+
+def dequant_nvfp4(p, codes, S, block):
+    p = np.ascontiguousarray(p, dtype=np.uint8)
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    R, C2 = p.shape
+    y = np.empty(R * C2 * 2, np.float32)
+    _load().orc_dequant_nvfp4(p.ctypes.data, codes.ctypes.data, float(np.float32(S)), R, C2 * 2, block[0], block[1],
+                              y.ctypes.data)
+    return y.reshape(R, C2 * 2)

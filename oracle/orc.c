@@ -1,0 +1,698 @@
+/*
+ * orc.c -- the CPU oracle for FP8/FP4 tensor quantization.
+ *
+ * TEST INFRASTRUCTURE. This file defines, plainly and slowly, what each
+ * quantization recipe computes, so that the GPU library can be checked
+ * against it byte for byte. Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load it. It shares no code, header or
+ * table with the GPU library, and the GPU library never calls it.
+ *
+ * Sources (three web pages on FP8/FP4 training; cited by short label):
+ *   [MP]  "混合精度训练：fp16 到 fp8" (garden.houmin.site, infra/mixed-precision-fp8)
+ *   [CS]  "FP8 Current Scaling：量化、缩放与精度边界" (notes.kuangjux.top)
+ *   [LP]  "从 BF16 到 FP8/FP4：大语言模型低精度训练与混合精度预训练" (r00kie-liu.github.io)
+ *
+ * Arithmetic: IEEE binary32 with round-to-nearest-even, as the pages fix a
+ * single fp32 scale per unit ([CS] section "Current Scaling"). Build with
+ * -ffp-contract=off and no fast-math, so that every product is rounded once
+ * and divisions are correctly rounded. Value tables and the nearest-code
+ * search use binary64, where every value involved is exact.
+ *
+ * Readings of the pages where they leave a step open are marked READING.
+ *
+ * Parity status per function is listed in the header of oracle/__init__.py.
+ */
+#include <float.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_E4M3 0
+#define ORC_E5M2 1
+#define ORC_E2M1 2
+
+#define ORC_IN_F32 0
+#define ORC_IN_BF16 1
+
+#define ORC_ROWWISE 1
+#define ORC_COLWISE 2
+
+/* ------------------------------------------------------------------ */
+/* Element formats                                                     */
+/* ------------------------------------------------------------------ */
+
+/*
+ * Bit layout of each element format: sign bit, then exponent bits, then
+ * mantissa bits, with an exponent bias.
+ *   E4M3: 1/4/3, bias 7.  No infinity; S.1111.111 is NaN.  ([MP] section
+ *         "FP8 数据格式"; [CS] table of the two formats: max 448.)
+ *   E5M2: 1/5/2, bias 15. IEEE-like: exponent all ones is Inf (mantissa 0)
+ *         or NaN.  ([MP] "FP8 数据格式"; [CS] table: max 57344.)
+ *   E2M1: 1/2/1, bias 1, four bits, every code finite.  ([MP] section
+ *         "NVFP4", the float4_e2m1fn_x2 nibble layout and its list of 16
+ *         values.)
+ * Biases are those of the OCP 8-bit and MX formats the pages refer to.
+ */
+typedef struct {
+    int bits, ebits, mbits, bias;
+} orc_fmt_def;
+
+static const orc_fmt_def FMT[3] = {
+    {8, 4, 3, 7},  /* E4M3 */
+    {8, 5, 2, 15}, /* E5M2 */
+    {4, 2, 1, 1},  /* E2M1 */
+};
+
+/* Largest positive finite code of each format. */
+unsigned orc_max_code(int fmt)
+{
+    switch (fmt) {
+    case ORC_E4M3: return 0x7E; /* 0x7F is NaN */
+    case ORC_E5M2: return 0x7B; /* 0x7C is +Inf */
+    case ORC_E2M1: return 0x7;
+    }
+    return 0;
+}
+
+/* Value of an element code, from sign, exponent and mantissa fields. */
+double orc_decode(int fmt, unsigned code)
+{
+    const orc_fmt_def *f = &FMT[fmt];
+    unsigned sign = (code >> (f->bits - 1)) & 1u;
+    unsigned e = (code >> f->mbits) & ((1u << f->ebits) - 1u);
+    unsigned m = code & ((1u << f->mbits) - 1u);
+    unsigned eall = (1u << f->ebits) - 1u;
+    double v;
+    if (fmt == ORC_E4M3 && e == eall && m == (1u << f->mbits) - 1u)
+        return NAN;
+    if (fmt == ORC_E5M2 && e == eall) {
+        if (m != 0)
+            return NAN;
+        v = INFINITY;
+    } else if (e == 0) {
+        /* subnormal: 0.m x 2^(1-bias) */
+        v = ldexp((double)m, 1 - f->bias - f->mbits);
+    } else {
+        /* normal: 1.m x 2^(e-bias) */
+        v = ldexp((double)((1u << f->mbits) + m), (int)e - f->bias - f->mbits);
+    }
+    return sign ? -v : v;
+}
+
+/* Largest finite magnitude of a format (448, 57344, 6). */
+float orc_fmax(int fmt) { return (float)orc_decode(fmt, orc_max_code(fmt)); }
+
+/*
+ * E8M0: an unsigned, exponent-only byte; code c stands for 2^(c-127), the
+ * same field as an fp32 exponent; 0xFF is NaN.  ([MP] section "MXFP8", the
+ * float8_e8m0fnu description.)
+ */
+double orc_decode_e8m0(unsigned code)
+{
+    if (code == 0xFF)
+        return NAN;
+    return ldexp(1.0, (int)code - 127);
+}
+
+/* Table of the positive finite values of each format, built on first use
+ * from orc_decode; ascending in the code. */
+static double g_tab[3][128];
+static int g_tab_ready[3];
+
+static const double *value_table(int fmt)
+{
+    if (!g_tab_ready[fmt]) {
+        unsigned c;
+        for (c = 0; c <= orc_max_code(fmt); c++)
+            g_tab[fmt][c] = orc_decode(fmt, c);
+        g_tab_ready[fmt] = 1;
+    }
+    return g_tab[fmt];
+}
+
+/*
+ * Q_F(y): round the finite fp32 value y to format F, to nearest, ties to the
+ * code whose last mantissa bit is 0 (round-to-nearest-even, [CS] section
+ * "Current Scaling"; [MP] section "NVFP4" gives RTNE as the FP4 default).
+ * READING (saturation): a magnitude at or above the largest finite value
+ * gives that value, never NaN or Inf.  The sign of y is kept, also when the
+ * result is zero.
+ */
+unsigned orc_encode(int fmt, float y)
+{
+    const double *v = value_table(fmt);
+    unsigned top = orc_max_code(fmt);
+    unsigned sign = signbit(y) ? (1u << (FMT[fmt].bits - 1)) : 0u;
+    double a = fabs((double)y);
+    unsigned k;
+    if (a >= v[top]) {
+        k = top;
+    } else {
+        /* find lo with v[lo] <= a < v[lo+1] */
+        unsigned lo = 0, hi = top;
+        while (hi - lo > 1) {
+            unsigned mid = (lo + hi) / 2;
+            if (v[mid] <= a)
+                lo = mid;
+            else
+                hi = mid;
+        }
+        double half = 0.5 * (v[lo] + v[hi]); /* exact: both are short dyadics */
+        if (a < half)
+            k = lo;
+        else if (a > half)
+            k = hi;
+        else
+            k = (lo & 1u) ? hi : lo; /* tie: the even code */
+    }
+    return sign | k;
+}
+
+/* orc_encode over an array of n fp32 values. */
+void orc_encode_array(int fmt, const float *y, int64_t n, uint8_t *q)
+{
+    int64_t i;
+    for (i = 0; i < n; i++)
+        q[i] = (uint8_t)orc_encode(fmt, y[i]);
+}
+
+/* ------------------------------------------------------------------ */
+/* Inputs                                                              */
+/* ------------------------------------------------------------------ */
+
+/* Element i of the input as fp32; bf16 widens exactly (its bits are the top
+ * half of the fp32 bits). */
+static float load_x(const void *x, int dt, int64_t i)
+{
+    if (dt == ORC_IN_F32)
+        return ((const float *)x)[i];
+    uint32_t b = (uint32_t)((const uint16_t *)x)[i] << 16;
+    float f;
+    memcpy(&f, &b, 4);
+    return f;
+}
+
+/* Inputs must be finite ([CS] section "Current Scaling" states the formula
+ * for finite tensors).  Returns 0 if all are finite. */
+static int check_finite(const void *x, int dt, int64_t n)
+{
+    int64_t i;
+    for (i = 0; i < n; i++)
+        if (!isfinite(load_x(x, dt, i)))
+            return -1;
+    return 0;
+}
+
+/* Transpose of a row-major [R,C] input into a row-major [C,R] copy of the
+ * same element type. */
+static void *transpose_input(const void *x, int dt, int64_t R, int64_t C)
+{
+    size_t es = dt == ORC_IN_F32 ? 4 : 2;
+    char *t = (char *)malloc((size_t)(R * C) * es);
+    int64_t r, c;
+    if (!t)
+        return NULL;
+    for (r = 0; r < R; r++)
+        for (c = 0; c < C; c++)
+            memcpy(t + (size_t)(c * R + r) * es, (const char *)x + (size_t)(r * C + c) * es, es);
+    return t;
+}
+
+/* Byte transpose [R,C] -> [C,R]. */
+void orc_transpose_u8(const uint8_t *q, int64_t R, int64_t C, uint8_t *qt)
+{
+    int64_t r, c;
+    for (r = 0; r < R; r++)
+        for (c = 0; c < C; c++)
+            qt[c * R + r] = q[r * C + c];
+}
+
+/* fp32 transpose [R,C] -> [C,R]. */
+static void transpose_f32(const float *s, int64_t R, int64_t C, float *st)
+{
+    int64_t r, c;
+    for (r = 0; r < R; r++)
+        for (c = 0; c < C; c++)
+            st[c * R + r] = s[r * C + c];
+}
+
+/* ------------------------------------------------------------------ */
+/* Per-tensor scaling                                                  */
+/* ------------------------------------------------------------------ */
+
+/* a = max_i |x_i| over a rectangle of a row-major [*, ld] input. */
+static float amax_rect(const void *x, int dt, int64_t ld, int64_t r0, int64_t nr, int64_t c0, int64_t nc)
+{
+    float a = 0.0f;
+    int64_t r, c;
+    for (r = r0; r < r0 + nr; r++)
+        for (c = c0; c < c0 + nc; c++) {
+            float v = fabsf(load_x(x, dt, r * ld + c));
+            if (v > a)
+                a = v;
+        }
+    return a;
+}
+
+/* a = max_i |x_i| of the whole tensor ([CS] "Current Scaling"; [MP] FP8
+ * recipe 3, step 1). */
+float orc_amax(const void *x, int dt, int64_t n) { return amax_rect(x, dt, n, 0, 1, 0, n); }
+
+/*
+ * Scales from an amax a for a format whose largest value is fmax
+ * ([CS] "Current Scaling": alpha = Fmax / a multiplies before the cast,
+ * s = a / Fmax multiplies after it; [MP] "FP8 recipe": a unit's amax maps to
+ * the format's largest value).
+ * READING: both are fp32 and each is its own correctly rounded quotient (so
+ * they need not be exact reciprocals in fp32); s is the one stored.
+ * READING ([CS] says an all-zero tensor needs its own rule): a = 0 gives
+ * alpha = s = 1.  An alpha that overflows fp32 is held at FLT_MAX.
+ */
+void orc_tensor_scales(float a, float fmax, float *alpha, float *s)
+{
+    if (a == 0.0f) {
+        *alpha = 1.0f;
+        *s = 1.0f;
+        return;
+    }
+    float al = fmax / a;
+    if (al > FLT_MAX)
+        al = FLT_MAX;
+    *alpha = al;
+    *s = a / fmax;
+}
+
+/* q_i = Q(fp32(alpha * x_i)) over n elements ([CS] "Current Scaling"). */
+static void cast_run(const void *x, int dt, int64_t n, float alpha, int fmt, uint8_t *q)
+{
+    int64_t i;
+    for (i = 0; i < n; i++) {
+        float y = load_x(x, dt, i) * alpha;
+        q[i] = (uint8_t)orc_encode(fmt, y);
+    }
+}
+
+/*
+ * Per-tensor quantization with a given amax: the second half of current
+ * scaling, and the sharded form where the amax was reduced across shards
+ * first ([CS] section "成本与多 GPU 使用", all-gather example;
+ * [MP] section "FP8 通信", TP all-gather steps).
+ * Rowwise bytes are [R,C]; the colwise bytes are the transposed copy [C,R]
+ * made with the same scale ([MP] section "Per-tensor Current Scaling",
+ * cast + cast_transpose).
+ */
+int orc_quantize_with_amax(const void *x, int dt, int64_t R, int64_t C, int fmt, unsigned outputs,
+                           float amax, uint8_t *q_row, uint8_t *q_col, float *s_out)
+{
+    float alpha, s;
+    uint8_t *q;
+    if (fmt != ORC_E4M3 && fmt != ORC_E5M2)
+        return -2;
+    if (R < 0 || C < 0)
+        return -3;
+    if (check_finite(x, dt, R * C))
+        return -1;
+    orc_tensor_scales(amax, orc_fmax(fmt), &alpha, &s);
+    q = q_row ? q_row : (uint8_t *)malloc((size_t)(R * C));
+    cast_run(x, dt, R * C, alpha, fmt, q);
+    if ((outputs & ORC_COLWISE) && q_col)
+        orc_transpose_u8(q, R, C, q_col);
+    if (!q_row)
+        free(q);
+    if (s_out)
+        *s_out = s;
+    return 0;
+}
+
+/* Per-tensor current scaling: amax of this tensor, then scale and cast
+ * ([MP] FP8 recipe 3; [CS] "Current Scaling"). */
+int orc_quantize_current(const void *x, int dt, int64_t R, int64_t C, int fmt, unsigned outputs,
+                         uint8_t *q_row, uint8_t *q_col, float *s_out, float *amax_out)
+{
+    if (R < 0 || C < 0)
+        return -3;
+    if (check_finite(x, dt, R * C))
+        return -1;
+    float a = orc_amax(x, dt, R * C);
+    if (amax_out)
+        *amax_out = a;
+    return orc_quantize_with_amax(x, dt, R, C, fmt, outputs, a, q_row, q_col, s_out);
+}
+
+/*
+ * Per-tensor delayed scaling, one step ([MP] FP8 recipe 2; window length
+ * and the max rule from the Megatron flags in [LP] section 4.3).
+ *   1. cast with the scale alpha left by the previous steps;
+ *   2. record this tensor's amax a_t in the window: hist[step mod H] = a_t;
+ *   3. the next scale comes from m = max over the window:
+ *      alpha = Fmax/m, s = m/Fmax (as orc_tensor_scales).
+ * READING: the state starts as hist = 0, alpha = s = 1; an all-zero window
+ * (m = 0) leaves alpha and s unchanged.
+ */
+int orc_quantize_delayed(const void *x, int dt, int64_t R, int64_t C, int fmt, unsigned outputs,
+                         float *hist, int32_t H, float *alpha, float *s, int64_t step,
+                         uint8_t *q_row, uint8_t *q_col, float *amax_out)
+{
+    uint8_t *q;
+    int32_t j;
+    if (fmt != ORC_E4M3 && fmt != ORC_E5M2)
+        return -2;
+    if (H < 1 || step < 0 || R < 0 || C < 0)
+        return -3;
+    if (check_finite(x, dt, R * C))
+        return -1;
+    q = q_row ? q_row : (uint8_t *)malloc((size_t)(R * C));
+    cast_run(x, dt, R * C, *alpha, fmt, q);
+    if ((outputs & ORC_COLWISE) && q_col)
+        orc_transpose_u8(q, R, C, q_col);
+    if (!q_row)
+        free(q);
+    float a = orc_amax(x, dt, R * C);
+    if (amax_out)
+        *amax_out = a;
+    hist[step % H] = a;
+    float m = 0.0f;
+    for (j = 0; j < H; j++)
+        if (hist[j] > m)
+            m = hist[j];
+    if (m > 0.0f)
+        orc_tensor_scales(m, orc_fmax(fmt), alpha, s);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Blockwise fp32 scaling                                              */
+/* ------------------------------------------------------------------ */
+
+/*
+ * Each tile of br x bc elements is quantized as its own tensor with
+ * per-tensor current scaling to E4M3; its scale s_B = a_B/448 is stored in
+ * fp32 ([MP] FP8 recipe 4 and section "Blockwise scaling": 1x128 tiles for
+ * inputs and gradients, 128x128 tiles for weights, fp32 scales, pure E4M3).
+ * Data is [R,C]; scales are row-major [R/br, C/bc].
+ */
+static void block_rowwise(const void *x, int dt, int64_t R, int64_t C, int br, int bc, uint8_t *q, float *sc)
+{
+    int64_t tr, tc, r, c;
+    int64_t nbc = C / bc;
+    for (tr = 0; tr < R / br; tr++)
+        for (tc = 0; tc < nbc; tc++) {
+            float a = amax_rect(x, dt, C, tr * br, br, tc * bc, bc);
+            float alpha, s;
+            orc_tensor_scales(a, 448.0f, &alpha, &s);
+            sc[tr * nbc + tc] = s;
+            for (r = tr * br; r < (tr + 1) * br; r++)
+                for (c = tc * bc; c < (tc + 1) * bc; c++)
+                    q[r * C + c] = (uint8_t)orc_encode(ORC_E4M3, load_x(x, dt, r * C + c) * alpha);
+        }
+}
+
+/*
+ * Colwise copies ([MP] "Blockwise scaling", the three GEMMs):
+ *   1-D tiles (1 x bc): the transposed tensor X^T [C,R] is quantized with
+ *     1 x bc tiles, i.e. the tiles run down the columns of X.
+ *   2-D tiles: the colwise copy is the transpose of the rowwise bytes and
+ *     scales, since a square tile quantizes to the same values either way
+ *     ([MP] "Blockwise scaling", the closing remark on 2-D tiles).
+ */
+int orc_quantize_block(const void *x, int dt, int64_t R, int64_t C, int br, int bc, unsigned outputs,
+                       uint8_t *q_row, float *s_row, uint8_t *q_col, float *s_col)
+{
+    if (R <= 0 || C <= 0)
+        return -3;
+    if (!((br == 1 && bc == 128) || (br == 128 && bc == 128)))
+        return -2;
+    if (R % br || C % bc)
+        return -3;
+    if (check_finite(x, dt, R * C))
+        return -1;
+    if (br == 1) {
+        if (outputs & ORC_ROWWISE)
+            block_rowwise(x, dt, R, C, 1, bc, q_row, s_row);
+        if (outputs & ORC_COLWISE) {
+            if (R % bc)
+                return -3;
+            void *xt = transpose_input(x, dt, R, C);
+            block_rowwise(xt, dt, C, R, 1, bc, q_col, s_col);
+            free(xt);
+        }
+    } else {
+        uint8_t *q = q_row ? q_row : (uint8_t *)malloc((size_t)(R * C));
+        float *s = s_row ? s_row : (float *)malloc(sizeof(float) * (size_t)((R / br) * (C / bc)));
+        block_rowwise(x, dt, R, C, br, bc, q, s);
+        if (outputs & ORC_COLWISE) {
+            orc_transpose_u8(q, R, C, q_col);
+            transpose_f32(s, R / br, C / bc, s_col);
+        }
+        if (!q_row)
+            free(q);
+        if (!s_row)
+            free(s);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* MXFP8                                                               */
+/* ------------------------------------------------------------------ */
+
+/*
+ * E8M0 code of a 32-element block with amax a: the block scale is the power
+ * of two 2^e with e = floor(log2 a) - 8 ([MP] section "MXFP8" and FP8 recipe
+ * 5: 32-element blocks sharing one E8M0 power-of-two scale, E4M3 elements).
+ * READING: the exponent rule is the one this engine is specified with
+ * (8 = floor(log2 448)); e is held to the E8M0 range [-127, 127]; a = 0
+ * gives e = -127.
+ */
+unsigned orc_mx_code(float a)
+{
+    int ex, e;
+    if (a == 0.0f)
+        return 0;
+    frexp((double)a, &ex); /* a = f * 2^ex with f in [0.5, 1) */
+    e = (ex - 1) - 8;      /* floor(log2 a) - 8 */
+    if (e < -127)
+        e = -127;
+    if (e > 127)
+        e = 127;
+    return (unsigned)(e + 127);
+}
+
+/* Rowwise 1x32 MX blocks of a row-major [R,C] input: q = Q_E4M3(x * 2^-e). */
+static void mx_rowwise(const void *x, int dt, int64_t R, int64_t C, uint8_t *q, uint8_t *codes)
+{
+    int64_t r, b, c, nb = C / 32;
+    for (r = 0; r < R; r++)
+        for (b = 0; b < nb; b++) {
+            float a = amax_rect(x, dt, C, r, 1, b * 32, 32);
+            unsigned code = orc_mx_code(a);
+            int e = (int)code - 127;
+            codes[r * nb + b] = (uint8_t)code;
+            for (c = b * 32; c < b * 32 + 32; c++)
+                q[r * C + c] = (uint8_t)orc_encode(ORC_E4M3, ldexpf(load_x(x, dt, r * C + c), -e));
+        }
+}
+
+/*
+ * MXFP8: rowwise 1x32 blocks along the rows, and a colwise copy whose 32x1
+ * blocks run down the columns, stored transposed: [C,R] bytes and [C,R/32]
+ * codes, i.e. the rowwise recipe applied to X^T ([MP] section "MXFP8 recipe":
+ * rowwise and colwise copies of the same tensor, 1x32 and 32x1).
+ */
+int orc_quantize_mx(const void *x, int dt, int64_t R, int64_t C, unsigned outputs,
+                    uint8_t *q_row, uint8_t *e_row, uint8_t *q_col, uint8_t *e_col)
+{
+    if (R <= 0 || C <= 0)
+        return -3;
+    if (C % 32)
+        return -3;
+    if ((outputs & ORC_COLWISE) && R % 32)
+        return -3;
+    if (check_finite(x, dt, R * C))
+        return -1;
+    if (outputs & ORC_ROWWISE)
+        mx_rowwise(x, dt, R, C, q_row, e_row);
+    if (outputs & ORC_COLWISE) {
+        void *xt = transpose_input(x, dt, R, C);
+        mx_rowwise(xt, dt, C, R, q_col, e_col);
+        free(xt);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* NVFP4                                                               */
+/* ------------------------------------------------------------------ */
+
+/*
+ * NVFP4 ([MP] FP8 recipe 6: 1x16 blocks, E4M3 block scales, one extra fp32
+ * tensor-level scale; [LP] section 2.4: E2M1 elements, 16-element blocks,
+ * 16x16 blocks for weights, 1x16 for activations and gradients).
+ * READING (the two levels): the block amaxes divided by 6 (E2M1's largest
+ * value) form a small tensor {b_B}; that tensor is quantized to E4M3 with
+ * per-tensor current scaling, whose fp32 scale S is the tensor-level scale.
+ * Its amax is fp32(A/6), A the amax of the whole tensor.  Each block's
+ * decode scale is d_B = dec(c_B) * S, and the elements are q = Q_E2M1(x/d_B)
+ * computed as fp32(x * fp32(1/d_B)).
+ */
+typedef struct {
+    float alpha_s, S;
+} nvfp4_tensor;
+
+static nvfp4_tensor nvfp4_tensor_scale(float A)
+{
+    nvfp4_tensor t;
+    float b_amax = A / 6.0f;
+    orc_tensor_scales(b_amax, 448.0f, &t.alpha_s, &t.S);
+    return t;
+}
+
+/* One block of NVFP4: returns the E4M3 scale code and writes the nibbles
+ * (0..15) of its elements. */
+static unsigned nvfp4_block(const void *x, int dt, int64_t ld, int64_t r0, int br, int64_t c0, int bc,
+                            nvfp4_tensor t, uint8_t *nib /* [R,C] nibble per element */)
+{
+    float a = amax_rect(x, dt, ld, r0, br, c0, bc);
+    float b = a / 6.0f;
+    unsigned code = orc_encode(ORC_E4M3, b * t.alpha_s);
+    float d = (float)orc_decode(ORC_E4M3, code) * t.S;
+    float r = 0.0f;
+    int64_t i, j;
+    if (d != 0.0f) {
+        r = 1.0f / d;
+        if (r > FLT_MAX)
+            r = FLT_MAX;
+    }
+    for (i = r0; i < r0 + br; i++)
+        for (j = c0; j < c0 + bc; j++)
+            nib[i * ld + j] = (uint8_t)orc_encode(ORC_E2M1, load_x(x, dt, i * ld + j) * r);
+    return code;
+}
+
+/* READING: element 2k of a row goes to bits 3..0 of byte k, element 2k+1 to
+ * bits 7..4 ([MP] "NVFP4": two FP4 values per byte, high and low nibble). */
+static void pack_nibbles(const uint8_t *nib, int64_t R, int64_t C, uint8_t *p)
+{
+    int64_t r, k;
+    for (r = 0; r < R; r++)
+        for (k = 0; k < C / 2; k++)
+            p[r * (C / 2) + k] = (uint8_t)(nib[r * C + 2 * k] | (nib[r * C + 2 * k + 1] << 4));
+}
+
+static void nvfp4_rowwise(const void *x, int dt, int64_t R, int64_t C, int br, int bc, nvfp4_tensor t,
+                          uint8_t *p, uint8_t *codes, uint8_t *nib_out)
+{
+    int64_t tr, tc, nbc = C / bc;
+    uint8_t *nib = (uint8_t *)malloc((size_t)(R * C));
+    for (tr = 0; tr < R / br; tr++)
+        for (tc = 0; tc < nbc; tc++)
+            codes[tr * nbc + tc] = (uint8_t)nvfp4_block(x, dt, C, tr * br, br, tc * bc, bc, t, nib);
+    pack_nibbles(nib, R, C, p);
+    if (nib_out)
+        memcpy(nib_out, nib, (size_t)(R * C));
+    free(nib);
+}
+
+/*
+ * Rowwise: packed data [R, C/2], E4M3 codes [R/br, C/bc], tensor scale S.
+ * Colwise (READING): 1x16 -> the same recipe on X^T, with the same tensor
+ * scale (the amax of X^T is the amax of X); 16x16 -> the element codes of
+ * the rowwise result transposed and re-packed along the rows of X^T, codes
+ * transposed ([MP] closing remarks: FP4 GEMMs need two copies even for 2-D
+ * weight tiles).
+ */
+int orc_quantize_nvfp4(const void *x, int dt, int64_t R, int64_t C, int br, int bc, unsigned outputs,
+                       uint8_t *p_row, uint8_t *c_row, uint8_t *p_col, uint8_t *c_col,
+                       float *S_out, float *amax_out)
+{
+    if (R <= 0 || C <= 0)
+        return -3;
+    if (!((br == 1 && bc == 16) || (br == 16 && bc == 16)))
+        return -2;
+    if (R % br || C % bc)
+        return -3;
+    if ((outputs & ORC_COLWISE) && (R % 16))
+        return -3;
+    if (check_finite(x, dt, R * C))
+        return -1;
+    float A = orc_amax(x, dt, R * C);
+    nvfp4_tensor t = nvfp4_tensor_scale(A);
+    if (S_out)
+        *S_out = t.S;
+    if (amax_out)
+        *amax_out = A;
+    if (br == 1) {
+        if (outputs & ORC_ROWWISE)
+            nvfp4_rowwise(x, dt, R, C, 1, bc, t, p_row, c_row, NULL);
+        if (outputs & ORC_COLWISE) {
+            void *xt = transpose_input(x, dt, R, C);
+            nvfp4_rowwise(xt, dt, C, R, 1, bc, t, p_col, c_col, NULL);
+            free(xt);
+        }
+    } else {
+        uint8_t *nib = (uint8_t *)malloc((size_t)(R * C));
+        uint8_t *p = p_row ? p_row : (uint8_t *)malloc((size_t)(R * C / 2));
+        uint8_t *cd = c_row ? c_row : (uint8_t *)malloc((size_t)((R / br) * (C / bc)));
+        nvfp4_rowwise(x, dt, R, C, br, bc, t, p, cd, nib);
+        if (outputs & ORC_COLWISE) {
+            uint8_t *nt = (uint8_t *)malloc((size_t)(R * C));
+            orc_transpose_u8(nib, R, C, nt);
+            pack_nibbles(nt, C, R, p_col);
+            orc_transpose_u8(cd, R / br, C / bc, c_col);
+            free(nt);
+        }
+        free(nib);
+        if (!p_row)
+            free(p);
+        if (!c_row)
+            free(cd);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Dequantization                                                      */
+/* ------------------------------------------------------------------ */
+
+/* x_hat = fp32(dec(q) * s) over n codes ([CS] "Current Scaling": the value
+ * is restored by multiplying the FP8 value by s). */
+void orc_dequant_tensor(const uint8_t *q, int64_t n, int fmt, float s, float *y)
+{
+    int64_t i;
+    for (i = 0; i < n; i++)
+        y[i] = (float)orc_decode(fmt, q[i]) * s;
+}
+
+/* Blockwise: each element times its tile's s_B. */
+void orc_dequant_block(const uint8_t *q, const float *sc, int64_t R, int64_t C, int br, int bc, float *y)
+{
+    int64_t r, c;
+    for (r = 0; r < R; r++)
+        for (c = 0; c < C; c++)
+            y[r * C + c] = (float)orc_decode(ORC_E4M3, q[r * C + c]) * sc[(r / br) * (C / bc) + c / bc];
+}
+
+/* MX: each element times 2^(code-127) of its block ([MP] "MXFP8": value is
+ * element times the block's shared scale). */
+void orc_dequant_mx(const uint8_t *q, const uint8_t *codes, int64_t R, int64_t C, float *y)
+{
+    int64_t r, c;
+    for (r = 0; r < R; r++)
+        for (c = 0; c < C; c++)
+            y[r * C + c] = ldexpf((float)orc_decode(ORC_E4M3, q[r * C + c]), (int)codes[r * (C / 32) + c / 32] - 127);
+}
+
+/* NVFP4: each element times d_B = fp32(dec(c_B) * S). */
+void orc_dequant_nvfp4(const uint8_t *p, const uint8_t *codes, float S, int64_t R, int64_t C, int br, int bc,
+                       float *y)
+{
+    int64_t r, c;
+    for (r = 0; r < R; r++)
+        for (c = 0; c < C; c++) {
+            uint8_t byte = p[r * (C / 2) + c / 2];
+            unsigned nib = (c & 1) ? (byte >> 4) : (byte & 0xF);
+            float d = (float)orc_decode(ORC_E4M3, codes[(r / br) * (C / bc) + c / bc]) * S;
+            y[r * C + c] = (float)orc_decode(ORC_E2M1, nib) * d;
+        }
+}
