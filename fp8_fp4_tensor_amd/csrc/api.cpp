@@ -1,0 +1,435 @@
+// api.cpp -- the C ABI of libfq.so (include/fq.h): argument validation,
+// buffer sizes and dispatch of the HIP kernels onto the caller's stream.
+//
+// Every check runs on the host before the first launch, so an invalid call
+// enqueues nothing and writes nothing.
+#include "fq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "launch.hpp"
+
+namespace {
+
+using namespace fq;
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+constexpr int32_t kMaxHistory = 1 << 24;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool per_tensor(int32_t r) { return r == FQ_PER_TENSOR_CURRENT || r == FQ_PER_TENSOR_DELAYED; }
+
+fq_status check_desc(const fq_desc* d)
+{
+    if (!d)
+        return FQ_E_INVALID;
+    if (d->recipe < FQ_PER_TENSOR_CURRENT || d->recipe > FQ_NVFP4)
+        return FQ_E_INVALID;
+    if (d->in_dtype != FQ_IN_F32 && d->in_dtype != FQ_IN_BF16)
+        return FQ_E_INVALID;
+    if (d->format < FQ_E4M3 || d->format > FQ_E2M1)
+        return FQ_E_INVALID;
+    if (d->rows < 0 || d->cols < 0)
+        return FQ_E_INVALID;
+    if ((d->outputs & ~3u) != 0 || (d->outputs & 3u) == 0)
+        return FQ_E_INVALID;
+    if (d->cols > 0 && d->rows > kMaxElems / d->cols)
+        return FQ_E_SHAPE;
+    const bool col = (d->outputs & FQ_COLWISE) != 0;
+    const int64_t R = d->rows, C = d->cols;
+    const int br = d->block_rows, bc = d->block_cols;
+    switch (d->recipe) {
+    case FQ_PER_TENSOR_CURRENT:
+    case FQ_PER_TENSOR_DELAYED:
+        if (d->format != FQ_E4M3 && d->format != FQ_E5M2)
+            return FQ_E_UNSUPPORTED;
+        return FQ_OK;
+    case FQ_BLOCK_FP32:
+        if (d->format != FQ_E4M3)
+            return FQ_E_UNSUPPORTED;
+        if (!((br == 1 && bc == 128) || (br == 128 && bc == 128)))
+            return FQ_E_UNSUPPORTED;
+        if (R % br || C % bc)
+            return FQ_E_SHAPE;
+        if (col && R % 128)
+            return FQ_E_SHAPE;
+        return FQ_OK;
+    case FQ_MX:
+        if (d->format != FQ_E4M3)
+            return FQ_E_UNSUPPORTED;
+        if (!(br == 1 && bc == 32))
+            return FQ_E_UNSUPPORTED;
+        if (C % 32 || (col && R % 32))
+            return FQ_E_SHAPE;
+        return FQ_OK;
+    case FQ_NVFP4:
+        if (d->format != FQ_E2M1)
+            return FQ_E_UNSUPPORTED;
+        if (!((br == 1 && bc == 16) || (br == 16 && bc == 16)))
+            return FQ_E_UNSUPPORTED;
+        if (R % br || C % 16 || (col && R % 16))
+            return FQ_E_SHAPE;
+        return FQ_OK;
+    }
+    return FQ_E_INVALID;
+}
+
+struct Sizes {
+    size_t row_data = 0, row_scale = 0, col_data = 0, col_scale = 0, ws = 0;
+};
+
+Sizes sizes_of(const fq_desc* d)
+{
+    Sizes z;
+    const size_t R = (size_t)d->rows, C = (size_t)d->cols;
+    const bool row = d->outputs & FQ_ROWWISE, col = d->outputs & FQ_COLWISE;
+    switch (d->recipe) {
+    case FQ_PER_TENSOR_CURRENT:
+    case FQ_PER_TENSOR_DELAYED:
+        z.row_data = row ? R * C : 0;
+        z.col_data = col ? R * C : 0;
+        z.ws = kPartialsBytes;
+        break;
+    case FQ_BLOCK_FP32:
+        z.row_data = row ? R * C : 0;
+        z.col_data = col ? R * C : 0;
+        if (d->block_rows == 1) {
+            z.row_scale = row ? R * (C / 128) * 4 : 0;
+            z.col_scale = col ? C * (R / 128) * 4 : 0;
+        } else {
+            z.row_scale = row ? (R / 128) * (C / 128) * 4 : 0;
+            z.col_scale = col ? (C / 128) * (R / 128) * 4 : 0;
+        }
+        break;
+    case FQ_MX:
+        z.row_data = row ? R * C : 0;
+        z.col_data = col ? R * C : 0;
+        z.row_scale = row ? R * (C / 32) : 0;
+        z.col_scale = col ? C * (R / 32) : 0;
+        break;
+    case FQ_NVFP4:
+        z.row_data = row ? R * C / 2 : 0;
+        z.col_data = col ? R * C / 2 : 0;
+        if (d->block_rows == 1) {
+            z.row_scale = row ? R * (C / 16) : 0;
+            z.col_scale = col ? C * (R / 16) : 0;
+        } else {
+            z.row_scale = row ? (R / 16) * (C / 16) : 0;
+            z.col_scale = col ? (C / 16) * (R / 16) : 0;
+        }
+        z.ws = kPartialsBytes;
+        break;
+    }
+    return z;
+}
+
+// Output planes a recipe needs, present and aligned.
+fq_status check_out(const fq_desc* d, const fq_quantized* o, bool need_tensor_scale)
+{
+    if (!o)
+        return FQ_E_INVALID;
+    const bool any = d->rows > 0 && d->cols > 0;
+    const bool scaled_planes = d->recipe == FQ_BLOCK_FP32 || d->recipe == FQ_MX || d->recipe == FQ_NVFP4;
+    const fq_plane* planes[2] = {&o->rowwise, &o->colwise};
+    const uint32_t bits[2] = {FQ_ROWWISE, FQ_COLWISE};
+    for (int i = 0; i < 2; ++i) {
+        if (!(d->outputs & bits[i]))
+            continue;
+        if (any && !planes[i]->data)
+            return FQ_E_INVALID;
+        if (any && scaled_planes && !planes[i]->scale)
+            return FQ_E_INVALID;
+        if (!aligned(planes[i]->data, 16) || !aligned(planes[i]->scale, 16))
+            return FQ_E_ALIGN;
+    }
+    if (need_tensor_scale && !o->tensor_scale)
+        return FQ_E_INVALID;
+    if (!aligned(o->tensor_scale, 4) || !aligned(o->amax, 4))
+        return FQ_E_ALIGN;
+    return FQ_OK;
+}
+
+fq_status check_x(const fq_desc* d, const void* x)
+{
+    if (d->rows > 0 && d->cols > 0 && !x)
+        return FQ_E_INVALID;
+    if (!aligned(x, 16))
+        return FQ_E_ALIGN;
+    return FQ_OK;
+}
+
+fq_status check_ws(const Sizes& z, const void* ws, size_t ws_bytes)
+{
+    if (z.ws == 0)
+        return FQ_OK;
+    if (!ws || ws_bytes < z.ws)
+        return FQ_E_WORKSPACE;
+    if (!aligned(ws, 16))
+        return FQ_E_ALIGN;
+    return FQ_OK;
+}
+
+fq_status hip_status(hipError_t e) { return e == hipSuccess ? FQ_OK : FQ_E_HIP; }
+
+int elem_bytes(const fq_desc* d) { return d->in_dtype == FQ_IN_BF16 ? 2 : 4; }
+
+// Per-tensor cast (current, with a given amax, or delayed) of a validated desc.
+fq_status run_per_tensor_cast(const fq_desc* d, const void* x, ScaleSrc src, const fq_quantized* o, float* s_out,
+                              float* amax_out, float* partials_out, int grid, hipStream_t st)
+{
+    const int bf = d->in_dtype == FQ_IN_BF16;
+    const int64_t n = d->rows * d->cols;
+    uint8_t* q = (d->outputs & FQ_ROWWISE) ? (uint8_t*)o->rowwise.data : nullptr;
+    uint8_t* qt = (d->outputs & FQ_COLWISE) ? (uint8_t*)o->colwise.data : nullptr;
+    if (qt)
+        return hip_status(launch_cast_tensor_2d(x, bf, d->format, d->rows, d->cols, src, q, qt, s_out, amax_out,
+                                                partials_out, grid, st));
+    return hip_status(launch_cast_tensor(x, bf, d->format, n, src, q, s_out, amax_out, partials_out, grid, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fq_status_str(fq_status s)
+{
+    switch (s) {
+    case FQ_OK: return "FQ_OK";
+    case FQ_E_INVALID: return "FQ_E_INVALID: null pointer, bad enum value or negative size";
+    case FQ_E_UNSUPPORTED: return "FQ_E_UNSUPPORTED: recipe, format or block combination not offered";
+    case FQ_E_SHAPE: return "FQ_E_SHAPE: shape not divisible by the block, or too large";
+    case FQ_E_ALIGN: return "FQ_E_ALIGN: pointer not 16-byte (tensor) or 4-byte (scalar) aligned";
+    case FQ_E_WORKSPACE: return "FQ_E_WORKSPACE: workspace missing or too small";
+    case FQ_E_HIP: return "FQ_E_HIP: a kernel launch failed";
+    }
+    return "unknown fq_status";
+}
+
+fq_status fq_sizes(const fq_desc* d, size_t* row_data, size_t* row_scale, size_t* col_data, size_t* col_scale,
+                   size_t* workspace)
+{
+    const fq_status st = check_desc(d);
+    if (st != FQ_OK)
+        return st;
+    const Sizes z = sizes_of(d);
+    if (row_data)
+        *row_data = z.row_data;
+    if (row_scale)
+        *row_scale = z.row_scale;
+    if (col_data)
+        *col_data = z.col_data;
+    if (col_scale)
+        *col_scale = z.col_scale;
+    if (workspace)
+        *workspace = z.ws;
+    return FQ_OK;
+}
+
+fq_status fq_amax(const fq_desc* d, const void* x, float* amax_out, void* ws, size_t ws_bytes, hipStream_t st)
+{
+    if (!d)
+        return FQ_E_INVALID;
+    if (d->in_dtype != FQ_IN_F32 && d->in_dtype != FQ_IN_BF16)
+        return FQ_E_INVALID;
+    if (d->rows < 0 || d->cols < 0)
+        return FQ_E_INVALID;
+    if (d->cols > 0 && d->rows > kMaxElems / d->cols)
+        return FQ_E_SHAPE;
+    if (!amax_out)
+        return FQ_E_INVALID;
+    fq_status s = check_x(d, x);
+    if (s != FQ_OK)
+        return s;
+    if (!aligned(amax_out, 4))
+        return FQ_E_ALIGN;
+    Sizes z;
+    z.ws = kPartialsBytes;
+    if ((s = check_ws(z, ws, ws_bytes)) != FQ_OK)
+        return s;
+    const int64_t n = d->rows * d->cols;
+    const int g = amax_grid(n, elem_bytes(d));
+    float* partials = (float*)ws;
+    if ((s = hip_status(launch_amax_partial(x, d->in_dtype == FQ_IN_BF16, n, partials, g, st))) != FQ_OK)
+        return s;
+    return hip_status(launch_amax_finish(partials, g, amax_out, st));
+}
+
+fq_status fq_quantize(const fq_desc* d, const void* x, const fq_quantized* o, void* ws, size_t ws_bytes,
+                      hipStream_t st)
+{
+    fq_status s = check_desc(d);
+    if (s != FQ_OK)
+        return s;
+    if (d->recipe == FQ_PER_TENSOR_DELAYED)
+        return FQ_E_UNSUPPORTED;
+    if ((s = check_x(d, x)) != FQ_OK)
+        return s;
+    const bool tensor_scale = d->recipe == FQ_PER_TENSOR_CURRENT || d->recipe == FQ_NVFP4;
+    if ((s = check_out(d, o, tensor_scale)) != FQ_OK)
+        return s;
+    const Sizes z = sizes_of(d);
+    if ((s = check_ws(z, ws, ws_bytes)) != FQ_OK)
+        return s;
+
+    const int bf = d->in_dtype == FQ_IN_BF16;
+    const int64_t R = d->rows, C = d->cols, n = R * C;
+    const bool row = d->outputs & FQ_ROWWISE, col = d->outputs & FQ_COLWISE;
+    switch (d->recipe) {
+    case FQ_PER_TENSOR_CURRENT: {
+        const int g = amax_grid(n, elem_bytes(d));
+        float* partials = (float*)ws;
+        if ((s = hip_status(launch_amax_partial(x, bf, n, partials, g, st))) != FQ_OK)
+            return s;
+        ScaleSrc src;
+        src.partials = partials;
+        src.n_partials = g;
+        return run_per_tensor_cast(d, x, src, o, o->tensor_scale, o->amax, nullptr, 0, st);
+    }
+    case FQ_BLOCK_FP32:
+        if (n == 0)
+            return FQ_OK;
+        if (d->block_rows == 1) {
+            if (row && (s = hip_status(launch_block_1x128(x, bf, R, C, (uint8_t*)o->rowwise.data,
+                                                          (float*)o->rowwise.scale, st))) != FQ_OK)
+                return s;
+            if (col)
+                return hip_status(launch_block_1x128_colwise(x, bf, R, C, (uint8_t*)o->colwise.data,
+                                                             (float*)o->colwise.scale, st));
+            return FQ_OK;
+        }
+        return hip_status(launch_block_128x128(x, bf, R, C, row ? (uint8_t*)o->rowwise.data : nullptr,
+                                               row ? (float*)o->rowwise.scale : nullptr,
+                                               col ? (uint8_t*)o->colwise.data : nullptr,
+                                               col ? (float*)o->colwise.scale : nullptr, st));
+    case FQ_MX:
+        if (n == 0)
+            return FQ_OK;
+        return hip_status(launch_mx(x, bf, R, C, row ? (uint8_t*)o->rowwise.data : nullptr,
+                                    row ? (uint8_t*)o->rowwise.scale : nullptr,
+                                    col ? (uint8_t*)o->colwise.data : nullptr,
+                                    col ? (uint8_t*)o->colwise.scale : nullptr, st));
+    case FQ_NVFP4: {
+        const int g = amax_grid(n, elem_bytes(d));
+        float* partials = (float*)ws;
+        if ((s = hip_status(launch_amax_partial(x, bf, n, partials, g, st))) != FQ_OK)
+            return s;
+        ScaleSrc src;
+        src.partials = partials;
+        src.n_partials = g;
+        return hip_status(launch_nvfp4(x, bf, R, C, d->block_rows, src, row ? (uint8_t*)o->rowwise.data : nullptr,
+                                       row ? (uint8_t*)o->rowwise.scale : nullptr,
+                                       col ? (uint8_t*)o->colwise.data : nullptr,
+                                       col ? (uint8_t*)o->colwise.scale : nullptr, o->tensor_scale, o->amax, st));
+    }
+    }
+    return FQ_E_INVALID;
+}
+
+fq_status fq_quantize_with_amax(const fq_desc* d, const void* x, const float* amax_in, const fq_quantized* o,
+                                void* ws, size_t ws_bytes, hipStream_t st)
+{
+    (void)ws;
+    (void)ws_bytes;
+    fq_status s = check_desc(d);
+    if (s != FQ_OK)
+        return s;
+    if (d->recipe != FQ_PER_TENSOR_CURRENT && d->recipe != FQ_NVFP4)
+        return FQ_E_UNSUPPORTED;
+    if (!amax_in)
+        return FQ_E_INVALID;
+    if (!aligned(amax_in, 4))
+        return FQ_E_ALIGN;
+    if ((s = check_x(d, x)) != FQ_OK)
+        return s;
+    if ((s = check_out(d, o, true)) != FQ_OK)
+        return s;
+    ScaleSrc src;
+    src.amax_in = amax_in;
+    if (d->recipe == FQ_PER_TENSOR_CURRENT)
+        return run_per_tensor_cast(d, x, src, o, o->tensor_scale, o->amax, nullptr, 0, st);
+    const bool row = d->outputs & FQ_ROWWISE, col = d->outputs & FQ_COLWISE;
+    return hip_status(launch_nvfp4(x, d->in_dtype == FQ_IN_BF16, d->rows, d->cols, d->block_rows, src,
+                                   row ? (uint8_t*)o->rowwise.data : nullptr,
+                                   row ? (uint8_t*)o->rowwise.scale : nullptr,
+                                   col ? (uint8_t*)o->colwise.data : nullptr,
+                                   col ? (uint8_t*)o->colwise.scale : nullptr, o->tensor_scale, o->amax, st));
+}
+
+fq_status fq_quantize_delayed(const fq_desc* d, const void* x, const fq_delayed_state* state,
+                              const fq_quantized* o, void* ws, size_t ws_bytes, hipStream_t st)
+{
+    fq_status s = check_desc(d);
+    if (s != FQ_OK)
+        return s;
+    if (d->recipe != FQ_PER_TENSOR_DELAYED)
+        return FQ_E_UNSUPPORTED;
+    if (!state || !state->amax_history || !state->scale || !state->scale_inv)
+        return FQ_E_INVALID;
+    if (state->history_len < 1 || state->history_len > kMaxHistory || state->step < 0)
+        return FQ_E_INVALID;
+    if (!aligned(state->amax_history, 4) || !aligned(state->scale, 4) || !aligned(state->scale_inv, 4))
+        return FQ_E_ALIGN;
+    if ((s = check_x(d, x)) != FQ_OK)
+        return s;
+    if ((s = check_out(d, o, false)) != FQ_OK)
+        return s;
+    const Sizes z = sizes_of(d);
+    if ((s = check_ws(z, ws, ws_bytes)) != FQ_OK)
+        return s;
+    const int64_t n = d->rows * d->cols;
+    float* partials = (float*)ws;
+    const int g = amax_grid(n, elem_bytes(d));
+    ScaleSrc src;
+    src.alpha_in = state->scale;
+    src.s_in = state->scale_inv;
+    if ((s = run_per_tensor_cast(d, x, src, o, o->tensor_scale, nullptr, partials, g, st)) != FQ_OK)
+        return s;
+    const int slot = (int)(state->step % state->history_len);
+    const float fmax_v = d->format == FQ_E4M3 ? 448.0f : 57344.0f;
+    return hip_status(launch_delayed_finish(partials, g, state->amax_history, state->history_len, slot,
+                                            state->scale, state->scale_inv, fmax_v, o->amax, st));
+}
+
+fq_status fq_dequantize(const fq_desc* d, const fq_quantized* in, int32_t which, float* y, hipStream_t st)
+{
+    fq_status s = check_desc(d);
+    if (s != FQ_OK)
+        return s;
+    if (which != FQ_ROWWISE && which != FQ_COLWISE)
+        return FQ_E_INVALID;
+    if (!(d->outputs & (uint32_t)which))
+        return FQ_E_INVALID;
+    const bool ts = per_tensor(d->recipe) || d->recipe == FQ_NVFP4;
+    if ((s = check_out(d, in, ts)) != FQ_OK)
+        return s;
+    const int64_t R0 = d->rows, C0 = d->cols;
+    if (R0 * C0 == 0)
+        return FQ_OK;
+    if (!y)
+        return FQ_E_INVALID;
+    if (!aligned(y, 16))
+        return FQ_E_ALIGN;
+    const bool colw = which == FQ_COLWISE;
+    const fq_plane& p = colw ? in->colwise : in->rowwise;
+    // a colwise plane is the rowwise layout of the transposed shape
+    const int64_t R = colw ? C0 : R0, C = colw ? R0 : C0;
+    switch (d->recipe) {
+    case FQ_PER_TENSOR_CURRENT:
+    case FQ_PER_TENSOR_DELAYED:
+        return hip_status(launch_dequant_tensor((const uint8_t*)p.data, d->format, R * C, in->tensor_scale, y, st));
+    case FQ_BLOCK_FP32:
+        return hip_status(launch_dequant_block((const uint8_t*)p.data, (const float*)p.scale, R, C,
+                                               d->block_rows, 128, y, st));
+    case FQ_MX:
+        return hip_status(launch_dequant_mx((const uint8_t*)p.data, (const uint8_t*)p.scale, R, C, y, st));
+    case FQ_NVFP4:
+        return hip_status(launch_dequant_nvfp4((const uint8_t*)p.data, (const uint8_t*)p.scale, in->tensor_scale, R,
+                                               C, d->block_rows, 16, y, st));
+    }
+    return FQ_E_INVALID;
+}
+
+}  // extern "C"

@@ -1,0 +1,230 @@
+// k_block.hip -- blockwise E4M3 quantization with an fp32 scale per tile:
+// 1x128 tiles for activations and gradients, 128x128 tiles for weights.
+//
+// Source: [MP] "混合精度训练：fp16 到 fp8" (garden.houmin.site), section
+// "FP8 recipe" item 4 and section "Blockwise scaling" (the DeepSeek-V3-like
+// recipe: pure E4M3, 1x128 and 128x128 tiles, fp32 scaling factors, and the
+// three GEMMs that read X^T with 1x128 tiles and W^T with 128x128 tiles).
+// Each tile is quantized like a tensor under current scaling:
+// a_B = max|x|, alpha_B = 448/a_B, q = Q(fp32(alpha_B x)), s_B = a_B/448.
+//
+//   k_block_1x128      rows are contiguous, so 1x128 tiles are consecutive
+//                      128-element runs of the flat tensor: one tile is 16
+//                      lanes x 16 bytes of bf16 (32 lanes for fp32), and the
+//                      tile max is a 4-step DPP reduction inside a row of
+//                      lanes. One read, no LDS.
+//   k_block_1x128_col  the colwise copy: 1x128 tiles of X^T, i.e. 128-row
+//                      runs down each column. A 128-row x 256-column slab is
+//                      staged in LDS with coalesced row loads; each thread
+//                      then owns one column: reduces it, casts it and writes
+//                      its 128 codes as one contiguous 128-byte line of X^T.
+//   k_block_128x128    one workgroup per tile, kept in registers between the
+//                      tile max and the cast; the colwise copy is the byte
+//                      transpose of the same codes, through LDS.
+#include <algorithm>
+
+#include "codec.hpp"
+#include "launch.hpp"
+
+namespace fq {
+namespace {
+
+constexpr int kLoads = 4;
+constexpr int kMaxGrid = 4096;
+
+template <typename T>
+__global__ __launch_bounds__(kWG) void k_block_1x128(const T* __restrict__ x, int64_t n, uint8_t* __restrict__ q,
+                                                     float* __restrict__ s_out)
+{
+    constexpr int E = In<T>::kE, U = 64 * E, LPB = 128 / E;
+    const int lane = threadIdx.x & 63;
+    const int64_t nunits = cdiv(n, U);
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    for (int64_t u0 = wave * kLoads; u0 < nunits; u0 += nwaves * kLoads) {
+        u32x4 v[kLoads];
+#pragma unroll
+        for (int j = 0; j < kLoads; ++j) {
+            const int64_t e = (u0 + j) * U + lane * E;
+            v[j] = (u0 + j < nunits && e < n) ? ld16_stream(x + e) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int j = 0; j < kLoads; ++j) {
+            if (u0 + j >= nunits)
+                break;
+            const int64_t e = (u0 + j) * U + lane * E;
+            float f[E];
+            In<T>::unpack(v[j], f);
+            const float a = max_lanes<LPB>(absmax<E>(f));
+            float alpha, s;
+            tensor_scales(a, 448.0f, alpha, s);
+            if (e < n) {
+                Enc8<kE4M3, E>::store(q + e, f, alpha);
+                if ((lane & (LPB - 1)) == 0)
+                    s_out[e / 128] = s;
+            }
+        }
+    }
+}
+
+// Colwise 1x128: tiles of X^T. Slab of 128 rows x TC columns in LDS.
+template <typename T>
+__global__ __launch_bounds__(kWG) void k_block_1x128_col(const T* __restrict__ x, int64_t R, int64_t C,
+                                                         uint8_t* __restrict__ qt, float* __restrict__ st)
+{
+    constexpr int TC = sizeof(T) == 2 ? 256 : 128;           // columns per slab (64 KiB of LDS)
+    constexpr int E = In<T>::kE, LPR = TC / E;               // lanes per slab row
+    constexpr int RPR = kWG / LPR;                           // slab rows per load round
+    extern __shared__ __align__(16) unsigned char smem[];
+    T* tile = reinterpret_cast<T*>(smem);                    // [128][TC]
+    const int64_t ntc = cdiv(C, TC);
+    const int64_t r0 = (int64_t)(blockIdx.x / ntc) * 128, c0 = (int64_t)(blockIdx.x % ntc) * TC;
+    const int cc = (threadIdx.x % LPR) * E;
+    // stage the slab: coalesced 16-byte loads along rows
+#pragma unroll 4
+    for (int rr = threadIdx.x / LPR; rr < 128; rr += RPR) {
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if (c0 + cc < C)
+            v = ld16_stream(x + (r0 + rr) * C + c0 + cc);
+        *reinterpret_cast<u32x4*>(tile + rr * TC + cc) = v;
+    }
+    __syncthreads();
+    const int c = threadIdx.x;
+    if (c >= TC || c0 + c >= C)
+        return;
+    float a = 0.0f;
+    for (int r = 0; r < 128; ++r)
+        a = fmaxf(a, fabsf(In<T>::load1(tile, (int64_t)r * TC + c)));
+    float alpha, s;
+    tensor_scales(a, 448.0f, alpha, s);
+    uint8_t* out = qt + (c0 + c) * R + r0;
+#pragma unroll 2
+    for (int r = 0; r < 128; r += 16) {
+        float f[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            f[k] = In<T>::load1(tile, (int64_t)(r + k) * TC + c);
+        u32x4 w;
+        w[0] = enc4<kE4M3>(f[0], f[1], f[2], f[3], alpha);
+        w[1] = enc4<kE4M3>(f[4], f[5], f[6], f[7], alpha);
+        w[2] = enc4<kE4M3>(f[8], f[9], f[10], f[11], alpha);
+        w[3] = enc4<kE4M3>(f[12], f[13], f[14], f[15], alpha);
+        st16_stream(out + r, w);
+    }
+    st[(c0 + c) * (R / 128) + r0 / 128] = s;
+}
+
+// 128x128 tiles, one workgroup each. q/s rowwise (may be null), qt/st
+// colwise (may be null).
+template <typename T>
+__global__ __launch_bounds__(kWG) void k_block_128x128(const T* __restrict__ x, int64_t R, int64_t C,
+                                                       uint8_t* __restrict__ q, float* __restrict__ s_out,
+                                                       uint8_t* __restrict__ qt, float* __restrict__ st)
+{
+    constexpr int E = In<T>::kE, LPR = 128 / E, RPR = kWG / LPR, ROUNDS = 128 / RPR;
+    __shared__ float lds[4];
+    __shared__ __align__(16) uint8_t codes[128][128 + 16];
+    const int64_t ntc = C / 128, ntr = R / 128;
+    const int64_t tr = blockIdx.x / ntc, tc = blockIdx.x % ntc;
+    const int64_t r0 = tr * 128, c0 = tc * 128;
+    const int cc = (threadIdx.x % LPR) * E, rr0 = threadIdx.x / LPR;
+    u32x4 v[ROUNDS];
+#pragma unroll
+    for (int k = 0; k < ROUNDS; ++k)
+        v[k] = ld16_stream(x + (r0 + rr0 + k * RPR) * C + c0 + cc);
+    float m = 0.0f;
+#pragma unroll
+    for (int k = 0; k < ROUNDS; ++k) {
+        float f[E];
+        In<T>::unpack(v[k], f);
+        m = fmaxf(m, absmax<E>(f));
+    }
+    const float a = max_workgroup(m, lds);
+    float alpha, s;
+    tensor_scales(a, 448.0f, alpha, s);
+#pragma unroll
+    for (int k = 0; k < ROUNDS; ++k) {
+        float f[E];
+        In<T>::unpack(v[k], f);
+        const int rr = rr0 + k * RPR;
+        if constexpr (E == 8) {
+            u32x2 w;
+            w[0] = enc4<kE4M3>(f[0], f[1], f[2], f[3], alpha);
+            w[1] = enc4<kE4M3>(f[4], f[5], f[6], f[7], alpha);
+            if (q)
+                st8_stream(q + (r0 + rr) * C + c0 + cc, w);
+            if (qt)
+                *reinterpret_cast<u32x2*>(&codes[rr][cc]) = w;
+        } else {
+            const uint32_t w = enc4<kE4M3>(f[0], f[1], f[2], f[3], alpha);
+            if (q)
+                st4_stream(q + (r0 + rr) * C + c0 + cc, w);
+            if (qt)
+                *reinterpret_cast<uint32_t*>(&codes[rr][cc]) = w;
+        }
+    }
+    if (threadIdx.x == 0) {
+        if (s_out)
+            s_out[tr * ntc + tc] = s;
+        if (st)
+            st[tc * ntr + tr] = s;
+    }
+    if (qt) {
+        __syncthreads();
+        // thread -> column c of the tile, 64 rows starting at 64h
+        const int c = threadIdx.x & 127, h = threadIdx.x >> 7;
+        uint8_t* out = qt + (c0 + c) * R + r0 + 64 * h;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            u32x4 w;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const int r = 64 * h + 16 * k + 4 * d;
+                w[d] = (uint32_t)codes[r][c] | ((uint32_t)codes[r + 1][c] << 8) |
+                       ((uint32_t)codes[r + 2][c] << 16) | ((uint32_t)codes[r + 3][c] << 24);
+            }
+            st16_stream(out + 16 * k, w);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_block_1x128(const void* x, int in_bf16, int64_t R, int64_t C, uint8_t* q, float* s,
+                              hipStream_t stream)
+{
+    const int64_t n = R * C;
+    const int E = in_bf16 ? 8 : 4;
+    const int64_t per_wg = (int64_t)kWG * E * kLoads;
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(n, per_wg), kMaxGrid));
+    if (in_bf16)
+        k_block_1x128<uint16_t><<<grid, kWG, 0, stream>>>((const uint16_t*)x, n, q, s);
+    else
+        k_block_1x128<float><<<grid, kWG, 0, stream>>>((const float*)x, n, q, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_block_1x128_colwise(const void* x, int in_bf16, int64_t R, int64_t C, uint8_t* qt, float* st,
+                                      hipStream_t stream)
+{
+    const int tc = in_bf16 ? 256 : 128;
+    const unsigned grid = (unsigned)(cdiv(C, tc) * (R / 128));
+    if (in_bf16)
+        k_block_1x128_col<uint16_t><<<grid, kWG, 128 * 256 * 2, stream>>>((const uint16_t*)x, R, C, qt, st);
+    else
+        k_block_1x128_col<float><<<grid, kWG, 128 * 128 * 4, stream>>>((const float*)x, R, C, qt, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_block_128x128(const void* x, int in_bf16, int64_t R, int64_t C, uint8_t* q, float* s,
+                                uint8_t* qt, float* st, hipStream_t stream)
+{
+    const unsigned grid = (unsigned)((C / 128) * (R / 128));
+    if (in_bf16)
+        k_block_128x128<uint16_t><<<grid, kWG, 0, stream>>>((const uint16_t*)x, R, C, q, s, qt, st);
+    else
+        k_block_128x128<float><<<grid, kWG, 0, stream>>>((const float*)x, R, C, q, s, qt, st);
+    return hipGetLastError();
+}
+
+}  // namespace fq

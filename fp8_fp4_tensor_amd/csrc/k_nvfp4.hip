@@ -1,0 +1,295 @@
+// k_nvfp4.hip -- NVFP4: E2M1 elements packed two per byte, 1x16 or 16x16
+// blocks with an E4M3 block scale, plus one fp32 tensor-level scale.
+//
+// Sources: [MP] "混合精度训练：fp16 到 fp8" (garden.houmin.site), section
+// "FP8 recipe" item 6 (1x16 blocks, E4M3 scales, one extra fp32 global
+// scale that makes up for E4M3's narrow range) and section "NVFP4" (the
+// float4_e2m1fn_x2 layout: two values per byte, 16 values); [LP] "从 BF16 到
+// FP8/FP4" section 2.4 (E2M1 elements, 16-element blocks with an E4M3 scale
+// and an FP32 tensor scale; 16x16 blocks for weights, 1x16 for activations
+// and gradients; round to nearest even).
+//
+// The two scale levels follow the per-tensor rule applied to the block
+// scales themselves: with A the tensor amax, the block decode scales a_B/6
+// form a tensor whose amax is A/6; it is quantized to E4M3 with current
+// scaling, alpha_s = 448/fp32(A/6), S = fp32(A/6)/448 (S is stored):
+//   c_B = Q_E4M3(fp32(fp32(a_B/6) * alpha_s)),  d_B = fp32(dec(c_B) * S),
+//   r_B = 1/d_B (0 if d_B = 0),  q = Q_E2M1(fp32(x * r_B)).
+// Two divisions per block (a_B/6 and 1/d_B), none per element.
+//
+// The amax pass (k_amax_partial) runs first; each workgroup of the block
+// pass re-reduces its partials to get A.
+//   k_nvfp4_1x16   flat: a 1x16 block is two lanes of bf16 (four of fp32),
+//                  one DPP step; each lane writes one packed dword.
+//   k_nvfp4_16x16  each lane owns E columns of a 16-row strip (16 loads), so
+//                  a 16x16 block is again two lanes; one DPP step.
+//   k_nvfp4_col    colwise copy: a 32-row slab in LDS, one thread per column;
+//                  1x16 -> blocks of 16 rows of one column; 16x16 -> the same
+//                  blocks as rowwise (max also across 16 neighbouring lanes),
+//                  so the colwise nibbles are the rowwise ones transposed.
+#include <algorithm>
+
+#include "codec.hpp"
+#include "launch.hpp"
+
+namespace fq {
+namespace {
+
+constexpr int kLoads = 4;
+constexpr int kMaxGrid = 4096;
+
+// Tensor-level scale from the amax source (uniform control flow).
+__device__ __forceinline__ void nvfp4_tensor(const ScaleSrc& src, float* lds, float& alpha_s, float& S, float& A)
+{
+    if (src.amax_in) {
+        A = *src.amax_in;
+    } else {
+        float m = 0.0f;
+        for (int i = threadIdx.x; i < src.n_partials; i += kWG)
+            m = fmaxf(m, src.partials[i]);
+        A = max_workgroup(m, lds);
+    }
+    tensor_scales(A / 6.0f, 448.0f, alpha_s, S);
+}
+
+// Block scale code and element multiplier from a block amax.
+__device__ __forceinline__ void nvfp4_block(float a, float alpha_s, float S, uint32_t& code, float& r)
+{
+    const float b = a / 6.0f;
+    code = enc_e4m3_one(clampf(b * alpha_s, 448.0f));
+    const float d = dec_e4m3(code) * S;
+    r = (d == 0.0f) ? 0.0f : fminf(1.0f / d, kFLT_MAX);
+}
+
+// E values times r -> E/2 packed bytes (E = 8: a dword; E = 4: 16 bits).
+template <int E>
+struct Fp4Store;
+template <>
+struct Fp4Store<8> {
+    __device__ static __forceinline__ void store(uint8_t* p, const float* f, float r)
+    {
+        st4_stream(p, enc8_e2m1(f, r));
+    }
+};
+template <>
+struct Fp4Store<4> {
+    __device__ static __forceinline__ void store(uint8_t* p, const float* f, float r)
+    {
+        uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, clampf(f[0] * r, 6.0f), clampf(f[1] * r, 6.0f),
+                                                              1.0f, 0);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, clampf(f[2] * r, 6.0f), clampf(f[3] * r, 6.0f), 1.0f, 1);
+        *reinterpret_cast<uint16_t*>(p) = (uint16_t)w;
+    }
+};
+
+template <typename T>
+__global__ __launch_bounds__(kWG) void k_nvfp4_1x16(const T* __restrict__ x, int64_t n, ScaleSrc src,
+                                                    uint8_t* __restrict__ p, uint8_t* __restrict__ codes,
+                                                    float* S_out, float* amax_out)
+{
+    __shared__ float lds[4];
+    constexpr int E = In<T>::kE, U = 64 * E, LPB = 16 / E;
+    float alpha_s, S, A;
+    nvfp4_tensor(src, lds, alpha_s, S, A);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (S_out)
+            *S_out = S;
+        if (amax_out)
+            *amax_out = A;
+    }
+    const int lane = threadIdx.x & 63;
+    const int64_t nunits = cdiv(n, U);
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    for (int64_t u0 = wave * kLoads; u0 < nunits; u0 += nwaves * kLoads) {
+        u32x4 v[kLoads];
+#pragma unroll
+        for (int j = 0; j < kLoads; ++j) {
+            const int64_t e = (u0 + j) * U + lane * E;
+            v[j] = (u0 + j < nunits && e < n) ? ld16_stream(x + e) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int j = 0; j < kLoads; ++j) {
+            if (u0 + j >= nunits)
+                break;
+            const int64_t e = (u0 + j) * U + lane * E;
+            float f[E];
+            In<T>::unpack(v[j], f);
+            const float a = max_lanes<LPB>(absmax<E>(f));
+            uint32_t code;
+            float r;
+            nvfp4_block(a, alpha_s, S, code, r);
+            if (e < n) {
+                Fp4Store<E>::store(p + e / 2, f, r);
+                if ((lane & (LPB - 1)) == 0)
+                    codes[e / 16] = (uint8_t)code;
+            }
+        }
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kWG) void k_nvfp4_16x16(const T* __restrict__ x, int64_t R, int64_t C, ScaleSrc src,
+                                                     uint8_t* __restrict__ p, uint8_t* __restrict__ codes,
+                                                     float* S_out, float* amax_out)
+{
+    __shared__ float lds[4];
+    constexpr int E = In<T>::kE, LPB = 16 / E, WC = kWG * E;  // columns per workgroup
+    float alpha_s, S, A;
+    nvfp4_tensor(src, lds, alpha_s, S, A);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (S_out)
+            *S_out = S;
+        if (amax_out)
+            *amax_out = A;
+    }
+    const int64_t nwc = cdiv(C, WC);
+    const int64_t r0 = (int64_t)(blockIdx.x / nwc) * 16;
+    const int64_t c = (int64_t)(blockIdx.x % nwc) * WC + (int64_t)threadIdx.x * E;
+    const bool in = c < C;
+    u32x4 v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        v[i] = in ? ld16_stream(x + (r0 + i) * C + c) : u32x4{0u, 0u, 0u, 0u};
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        float f[E];
+        In<T>::unpack(v[i], f);
+        m = fmaxf(m, absmax<E>(f));
+    }
+    const float a = max_lanes<LPB>(m);
+    uint32_t code;
+    float r;
+    nvfp4_block(a, alpha_s, S, code, r);
+    if (!in)
+        return;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        float f[E];
+        In<T>::unpack(v[i], f);
+        Fp4Store<E>::store(p + (r0 + i) * (C / 2) + c / 2, f, r);
+    }
+    if ((threadIdx.x & (LPB - 1)) == 0)
+        codes[(r0 / 16) * (C / 16) + c / 16] = (uint8_t)code;
+}
+
+// Colwise copy. BR = 1: 1x16 blocks of X^T (16 rows of a column);
+// BR = 16: 16x16 blocks. Slab of 32 rows x 256 columns in LDS.
+template <typename T, int BR>
+__global__ __launch_bounds__(kWG) void k_nvfp4_col(const T* __restrict__ x, int64_t R, int64_t C, ScaleSrc src,
+                                                   uint8_t* __restrict__ pt, uint8_t* __restrict__ ct,
+                                                   float* S_out, float* amax_out)
+{
+    __shared__ float lds[4];
+    constexpr int TC = 256, E = In<T>::kE, LPR = TC / E, RPR = kWG / LPR;
+    __shared__ __align__(16) T tile[32][TC];
+    float alpha_s, S, A;
+    nvfp4_tensor(src, lds, alpha_s, S, A);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (S_out)
+            *S_out = S;
+        if (amax_out)
+            *amax_out = A;
+    }
+    const int64_t ntc = cdiv(C, TC);
+    const int64_t r0 = (int64_t)(blockIdx.x / ntc) * 32, c0 = (int64_t)(blockIdx.x % ntc) * TC;
+    const int cc = (threadIdx.x % LPR) * E;
+    for (int rr = threadIdx.x / LPR; rr < 32; rr += RPR) {
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if (c0 + cc < C && r0 + rr < R)
+            v = ld16_stream(x + (r0 + rr) * C + c0 + cc);
+        *reinterpret_cast<u32x4*>(&tile[rr][cc]) = v;
+    }
+    __syncthreads();
+    const int c = threadIdx.x;
+    const bool in = c0 + c < C;
+    const int nb = (r0 + 32 <= R) ? 2 : 1;  // R % 16 == 0
+    uint32_t w[4];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        float f[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            f[k] = In<T>::load1(&tile[0][0], (int64_t)(16 * b + k) * TC + c);
+        float a = absmax<16>(f);
+        if constexpr (BR == 16)
+            a = max_lanes<16>(a);
+        uint32_t code;
+        float r;
+        nvfp4_block(a, alpha_s, S, code, r);
+        w[2 * b] = enc8_e2m1(f, r);
+        w[2 * b + 1] = enc8_e2m1(f + 8, r);
+        if (in && b < nb) {
+            const int64_t rb = (r0 + 16 * b) / 16;
+            if constexpr (BR == 1)
+                ct[(c0 + c) * (R / 16) + rb] = (uint8_t)code;
+            else if ((c & 15) == 0)
+                ct[((c0 + c) / 16) * (R / 16) + rb] = (uint8_t)code;
+        }
+    }
+    if (!in)
+        return;
+    // row c of the colwise plane is only 8-byte aligned (R/2 is a multiple of 8)
+    uint8_t* out = pt + (c0 + c) * (R / 2) + r0 / 2;
+    u32x2 v2;
+    v2[0] = w[0];
+    v2[1] = w[1];
+    st8_stream(out, v2);
+    if (nb == 2) {
+        v2[0] = w[2];
+        v2[1] = w[3];
+        st8_stream(out + 8, v2);
+    }
+}
+
+template <typename T>
+void launch_t(const void* xv, int64_t R, int64_t C, int br, ScaleSrc src, uint8_t* p, uint8_t* codes, uint8_t* pt,
+              uint8_t* codest, float* S_out, float* amax_out, hipStream_t stream)
+{
+    const T* x = (const T*)xv;
+    constexpr int E = In<T>::kE;
+    bool wrote_scalars = false;
+    if (p) {
+        if (br == 1) {
+            const int64_t n = R * C;
+            const int64_t per_wg = (int64_t)kWG * E * kLoads;
+            const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(n, per_wg), kMaxGrid));
+            k_nvfp4_1x16<T><<<grid, kWG, 0, stream>>>(x, n, src, p, codes, S_out, amax_out);
+            wrote_scalars = true;
+        } else if (R > 0 && C > 0) {
+            const int64_t grid = (R / 16) * cdiv(C, (int64_t)kWG * E);
+            k_nvfp4_16x16<T><<<(unsigned)grid, kWG, 0, stream>>>(x, R, C, src, p, codes, S_out, amax_out);
+            wrote_scalars = true;
+        }
+    }
+    if (pt && R > 0 && C > 0) {
+        const int64_t grid = cdiv(R, 32) * cdiv(C, 256);
+        float* s2 = wrote_scalars ? nullptr : S_out;
+        float* a2 = wrote_scalars ? nullptr : amax_out;
+        if (br == 1)
+            k_nvfp4_col<T, 1><<<(unsigned)grid, kWG, 0, stream>>>(x, R, C, src, pt, codest, s2, a2);
+        else
+            k_nvfp4_col<T, 16><<<(unsigned)grid, kWG, 0, stream>>>(x, R, C, src, pt, codest, s2, a2);
+        wrote_scalars = true;
+    }
+    if (!wrote_scalars) {
+        // empty tensor: only the tensor scale and amax
+        k_nvfp4_1x16<T><<<1, kWG, 0, stream>>>(x, 0, src, p, codes, S_out, amax_out);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_nvfp4(const void* x, int in_bf16, int64_t R, int64_t C, int br, ScaleSrc src, uint8_t* p,
+                        uint8_t* codes, uint8_t* pt, uint8_t* codest, float* S_out, float* amax_out,
+                        hipStream_t stream)
+{
+    if (in_bf16)
+        launch_t<uint16_t>(x, R, C, br, src, p, codes, pt, codest, S_out, amax_out, stream);
+    else
+        launch_t<float>(x, R, C, br, src, p, codes, pt, codest, S_out, amax_out, stream);
+    return hipGetLastError();
+}
+
+}  // namespace fq

@@ -1,0 +1,321 @@
+// k_tensor.hip -- per-tensor scaling kernels: the grid-wide amax, the
+// scale+cast pass, the fused delayed-scaling cast and its finish.
+//
+// Sources: [MP] "混合精度训练：fp16 到 fp8" (garden.houmin.site), section
+// "FP8 recipe" items 2 (delayed) and 3 (current); [CS] "FP8 Current
+// Scaling：量化、缩放与精度边界" (notes.kuangjux.top), sections "Current
+// Scaling" (a, alpha, q, s) and "成本与多 GPU 使用" (two reads of the tensor).
+//
+// Layout of the work: a flat tensor of n elements is cut into wave units of
+// 64 lanes x 16 bytes (512 bf16 or 256 fp32 elements, 1 KiB). Each wave takes
+// kLoads consecutive units per step, so every lane has kLoads 16-byte loads
+// in flight and each load instruction of the wave reads 1 KiB contiguously.
+// Workgroups stride over the units; fewer than one unit of ragged tail is
+// handled one element per thread.
+//
+// Current scaling is two passes: k_amax_partial writes one exact max per
+// workgroup (lane max -> DPP within 16 lanes -> shuffles across the wave ->
+// LDS across 4 waves), and every workgroup of the cast pass re-reduces those
+// few KiB of partials itself (they stay in L2), so no atomics and no third
+// kernel are needed and the result does not depend on scheduling order.
+#include <algorithm>
+
+#include "codec.hpp"
+#include "launch.hpp"
+
+namespace fq {
+namespace {
+
+constexpr int kLoads = 4;
+constexpr int kCastMaxGrid = 2048;
+
+template <typename T>
+__global__ __launch_bounds__(kWG) void k_amax_partial(const T* __restrict__ x, int64_t n,
+                                                      float* __restrict__ partials)
+{
+    __shared__ float lds[4];
+    constexpr int E = In<T>::kE, U = 64 * E;
+    const int lane = threadIdx.x & 63;
+    const int64_t nunits = n / U;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    float m = 0.0f;
+    for (int64_t u0 = wave * kLoads; u0 < nunits; u0 += nwaves * kLoads) {
+        u32x4 v[kLoads];
+#pragma unroll
+        for (int j = 0; j < kLoads; ++j)
+            v[j] = (u0 + j < nunits) ? ld16(x + (u0 + j) * U + lane * E) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < kLoads; ++j) {
+            float f[E];
+            In<T>::unpack(v[j], f);
+            m = fmaxf(m, absmax<E>(f));
+        }
+    }
+    for (int64_t i = nunits * U + (int64_t)blockIdx.x * kWG + threadIdx.x; i < n; i += (int64_t)gridDim.x * kWG)
+        m = fmaxf(m, fabsf(In<T>::load1(x, i)));
+    m = max_workgroup(m, lds);
+    if (threadIdx.x == 0)
+        partials[blockIdx.x] = m;
+}
+
+// alpha and s for this launch, from the scale source. Uniform control flow.
+template <int FMT>
+__device__ __forceinline__ void resolve_scale(const ScaleSrc& src, float* lds, float& alpha, float& s, float& a)
+{
+    if (src.alpha_in) {
+        alpha = *src.alpha_in;
+        s = *src.s_in;
+        a = 0.0f;
+        return;
+    }
+    if (src.amax_in) {
+        a = *src.amax_in;
+    } else {
+        float m = 0.0f;
+        for (int i = threadIdx.x; i < src.n_partials; i += kWG)
+            m = fmaxf(m, src.partials[i]);
+        a = max_workgroup(m, lds);
+    }
+    tensor_scales(a, Fmt<FMT>::kMax, alpha, s);
+}
+
+// q = Q(fp32(alpha * x)) over a flat tensor; optionally one amax partial per
+// workgroup (delayed scaling casts and records the amax in the same read).
+template <typename T, int FMT>
+__global__ __launch_bounds__(kWG) void k_cast_tensor(const T* __restrict__ x, int64_t n, ScaleSrc src,
+                                                     uint8_t* __restrict__ q, float* s_out, float* amax_out,
+                                                     float* partials_out)
+{
+    __shared__ float lds[4];
+    constexpr int E = In<T>::kE, U = 64 * E;
+    float alpha, s, a;
+    resolve_scale<FMT>(src, lds, alpha, s, a);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (s_out)
+            *s_out = s;
+        if (amax_out)
+            *amax_out = a;
+    }
+    const bool want_amax = partials_out != nullptr;
+    const int lane = threadIdx.x & 63;
+    const int64_t nunits = n / U;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    float m = 0.0f;
+    for (int64_t u0 = wave * kLoads; u0 < nunits; u0 += nwaves * kLoads) {
+        u32x4 v[kLoads];
+#pragma unroll
+        for (int j = 0; j < kLoads; ++j)
+            v[j] = (u0 + j < nunits) ? ld16_stream(x + (u0 + j) * U + lane * E) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < kLoads; ++j) {
+            if (u0 + j < nunits) {
+                float f[E];
+                In<T>::unpack(v[j], f);
+                if (want_amax)
+                    m = fmaxf(m, absmax<E>(f));
+                Enc8<FMT, E>::store(q + (u0 + j) * U + lane * E, f, alpha);
+            }
+        }
+    }
+    for (int64_t i = nunits * U + (int64_t)blockIdx.x * kWG + threadIdx.x; i < n; i += (int64_t)gridDim.x * kWG) {
+        const float v = In<T>::load1(x, i);
+        m = fmaxf(m, fabsf(v));
+        q[i] = enc1<FMT>(v, alpha);
+    }
+    if (want_amax) {
+        m = max_workgroup(m, lds);
+        if (threadIdx.x == 0)
+            partials_out[blockIdx.x] = m;
+    }
+}
+
+// Per-tensor cast through 64x64 tiles, for the transposed (colwise) copy:
+// rowwise bytes q[r*C + c] and transposed bytes qt[c*R + r] from one read.
+// Byte-granular and bounds-checked: any shape.
+template <typename T, int FMT>
+__global__ __launch_bounds__(kWG) void k_cast_tensor_2d(const T* __restrict__ x, int64_t R, int64_t C,
+                                                        ScaleSrc src, uint8_t* __restrict__ q,
+                                                        uint8_t* __restrict__ qt, float* s_out, float* amax_out,
+                                                        float* partials_out)
+{
+    __shared__ float lds[4];
+    __shared__ uint8_t tile[64][68];
+    float alpha, s, a;
+    resolve_scale<FMT>(src, lds, alpha, s, a);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (s_out)
+            *s_out = s;
+        if (amax_out)
+            *amax_out = a;
+    }
+    const int64_t tcols = (C + 63) / 64, ntiles = ((R + 63) / 64) * tcols;
+    float m = 0.0f;
+    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const int64_t r0 = (t / tcols) * 64, c0 = (t % tcols) * 64;
+        __syncthreads();
+        for (int i = threadIdx.x; i < 64 * 64; i += kWG) {
+            const int r = i >> 6, c = i & 63;
+            const int64_t gr = r0 + r, gc = c0 + c;
+            uint8_t code = 0;
+            if (gr < R && gc < C) {
+                const float v = In<T>::load1(x, gr * C + gc);
+                m = fmaxf(m, fabsf(v));
+                code = enc1<FMT>(v, alpha);
+                if (q)
+                    q[gr * C + gc] = code;
+            }
+            tile[r][c] = code;
+        }
+        __syncthreads();
+        if (qt) {
+            for (int i = threadIdx.x; i < 64 * 64; i += kWG) {
+                const int c = i >> 6, r = i & 63;
+                const int64_t gr = r0 + r, gc = c0 + c;
+                if (gr < R && gc < C)
+                    qt[gc * R + gr] = tile[r][c];
+            }
+        }
+    }
+    if (partials_out) {
+        m = max_workgroup(m, lds);
+        if (threadIdx.x == 0)
+            partials_out[blockIdx.x] = m;
+    }
+}
+
+__global__ __launch_bounds__(kWG) void k_amax_finish(const float* __restrict__ partials, int n, float* out)
+{
+    __shared__ float lds[4];
+    float m = 0.0f;
+    for (int i = threadIdx.x; i < n; i += kWG)
+        m = fmaxf(m, partials[i]);
+    m = max_workgroup(m, lds);
+    if (threadIdx.x == 0)
+        *out = m;
+}
+
+// Delayed scaling, second half of a step ([MP] recipe 2: record this step's
+// amax in the window; the next step's scale comes from the window's max).
+__global__ __launch_bounds__(kWG) void k_delayed_finish(const float* __restrict__ partials, int n, float* hist,
+                                                        int H, int slot, float* alpha, float* s, float fmax_v,
+                                                        float* amax_out)
+{
+    __shared__ float lds[4];
+    float m = 0.0f;
+    for (int i = threadIdx.x; i < n; i += kWG)
+        m = fmaxf(m, partials[i]);
+    const float at = max_workgroup(m, lds);
+    float w = at;
+    for (int i = threadIdx.x; i < H; i += kWG)
+        if (i != slot)
+            w = fmaxf(w, hist[i]);
+    w = max_workgroup(w, lds);
+    if (threadIdx.x == 0) {
+        hist[slot] = at;
+        if (amax_out)
+            *amax_out = at;
+        if (w > 0.0f) {
+            float al, ss;
+            tensor_scales(w, fmax_v, al, ss);
+            *alpha = al;
+            *s = ss;
+        }
+    }
+}
+
+template <typename T>
+int64_t elems_per_wg_step()
+{
+    return (int64_t)kWG * (16 / (int)sizeof(T)) * kLoads;
+}
+
+}  // namespace
+
+int amax_grid(int64_t n, int elem_bytes)
+{
+    const int64_t per = (int64_t)kWG * (16 / elem_bytes) * kLoads;
+    return (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(n, per), kMaxPartials));
+}
+
+hipError_t launch_amax_partial(const void* x, int in_bf16, int64_t n, float* partials, int grid, hipStream_t stream)
+{
+    if (in_bf16)
+        k_amax_partial<uint16_t><<<grid, kWG, 0, stream>>>((const uint16_t*)x, n, partials);
+    else
+        k_amax_partial<float><<<grid, kWG, 0, stream>>>((const float*)x, n, partials);
+    return hipGetLastError();
+}
+
+hipError_t launch_amax_finish(const float* partials, int n, float* out, hipStream_t stream)
+{
+    k_amax_finish<<<1, kWG, 0, stream>>>(partials, n, out);
+    return hipGetLastError();
+}
+
+template <typename T, int FMT>
+static void cast_tensor_t(const void* x, int64_t n, ScaleSrc src, uint8_t* q, float* s_out, float* amax_out,
+                          float* partials_out, int grid, hipStream_t stream)
+{
+    k_cast_tensor<T, FMT><<<grid, kWG, 0, stream>>>((const T*)x, n, src, q, s_out, amax_out, partials_out);
+}
+
+hipError_t launch_cast_tensor(const void* x, int in_bf16, int fmt, int64_t n, ScaleSrc src, uint8_t* q,
+                              float* s_out, float* amax_out, float* partials_out, int grid, hipStream_t stream)
+{
+    if (grid <= 0) {
+        const int64_t per = in_bf16 ? elems_per_wg_step<uint16_t>() : elems_per_wg_step<float>();
+        grid = (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(n, per), kCastMaxGrid));
+    }
+    if (in_bf16) {
+        if (fmt == kE4M3)
+            cast_tensor_t<uint16_t, kE4M3>(x, n, src, q, s_out, amax_out, partials_out, grid, stream);
+        else
+            cast_tensor_t<uint16_t, kE5M2>(x, n, src, q, s_out, amax_out, partials_out, grid, stream);
+    } else {
+        if (fmt == kE4M3)
+            cast_tensor_t<float, kE4M3>(x, n, src, q, s_out, amax_out, partials_out, grid, stream);
+        else
+            cast_tensor_t<float, kE5M2>(x, n, src, q, s_out, amax_out, partials_out, grid, stream);
+    }
+    return hipGetLastError();
+}
+
+template <typename T, int FMT>
+static void cast_2d_t(const void* x, int64_t R, int64_t C, ScaleSrc src, uint8_t* q, uint8_t* qt, float* s_out,
+                      float* amax_out, float* partials_out, int grid, hipStream_t stream)
+{
+    k_cast_tensor_2d<T, FMT><<<grid, kWG, 0, stream>>>((const T*)x, R, C, src, q, qt, s_out, amax_out,
+                                                       partials_out);
+}
+
+hipError_t launch_cast_tensor_2d(const void* x, int in_bf16, int fmt, int64_t R, int64_t C, ScaleSrc src,
+                                 uint8_t* q, uint8_t* qt, float* s_out, float* amax_out, float* partials_out,
+                                 int grid, hipStream_t stream)
+{
+    const int64_t ntiles = cdiv(R, 64) * cdiv(C, 64);
+    if (grid <= 0)
+        grid = (int)std::max<int64_t>(1, std::min<int64_t>(ntiles, kCastMaxGrid));
+    if (in_bf16) {
+        if (fmt == kE4M3)
+            cast_2d_t<uint16_t, kE4M3>(x, R, C, src, q, qt, s_out, amax_out, partials_out, grid, stream);
+        else
+            cast_2d_t<uint16_t, kE5M2>(x, R, C, src, q, qt, s_out, amax_out, partials_out, grid, stream);
+    } else {
+        if (fmt == kE4M3)
+            cast_2d_t<float, kE4M3>(x, R, C, src, q, qt, s_out, amax_out, partials_out, grid, stream);
+        else
+            cast_2d_t<float, kE5M2>(x, R, C, src, q, qt, s_out, amax_out, partials_out, grid, stream);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_delayed_finish(const float* partials, int n_partials, float* hist, int H, int slot, float* alpha,
+                                 float* s, float fmax_v, float* amax_out, hipStream_t stream)
+{
+    k_delayed_finish<<<1, kWG, 0, stream>>>(partials, n_partials, hist, H, slot, alpha, s, fmax_v, amax_out);
+    return hipGetLastError();
+}
+
+}  // namespace fq

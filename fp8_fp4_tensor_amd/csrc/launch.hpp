@@ -1,0 +1,80 @@
+// launch.hpp -- host-side launchers of the HIP kernels, called by api.cpp
+// after it has validated every argument. Each launcher enqueues on `stream`
+// and returns hipGetLastError() of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fq {
+
+// Workspace layout shared by the per-tensor and NVFP4 paths: one fp32 amax
+// partial per workgroup of the amax pass.
+constexpr int kMaxPartials = 1024;
+constexpr size_t kPartialsBytes = kMaxPartials * sizeof(float);
+
+// Where a per-tensor cast takes its amax from.
+struct ScaleSrc {
+    const float* partials = nullptr;  // reduce partials[0..n_partials) (current scaling)
+    int n_partials = 0;
+    const float* amax_in = nullptr;   // or a given amax (quantize_with_amax)
+    const float* alpha_in = nullptr;  // or a given alpha and s (delayed scaling)
+    const float* s_in = nullptr;
+};
+
+// Number of workgroups of the amax pass for n elements of the given size.
+int amax_grid(int64_t n, int elem_bytes);
+
+// partials[g] = max|x| over workgroup g's share; grid from amax_grid().
+hipError_t launch_amax_partial(const void* x, int in_bf16, int64_t n, float* partials, int grid,
+                               hipStream_t stream);
+// out[0] = max(partials[0..n)).
+hipError_t launch_amax_finish(const float* partials, int n, float* out, hipStream_t stream);
+
+// Per-tensor cast of a flat tensor (rowwise bytes only). Optional
+// partials_out receives one amax partial per workgroup (delayed scaling);
+// pass grid = amax_grid(n) then. grid <= 0 picks a default.
+hipError_t launch_cast_tensor(const void* x, int in_bf16, int fmt, int64_t n, ScaleSrc src, uint8_t* q,
+                              float* s_out, float* amax_out, float* partials_out, int grid, hipStream_t stream);
+
+// Per-tensor cast of a [R, C] tensor through 64x64 tiles, writing rowwise
+// bytes q (may be null) and transposed bytes qt (may be null). Optional
+// partials_out receives one amax per workgroup; grid <= 0 picks a default
+// (pass amax_grid-sized grids, <= kMaxPartials, when partials_out is set).
+hipError_t launch_cast_tensor_2d(const void* x, int in_bf16, int fmt, int64_t R, int64_t C, ScaleSrc src,
+                                 uint8_t* q, uint8_t* qt, float* s_out, float* amax_out, float* partials_out,
+                                 int grid, hipStream_t stream);
+
+// Delayed scaling, after the cast wrote partials: a_t = max(partials),
+// hist[slot] = a_t, m = max(hist), new alpha/s if m > 0.
+hipError_t launch_delayed_finish(const float* partials, int n_partials, float* hist, int H, int slot,
+                                 float* alpha, float* s, float fmax_v, float* amax_out, hipStream_t stream);
+
+// Blockwise fp32 scales, E4M3. 1x128: flat blocks; 128x128: tiles.
+hipError_t launch_block_1x128(const void* x, int in_bf16, int64_t R, int64_t C, uint8_t* q, float* s,
+                              hipStream_t stream);
+hipError_t launch_block_1x128_colwise(const void* x, int in_bf16, int64_t R, int64_t C, uint8_t* qt, float* st,
+                                      hipStream_t stream);
+hipError_t launch_block_128x128(const void* x, int in_bf16, int64_t R, int64_t C, uint8_t* q, float* s,
+                                uint8_t* qt, float* st, hipStream_t stream);
+
+// MXFP8 E4M3: rowwise 1x32 and/or colwise 32x1 (transposed).
+hipError_t launch_mx(const void* x, int in_bf16, int64_t R, int64_t C, uint8_t* q, uint8_t* e, uint8_t* qt,
+                     uint8_t* et, hipStream_t stream);
+
+// NVFP4 block pass (after the amax pass): 1x16 or 16x16 blocks.
+hipError_t launch_nvfp4(const void* x, int in_bf16, int64_t R, int64_t C, int br, ScaleSrc src, uint8_t* p,
+                        uint8_t* codes, uint8_t* pt, uint8_t* codest, float* S_out, float* amax_out,
+                        hipStream_t stream);
+
+// Dequantization to fp32.
+hipError_t launch_dequant_tensor(const uint8_t* q, int fmt, int64_t n, const float* s, float* y,
+                                 hipStream_t stream);
+hipError_t launch_dequant_block(const uint8_t* q, const float* s, int64_t R, int64_t C, int br, int bc, float* y,
+                                hipStream_t stream);
+hipError_t launch_dequant_mx(const uint8_t* q, const uint8_t* e, int64_t R, int64_t C, float* y,
+                             hipStream_t stream);
+hipError_t launch_dequant_nvfp4(const uint8_t* p, const uint8_t* codes, const float* S, int64_t R, int64_t C,
+                                int br, int bc, float* y, hipStream_t stream);
+
+}  // namespace fq

@@ -86,6 +86,8 @@ def _load():
         "orc_quantize_mx": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, _u32, _p, _p, _p, _p]),
         "orc_quantize_nvfp4": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, ctypes.c_int, ctypes.c_int, _u32,
                                               _p, _p, _p, _p, _fp, _fp]),
+        "orc_quantize_nvfp4_with_amax": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, ctypes.c_int, ctypes.c_int,
+                                                        _u32, _f32, _p, _p, _p, _p, _fp, _fp]),
         "orc_dequant_tensor": (None, [_p, _i64, ctypes.c_int, _f32, _p]),
         "orc_dequant_block": (None, [_p, _p, _i64, _i64, ctypes.c_int, ctypes.c_int, _p]),
         "orc_dequant_mx": (None, [_p, _p, _i64, _i64, _p]),
@@ -273,8 +275,9 @@ def quantize_mx(x, outputs=ROWWISE | COLWISE, shape=None):
                 e_col=None if e_col is None else e_col.reshape(C, R // 32))
 
 
-def quantize_nvfp4(x, block, outputs=ROWWISE, shape=None):
-    """NVFP4: packed E2M1 pairs, E4M3 block codes and the fp32 tensor scale S."""
+def quantize_nvfp4(x, block, outputs=ROWWISE, shape=None, amax=None):
+    """NVFP4: packed E2M1 pairs, E4M3 block codes and the fp32 tensor scale S.
+    `amax` gives the tensor amax A (default: this tensor's own)."""
     p, dt, keep = _in(x)
     R, C = _shape2(keep, shape)
     br, bc = block
@@ -285,8 +288,14 @@ def quantize_nvfp4(x, block, outputs=ROWWISE, shape=None):
     if outputs & COLWISE:
         c_col = np.empty(C * (R // 16) if br == 1 else (C // 16) * (R // 16), np.uint8)
     S, A = ctypes.c_float(), ctypes.c_float()
-    _check(_load().orc_quantize_nvfp4(p, dt, R, C, br, bc, outputs, _ptr(p_row), _ptr(c_row), _ptr(p_col),
-                                      _ptr(c_col), ctypes.byref(S), ctypes.byref(A)), "quantize_nvfp4")
+    if amax is None:
+        rc = _load().orc_quantize_nvfp4(p, dt, R, C, br, bc, outputs, _ptr(p_row), _ptr(c_row), _ptr(p_col),
+                                        _ptr(c_col), ctypes.byref(S), ctypes.byref(A))
+    else:
+        rc = _load().orc_quantize_nvfp4_with_amax(p, dt, R, C, br, bc, outputs, float(np.float32(amax)),
+                                                  _ptr(p_row), _ptr(c_row), _ptr(p_col), _ptr(c_col),
+                                                  ctypes.byref(S), ctypes.byref(A))
+    _check(rc, "quantize_nvfp4")
     out = dict(p_row=None if p_row is None else p_row.reshape(R, C // 2),
                c_row=None if c_row is None else c_row.reshape(R // br, C // bc),
                p_col=None if p_col is None else p_col.reshape(C, R // 2),

@@ -596,15 +596,16 @@ static void nvfp4_rowwise(const void *x, int dt, int64_t R, int64_t C, int br, i
 
 /*
  * Rowwise: packed data [R, C/2], E4M3 codes [R/br, C/bc], tensor scale S.
+ * A is the tensor amax (given here, e.g. reduced across shards first).
  * Colwise (READING): 1x16 -> the same recipe on X^T, with the same tensor
  * scale (the amax of X^T is the amax of X); 16x16 -> the element codes of
  * the rowwise result transposed and re-packed along the rows of X^T, codes
  * transposed ([MP] closing remarks: FP4 GEMMs need two copies even for 2-D
  * weight tiles).
  */
-int orc_quantize_nvfp4(const void *x, int dt, int64_t R, int64_t C, int br, int bc, unsigned outputs,
-                       uint8_t *p_row, uint8_t *c_row, uint8_t *p_col, uint8_t *c_col,
-                       float *S_out, float *amax_out)
+int orc_quantize_nvfp4_with_amax(const void *x, int dt, int64_t R, int64_t C, int br, int bc, unsigned outputs,
+                                 float A, uint8_t *p_row, uint8_t *c_row, uint8_t *p_col, uint8_t *c_col,
+                                 float *S_out, float *amax_out)
 {
     if (R <= 0 || C <= 0)
         return -3;
@@ -616,7 +617,6 @@ int orc_quantize_nvfp4(const void *x, int dt, int64_t R, int64_t C, int br, int 
         return -3;
     if (check_finite(x, dt, R * C))
         return -1;
-    float A = orc_amax(x, dt, R * C);
     nvfp4_tensor t = nvfp4_tensor_scale(A);
     if (S_out)
         *S_out = t.S;
@@ -649,6 +649,19 @@ int orc_quantize_nvfp4(const void *x, int dt, int64_t R, int64_t C, int br, int 
             free(cd);
     }
     return 0;
+}
+
+/* NVFP4 with A = the amax of this tensor. */
+int orc_quantize_nvfp4(const void *x, int dt, int64_t R, int64_t C, int br, int bc, unsigned outputs,
+                       uint8_t *p_row, uint8_t *c_row, uint8_t *p_col, uint8_t *c_col, float *S_out,
+                       float *amax_out)
+{
+    if (R <= 0 || C <= 0)
+        return -3;
+    if (check_finite(x, dt, R * C))
+        return -1;
+    return orc_quantize_nvfp4_with_amax(x, dt, R, C, br, bc, outputs, orc_amax(x, dt, R * C), p_row, c_row, p_col,
+                                        c_col, S_out, amax_out);
 }
 
 /* ------------------------------------------------------------------ */
