@@ -1,0 +1,293 @@
+"""Benchmark: FP8/FP4 quantization throughput on one MI355X.
+
+One step quantizes every large workload once, each with its own recipe:
+per-tensor current scaling (E4M3 activation, E5M2 gradient, 8192x4096 bf16),
+delayed scaling with a 1024-entry window (same two tensors), blockwise 1x128
+(16384x7168) and 128x128 (7168x18432), MXFP8 rowwise + colwise (8192x8192)
+and NVFP4 1x16 (8192x14336) and 16x16 (14336x4096). Inputs are seeded,
+synthetic and resident in HBM before timing; the step touches more than the
+256 MB Infinity Cache, so each workload starts cold.
+
+value = algorithmic bytes per step / time per step, in GB/s. Algorithmic
+bytes count one read of the input per pass the method makes (two for current
+scaling and NVFP4, one otherwise) plus every byte written (codes, scales,
+delayed-scaling window and scale).
+
+Prints one JSON line. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "quantize GB/s (bytes read+written) and % of HBM peak, per recipe"
+HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def algorithmic_bytes(w) -> int:
+    R, C = w.shape
+    n = R * C
+    eb = 2 if w.dtype == "bf16" else 4
+    if w.recipe == "current":
+        return 2 * n * eb + n + 4                      # amax read, cast read, codes, s
+    if w.recipe == "delayed":
+        H = w.extra["history_len"]
+        return n * eb + n + 2 * 4 * H + 3 * 4          # one read, codes, window r/w, alpha, s, s_used
+    if w.recipe == "block":
+        br, bc = w.block
+        return n * eb + n + (R // br) * (C // bc) * 4
+    if w.recipe == "mx":
+        return n * eb + 2 * n + 2 * (n // 32)          # rowwise + colwise codes and E8M0 scales
+    if w.recipe == "nvfp4":
+        br, bc = w.block
+        return 2 * n * eb + n // 2 + (R // br) * (C // bc) + 4
+    raise ValueError(w.recipe)
+
+
+def kernel_source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "fp8_fp4_tensor_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# which source files define each workload's kernels (for the traffic counters)
+KERNEL_FILES = {"current": ["k_tensor.hip", "codec.hpp"], "delayed": ["k_tensor.hip", "codec.hpp"],
+                "block": ["k_block.hip", "codec.hpp"], "mx": ["k_mx.hip", "codec.hpp"],
+                "nvfp4": ["k_nvfp4.hip", "k_tensor.hip", "codec.hpp"]}
+KERNEL_NAMES = {"current": "k_cast_tensor", "delayed": "k_cast_tensor", "block1x128": "k_block_1x128",
+                "block128x128": "k_block_128x128", "mx": "k_mx", "nvfp4_1x16": "k_nvfp4_1x16",
+                "nvfp4_16x16": "k_nvfp4_16x16"}
+
+
+def kernel_key(w):
+    if w.recipe == "block":
+        return "block1x128" if w.block == (1, 128) else "block128x128"
+    if w.recipe == "nvfp4":
+        return "nvfp4_1x16" if w.block == (1, 16) else "nvfp4_16x16"
+    return w.recipe
+
+
+def traffic_for(w, per_launch_alg_bytes):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None if there is none or the kernel's sources changed since."""
+    path = os.path.join(PROFILES, f"traffic_{kernel_key(w)}_{w.shape[0]}x{w.shape[1]}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != kernel_source_hash(KERNEL_FILES[w.recipe]):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+COPY_BYTES = 256 << 20
+
+
+def plain_copy(torch, stream, reps):
+    """Bandwidth of a plain device-to-device copy of 256 MiB (read + write)."""
+    a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / reps * 1e-3
+    del a, b
+    return 2 * COPY_BYTES / t / 1e9
+
+
+def cpu_baseline(workloads, row_fraction):
+    """The oracle (single-threaded C) on the first rows of each workload."""
+    import numpy as np
+
+    import oracle as orc
+    from fp8_fp4_tensor_amd import workloads as W
+
+    total_bytes, total_t = 0, 0.0
+    for w in workloads:
+        R, C = w.shape
+        r = max(w.block[0] if w.block else 1, 16, int(R * row_fraction) // 128 * 128)
+        sub = W.Workload(w.name, (r, C), w.dtype, w.recipe, w.fmt, w.block, w.outputs, w.seed, w.dist, w.std,
+                         w.extra)
+        x = sub.make()
+        fmt = {"e4m3": orc.E4M3, "e5m2": orc.E5M2}.get(w.fmt)
+        t0 = time.perf_counter()
+        if w.recipe == "current":
+            orc.quantize_current(x, fmt)
+        elif w.recipe == "delayed":
+            orc.quantize_delayed(x, fmt, orc.DelayedState(w.extra["history_len"]))
+        elif w.recipe == "block":
+            orc.quantize_block(x, w.block)
+        elif w.recipe == "mx":
+            orc.quantize_mx(x, outputs=w.outputs)
+        elif w.recipe == "nvfp4":
+            orc.quantize_nvfp4(x, w.block)
+        total_t += time.perf_counter() - t0
+        total_bytes += algorithmic_bytes(sub)
+        del x
+    return {"value": round(total_bytes / total_t / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"every workload of one step on its first {row_fraction:.0%} of rows "
+                      f"({total_bytes / 1e9:.2f} GB algorithmic, {total_t:.1f} s, one thread)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=float, default=0.25, help="row fraction for the oracle baseline")
+    ap.add_argument("--only", default="", help="comma-separated workload names (profiling runs)")
+    ap.add_argument("--copy-only", action="store_true",
+                    help="time only a plain 256 MiB device copy (counter calibration and reference)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the sharded path is "
+              "design-only, see the library's documentation)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from fp8_fp4_tensor_amd import fq
+    from fp8_fp4_tensor_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+
+    copy_gbs = plain_copy(torch, stream, args.steps if args.copy_only else 10)
+    if args.copy_only:
+        print(json.dumps({"copy_bytes": 2 * COPY_BYTES, "copy_GBps": round(copy_gbs, 1)}), flush=True)
+        return
+
+    recipes = {"current": fq.FQ_PER_TENSOR_CURRENT, "delayed": fq.FQ_PER_TENSOR_DELAYED,
+               "block": fq.FQ_BLOCK_FP32, "mx": fq.FQ_MX, "nvfp4": fq.FQ_NVFP4}
+    fmts = {"e4m3": fq.FQ_E4M3, "e5m2": fq.FQ_E5M2, "e2m1": fq.FQ_E2M1}
+    wls = W.LARGE
+    if args.only:
+        keep = set(args.only.split(","))
+        wls = [w for w in wls if w.name in keep]
+
+    L = fq.lib()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    jobs = []
+    for w in wls:
+        R, C = w.shape
+        x = w.make()
+        xd = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+        d = fq.desc(recipes[w.recipe], fq.FQ_IN_BF16, fmts[w.fmt], R, C, w.block or (0, 0), w.outputs)
+        out = fq.alloc_quantized(d)
+        ws = fq.alloc_workspace(d)
+        st = fq.DelayedState(w.extra["history_len"]) if w.recipe == "delayed" else None
+        # the C arguments, built once: each call below is one ctypes call into libfq.so
+        j = dict(w=w, x=xd, d=d, out=out, ws=ws, st=st, bytes=algorithmic_bytes(w), cq=out.c(),
+                 xp=ctypes.c_void_p(xd.data_ptr()), wsp=ctypes.c_void_p(ws.data_ptr()) if ws is not None else None,
+                 wsn=0 if ws is None else ws.numel(), cst=st.c() if st is not None else None)
+        jobs.append(j)
+        del x
+    print(f"bench: {len(jobs)} workloads resident, {sum(j['x'].numel() * 2 for j in jobs) / 2**30:.2f} GiB input",
+          file=sys.stderr, flush=True)
+
+    def call(j):
+        if j["cst"] is not None:
+            rc = L.fq_quantize_delayed(ctypes.byref(j["d"]), j["xp"], ctypes.byref(j["cst"]), ctypes.byref(j["cq"]),
+                                       j["wsp"], j["wsn"], sp)
+            j["cst"].step += 1
+        else:
+            rc = L.fq_quantize(ctypes.byref(j["d"]), j["xp"], ctypes.byref(j["cq"]), j["wsp"], j["wsn"], sp)
+        if rc != fq.FQ_OK:
+            raise fq.FqError(rc, j["w"].name)
+
+    for _ in range(args.warmup):
+        for j in jobs:
+            call(j)
+    torch.cuda.synchronize()
+
+    # per-recipe breakdown: K instrumented steps, every call bracketed by events
+    # (each call starts with its input cold, as in the timed region below)
+    for j in jobs:
+        j["events"] = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(args.steps)]
+    for k in range(args.steps):
+        for j in jobs:
+            j["events"][k][0].record(stream)
+            call(j)
+            j["events"][k][1].record(stream)
+    torch.cuda.synchronize()
+    per = {}
+    for j in jobs:
+        us = 1e3 * sum(a.elapsed_time(b) for a, b in j["events"]) / args.steps
+        gbs = j["bytes"] / (us * 1e-6) / 1e9
+        per[j["w"].name] = {"us_per_call": round(us, 2), "GB/s": round(gbs, 1),
+                            "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 1), "bytes": j["bytes"],
+                            "kernels": 2 if j["w"].recipe in ("current", "nvfp4", "delayed") else 1}
+    # the dominant kernel: the single-kernel workload with the largest time per call
+    single = [j for j in jobs if per[j["w"].name]["kernels"] == 1]
+    dom = max(single, key=lambda j: per[j["w"].name]["us_per_call"]) if single else None
+
+    # timed region: K steps; events on the stream bracket the dominant kernel's launch in each step
+    dom_events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for k in range(args.steps):
+        for j in jobs:
+            if j is dom:
+                dom_events[k][0].record(stream)
+                call(j)
+                dom_events[k][1].record(stream)
+            else:
+                call(j)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    step_bytes = sum(j["bytes"] for j in jobs)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    roofline = None
+    if dom is not None:
+        us = 1e3 * sum(a.elapsed_time(b) for a, b in dom_events) / args.steps
+        gbs = dom["bytes"] / (us * 1e-6) / 1e9
+        roofline = {"kernel": KERNEL_NAMES[kernel_key(dom["w"])], "workload": dom["w"].name, "bound": "hbm",
+                    "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(gbs / HBM_PEAK_GBS, 4),
+                    "traffic": traffic_for(dom["w"], dom["bytes"]),
+                    "alg_bytes_per_launch": dom["bytes"], "us_per_launch": round(us, 2)}
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+        "config": {"workload": "one step = every large workload once: " + ", ".join(j["w"].name for j in jobs),
+                   "bytes_per_step": step_bytes, "input": "bf16",
+                   "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1)},
+        "per_recipe": per,
+        "roofline": roofline,
+        "copy_reference_GBps": round(copy_gbs, 1),
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the oracle on the host", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline([j["w"] for j in jobs], args.cpu_rows)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

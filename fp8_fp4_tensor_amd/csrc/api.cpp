@@ -88,6 +88,10 @@ Sizes sizes_of(const fq_desc* d)
     const bool row = d->outputs & FQ_ROWWISE, col = d->outputs & FQ_COLWISE;
     switch (d->recipe) {
     case FQ_PER_TENSOR_CURRENT:
+        z.row_data = row ? R * C : 0;
+        z.col_data = col ? R * C : 0;
+        z.ws = kPartialsBytes;
+        break;
     case FQ_PER_TENSOR_DELAYED:
         z.row_data = row ? R * C : 0;
         z.col_data = col ? R * C : 0;
@@ -250,7 +254,7 @@ fq_status fq_amax(const fq_desc* d, const void* x, float* amax_out, void* ws, si
     if ((s = check_ws(z, ws, ws_bytes)) != FQ_OK)
         return s;
     const int64_t n = d->rows * d->cols;
-    const int g = amax_grid(n, elem_bytes(d));
+    const int g = amax_grid(n, elem_bytes(d), kMaxPartials);
     float* partials = (float*)ws;
     if ((s = hip_status(launch_amax_partial(x, d->in_dtype == FQ_IN_BF16, n, partials, g, st))) != FQ_OK)
         return s;
@@ -279,8 +283,8 @@ fq_status fq_quantize(const fq_desc* d, const void* x, const fq_quantized* o, vo
     const bool row = d->outputs & FQ_ROWWISE, col = d->outputs & FQ_COLWISE;
     switch (d->recipe) {
     case FQ_PER_TENSOR_CURRENT: {
-        const int g = amax_grid(n, elem_bytes(d));
         float* partials = (float*)ws;
+        const int g = amax_grid(n, elem_bytes(d), kMaxPartials);
         if ((s = hip_status(launch_amax_partial(x, bf, n, partials, g, st))) != FQ_OK)
             return s;
         ScaleSrc src;
@@ -312,7 +316,7 @@ fq_status fq_quantize(const fq_desc* d, const void* x, const fq_quantized* o, vo
                                     col ? (uint8_t*)o->colwise.data : nullptr,
                                     col ? (uint8_t*)o->colwise.scale : nullptr, st));
     case FQ_NVFP4: {
-        const int g = amax_grid(n, elem_bytes(d));
+        const int g = amax_grid(n, elem_bytes(d), kMaxPartials);
         float* partials = (float*)ws;
         if ((s = hip_status(launch_amax_partial(x, bf, n, partials, g, st))) != FQ_OK)
             return s;
@@ -381,7 +385,7 @@ fq_status fq_quantize_delayed(const fq_desc* d, const void* x, const fq_delayed_
         return s;
     const int64_t n = d->rows * d->cols;
     float* partials = (float*)ws;
-    const int g = amax_grid(n, elem_bytes(d));
+    const int g = amax_grid(n, elem_bytes(d), kMaxPartials);
     ScaleSrc src;
     src.alpha_in = state->scale;
     src.s_in = state->scale_inv;

@@ -218,6 +218,12 @@ struct In<float> {
         f[3] = __uint_as_float(v[3]);
     }
     __device__ static __forceinline__ float load1(const float* x, int64_t i) { return x[i]; }
+    // max |x| over the four values of a load
+    __device__ static __forceinline__ float absmax16(u32x4 v)
+    {
+        return fmaxf(fmaxf(fabsf(__uint_as_float(v[0])), fabsf(__uint_as_float(v[1]))),
+                     fmaxf(fabsf(__uint_as_float(v[2])), fabsf(__uint_as_float(v[3]))));
+    }
 };
 template <>
 struct In<uint16_t> {
@@ -233,6 +239,19 @@ struct In<uint16_t> {
     __device__ static __forceinline__ float load1(const uint16_t* x, int64_t i)
     {
         return __uint_as_float((uint32_t)x[i] << 16);
+    }
+    // max |x| over the eight values of a load, on the bits: for finite bf16
+    // the magnitude bits (sign cleared) order exactly as the magnitudes, so
+    // a 16-bit integer max (two lanes per dword) is the float max. No value
+    // is unpacked, so nothing from this pass stays live in registers.
+    __device__ static __forceinline__ float absmax16(u32x4 v)
+    {
+        typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+        u16x2 m = __builtin_bit_cast(u16x2, v[0] & 0x7fff7fffu);
+        m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, v[1] & 0x7fff7fffu));
+        m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, v[2] & 0x7fff7fffu));
+        m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, v[3] & 0x7fff7fffu));
+        return __uint_as_float((uint32_t)(m[0] > m[1] ? m[0] : m[1]) << 16);
     }
 };
 

@@ -30,7 +30,7 @@ namespace fq {
 namespace {
 
 constexpr int kLoads = 4;
-constexpr int kMaxGrid = 4096;
+constexpr int kMaxGrid = 16384;
 
 template <typename T>
 __global__ __launch_bounds__(kWG) void k_block_1x128(const T* __restrict__ x, int64_t n, uint8_t* __restrict__ q,

@@ -14,9 +14,11 @@
 // row, a quad of lanes is one 1x32 block (bf16), reduced with two DPP steps;
 // codes and E8M0 scales are written straight from registers. Colwise: the
 // tile's raw inputs go to LDS in the same pass; then each thread owns one
-// column and 64 rows (two 32x1 blocks), reads them back (lanes of a wave
-// read consecutive columns of one row: no bank conflicts), and writes each
-// block's 32 codes as 32 contiguous bytes of the transposed plane.
+// column pair and 32 rows (two 32x1 blocks), reads them back (lanes of a
+// wave read consecutive columns of one row: no bank conflicts) and puts its codes
+// into a second LDS tile laid out as X^T; that tile is written out with
+// eight lanes per 128-byte row of X^T, so every store instruction writes
+// whole lines instead of one 16-byte piece of 64 different lines.
 #include <algorithm>
 
 #include "codec.hpp"
@@ -25,12 +27,31 @@
 namespace fq {
 namespace {
 
+constexpr int kOP = 128 + 16;  // pitch of the LDS tile of transposed codes
+static_assert(128 * kOP + 128 * 4 <= 128 * 128 * 2, "the code tile must fit in the input tile it reuses");
+
 template <typename T>
 constexpr int tile_pitch()
 {
-    return sizeof(T) == 2 ? 128 + 8 : 128;  // bf16 rows padded by 16 bytes; fp32 fits 64 KiB unpadded
+    return sizeof(T) == 2 ? 128 + 8 : 128;  // bf16 rows padded by 16 bytes; fp32 unpadded (64 KiB)
 }
 
+// Loads of one tile row band for this thread: ROUNDS x 16 bytes.
+template <typename T, int ROUNDS>
+__device__ __forceinline__ void mx_load_tile(const T* __restrict__ x, int64_t R, int64_t C, int64_t r0, int64_t c0,
+                                             int cc, int rr0, int rpr, u32x4* v)
+{
+    const bool col_in = c0 + cc < C;
+#pragma unroll
+    for (int k = 0; k < ROUNDS; ++k) {
+        const int64_t r = r0 + rr0 + k * rpr;
+        v[k] = (col_in && r < R) ? ld16_stream(x + r * C + c0 + cc) : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+// Persistent: workgroup g takes tiles g, g + G, ..., with G the number of
+// workgroups the device holds at once, so no tail of late workgroups forms;
+// the resident workgroups of a CU overlap each other's loads and compute.
 template <typename T>
 __global__ __launch_bounds__(kWG) void k_mx(const T* __restrict__ x, int64_t R, int64_t C,
                                             uint8_t* __restrict__ q, uint8_t* __restrict__ e,
@@ -41,63 +62,312 @@ __global__ __launch_bounds__(kWG) void k_mx(const T* __restrict__ x, int64_t R, 
     extern __shared__ __align__(16) unsigned char smem[];
     T* tile = reinterpret_cast<T*>(smem);
     const int lane = threadIdx.x & 63;
-    const int64_t ntc = cdiv(C, 128);
-    const int64_t r0 = (int64_t)(blockIdx.x / ntc) * 128, c0 = (int64_t)(blockIdx.x % ntc) * 128;
+    const int64_t ntc = cdiv(C, 128), ntiles = ntc * cdiv(R, 128);
     const int cc = (threadIdx.x % LPR) * E, rr0 = threadIdx.x / LPR;
-    const bool col_in = c0 + cc < C;
-    u32x4 v[ROUNDS];
-#pragma unroll
-    for (int k = 0; k < ROUNDS; ++k) {
-        const int64_t r = r0 + rr0 + k * RPR;
-        v[k] = (col_in && r < R) ? ld16_stream(x + r * C + c0 + cc) : u32x4{0u, 0u, 0u, 0u};
-    }
-    const int64_t nbc = C / 32;
-#pragma unroll
-    for (int k = 0; k < ROUNDS; ++k) {
-        const int rr = rr0 + k * RPR;
+    const int64_t nbc = C / 32, nbr = R / 32;
+    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const int64_t r0 = (t / ntc) * 128, c0 = (t % ntc) * 128;
+        u32x4 v[ROUNDS];
+        mx_load_tile<T, ROUNDS>(x, R, C, r0, c0, cc, rr0, RPR, v);
+        const bool col_in = c0 + cc < C;
+        // whole 4-code words: the tile spans 128 columns and rows of codes are 4-byte aligned
+        const bool full_row_codes = c0 + 128 <= C && (nbc & 3) == 0;
         if (qt)
-            *reinterpret_cast<u32x4*>(tile + rr * P + cc) = v[k];
-        if (q) {
-            float f[E];
-            In<T>::unpack(v[k], f);
-            const float a = max_lanes<LPB>(absmax<E>(f));
-            const uint32_t code = mx_code(a);
-            const float mult = mx_multiplier(code);
-            if (col_in && r0 + rr < R) {
-                Enc8<kE4M3, E>::store(q + (r0 + rr) * C + c0 + cc, f, mult);
-                if ((lane & (LPB - 1)) == 0)
-                    e[(r0 + rr) * nbc + (c0 + cc) / 32] = (uint8_t)code;
+            __syncthreads();  // the previous tile's LDS reads are done
+#pragma unroll
+        for (int k = 0; k < ROUNDS; ++k) {
+            const int rr = rr0 + k * RPR;
+            if (qt)
+                *reinterpret_cast<u32x4*>(tile + rr * P + cc) = v[k];
+            if (q) {
+                float f[E];
+                In<T>::unpack(v[k], f);
+                const float a = max_lanes<LPB>(absmax<E>(f));
+                const uint32_t code = mx_code(a);
+                const float mult = mx_multiplier(code);
+                // the row's four block codes, gathered into its first lane
+                const int rbase = lane & ~(LPR - 1);
+                const uint32_t word = (uint32_t)__shfl((int)code, rbase) |
+                                      ((uint32_t)__shfl((int)code, rbase + LPB) << 8) |
+                                      ((uint32_t)__shfl((int)code, rbase + 2 * LPB) << 16) |
+                                      ((uint32_t)__shfl((int)code, rbase + 3 * LPB) << 24);
+                if (col_in && r0 + rr < R) {
+                    Enc8<kE4M3, E>::store(q + (r0 + rr) * C + c0 + cc, f, mult);
+                    if (full_row_codes) {
+                        if (lane == rbase)
+                            *reinterpret_cast<uint32_t*>(e + (r0 + rr) * nbc + c0 / 32) = word;
+                    } else if ((lane & (LPB - 1)) == 0) {
+                        e[(r0 + rr) * nbc + (c0 + cc) / 32] = (uint8_t)code;
+                    }
+                }
+            }
+        }
+        if (!qt)
+            continue;
+        __syncthreads();
+        // colwise: thread (p, rb) quantizes rows 32rb..32rb+31 of tile columns
+        // 2p and 2p+1 (two 32x1 blocks); a wave reads one LDS row of 128
+        // columns per instruction. After a barrier the codes go to an LDS
+        // tile laid out as X^T, which reuses the input tile's memory.
+        const int pc = threadIdx.x & 63, rb = threadIdx.x >> 6;
+        u32x4 w[4];
+        uint32_t codes2[2];
+        if constexpr (sizeof(T) == 2) {
+            // keep the 32 packed bf16 pairs (32 registers) and widen on use
+            uint32_t pr[32];
+#pragma unroll
+            for (int k = 0; k < 32; ++k)
+                pr[k] = *reinterpret_cast<const uint32_t*>(tile + (int64_t)(32 * rb + k) * P + 2 * pc);
+            float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 32; ++k) {
+                a0 = fmaxf(a0, fabsf(bf16_lo(pr[k])));
+                a1 = fmaxf(a1, fabsf(bf16_hi(pr[k])));
+            }
+            codes2[0] = mx_code(a0);
+            codes2[1] = mx_code(a1);
+            const float m0 = mx_multiplier(codes2[0]), m1 = mx_multiplier(codes2[1]);
+#pragma unroll
+            for (int d = 0; d < 8; ++d) {
+                w[d >> 2][d & 3] = enc4<kE4M3>(bf16_lo(pr[4 * d]), bf16_lo(pr[4 * d + 1]), bf16_lo(pr[4 * d + 2]),
+                                               bf16_lo(pr[4 * d + 3]), m0);
+                w[2 + (d >> 2)][d & 3] = enc4<kE4M3>(bf16_hi(pr[4 * d]), bf16_hi(pr[4 * d + 1]),
+                                                     bf16_hi(pr[4 * d + 2]), bf16_hi(pr[4 * d + 3]), m1);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                float f[32];
+#pragma unroll
+                for (int k = 0; k < 32; ++k)
+                    f[k] = In<T>::load1(tile, (int64_t)(32 * rb + k) * P + 2 * pc + j);
+                codes2[j] = mx_code(absmax<32>(f));
+                const float m = mx_multiplier(codes2[j]);
+#pragma unroll
+                for (int d = 0; d < 8; ++d)
+                    w[2 * j + (d >> 2)][d & 3] = enc4<kE4M3>(f[4 * d], f[4 * d + 1], f[4 * d + 2], f[4 * d + 3], m);
+            }
+        }
+        __syncthreads();
+        uint8_t* otile = smem;              // [128][kOP] codes of X^T
+        uint8_t* ocode = smem + 128 * kOP;  // [128][4] E8M0 codes of X^T
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            *reinterpret_cast<u32x4*>(otile + (2 * pc + j) * kOP + 32 * rb) = w[2 * j];
+            *reinterpret_cast<u32x4*>(otile + (2 * pc + j) * kOP + 32 * rb + 16) = w[2 * j + 1];
+            ocode[(2 * pc + j) * 4 + rb] = (uint8_t)codes2[j];
+        }
+        __syncthreads();
+        // write X^T rows c0..c0+127, bytes r0..r0+127 of each: eight lanes per
+        // 128-byte row, so each store instruction writes eight whole lines.
+        const int64_t nrows = min((int64_t)128, C - c0), nbytes = min((int64_t)128, R - r0);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int i = k * kWG + threadIdx.x;
+            const int row = i >> 3, seg = (i & 7) * 16;
+            if (row < nrows && seg < nbytes)
+                st16_stream(qt + (c0 + row) * R + r0 + seg,
+                            *reinterpret_cast<const u32x4*>(otile + row * kOP + seg));
+        }
+        if (threadIdx.x < nrows) {
+            const int row = threadIdx.x;
+            uint8_t* dst = et + (c0 + row) * nbr + r0 / 32;
+            if (nbytes == 128 && (nbr & 3) == 0) {
+                *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(ocode + row * 4);
+            } else {
+                for (int j = 0; j < nbytes / 32; ++j)
+                    dst[j] = ocode[row * 4 + j];
             }
         }
     }
-    if (!qt)
-        return;
-    __syncthreads();
-    const int c = threadIdx.x & 127, h = threadIdx.x >> 7;
-    if (c0 + c >= C)
-        return;
-    const int64_t nbr = R / 32;
+}
+
+// ---------------------------------------------------------------- bf16 fast path
+// The same MXFP8 computation for bf16 inputs, on packed bf16 pairs, with the
+// gfx950 converter that takes bf16 and a power-of-two scale directly
+// (v_cvt_scalef32_pk_fp8_bf16: two elements, each divided by the scale and
+// rounded to nearest even). It equals Q_E4M3(x * 2^-e) for every finite bf16
+// x and every E8M0 code, as long as |x * 2^-e| <= 448; beyond that it gives
+// NaN instead of saturating. A block's scaled values stay below 512, so the
+// magnitudes are first clamped, as bf16 bit patterns, to the pattern of
+// 448 * 2^e (a normal bf16 for every code): that clamp is exact, and the
+// clamped elements then convert to exactly 448. The block amax is an integer
+// max of the magnitude bits (exact for finite bf16). Per element this costs
+// about a third of the VALU work of widening, multiplying and clamping in
+// fp32.
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pk_max16(uint32_t a, uint32_t b)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                  __builtin_bit_cast(u16x2, b)));
+}
+__device__ __forceinline__ uint32_t pk_min16(uint32_t a, uint32_t b)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, a),
+                                                                  __builtin_bit_cast(u16x2, b)));
+}
+// bf16 pattern of 448 * 2^(code - 127): exponent field code + 8, mantissa 1.75
+__device__ __forceinline__ uint32_t mx_limit_bf16(uint32_t code) { return ((code + 8u) << 7) | 0x60u; }
+// E8M0 code from the bf16 magnitude bits of a block amax
+__device__ __forceinline__ uint32_t mx_code_bf16(uint32_t mag) { return (uint32_t)max((int)((mag >> 7) & 0xFFu) - 8, 0); }
+// clamp both magnitudes of a pair to lim2 (limit in each half, below
+// 0x8000), keep the signs
+__device__ __forceinline__ uint32_t clamp_pair(uint32_t w, uint32_t lim2)
+{
+    return pk_min16(w & 0x7fff7fffu, lim2) | (w & 0x80008000u);
+}
+// two clamped bf16 pairs -> four E4M3 codes (pair a in bytes 0-1, b in 2-3)
+__device__ __forceinline__ uint32_t cvt4_scaled(uint32_t a, uint32_t b, float scale)
+{
+    s16x2 r = {0, 0};
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(bf16x2, a), scale, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(bf16x2, b), scale, true);
+    return __builtin_bit_cast(uint32_t, r);
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dppu(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+__global__ __launch_bounds__(kWG) void k_mx_bf16(const uint16_t* __restrict__ x, int64_t R, int64_t C,
+                                                 uint8_t* __restrict__ q, uint8_t* __restrict__ e,
+                                                 uint8_t* __restrict__ qt, uint8_t* __restrict__ et)
+{
+    constexpr int ROUNDS = 8, P = 128 + 8;  // 16 lanes x 8 bf16 per tile row; LDS pitch in bf16
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint16_t* tile = reinterpret_cast<uint16_t*>(smem);
+    const int lane = threadIdx.x & 63;
+    const int64_t ntc = cdiv(C, 128), ntiles = ntc * cdiv(R, 128);
+    const int cc = (threadIdx.x & 15) * 8, rr0 = threadIdx.x >> 4;
+    const int64_t nbc = C / 32, nbr = R / 32;
+    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const int64_t r0 = (t / ntc) * 128, c0 = (t % ntc) * 128;
+        const bool col_in = c0 + cc < C;
+        u32x4 v[ROUNDS];
+        {
+            const uint16_t* src = x + (r0 + rr0) * C + c0 + cc;
+            const int64_t step = 16 * C;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        const int rb = 64 * h + 32 * b;
-        if (r0 + rb >= R)
-            break;
-        float f[32];
-#pragma unroll
-        for (int k = 0; k < 32; ++k)
-            f[k] = In<T>::load1(tile, (int64_t)(rb + k) * P + c);
-        const uint32_t code = mx_code(absmax<32>(f));
-        const float mult = mx_multiplier(code);
-        u32x4 w0, w1;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            w0[d] = enc4<kE4M3>(f[4 * d], f[4 * d + 1], f[4 * d + 2], f[4 * d + 3], mult);
-            w1[d] = enc4<kE4M3>(f[16 + 4 * d], f[17 + 4 * d], f[18 + 4 * d], f[19 + 4 * d], mult);
+            for (int k = 0; k < ROUNDS; ++k) {
+                v[k] = (col_in && r0 + rr0 + 16 * k < R) ? ld16_stream(src) : u32x4{0u, 0u, 0u, 0u};
+                src += step;
+            }
         }
-        uint8_t* out = qt + (c0 + c) * R + r0 + rb;
-        st16_stream(out, w0);
-        st16_stream(out + 16, w1);
-        et[(c0 + c) * nbr + (r0 + rb) / 32] = (uint8_t)code;
+        const bool full_row_codes = c0 + 128 <= C && (nbc & 3) == 0;
+        if (qt)
+            __syncthreads();  // the previous tile's LDS reads are done
+        {
+            uint8_t* dst = q ? q + (r0 + rr0) * C + c0 + cc : nullptr;
+            uint8_t* edst = q ? e + (r0 + rr0) * nbc + c0 / 32 : nullptr;
+#pragma unroll
+            for (int k = 0; k < ROUNDS; ++k) {
+                const int rr = rr0 + 16 * k;
+                if (qt)
+                    *reinterpret_cast<u32x4*>(tile + rr * P + cc) = v[k];
+                if (q) {
+                    uint32_t m = pk_max16(pk_max16(v[k][0] & 0x7fff7fffu, v[k][1] & 0x7fff7fffu),
+                                          pk_max16(v[k][2] & 0x7fff7fffu, v[k][3] & 0x7fff7fffu));
+                    m = max(m & 0xFFFFu, m >> 16);
+                    m = max(m, dppu<kDppXor1>(m));
+                    m = max(m, dppu<kDppXor2>(m));  // the 1x32 block: a quad of lanes
+                    const uint32_t code = mx_code_bf16(m);
+                    const uint32_t lim = mx_limit_bf16(code), lim2 = lim | (lim << 16);
+                    const float scale = e8m0_value(code);
+                    u32x2 w;
+                    w[0] = cvt4_scaled(clamp_pair(v[k][0], lim2), clamp_pair(v[k][1], lim2), scale);
+                    w[1] = cvt4_scaled(clamp_pair(v[k][2], lim2), clamp_pair(v[k][3], lim2), scale);
+                    // the row's four block codes into its first lane (DPP row_shl 4, 8, 12)
+                    const int rbase = lane & ~15;
+                    const uint32_t word = code | (dppu<0x104>(code) << 8) | (dppu<0x108>(code) << 16) |
+                                          (dppu<0x10C>(code) << 24);
+                    if (col_in && r0 + rr < R) {
+                        st8_stream(dst, w);
+                        if (full_row_codes) {
+                            if (lane == rbase)
+                                *reinterpret_cast<uint32_t*>(edst) = word;
+                        } else if ((lane & 3) == 0) {
+                            edst[cc / 32] = (uint8_t)code;
+                        }
+                    }
+                }
+                if (q) {
+                    dst += 16 * C;
+                    edst += 16 * nbc;
+                }
+            }
+        }
+        if (!qt)
+            continue;
+        __syncthreads();
+        // colwise: thread (p, rb) takes tile columns 2p, 2p+1, rows 32rb..+31
+        const int pc = threadIdx.x & 63, rb = threadIdx.x >> 6;
+        u32x4 w[4];
+        uint32_t code0, code1;
+        {
+            uint32_t pr[32];
+#pragma unroll
+            for (int k = 0; k < 32; ++k)
+                pr[k] = *reinterpret_cast<const uint32_t*>(tile + (32 * rb + k) * P + 2 * pc);
+            uint32_t m = 0;
+#pragma unroll
+            for (int k = 0; k < 32; ++k)
+                m = pk_max16(m, pr[k] & 0x7fff7fffu);
+            code0 = mx_code_bf16(m & 0xFFFFu);
+            code1 = mx_code_bf16(m >> 16);
+            const uint32_t lim2 = mx_limit_bf16(code0) | (mx_limit_bf16(code1) << 16);
+            const float s0 = e8m0_value(code0), s1 = e8m0_value(code1);
+#pragma unroll
+            for (int k = 0; k < 32; ++k)
+                pr[k] = clamp_pair(pr[k], lim2);
+#pragma unroll
+            for (int d = 0; d < 8; ++d) {
+                // rows 4d..4d+3 of column 2p (low halves) and of column 2p+1 (high halves)
+                const uint32_t a0 = __builtin_amdgcn_perm(pr[4 * d + 1], pr[4 * d], 0x05040100u);
+                const uint32_t b0 = __builtin_amdgcn_perm(pr[4 * d + 3], pr[4 * d + 2], 0x05040100u);
+                const uint32_t a1 = __builtin_amdgcn_perm(pr[4 * d + 1], pr[4 * d], 0x07060302u);
+                const uint32_t b1 = __builtin_amdgcn_perm(pr[4 * d + 3], pr[4 * d + 2], 0x07060302u);
+                w[d >> 2][d & 3] = cvt4_scaled(a0, b0, s0);
+                w[2 + (d >> 2)][d & 3] = cvt4_scaled(a1, b1, s1);
+            }
+        }
+        __syncthreads();
+        uint8_t* otile = smem;              // [128][kOP] codes of X^T
+        uint8_t* ocode = smem + 128 * kOP;  // [128][4] E8M0 codes of X^T
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            *reinterpret_cast<u32x4*>(otile + (2 * pc + j) * kOP + 32 * rb) = w[2 * j];
+            *reinterpret_cast<u32x4*>(otile + (2 * pc + j) * kOP + 32 * rb + 16) = w[2 * j + 1];
+        }
+        ocode[(2 * pc) * 4 + rb] = (uint8_t)code0;
+        ocode[(2 * pc + 1) * 4 + rb] = (uint8_t)code1;
+        __syncthreads();
+        const int64_t nrows = min((int64_t)128, C - c0), nbytes = min((int64_t)128, R - r0);
+        {
+            const int row0 = threadIdx.x >> 3, seg = (threadIdx.x & 7) * 16;
+            uint8_t* dst = qt + (c0 + row0) * R + r0 + seg;
+            const int64_t step = 32 * R;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int row = row0 + 32 * k;
+                if (row < nrows && seg < nbytes)
+                    st16_stream(dst, *reinterpret_cast<const u32x4*>(otile + row * kOP + seg));
+                dst += step;
+            }
+        }
+        if (threadIdx.x < nrows) {
+            const int row = threadIdx.x;
+            uint8_t* dst = et + (c0 + row) * nbr + r0 / 32;
+            if (nbytes == 128 && (nbr & 3) == 0) {
+                *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(ocode + row * 4);
+            } else {
+                for (int j = 0; j < nbytes / 32; ++j)
+                    dst[j] = ocode[row * 4 + j];
+            }
+        }
     }
 }
 
@@ -106,13 +376,17 @@ __global__ __launch_bounds__(kWG) void k_mx(const T* __restrict__ x, int64_t R, 
 hipError_t launch_mx(const void* x, int in_bf16, int64_t R, int64_t C, uint8_t* q, uint8_t* e, uint8_t* qt,
                      uint8_t* et, hipStream_t stream)
 {
-    const unsigned grid = (unsigned)(cdiv(C, 128) * cdiv(R, 128));
+    const int64_t ntiles = cdiv(C, 128) * cdiv(R, 128);
     if (in_bf16) {
         const size_t lds = qt ? 128 * tile_pitch<uint16_t>() * 2 : 0;
-        k_mx<uint16_t><<<grid, kWG, lds, stream>>>((const uint16_t*)x, R, C, q, e, qt, et);
+        static ResidentGrid cache;
+        const int64_t grid = std::min<int64_t>(ntiles, cache.get(k_mx_bf16, kWG, lds));
+        k_mx_bf16<<<(unsigned)grid, kWG, lds, stream>>>((const uint16_t*)x, R, C, q, e, qt, et);
     } else {
         const size_t lds = qt ? 128 * tile_pitch<float>() * 4 : 0;
-        k_mx<float><<<grid, kWG, lds, stream>>>((const float*)x, R, C, q, e, qt, et);
+        static ResidentGrid cache;
+        const int64_t grid = std::min<int64_t>(ntiles, cache.get(k_mx<float>, kWG, lds));
+        k_mx<float><<<(unsigned)grid, kWG, lds, stream>>>((const float*)x, R, C, q, e, qt, et);
     }
     return hipGetLastError();
 }

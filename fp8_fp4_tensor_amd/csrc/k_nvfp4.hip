@@ -36,7 +36,7 @@ namespace fq {
 namespace {
 
 constexpr int kLoads = 4;
-constexpr int kMaxGrid = 4096;
+constexpr int kMaxGrid = 16384;
 
 // Tensor-level scale from the amax source (uniform control flow).
 __device__ __forceinline__ void nvfp4_tensor(const ScaleSrc& src, float* lds, float& alpha_s, float& S, float& A)

@@ -27,7 +27,7 @@ namespace fq {
 namespace {
 
 constexpr int kLoads = 4;
-constexpr int kCastMaxGrid = 2048;
+constexpr int kCastMaxGrid = 16384;
 
 template <typename T>
 __global__ __launch_bounds__(kWG) void k_amax_partial(const T* __restrict__ x, int64_t n,
@@ -46,11 +46,8 @@ __global__ __launch_bounds__(kWG) void k_amax_partial(const T* __restrict__ x, i
         for (int j = 0; j < kLoads; ++j)
             v[j] = (u0 + j < nunits) ? ld16(x + (u0 + j) * U + lane * E) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int j = 0; j < kLoads; ++j) {
-            float f[E];
-            In<T>::unpack(v[j], f);
-            m = fmaxf(m, absmax<E>(f));
-        }
+        for (int j = 0; j < kLoads; ++j)
+            m = fmaxf(m, In<T>::absmax16(v[j]));
     }
     for (int64_t i = nunits * U + (int64_t)blockIdx.x * kWG + threadIdx.x; i < n; i += (int64_t)gridDim.x * kWG)
         m = fmaxf(m, fabsf(In<T>::load1(x, i)));
@@ -198,27 +195,42 @@ __global__ __launch_bounds__(kWG) void k_amax_finish(const float* __restrict__ p
 
 // Delayed scaling, second half of a step ([MP] recipe 2: record this step's
 // amax in the window; the next step's scale comes from the window's max).
-__global__ __launch_bounds__(kWG) void k_delayed_finish(const float* __restrict__ partials, int n, float* hist,
-                                                        int H, int slot, float* alpha, float* s, float fmax_v,
-                                                        float* amax_out)
+// One workgroup reads the partials and the window together, so both
+// reductions share one round of loads and one LDS exchange.
+constexpr int kFinishThreads = 256;
+
+__global__ __launch_bounds__(kFinishThreads) void k_delayed_finish(const float* __restrict__ partials, int n,
+                                                                   float* hist, int H, int slot, float* alpha,
+                                                                   float* s, float fmax_v, float* amax_out)
 {
-    __shared__ float lds[4];
-    float m = 0.0f;
-    for (int i = threadIdx.x; i < n; i += kWG)
-        m = fmaxf(m, partials[i]);
-    const float at = max_workgroup(m, lds);
-    float w = at;
-    for (int i = threadIdx.x; i < H; i += kWG)
+    __shared__ float lds[2][kFinishThreads / 64];
+    float mp = 0.0f, mh = 0.0f;
+    for (int i = threadIdx.x; i < n; i += kFinishThreads)
+        mp = fmaxf(mp, partials[i]);
+    for (int i = threadIdx.x; i < H; i += kFinishThreads)
         if (i != slot)
-            w = fmaxf(w, hist[i]);
-    w = max_workgroup(w, lds);
+            mh = fmaxf(mh, hist[i]);
+    mp = max_wave(mp);
+    mh = max_wave(mh);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        lds[0][w] = mp;
+        lds[1][w] = mh;
+    }
+    __syncthreads();
     if (threadIdx.x == 0) {
+        float at = 0.0f, wm = 0.0f;
+        for (int k = 0; k < kFinishThreads / 64; ++k) {
+            at = fmaxf(at, lds[0][k]);
+            wm = fmaxf(wm, lds[1][k]);
+        }
+        wm = fmaxf(wm, at);
         hist[slot] = at;
         if (amax_out)
             *amax_out = at;
-        if (w > 0.0f) {
+        if (wm > 0.0f) {
             float al, ss;
-            tensor_scales(w, fmax_v, al, ss);
+            tensor_scales(wm, fmax_v, al, ss);
             *alpha = al;
             *s = ss;
         }
@@ -233,10 +245,10 @@ int64_t elems_per_wg_step()
 
 }  // namespace
 
-int amax_grid(int64_t n, int elem_bytes)
+int amax_grid(int64_t n, int elem_bytes, int max_grid)
 {
     const int64_t per = (int64_t)kWG * (16 / elem_bytes) * kLoads;
-    return (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(n, per), kMaxPartials));
+    return (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(n, per), max_grid));
 }
 
 hipError_t launch_amax_partial(const void* x, int in_bf16, int64_t n, float* partials, int grid, hipStream_t stream)
@@ -314,7 +326,8 @@ hipError_t launch_cast_tensor_2d(const void* x, int in_bf16, int fmt, int64_t R,
 hipError_t launch_delayed_finish(const float* partials, int n_partials, float* hist, int H, int slot, float* alpha,
                                  float* s, float fmax_v, float* amax_out, hipStream_t stream)
 {
-    k_delayed_finish<<<1, kWG, 0, stream>>>(partials, n_partials, hist, H, slot, alpha, s, fmax_v, amax_out);
+    k_delayed_finish<<<1, kFinishThreads, 0, stream>>>(partials, n_partials, hist, H, slot, alpha, s, fmax_v,
+                                                        amax_out);
     return hipGetLastError();
 }
 

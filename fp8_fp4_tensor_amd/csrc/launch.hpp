@@ -6,10 +6,42 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace fq {
 
-// Workspace layout shared by the per-tensor and NVFP4 paths: one fp32 amax
-// partial per workgroup of the amax pass.
+// Number of workgroups of one kernel that fit on the current device at once
+// (occupancy x CUs), for persistent kernels whose workgroups loop over
+// tiles. Computed once per device; the library keeps no other state.
+struct ResidentGrid {
+    static constexpr int kMaxDevices = 64;
+    std::atomic<int> slots[kMaxDevices][2] = {};  // [device][lds > 0]
+    template <typename K>
+    int get(K kernel, int threads, size_t lds)
+    {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+            return 1024;
+        std::atomic<int>& slot = slots[dev][lds > 0];
+        int c = slot.load(std::memory_order_relaxed);
+        if (c > 0)
+            return c;
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kernel), threads,
+                                                         lds) != hipSuccess ||
+            cus <= 0 || per_cu <= 0)
+            return 1024;
+        c = cus * per_cu;
+        slot.store(c, std::memory_order_relaxed);
+        return c;
+    }
+};
+
+// Workspace layout of the per-tensor and NVFP4 paths: one fp32 amax partial
+// per workgroup of the amax pass, at most kMaxPartials. They are combined
+// without atomics: every workgroup of the second pass (or the delayed-scaling
+// finish) re-reduces them from L2.
 constexpr int kMaxPartials = 1024;
 constexpr size_t kPartialsBytes = kMaxPartials * sizeof(float);
 
@@ -22,8 +54,9 @@ struct ScaleSrc {
     const float* s_in = nullptr;
 };
 
-// Number of workgroups of the amax pass for n elements of the given size.
-int amax_grid(int64_t n, int elem_bytes);
+// Number of workgroups of an amax pass over n elements of the given size,
+// at most max_grid.
+int amax_grid(int64_t n, int elem_bytes, int max_grid);
 
 // partials[g] = max|x| over workgroup g's share; grid from amax_grid().
 hipError_t launch_amax_partial(const void* x, int in_bf16, int64_t n, float* partials, int grid,

@@ -49,6 +49,7 @@ def test_sizes_per_recipe():
     both = fq.FQ_ROWWISE | fq.FQ_COLWISE
     z = sizes(fq.FQ_PER_TENSOR_CURRENT, fq.FQ_E4M3, 8192, 4096)
     assert (z.row_data, z.row_scale, z.col_data, z.col_scale) == (8192 * 4096, 0, 0, 0) and z.workspace == 4096
+    assert sizes(fq.FQ_PER_TENSOR_DELAYED, fq.FQ_E4M3, 8192, 4096).workspace == 4096
     z = sizes(fq.FQ_BLOCK_FP32, fq.FQ_E4M3, 16384, 7168, (1, 128), both)
     assert (z.row_data, z.row_scale) == (16384 * 7168, 16384 * 56 * 4)
     assert (z.col_data, z.col_scale) == (16384 * 7168, 7168 * 128 * 4) and z.workspace == 0

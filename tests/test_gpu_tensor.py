@@ -68,6 +68,16 @@ def test_ragged_shapes(shape, dt, fmt):
     check_current(x, fmt)
 
 
+@pytest.mark.parametrize("shape,dt", [((2048, 1000), "bf16"), ((1024, 1025), "f32"), ((1024, 1025), "bf16"),
+                                      ((1023, 1025), "bf16"), ((4100, 10000), "bf16"), ((4096, 4096), "f32")])
+@pytest.mark.parametrize("fmt", [fq.FQ_E4M3, fq.FQ_E5M2])
+def test_mid_and_large_sizes(shape, dt, fmt):
+    """Multi-megabyte tensors, with and without a ragged tail of elements
+    beyond the last whole 16-byte load of a wave."""
+    x = W.normal(shape, 2.0, shape[0] + shape[1], W.BF16 if dt == "bf16" else W.F32)
+    check_current(x, fmt)
+
+
 @pytest.mark.parametrize("shape", [(65, 130), (64, 64), (1, 300), (200, 3)])
 @pytest.mark.parametrize("fmt", [fq.FQ_E4M3, fq.FQ_E5M2])
 def test_colwise_transpose(shape, fmt):
