@@ -17,7 +17,6 @@ Prints one JSON line. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
 import argparse
 import ctypes
-import hashlib
 import json
 import os
 import sys
@@ -51,20 +50,12 @@ def algorithmic_bytes(w) -> int:
     raise ValueError(w.recipe)
 
 
-def kernel_source_hash(files):
-    h = hashlib.sha256()
-    for f in files:
-        with open(os.path.join(ROOT, "fp8_fp4_tensor_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
 # which source files define each workload's kernels (for the traffic counters)
 KERNEL_FILES = {"current": ["k_tensor.hip", "codec.hpp"], "delayed": ["k_tensor.hip", "codec.hpp"],
                 "block": ["k_block.hip", "codec.hpp"], "mx": ["k_mx.hip", "codec.hpp"],
                 "nvfp4": ["k_nvfp4.hip", "k_tensor.hip", "codec.hpp"]}
 KERNEL_NAMES = {"current": "k_cast_tensor", "delayed": "k_cast_tensor", "block1x128": "k_block_1x128",
-                "block128x128": "k_block_128x128", "mx": "k_mx", "nvfp4_1x16": "k_nvfp4_1x16",
+                "block128x128": "k_block_128x128", "mx": "k_mx_bf16", "nvfp4_1x16": "k_nvfp4_1x16",
                 "nvfp4_16x16": "k_nvfp4_16x16"}
 
 
@@ -84,7 +75,8 @@ def traffic_for(w, per_launch_alg_bytes):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("source_hash") != kernel_source_hash(KERNEL_FILES[w.recipe]):
+    from fp8_fp4_tensor_amd.profsum import source_hash
+    if t.get("source_hash") != source_hash(KERNEL_FILES[w.recipe]):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -151,7 +143,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=float, default=0.25, help="row fraction for the oracle baseline")
+    ap.add_argument("--cpu-rows", type=float, default=0.6, help="row fraction for the oracle baseline")
     ap.add_argument("--only", default="", help="comma-separated workload names (profiling runs)")
     ap.add_argument("--copy-only", action="store_true",
                     help="time only a plain 256 MiB device copy (counter calibration and reference)")

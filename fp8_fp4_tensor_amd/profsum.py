@@ -1,0 +1,118 @@
+"""Summaries of rocprofv3 runs of bench.py, for the profiles/ directory.
+
+  python -m fp8_fp4_tensor_amd.profsum trace  STATS_CSV TRACE_CSV OUT.md "COMMAND"
+      per-kernel durations (calls, mean, min, max) from a --kernel-trace --stats run.
+
+  python -m fp8_fp4_tensor_amd.profsum traffic FETCH_CSV WRITE_CSV KERNEL WORKLOAD ROWSxCOLS OUT.json "COMMANDS"
+      HBM bytes per launch of KERNEL from two --pmc runs (FETCH_SIZE, then
+      WRITE_SIZE; both in KiB per dispatch). Each counter is scaled by what it
+      reads for the plain 256 MiB device copy that bench.py runs first
+      (256 MiB read and 256 MiB written), so the result is in true bytes.
+      The file records a hash of the kernel's sources; bench.py reports the
+      traffic only while the sources are unchanged.
+"""
+import collections
+import csv
+import json
+import os
+import sys
+
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+COPY_BYTES = 256 << 20
+
+
+def _rows(path):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def short_name(name):
+    """Kernel name without namespaces, parameter list or return type."""
+    n = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    return n.split("(")[0].replace("fq::", "")
+
+
+def trace(stats_csv, trace_csv, out_md, command):
+    stats = _rows(stats_csv)
+    lines = ["# Kernel durations (rocprofv3 --kernel-trace --stats)", "", f"Command: `{command}`", "",
+             "| kernel | calls | mean us | min us | max us | share |", "|---|---|---|---|---|---|"]
+    for r in stats:
+        name = r["Name"]
+        short = short_name(name)
+        lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
+    # one step in dispatch order, from the trace: durations and gaps
+    rows = sorted(_rows(trace_csv), key=lambda r: int(r["Start_Timestamp"]))
+    lines += ["", "Last dispatches in order (duration, gap after the previous kernel):", "",
+              "| kernel | us | gap us |", "|---|---|---|"]
+    prev = None
+    for r in rows[-16:]:
+        s, e = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+        short = short_name(r["Kernel_Name"])
+        gap = "" if prev is None else f"{(s - prev) / 1e3:.2f}"
+        lines.append(f"| `{short}` | {(e - s) / 1e3:.2f} | {gap} |")
+        prev = e
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def _mean_counter(rows, kernel_substr, counter):
+    vals = [float(r["Counter_Value"]) for r in rows
+            if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter]
+    # several rows per dispatch (one per counter instance) are summed per dispatch
+    per = collections.defaultdict(float)
+    for r in rows:
+        if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter:
+            per[r["Dispatch_Id"]] += float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no {counter} rows for {kernel_substr}")
+    return sum(per.values()) / len(per), len(per), len(vals)
+
+
+def source_hash(files):
+    import hashlib
+    h = hashlib.sha256()
+    here = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+    for f in files:
+        with open(os.path.join(here, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {"k_block_128x128": ["k_block.hip", "codec.hpp"], "k_block_1x128": ["k_block.hip", "codec.hpp"],
+                  "k_mx_bf16": ["k_mx.hip", "codec.hpp"], "k_cast_tensor": ["k_tensor.hip", "codec.hpp"],
+                  "k_nvfp4_1x16": ["k_nvfp4.hip", "k_tensor.hip", "codec.hpp"],
+                  "k_nvfp4_16x16": ["k_nvfp4.hip", "k_tensor.hip", "codec.hpp"]}
+
+
+def traffic(fetch_csv, write_csv, kernel, workload, shape, out_json, commands):
+    fr, wr = _rows(fetch_csv), _rows(write_csv)
+    f_k, nf, _ = _mean_counter(fr, kernel, "FETCH_SIZE")
+    w_k, nw, _ = _mean_counter(wr, kernel, "WRITE_SIZE")
+    f_c, _, _ = _mean_counter(fr, COPY_KERNEL, "FETCH_SIZE")
+    w_c, _, _ = _mean_counter(wr, COPY_KERNEL, "WRITE_SIZE")
+    f_scale = COPY_BYTES / (f_c * 1024.0)
+    w_scale = COPY_BYTES / (w_c * 1024.0)
+    read_b = f_k * 1024.0 * f_scale
+    write_b = w_k * 1024.0 * w_scale
+    family = kernel.split("<")[0].split("(")[0]
+    out = {"kernel": kernel, "workload": workload, "shape": shape, "dispatches": {"fetch": nf, "write": nw},
+           "fetch_kib_per_dispatch": f_k, "write_kib_per_dispatch": w_k,
+           "copy_fetch_kib": f_c, "copy_write_kib": w_c,
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "hbm_read_bytes_per_launch": int(read_b), "hbm_write_bytes_per_launch": int(write_b),
+           "hbm_bytes_per_launch": int(read_b + write_b),
+           "source_hash": source_hash(KERNEL_SOURCES[family]), "commands": commands}
+    with open(out_json, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
+
+
+if __name__ == "__main__":
+    if sys.argv[1] == "trace":
+        trace(*sys.argv[2:6])
+    elif sys.argv[1] == "traffic":
+        traffic(*sys.argv[2:9])
+    else:
+        raise SystemExit(__doc__)
