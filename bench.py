@@ -137,6 +137,66 @@ def cpu_baseline(workloads, row_fraction):
                       f"({total_bytes / 1e9:.2f} GB algorithmic, {total_t:.1f} s, one thread)"}
 
 
+def plane_bytes(w, which):
+    """Code and scale bytes of one plane of workload w (what a dequantize reads)."""
+    R, C = w.shape
+    n = R * C
+    if w.recipe in ("current", "delayed"):
+        return n + 4
+    if w.recipe == "block":
+        br, bc = w.block
+        return n + 4 * n // (br * bc)
+    if w.recipe == "mx":
+        return n + n // 32
+    br, bc = w.block
+    return n // 2 + n // (br * bc) + 4
+
+
+def time_extras(torch, fq, L, stream_p, jobs, steps):
+    """Dequantize (rowwise plane to bf16) and MXFP8 rowwise-to-colwise requantize at
+    the large workloads' shapes, each call bracketed by events; not part of the step."""
+    out = {}
+    for j in jobs:
+        w = j["w"]
+        R, C = w.shape
+        y = torch.empty((R, C), dtype=torch.bfloat16, device="cuda")
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for k in range(-1, steps):
+            if k >= 0:
+                ev[k][0].record()
+            rc = L.fq_dequantize(ctypes.byref(j["d"]), ctypes.byref(j["cq"]), fq.FQ_ROWWISE,
+                                 ctypes.c_void_p(y.data_ptr()), fq.FQ_IN_BF16, stream_p)
+            if k >= 0:
+                ev[k][1].record()
+            if rc != fq.FQ_OK:
+                raise fq.FqError(rc, "dequantize " + w.name)
+        torch.cuda.synchronize()
+        us = 1e3 * sum(a.elapsed_time(b) for a, b in ev) / steps
+        nbytes = plane_bytes(w, fq.FQ_ROWWISE) + 2 * R * C
+        out["dequant_bf16/" + w.name] = {"us_per_call": round(us, 2), "bytes": nbytes,
+                                         "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1)}
+        del y
+        if w.recipe == "mx":
+            d = fq.desc(fq.FQ_MX, fq.FQ_IN_BF16, fq.FQ_E4M3, R, C, (1, 32), fq.FQ_COLWISE)
+            dst = fq.alloc_quantized(d)
+            cdst = dst.c()
+            for k in range(-1, steps):
+                if k >= 0:
+                    ev[k][0].record()
+                rc = L.fq_requantize_transpose(ctypes.byref(j["d"]), ctypes.byref(j["cq"]), ctypes.byref(cdst),
+                                               stream_p)
+                if k >= 0:
+                    ev[k][1].record()
+                if rc != fq.FQ_OK:
+                    raise fq.FqError(rc, "requantize " + w.name)
+            torch.cuda.synchronize()
+            us = 1e3 * sum(a.elapsed_time(b) for a, b in ev) / steps
+            nbytes = 2 * (R * C + R * C // 32)
+            out["requant_colwise/" + w.name] = {"us_per_call": round(us, 2), "bytes": nbytes,
+                                                "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -145,6 +205,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=float, default=0.6, help="row fraction for the oracle baseline")
     ap.add_argument("--only", default="", help="comma-separated workload names (profiling runs)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the dequantize / requantize timings reported beside the step")
     ap.add_argument("--copy-only", action="store_true",
                     help="time only a plain 256 MiB device copy (counter calibration and reference)")
     args = ap.parse_args()
@@ -275,6 +337,8 @@ def main():
         "roofline": roofline,
         "copy_reference_GBps": round(copy_gbs, 1),
     }
+    if not args.no_extras:
+        result["dequant_requant"] = time_extras(torch, fq, L, sp, jobs, args.steps)
     if not args.no_cpu_baseline:
         print("bench: timing the oracle on the host", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline([j["w"] for j in jobs], args.cpu_rows)

@@ -397,7 +397,8 @@ fq_status fq_quantize_delayed(const fq_desc* d, const void* x, const fq_delayed_
                                             state->scale, state->scale_inv, fmax_v, o->amax, st));
 }
 
-fq_status fq_dequantize(const fq_desc* d, const fq_quantized* in, int32_t which, float* y, hipStream_t st)
+fq_status fq_dequantize(const fq_desc* d, const fq_quantized* in, int32_t which, void* y, int32_t y_dtype,
+                        hipStream_t st)
 {
     fq_status s = check_desc(d);
     if (s != FQ_OK)
@@ -405,6 +406,8 @@ fq_status fq_dequantize(const fq_desc* d, const fq_quantized* in, int32_t which,
     if (which != FQ_ROWWISE && which != FQ_COLWISE)
         return FQ_E_INVALID;
     if (!(d->outputs & (uint32_t)which))
+        return FQ_E_INVALID;
+    if (y_dtype != FQ_IN_F32 && y_dtype != FQ_IN_BF16)
         return FQ_E_INVALID;
     const bool ts = per_tensor(d->recipe) || d->recipe == FQ_NVFP4;
     if ((s = check_out(d, in, ts)) != FQ_OK)
@@ -417,23 +420,50 @@ fq_status fq_dequantize(const fq_desc* d, const fq_quantized* in, int32_t which,
     if (!aligned(y, 16))
         return FQ_E_ALIGN;
     const bool colw = which == FQ_COLWISE;
+    const int bf = y_dtype == FQ_IN_BF16;
     const fq_plane& p = colw ? in->colwise : in->rowwise;
     // a colwise plane is the rowwise layout of the transposed shape
     const int64_t R = colw ? C0 : R0, C = colw ? R0 : C0;
     switch (d->recipe) {
     case FQ_PER_TENSOR_CURRENT:
     case FQ_PER_TENSOR_DELAYED:
-        return hip_status(launch_dequant_tensor((const uint8_t*)p.data, d->format, R * C, in->tensor_scale, y, st));
+        return hip_status(launch_dequant_tensor((const uint8_t*)p.data, d->format, R * C, in->tensor_scale, y, bf, st));
     case FQ_BLOCK_FP32:
         return hip_status(launch_dequant_block((const uint8_t*)p.data, (const float*)p.scale, R, C,
-                                               d->block_rows, 128, y, st));
+                                               d->block_rows, 128, y, bf, st));
     case FQ_MX:
-        return hip_status(launch_dequant_mx((const uint8_t*)p.data, (const uint8_t*)p.scale, R, C, y, st));
+        return hip_status(launch_dequant_mx((const uint8_t*)p.data, (const uint8_t*)p.scale, R, C, y, bf, st));
     case FQ_NVFP4:
         return hip_status(launch_dequant_nvfp4((const uint8_t*)p.data, (const uint8_t*)p.scale, in->tensor_scale, R,
-                                               C, d->block_rows, 16, y, st));
+                                               C, d->block_rows, 16, y, bf, st));
     }
     return FQ_E_INVALID;
+}
+
+fq_status fq_requantize_transpose(const fq_desc* d, const fq_quantized* in, const fq_quantized* out, hipStream_t st)
+{
+    if (!d)
+        return FQ_E_INVALID;
+    if (d->recipe < FQ_PER_TENSOR_CURRENT || d->recipe > FQ_NVFP4 || d->rows < 0 || d->cols < 0)
+        return FQ_E_INVALID;
+    if (d->recipe != FQ_MX || d->format != FQ_E4M3 || d->block_rows != 1 || d->block_cols != 32)
+        return FQ_E_UNSUPPORTED;
+    if (d->cols > 0 && d->rows > kMaxElems / d->cols)
+        return FQ_E_SHAPE;
+    if (d->rows % 32 || d->cols % 32)
+        return FQ_E_SHAPE;
+    if (!in || !out)
+        return FQ_E_INVALID;
+    const int64_t R = d->rows, C = d->cols;
+    if (R * C == 0)
+        return FQ_OK;
+    if (!in->rowwise.data || !in->rowwise.scale || !out->colwise.data || !out->colwise.scale)
+        return FQ_E_INVALID;
+    if (!aligned(in->rowwise.data, 16) || !aligned(in->rowwise.scale, 16) || !aligned(out->colwise.data, 16) ||
+        !aligned(out->colwise.scale, 16))
+        return FQ_E_ALIGN;
+    return hip_status(launch_mx_requant((const uint8_t*)in->rowwise.data, (const uint8_t*)in->rowwise.scale, R, C,
+                                        (uint8_t*)out->colwise.data, (uint8_t*)out->colwise.scale, st));
 }
 
 }  // extern "C"

@@ -89,6 +89,18 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_1x16(const T* __restrict__ x, int
 {
     __shared__ float lds[4];
     constexpr int E = In<T>::kE, U = 64 * E, LPB = 16 / E;
+    const int lane = threadIdx.x & 63;
+    const int64_t nunits = cdiv(n, U);
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    // the first step's loads go out before the tensor scale is resolved
+    u32x4 v[kLoads];
+    int64_t u0 = wave * kLoads;
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+        const int64_t e = (u0 + j) * U + lane * E;
+        v[j] = (u0 + j < nunits && e < n) ? ld16_stream(x + e) : u32x4{0u, 0u, 0u, 0u};
+    }
     float alpha_s, S, A;
     nvfp4_tensor(src, lds, alpha_s, S, A);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -97,16 +109,13 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_1x16(const T* __restrict__ x, int
         if (amax_out)
             *amax_out = A;
     }
-    const int lane = threadIdx.x & 63;
-    const int64_t nunits = cdiv(n, U);
-    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int64_t nwaves = (int64_t)gridDim.x * 4;
-    for (int64_t u0 = wave * kLoads; u0 < nunits; u0 += nwaves * kLoads) {
-        u32x4 v[kLoads];
+    for (; u0 < nunits; u0 += nwaves * kLoads) {
+        if (u0 != wave * kLoads) {
 #pragma unroll
-        for (int j = 0; j < kLoads; ++j) {
-            const int64_t e = (u0 + j) * U + lane * E;
-            v[j] = (u0 + j < nunits && e < n) ? ld16_stream(x + e) : u32x4{0u, 0u, 0u, 0u};
+            for (int j = 0; j < kLoads; ++j) {
+                const int64_t e = (u0 + j) * U + lane * E;
+                v[j] = (u0 + j < nunits && e < n) ? ld16_stream(x + e) : u32x4{0u, 0u, 0u, 0u};
+            }
         }
 #pragma unroll
         for (int j = 0; j < kLoads; ++j) {
@@ -135,14 +144,6 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_16x16(const T* __restrict__ x, in
 {
     __shared__ float lds[4];
     constexpr int E = In<T>::kE, LPB = 16 / E, WC = kWG * E;  // columns per workgroup
-    float alpha_s, S, A;
-    nvfp4_tensor(src, lds, alpha_s, S, A);
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        if (S_out)
-            *S_out = S;
-        if (amax_out)
-            *amax_out = A;
-    }
     const int64_t nwc = cdiv(C, WC);
     const int64_t r0 = (int64_t)(blockIdx.x / nwc) * 16;
     const int64_t c = (int64_t)(blockIdx.x % nwc) * WC + (int64_t)threadIdx.x * E;
@@ -151,6 +152,14 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_16x16(const T* __restrict__ x, in
 #pragma unroll
     for (int i = 0; i < 16; ++i)
         v[i] = in ? ld16_stream(x + (r0 + i) * C + c) : u32x4{0u, 0u, 0u, 0u};
+    float alpha_s, S, A;
+    nvfp4_tensor(src, lds, alpha_s, S, A);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (S_out)
+            *S_out = S;
+        if (amax_out)
+            *amax_out = A;
+    }
     float m = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {

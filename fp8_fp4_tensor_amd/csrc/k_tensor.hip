@@ -86,6 +86,17 @@ __global__ __launch_bounds__(kWG) void k_cast_tensor(const T* __restrict__ x, in
 {
     __shared__ float lds[4];
     constexpr int E = In<T>::kE, U = 64 * E;
+    const int lane = threadIdx.x & 63;
+    const int64_t nunits = n / U;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    // the first step's loads go out before the scale is resolved, so the
+    // partials' round trip overlaps them
+    u32x4 v[kLoads];
+    int64_t u0 = wave * kLoads;
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j)
+        v[j] = (u0 + j < nunits) ? ld16_stream(x + (u0 + j) * U + lane * E) : u32x4{0u, 0u, 0u, 0u};
     float alpha, s, a;
     resolve_scale<FMT>(src, lds, alpha, s, a);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -95,16 +106,13 @@ __global__ __launch_bounds__(kWG) void k_cast_tensor(const T* __restrict__ x, in
             *amax_out = a;
     }
     const bool want_amax = partials_out != nullptr;
-    const int lane = threadIdx.x & 63;
-    const int64_t nunits = n / U;
-    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int64_t nwaves = (int64_t)gridDim.x * 4;
     float m = 0.0f;
-    for (int64_t u0 = wave * kLoads; u0 < nunits; u0 += nwaves * kLoads) {
-        u32x4 v[kLoads];
+    for (; u0 < nunits; u0 += nwaves * kLoads) {
+        if (u0 != wave * kLoads) {
 #pragma unroll
-        for (int j = 0; j < kLoads; ++j)
-            v[j] = (u0 + j < nunits) ? ld16_stream(x + (u0 + j) * U + lane * E) : u32x4{0u, 0u, 0u, 0u};
+            for (int j = 0; j < kLoads; ++j)
+                v[j] = (u0 + j < nunits) ? ld16_stream(x + (u0 + j) * U + lane * E) : u32x4{0u, 0u, 0u, 0u};
+        }
 #pragma unroll
         for (int j = 0; j < kLoads; ++j) {
             if (u0 + j < nunits) {

@@ -100,14 +100,18 @@ hipError_t launch_nvfp4(const void* x, int in_bf16, int64_t R, int64_t C, int br
                         uint8_t* codes, uint8_t* pt, uint8_t* codest, float* S_out, float* amax_out,
                         hipStream_t stream);
 
-// Dequantization to fp32.
-hipError_t launch_dequant_tensor(const uint8_t* q, int fmt, int64_t n, const float* s, float* y,
+// MXFP8 colwise copy (transposed codes and E8M0 codes) from the rowwise copy.
+hipError_t launch_mx_requant(const uint8_t* q, const uint8_t* e, int64_t R, int64_t C, uint8_t* qt, uint8_t* et,
+                             hipStream_t stream);
+
+// Dequantization to fp32 (bf = 0) or bf16 (bf = 1).
+hipError_t launch_dequant_tensor(const uint8_t* q, int fmt, int64_t n, const float* s, void* y, int bf,
                                  hipStream_t stream);
-hipError_t launch_dequant_block(const uint8_t* q, const float* s, int64_t R, int64_t C, int br, int bc, float* y,
-                                hipStream_t stream);
-hipError_t launch_dequant_mx(const uint8_t* q, const uint8_t* e, int64_t R, int64_t C, float* y,
+hipError_t launch_dequant_block(const uint8_t* q, const float* s, int64_t R, int64_t C, int br, int bc, void* y,
+                                int bf, hipStream_t stream);
+hipError_t launch_dequant_mx(const uint8_t* q, const uint8_t* e, int64_t R, int64_t C, void* y, int bf,
                              hipStream_t stream);
 hipError_t launch_dequant_nvfp4(const uint8_t* p, const uint8_t* codes, const float* S, int64_t R, int64_t C,
-                                int br, int bc, float* y, hipStream_t stream);
+                                int br, int bc, void* y, int bf, hipStream_t stream);
 
 }  // namespace fq

@@ -74,7 +74,8 @@ def lib():
         "fq_amax": (ctypes.c_int, [dp, _P, _P, _P, ctypes.c_size_t, _P]),
         "fq_quantize_with_amax": (ctypes.c_int, [dp, _P, _P, qp, _P, ctypes.c_size_t, _P]),
         "fq_quantize_delayed": (ctypes.c_int, [dp, _P, ctypes.POINTER(FqDelayedState), qp, _P, ctypes.c_size_t, _P]),
-        "fq_dequantize": (ctypes.c_int, [dp, qp, ctypes.c_int32, _P, _P]),
+        "fq_dequantize": (ctypes.c_int, [dp, qp, ctypes.c_int32, _P, ctypes.c_int32, _P]),
+        "fq_requantize_transpose": (ctypes.c_int, [dp, qp, qp, _P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -234,5 +235,14 @@ def fq_quantize_delayed(d: FqDesc, x: torch.Tensor, state: DelayedState, out: Qu
 
 
 def fq_dequantize(d: FqDesc, qt: Quantized, which: int, y: torch.Tensor, stream=None):
+    """y (float32 or bfloat16) = the values of plane `which` of qt."""
     q = qt.c()
-    _check(lib().fq_dequantize(ctypes.byref(d), ctypes.byref(q), which, _ptr(y), _stream(stream)), "fq_dequantize")
+    _check(lib().fq_dequantize(ctypes.byref(d), ctypes.byref(q), which, _ptr(y), in_dtype_of(y), _stream(stream)),
+           "fq_dequantize")
+
+
+def fq_requantize_transpose(d: FqDesc, src: Quantized, dst: Quantized, stream=None):
+    """MXFP8: dst's colwise planes from src's rowwise planes (no bf16 source)."""
+    a, b = src.c(), dst.c()
+    _check(lib().fq_requantize_transpose(ctypes.byref(d), ctypes.byref(a), ctypes.byref(b), _stream(stream)),
+           "fq_requantize_transpose")

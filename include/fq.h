@@ -237,15 +237,32 @@ fq_status fq_quantize_delayed(const fq_desc *desc, const void *x, const fq_delay
                               hipStream_t stream);
 
 /*
- * y = the fp32 values that `in` represents ([CS] "Current Scaling": the code
- * value times s), for the plane `which` (FQ_ROWWISE or FQ_COLWISE): y has the
- * shape of that plane's data in elements ([rows, cols] or [cols, rows]).
+ * y = the values that `in` represents ([CS] "Current Scaling": the code value
+ * times s), for the plane `which` (FQ_ROWWISE or FQ_COLWISE): y has the shape
+ * of that plane's data in elements ([rows, cols] or [cols, rows]), element
+ * type y_dtype (FQ_IN_F32 or FQ_IN_BF16), 16-byte aligned device memory.
  *   per-tensor: dec(q) * s;  block: dec(q) * s_tile;
  *   MX: dec(q) * 2^(code-127);  NVFP4: dec(q) * fp32(dec(c_block) * S).
- * Every product is one fp32 multiply, rounded to nearest even.
+ * Every product is one fp32 multiply, rounded to nearest even; bf16 output
+ * rounds that fp32 value to nearest even once more.
  */
-fq_status fq_dequantize(const fq_desc *desc, const fq_quantized *in, int32_t which, float *y,
+fq_status fq_dequantize(const fq_desc *desc, const fq_quantized *in, int32_t which, void *y, int32_t y_dtype,
                         hipStream_t stream);
+
+/*
+ * The colwise copy from the rowwise copy alone: de-quantize in->rowwise and
+ * re-quantize in the other direction into out->colwise ([MP] section "FP8
+ * 通信": the expert-parallel backward pass receives only rowwise FP8 data and
+ * needs the colwise copy). Recipe FQ_MX only: its power-of-two scales restore
+ * the values exactly, so the result is the MX recipe applied down the columns
+ * of those restored values (32x1 blocks, stored transposed: codes [cols,
+ * rows], E8M0 codes [cols, rows/32]). It equals quantizing the original
+ * tensor down the columns except where an element is subnormal or saturated
+ * in one of the two scalings. Requires rows % 32 == 0 and cols % 32 == 0.
+ * desc->outputs is ignored. Reads one code byte and writes one per element.
+ */
+fq_status fq_requantize_transpose(const fq_desc *desc, const fq_quantized *in, const fq_quantized *out,
+                                  hipStream_t stream);
 
 /* A static, human-readable name for a status code. */
 const char *fq_status_str(fq_status status);

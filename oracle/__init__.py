@@ -88,6 +88,8 @@ def _load():
                                               _p, _p, _p, _p, _fp, _fp]),
         "orc_quantize_nvfp4_with_amax": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, ctypes.c_int, ctypes.c_int,
                                                         _u32, _f32, _p, _p, _p, _p, _fp, _fp]),
+        "orc_f32_to_bf16_array": (None, [_p, _i64, _p]),
+        "orc_requant_mx_colwise": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p]),
         "orc_dequant_tensor": (None, [_p, _i64, ctypes.c_int, _f32, _p]),
         "orc_dequant_block": (None, [_p, _p, _i64, _i64, ctypes.c_int, ctypes.c_int, _p]),
         "orc_dequant_mx": (None, [_p, _p, _i64, _i64, _p]),
@@ -341,3 +343,23 @@ def dequant_nvfp4(p, codes, S, block):
     _load().orc_dequant_nvfp4(p.ctypes.data, codes.ctypes.data, float(np.float32(S)), R, C2 * 2, block[0], block[1],
                               y.ctypes.data)
     return y.reshape(R, C2 * 2)
+
+
+def f32_to_bf16(y):
+    """fp32 -> bf16 bit patterns (uint16), round to nearest even."""
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    out = np.empty(y.shape, np.uint16)
+    _load().orc_f32_to_bf16_array(y.ctypes.data, y.size, out.ctypes.data)
+    return out
+
+
+def requant_mx_colwise(q_row, e_row):
+    """MXFP8 colwise copy (codes [C,R], E8M0 [C,R/32]) from the rowwise copy alone."""
+    q_row = np.ascontiguousarray(q_row, dtype=np.uint8)
+    e_row = np.ascontiguousarray(e_row, dtype=np.uint8)
+    R, C = q_row.shape
+    q_col = np.empty(R * C, np.uint8)
+    e_col = np.empty(C * (R // 32), np.uint8)
+    _check(_load().orc_requant_mx_colwise(q_row.ctypes.data, e_row.ctypes.data, R, C, q_col.ctypes.data,
+                                          e_col.ctypes.data), "requant_mx_colwise")
+    return dict(q_col=q_col.reshape(C, R), e_col=e_col.reshape(C, R // 32))

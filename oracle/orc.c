@@ -709,3 +709,52 @@ void orc_dequant_nvfp4(const uint8_t *p, const uint8_t *codes, float S, int64_t 
             y[r * C + c] = (float)orc_decode(ORC_E2M1, nib) * d;
         }
 }
+
+/* ------------------------------------------------------------------ */
+/* bf16 output and requantization                                      */
+/* ------------------------------------------------------------------ */
+
+/* fp32 -> bf16 bits, rounded to nearest even (the top 16 bits of the fp32
+ * pattern after adding half an ulp of bf16 with ties to even). Finite inputs;
+ * a NaN keeps a quiet NaN pattern. */
+uint16_t orc_f32_to_bf16(float f)
+{
+    uint32_t b;
+    memcpy(&b, &f, 4);
+    if ((b & 0x7fffffffu) > 0x7f800000u)
+        return (uint16_t)((b >> 16) | 0x40u);
+    uint32_t lsb = (b >> 16) & 1u;
+    b += 0x7fffu + lsb;
+    return (uint16_t)(b >> 16);
+}
+
+void orc_f32_to_bf16_array(const float *y, int64_t n, uint16_t *out)
+{
+    int64_t i;
+    for (i = 0; i < n; i++)
+        out[i] = orc_f32_to_bf16(y[i]);
+}
+
+/*
+ * MXFP8 "de-quantize and re-quantize in the other direction" ([MP] section
+ * "FP8 通信", the EP backward step): from the rowwise copy alone (codes and
+ * E8M0 codes of 1x32 blocks), restore the fp32 values
+ * x_hat = dec(q) * 2^(code-127), and quantize x_hat^T with the MX recipe, i.e.
+ * 32x1 blocks down the columns, stored transposed. Power-of-two scales make
+ * the restored values exact in fp32.
+ */
+int orc_requant_mx_colwise(const uint8_t *q_row, const uint8_t *e_row, int64_t R, int64_t C, uint8_t *q_col,
+                           uint8_t *e_col)
+{
+    float *xhat, *xt;
+    if (R <= 0 || C <= 0 || C % 32 || R % 32)
+        return -3;
+    xhat = (float *)malloc(sizeof(float) * (size_t)(R * C));
+    orc_dequant_mx(q_row, e_row, R, C, xhat);
+    xt = (float *)malloc(sizeof(float) * (size_t)(R * C));
+    transpose_f32(xhat, R, C, xt);
+    mx_rowwise(xt, ORC_IN_F32, C, R, q_col, e_col);
+    free(xt);
+    free(xhat);
+    return 0;
+}

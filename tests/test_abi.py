@@ -30,7 +30,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
     assert {"fq_sizes", "fq_quantize", "fq_amax", "fq_quantize_with_amax", "fq_quantize_delayed",
-            "fq_dequantize", "fq_status_str"} <= set(names)
+            "fq_dequantize", "fq_requantize_transpose", "fq_status_str"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -155,7 +155,27 @@ def test_delayed_and_amax_checks(L):
 def test_dequantize_checks(L):
     d = fq.desc(fq.FQ_MX, fq.FQ_IN_BF16, fq.FQ_E4M3, 64, 64, (1, 32), fq.FQ_ROWWISE)
     q = fq.FqQuantized(fq.FqPlane(B, B), fq.FqPlane(None, None), None, None)
-    assert L.fq_dequantize(ctypes.byref(d), ctypes.byref(q), 3, B, None) == fq.FQ_E_INVALID
-    assert L.fq_dequantize(ctypes.byref(d), ctypes.byref(q), fq.FQ_COLWISE, B, None) == fq.FQ_E_INVALID
-    assert L.fq_dequantize(ctypes.byref(d), ctypes.byref(q), fq.FQ_ROWWISE, None, None) == fq.FQ_E_INVALID
-    assert L.fq_dequantize(ctypes.byref(d), ctypes.byref(q), fq.FQ_ROWWISE, B + 4, None) == fq.FQ_E_ALIGN
+    assert L.fq_dequantize(ctypes.byref(d), ctypes.byref(q), 3, B, 0, None) == fq.FQ_E_INVALID
+    assert L.fq_dequantize(ctypes.byref(d), ctypes.byref(q), fq.FQ_COLWISE, B, 0, None) == fq.FQ_E_INVALID
+    assert L.fq_dequantize(ctypes.byref(d), ctypes.byref(q), fq.FQ_ROWWISE, None, 0, None) == fq.FQ_E_INVALID
+    assert L.fq_dequantize(ctypes.byref(d), ctypes.byref(q), fq.FQ_ROWWISE, B + 4, 0, None) == fq.FQ_E_ALIGN
+    assert L.fq_dequantize(ctypes.byref(d), ctypes.byref(q), fq.FQ_ROWWISE, B, 2, None) == fq.FQ_E_INVALID
+
+
+def test_requantize_checks(L):
+    ok = fq.FqQuantized(fq.FqPlane(B, B), fq.FqPlane(B, B), None, None)
+    d = fq.desc(fq.FQ_MX, fq.FQ_IN_BF16, fq.FQ_E4M3, 64, 64, (1, 32), fq.FQ_ROWWISE)
+    assert L.fq_requantize_transpose(None, ctypes.byref(ok), ctypes.byref(ok), None) == fq.FQ_E_INVALID
+    assert L.fq_requantize_transpose(ctypes.byref(d), None, ctypes.byref(ok), None) == fq.FQ_E_INVALID
+    for bad in (fq.desc(fq.FQ_BLOCK_FP32, fq.FQ_IN_BF16, fq.FQ_E4M3, 128, 128, (1, 128)),
+                fq.desc(fq.FQ_NVFP4, fq.FQ_IN_BF16, fq.FQ_E2M1, 64, 64, (1, 16)),
+                fq.desc(fq.FQ_MX, fq.FQ_IN_BF16, fq.FQ_E5M2, 64, 64, (1, 32))):
+        assert L.fq_requantize_transpose(ctypes.byref(bad), ctypes.byref(ok), ctypes.byref(ok), None) \
+            == fq.FQ_E_UNSUPPORTED
+    d48 = fq.desc(fq.FQ_MX, fq.FQ_IN_BF16, fq.FQ_E4M3, 48, 64, (1, 32), fq.FQ_ROWWISE)
+    assert L.fq_requantize_transpose(ctypes.byref(d48), ctypes.byref(ok), ctypes.byref(ok), None) == fq.FQ_E_SHAPE
+    mis = fq.FqQuantized(fq.FqPlane(B, B + 1), fq.FqPlane(B, B), None, None)
+    assert L.fq_requantize_transpose(ctypes.byref(d), ctypes.byref(mis), ctypes.byref(ok), None) == fq.FQ_E_ALIGN
+    nocol = fq.FqQuantized(fq.FqPlane(B, B), fq.FqPlane(None, None), None, None)
+    assert L.fq_requantize_transpose(ctypes.byref(d), ctypes.byref(ok), ctypes.byref(nocol), None) \
+        == fq.FQ_E_INVALID

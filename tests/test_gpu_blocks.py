@@ -28,14 +28,21 @@ def run(recipe, fmt, x, block, outputs, amax_in=None):
 
 
 def dequant_check(d, out, want_fn):
+    """fp32 and bf16 dequantization of every selected plane vs the oracle
+    (bf16: the oracle's fp32 values rounded to nearest even)."""
     for which in (fq.FQ_ROWWISE, fq.FQ_COLWISE):
         if not d.outputs & which:
             continue
         shape = (d.rows, d.cols) if which == fq.FQ_ROWWISE else (d.cols, d.rows)
+        want = want_fn(which)
         y = torch.empty(shape, dtype=torch.float32, device="cuda")
         fq.fq_dequantize(d, out, which, y)
+        yb = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+        fq.fq_dequantize(d, out, which, yb)
         torch.cuda.synchronize()
-        same_bytes(host(y), want_fn(which), f"dequantized {'rowwise' if which == 1 else 'colwise'}")
+        name = "rowwise" if which == 1 else "colwise"
+        same_bytes(host(y), want, f"dequantized {name} fp32")
+        same_bytes(host(yb.view(torch.int16)).view(np.uint16), orc.f32_to_bf16(want), f"dequantized {name} bf16")
 
 
 # ---------------------------------------------------------------- blockwise
@@ -201,3 +208,40 @@ def test_dequant_per_tensor(fmt):
     ofmt = orc.E4M3 if fmt == fq.FQ_E4M3 else orc.E5M2
     want = orc.quantize_current(x, ofmt, outputs=BOTH)
     dequant_check(d, out, lambda w: orc.dequant_tensor(want["q_row"] if w == 1 else want["q_col"], ofmt, want["s"]))
+
+
+# ---------------------------------------------------------------- MX requantize (rowwise -> colwise)
+def check_requant(x):
+    R, C = x.shape
+    d, out = run(fq.FQ_MX, fq.FQ_E4M3, x, (1, 32), fq.FQ_ROWWISE)
+    dst = fq.alloc_quantized(fq.desc(fq.FQ_MX, fq.FQ_IN_BF16, fq.FQ_E4M3, R, C, (1, 32), fq.FQ_COLWISE))
+    fq.fq_requantize_transpose(d, out, dst)
+    torch.cuda.synchronize()
+    want = orc.requant_mx_colwise(host(out.row_data), host(out.row_scale).reshape(R, C // 32))
+    same_bytes(host(dst.col_data), want["q_col"], "requantized colwise codes")
+    same_bytes(host(dst.col_scale), want["e_col"], "requantized colwise E8M0")
+
+
+@pytest.mark.parametrize("shape", [(32, 32), (64, 96), (96, 64), (160, 288), (256, 384)])
+def test_mx_requant_small(shape):
+    check_requant(W.student_t(shape, 3.0, shape[0] * 7 + shape[1], W.BF16))
+
+
+def test_mx_requant_wide_range():
+    check_requant(W.uniform_bits_bf16((256, 256), 13, max_abs=3e38))
+    check_requant(np.zeros((64, 64), np.uint16))
+
+
+@pytest.mark.parametrize("w", [w for w in W.LARGE if w.recipe == "mx"], ids=lambda w: w.name)
+def test_full_size_mx_requant(w):
+    check_requant(w.make())
+
+
+@pytest.mark.parametrize("shape", [(1, 37), (3, 1000), (257, 129)])
+@pytest.mark.parametrize("fmt", [fq.FQ_E4M3, fq.FQ_E5M2])
+def test_dequant_per_tensor_ragged(shape, fmt):
+    x = W.normal(shape, 3.0, shape[0] + 17 * shape[1], W.F32)
+    d, out = run(fq.FQ_PER_TENSOR_CURRENT, fmt, x, (0, 0), fq.FQ_ROWWISE)
+    ofmt = orc.E4M3 if fmt == fq.FQ_E4M3 else orc.E5M2
+    want = orc.quantize_current(x, ofmt)
+    dequant_check(d, out, lambda w: orc.dequant_tensor(want["q_row"], ofmt, want["s"]))

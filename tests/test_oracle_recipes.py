@@ -393,3 +393,56 @@ def test_nvfp4_nibble_order(orc):
 def test_nvfp4_zero_tensor(orc):
     r = orc.quantize_nvfp4(np.zeros((16, 32), np.float32), (16, 16))
     assert r["S"] == 1.0 and not r["p_row"].any() and not r["c_row"].any()
+
+
+# ------------------------------------------------------------ bf16 output, MX requantization
+def test_f32_to_bf16_matches_torch(orc):
+    import torch
+    rng = np.random.default_rng(31)
+    bits = rng.integers(0, 2 ** 32, size=1 << 20, dtype=np.uint64).astype(np.uint32)
+    y = bits.view(np.float32)
+    y = y[np.isfinite(y)]
+    # values just below the bf16 overflow threshold round to the largest bf16 or to inf, as torch does
+    ref = torch.from_numpy(y).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(orc.f32_to_bf16(y), ref)
+    ties = (np.arange(1, 4096, dtype=np.uint32) << 16 | 0x8000).view(np.float32)
+    ref = torch.from_numpy(ties).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(orc.f32_to_bf16(ties), ref)
+
+
+def test_mx_requant_equals_single_quantization_where_exact(orc):
+    """[MP] "FP8 通信": with power-of-two scales, de-quantizing the rowwise copy
+    and re-quantizing it down the columns gives the same bytes as quantizing
+    the source down the columns, except for special values such as
+    subnormals. Precisely: when an element's column block gets the same code
+    both ways and its scaled value is a normal, unsaturated E4M3 value in
+    both the row scaling and the column scaling, the codes are equal."""
+    R, C = 96, 128
+    x = W.student_t((R, C), 3.0, 61, W.BF16)
+    xf = W.bf16_bits_to_f32(x).reshape(R, C)
+    single = orc.quantize_mx(x)                      # colwise from the source
+    rq = orc.requant_mx_colwise(single["q_row"], single["e_row"])
+    q1, q2 = single["q_col"], rq["q_col"]            # both [C, R]
+    c1 = np.repeat(single["e_col"].astype(np.int64), 32, axis=1)
+    c2 = np.repeat(rq["e_col"].astype(np.int64), 32, axis=1)
+    er = np.repeat(single["e_row"].astype(np.int64), 32, axis=1).T   # row-block code of each element, [C, R]
+    xt = np.abs(xf.T).astype(np.float64)
+    y_row = xt * 2.0 ** (127 - er)
+    y_col = xt * 2.0 ** (127 - c1)
+    exact = (c1 == c2) & (y_row >= 2.0 ** -6) & (y_col >= 2.0 ** -6) & (y_row <= 448) & (y_col <= 448)
+    assert exact.mean() > 0.8
+    assert np.array_equal(q1[exact], q2[exact])
+    # and the codes agree for almost every element overall
+    assert (q1 == q2).mean() > 0.9
+
+
+def test_mx_requant_error_bound(orc):
+    x = W.normal((64, 64), 1.0, 62, W.BF16)
+    single = orc.quantize_mx(x)
+    rq = orc.requant_mx_colwise(single["q_row"], single["e_row"])
+    xhat = orc.dequant_mx(single["q_row"], single["e_row"]).T       # restored values, transposed
+    back = orc.dequant_mx(rq["q_col"], rq["e_col"])
+    scale = np.repeat(np.exp2(rq["e_col"].astype(np.float64) - 127), 32, axis=1)
+    ys = np.abs(xhat) / scale
+    ok = (ys >= 2.0 ** -6) & (ys <= 448)
+    assert (np.abs(back - xhat)[ok] / np.abs(xhat)[ok]).max() <= 2.0 ** -4 * (1 + 1e-6)
