@@ -153,8 +153,9 @@ def plane_bytes(w, which):
 
 
 def time_extras(torch, fq, L, stream_p, jobs, steps):
-    """Dequantize (rowwise plane to bf16) and MXFP8 rowwise-to-colwise requantize at
-    the large workloads' shapes, each call bracketed by events; not part of the step."""
+    """Dequantize (rowwise plane to bf16), MXFP8 rowwise-to-colwise requantize and
+    NVFP4 1x16 with stochastic rounding at the large workloads' shapes, each call
+    bracketed by events; not part of the step."""
     out = {}
     for j in jobs:
         w = j["w"]
@@ -176,6 +177,24 @@ def time_extras(torch, fq, L, stream_p, jobs, steps):
         out["dequant_bf16/" + w.name] = {"us_per_call": round(us, 2), "bytes": nbytes,
                                          "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1)}
         del y
+        if w.recipe == "nvfp4" and tuple(w.block) == (1, 16):
+            # the same workload with stochastically rounded elements (a gradient)
+            d = j["d"]
+            dsr = fq.desc(d.recipe, d.in_dtype, d.format, R, C, (1, 16), d.outputs,
+                          rounding=fq.FQ_ROUND_STOCHASTIC, seed=2024, offset=0)
+            for k in range(-1, steps):
+                dsr.offset = k + 1
+                if k >= 0:
+                    ev[k][0].record()
+                rc = L.fq_quantize(ctypes.byref(dsr), j["xp"], ctypes.byref(j["cq"]), j["wsp"], j["wsn"], stream_p)
+                if k >= 0:
+                    ev[k][1].record()
+                if rc != fq.FQ_OK:
+                    raise fq.FqError(rc, "stochastic rounding " + w.name)
+            torch.cuda.synchronize()
+            us = 1e3 * sum(a.elapsed_time(b) for a, b in ev) / steps
+            out["nvfp4_1x16_sr/" + w.name] = {"us_per_call": round(us, 2), "bytes": j["bytes"],
+                                              "GB/s": round(j["bytes"] / (us * 1e-6) / 1e9, 1)}
         if w.recipe == "mx":
             d = fq.desc(fq.FQ_MX, fq.FQ_IN_BF16, fq.FQ_E4M3, R, C, (1, 32), fq.FQ_COLWISE)
             dst = fq.alloc_quantized(d)

@@ -38,6 +38,13 @@ fq_status check_desc(const fq_desc* d)
         return FQ_E_INVALID;
     if (d->cols > 0 && d->rows > kMaxElems / d->cols)
         return FQ_E_SHAPE;
+    if (d->rounding != FQ_ROUND_NEAREST_EVEN && d->rounding != FQ_ROUND_STOCHASTIC)
+        return FQ_E_INVALID;
+    if (d->scale_mode != FQ_SCALE_DEFAULT)
+        return FQ_E_INVALID;
+    if (d->rounding == FQ_ROUND_STOCHASTIC &&
+        !(d->recipe == FQ_NVFP4 && d->block_rows == 1 && d->block_cols == 16))
+        return FQ_E_UNSUPPORTED;
     const bool col = (d->outputs & FQ_COLWISE) != 0;
     const int64_t R = d->rows, C = d->cols;
     const int br = d->block_rows, bc = d->block_cols;
@@ -75,6 +82,15 @@ fq_status check_desc(const fq_desc* d)
         return FQ_OK;
     }
     return FQ_E_INVALID;
+}
+
+SrArgs sr_of(const fq_desc* d)
+{
+    SrArgs sr;
+    sr.on = d->rounding == FQ_ROUND_STOCHASTIC;
+    sr.seed = d->seed;
+    sr.offset = d->offset;
+    return sr;
 }
 
 struct Sizes {
@@ -326,7 +342,8 @@ fq_status fq_quantize(const fq_desc* d, const void* x, const fq_quantized* o, vo
         return hip_status(launch_nvfp4(x, bf, R, C, d->block_rows, src, row ? (uint8_t*)o->rowwise.data : nullptr,
                                        row ? (uint8_t*)o->rowwise.scale : nullptr,
                                        col ? (uint8_t*)o->colwise.data : nullptr,
-                                       col ? (uint8_t*)o->colwise.scale : nullptr, o->tensor_scale, o->amax, st));
+                                       col ? (uint8_t*)o->colwise.scale : nullptr, o->tensor_scale, o->amax,
+                                       sr_of(d), st));
     }
     }
     return FQ_E_INVALID;
@@ -359,7 +376,8 @@ fq_status fq_quantize_with_amax(const fq_desc* d, const void* x, const float* am
                                    row ? (uint8_t*)o->rowwise.data : nullptr,
                                    row ? (uint8_t*)o->rowwise.scale : nullptr,
                                    col ? (uint8_t*)o->colwise.data : nullptr,
-                                   col ? (uint8_t*)o->colwise.scale : nullptr, o->tensor_scale, o->amax, st));
+                                   col ? (uint8_t*)o->colwise.scale : nullptr, o->tensor_scale, o->amax,
+                                   sr_of(d), st));
 }
 
 fq_status fq_quantize_delayed(const fq_desc* d, const void* x, const fq_delayed_state* state,
@@ -446,7 +464,12 @@ fq_status fq_requantize_transpose(const fq_desc* d, const fq_quantized* in, cons
         return FQ_E_INVALID;
     if (d->recipe < FQ_PER_TENSOR_CURRENT || d->recipe > FQ_NVFP4 || d->rows < 0 || d->cols < 0)
         return FQ_E_INVALID;
-    if (d->recipe != FQ_MX || d->format != FQ_E4M3 || d->block_rows != 1 || d->block_cols != 32)
+    if (d->rounding != FQ_ROUND_NEAREST_EVEN && d->rounding != FQ_ROUND_STOCHASTIC)
+        return FQ_E_INVALID;
+    if (d->scale_mode != FQ_SCALE_DEFAULT)
+        return FQ_E_INVALID;
+    if (d->recipe != FQ_MX || d->format != FQ_E4M3 || d->block_rows != 1 || d->block_cols != 32 ||
+        d->rounding != FQ_ROUND_NEAREST_EVEN)
         return FQ_E_UNSUPPORTED;
     if (d->cols > 0 && d->rows > kMaxElems / d->cols)
         return FQ_E_SHAPE;

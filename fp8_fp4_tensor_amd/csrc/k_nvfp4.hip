@@ -27,6 +27,10 @@
 //                  1x16 -> blocks of 16 rows of one column; 16x16 -> the same
 //                  blocks as rowwise (max also across 16 neighbouring lanes),
 //                  so the colwise nibbles are the rowwise ones transposed.
+//   k_nvfp4_1x16_sr  stochastic rounding of the elements ([MP] "NVFP4"; [LP]
+//                  2.4 item 5): a lane owns a whole 1x16 block, which is one
+//                  Philox4x64-10 call (16 x 16 random bits); the colwise
+//                  kernel takes the same path per 16-row block.
 #include <algorithm>
 
 #include "codec.hpp"
@@ -81,6 +85,115 @@ struct Fp4Store<4> {
         *reinterpret_cast<uint16_t*>(p) = (uint16_t)w;
     }
 };
+
+// ---------------------------------------------------------------- stochastic rounding
+// Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC 2011): the published multipliers and Weyl constants.
+constexpr uint64_t kPhM0 = 0xD2E7470EE14C6C93ull, kPhM1 = 0xCA5A826395121157ull;
+constexpr uint64_t kPhW0 = 0x9E3779B97F4A7C15ull, kPhW1 = 0xBB67AE8584CAA73Bull;
+
+struct Philox4 {
+    uint64_t w[4];
+};
+
+__device__ __forceinline__ Philox4 philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3, uint64_t k0,
+                                                 uint64_t k1)
+{
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+        const uint64_t lo0 = kPhM0 * c0, hi0 = __umul64hi(kPhM0, c0);
+        const uint64_t lo1 = kPhM1 * c2, hi1 = __umul64hi(kPhM1, c2);
+        c0 = hi1 ^ c1 ^ k0;
+        c1 = lo1;
+        c2 = hi0 ^ c3 ^ k1;
+        c3 = lo0;
+        k0 += kPhW0;
+        k1 += kPhW1;
+    }
+    return Philox4{{c0, c1, c2, c3}};
+}
+
+// the 16 random bits of element j (0..15) of a Philox block
+__device__ __forceinline__ uint32_t sr_u16(const Philox4& ph, int j)
+{
+    return (uint32_t)(ph.w[j >> 2] >> (16 * (j & 3))) & 0xFFFFu;
+}
+
+// Stochastic rounding of y to E2M1: the result is an E2M1 value (exact in
+// fp32) with y's sign. With v = min(|y|, 6) and q the E2M1 spacing at v
+// (0.5 below 2, 1 on [2, 4), 2 on [4, 6]), t = v/q splits exactly into the
+// count of whole spacings and the fraction g = (v - lo)/q; the value goes up
+// one spacing iff u < g * 2^16 (all steps exact: powers of two and fract).
+__device__ __forceinline__ float sr_e2m1(float y, uint32_t u)
+{
+    const float v = fminf(fabsf(y), 6.0f);
+    const int e = __builtin_amdgcn_frexp_expf(v);  // v = m * 2^e, m in [0.5, 1)
+    const int sh = 2 - max(e, 1);                   // 1/q = 2^sh
+    const float t = ldexpf(v, sh);
+    const float g = __builtin_amdgcn_fractf(t);
+    const float n = ((float)u < g * 65536.0f) ? (t - g) + 1.0f : (t - g);
+    return copysignf(ldexpf(n, -sh), y);
+}
+
+// 8 values (times r, stochastically rounded) -> one dword of packed E2M1;
+// random bits j0 .. j0+7 of the block
+__device__ __forceinline__ uint32_t enc8_e2m1_sr(const float* f, float r, const Philox4& ph, int j0)
+{
+    uint32_t w = 0;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, sr_e2m1(f[0] * r, sr_u16(ph, j0)),
+                                                 sr_e2m1(f[1] * r, sr_u16(ph, j0 + 1)), 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, sr_e2m1(f[2] * r, sr_u16(ph, j0 + 2)),
+                                                 sr_e2m1(f[3] * r, sr_u16(ph, j0 + 3)), 1.0f, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, sr_e2m1(f[4] * r, sr_u16(ph, j0 + 4)),
+                                                 sr_e2m1(f[5] * r, sr_u16(ph, j0 + 5)), 1.0f, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, sr_e2m1(f[6] * r, sr_u16(ph, j0 + 6)),
+                                                 sr_e2m1(f[7] * r, sr_u16(ph, j0 + 7)), 1.0f, 3);
+    return w;
+}
+
+// Rowwise 1x16 with stochastic rounding: thread = block of 16 elements
+// (two 16-byte loads of bf16, four of fp32), grid-stride over blocks, the
+// next block's loads issued before the current block's arithmetic.
+template <typename T>
+__global__ __launch_bounds__(kWG) void k_nvfp4_1x16_sr(const T* __restrict__ x, int64_t nblk, ScaleSrc src,
+                                                       uint64_t seed, uint64_t offset, uint8_t* __restrict__ p,
+                                                       uint8_t* __restrict__ codes, float* S_out, float* amax_out)
+{
+    __shared__ float lds[4];
+    constexpr int E = In<T>::kE, NL = 16 / E;
+    const int64_t first = (int64_t)blockIdx.x * kWG + threadIdx.x, stride = (int64_t)gridDim.x * kWG;
+    u32x4 v[NL];
+#pragma unroll
+    for (int k = 0; k < NL; ++k)
+        v[k] = first < nblk ? ld16_stream(x + first * 16 + k * E) : u32x4{0u, 0u, 0u, 0u};
+    float alpha_s, S, A;
+    nvfp4_tensor(src, lds, alpha_s, S, A);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (S_out)
+            *S_out = S;
+        if (amax_out)
+            *amax_out = A;
+    }
+    for (int64_t b = first; b < nblk; b += stride) {
+        float f[16];
+#pragma unroll
+        for (int k = 0; k < NL; ++k)
+            In<T>::unpack(v[k], f + k * E);
+        const int64_t nb = b + stride;
+#pragma unroll
+        for (int k = 0; k < NL; ++k)
+            v[k] = nb < nblk ? ld16_stream(x + nb * 16 + k * E) : u32x4{0u, 0u, 0u, 0u};
+        uint32_t code;
+        float r;
+        nvfp4_block(absmax<16>(f), alpha_s, S, code, r);
+        const Philox4 ph = philox4x64_10((uint64_t)b, offset, 0, 0, seed, 0);
+        u32x2 out;
+        out[0] = enc8_e2m1_sr(f, r, ph, 0);
+        out[1] = enc8_e2m1_sr(f + 8, r, ph, 8);
+        st8_stream(p + b * 8, out);
+        codes[b] = (uint8_t)code;
+    }
+}
 
 template <typename T>
 __global__ __launch_bounds__(kWG) void k_nvfp4_1x16(const T* __restrict__ x, int64_t n, ScaleSrc src,
@@ -185,10 +298,11 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_16x16(const T* __restrict__ x, in
 
 // Colwise copy. BR = 1: 1x16 blocks of X^T (16 rows of a column);
 // BR = 16: 16x16 blocks. Slab of 32 rows x 256 columns in LDS.
-template <typename T, int BR>
+template <typename T, int BR, bool SR = false>
 __global__ __launch_bounds__(kWG) void k_nvfp4_col(const T* __restrict__ x, int64_t R, int64_t C, ScaleSrc src,
                                                    uint8_t* __restrict__ pt, uint8_t* __restrict__ ct,
-                                                   float* S_out, float* amax_out)
+                                                   float* S_out, float* amax_out, uint64_t seed = 0,
+                                                   uint64_t offset = 0)
 {
     __shared__ float lds[4];
     constexpr int TC = 256, E = In<T>::kE, LPR = TC / E, RPR = kWG / LPR;
@@ -227,8 +341,16 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_col(const T* __restrict__ x, int6
         uint32_t code;
         float r;
         nvfp4_block(a, alpha_s, S, code, r);
-        w[2 * b] = enc8_e2m1(f, r);
-        w[2 * b + 1] = enc8_e2m1(f + 8, r);
+        if constexpr (SR) {
+            // element (c, r0 + 16b + k) of X^T: group (c0+c)*(R/16) + r0/16 + b, plane 1
+            const uint64_t g = (uint64_t)((c0 + c) * (R / 16) + r0 / 16 + b);
+            const Philox4 ph = philox4x64_10(g, offset, 1, 0, seed, 0);
+            w[2 * b] = enc8_e2m1_sr(f, r, ph, 0);
+            w[2 * b + 1] = enc8_e2m1_sr(f + 8, r, ph, 8);
+        } else {
+            w[2 * b] = enc8_e2m1(f, r);
+            w[2 * b + 1] = enc8_e2m1(f + 8, r);
+        }
         if (in && b < nb) {
             const int64_t rb = (r0 + 16 * b) / 16;
             if constexpr (BR == 1)
@@ -254,13 +376,19 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_col(const T* __restrict__ x, int6
 
 template <typename T>
 void launch_t(const void* xv, int64_t R, int64_t C, int br, ScaleSrc src, uint8_t* p, uint8_t* codes, uint8_t* pt,
-              uint8_t* codest, float* S_out, float* amax_out, hipStream_t stream)
+              uint8_t* codest, float* S_out, float* amax_out, SrArgs sr, hipStream_t stream)
 {
     const T* x = (const T*)xv;
     constexpr int E = In<T>::kE;
     bool wrote_scalars = false;
     if (p) {
-        if (br == 1) {
+        if (sr.on) {
+            const int64_t nblk = R * C / 16;
+            const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(nblk, kWG), kMaxGrid));
+            k_nvfp4_1x16_sr<T><<<grid, kWG, 0, stream>>>(x, nblk, src, sr.seed, sr.offset, p, codes, S_out,
+                                                         amax_out);
+            wrote_scalars = true;
+        } else if (br == 1) {
             const int64_t n = R * C;
             const int64_t per_wg = (int64_t)kWG * E * kLoads;
             const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(n, per_wg), kMaxGrid));
@@ -276,7 +404,10 @@ void launch_t(const void* xv, int64_t R, int64_t C, int br, ScaleSrc src, uint8_
         const int64_t grid = cdiv(R, 32) * cdiv(C, 256);
         float* s2 = wrote_scalars ? nullptr : S_out;
         float* a2 = wrote_scalars ? nullptr : amax_out;
-        if (br == 1)
+        if (sr.on)
+            k_nvfp4_col<T, 1, true><<<(unsigned)grid, kWG, 0, stream>>>(x, R, C, src, pt, codest, s2, a2, sr.seed,
+                                                                        sr.offset);
+        else if (br == 1)
             k_nvfp4_col<T, 1><<<(unsigned)grid, kWG, 0, stream>>>(x, R, C, src, pt, codest, s2, a2);
         else
             k_nvfp4_col<T, 16><<<(unsigned)grid, kWG, 0, stream>>>(x, R, C, src, pt, codest, s2, a2);
@@ -291,13 +422,13 @@ void launch_t(const void* xv, int64_t R, int64_t C, int br, ScaleSrc src, uint8_
 }  // namespace
 
 hipError_t launch_nvfp4(const void* x, int in_bf16, int64_t R, int64_t C, int br, ScaleSrc src, uint8_t* p,
-                        uint8_t* codes, uint8_t* pt, uint8_t* codest, float* S_out, float* amax_out,
+                        uint8_t* codes, uint8_t* pt, uint8_t* codest, float* S_out, float* amax_out, SrArgs sr,
                         hipStream_t stream)
 {
     if (in_bf16)
-        launch_t<uint16_t>(x, R, C, br, src, p, codes, pt, codest, S_out, amax_out, stream);
+        launch_t<uint16_t>(x, R, C, br, src, p, codes, pt, codest, S_out, amax_out, sr, stream);
     else
-        launch_t<float>(x, R, C, br, src, p, codes, pt, codest, S_out, amax_out, stream);
+        launch_t<float>(x, R, C, br, src, p, codes, pt, codest, S_out, amax_out, sr, stream);
     return hipGetLastError();
 }
 

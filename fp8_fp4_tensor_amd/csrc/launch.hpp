@@ -95,9 +95,15 @@ hipError_t launch_block_128x128(const void* x, int in_bf16, int64_t R, int64_t C
 hipError_t launch_mx(const void* x, int in_bf16, int64_t R, int64_t C, uint8_t* q, uint8_t* e, uint8_t* qt,
                      uint8_t* et, hipStream_t stream);
 
-// NVFP4 block pass (after the amax pass): 1x16 or 16x16 blocks.
+// Stochastic rounding of elements: Philox4x64-10 key (seed, 0), counter word 1 = offset.
+struct SrArgs {
+    int on = 0;
+    uint64_t seed = 0, offset = 0;
+};
+
+// NVFP4 block pass (after the amax pass): 1x16 or 16x16 blocks; sr.on only with 1x16.
 hipError_t launch_nvfp4(const void* x, int in_bf16, int64_t R, int64_t C, int br, ScaleSrc src, uint8_t* p,
-                        uint8_t* codes, uint8_t* pt, uint8_t* codest, float* S_out, float* amax_out,
+                        uint8_t* codes, uint8_t* pt, uint8_t* codest, float* S_out, float* amax_out, SrArgs sr,
                         hipStream_t stream);
 
 // MXFP8 colwise copy (transposed codes and E8M0 codes) from the rowwise copy.

@@ -22,6 +22,8 @@ FQ_IN_F32, FQ_IN_BF16 = 0, 1
 FQ_E4M3, FQ_E5M2, FQ_E2M1 = 0, 1, 2
 FQ_PER_TENSOR_CURRENT, FQ_PER_TENSOR_DELAYED, FQ_BLOCK_FP32, FQ_MX, FQ_NVFP4 = range(5)
 FQ_ROWWISE, FQ_COLWISE = 1, 2
+FQ_ROUND_NEAREST_EVEN, FQ_ROUND_STOCHASTIC = 0, 1
+FQ_SCALE_DEFAULT = 0
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfq.so")
 
@@ -29,7 +31,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfq.so")
 class FqDesc(ctypes.Structure):
     _fields_ = [("recipe", ctypes.c_int32), ("in_dtype", ctypes.c_int32), ("format", ctypes.c_int32),
                 ("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("block_rows", ctypes.c_int32),
-                ("block_cols", ctypes.c_int32), ("outputs", ctypes.c_uint32)]
+                ("block_cols", ctypes.c_int32), ("outputs", ctypes.c_uint32), ("rounding", ctypes.c_int32),
+                ("scale_mode", ctypes.c_int32), ("seed", ctypes.c_uint64), ("offset", ctypes.c_uint64)]
 
 
 class FqPlane(ctypes.Structure):
@@ -106,8 +109,10 @@ def _stream(stream) -> ctypes.c_void_p:
 
 # ---------------------------------------------------------------- descriptors
 def desc(recipe: int, in_dtype: int, fmt: int, rows: int, cols: int, block=(0, 0),
-         outputs: int = FQ_ROWWISE) -> FqDesc:
-    return FqDesc(recipe, in_dtype, fmt, rows, cols, block[0], block[1], outputs)
+         outputs: int = FQ_ROWWISE, rounding: int = FQ_ROUND_NEAREST_EVEN, seed: int = 0, offset: int = 0,
+         scale_mode: int = FQ_SCALE_DEFAULT) -> FqDesc:
+    return FqDesc(recipe, in_dtype, fmt, rows, cols, block[0], block[1], outputs, rounding, scale_mode, seed,
+                  offset)
 
 
 def in_dtype_of(x: torch.Tensor) -> int:

@@ -98,6 +98,30 @@ typedef enum {
 enum { FQ_ROWWISE = 1, FQ_COLWISE = 2 };
 
 /*
+ * Element rounding.
+ *   FQ_ROUND_NEAREST_EVEN  every recipe (the default).
+ *   FQ_ROUND_STOCHASTIC    NVFP4 with 1x16 blocks only ([MP] "NVFP4": an
+ *                          option for FP4 values; [LP] section 2.4 item 5:
+ *                          applied to gradients). A scaled value of
+ *                          magnitude v < 6 between neighbouring E2M1 values
+ *                          lo <= v < hi rounds to hi iff u / 2^16 <
+ *                          (v - lo) / (hi - lo), u a 16-bit random number;
+ *                          v >= 6 saturates; block scales stay
+ *                          round-to-nearest-even. u comes from Philox4x64-10
+ *                          (Salmon et al., SC 2011) with key (seed, 0): the
+ *                          element at index e of an output plane (row-major
+ *                          in that plane) uses counter (e/16, offset, plane,
+ *                          0), plane 0 rowwise and 1 colwise, and bits
+ *                          16*(e%4) .. +15 of output word (e%16)/4.
+ *                          Results are a pure function of (input, seed,
+ *                          offset), independent of launch shape.
+ */
+typedef enum { FQ_ROUND_NEAREST_EVEN = 0, FQ_ROUND_STOCHASTIC = 1 } fq_rounding;
+
+/* Scale encoding of FQ_BLOCK_FP32 (other recipes: FQ_SCALE_DEFAULT only). */
+typedef enum { FQ_SCALE_DEFAULT = 0 } fq_scale_mode;
+
+/*
  * What to quantize and how.
  *   recipe, in_dtype, format: the enums above.
  *   rows, cols:               tensor shape, each >= 0, rows*cols < 2^40.
@@ -105,6 +129,9 @@ enum { FQ_ROWWISE = 1, FQ_COLWISE = 2 };
  *                             FQ_MX (1,32); FQ_NVFP4 (1,16) or (16,16);
  *                             ignored by the per-tensor recipes.
  *   outputs:                  FQ_ROWWISE | FQ_COLWISE, at least one.
+ *   rounding, seed, offset:   element rounding (fq_rounding above); seed and
+ *                             offset are read only for FQ_ROUND_STOCHASTIC.
+ *   scale_mode:               fq_scale_mode above.
  *
  * Supported combinations (anything else is FQ_E_UNSUPPORTED):
  *   CURRENT, DELAYED  E4M3 or E5M2, f32 or bf16 input, any shape
@@ -123,6 +150,10 @@ typedef struct {
     int32_t block_rows;
     int32_t block_cols;
     uint32_t outputs;
+    int32_t rounding;   /* fq_rounding */
+    int32_t scale_mode; /* fq_scale_mode */
+    uint64_t seed;      /* stochastic rounding: Philox key word 0 */
+    uint64_t offset;    /* stochastic rounding: counter word 1 (e.g. the step) */
 } fq_desc;
 
 /* One quantized copy: data codes and per-block scales (device memory). */

@@ -88,6 +88,13 @@ def _load():
                                               _p, _p, _p, _p, _fp, _fp]),
         "orc_quantize_nvfp4_with_amax": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, ctypes.c_int, ctypes.c_int,
                                                         _u32, _f32, _p, _p, _p, _p, _fp, _fp]),
+        "orc_quantize_nvfp4_sr_with_amax": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, _u32, _f32,
+                                                           ctypes.c_uint64, ctypes.c_uint64, _p, _p, _p, _p,
+                                                           _fp, _fp]),
+        "orc_philox4x64_10": (None, [_p, _p, _p]),
+        "orc_sr_bits": (_u32, [ctypes.c_uint64, ctypes.c_uint64, _u32, _i64]),
+        "orc_encode_e2m1_sr": (_u32, [_f32, _u32]),
+        "orc_encode_e2m1_sr_array": (None, [_p, _p, _i64, _p]),
         "orc_f32_to_bf16_array": (None, [_p, _i64, _p]),
         "orc_requant_mx_colwise": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p]),
         "orc_dequant_tensor": (None, [_p, _i64, ctypes.c_int, _f32, _p]),
@@ -277,9 +284,10 @@ def quantize_mx(x, outputs=ROWWISE | COLWISE, shape=None):
                 e_col=None if e_col is None else e_col.reshape(C, R // 32))
 
 
-def quantize_nvfp4(x, block, outputs=ROWWISE, shape=None, amax=None):
+def quantize_nvfp4(x, block, outputs=ROWWISE, shape=None, amax=None, sr=None):
     """NVFP4: packed E2M1 pairs, E4M3 block codes and the fp32 tensor scale S.
-    `amax` gives the tensor amax A (default: this tensor's own)."""
+    `amax` gives the tensor amax A (default: this tensor's own).
+    `sr` = (seed, offset) rounds the elements stochastically (1x16 blocks only)."""
     p, dt, keep = _in(x)
     R, C = _shape2(keep, shape)
     br, bc = block
@@ -290,7 +298,14 @@ def quantize_nvfp4(x, block, outputs=ROWWISE, shape=None, amax=None):
     if outputs & COLWISE:
         c_col = np.empty(C * (R // 16) if br == 1 else (C // 16) * (R // 16), np.uint8)
     S, A = ctypes.c_float(), ctypes.c_float()
-    if amax is None:
+    if sr is not None:
+        if block != (1, 16):
+            raise ValueError("stochastic rounding is offered for 1x16 blocks")
+        a = _load().orc_amax(p, dt, R * C) if amax is None else amax
+        rc = _load().orc_quantize_nvfp4_sr_with_amax(p, dt, R, C, outputs, float(np.float32(a)), int(sr[0]),
+                                                     int(sr[1]), _ptr(p_row), _ptr(c_row), _ptr(p_col),
+                                                     _ptr(c_col), ctypes.byref(S), ctypes.byref(A))
+    elif amax is None:
         rc = _load().orc_quantize_nvfp4(p, dt, R, C, br, bc, outputs, _ptr(p_row), _ptr(c_row), _ptr(p_col),
                                         _ptr(c_col), ctypes.byref(S), ctypes.byref(A))
     else:
@@ -307,6 +322,31 @@ def quantize_nvfp4(x, block, outputs=ROWWISE, shape=None, amax=None):
     else:
         out["c_col"] = None
     return out
+
+
+# ---------------------------------------------------------------- stochastic rounding
+def philox4x64_10(counter, key):
+    """Philox4x64-10 of a 4-word counter and a 2-word key (uint64 words)."""
+    c = np.asarray(counter, np.uint64)
+    k = np.asarray(key, np.uint64)
+    out = np.empty(4, np.uint64)
+    _load().orc_philox4x64_10(c.ctypes.data, k.ctypes.data, out.ctypes.data)
+    return out
+
+
+def sr_bits(seed, offset, plane, e):
+    """The 16 random bits of element e of an output plane (0 rowwise, 1 colwise)."""
+    return int(_load().orc_sr_bits(int(seed), int(offset), int(plane), int(e)))
+
+
+def encode_e2m1_sr(y, u):
+    """Stochastically rounded E2M1 codes of fp32 values y with 16-bit randoms u."""
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    u = np.ascontiguousarray(u, dtype=np.uint16)
+    assert y.shape == u.shape
+    q = np.empty(y.size, np.uint8)
+    _load().orc_encode_e2m1_sr_array(y.ctypes.data, u.ctypes.data, y.size, q.ctypes.data)
+    return q.reshape(y.shape)
 
 
 # ---------------------------------------------------------------- dequantize

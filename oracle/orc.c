@@ -548,10 +548,109 @@ static nvfp4_tensor nvfp4_tensor_scale(float A)
     return t;
 }
 
+/* ------------------------------------------------------------------ */
+/* Stochastic rounding                                                 */
+/* ------------------------------------------------------------------ */
+
+/*
+ * Philox4x64-10, the counter-based generator of Salmon, Moraes, Dror and
+ * Shaw, "Parallel random numbers: as easy as 1, 2, 3" (SC 2011): ten rounds
+ * over a 4 x 64-bit counter; each round multiplies counter words 0 and 2 by
+ * the two published 64-bit multipliers (full 128-bit products), and the new
+ * counter is (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0); the 2 x 64-bit key
+ * is bumped by the two published Weyl constants after every round.
+ */
+void orc_philox4x64_10(const uint64_t ctr[4], const uint64_t key[2], uint64_t out[4])
+{
+    uint64_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3], k0 = key[0], k1 = key[1];
+    int round;
+    for (round = 0; round < 10; round++) {
+        unsigned __int128 p0 = (unsigned __int128)0xD2E7470EE14C6C93ULL * c0;
+        unsigned __int128 p1 = (unsigned __int128)0xCA5A826395121157ULL * c2;
+        uint64_t hi0 = (uint64_t)(p0 >> 64), lo0 = (uint64_t)p0;
+        uint64_t hi1 = (uint64_t)(p1 >> 64), lo1 = (uint64_t)p1;
+        c0 = hi1 ^ c1 ^ k0;
+        c1 = lo1;
+        c2 = hi0 ^ c3 ^ k1;
+        c3 = lo0;
+        k0 += 0x9E3779B97F4A7C15ULL;
+        k1 += 0xBB67AE8584CAA73BULL;
+    }
+    out[0] = c0;
+    out[1] = c1;
+    out[2] = c2;
+    out[3] = c3;
+}
+
+/*
+ * READING (random numbers of stochastic rounding; the pages name the
+ * technique, [MP] "NVFP4" and [LP] section 2.4 item 5, but fix no generator):
+ * element e of an output plane (its index in that plane's row-major order)
+ * takes 16 random bits.  Elements are grouped by 16: group g = e / 16 is one
+ * Philox4x64-10 call with key (seed, 0) and counter (g, offset, plane, 0),
+ * plane 0 for the rowwise copy and 1 for the colwise one; element j = e % 16
+ * of the group takes bits 16*(j%4) .. 16*(j%4)+15 of output word j / 4.
+ */
+unsigned orc_sr_bits(uint64_t seed, uint64_t offset, unsigned plane, int64_t e)
+{
+    uint64_t ctr[4], key[2], out[4];
+    int j = (int)(e % 16);
+    ctr[0] = (uint64_t)(e / 16);
+    ctr[1] = offset;
+    ctr[2] = plane;
+    ctr[3] = 0;
+    key[0] = seed;
+    key[1] = 0;
+    orc_philox4x64_10(ctr, key, out);
+    return (unsigned)(out[j / 4] >> (16 * (j % 4))) & 0xFFFFu;
+}
+
+/*
+ * READING (stochastic rounding to E2M1): a scaled value y of magnitude v
+ * below the largest, 6, lies between two neighbouring E2M1 values lo <= v < hi;
+ * with g = (v - lo) / (hi - lo) (exact in fp32), it rounds to hi when
+ * u / 2^16 < g and to lo otherwise, so it goes up with probability
+ * ceil(g * 2^16) / 2^16, which differs from g by less than 2^-16 (the method
+ * is unbiased to that resolution).  Values of magnitude 6 or more saturate
+ * to 6, as in round-to-nearest.  The sign of y is kept, also on zero.
+ */
+unsigned orc_encode_e2m1_sr(float y, unsigned u)
+{
+    unsigned sign = signbit(y) ? 0x8u : 0u, k = 0;
+    float v = fabsf(y), lo, hi, g;
+    if (v >= 6.0f)
+        return sign | 0x7u;
+    while (k < 7 && (float)orc_decode(ORC_E2M1, k + 1) <= v)
+        k++;
+    lo = (float)orc_decode(ORC_E2M1, k);
+    hi = (float)orc_decode(ORC_E2M1, k + 1);
+    g = (v - lo) / (hi - lo);
+    if ((float)u < g * 65536.0f)
+        k++;
+    return sign | k;
+}
+
+void orc_encode_e2m1_sr_array(const float *y, const uint16_t *u, int64_t n, uint8_t *q)
+{
+    int64_t i;
+    for (i = 0; i < n; i++)
+        q[i] = (uint8_t)orc_encode_e2m1_sr(y[i], u[i]);
+}
+
+/* Stochastic rounding of one plane: on = 0 means round to nearest even. */
+typedef struct {
+    int on;
+    uint64_t seed, offset;
+    unsigned plane;
+} sr_ctx;
+
+static const sr_ctx kNoSR = {0, 0, 0, 0};
+
 /* One block of NVFP4: returns the E4M3 scale code and writes the nibbles
- * (0..15) of its elements. */
+ * (0..15) of its elements.  Only the elements are rounded stochastically
+ * (when sr.on); the block scale is always rounded to nearest even. */
 static unsigned nvfp4_block(const void *x, int dt, int64_t ld, int64_t r0, int br, int64_t c0, int bc,
-                            nvfp4_tensor t, uint8_t *nib /* [R,C] nibble per element */)
+                            nvfp4_tensor t, sr_ctx sr, uint8_t *nib /* [R,C] nibble per element */)
 {
     float a = amax_rect(x, dt, ld, r0, br, c0, bc);
     float b = a / 6.0f;
@@ -565,8 +664,12 @@ static unsigned nvfp4_block(const void *x, int dt, int64_t ld, int64_t r0, int b
             r = FLT_MAX;
     }
     for (i = r0; i < r0 + br; i++)
-        for (j = c0; j < c0 + bc; j++)
-            nib[i * ld + j] = (uint8_t)orc_encode(ORC_E2M1, load_x(x, dt, i * ld + j) * r);
+        for (j = c0; j < c0 + bc; j++) {
+            float y = load_x(x, dt, i * ld + j) * r;
+            nib[i * ld + j] = (uint8_t)(sr.on ? orc_encode_e2m1_sr(y, orc_sr_bits(sr.seed, sr.offset, sr.plane,
+                                                                                     i * ld + j))
+                                              : orc_encode(ORC_E2M1, y));
+        }
     return code;
 }
 
@@ -581,13 +684,13 @@ static void pack_nibbles(const uint8_t *nib, int64_t R, int64_t C, uint8_t *p)
 }
 
 static void nvfp4_rowwise(const void *x, int dt, int64_t R, int64_t C, int br, int bc, nvfp4_tensor t,
-                          uint8_t *p, uint8_t *codes, uint8_t *nib_out)
+                          sr_ctx sr, uint8_t *p, uint8_t *codes, uint8_t *nib_out)
 {
     int64_t tr, tc, nbc = C / bc;
     uint8_t *nib = (uint8_t *)malloc((size_t)(R * C));
     for (tr = 0; tr < R / br; tr++)
         for (tc = 0; tc < nbc; tc++)
-            codes[tr * nbc + tc] = (uint8_t)nvfp4_block(x, dt, C, tr * br, br, tc * bc, bc, t, nib);
+            codes[tr * nbc + tc] = (uint8_t)nvfp4_block(x, dt, C, tr * br, br, tc * bc, bc, t, sr, nib);
     pack_nibbles(nib, R, C, p);
     if (nib_out)
         memcpy(nib_out, nib, (size_t)(R * C));
@@ -603,10 +706,11 @@ static void nvfp4_rowwise(const void *x, int dt, int64_t R, int64_t C, int br, i
  * transposed ([MP] closing remarks: FP4 GEMMs need two copies even for 2-D
  * weight tiles).
  */
-int orc_quantize_nvfp4_with_amax(const void *x, int dt, int64_t R, int64_t C, int br, int bc, unsigned outputs,
-                                 float A, uint8_t *p_row, uint8_t *c_row, uint8_t *p_col, uint8_t *c_col,
-                                 float *S_out, float *amax_out)
+static int nvfp4_core(const void *x, int dt, int64_t R, int64_t C, int br, int bc, unsigned outputs, float A,
+                      int sr_on, uint64_t seed, uint64_t offset, uint8_t *p_row, uint8_t *c_row, uint8_t *p_col,
+                      uint8_t *c_col, float *S_out, float *amax_out)
 {
+    sr_ctx sr_row = {sr_on, seed, offset, 0}, sr_col = {sr_on, seed, offset, 1};
     if (R <= 0 || C <= 0)
         return -3;
     if (!((br == 1 && bc == 16) || (br == 16 && bc == 16)))
@@ -622,19 +726,21 @@ int orc_quantize_nvfp4_with_amax(const void *x, int dt, int64_t R, int64_t C, in
         *S_out = t.S;
     if (amax_out)
         *amax_out = A;
+    if (sr_on && br != 1)
+        return -2;
     if (br == 1) {
         if (outputs & ORC_ROWWISE)
-            nvfp4_rowwise(x, dt, R, C, 1, bc, t, p_row, c_row, NULL);
+            nvfp4_rowwise(x, dt, R, C, 1, bc, t, sr_row, p_row, c_row, NULL);
         if (outputs & ORC_COLWISE) {
             void *xt = transpose_input(x, dt, R, C);
-            nvfp4_rowwise(xt, dt, C, R, 1, bc, t, p_col, c_col, NULL);
+            nvfp4_rowwise(xt, dt, C, R, 1, bc, t, sr_col, p_col, c_col, NULL);
             free(xt);
         }
     } else {
         uint8_t *nib = (uint8_t *)malloc((size_t)(R * C));
         uint8_t *p = p_row ? p_row : (uint8_t *)malloc((size_t)(R * C / 2));
         uint8_t *cd = c_row ? c_row : (uint8_t *)malloc((size_t)((R / br) * (C / bc)));
-        nvfp4_rowwise(x, dt, R, C, br, bc, t, p, cd, nib);
+        nvfp4_rowwise(x, dt, R, C, br, bc, t, kNoSR, p, cd, nib);
         if (outputs & ORC_COLWISE) {
             uint8_t *nt = (uint8_t *)malloc((size_t)(R * C));
             orc_transpose_u8(nib, R, C, nt);
@@ -649,6 +755,27 @@ int orc_quantize_nvfp4_with_amax(const void *x, int dt, int64_t R, int64_t C, in
             free(cd);
     }
     return 0;
+}
+
+int orc_quantize_nvfp4_with_amax(const void *x, int dt, int64_t R, int64_t C, int br, int bc, unsigned outputs,
+                                 float A, uint8_t *p_row, uint8_t *c_row, uint8_t *p_col, uint8_t *c_col,
+                                 float *S_out, float *amax_out)
+{
+    return nvfp4_core(x, dt, R, C, br, bc, outputs, A, 0, 0, 0, p_row, c_row, p_col, c_col, S_out, amax_out);
+}
+
+/*
+ * NVFP4 1x16 with stochastically rounded elements ([MP] "NVFP4": stochastic
+ * rounding as an option for FP4; [LP] section 2.4 item 5: on gradients).
+ * Everything but the element rounding is the round-to-nearest recipe above;
+ * random bits from orc_sr_bits (plane 0 rowwise, 1 colwise).
+ */
+int orc_quantize_nvfp4_sr_with_amax(const void *x, int dt, int64_t R, int64_t C, unsigned outputs, float A,
+                                    uint64_t seed, uint64_t offset, uint8_t *p_row, uint8_t *c_row,
+                                    uint8_t *p_col, uint8_t *c_col, float *S_out, float *amax_out)
+{
+    return nvfp4_core(x, dt, R, C, 1, 16, outputs, A, 1, seed, offset, p_row, c_row, p_col, c_col, S_out,
+                      amax_out);
 }
 
 /* NVFP4 with A = the amax of this tensor. */

@@ -95,6 +95,33 @@ def test_desc_validation(L, recipe, fmt, R, C, block, outputs, want):
     assert L.fq_quantize(ctypes.byref(d), B, ctypes.byref(q), B, 1 << 20, None) == want
 
 
+@pytest.mark.parametrize("recipe,fmt,block,rounding,scale_mode,want", [
+    (fq.FQ_NVFP4, fq.FQ_E2M1, (1, 16), fq.FQ_ROUND_STOCHASTIC, 0, fq.FQ_OK),
+    (fq.FQ_NVFP4, fq.FQ_E2M1, (16, 16), fq.FQ_ROUND_STOCHASTIC, 0, fq.FQ_E_UNSUPPORTED),
+    (fq.FQ_PER_TENSOR_CURRENT, fq.FQ_E4M3, (0, 0), fq.FQ_ROUND_STOCHASTIC, 0, fq.FQ_E_UNSUPPORTED),
+    (fq.FQ_BLOCK_FP32, fq.FQ_E4M3, (1, 128), fq.FQ_ROUND_STOCHASTIC, 0, fq.FQ_E_UNSUPPORTED),
+    (fq.FQ_MX, fq.FQ_E4M3, (1, 32), fq.FQ_ROUND_STOCHASTIC, 0, fq.FQ_E_UNSUPPORTED),
+    (fq.FQ_NVFP4, fq.FQ_E2M1, (1, 16), 2, 0, fq.FQ_E_INVALID),
+    (fq.FQ_NVFP4, fq.FQ_E2M1, (1, 16), -1, 0, fq.FQ_E_INVALID),
+    (fq.FQ_NVFP4, fq.FQ_E2M1, (1, 16), 0, 7, fq.FQ_E_INVALID),
+])
+def test_rounding_and_scale_mode_validation(L, recipe, fmt, block, rounding, scale_mode, want):
+    d = fq.desc(recipe, fq.FQ_IN_BF16, fmt, 256, 256, block, 3, rounding=rounding, seed=1, offset=2,
+                scale_mode=scale_mode)
+    z = [ctypes.c_size_t() for _ in range(5)]
+    assert L.fq_sizes(ctypes.byref(d), *[ctypes.byref(v) for v in z]) == want
+    if want != fq.FQ_OK:
+        q = fq.FqQuantized(fq.FqPlane(B, B), fq.FqPlane(B, B), B, B)
+        assert L.fq_quantize(ctypes.byref(d), B, ctypes.byref(q), B, 1 << 20, None) == want
+        assert L.fq_quantize_with_amax(ctypes.byref(d), B, B, ctypes.byref(q), B, 1 << 20, None) == want
+
+
+def test_desc_layout():
+    # the C struct: three int32, two int64, two int32, uint32, two int32, two uint64
+    assert ctypes.sizeof(fq.FqDesc) == 72
+    assert fq.FqDesc.seed.offset == 56 and fq.FqDesc.offset.offset == 64
+
+
 def test_null_desc(L):
     assert L.fq_sizes(None, None, None, None, None, None) == fq.FQ_E_INVALID
     assert L.fq_quantize(None, B, None, B, 4096, None) == fq.FQ_E_INVALID
@@ -176,6 +203,9 @@ def test_requantize_checks(L):
     assert L.fq_requantize_transpose(ctypes.byref(d48), ctypes.byref(ok), ctypes.byref(ok), None) == fq.FQ_E_SHAPE
     mis = fq.FqQuantized(fq.FqPlane(B, B + 1), fq.FqPlane(B, B), None, None)
     assert L.fq_requantize_transpose(ctypes.byref(d), ctypes.byref(mis), ctypes.byref(ok), None) == fq.FQ_E_ALIGN
+    sr = fq.desc(fq.FQ_MX, fq.FQ_IN_BF16, fq.FQ_E4M3, 64, 64, (1, 32), fq.FQ_ROWWISE, rounding=1)
+    assert L.fq_requantize_transpose(ctypes.byref(sr), ctypes.byref(ok), ctypes.byref(ok), None) \
+        == fq.FQ_E_UNSUPPORTED
     nocol = fq.FqQuantized(fq.FqPlane(B, B), fq.FqPlane(None, None), None, None)
     assert L.fq_requantize_transpose(ctypes.byref(d), ctypes.byref(ok), ctypes.byref(nocol), None) \
         == fq.FQ_E_INVALID
