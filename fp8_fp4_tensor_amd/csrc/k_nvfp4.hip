@@ -28,8 +28,8 @@
 //                  blocks as rowwise (max also across 16 neighbouring lanes),
 //                  so the colwise nibbles are the rowwise ones transposed.
 //   k_nvfp4_1x16_sr  stochastic rounding of the elements ([MP] "NVFP4"; [LP]
-//                  2.4 item 5): a lane owns a whole 1x16 block, which is one
-//                  Philox4x64-10 call (16 x 16 random bits); the colwise
+//                  2.4 item 5): a lane owns a whole 1x16 block, which is two
+//                  Philox4x32-10 calls (8 x 16 random bits each); the colwise
 //                  kernel takes the same path per 16-row block.
 #include <algorithm>
 
@@ -87,67 +87,66 @@ struct Fp4Store<4> {
 };
 
 // ---------------------------------------------------------------- stochastic rounding
-// Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
 // easy as 1, 2, 3", SC 2011): the published multipliers and Weyl constants.
-constexpr uint64_t kPhM0 = 0xD2E7470EE14C6C93ull, kPhM1 = 0xCA5A826395121157ull;
-constexpr uint64_t kPhW0 = 0x9E3779B97F4A7C15ull, kPhW1 = 0xBB67AE8584CAA73Bull;
+// Each round's two 32 x 32 -> 64-bit products are one v_mad_u64_u32 each.
+constexpr uint32_t kPhM0 = 0xD2511F53u, kPhM1 = 0xCD9E8D57u;
+constexpr uint32_t kPhW0 = 0x9E3779B9u, kPhW1 = 0xBB67AE85u;
 
 struct Philox4 {
-    uint64_t w[4];
+    uint32_t w[4];
 };
 
-__device__ __forceinline__ Philox4 philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3, uint64_t k0,
-                                                 uint64_t k1)
+__device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                                 uint32_t k1)
 {
 #pragma unroll
     for (int i = 0; i < 10; ++i) {
-        const uint64_t lo0 = kPhM0 * c0, hi0 = __umul64hi(kPhM0, c0);
-        const uint64_t lo1 = kPhM1 * c2, hi1 = __umul64hi(kPhM1, c2);
-        c0 = hi1 ^ c1 ^ k0;
-        c1 = lo1;
-        c2 = hi0 ^ c3 ^ k1;
-        c3 = lo0;
+        const uint64_t p0 = (uint64_t)kPhM0 * c0, p1 = (uint64_t)kPhM1 * c2;
+        c0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        c1 = (uint32_t)p1;
+        c2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        c3 = (uint32_t)p0;
         k0 += kPhW0;
         k1 += kPhW1;
     }
     return Philox4{{c0, c1, c2, c3}};
 }
 
-// the 16 random bits of element j (0..15) of a Philox block
-__device__ __forceinline__ uint32_t sr_u16(const Philox4& ph, int j)
+// The random bits of elements 8h .. 8h+7 of a plane: one call with counter
+// (h, s) as 32-bit words and key = seed, s = 2 * offset + plane.
+__device__ __forceinline__ Philox4 sr_group(uint64_t h, uint64_t s, uint64_t seed)
 {
-    return (uint32_t)(ph.w[j >> 2] >> (16 * (j & 3))) & 0xFFFFu;
+    return philox4x32_10((uint32_t)h, (uint32_t)(h >> 32), (uint32_t)s, (uint32_t)(s >> 32), (uint32_t)seed,
+                         (uint32_t)(seed >> 32));
 }
 
-// Stochastic rounding of y to E2M1: the result is an E2M1 value (exact in
-// fp32) with y's sign. With v = min(|y|, 6) and q the E2M1 spacing at v
-// (0.5 below 2, 1 on [2, 4), 2 on [4, 6]), t = v/q splits exactly into the
-// count of whole spacings and the fraction g = (v - lo)/q; the value goes up
-// one spacing iff u < g * 2^16 (all steps exact: powers of two and fract).
-__device__ __forceinline__ float sr_e2m1(float y, uint32_t u)
+// Stochastic rounding to E2M1 with gfx950's v_cvt_scalef32_sr_pk_fp4_f32 at
+// unit scale. For its first value the converter adds bits 31..10 of its
+// random word below the last kept bit and truncates (saturating at 6, sign
+// kept); with a word whose bits 31..16 are u and 15..0 zero this is exactly
+// "round up iff u + g * 2^16 >= 2^16". Its second value would read bits
+// 30..9 of the same word, so each element gets a call of its own, with 0 as
+// the second value (code 0 for any random word). Only byte 0 of each result
+// is used: the compiler does not carry the other bytes of the destination
+// through, so they are undefined.
+__device__ __forceinline__ uint32_t sr_nibble(float y, uint32_t word_hi16)
 {
-    const float v = fminf(fabsf(y), 6.0f);
-    const int e = __builtin_amdgcn_frexp_expf(v);  // v = m * 2^e, m in [0.5, 1)
-    const int sh = 2 - max(e, 1);                   // 1/q = 2^sh
-    const float t = ldexpf(v, sh);
-    const float g = __builtin_amdgcn_fractf(t);
-    const float n = ((float)u < g * 65536.0f) ? (t - g) + 1.0f : (t - g);
-    return copysignf(ldexpf(n, -sh), y);
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, f32x2{y, 0.0f}, word_hi16, 1.0f, 0) & 0xFu;
 }
 
-// 8 values (times r, stochastically rounded) -> one dword of packed E2M1;
-// random bits j0 .. j0+7 of the block
-__device__ __forceinline__ uint32_t enc8_e2m1_sr(const float* f, float r, const Philox4& ph, int j0)
+// 8 values (times r, stochastically rounded with one group's random bits:
+// element 2k takes bits 15..0 of word k, element 2k+1 bits 31..16) -> one
+// dword of packed E2M1, element j in bits 4j..4j+3
+__device__ __forceinline__ uint32_t enc8_e2m1_sr(const float* f, float r, const Philox4& ph)
 {
     uint32_t w = 0;
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, sr_e2m1(f[0] * r, sr_u16(ph, j0)),
-                                                 sr_e2m1(f[1] * r, sr_u16(ph, j0 + 1)), 1.0f, 0);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, sr_e2m1(f[2] * r, sr_u16(ph, j0 + 2)),
-                                                 sr_e2m1(f[3] * r, sr_u16(ph, j0 + 3)), 1.0f, 1);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, sr_e2m1(f[4] * r, sr_u16(ph, j0 + 4)),
-                                                 sr_e2m1(f[5] * r, sr_u16(ph, j0 + 5)), 1.0f, 2);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, sr_e2m1(f[6] * r, sr_u16(ph, j0 + 6)),
-                                                 sr_e2m1(f[7] * r, sr_u16(ph, j0 + 7)), 1.0f, 3);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        w |= sr_nibble(f[2 * k] * r, ph.w[k] << 16) << (8 * k);
+        w |= sr_nibble(f[2 * k + 1] * r, ph.w[k] & 0xFFFF0000u) << (8 * k + 4);
+    }
     return w;
 }
 
@@ -186,10 +185,10 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_1x16_sr(const T* __restrict__ x, 
         uint32_t code;
         float r;
         nvfp4_block(absmax<16>(f), alpha_s, S, code, r);
-        const Philox4 ph = philox4x64_10((uint64_t)b, offset, 0, 0, seed, 0);
+        const uint64_t s = 2 * offset;  // plane 0
         u32x2 out;
-        out[0] = enc8_e2m1_sr(f, r, ph, 0);
-        out[1] = enc8_e2m1_sr(f + 8, r, ph, 8);
+        out[0] = enc8_e2m1_sr(f, r, sr_group(2 * (uint64_t)b, s, seed));
+        out[1] = enc8_e2m1_sr(f + 8, r, sr_group(2 * (uint64_t)b + 1, s, seed));
         st8_stream(p + b * 8, out);
         codes[b] = (uint8_t)code;
     }
@@ -342,11 +341,10 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_col(const T* __restrict__ x, int6
         float r;
         nvfp4_block(a, alpha_s, S, code, r);
         if constexpr (SR) {
-            // element (c, r0 + 16b + k) of X^T: group (c0+c)*(R/16) + r0/16 + b, plane 1
-            const uint64_t g = (uint64_t)((c0 + c) * (R / 16) + r0 / 16 + b);
-            const Philox4 ph = philox4x64_10(g, offset, 1, 0, seed, 0);
-            w[2 * b] = enc8_e2m1_sr(f, r, ph, 0);
-            w[2 * b + 1] = enc8_e2m1_sr(f + 8, r, ph, 8);
+            // elements (c0 + c, r0 + 16b + k) of X^T: index e0 + k, plane 1
+            const uint64_t e0 = (uint64_t)((c0 + c) * R + r0 + 16 * b), s = 2 * offset + 1;
+            w[2 * b] = enc8_e2m1_sr(f, r, sr_group(e0 / 8, s, seed));
+            w[2 * b + 1] = enc8_e2m1_sr(f + 8, r, sr_group(e0 / 8 + 1, s, seed));
         } else {
             w[2 * b] = enc8_e2m1(f, r);
             w[2 * b + 1] = enc8_e2m1(f + 8, r);

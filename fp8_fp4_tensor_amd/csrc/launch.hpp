@@ -95,7 +95,7 @@ hipError_t launch_block_128x128(const void* x, int in_bf16, int64_t R, int64_t C
 hipError_t launch_mx(const void* x, int in_bf16, int64_t R, int64_t C, uint8_t* q, uint8_t* e, uint8_t* qt,
                      uint8_t* et, hipStream_t stream);
 
-// Stochastic rounding of elements: Philox4x64-10 key (seed, 0), counter word 1 = offset.
+// Stochastic rounding of elements: Philox4x32-10 keyed by seed, stream 2*offset + plane.
 struct SrArgs {
     int on = 0;
     uint64_t seed = 0, offset = 0;

@@ -107,12 +107,14 @@ enum { FQ_ROWWISE = 1, FQ_COLWISE = 2 };
  *                          lo <= v < hi rounds to hi iff u / 2^16 <
  *                          (v - lo) / (hi - lo), u a 16-bit random number;
  *                          v >= 6 saturates; block scales stay
- *                          round-to-nearest-even. u comes from Philox4x64-10
- *                          (Salmon et al., SC 2011) with key (seed, 0): the
- *                          element at index e of an output plane (row-major
- *                          in that plane) uses counter (e/16, offset, plane,
- *                          0), plane 0 rowwise and 1 colwise, and bits
- *                          16*(e%4) .. +15 of output word (e%16)/4.
+ *                          round-to-nearest-even. u comes from Philox4x32-10
+ *                          (Salmon et al., SC 2011) with key = seed (low word
+ *                          first): the element at index e of an output plane
+ *                          (row-major in that plane) uses counter
+ *                          (h mod 2^32, h >> 32, s mod 2^32, s >> 32) with
+ *                          h = e/8 and s = 2*offset + plane (mod 2^64), plane
+ *                          0 rowwise and 1 colwise, and bits 16*(e%2) .. +15
+ *                          of output word (e%8)/2.
  *                          Results are a pure function of (input, seed,
  *                          offset), independent of launch shape.
  */
@@ -152,8 +154,8 @@ typedef struct {
     uint32_t outputs;
     int32_t rounding;   /* fq_rounding */
     int32_t scale_mode; /* fq_scale_mode */
-    uint64_t seed;      /* stochastic rounding: Philox key word 0 */
-    uint64_t offset;    /* stochastic rounding: counter word 1 (e.g. the step) */
+    uint64_t seed;      /* stochastic rounding: the Philox key */
+    uint64_t offset;    /* stochastic rounding: stream number (e.g. the step) */
 } fq_desc;
 
 /* One quantized copy: data codes and per-block scales (device memory). */

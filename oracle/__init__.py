@@ -91,7 +91,7 @@ def _load():
         "orc_quantize_nvfp4_sr_with_amax": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, _u32, _f32,
                                                            ctypes.c_uint64, ctypes.c_uint64, _p, _p, _p, _p,
                                                            _fp, _fp]),
-        "orc_philox4x64_10": (None, [_p, _p, _p]),
+        "orc_philox4x32_10": (None, [_p, _p, _p]),
         "orc_sr_bits": (_u32, [ctypes.c_uint64, ctypes.c_uint64, _u32, _i64]),
         "orc_encode_e2m1_sr": (_u32, [_f32, _u32]),
         "orc_encode_e2m1_sr_array": (None, [_p, _p, _i64, _p]),
@@ -325,12 +325,12 @@ def quantize_nvfp4(x, block, outputs=ROWWISE, shape=None, amax=None, sr=None):
 
 
 # ---------------------------------------------------------------- stochastic rounding
-def philox4x64_10(counter, key):
-    """Philox4x64-10 of a 4-word counter and a 2-word key (uint64 words)."""
-    c = np.asarray(counter, np.uint64)
-    k = np.asarray(key, np.uint64)
-    out = np.empty(4, np.uint64)
-    _load().orc_philox4x64_10(c.ctypes.data, k.ctypes.data, out.ctypes.data)
+def philox4x32_10(counter, key):
+    """Philox4x32-10 of a 4-word counter and a 2-word key (uint32 words)."""
+    c = np.asarray(counter, np.uint32)
+    k = np.asarray(key, np.uint32)
+    out = np.empty(4, np.uint32)
+    _load().orc_philox4x32_10(c.ctypes.data, k.ctypes.data, out.ctypes.data)
     return out
 
 

@@ -553,28 +553,28 @@ static nvfp4_tensor nvfp4_tensor_scale(float A)
 /* ------------------------------------------------------------------ */
 
 /*
- * Philox4x64-10, the counter-based generator of Salmon, Moraes, Dror and
+ * Philox4x32-10, the counter-based generator of Salmon, Moraes, Dror and
  * Shaw, "Parallel random numbers: as easy as 1, 2, 3" (SC 2011): ten rounds
- * over a 4 x 64-bit counter; each round multiplies counter words 0 and 2 by
- * the two published 64-bit multipliers (full 128-bit products), and the new
- * counter is (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0); the 2 x 64-bit key
- * is bumped by the two published Weyl constants after every round.
+ * over a 4 x 32-bit counter; each round multiplies counter words 0 and 2 by
+ * the two published 32-bit multipliers (full 64-bit products), and the new
+ * counter is (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0); the 2 x 32-bit key is
+ * bumped by the two published Weyl constants after every round.
  */
-void orc_philox4x64_10(const uint64_t ctr[4], const uint64_t key[2], uint64_t out[4])
+void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4])
 {
-    uint64_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3], k0 = key[0], k1 = key[1];
+    uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3], k0 = key[0], k1 = key[1];
     int round;
     for (round = 0; round < 10; round++) {
-        unsigned __int128 p0 = (unsigned __int128)0xD2E7470EE14C6C93ULL * c0;
-        unsigned __int128 p1 = (unsigned __int128)0xCA5A826395121157ULL * c2;
-        uint64_t hi0 = (uint64_t)(p0 >> 64), lo0 = (uint64_t)p0;
-        uint64_t hi1 = (uint64_t)(p1 >> 64), lo1 = (uint64_t)p1;
+        uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+        uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
         c0 = hi1 ^ c1 ^ k0;
         c1 = lo1;
         c2 = hi0 ^ c3 ^ k1;
         c3 = lo0;
-        k0 += 0x9E3779B97F4A7C15ULL;
-        k1 += 0xBB67AE8584CAA73BULL;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
     }
     out[0] = c0;
     out[1] = c1;
@@ -586,33 +586,37 @@ void orc_philox4x64_10(const uint64_t ctr[4], const uint64_t key[2], uint64_t ou
  * READING (random numbers of stochastic rounding; the pages name the
  * technique, [MP] "NVFP4" and [LP] section 2.4 item 5, but fix no generator):
  * element e of an output plane (its index in that plane's row-major order)
- * takes 16 random bits.  Elements are grouped by 16: group g = e / 16 is one
- * Philox4x64-10 call with key (seed, 0) and counter (g, offset, plane, 0),
- * plane 0 for the rowwise copy and 1 for the colwise one; element j = e % 16
- * of the group takes bits 16*(j%4) .. 16*(j%4)+15 of output word j / 4.
+ * takes 16 random bits.  Elements are grouped by 8: group h = e / 8 is one
+ * Philox4x32-10 call with key (seed mod 2^32, seed >> 32) and counter
+ * (h mod 2^32, h >> 32, s mod 2^32, s >> 32), where the stream number
+ * s = 2 * offset + plane (mod 2^64), plane 0 for the rowwise copy and 1 for
+ * the colwise one; element j = e % 8 of the group takes bits
+ * 16*(j%2) .. 16*(j%2)+15 of output word j / 2.
  */
 unsigned orc_sr_bits(uint64_t seed, uint64_t offset, unsigned plane, int64_t e)
 {
-    uint64_t ctr[4], key[2], out[4];
-    int j = (int)(e % 16);
-    ctr[0] = (uint64_t)(e / 16);
-    ctr[1] = offset;
-    ctr[2] = plane;
-    ctr[3] = 0;
-    key[0] = seed;
-    key[1] = 0;
-    orc_philox4x64_10(ctr, key, out);
-    return (unsigned)(out[j / 4] >> (16 * (j % 4))) & 0xFFFFu;
+    uint32_t ctr[4], key[2], out[4];
+    uint64_t h = (uint64_t)(e / 8), s = 2 * offset + plane;
+    int j = (int)(e % 8);
+    ctr[0] = (uint32_t)h;
+    ctr[1] = (uint32_t)(h >> 32);
+    ctr[2] = (uint32_t)s;
+    ctr[3] = (uint32_t)(s >> 32);
+    key[0] = (uint32_t)seed;
+    key[1] = (uint32_t)(seed >> 32);
+    orc_philox4x32_10(ctr, key, out);
+    return (out[j / 2] >> (16 * (j % 2))) & 0xFFFFu;
 }
 
 /*
  * READING (stochastic rounding to E2M1): a scaled value y of magnitude v
  * below the largest, 6, lies between two neighbouring E2M1 values lo <= v < hi;
- * with g = (v - lo) / (hi - lo) (exact in fp32), it rounds to hi when
- * u / 2^16 < g and to lo otherwise, so it goes up with probability
- * ceil(g * 2^16) / 2^16, which differs from g by less than 2^-16 (the method
- * is unbiased to that resolution).  Values of magnitude 6 or more saturate
- * to 6, as in round-to-nearest.  The sign of y is kept, also on zero.
+ * with g = (v - lo) / (hi - lo) (exact in fp32) and u a 16-bit random number,
+ * the 16 random bits are added below the last kept bit and the sum truncated:
+ * v rounds to hi iff u + g * 2^16 >= 2^16, else to lo.  It goes up with
+ * probability floor(g * 2^16) / 2^16, within 2^-16 of g (unbiased to that
+ * resolution).  Values of magnitude 6 or more saturate to 6, as in
+ * round-to-nearest.  The sign of y is kept, also on zero.
  */
 unsigned orc_encode_e2m1_sr(float y, unsigned u)
 {
@@ -625,7 +629,8 @@ unsigned orc_encode_e2m1_sr(float y, unsigned u)
     lo = (float)orc_decode(ORC_E2M1, k);
     hi = (float)orc_decode(ORC_E2M1, k + 1);
     g = (v - lo) / (hi - lo);
-    if ((float)u < g * 65536.0f)
+    /* u + g*2^16 >= 2^16, compared exactly: g*2^16 is exact, 2^16 - u an integer */
+    if (g * 65536.0f >= (float)(65536u - u))
         k++;
     return sign | k;
 }

@@ -2,53 +2,70 @@
 
 The pages name stochastic rounding for FP4 gradients ([MP] "NVFP4"; [LP]
 section 2.4 item 5) without fixing its arithmetic; the oracle's reading is
-"round up with probability equal to the distance to the lower neighbour,
-measured in 2^-16 steps", driven by Philox4x64-10. These tests pin
-  - the generator against numpy's independent Philox4x64-10,
-  - the element mapping against one continuous numpy Philox stream,
+"add 16 random bits below the last kept bit and truncate", so a value goes up
+with probability equal to its distance to the lower neighbour in 2^-16
+steps; the bits come from Philox4x32-10. These tests pin
+  - the generator against PyTorch's independent Philox4x32-10 engine,
+  - the element mapping against one continuous stream of that engine,
   - the rounding against its defining properties: only the two neighbours,
     the exact up-count over all 65536 random values, unbiasedness,
     saturation and sign,
   - the NVFP4 recipe with SR against the round-to-nearest recipe.
 """
 import math
+import os
+import subprocess
 
 import numpy as np
 import pytest
 
-from conftest import golden
+from conftest import ROOT, golden
 
+M32 = (1 << 32) - 1
 M64 = (1 << 64) - 1
 
 
-def numpy_philox(counter_words, key_words, n_blocks=1):
-    """numpy's Philox4x64-10 blocks for counters c, c+1, ... (numpy bumps the
-    counter before each block, hence the -1)."""
-    c = sum(int(v) << (64 * i) for i, v in enumerate(counter_words))
-    k = int(key_words[0]) | (int(key_words[1]) << 64)
-    g = np.random.Philox(counter=(c - 1) % (1 << 256), key=k)
-    return g.random_raw(4 * n_blocks).reshape(n_blocks, 4)
+@pytest.fixture(scope="module")
+def torch_philox(tmp_path_factory):
+    """PyTorch's CPU Philox4x32-10 engine, compiled from its header: an
+    implementation of the generator independent of the oracle. Returns
+    f(seed, subsequence, offset, count) -> the engine's first `count` words
+    (counter = (offset, subsequence) as 4 x 32-bit words, key = seed)."""
+    import torch
+    inc = os.path.join(os.path.dirname(torch.__file__), "include")
+    exe = str(tmp_path_factory.mktemp("philox") / "philox_ref")
+    subprocess.run(["g++", "-std=c++17", "-O1", "-I", inc, os.path.join(ROOT, "tests", "philox_ref.cpp"),
+                    "-o", exe], check=True)
+
+    def run(queries):
+        text = "".join(f"{s} {q} {o} {n}\n" for s, q, o, n in queries)
+        out = subprocess.run([exe], input=text, capture_output=True, text=True, check=True).stdout
+        return [[int(v) for v in line.split()] for line in out.splitlines()]
+    return run
 
 
-def test_philox_matches_numpy(orc):
+def test_philox_matches_torch_engine(orc, torch_philox):
     rng = np.random.default_rng(11)
-    cases = [([0, 0, 0, 0], [0, 0]), ([M64] * 4, [M64, M64]), ([M64, 0, 0, 0], [1, 0]),
-             ([1, 2, 3, 4], [5, 6])]
+    cases = [(0, 0, 0), (M64, M64, M64), (1, 2, 3), (0x0123456789ABCDEF, 5, 9), (7, 0, M32), (7, M32, M64 - 1)]
     for _ in range(200):
-        cases.append(([int(v) for v in rng.integers(0, 1 << 64, 4, dtype=np.uint64)],
-                      [int(v) for v in rng.integers(0, 1 << 64, 2, dtype=np.uint64)]))
-    for c, k in cases:
-        assert np.array_equal(orc.philox4x64_10(c, k), numpy_philox(c, k)[0]), (c, k)
+        cases.append(tuple(int(v) for v in rng.integers(0, 1 << 64, 3, dtype=np.uint64)))
+    ref = torch_philox([(s, q, o, 4) for s, q, o in cases])
+    for (seed, sub, off), want in zip(cases, ref):
+        ctr = [off & M32, off >> 32, sub & M32, sub >> 32]
+        key = [seed & M32, seed >> 32]
+        assert list(orc.philox4x32_10(ctr, key)) == want, (seed, sub, off)
 
 
-@pytest.mark.parametrize("seed,offset,plane", [(0, 0, 0), (1234567, 9, 0), (2**64 - 5, 2**40, 1)])
-def test_sr_bits_follow_one_numpy_stream(orc, seed, offset, plane):
-    # groups g0, g0+1, ... are consecutive counters of one stream
-    g0, n = 1000, 64
-    blocks = numpy_philox([g0, offset, plane, 0], [seed, 0], n)
-    for e in range(16 * g0, 16 * (g0 + n), 7):
-        g, j = divmod(e, 16)
-        want = int(blocks[g - g0][j // 4]) >> (16 * (j % 4)) & 0xFFFF
+@pytest.mark.parametrize("seed,offset,plane", [(0, 0, 0), (1234567, 9, 0), (2**64 - 5, 2**40, 1),
+                                               (3, 2**63 + 4, 1)])
+def test_sr_bits_follow_one_torch_stream(orc, torch_philox, seed, offset, plane):
+    # groups h0, h0+1, ... are consecutive counters of one engine stream
+    h0, n = (1 << 32) - 5, 32            # crosses the carry into counter word 1
+    stream = (2 * offset + plane) & M64
+    words = torch_philox([(seed, stream, h0, 4 * n)])[0]
+    for e in range(8 * h0, 8 * (h0 + n), 3):
+        h, j = divmod(e, 8)
+        want = words[4 * (h - h0) + j // 2] >> (16 * (j % 2)) & 0xFFFF
         assert orc.sr_bits(seed, offset, plane, e) == want, e
 
 
@@ -74,10 +91,13 @@ def test_e2m1_sr_neighbours_and_exact_up_count(orc):
         lo, hi = neighbours(v)
         mags = np.abs(vals)
         assert set(np.unique(mags)) <= {lo, hi}, y
-        # exact count: round up iff u / 2^16 < g, so ceil(g * 2^16) values go up
+        # exact count: round up iff u + g * 2^16 >= 2^16, so floor(g * 2^16) values go up,
+        # and they are the largest u
         g = (v - lo) / (hi - lo)
-        ups = int((mags == hi).sum())
-        assert ups == math.ceil(g * 65536), (y, ups, g)
+        up = mags == hi
+        ups = int(up.sum())
+        assert ups == math.floor(g * 65536), (y, ups, g)
+        assert np.all(up[65536 - ups:]) and not np.any(up[:65536 - ups])
         # unbiased to within one 2^-16 step of the spacing
         assert abs(mags.mean() - v) <= (hi - lo) / 65536 + 1e-12, y
         # sign kept
@@ -96,9 +116,10 @@ def test_e2m1_sr_saturation_and_signed_zero(orc):
     for y, want in ((6.0, 0x7), (7.5, 0x7), (1e30, 0x7), (-6.0, 0xF), (-300.0, 0xF)):
         assert np.all(orc.encode_e2m1_sr(np.full(65536, y, np.float32), u) == want), y
     assert np.all(orc.encode_e2m1_sr(np.full(65536, -0.0, np.float32), u) == 0x8)
-    # a negative value far below 0.5 rounds up (to -0.5) for u = 0 only
-    q = orc.encode_e2m1_sr(np.full(65536, -1e-30, np.float32), u)
-    assert q[0] == 0x9 and np.all(q[1:] == 0x8)
+    # a negative value far below 2^-17 never reaches -0.5; one of 2^-16 does for u = 65535 only
+    assert np.all(orc.encode_e2m1_sr(np.full(65536, -1e-30, np.float32), u) == 0x8)
+    q = orc.encode_e2m1_sr(np.full(65536, -2.0**-17, np.float32), u)
+    assert q[-1] == 0x9 and np.all(q[:-1] == 0x8)
 
 
 def grid_index(val):
