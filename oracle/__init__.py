@@ -84,6 +84,11 @@ def _load():
         "orc_quantize_block": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, ctypes.c_int, ctypes.c_int, _u32,
                                               _p, _p, _p, _p]),
         "orc_quantize_mx": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, _u32, _p, _p, _p, _p]),
+        "orc_quantize_mx_fmt": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, ctypes.c_int, _u32, _p, _p, _p, _p]),
+        "orc_mx_code_fmt": (_u32, [_f32, ctypes.c_int]),
+        "orc_quantize_block_mode": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, ctypes.c_int, ctypes.c_int,
+                                                   ctypes.c_int, _u32, _p, _p, _p, _p]),
+        "orc_dequant_mx_fmt": (None, [_p, _p, _i64, _i64, ctypes.c_int, _p]),
         "orc_quantize_nvfp4": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, ctypes.c_int, ctypes.c_int, _u32,
                                               _p, _p, _p, _p, _fp, _fp]),
         "orc_quantize_nvfp4_with_amax": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, ctypes.c_int, ctypes.c_int,
@@ -170,8 +175,11 @@ def encode_array(fmt, y):
     return q
 
 
-def mx_code(a):
-    return int(_load().orc_mx_code(float(np.float32(a))))
+def mx_code(a, fmt=None):
+    """E8M0 code of a block amax for MX elements of format fmt (default E4M3)."""
+    if fmt is None:
+        return int(_load().orc_mx_code(float(np.float32(a))))
+    return int(_load().orc_mx_code_fmt(float(np.float32(a)), fmt))
 
 
 def tensor_scales(a, fmax_value):
@@ -244,8 +252,9 @@ def quantize_delayed(x, fmt, state, outputs=ROWWISE, shape=None):
                 amax=np.float32(a.value))
 
 
-def quantize_block(x, block, outputs=ROWWISE, shape=None):
-    """Blockwise E4M3 with fp32 tile scales; block is (1,128) or (128,128)."""
+def quantize_block(x, block, outputs=ROWWISE, shape=None, pow2=False):
+    """Blockwise E4M3 with fp32 tile scales; block is (1,128) or (128,128);
+    pow2=True rounds each tile scale to the MX power of two."""
     p, dt, keep = _in(x)
     R, C = _shape2(keep, shape)
     br, bc = block
@@ -256,8 +265,8 @@ def quantize_block(x, block, outputs=ROWWISE, shape=None):
     s_col = None
     if outputs & COLWISE:
         s_col = np.empty(C * (R // bc) if br == 1 else (C // bc) * (R // br), np.float32)
-    _check(_load().orc_quantize_block(p, dt, R, C, br, bc, outputs, _ptr(q_row), _ptr(s_row), _ptr(q_col),
-                                      _ptr(s_col)), "quantize_block")
+    _check(_load().orc_quantize_block_mode(p, dt, R, C, br, bc, 1 if pow2 else 0, outputs, _ptr(q_row),
+                                           _ptr(s_row), _ptr(q_col), _ptr(s_col)), "quantize_block")
     out["q_row"] = None if q_row is None else q_row.reshape(R, C)
     out["s_row"] = None if s_row is None else s_row.reshape(R // br, C // bc)
     out["q_col"] = None if q_col is None else q_col.reshape(C, R)
@@ -268,19 +277,22 @@ def quantize_block(x, block, outputs=ROWWISE, shape=None):
     return out
 
 
-def quantize_mx(x, outputs=ROWWISE | COLWISE, shape=None):
-    """MXFP8 E4M3 with E8M0 codes; rowwise 1x32 and colwise 32x1 (transposed)."""
+def quantize_mx(x, outputs=ROWWISE | COLWISE, shape=None, fmt=None):
+    """MX with E8M0 codes; rowwise 1x32 and colwise 32x1 (transposed).
+    fmt: E4M3 (default, MXFP8), E5M2, or E2M1 (MXFP4, codes packed two per byte)."""
     p, dt, keep = _in(x)
     R, C = _shape2(keep, shape)
-    q_row = np.empty(R * C, np.uint8) if outputs & ROWWISE else None
+    fmt = E4M3 if fmt is None else fmt
+    k = 2 if fmt == E2M1 else 1
+    q_row = np.empty(R * C // k, np.uint8) if outputs & ROWWISE else None
     e_row = np.empty(R * (C // 32), np.uint8) if outputs & ROWWISE else None
-    q_col = np.empty(R * C, np.uint8) if outputs & COLWISE else None
+    q_col = np.empty(R * C // k, np.uint8) if outputs & COLWISE else None
     e_col = np.empty(C * (R // 32), np.uint8) if outputs & COLWISE else None
-    _check(_load().orc_quantize_mx(p, dt, R, C, outputs, _ptr(q_row), _ptr(e_row), _ptr(q_col), _ptr(e_col)),
-           "quantize_mx")
-    return dict(q_row=None if q_row is None else q_row.reshape(R, C),
+    _check(_load().orc_quantize_mx_fmt(p, dt, R, C, fmt, outputs, _ptr(q_row), _ptr(e_row), _ptr(q_col),
+                                       _ptr(e_col)), "quantize_mx")
+    return dict(q_row=None if q_row is None else q_row.reshape(R, C // k),
                 e_row=None if e_row is None else e_row.reshape(R, C // 32),
-                q_col=None if q_col is None else q_col.reshape(C, R),
+                q_col=None if q_col is None else q_col.reshape(C, R // k),
                 e_col=None if e_col is None else e_col.reshape(C, R // 32))
 
 
@@ -366,12 +378,15 @@ def dequant_block(q, s, block):
     return y.reshape(R, C)
 
 
-def dequant_mx(q, codes):
+def dequant_mx(q, codes, fmt=None):
+    """MX values: element times 2^(code-127); E2M1 q is packed [R, C/2]."""
     q = np.ascontiguousarray(q, dtype=np.uint8)
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
-    R, C = q.shape
+    fmt = E4M3 if fmt is None else fmt
+    R = q.shape[0]
+    C = q.shape[1] * (2 if fmt == E2M1 else 1)
     y = np.empty(R * C, np.float32)
-    _load().orc_dequant_mx(q.ctypes.data, codes.ctypes.data, R, C, y.ctypes.data)
+    _load().orc_dequant_mx_fmt(q.ctypes.data, codes.ctypes.data, R, C, fmt, y.ctypes.data)
     return y.reshape(R, C)
 
 

@@ -392,7 +392,18 @@ int orc_quantize_delayed(const void *x, int dt, int64_t R, int64_t C, int fmt, u
  * inputs and gradients, 128x128 tiles for weights, fp32 scales, pure E4M3).
  * Data is [R,C]; scales are row-major [R/br, C/bc].
  */
-static void block_rowwise(const void *x, int dt, int64_t R, int64_t C, int br, int bc, uint8_t *q, float *sc)
+unsigned orc_mx_code_fmt(float a, int fmt);
+
+/*
+ * READING (power-of-two tile scales, the pow2 option): [MP] "Blockwise
+ * scaling" describes running the blockwise recipe on Blackwell as MXFP8
+ * blocks that share one scaling factor per tile, i.e. an E8M0 power of two;
+ * the tile's scale is then the MX rule applied to the tile amax,
+ * s_B = 2^(floor(log2 a_B) - 8) (orc_mx_code_fmt), stored as its fp32 value,
+ * and the elements are Q_E4M3(x * 2^-e) (exact scaling, saturating).
+ */
+static void block_rowwise(const void *x, int dt, int64_t R, int64_t C, int br, int bc, int pow2, uint8_t *q,
+                          float *sc)
 {
     int64_t tr, tc, r, c;
     int64_t nbc = C / bc;
@@ -400,11 +411,20 @@ static void block_rowwise(const void *x, int dt, int64_t R, int64_t C, int br, i
         for (tc = 0; tc < nbc; tc++) {
             float a = amax_rect(x, dt, C, tr * br, br, tc * bc, bc);
             float alpha, s;
-            orc_tensor_scales(a, 448.0f, &alpha, &s);
+            int e = 0;
+            if (pow2) {
+                e = (int)orc_mx_code_fmt(a, ORC_E4M3) - 127;
+                s = ldexpf(1.0f, e);
+                alpha = 0.0f; /* unused */
+            } else {
+                orc_tensor_scales(a, 448.0f, &alpha, &s);
+            }
             sc[tr * nbc + tc] = s;
             for (r = tr * br; r < (tr + 1) * br; r++)
-                for (c = tc * bc; c < (tc + 1) * bc; c++)
-                    q[r * C + c] = (uint8_t)orc_encode(ORC_E4M3, load_x(x, dt, r * C + c) * alpha);
+                for (c = tc * bc; c < (tc + 1) * bc; c++) {
+                    float v = load_x(x, dt, r * C + c);
+                    q[r * C + c] = (uint8_t)orc_encode(ORC_E4M3, pow2 ? ldexpf(v, -e) : v * alpha);
+                }
         }
 }
 
@@ -416,8 +436,8 @@ static void block_rowwise(const void *x, int dt, int64_t R, int64_t C, int br, i
  *     scales, since a square tile quantizes to the same values either way
  *     ([MP] "Blockwise scaling", the closing remark on 2-D tiles).
  */
-int orc_quantize_block(const void *x, int dt, int64_t R, int64_t C, int br, int bc, unsigned outputs,
-                       uint8_t *q_row, float *s_row, uint8_t *q_col, float *s_col)
+int orc_quantize_block_mode(const void *x, int dt, int64_t R, int64_t C, int br, int bc, int pow2,
+                            unsigned outputs, uint8_t *q_row, float *s_row, uint8_t *q_col, float *s_col)
 {
     if (R <= 0 || C <= 0)
         return -3;
@@ -429,18 +449,18 @@ int orc_quantize_block(const void *x, int dt, int64_t R, int64_t C, int br, int 
         return -1;
     if (br == 1) {
         if (outputs & ORC_ROWWISE)
-            block_rowwise(x, dt, R, C, 1, bc, q_row, s_row);
+            block_rowwise(x, dt, R, C, 1, bc, pow2, q_row, s_row);
         if (outputs & ORC_COLWISE) {
             if (R % bc)
                 return -3;
             void *xt = transpose_input(x, dt, R, C);
-            block_rowwise(xt, dt, C, R, 1, bc, q_col, s_col);
+            block_rowwise(xt, dt, C, R, 1, bc, pow2, q_col, s_col);
             free(xt);
         }
     } else {
         uint8_t *q = q_row ? q_row : (uint8_t *)malloc((size_t)(R * C));
         float *s = s_row ? s_row : (float *)malloc(sizeof(float) * (size_t)((R / br) * (C / bc)));
-        block_rowwise(x, dt, R, C, br, bc, q, s);
+        block_rowwise(x, dt, R, C, br, bc, pow2, q, s);
         if (outputs & ORC_COLWISE) {
             orc_transpose_u8(q, R, C, q_col);
             transpose_f32(s, R / br, C / bc, s_col);
@@ -453,25 +473,43 @@ int orc_quantize_block(const void *x, int dt, int64_t R, int64_t C, int br, int 
     return 0;
 }
 
+int orc_quantize_block(const void *x, int dt, int64_t R, int64_t C, int br, int bc, unsigned outputs,
+                       uint8_t *q_row, float *s_row, uint8_t *q_col, float *s_col)
+{
+    return orc_quantize_block_mode(x, dt, R, C, br, bc, 0, outputs, q_row, s_row, q_col, s_col);
+}
+
 /* ------------------------------------------------------------------ */
 /* MXFP8                                                               */
 /* ------------------------------------------------------------------ */
 
 /*
  * E8M0 code of a 32-element block with amax a: the block scale is the power
- * of two 2^e with e = floor(log2 a) - 8 ([MP] section "MXFP8" and FP8 recipe
- * 5: 32-element blocks sharing one E8M0 power-of-two scale, E4M3 elements).
- * READING: the exponent rule is the one this engine is specified with
- * (8 = floor(log2 448)); e is held to the E8M0 range [-127, 127]; a = 0
- * gives e = -127.
+ * of two 2^e with e = floor(log2 a) - emax, emax = floor(log2 Fmax) of the
+ * element format: 8 for E4M3 (448), 15 for E5M2 (57344), 2 for E2M1 (6)
+ * ([MP] section "MXFP8" and FP8 recipe 5: 32-element blocks sharing one E8M0
+ * power-of-two scale, E4M3 or E5M2 elements; [LP] section 2.4: MXFP4 uses
+ * 32-element blocks with a UE8M0 scale and E2M1 elements).
+ * READING: the exponent rule is the one this engine is specified with for
+ * E4M3 (8 = floor(log2 448)), carried to the other element formats by their
+ * own floor(log2 Fmax); e is held to the E8M0 range [-127, 127]; a = 0
+ * gives e = -127.  Scaled values above Fmax (block maxima with a large
+ * mantissa) saturate.
  */
-unsigned orc_mx_code(float a)
+static int fmt_emax(int fmt)
+{
+    int ex;
+    frexp((double)orc_fmax(fmt), &ex); /* Fmax = f * 2^ex, f in [0.5, 1) */
+    return ex - 1;
+}
+
+unsigned orc_mx_code_fmt(float a, int fmt)
 {
     int ex, e;
     if (a == 0.0f)
         return 0;
-    frexp((double)a, &ex); /* a = f * 2^ex with f in [0.5, 1) */
-    e = (ex - 1) - 8;      /* floor(log2 a) - 8 */
+    frexp((double)a, &ex);          /* a = f * 2^ex with f in [0.5, 1) */
+    e = (ex - 1) - fmt_emax(fmt);   /* floor(log2 a) - emax */
     if (e < -127)
         e = -127;
     if (e > 127)
@@ -479,32 +517,48 @@ unsigned orc_mx_code(float a)
     return (unsigned)(e + 127);
 }
 
-/* Rowwise 1x32 MX blocks of a row-major [R,C] input: q = Q_E4M3(x * 2^-e). */
-static void mx_rowwise(const void *x, int dt, int64_t R, int64_t C, uint8_t *q, uint8_t *codes)
+unsigned orc_mx_code(float a)
+{
+    return orc_mx_code_fmt(a, ORC_E4M3);
+}
+
+static void pack_nibbles(const uint8_t *nib, int64_t R, int64_t C, uint8_t *p);
+
+/* Rowwise 1x32 MX blocks of a row-major [R,C] input: q = Q_fmt(x * 2^-e);
+ * E2M1 codes are packed two per byte. */
+static void mx_rowwise(const void *x, int dt, int64_t R, int64_t C, int fmt, uint8_t *q, uint8_t *codes)
 {
     int64_t r, b, c, nb = C / 32;
+    uint8_t *nib = fmt == ORC_E2M1 ? (uint8_t *)malloc((size_t)(R * C)) : q;
     for (r = 0; r < R; r++)
         for (b = 0; b < nb; b++) {
             float a = amax_rect(x, dt, C, r, 1, b * 32, 32);
-            unsigned code = orc_mx_code(a);
+            unsigned code = orc_mx_code_fmt(a, fmt);
             int e = (int)code - 127;
             codes[r * nb + b] = (uint8_t)code;
             for (c = b * 32; c < b * 32 + 32; c++)
-                q[r * C + c] = (uint8_t)orc_encode(ORC_E4M3, ldexpf(load_x(x, dt, r * C + c), -e));
+                nib[r * C + c] = (uint8_t)orc_encode(fmt, ldexpf(load_x(x, dt, r * C + c), -e));
         }
+    if (fmt == ORC_E2M1) {
+        pack_nibbles(nib, R, C, q);
+        free(nib);
+    }
 }
 
 /*
- * MXFP8: rowwise 1x32 blocks along the rows, and a colwise copy whose 32x1
- * blocks run down the columns, stored transposed: [C,R] bytes and [C,R/32]
- * codes, i.e. the rowwise recipe applied to X^T ([MP] section "MXFP8 recipe":
- * rowwise and colwise copies of the same tensor, 1x32 and 32x1).
+ * MX: rowwise 1x32 blocks along the rows, and a colwise copy whose 32x1
+ * blocks run down the columns, stored transposed: [C,R] codes (E2M1: [C,R/2]
+ * packed) and [C,R/32] scale codes, i.e. the rowwise recipe applied to X^T
+ * ([MP] section "MXFP8 recipe": rowwise and colwise copies of the same
+ * tensor, 1x32 and 32x1).
  */
-int orc_quantize_mx(const void *x, int dt, int64_t R, int64_t C, unsigned outputs,
-                    uint8_t *q_row, uint8_t *e_row, uint8_t *q_col, uint8_t *e_col)
+int orc_quantize_mx_fmt(const void *x, int dt, int64_t R, int64_t C, int fmt, unsigned outputs,
+                        uint8_t *q_row, uint8_t *e_row, uint8_t *q_col, uint8_t *e_col)
 {
     if (R <= 0 || C <= 0)
         return -3;
+    if (fmt != ORC_E4M3 && fmt != ORC_E5M2 && fmt != ORC_E2M1)
+        return -2;
     if (C % 32)
         return -3;
     if ((outputs & ORC_COLWISE) && R % 32)
@@ -512,13 +566,19 @@ int orc_quantize_mx(const void *x, int dt, int64_t R, int64_t C, unsigned output
     if (check_finite(x, dt, R * C))
         return -1;
     if (outputs & ORC_ROWWISE)
-        mx_rowwise(x, dt, R, C, q_row, e_row);
+        mx_rowwise(x, dt, R, C, fmt, q_row, e_row);
     if (outputs & ORC_COLWISE) {
         void *xt = transpose_input(x, dt, R, C);
-        mx_rowwise(xt, dt, C, R, q_col, e_col);
+        mx_rowwise(xt, dt, C, R, fmt, q_col, e_col);
         free(xt);
     }
     return 0;
+}
+
+int orc_quantize_mx(const void *x, int dt, int64_t R, int64_t C, unsigned outputs,
+                    uint8_t *q_row, uint8_t *e_row, uint8_t *q_col, uint8_t *e_col)
+{
+    return orc_quantize_mx_fmt(x, dt, R, C, ORC_E4M3, outputs, q_row, e_row, q_col, e_col);
 }
 
 /* ------------------------------------------------------------------ */
@@ -820,12 +880,25 @@ void orc_dequant_block(const uint8_t *q, const float *sc, int64_t R, int64_t C, 
 
 /* MX: each element times 2^(code-127) of its block ([MP] "MXFP8": value is
  * element times the block's shared scale). */
-void orc_dequant_mx(const uint8_t *q, const uint8_t *codes, int64_t R, int64_t C, float *y)
+/* MX: element times 2^(code - 127); E2M1 elements packed two per byte
+ * ([R, C/2]), element 2k in the low nibble. */
+void orc_dequant_mx_fmt(const uint8_t *q, const uint8_t *codes, int64_t R, int64_t C, int fmt, float *y)
 {
     int64_t r, c;
     for (r = 0; r < R; r++)
-        for (c = 0; c < C; c++)
-            y[r * C + c] = ldexpf((float)orc_decode(ORC_E4M3, q[r * C + c]), (int)codes[r * (C / 32) + c / 32] - 127);
+        for (c = 0; c < C; c++) {
+            unsigned code;
+            if (fmt == ORC_E2M1)
+                code = (q[r * (C / 2) + c / 2] >> (4 * (c % 2))) & 0xFu;
+            else
+                code = q[r * C + c];
+            y[r * C + c] = ldexpf((float)orc_decode(fmt, code), (int)codes[r * (C / 32) + c / 32] - 127);
+        }
+}
+
+void orc_dequant_mx(const uint8_t *q, const uint8_t *codes, int64_t R, int64_t C, float *y)
+{
+    orc_dequant_mx_fmt(q, codes, R, C, ORC_E4M3, y);
 }
 
 /* NVFP4: each element times d_B = fp32(dec(c_B) * S). */
@@ -885,7 +958,7 @@ int orc_requant_mx_colwise(const uint8_t *q_row, const uint8_t *e_row, int64_t R
     orc_dequant_mx(q_row, e_row, R, C, xhat);
     xt = (float *)malloc(sizeof(float) * (size_t)(R * C));
     transpose_f32(xhat, R, C, xt);
-    mx_rowwise(xt, ORC_IN_F32, C, R, q_col, e_col);
+    mx_rowwise(xt, ORC_IN_F32, C, R, ORC_E4M3, q_col, e_col);
     free(xt);
     free(xhat);
     return 0;
