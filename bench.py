@@ -153,9 +153,10 @@ def plane_bytes(w, which):
 
 
 def time_extras(torch, fq, L, stream_p, jobs, steps):
-    """Dequantize (rowwise plane to bf16), MXFP8 rowwise-to-colwise requantize and
-    NVFP4 1x16 with stochastic rounding at the large workloads' shapes, each call
-    bracketed by events; not part of the step."""
+    """Dequantize (rowwise plane to bf16), MXFP8 rowwise-to-colwise requantize,
+    NVFP4 1x16 with stochastic rounding, MX with E5M2 and E2M1 elements and
+    blockwise with power-of-two scales, at the large workloads' shapes, each
+    call bracketed by events; not part of the step."""
     out = {}
     for j in jobs:
         w = j["w"]
@@ -195,6 +196,31 @@ def time_extras(torch, fq, L, stream_p, jobs, steps):
             us = 1e3 * sum(a.elapsed_time(b) for a, b in ev) / steps
             out["nvfp4_1x16_sr/" + w.name] = {"us_per_call": round(us, 2), "bytes": j["bytes"],
                                               "GB/s": round(j["bytes"] / (us * 1e-6) / 1e9, 1)}
+        variants = []
+        if w.recipe == "mx":
+            variants = [("mx_e5m2", fq.desc(fq.FQ_MX, fq.FQ_IN_BF16, fq.FQ_E5M2, R, C, (1, 32), w.outputs),
+                         j["bytes"]),
+                        ("mxfp4", fq.desc(fq.FQ_MX, fq.FQ_IN_BF16, fq.FQ_E2M1, R, C, (1, 32), w.outputs),
+                         2 * R * C + R * C + 2 * (R * C // 32))]
+        if w.recipe == "block":
+            variants = [("block_pow2", fq.desc(fq.FQ_BLOCK_FP32, fq.FQ_IN_BF16, fq.FQ_E4M3, R, C, w.block, w.outputs,
+                                               scale_mode=fq.FQ_SCALE_POW2), j["bytes"])]
+        for vname, dv, nbytes in variants:
+            ov = fq.alloc_quantized(dv)
+            cov = ov.c()
+            for k in range(-1, steps):
+                if k >= 0:
+                    ev[k][0].record()
+                rc = L.fq_quantize(ctypes.byref(dv), j["xp"], ctypes.byref(cov), None, 0, stream_p)
+                if k >= 0:
+                    ev[k][1].record()
+                if rc != fq.FQ_OK:
+                    raise fq.FqError(rc, vname + " " + w.name)
+            torch.cuda.synchronize()
+            us = 1e3 * sum(a.elapsed_time(b) for a, b in ev) / steps
+            out[vname + "/" + w.name] = {"us_per_call": round(us, 2), "bytes": nbytes,
+                                         "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1)}
+            del ov
         if w.recipe == "mx":
             d = fq.desc(fq.FQ_MX, fq.FQ_IN_BF16, fq.FQ_E4M3, R, C, (1, 32), fq.FQ_COLWISE)
             dst = fq.alloc_quantized(d)

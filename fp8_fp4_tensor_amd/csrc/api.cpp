@@ -40,8 +40,10 @@ fq_status check_desc(const fq_desc* d)
         return FQ_E_SHAPE;
     if (d->rounding != FQ_ROUND_NEAREST_EVEN && d->rounding != FQ_ROUND_STOCHASTIC)
         return FQ_E_INVALID;
-    if (d->scale_mode != FQ_SCALE_DEFAULT)
+    if (d->scale_mode != FQ_SCALE_DEFAULT && d->scale_mode != FQ_SCALE_POW2)
         return FQ_E_INVALID;
+    if (d->scale_mode == FQ_SCALE_POW2 && d->recipe != FQ_BLOCK_FP32)
+        return FQ_E_UNSUPPORTED;
     if (d->rounding == FQ_ROUND_STOCHASTIC &&
         !(d->recipe == FQ_NVFP4 && d->block_rows == 1 && d->block_cols == 16))
         return FQ_E_UNSUPPORTED;
@@ -65,7 +67,7 @@ fq_status check_desc(const fq_desc* d)
             return FQ_E_SHAPE;
         return FQ_OK;
     case FQ_MX:
-        if (d->format != FQ_E4M3)
+        if (d->format != FQ_E4M3 && d->format != FQ_E5M2 && d->format != FQ_E2M1)
             return FQ_E_UNSUPPORTED;
         if (!(br == 1 && bc == 32))
             return FQ_E_UNSUPPORTED;
@@ -125,8 +127,8 @@ Sizes sizes_of(const fq_desc* d)
         }
         break;
     case FQ_MX:
-        z.row_data = row ? R * C : 0;
-        z.col_data = col ? R * C : 0;
+        z.row_data = row ? R * C / (d->format == FQ_E2M1 ? 2 : 1) : 0;
+        z.col_data = col ? R * C / (d->format == FQ_E2M1 ? 2 : 1) : 0;
         z.row_scale = row ? R * (C / 32) : 0;
         z.col_scale = col ? C * (R / 32) : 0;
         break;
@@ -308,26 +310,33 @@ fq_status fq_quantize(const fq_desc* d, const void* x, const fq_quantized* o, vo
         src.n_partials = g;
         return run_per_tensor_cast(d, x, src, o, o->tensor_scale, o->amax, nullptr, 0, st);
     }
-    case FQ_BLOCK_FP32:
+    case FQ_BLOCK_FP32: {
         if (n == 0)
             return FQ_OK;
+        const int pow2 = d->scale_mode == FQ_SCALE_POW2;
         if (d->block_rows == 1) {
-            if (row && (s = hip_status(launch_block_1x128(x, bf, R, C, (uint8_t*)o->rowwise.data,
+            if (row && (s = hip_status(launch_block_1x128(x, bf, pow2, R, C, (uint8_t*)o->rowwise.data,
                                                           (float*)o->rowwise.scale, st))) != FQ_OK)
                 return s;
             if (col)
-                return hip_status(launch_block_1x128_colwise(x, bf, R, C, (uint8_t*)o->colwise.data,
+                return hip_status(launch_block_1x128_colwise(x, bf, pow2, R, C, (uint8_t*)o->colwise.data,
                                                              (float*)o->colwise.scale, st));
             return FQ_OK;
         }
-        return hip_status(launch_block_128x128(x, bf, R, C, row ? (uint8_t*)o->rowwise.data : nullptr,
+        return hip_status(launch_block_128x128(x, bf, pow2, R, C, row ? (uint8_t*)o->rowwise.data : nullptr,
                                                row ? (float*)o->rowwise.scale : nullptr,
                                                col ? (uint8_t*)o->colwise.data : nullptr,
                                                col ? (float*)o->colwise.scale : nullptr, st));
+    }
     case FQ_MX:
         if (n == 0)
             return FQ_OK;
-        return hip_status(launch_mx(x, bf, R, C, row ? (uint8_t*)o->rowwise.data : nullptr,
+        if (d->format == FQ_E2M1)
+            return hip_status(launch_mxfp4(x, bf, R, C, row ? (uint8_t*)o->rowwise.data : nullptr,
+                                           row ? (uint8_t*)o->rowwise.scale : nullptr,
+                                           col ? (uint8_t*)o->colwise.data : nullptr,
+                                           col ? (uint8_t*)o->colwise.scale : nullptr, st));
+        return hip_status(launch_mx(x, bf, d->format, R, C, row ? (uint8_t*)o->rowwise.data : nullptr,
                                     row ? (uint8_t*)o->rowwise.scale : nullptr,
                                     col ? (uint8_t*)o->colwise.data : nullptr,
                                     col ? (uint8_t*)o->colwise.scale : nullptr, st));
@@ -450,7 +459,8 @@ fq_status fq_dequantize(const fq_desc* d, const fq_quantized* in, int32_t which,
         return hip_status(launch_dequant_block((const uint8_t*)p.data, (const float*)p.scale, R, C,
                                                d->block_rows, 128, y, bf, st));
     case FQ_MX:
-        return hip_status(launch_dequant_mx((const uint8_t*)p.data, (const uint8_t*)p.scale, R, C, y, bf, st));
+        return hip_status(launch_dequant_mx((const uint8_t*)p.data, (const uint8_t*)p.scale, d->format, R, C, y, bf,
+                                            st));
     case FQ_NVFP4:
         return hip_status(launch_dequant_nvfp4((const uint8_t*)p.data, (const uint8_t*)p.scale, in->tensor_scale, R,
                                                C, d->block_rows, 16, y, bf, st));
@@ -466,9 +476,10 @@ fq_status fq_requantize_transpose(const fq_desc* d, const fq_quantized* in, cons
         return FQ_E_INVALID;
     if (d->rounding != FQ_ROUND_NEAREST_EVEN && d->rounding != FQ_ROUND_STOCHASTIC)
         return FQ_E_INVALID;
-    if (d->scale_mode != FQ_SCALE_DEFAULT)
+    if (d->scale_mode != FQ_SCALE_DEFAULT && d->scale_mode != FQ_SCALE_POW2)
         return FQ_E_INVALID;
     if (d->recipe != FQ_MX || d->format != FQ_E4M3 || d->block_rows != 1 || d->block_cols != 32 ||
+        d->scale_mode != FQ_SCALE_DEFAULT ||
         d->rounding != FQ_ROUND_NEAREST_EVEN)
         return FQ_E_UNSUPPORTED;
     if (d->cols > 0 && d->rows > kMaxElems / d->cols)

@@ -32,17 +32,25 @@ __host__ __device__ __forceinline__ int64_t cdiv(int64_t a, int64_t b) { return 
 
 template <int FMT>
 struct Fmt;
+// kMax: largest finite value; kEmax = floor(log2 kMax); kMantBf16: the 7
+// mantissa bits of kMax as a bf16 (448 and 57344 are 1.75 * 2^e, 6 is 1.5 * 2^2)
 template <>
 struct Fmt<kE4M3> {
     static constexpr float kMax = 448.0f;
+    static constexpr int kEmax = 8;
+    static constexpr uint32_t kMantBf16 = 0x60u;
 };
 template <>
 struct Fmt<kE5M2> {
     static constexpr float kMax = 57344.0f;
+    static constexpr int kEmax = 15;
+    static constexpr uint32_t kMantBf16 = 0x60u;
 };
 template <>
 struct Fmt<kE2M1> {
     static constexpr float kMax = 6.0f;
+    static constexpr int kEmax = 2;
+    static constexpr uint32_t kMantBf16 = 0x40u;
 };
 
 // ---------------------------------------------------------------- bf16
@@ -171,18 +179,21 @@ __device__ __forceinline__ float dec_e2m1(uint32_t nib)
 }
 
 // ---------------------------------------------------------------- MX scale
-// E8M0 code of a block amax a: 2^(floor(log2 a) - 8) held to [2^-127, 2^127]
-// ([MP] "MXFP8": a 32-element block shares one power-of-two E8M0 scale).
+// E8M0 code of a block amax a: 2^(floor(log2 a) - emax) held to
+// [2^-127, 2^127], emax = floor(log2 Fmax) of the element format (8 for
+// E4M3, 15 for E5M2, 2 for E2M1) ([MP] "MXFP8": a 32-element block shares
+// one power-of-two E8M0 scale; [LP] 2.4: MXFP4 likewise with E2M1).
 // From the fp32 bits: floor(log2 a) = E - 127 for the exponent field E of a
-// normal a, so code = max(E - 8, 0); subnormal a (E = 0) and a = 0 give 0.
+// normal a, so code = max(E - emax, 0); subnormal a (E = 0) and a = 0 give 0.
+template <int FMT = kE4M3>
 __device__ __forceinline__ uint32_t mx_code(float a)
 {
     const int e = (int)((__float_as_uint(a) >> 23) & 0xFFu);
-    return (uint32_t)max(e - 8, 0);
+    return (uint32_t)max(e - Fmt<FMT>::kEmax, 0);
 }
-// The fp32 multiplier 2^(127 - code) that scales a block into E4M3 range;
-// for code in [0, 246] it is a normal fp32 power of two, so x * it is exact
-// unless the product leaves the normal range.
+// The fp32 multiplier 2^(127 - code) that scales a block into the element
+// range; for code in [0, 253] it is a normal fp32 power of two, so x * it is
+// exact unless the product leaves the normal range.
 __device__ __forceinline__ float mx_multiplier(uint32_t code) { return __uint_as_float((254u - code) << 23); }
 // 2^(code - 127) as fp32 (code 0 is the subnormal 2^-127).
 __device__ __forceinline__ float e8m0_value(uint32_t code)

@@ -7,6 +7,9 @@
 // three GEMMs that read X^T with 1x128 tiles and W^T with 128x128 tiles).
 // Each tile is quantized like a tensor under current scaling:
 // a_B = max|x|, alpha_B = 448/a_B, q = Q(fp32(alpha_B x)), s_B = a_B/448.
+// With power-of-two scales (the section's MXFP8 emulation, a tile as MX
+// blocks sharing one E8M0 scale): s_B = 2^(floor(log2 a_B) - 8), alpha_B =
+// 1/s_B, both exact powers of two, so alpha_B x is exact.
 //
 //   k_block_1x128      rows are contiguous, so 1x128 tiles are consecutive
 //                      128-element runs of the flat tensor: one tile is 16
@@ -32,7 +35,20 @@ namespace {
 constexpr int kLoads = 4;
 constexpr int kMaxGrid = 16384;
 
-template <typename T>
+// Tile multiplier and stored scale from the tile amax.
+template <bool POW2>
+__device__ __forceinline__ void tile_scales(float a, float& alpha, float& s)
+{
+    if constexpr (POW2) {
+        const uint32_t code = mx_code<kE4M3>(a);
+        alpha = mx_multiplier(code);
+        s = e8m0_value(code);
+    } else {
+        tensor_scales(a, 448.0f, alpha, s);
+    }
+}
+
+template <typename T, bool POW2>
 __global__ __launch_bounds__(kWG) void k_block_1x128(const T* __restrict__ x, int64_t n, uint8_t* __restrict__ q,
                                                      float* __restrict__ s_out)
 {
@@ -57,7 +73,7 @@ __global__ __launch_bounds__(kWG) void k_block_1x128(const T* __restrict__ x, in
             In<T>::unpack(v[j], f);
             const float a = max_lanes<LPB>(absmax<E>(f));
             float alpha, s;
-            tensor_scales(a, 448.0f, alpha, s);
+            tile_scales<POW2>(a, alpha, s);
             if (e < n) {
                 Enc8<kE4M3, E>::store(q + e, f, alpha);
                 if ((lane & (LPB - 1)) == 0)
@@ -68,7 +84,7 @@ __global__ __launch_bounds__(kWG) void k_block_1x128(const T* __restrict__ x, in
 }
 
 // Colwise 1x128: tiles of X^T. Slab of 128 rows x TC columns in LDS.
-template <typename T>
+template <typename T, bool POW2>
 __global__ __launch_bounds__(kWG) void k_block_1x128_col(const T* __restrict__ x, int64_t R, int64_t C,
                                                          uint8_t* __restrict__ qt, float* __restrict__ st)
 {
@@ -96,7 +112,7 @@ __global__ __launch_bounds__(kWG) void k_block_1x128_col(const T* __restrict__ x
     for (int r = 0; r < 128; ++r)
         a = fmaxf(a, fabsf(In<T>::load1(tile, (int64_t)r * TC + c)));
     float alpha, s;
-    tensor_scales(a, 448.0f, alpha, s);
+    tile_scales<POW2>(a, alpha, s);
     uint8_t* out = qt + (c0 + c) * R + r0;
 #pragma unroll 2
     for (int r = 0; r < 128; r += 16) {
@@ -116,7 +132,7 @@ __global__ __launch_bounds__(kWG) void k_block_1x128_col(const T* __restrict__ x
 
 // 128x128 tiles, one workgroup each. q/s rowwise (may be null), qt/st
 // colwise (may be null).
-template <typename T>
+template <typename T, bool POW2>
 __global__ __launch_bounds__(kWG) void k_block_128x128(const T* __restrict__ x, int64_t R, int64_t C,
                                                        uint8_t* __restrict__ q, float* __restrict__ s_out,
                                                        uint8_t* __restrict__ qt, float* __restrict__ st)
@@ -141,7 +157,7 @@ __global__ __launch_bounds__(kWG) void k_block_128x128(const T* __restrict__ x, 
     }
     const float a = max_workgroup(m, lds);
     float alpha, s;
-    tensor_scales(a, 448.0f, alpha, s);
+    tile_scales<POW2>(a, alpha, s);
 #pragma unroll
     for (int k = 0; k < ROUNDS; ++k) {
         float f[E];
@@ -190,40 +206,58 @@ __global__ __launch_bounds__(kWG) void k_block_128x128(const T* __restrict__ x, 
 
 }  // namespace
 
-hipError_t launch_block_1x128(const void* x, int in_bf16, int64_t R, int64_t C, uint8_t* q, float* s,
+hipError_t launch_block_1x128(const void* x, int in_bf16, int pow2, int64_t R, int64_t C, uint8_t* q, float* s,
                               hipStream_t stream)
 {
     const int64_t n = R * C;
     const int E = in_bf16 ? 8 : 4;
     const int64_t per_wg = (int64_t)kWG * E * kLoads;
     const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(n, per_wg), kMaxGrid));
-    if (in_bf16)
-        k_block_1x128<uint16_t><<<grid, kWG, 0, stream>>>((const uint16_t*)x, n, q, s);
+    const uint16_t* xb = (const uint16_t*)x;
+    const float* xf = (const float*)x;
+    if (in_bf16 && pow2)
+        k_block_1x128<uint16_t, true><<<grid, kWG, 0, stream>>>(xb, n, q, s);
+    else if (in_bf16)
+        k_block_1x128<uint16_t, false><<<grid, kWG, 0, stream>>>(xb, n, q, s);
+    else if (pow2)
+        k_block_1x128<float, true><<<grid, kWG, 0, stream>>>(xf, n, q, s);
     else
-        k_block_1x128<float><<<grid, kWG, 0, stream>>>((const float*)x, n, q, s);
+        k_block_1x128<float, false><<<grid, kWG, 0, stream>>>(xf, n, q, s);
     return hipGetLastError();
 }
 
-hipError_t launch_block_1x128_colwise(const void* x, int in_bf16, int64_t R, int64_t C, uint8_t* qt, float* st,
-                                      hipStream_t stream)
+hipError_t launch_block_1x128_colwise(const void* x, int in_bf16, int pow2, int64_t R, int64_t C, uint8_t* qt,
+                                      float* st, hipStream_t stream)
 {
     const int tc = in_bf16 ? 256 : 128;
     const unsigned grid = (unsigned)(cdiv(C, tc) * (R / 128));
-    if (in_bf16)
-        k_block_1x128_col<uint16_t><<<grid, kWG, 128 * 256 * 2, stream>>>((const uint16_t*)x, R, C, qt, st);
+    const uint16_t* xb = (const uint16_t*)x;
+    const float* xf = (const float*)x;
+    if (in_bf16 && pow2)
+        k_block_1x128_col<uint16_t, true><<<grid, kWG, 128 * 256 * 2, stream>>>(xb, R, C, qt, st);
+    else if (in_bf16)
+        k_block_1x128_col<uint16_t, false><<<grid, kWG, 128 * 256 * 2, stream>>>(xb, R, C, qt, st);
+    else if (pow2)
+        k_block_1x128_col<float, true><<<grid, kWG, 128 * 128 * 4, stream>>>(xf, R, C, qt, st);
     else
-        k_block_1x128_col<float><<<grid, kWG, 128 * 128 * 4, stream>>>((const float*)x, R, C, qt, st);
+        k_block_1x128_col<float, false><<<grid, kWG, 128 * 128 * 4, stream>>>(xf, R, C, qt, st);
     return hipGetLastError();
 }
 
-hipError_t launch_block_128x128(const void* x, int in_bf16, int64_t R, int64_t C, uint8_t* q, float* s,
+hipError_t launch_block_128x128(const void* x, int in_bf16, int pow2, int64_t R, int64_t C, uint8_t* q, float* s,
                                 uint8_t* qt, float* st, hipStream_t stream)
 {
     const unsigned grid = (unsigned)((C / 128) * (R / 128));
-    if (in_bf16)
-        k_block_128x128<uint16_t><<<grid, kWG, 0, stream>>>((const uint16_t*)x, R, C, q, s, qt, st);
+    const uint16_t* xb = (const uint16_t*)x;
+    const float* xf = (const float*)x;
+    if (in_bf16 && pow2)
+        k_block_128x128<uint16_t, true><<<grid, kWG, 0, stream>>>(xb, R, C, q, s, qt, st);
+    else if (in_bf16)
+        k_block_128x128<uint16_t, false><<<grid, kWG, 0, stream>>>(xb, R, C, q, s, qt, st);
+    else if (pow2)
+        k_block_128x128<float, true><<<grid, kWG, 0, stream>>>(xf, R, C, q, s, qt, st);
     else
-        k_block_128x128<float><<<grid, kWG, 0, stream>>>((const float*)x, R, C, q, s, qt, st);
+        k_block_128x128<float, false><<<grid, kWG, 0, stream>>>(xf, R, C, q, s, qt, st);
     return hipGetLastError();
 }
 

@@ -6,7 +6,8 @@
 // (notes.kuangjux.top), section "Current Scaling" (restored value = q * s)
 // and section "实现接口与精度边界" (a quantized tensor supports dequantize);
 // [MP] "混合精度训练：fp16 到 fp8" (garden.houmin.site), section "MXFP8"
-// (value = element x block scale) and section "NVFP4".
+// (value = element x block scale; E4M3 or E5M2 elements) and section
+// "NVFP4"; [LP] "从 BF16 到 FP8/FP4" section 2.4 (MXFP4).
 //
 // Bandwidth layout: a thread step is 16 elements (16 code bytes, or 8 packed
 // FP4 bytes) read with one vector load and written as 64 (fp32) or 32 (bf16)
@@ -209,10 +210,15 @@ hipError_t launch_dequant_block(const uint8_t* q, const float* s, int64_t R, int
     return hipGetLastError();
 }
 
-hipError_t launch_dequant_mx(const uint8_t* q, const uint8_t* e, int64_t R, int64_t C, void* y, int bf,
+hipError_t launch_dequant_mx(const uint8_t* q, const uint8_t* e, int fmt, int64_t R, int64_t C, void* y, int bf,
                              hipStream_t stream)
 {
-    rows_t<kDqE4M3, 1>(q, e, nullptr, R, C, 1, 32, y, bf, stream);
+    if (fmt == kE2M1)
+        rows_t<kDqFp4, 1>(q, e, nullptr, R, C, 1, 32, y, bf, stream);
+    else if (fmt == kE5M2)
+        rows_t<kDqE5M2, 1>(q, e, nullptr, R, C, 1, 32, y, bf, stream);
+    else
+        rows_t<kDqE4M3, 1>(q, e, nullptr, R, C, 1, 32, y, bf, stream);
     return hipGetLastError();
 }
 

@@ -1,14 +1,16 @@
-// k_mx.hip -- MXFP8: E4M3 elements in 32-element blocks that share one E8M0
-// (power-of-two) scale, rowwise (1x32 along a row) and colwise (32x1 down a
-// column, stored transposed), both from a single read of the input.
+// k_mx.hip -- MX: E4M3 (MXFP8) or E5M2 elements in 32-element blocks that
+// share one E8M0 (power-of-two) scale, rowwise (1x32 along a row) and colwise
+// (32x1 down a column, stored transposed), both from a single read of the
+// input. (MXFP4 elements: k_mxfp4.hip.)
 //
 // Source: [MP] "混合精度训练：fp16 到 fp8" (garden.houmin.site), section
 // "MXFP8" (32-element blocks, one E8M0 scale each, value = element x scale;
 // E8M0 is the exponent field of an fp32), "FP8 recipe" item 5 (E4M3, 1x32
 // for inputs, gradients and weights) and "MXFP8 recipe" (rowwise and colwise
 // copies of each tensor, 1x32 and 32x1).
-// Block scale: 2^e with e = floor(log2 amax) - 8 (8 = floor(log2 448)),
-// held to the E8M0 range; q = Q_E4M3(x * 2^-e), exact multiply, saturating.
+// Block scale: 2^e with e = floor(log2 amax) - emax (8 = floor(log2 448) for
+// E4M3, 15 = floor(log2 57344) for E5M2), held to the E8M0 range;
+// q = Q(x * 2^-e), exact multiply, saturating.
 //
 // One workgroup per 128x128 tile. Rowwise: each lane holds 16 bytes of a
 // row, a quad of lanes is one 1x32 block (bf16), reduced with two DPP steps;
@@ -52,7 +54,7 @@ __device__ __forceinline__ void mx_load_tile(const T* __restrict__ x, int64_t R,
 // Persistent: workgroup g takes tiles g, g + G, ..., with G the number of
 // workgroups the device holds at once, so no tail of late workgroups forms;
 // the resident workgroups of a CU overlap each other's loads and compute.
-template <typename T>
+template <typename T, int FMT>
 __global__ __launch_bounds__(kWG) void k_mx(const T* __restrict__ x, int64_t R, int64_t C,
                                             uint8_t* __restrict__ q, uint8_t* __restrict__ e,
                                             uint8_t* __restrict__ qt, uint8_t* __restrict__ et)
@@ -83,7 +85,7 @@ __global__ __launch_bounds__(kWG) void k_mx(const T* __restrict__ x, int64_t R, 
                 float f[E];
                 In<T>::unpack(v[k], f);
                 const float a = max_lanes<LPB>(absmax<E>(f));
-                const uint32_t code = mx_code(a);
+                const uint32_t code = mx_code<FMT>(a);
                 const float mult = mx_multiplier(code);
                 // the row's four block codes, gathered into its first lane
                 const int rbase = lane & ~(LPR - 1);
@@ -92,7 +94,7 @@ __global__ __launch_bounds__(kWG) void k_mx(const T* __restrict__ x, int64_t R, 
                                       ((uint32_t)__shfl((int)code, rbase + 2 * LPB) << 16) |
                                       ((uint32_t)__shfl((int)code, rbase + 3 * LPB) << 24);
                 if (col_in && r0 + rr < R) {
-                    Enc8<kE4M3, E>::store(q + (r0 + rr) * C + c0 + cc, f, mult);
+                    Enc8<FMT, E>::store(q + (r0 + rr) * C + c0 + cc, f, mult);
                     if (full_row_codes) {
                         if (lane == rbase)
                             *reinterpret_cast<uint32_t*>(e + (r0 + rr) * nbc + c0 / 32) = word;
@@ -124,14 +126,14 @@ __global__ __launch_bounds__(kWG) void k_mx(const T* __restrict__ x, int64_t R, 
                 a0 = fmaxf(a0, fabsf(bf16_lo(pr[k])));
                 a1 = fmaxf(a1, fabsf(bf16_hi(pr[k])));
             }
-            codes2[0] = mx_code(a0);
-            codes2[1] = mx_code(a1);
+            codes2[0] = mx_code<FMT>(a0);
+            codes2[1] = mx_code<FMT>(a1);
             const float m0 = mx_multiplier(codes2[0]), m1 = mx_multiplier(codes2[1]);
 #pragma unroll
             for (int d = 0; d < 8; ++d) {
-                w[d >> 2][d & 3] = enc4<kE4M3>(bf16_lo(pr[4 * d]), bf16_lo(pr[4 * d + 1]), bf16_lo(pr[4 * d + 2]),
+                w[d >> 2][d & 3] = enc4<FMT>(bf16_lo(pr[4 * d]), bf16_lo(pr[4 * d + 1]), bf16_lo(pr[4 * d + 2]),
                                                bf16_lo(pr[4 * d + 3]), m0);
-                w[2 + (d >> 2)][d & 3] = enc4<kE4M3>(bf16_hi(pr[4 * d]), bf16_hi(pr[4 * d + 1]),
+                w[2 + (d >> 2)][d & 3] = enc4<FMT>(bf16_hi(pr[4 * d]), bf16_hi(pr[4 * d + 1]),
                                                      bf16_hi(pr[4 * d + 2]), bf16_hi(pr[4 * d + 3]), m1);
             }
         } else {
@@ -141,11 +143,11 @@ __global__ __launch_bounds__(kWG) void k_mx(const T* __restrict__ x, int64_t R, 
 #pragma unroll
                 for (int k = 0; k < 32; ++k)
                     f[k] = In<T>::load1(tile, (int64_t)(32 * rb + k) * P + 2 * pc + j);
-                codes2[j] = mx_code(absmax<32>(f));
+                codes2[j] = mx_code<FMT>(absmax<32>(f));
                 const float m = mx_multiplier(codes2[j]);
 #pragma unroll
                 for (int d = 0; d < 8; ++d)
-                    w[2 * j + (d >> 2)][d & 3] = enc4<kE4M3>(f[4 * d], f[4 * d + 1], f[4 * d + 2], f[4 * d + 3], m);
+                    w[2 * j + (d >> 2)][d & 3] = enc4<FMT>(f[4 * d], f[4 * d + 1], f[4 * d + 2], f[4 * d + 3], m);
             }
         }
         __syncthreads();
@@ -183,10 +185,11 @@ __global__ __launch_bounds__(kWG) void k_mx(const T* __restrict__ x, int64_t R, 
 }
 
 // ---------------------------------------------------------------- bf16 fast path
-// The same MXFP8 computation for bf16 inputs, on packed bf16 pairs, with the
-// gfx950 converter that takes bf16 and a power-of-two scale directly
-// (v_cvt_scalef32_pk_fp8_bf16: two elements, each divided by the scale and
-// rounded to nearest even). It equals Q_E4M3(x * 2^-e) for every finite bf16
+// The same MX computation for bf16 inputs, on packed bf16 pairs, with the
+// gfx950 converters that take bf16 and a power-of-two scale directly
+// (v_cvt_scalef32_pk_fp8_bf16 / _bf8_bf16: two elements, each divided by the
+// scale and rounded to nearest even; E5M2 elements go through the same
+// steps with its own emax and limit). It equals Q_E4M3(x * 2^-e) for every finite bf16
 // x and every E8M0 code, as long as |x * 2^-e| <= 448; beyond that it gives
 // NaN instead of saturating. A block's scaled values stay below 512, so the
 // magnitudes are first clamped, as bf16 bit patterns, to the pattern of
@@ -210,22 +213,37 @@ __device__ __forceinline__ uint32_t pk_min16(uint32_t a, uint32_t b)
     return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, a),
                                                                   __builtin_bit_cast(u16x2, b)));
 }
-// bf16 pattern of 448 * 2^(code - 127): exponent field code + 8, mantissa 1.75
-__device__ __forceinline__ uint32_t mx_limit_bf16(uint32_t code) { return ((code + 8u) << 7) | 0x60u; }
+// bf16 pattern of Fmax * 2^(code - 127): exponent field code + emax, the
+// mantissa of Fmax (448 * 2^e: code + 8, 1.75; 57344 * 2^e: code + 15, 1.75)
+template <int FMT>
+__device__ __forceinline__ uint32_t mx_limit_bf16(uint32_t code)
+{
+    return ((code + (uint32_t)Fmt<FMT>::kEmax) << 7) | Fmt<FMT>::kMantBf16;
+}
 // E8M0 code from the bf16 magnitude bits of a block amax
-__device__ __forceinline__ uint32_t mx_code_bf16(uint32_t mag) { return (uint32_t)max((int)((mag >> 7) & 0xFFu) - 8, 0); }
+template <int FMT>
+__device__ __forceinline__ uint32_t mx_code_bf16(uint32_t mag)
+{
+    return (uint32_t)max((int)((mag >> 7) & 0xFFu) - Fmt<FMT>::kEmax, 0);
+}
 // clamp both magnitudes of a pair to lim2 (limit in each half, below
 // 0x8000), keep the signs
 __device__ __forceinline__ uint32_t clamp_pair(uint32_t w, uint32_t lim2)
 {
     return pk_min16(w & 0x7fff7fffu, lim2) | (w & 0x80008000u);
 }
-// two clamped bf16 pairs -> four E4M3 codes (pair a in bytes 0-1, b in 2-3)
+// two clamped bf16 pairs -> four E4M3 (or E5M2) codes (pair a in bytes 0-1, b in 2-3)
+template <int FMT>
 __device__ __forceinline__ uint32_t cvt4_scaled(uint32_t a, uint32_t b, float scale)
 {
     s16x2 r = {0, 0};
-    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(bf16x2, a), scale, false);
-    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(bf16x2, b), scale, true);
+    if constexpr (FMT == kE4M3) {
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(bf16x2, a), scale, false);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(bf16x2, b), scale, true);
+    } else {
+        r = __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(r, __builtin_bit_cast(bf16x2, a), scale, false);
+        r = __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(r, __builtin_bit_cast(bf16x2, b), scale, true);
+    }
     return __builtin_bit_cast(uint32_t, r);
 }
 template <int CTRL>
@@ -234,6 +252,7 @@ __device__ __forceinline__ uint32_t dppu(uint32_t v)
     return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
 
+template <int FMT>
 __global__ __launch_bounds__(kWG) void k_mx_bf16(const uint16_t* __restrict__ x, int64_t R, int64_t C,
                                                  uint8_t* __restrict__ q, uint8_t* __restrict__ e,
                                                  uint8_t* __restrict__ qt, uint8_t* __restrict__ et)
@@ -275,12 +294,12 @@ __global__ __launch_bounds__(kWG) void k_mx_bf16(const uint16_t* __restrict__ x,
                     m = max(m & 0xFFFFu, m >> 16);
                     m = max(m, dppu<kDppXor1>(m));
                     m = max(m, dppu<kDppXor2>(m));  // the 1x32 block: a quad of lanes
-                    const uint32_t code = mx_code_bf16(m);
-                    const uint32_t lim = mx_limit_bf16(code), lim2 = lim | (lim << 16);
+                    const uint32_t code = mx_code_bf16<FMT>(m);
+                    const uint32_t lim = mx_limit_bf16<FMT>(code), lim2 = lim | (lim << 16);
                     const float scale = e8m0_value(code);
                     u32x2 w;
-                    w[0] = cvt4_scaled(clamp_pair(v[k][0], lim2), clamp_pair(v[k][1], lim2), scale);
-                    w[1] = cvt4_scaled(clamp_pair(v[k][2], lim2), clamp_pair(v[k][3], lim2), scale);
+                    w[0] = cvt4_scaled<FMT>(clamp_pair(v[k][0], lim2), clamp_pair(v[k][1], lim2), scale);
+                    w[1] = cvt4_scaled<FMT>(clamp_pair(v[k][2], lim2), clamp_pair(v[k][3], lim2), scale);
                     // the row's four block codes into its first lane (DPP row_shl 4, 8, 12)
                     const int rbase = lane & ~15;
                     const uint32_t word = code | (dppu<0x104>(code) << 8) | (dppu<0x108>(code) << 16) |
@@ -317,9 +336,9 @@ __global__ __launch_bounds__(kWG) void k_mx_bf16(const uint16_t* __restrict__ x,
 #pragma unroll
             for (int k = 0; k < 32; ++k)
                 m = pk_max16(m, pr[k] & 0x7fff7fffu);
-            code0 = mx_code_bf16(m & 0xFFFFu);
-            code1 = mx_code_bf16(m >> 16);
-            const uint32_t lim2 = mx_limit_bf16(code0) | (mx_limit_bf16(code1) << 16);
+            code0 = mx_code_bf16<FMT>(m & 0xFFFFu);
+            code1 = mx_code_bf16<FMT>(m >> 16);
+            const uint32_t lim2 = mx_limit_bf16<FMT>(code0) | (mx_limit_bf16<FMT>(code1) << 16);
             const float s0 = e8m0_value(code0), s1 = e8m0_value(code1);
 #pragma unroll
             for (int k = 0; k < 32; ++k)
@@ -331,8 +350,8 @@ __global__ __launch_bounds__(kWG) void k_mx_bf16(const uint16_t* __restrict__ x,
                 const uint32_t b0 = __builtin_amdgcn_perm(pr[4 * d + 3], pr[4 * d + 2], 0x05040100u);
                 const uint32_t a1 = __builtin_amdgcn_perm(pr[4 * d + 1], pr[4 * d], 0x07060302u);
                 const uint32_t b1 = __builtin_amdgcn_perm(pr[4 * d + 3], pr[4 * d + 2], 0x07060302u);
-                w[d >> 2][d & 3] = cvt4_scaled(a0, b0, s0);
-                w[2 + (d >> 2)][d & 3] = cvt4_scaled(a1, b1, s1);
+                w[d >> 2][d & 3] = cvt4_scaled<FMT>(a0, b0, s0);
+                w[2 + (d >> 2)][d & 3] = cvt4_scaled<FMT>(a1, b1, s1);
             }
         }
         __syncthreads();
@@ -366,6 +385,159 @@ __global__ __launch_bounds__(kWG) void k_mx_bf16(const uint16_t* __restrict__ x,
                 *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(ocode + row * 4);
             } else {
                 for (int j = 0; j < nbytes / 32; ++j)
+                    dst[j] = ocode[row * 4 + j];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- MXFP4 from bf16
+// MXFP4 (E2M1 elements, two per byte) with the same tile walk as k_mx_bf16:
+// both planes from one read. Magnitudes are clamped as bf16 patterns to
+// 6 * 2^e (exact), then v_cvt_scalef32_pk_fp4_bf16 divides each pair by the
+// power-of-two scale and rounds to nearest even. A row of X^T gets 64 bytes
+// per tile (128 rows of 4-bit codes), written by four lanes.
+constexpr int kOP4 = 64 + 16;  // pitch of the LDS tile of transposed FP4 codes
+
+// four clamped bf16 pairs (elements 2i, 2i+1 in pair i) -> one dword of E2M1, element k in bits 4k..4k+3
+__device__ __forceinline__ uint32_t cvt8_fp4_scaled(uint32_t p0, uint32_t p1, uint32_t p2, uint32_t p3, float scale)
+{
+    uint32_t w = 0;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, __builtin_bit_cast(bf16x2, p0), scale, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, __builtin_bit_cast(bf16x2, p1), scale, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, __builtin_bit_cast(bf16x2, p2), scale, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, __builtin_bit_cast(bf16x2, p3), scale, 3);
+    return w;
+}
+
+__global__ __launch_bounds__(kWG) void k_mxfp4_bf16(const uint16_t* __restrict__ x, int64_t R, int64_t C,
+                                                    uint8_t* __restrict__ q, uint8_t* __restrict__ e,
+                                                    uint8_t* __restrict__ qt, uint8_t* __restrict__ et)
+{
+    constexpr int ROUNDS = 8, P = 128 + 8;
+    static_assert(128 * kOP4 + 128 * 4 <= 128 * P * 2, "the code tile must fit in the input tile it reuses");
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint16_t* tile = reinterpret_cast<uint16_t*>(smem);
+    const int lane = threadIdx.x & 63;
+    const int64_t ntc = cdiv(C, 128), ntiles = ntc * cdiv(R, 128);
+    const int cc = (threadIdx.x & 15) * 8, rr0 = threadIdx.x >> 4;
+    const int64_t nbc = C / 32, nbr = R / 32;
+    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const int64_t r0 = (t / ntc) * 128, c0 = (t % ntc) * 128;
+        const bool col_in = c0 + cc < C;
+        u32x4 v[ROUNDS];
+        {
+            const uint16_t* src = x + (r0 + rr0) * C + c0 + cc;
+            const int64_t step = 16 * C;
+#pragma unroll
+            for (int k = 0; k < ROUNDS; ++k) {
+                v[k] = (col_in && r0 + rr0 + 16 * k < R) ? ld16_stream(src) : u32x4{0u, 0u, 0u, 0u};
+                src += step;
+            }
+        }
+        const bool full_row_codes = c0 + 128 <= C && (nbc & 3) == 0;
+        if (qt)
+            __syncthreads();  // the previous tile's LDS reads are done
+        {
+            uint8_t* dst = q ? q + (r0 + rr0) * (C / 2) + (c0 + cc) / 2 : nullptr;
+            uint8_t* edst = q ? e + (r0 + rr0) * nbc + c0 / 32 : nullptr;
+#pragma unroll
+            for (int k = 0; k < ROUNDS; ++k) {
+                const int rr = rr0 + 16 * k;
+                if (qt)
+                    *reinterpret_cast<u32x4*>(tile + rr * P + cc) = v[k];
+                if (q) {
+                    uint32_t m = pk_max16(pk_max16(v[k][0] & 0x7fff7fffu, v[k][1] & 0x7fff7fffu),
+                                          pk_max16(v[k][2] & 0x7fff7fffu, v[k][3] & 0x7fff7fffu));
+                    m = max(m & 0xFFFFu, m >> 16);
+                    m = max(m, dppu<kDppXor1>(m));
+                    m = max(m, dppu<kDppXor2>(m));  // the 1x32 block: a quad of lanes
+                    const uint32_t code = mx_code_bf16<kE2M1>(m);
+                    const uint32_t lim = mx_limit_bf16<kE2M1>(code), lim2 = lim | (lim << 16);
+                    const uint32_t w = cvt8_fp4_scaled(clamp_pair(v[k][0], lim2), clamp_pair(v[k][1], lim2),
+                                                       clamp_pair(v[k][2], lim2), clamp_pair(v[k][3], lim2),
+                                                       e8m0_value(code));
+                    const int rbase = lane & ~15;
+                    const uint32_t word = code | (dppu<0x104>(code) << 8) | (dppu<0x108>(code) << 16) |
+                                          (dppu<0x10C>(code) << 24);
+                    if (col_in && r0 + rr < R) {
+                        st4_stream(dst, w);
+                        if (full_row_codes) {
+                            if (lane == rbase)
+                                *reinterpret_cast<uint32_t*>(edst) = word;
+                        } else if ((lane & 3) == 0) {
+                            edst[cc / 32] = (uint8_t)code;
+                        }
+                    }
+                    dst += 16 * (C / 2);
+                    edst += 16 * nbc;
+                }
+            }
+        }
+        if (!qt)
+            continue;
+        __syncthreads();
+        // colwise: thread (p, rb) takes tile columns 2p, 2p+1, rows 32rb..+31
+        const int pc = threadIdx.x & 63, rb = threadIdx.x >> 6;
+        u32x4 w0, w1;
+        uint32_t code0, code1;
+        {
+            uint32_t pr[32];
+#pragma unroll
+            for (int k = 0; k < 32; ++k)
+                pr[k] = *reinterpret_cast<const uint32_t*>(tile + (32 * rb + k) * P + 2 * pc);
+            uint32_t m = 0;
+#pragma unroll
+            for (int k = 0; k < 32; ++k)
+                m = pk_max16(m, pr[k] & 0x7fff7fffu);
+            code0 = mx_code_bf16<kE2M1>(m & 0xFFFFu);
+            code1 = mx_code_bf16<kE2M1>(m >> 16);
+            const uint32_t lim2 = mx_limit_bf16<kE2M1>(code0) | (mx_limit_bf16<kE2M1>(code1) << 16);
+            const float s0 = e8m0_value(code0), s1 = e8m0_value(code1);
+#pragma unroll
+            for (int k = 0; k < 32; ++k)
+                pr[k] = clamp_pair(pr[k], lim2);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                // rows 8d..8d+7: column 2p from the low halves, column 2p+1 from the high halves
+                uint32_t lo[4], hi[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    lo[i] = __builtin_amdgcn_perm(pr[8 * d + 2 * i + 1], pr[8 * d + 2 * i], 0x05040100u);
+                    hi[i] = __builtin_amdgcn_perm(pr[8 * d + 2 * i + 1], pr[8 * d + 2 * i], 0x07060302u);
+                }
+                w0[d] = cvt8_fp4_scaled(lo[0], lo[1], lo[2], lo[3], s0);
+                w1[d] = cvt8_fp4_scaled(hi[0], hi[1], hi[2], hi[3], s1);
+            }
+        }
+        __syncthreads();
+        uint8_t* otile = smem;               // [128][kOP4] FP4 codes of X^T (64 bytes per row)
+        uint8_t* ocode = smem + 128 * kOP4;  // [128][4] E8M0 codes of X^T
+        *reinterpret_cast<u32x4*>(otile + (2 * pc) * kOP4 + 16 * rb) = w0;
+        *reinterpret_cast<u32x4*>(otile + (2 * pc + 1) * kOP4 + 16 * rb) = w1;
+        ocode[(2 * pc) * 4 + rb] = (uint8_t)code0;
+        ocode[(2 * pc + 1) * 4 + rb] = (uint8_t)code1;
+        __syncthreads();
+        const int64_t nrows = min((int64_t)128, C - c0), nbytes = min((int64_t)128, R - r0) / 2;
+        {
+            const int row0 = threadIdx.x >> 2, seg = (threadIdx.x & 3) * 16;
+            uint8_t* dst = qt + (c0 + row0) * (R / 2) + r0 / 2 + seg;
+            const int64_t step = 64 * (R / 2);
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int row = row0 + 64 * k;
+                if (row < nrows && seg < nbytes)
+                    st16_stream(dst, *reinterpret_cast<const u32x4*>(otile + row * kOP4 + seg));
+                dst += step;
+            }
+        }
+        if (threadIdx.x < nrows) {
+            const int row = threadIdx.x;
+            uint8_t* dst = et + (c0 + row) * nbr + r0 / 32;
+            if (nbytes == 64 && (nbr & 3) == 0) {
+                *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(ocode + row * 4);
+            } else {
+                for (int j = 0; j < nbytes / 16; ++j)
                     dst[j] = ocode[row * 4 + j];
             }
         }
@@ -463,21 +635,42 @@ __global__ __launch_bounds__(kWG) void k_mx_requant(const uint8_t* __restrict__ 
 
 }  // namespace
 
-hipError_t launch_mx(const void* x, int in_bf16, int64_t R, int64_t C, uint8_t* q, uint8_t* e, uint8_t* qt,
-                     uint8_t* et, hipStream_t stream)
+template <int FMT>
+void launch_mx_t(const void* x, int in_bf16, int64_t R, int64_t C, uint8_t* q, uint8_t* e, uint8_t* qt,
+                 uint8_t* et, hipStream_t stream)
 {
     const int64_t ntiles = cdiv(C, 128) * cdiv(R, 128);
     if (in_bf16) {
         const size_t lds = qt ? 128 * tile_pitch<uint16_t>() * 2 : 0;
         static ResidentGrid cache;
-        const int64_t grid = std::min<int64_t>(ntiles, cache.get(k_mx_bf16, kWG, lds));
-        k_mx_bf16<<<(unsigned)grid, kWG, lds, stream>>>((const uint16_t*)x, R, C, q, e, qt, et);
+        const int64_t grid = std::min<int64_t>(ntiles, cache.get(k_mx_bf16<FMT>, kWG, lds));
+        k_mx_bf16<FMT><<<(unsigned)grid, kWG, lds, stream>>>((const uint16_t*)x, R, C, q, e, qt, et);
     } else {
         const size_t lds = qt ? 128 * tile_pitch<float>() * 4 : 0;
         static ResidentGrid cache;
-        const int64_t grid = std::min<int64_t>(ntiles, cache.get(k_mx<float>, kWG, lds));
-        k_mx<float><<<(unsigned)grid, kWG, lds, stream>>>((const float*)x, R, C, q, e, qt, et);
+        const int64_t grid = std::min<int64_t>(ntiles, cache.get(k_mx<float, FMT>, kWG, lds));
+        k_mx<float, FMT><<<(unsigned)grid, kWG, lds, stream>>>((const float*)x, R, C, q, e, qt, et);
     }
+}
+
+hipError_t launch_mxfp4_bf16(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, uint8_t* e, uint8_t* qt,
+                             uint8_t* et, hipStream_t stream)
+{
+    const int64_t ntiles = cdiv(C, 128) * cdiv(R, 128);
+    const size_t lds = qt ? 128 * (128 + 8) * 2 : 0;
+    static ResidentGrid cache;
+    const int64_t grid = std::min<int64_t>(ntiles, cache.get(k_mxfp4_bf16, kWG, lds));
+    k_mxfp4_bf16<<<(unsigned)grid, kWG, lds, stream>>>(x, R, C, q, e, qt, et);
+    return hipGetLastError();
+}
+
+hipError_t launch_mx(const void* x, int in_bf16, int fmt, int64_t R, int64_t C, uint8_t* q, uint8_t* e,
+                     uint8_t* qt, uint8_t* et, hipStream_t stream)
+{
+    if (fmt == kE5M2)
+        launch_mx_t<kE5M2>(x, in_bf16, R, C, q, e, qt, et, stream);
+    else
+        launch_mx_t<kE4M3>(x, in_bf16, R, C, q, e, qt, et, stream);
     return hipGetLastError();
 }
 

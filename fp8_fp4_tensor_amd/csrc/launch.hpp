@@ -84,16 +84,25 @@ hipError_t launch_delayed_finish(const float* partials, int n_partials, float* h
                                  float* alpha, float* s, float fmax_v, float* amax_out, hipStream_t stream);
 
 // Blockwise fp32 scales, E4M3. 1x128: flat blocks; 128x128: tiles.
-hipError_t launch_block_1x128(const void* x, int in_bf16, int64_t R, int64_t C, uint8_t* q, float* s,
+// pow2 = 1: tile scales rounded to the MX power of two 2^(floor(log2 a) - 8).
+hipError_t launch_block_1x128(const void* x, int in_bf16, int pow2, int64_t R, int64_t C, uint8_t* q, float* s,
                               hipStream_t stream);
-hipError_t launch_block_1x128_colwise(const void* x, int in_bf16, int64_t R, int64_t C, uint8_t* qt, float* st,
-                                      hipStream_t stream);
-hipError_t launch_block_128x128(const void* x, int in_bf16, int64_t R, int64_t C, uint8_t* q, float* s,
+hipError_t launch_block_1x128_colwise(const void* x, int in_bf16, int pow2, int64_t R, int64_t C, uint8_t* qt,
+                                      float* st, hipStream_t stream);
+hipError_t launch_block_128x128(const void* x, int in_bf16, int pow2, int64_t R, int64_t C, uint8_t* q, float* s,
                                 uint8_t* qt, float* st, hipStream_t stream);
 
-// MXFP8 E4M3: rowwise 1x32 and/or colwise 32x1 (transposed).
-hipError_t launch_mx(const void* x, int in_bf16, int64_t R, int64_t C, uint8_t* q, uint8_t* e, uint8_t* qt,
-                     uint8_t* et, hipStream_t stream);
+// MX with E4M3 (fmt 0) or E5M2 (fmt 1) elements: rowwise 1x32 and/or colwise 32x1 (transposed).
+hipError_t launch_mx(const void* x, int in_bf16, int fmt, int64_t R, int64_t C, uint8_t* q, uint8_t* e,
+                     uint8_t* qt, uint8_t* et, hipStream_t stream);
+
+// MXFP4 from bf16, both planes from one read (tile kernel in k_mx.hip).
+hipError_t launch_mxfp4_bf16(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, uint8_t* e, uint8_t* qt,
+                             uint8_t* et, hipStream_t stream);
+
+// MXFP4 (E2M1 elements packed two per byte): rowwise 1x32 and/or colwise 32x1 (transposed).
+hipError_t launch_mxfp4(const void* x, int in_bf16, int64_t R, int64_t C, uint8_t* q, uint8_t* e, uint8_t* qt,
+                        uint8_t* et, hipStream_t stream);
 
 // Stochastic rounding of elements: Philox4x32-10 keyed by seed, stream 2*offset + plane.
 struct SrArgs {
@@ -115,7 +124,7 @@ hipError_t launch_dequant_tensor(const uint8_t* q, int fmt, int64_t n, const flo
                                  hipStream_t stream);
 hipError_t launch_dequant_block(const uint8_t* q, const float* s, int64_t R, int64_t C, int br, int bc, void* y,
                                 int bf, hipStream_t stream);
-hipError_t launch_dequant_mx(const uint8_t* q, const uint8_t* e, int64_t R, int64_t C, void* y, int bf,
+hipError_t launch_dequant_mx(const uint8_t* q, const uint8_t* e, int fmt, int64_t R, int64_t C, void* y, int bf,
                              hipStream_t stream);
 hipError_t launch_dequant_nvfp4(const uint8_t* p, const uint8_t* codes, const float* S, int64_t R, int64_t C,
                                 int br, int bc, void* y, int bf, hipStream_t stream);

@@ -23,7 +23,7 @@ FQ_E4M3, FQ_E5M2, FQ_E2M1 = 0, 1, 2
 FQ_PER_TENSOR_CURRENT, FQ_PER_TENSOR_DELAYED, FQ_BLOCK_FP32, FQ_MX, FQ_NVFP4 = range(5)
 FQ_ROWWISE, FQ_COLWISE = 1, 2
 FQ_ROUND_NEAREST_EVEN, FQ_ROUND_STOCHASTIC = 0, 1
-FQ_SCALE_DEFAULT = 0
+FQ_SCALE_DEFAULT, FQ_SCALE_POW2 = 0, 1
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfq.so")
 
@@ -166,7 +166,7 @@ def alloc_quantized(d: FqDesc, device="cuda") -> Quantized:
     q = Quantized()
     sd = _scale_dtype(d)
     es = 4 if sd == torch.float32 else 1
-    packed = d.recipe == FQ_NVFP4
+    packed = d.format == FQ_E2M1
     if z.row_data:
         q.row_data = torch.empty((R, C // 2) if packed else (R, C), dtype=torch.uint8, device=device)
     if z.col_data:

@@ -79,9 +79,12 @@ typedef enum { FQ_E4M3 = 0, FQ_E5M2 = 1, FQ_E2M1 = 2 } fq_format;
  *   FQ_BLOCK_FP32          per-tile current scaling to E4M3 with an fp32
  *                          scale per tile; tiles 1x128 or 128x128
  *                          ([MP] recipe 4 and "Blockwise scaling").
- *   FQ_MX                  MXFP8: 1x32 blocks sharing one E8M0 power-of-two
- *                          scale 2^(floor(log2 amax) - 8), E4M3 elements
- *                          ([MP] "MXFP8" and recipe 5).
+ *   FQ_MX                  MX: 1x32 blocks sharing one E8M0 power-of-two
+ *                          scale 2^(floor(log2 amax) - emax), emax =
+ *                          floor(log2 Fmax) of the element format: E4M3
+ *                          (MXFP8, emax 8) or E5M2 (emax 15) ([MP] "MXFP8"
+ *                          and recipe 5), or E2M1 (MXFP4, emax 2, packed two
+ *                          per byte; [LP] section 2.4).
  *   FQ_NVFP4               E2M1 elements, 1x16 or 16x16 blocks with E4M3
  *                          block scales, plus one fp32 tensor scale
  *                          ([MP] recipe 6; [LP] section 2.4).
@@ -120,8 +123,16 @@ enum { FQ_ROWWISE = 1, FQ_COLWISE = 2 };
  */
 typedef enum { FQ_ROUND_NEAREST_EVEN = 0, FQ_ROUND_STOCHASTIC = 1 } fq_rounding;
 
-/* Scale encoding of FQ_BLOCK_FP32 (other recipes: FQ_SCALE_DEFAULT only). */
-typedef enum { FQ_SCALE_DEFAULT = 0 } fq_scale_mode;
+/*
+ * Scale encoding of FQ_BLOCK_FP32 (other recipes: FQ_SCALE_DEFAULT only).
+ *   FQ_SCALE_DEFAULT  s_B = a_B/448 in fp32.
+ *   FQ_SCALE_POW2     s_B = 2^(floor(log2 a_B) - 8), the MX rule on the tile
+ *                     amax, stored as its fp32 value (2^-127 for an all-zero
+ *                     tile); elements are Q_E4M3(x / s_B), the division exact
+ *                     ([MP] "Blockwise scaling": the recipe run as MXFP8 blocks
+ *                     sharing one power-of-two scale per tile).
+ */
+typedef enum { FQ_SCALE_DEFAULT = 0, FQ_SCALE_POW2 = 1 } fq_scale_mode;
 
 /*
  * What to quantize and how.
@@ -139,7 +150,10 @@ typedef enum { FQ_SCALE_DEFAULT = 0 } fq_scale_mode;
  *   CURRENT, DELAYED  E4M3 or E5M2, f32 or bf16 input, any shape
  *   BLOCK_FP32        E4M3, rows % br == 0, cols % 128 == 0;
  *                     colwise of 1x128 also needs rows % 128 == 0
- *   MX                E4M3, cols % 32 == 0; colwise needs rows % 32 == 0
+ *   MX                E4M3, E5M2 or E2M1, cols % 32 == 0; colwise needs
+ *                     rows % 32 == 0
+ *   scale_mode POW2   BLOCK_FP32 only
+ *   rounding STOCHASTIC  NVFP4 with 1x16 blocks only
  *   NVFP4             E2M1, rows % br == 0, cols % 16 == 0;
  *                     colwise needs rows % 16 == 0
  */
@@ -172,6 +186,7 @@ typedef struct {
  *   block 1x128  [R,C] u8            [R, C/128] f32            [C,R] u8, [C, R/128] f32
  *   block 128^2  [R,C] u8            [R/128, C/128] f32        [C,R] u8, [C/128, R/128] f32
  *   MX           [R,C] u8            [R, C/32] u8 (E8M0)       [C,R] u8, [C, R/32] u8
+ *   MXFP4        [R, C/2] u8 packed  [R, C/32] u8 (E8M0)       [C, R/2] u8, [C, R/32] u8
  *   NVFP4 1x16   [R, C/2] u8 packed  [R, C/16] u8 (E4M3)       [C, R/2] u8, [C, R/16] u8
  *   NVFP4 16x16  [R, C/2] u8 packed  [R/16, C/16] u8 (E4M3)    [C, R/2] u8, [C/16, R/16] u8
  *

@@ -104,6 +104,13 @@ def test_desc_validation(L, recipe, fmt, R, C, block, outputs, want):
     (fq.FQ_NVFP4, fq.FQ_E2M1, (1, 16), 2, 0, fq.FQ_E_INVALID),
     (fq.FQ_NVFP4, fq.FQ_E2M1, (1, 16), -1, 0, fq.FQ_E_INVALID),
     (fq.FQ_NVFP4, fq.FQ_E2M1, (1, 16), 0, 7, fq.FQ_E_INVALID),
+    (fq.FQ_BLOCK_FP32, fq.FQ_E4M3, (1, 128), 0, fq.FQ_SCALE_POW2, fq.FQ_OK),
+    (fq.FQ_BLOCK_FP32, fq.FQ_E4M3, (128, 128), 0, fq.FQ_SCALE_POW2, fq.FQ_OK),
+    (fq.FQ_MX, fq.FQ_E4M3, (1, 32), 0, fq.FQ_SCALE_POW2, fq.FQ_E_UNSUPPORTED),
+    (fq.FQ_NVFP4, fq.FQ_E2M1, (1, 16), 0, fq.FQ_SCALE_POW2, fq.FQ_E_UNSUPPORTED),
+    (fq.FQ_PER_TENSOR_CURRENT, fq.FQ_E4M3, (0, 0), 0, fq.FQ_SCALE_POW2, fq.FQ_E_UNSUPPORTED),
+    (fq.FQ_MX, fq.FQ_E5M2, (1, 32), 0, 0, fq.FQ_OK),
+    (fq.FQ_MX, fq.FQ_E2M1, (1, 32), 0, 0, fq.FQ_OK),
 ])
 def test_rounding_and_scale_mode_validation(L, recipe, fmt, block, rounding, scale_mode, want):
     d = fq.desc(recipe, fq.FQ_IN_BF16, fmt, 256, 256, block, 3, rounding=rounding, seed=1, offset=2,
@@ -114,6 +121,14 @@ def test_rounding_and_scale_mode_validation(L, recipe, fmt, block, rounding, sca
         q = fq.FqQuantized(fq.FqPlane(B, B), fq.FqPlane(B, B), B, B)
         assert L.fq_quantize(ctypes.byref(d), B, ctypes.byref(q), B, 1 << 20, None) == want
         assert L.fq_quantize_with_amax(ctypes.byref(d), B, B, ctypes.byref(q), B, 1 << 20, None) == want
+
+
+def test_mx_variant_sizes():
+    both = fq.FQ_ROWWISE | fq.FQ_COLWISE
+    z = sizes(fq.FQ_MX, fq.FQ_E2M1, 8192, 8192, (1, 32), both)
+    assert (z.row_data, z.row_scale, z.col_data, z.col_scale) == (8192 * 4096, 8192 * 256, 8192 * 4096, 8192 * 256)
+    z = sizes(fq.FQ_MX, fq.FQ_E5M2, 64, 96, (1, 32), both)
+    assert (z.row_data, z.row_scale, z.col_data, z.col_scale) == (64 * 96, 64 * 3, 64 * 96, 96 * 2)
 
 
 def test_desc_layout():
@@ -206,6 +221,10 @@ def test_requantize_checks(L):
     sr = fq.desc(fq.FQ_MX, fq.FQ_IN_BF16, fq.FQ_E4M3, 64, 64, (1, 32), fq.FQ_ROWWISE, rounding=1)
     assert L.fq_requantize_transpose(ctypes.byref(sr), ctypes.byref(ok), ctypes.byref(ok), None) \
         == fq.FQ_E_UNSUPPORTED
+    for fmt in (fq.FQ_E5M2, fq.FQ_E2M1):
+        v = fq.desc(fq.FQ_MX, fq.FQ_IN_BF16, fmt, 64, 64, (1, 32), fq.FQ_ROWWISE)
+        assert L.fq_requantize_transpose(ctypes.byref(v), ctypes.byref(ok), ctypes.byref(ok), None) \
+            == fq.FQ_E_UNSUPPORTED
     nocol = fq.FqQuantized(fq.FqPlane(B, B), fq.FqPlane(None, None), None, None)
     assert L.fq_requantize_transpose(ctypes.byref(d), ctypes.byref(ok), ctypes.byref(nocol), None) \
         == fq.FQ_E_INVALID
