@@ -97,6 +97,9 @@ def _load():
                                                            ctypes.c_uint64, ctypes.c_uint64, _p, _p, _p, _p,
                                                            _fp, _fp]),
         "orc_philox4x32_10": (None, [_p, _p, _p]),
+        "orc_rht16_array": (None, [_p, _i64, _u32, _p]),
+        "orc_quantize_nvfp4_rht": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, _u32, ctypes.c_int, _f32,
+                                                  ctypes.c_int, ctypes.c_uint64, ctypes.c_uint64, _p, _p, _fp, _fp]),
         "orc_sr_bits": (_u32, [ctypes.c_uint64, ctypes.c_uint64, _u32, _i64]),
         "orc_encode_e2m1_sr": (_u32, [_f32, _u32]),
         "orc_encode_e2m1_sr_array": (None, [_p, _p, _i64, _p]),
@@ -359,6 +362,33 @@ def encode_e2m1_sr(y, u):
     q = np.empty(y.size, np.uint8)
     _load().orc_encode_e2m1_sr_array(y.ctypes.data, u.ctypes.data, y.size, q.ctypes.data)
     return q.reshape(y.shape)
+
+
+# ---------------------------------------------------------------- random Hadamard transform
+def rht16(x, signs):
+    """The 16-point RHT of every consecutive 16-element chunk of x (fp32)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    assert x.size % 16 == 0
+    y = np.empty_like(x)
+    _load().orc_rht16_array(x.ctypes.data, x.size // 16, int(signs) & 0xFFFF, y.ctypes.data)
+    return y
+
+
+def quantize_nvfp4_rht(x, signs, amax=None, sr=None, shape=None):
+    """NVFP4 1x16 colwise copy of the RHT-transformed X^T: dict(p_col [C, R/2],
+    c_col [C, R/16], S, amax) with amax that of the transformed tensor."""
+    p, dt, keep = _in(x)
+    R, C = _shape2(keep, shape)
+    p_col = np.empty(R * C // 2, np.uint8)
+    c_col = np.empty(C * (R // 16), np.uint8)
+    S, A = ctypes.c_float(), ctypes.c_float()
+    seed, off = (0, 0) if sr is None else sr
+    _check(_load().orc_quantize_nvfp4_rht(p, dt, R, C, int(signs) & 0xFFFF, 0 if amax is None else 1,
+                                          0.0 if amax is None else float(np.float32(amax)),
+                                          0 if sr is None else 1, int(seed), int(off), _ptr(p_col), _ptr(c_col),
+                                          ctypes.byref(S), ctypes.byref(A)), "quantize_nvfp4_rht")
+    return dict(p_col=p_col.reshape(C, R // 2), c_col=c_col.reshape(C, R // 16), S=np.float32(S.value),
+                amax=np.float32(A.value))
 
 
 # ---------------------------------------------------------------- dequantize

@@ -843,6 +843,88 @@ int orc_quantize_nvfp4_sr_with_amax(const void *x, int dt, int64_t R, int64_t C,
                       amax_out);
 }
 
+/*
+ * Random Hadamard transform of 16 consecutive values ([LP] section 2.4
+ * item 3: applied to the inputs of the weight-gradient GEMM to spread
+ * block-level outliers before FP4 quantization).
+ * READING (the pages give no size, signs or arithmetic): y = (1/4) H16 (s.x),
+ * H16 the 16 x 16 Sylvester Hadamard matrix (entry (i, j) = (-1)^popcount(i&j)),
+ * s_i = -1 where bit i of `signs` is set, else +1; (1/4) H16 diag(s) is
+ * orthogonal, so applying it to both GEMM operands along the contraction
+ * leaves the product unchanged.  Arithmetic: the sign flips are exact; the
+ * sums are the fast Walsh-Hadamard transform in fp32, stages h = 1, 2, 4, 8,
+ * each replacing the pair (w_i, w_{i+h}), bit h of i clear, by
+ * (w_i + w_{i+h}, w_i - w_{i+h}); the factor 1/4 is an exact multiply.
+ */
+void orc_rht16(const float *x, unsigned signs, float *y)
+{
+    float w[16];
+    int i, h;
+    for (i = 0; i < 16; i++)
+        w[i] = ((signs >> i) & 1u) ? -x[i] : x[i];
+    for (h = 1; h < 16; h *= 2)
+        for (i = 0; i < 16; i++)
+            if (!(i & h)) {
+                float a = w[i], b = w[i + h];
+                w[i] = a + b;
+                w[i + h] = a - b;
+            }
+    for (i = 0; i < 16; i++)
+        y[i] = w[i] * 0.25f;
+}
+
+void orc_rht16_array(const float *x, int64_t nchunks, unsigned signs, float *y)
+{
+    int64_t k;
+    for (k = 0; k < nchunks; k++)
+        orc_rht16(x + 16 * k, signs, y + 16 * k);
+}
+
+/*
+ * NVFP4 1x16 colwise copy of a weight-gradient input with the RHT
+ * ([LP] section 2.4 items 1, 3 and 5).  READING: the GEMM contracts X^T
+ * [C,R] along R, so each row of X^T is transformed in 16-element chunks
+ * (the 1x16 blocks) and the transformed tensor Y^T is quantized with the
+ * NVFP4 recipe: its tensor amax A' = max|Y^T| (or the given amax of the
+ * transformed tensor, e.g. reduced across shards) sets the tensor scale.
+ * The rowwise copy (other GEMMs) is not transformed and is produced by the
+ * plain recipe.  Elements may be rounded stochastically (plane 1 bits).
+ */
+int orc_quantize_nvfp4_rht(const void *x, int dt, int64_t R, int64_t C, unsigned signs, int use_amax, float A,
+                           int sr_on, uint64_t seed, uint64_t offset, uint8_t *p_col, uint8_t *c_col,
+                           float *S_out, float *amax_out)
+{
+    int64_t r, c;
+    float *yt, a = 0.0f;
+    if (R <= 0 || C <= 0)
+        return -3;
+    if (R % 16 || C % 16)
+        return -3;
+    if (check_finite(x, dt, R * C))
+        return -1;
+    yt = (float *)malloc(sizeof(float) * (size_t)(R * C));
+    for (c = 0; c < C; c++)
+        for (r = 0; r < R; r++)
+            yt[c * R + r] = load_x(x, dt, r * C + c);
+    orc_rht16_array(yt, R * C / 16, signs, yt);
+    for (r = 0; r < R * C; r++)
+        if (fabsf(yt[r]) > a)
+            a = fabsf(yt[r]);
+    if (use_amax)
+        a = A;
+    {
+        nvfp4_tensor t = nvfp4_tensor_scale(a);
+        sr_ctx sr = {sr_on, seed, offset, 1};
+        if (S_out)
+            *S_out = t.S;
+        if (amax_out)
+            *amax_out = a;
+        nvfp4_rowwise(yt, ORC_IN_F32, C, R, 1, 16, t, sr, p_col, c_col, NULL);
+    }
+    free(yt);
+    return 0;
+}
+
 /* NVFP4 with A = the amax of this tensor. */
 int orc_quantize_nvfp4(const void *x, int dt, int64_t R, int64_t C, int br, int bc, unsigned outputs,
                        uint8_t *p_row, uint8_t *c_row, uint8_t *p_col, uint8_t *c_col, float *S_out,
