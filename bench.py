@@ -154,9 +154,10 @@ def plane_bytes(w, which):
 
 def time_extras(torch, fq, L, stream_p, jobs, steps):
     """Dequantize (rowwise plane to bf16), MXFP8 rowwise-to-colwise requantize,
-    NVFP4 1x16 with stochastic rounding, MX with E5M2 and E2M1 elements and
-    blockwise with power-of-two scales, at the large workloads' shapes, each
-    call bracketed by events; not part of the step."""
+    NVFP4 1x16 with stochastic rounding, the NVFP4 colwise copy with the RHT and
+    stochastic rounding, MX with E5M2 and E2M1 elements and blockwise with
+    power-of-two scales, at the large workloads' shapes, each call bracketed by
+    events; not part of the step."""
     out = {}
     for j in jobs:
         w = j["w"]
@@ -205,13 +206,23 @@ def time_extras(torch, fq, L, stream_p, jobs, steps):
         if w.recipe == "block":
             variants = [("block_pow2", fq.desc(fq.FQ_BLOCK_FP32, fq.FQ_IN_BF16, fq.FQ_E4M3, R, C, w.block, w.outputs,
                                                scale_mode=fq.FQ_SCALE_POW2), j["bytes"])]
+        if w.recipe == "nvfp4" and tuple(w.block) == (1, 16):
+            # weight-gradient input: colwise copy with the RHT and stochastic rounding (two reads)
+            variants = [("nvfp4_colwise_rht_sr",
+                         fq.desc(fq.FQ_NVFP4, fq.FQ_IN_BF16, fq.FQ_E2M1, R, C, (1, 16), fq.FQ_COLWISE,
+                                 rounding=fq.FQ_ROUND_STOCHASTIC, seed=2024, offset=1,
+                                 transform=fq.FQ_TRANSFORM_RHT16, rht_signs=0xA5C3),
+                         2 * 2 * R * C + R * C // 2 + R * C // 16 + 4)]
         for vname, dv, nbytes in variants:
             ov = fq.alloc_quantized(dv)
             cov = ov.c()
+            wsv = fq.alloc_workspace(dv)
+            wsp = None if wsv is None else ctypes.c_void_p(wsv.data_ptr())
+            wsn = 0 if wsv is None else wsv.numel()
             for k in range(-1, steps):
                 if k >= 0:
                     ev[k][0].record()
-                rc = L.fq_quantize(ctypes.byref(dv), j["xp"], ctypes.byref(cov), None, 0, stream_p)
+                rc = L.fq_quantize(ctypes.byref(dv), j["xp"], ctypes.byref(cov), wsp, wsn, stream_p)
                 if k >= 0:
                     ev[k][1].record()
                 if rc != fq.FQ_OK:

@@ -47,6 +47,11 @@ fq_status check_desc(const fq_desc* d)
     if (d->rounding == FQ_ROUND_STOCHASTIC &&
         !(d->recipe == FQ_NVFP4 && d->block_rows == 1 && d->block_cols == 16))
         return FQ_E_UNSUPPORTED;
+    if (d->transform != FQ_TRANSFORM_NONE && d->transform != FQ_TRANSFORM_RHT16)
+        return FQ_E_INVALID;
+    if (d->transform == FQ_TRANSFORM_RHT16 &&
+        !(d->recipe == FQ_NVFP4 && d->block_rows == 1 && d->block_cols == 16 && d->outputs == FQ_COLWISE))
+        return FQ_E_UNSUPPORTED;
     const bool col = (d->outputs & FQ_COLWISE) != 0;
     const int64_t R = d->rows, C = d->cols;
     const int br = d->block_rows, bc = d->block_cols;
@@ -84,6 +89,14 @@ fq_status check_desc(const fq_desc* d)
         return FQ_OK;
     }
     return FQ_E_INVALID;
+}
+
+RhtArgs rht_of(const fq_desc* d)
+{
+    RhtArgs r;
+    r.on = d->transform == FQ_TRANSFORM_RHT16;
+    r.signs = d->rht_signs & 0xFFFFu;
+    return r;
 }
 
 SrArgs sr_of(const fq_desc* d)
@@ -272,9 +285,23 @@ fq_status fq_amax(const fq_desc* d, const void* x, float* amax_out, void* ws, si
     if ((s = check_ws(z, ws, ws_bytes)) != FQ_OK)
         return s;
     const int64_t n = d->rows * d->cols;
-    const int g = amax_grid(n, elem_bytes(d), kMaxPartials);
     float* partials = (float*)ws;
-    if ((s = hip_status(launch_amax_partial(x, d->in_dtype == FQ_IN_BF16, n, partials, g, st))) != FQ_OK)
+    int g;
+    if (d->transform == FQ_TRANSFORM_RHT16) {
+        // the amax of the transformed tensor (NVFP4 1x16 colwise with the RHT)
+        if ((s = check_desc(d)) != FQ_OK)
+            return s;
+        g = rht_amax_grid(d->rows, d->cols);
+        s = n > 0 ? hip_status(launch_rht_amax_partial(x, d->in_dtype == FQ_IN_BF16, d->rows, d->cols,
+                                                       d->rht_signs & 0xFFFFu, partials, g, st))
+                  : hip_status(launch_amax_partial(x, d->in_dtype == FQ_IN_BF16, n, partials, g, st));
+    } else {
+        if (d->transform != FQ_TRANSFORM_NONE)
+            return FQ_E_INVALID;
+        g = amax_grid(n, elem_bytes(d), kMaxPartials);
+        s = hip_status(launch_amax_partial(x, d->in_dtype == FQ_IN_BF16, n, partials, g, st));
+    }
+    if (s != FQ_OK)
         return s;
     return hip_status(launch_amax_finish(partials, g, amax_out, st));
 }
@@ -341,9 +368,14 @@ fq_status fq_quantize(const fq_desc* d, const void* x, const fq_quantized* o, vo
                                     col ? (uint8_t*)o->colwise.data : nullptr,
                                     col ? (uint8_t*)o->colwise.scale : nullptr, st));
     case FQ_NVFP4: {
-        const int g = amax_grid(n, elem_bytes(d), kMaxPartials);
+        const bool rht = d->transform == FQ_TRANSFORM_RHT16;
+        const int g = rht ? rht_amax_grid(R, C) : amax_grid(n, elem_bytes(d), kMaxPartials);
         float* partials = (float*)ws;
-        if ((s = hip_status(launch_amax_partial(x, bf, n, partials, g, st))) != FQ_OK)
+        if (rht && n > 0)
+            s = hip_status(launch_rht_amax_partial(x, bf, R, C, d->rht_signs & 0xFFFFu, partials, g, st));
+        else
+            s = hip_status(launch_amax_partial(x, bf, n, partials, g, st));
+        if (s != FQ_OK)
             return s;
         ScaleSrc src;
         src.partials = partials;
@@ -352,7 +384,7 @@ fq_status fq_quantize(const fq_desc* d, const void* x, const fq_quantized* o, vo
                                        row ? (uint8_t*)o->rowwise.scale : nullptr,
                                        col ? (uint8_t*)o->colwise.data : nullptr,
                                        col ? (uint8_t*)o->colwise.scale : nullptr, o->tensor_scale, o->amax,
-                                       sr_of(d), st));
+                                       sr_of(d), rht_of(d), st));
     }
     }
     return FQ_E_INVALID;
@@ -386,7 +418,7 @@ fq_status fq_quantize_with_amax(const fq_desc* d, const void* x, const float* am
                                    row ? (uint8_t*)o->rowwise.scale : nullptr,
                                    col ? (uint8_t*)o->colwise.data : nullptr,
                                    col ? (uint8_t*)o->colwise.scale : nullptr, o->tensor_scale, o->amax,
-                                   sr_of(d), st));
+                                   sr_of(d), rht_of(d), st));
 }
 
 fq_status fq_quantize_delayed(const fq_desc* d, const void* x, const fq_delayed_state* state,
@@ -478,8 +510,10 @@ fq_status fq_requantize_transpose(const fq_desc* d, const fq_quantized* in, cons
         return FQ_E_INVALID;
     if (d->scale_mode != FQ_SCALE_DEFAULT && d->scale_mode != FQ_SCALE_POW2)
         return FQ_E_INVALID;
+    if (d->transform != FQ_TRANSFORM_NONE && d->transform != FQ_TRANSFORM_RHT16)
+        return FQ_E_INVALID;
     if (d->recipe != FQ_MX || d->format != FQ_E4M3 || d->block_rows != 1 || d->block_cols != 32 ||
-        d->scale_mode != FQ_SCALE_DEFAULT ||
+        d->scale_mode != FQ_SCALE_DEFAULT || d->transform != FQ_TRANSFORM_NONE ||
         d->rounding != FQ_ROUND_NEAREST_EVEN)
         return FQ_E_UNSUPPORTED;
     if (d->cols > 0 && d->rows > kMaxElems / d->cols)

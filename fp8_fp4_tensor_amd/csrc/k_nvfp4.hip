@@ -23,10 +23,16 @@
 //                  one DPP step; each lane writes one packed dword.
 //   k_nvfp4_16x16  each lane owns E columns of a 16-row strip (16 loads), so
 //                  a 16x16 block is again two lanes; one DPP step.
-//   k_nvfp4_col    colwise copy: a 32-row slab in LDS, one thread per column;
-//                  1x16 -> blocks of 16 rows of one column; 16x16 -> the same
-//                  blocks as rowwise (max also across 16 neighbouring lanes),
-//                  so the colwise nibbles are the rowwise ones transposed.
+//   k_nvfp4_colt   colwise 1x16 copy (blocks of 16 rows of one column): a
+//                  128 x 64 tile in LDS, four lanes per column, each X^T row
+//                  written as 64-byte segments (optionally with SR and RHT).
+//   k_nvfp4_col    colwise 16x16 copy: a 32-row slab in LDS, one thread per
+//                  column; the same blocks as rowwise (max also across 16
+//                  neighbouring lanes), so the nibbles are the rowwise ones
+//                  transposed.
+//   k_rht_amax_partial, k_nvfp4_col<..., RHT>  the random Hadamard transform
+//                  of weight-gradient inputs ([LP] 2.4 item 3): 16-row chunks
+//                  of each column transformed in registers in both passes.
 //   k_nvfp4_1x16_sr  stochastic rounding of the elements ([MP] "NVFP4"; [LP]
 //                  2.4 item 5): a lane owns a whole 1x16 block, which is two
 //                  Philox4x32-10 calls (8 x 16 random bits each); the colwise
@@ -148,6 +154,74 @@ __device__ __forceinline__ uint32_t enc8_e2m1_sr(const float* f, float r, const 
         w |= sr_nibble(f[2 * k + 1] * r, ph.w[k] & 0xFFFF0000u) << (8 * k + 4);
     }
     return w;
+}
+
+// ---------------------------------------------------------------- random Hadamard transform
+// ([LP] 2.4 item 3) y = (1/4) H16 diag(s) x on 16 values in registers: the
+// sign flips (exact), the fast Walsh-Hadamard butterfly in fp32 with stages
+// h = 1, 2, 4, 8 (pair (i, i+h), bit h of i clear -> (a + b, a - b): the
+// same additions, in the same order, as the transform's definition), and
+// the exact factor 1/4. 64 additions for 16 values.
+__device__ __forceinline__ void rht16(float* f, uint32_t signs)
+{
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        f[i] = ((signs >> i) & 1u) ? -f[i] : f[i];
+#pragma unroll
+    for (int h = 1; h < 16; h *= 2) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (!(i & h)) {
+                const float a = f[i], b = f[i + h];
+                f[i] = a + b;
+                f[i + h] = a - b;
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        f[i] *= 0.25f;
+}
+
+// Amax of the transformed X^T. A thread holds a 16-row strip of E columns
+// in registers (16 loads; a wave reads 1 KiB of each row), transforms each
+// column's 16 values and keeps the max; workgroups stride over strips; one
+// partial per workgroup. Ordinary loads, so the block pass that follows
+// finds the tensor in the memory-side cache.
+template <typename T>
+__global__ __launch_bounds__(kWG) void k_rht_amax_partial(const T* __restrict__ x, int64_t R, int64_t C,
+                                                          uint32_t signs, float* __restrict__ partials)
+{
+    __shared__ float lds[4];
+    constexpr int E = In<T>::kE, WC = kWG * E;  // columns per workgroup strip
+    const int64_t nwc = cdiv(C, WC), nstrips = (R / 16) * nwc;
+    float m = 0.0f;
+    for (int64_t st = blockIdx.x; st < nstrips; st += gridDim.x) {
+        const int64_t r0 = (st / nwc) * 16;
+        const int64_t c = (st % nwc) * WC + (int64_t)threadIdx.x * E;
+        if (c >= C)
+            continue;
+        u32x4 v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            v[i] = ld16(x + (r0 + i) * C + c);
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+            float f[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if constexpr (E == 8)
+                    f[i] = (j & 1) ? bf16_hi(v[i][j >> 1]) : bf16_lo(v[i][j >> 1]);
+                else
+                    f[i] = __uint_as_float(v[i][j]);
+            }
+            rht16(f, signs);
+            m = fmaxf(m, absmax<16>(f));
+        }
+    }
+    const float a = max_workgroup(m, lds);
+    if (threadIdx.x == 0)
+        partials[blockIdx.x] = a;
 }
 
 // Rowwise 1x16 with stochastic rounding: thread = block of 16 elements
@@ -295,13 +369,118 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_16x16(const T* __restrict__ x, in
         codes[(r0 / 16) * (C / 16) + c / 16] = (uint8_t)code;
 }
 
-// Colwise copy. BR = 1: 1x16 blocks of X^T (16 rows of a column);
-// BR = 16: 16x16 blocks. Slab of 32 rows x 256 columns in LDS.
-template <typename T, int BR, bool SR = false>
+// Colwise 1x16 copy (1x16 blocks of X^T = 16 rows of one column of X), one
+// 128-row x 64-column tile per workgroup, so each row of X^T gets 64
+// contiguous bytes per tile. Thread t: column c = t >> 2 of the tile and
+// q = t & 3, which owns the blocks at rows 16q and 64 + 16q. The tile sits in
+// LDS with its 16-byte chunks XOR-swizzled by the row's 16-row group, so the
+// four rows 16 apart that a wave reads at each step hit distinct banks.
+// Lane pairs (q even, q odd) swap one 8-byte half with DPP so each lane
+// stores 16 contiguous bytes (blocks 2h, 2h+1 or 2h+4, 2h+5): a wave writes
+// 16 whole 64-byte row segments per store instruction. Tiles that are not
+// full, or rows of X^T that are only 8-byte aligned (R % 32 == 16), take
+// 8-byte stores instead.
+template <typename T, bool SR, bool RHT>
+__global__ __launch_bounds__(kWG) void k_nvfp4_colt(const T* __restrict__ x, int64_t R, int64_t C, ScaleSrc src,
+                                                    uint8_t* __restrict__ pt, uint8_t* __restrict__ ct,
+                                                    float* S_out, float* amax_out, uint64_t seed, uint64_t offset,
+                                                    uint32_t signs)
+{
+    constexpr int TC = 64, E = In<T>::kE, CPR = TC / E, SW = 16 / E;  // 16-byte chunks per row; swizzle step
+    __shared__ float lds[4];
+    __shared__ __align__(16) T tile[128][TC];
+    const int64_t ntc = C / TC + (C % TC != 0);
+    const int64_t r0 = (int64_t)(blockIdx.x / ntc) * 128, c0 = (int64_t)(blockIdx.x % ntc) * TC;
+    const int64_t rows_in = min((int64_t)128, R - r0);
+    // stage the tile: chunk j of row r goes to chunk j ^ (SW * ((r >> 4) & 3))
+    for (int i = threadIdx.x; i < 128 * CPR; i += kWG) {
+        const int r = i / CPR, j = i % CPR;
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if (r < rows_in && c0 + j * E < C)
+            v = ld16_stream(x + (r0 + r) * C + c0 + j * E);
+        *reinterpret_cast<u32x4*>(&tile[r][(j ^ (SW * ((r >> 4) & 3))) * E]) = v;
+    }
+    float alpha_s, S, A;
+    nvfp4_tensor(src, lds, alpha_s, S, A);  // includes a workgroup barrier
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (S_out)
+            *S_out = S;
+        if (amax_out)
+            *amax_out = A;
+    }
+    __syncthreads();
+    const int c = threadIdx.x >> 2, q = threadIdx.x & 3;
+    const bool in = c0 + c < C;
+    uint32_t wb[2][2];
+    uint32_t codes[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        const int rb = 64 * half + 16 * q;  // first row of this block in the tile
+        float f[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int r = rb + k;
+            f[k] = In<T>::load1(&tile[r][0], ((c / E) ^ (SW * q)) * E + (c % E));
+        }
+        if constexpr (RHT)
+            rht16(f, signs);
+        uint32_t code;
+        float rr;
+        nvfp4_block(absmax<16>(f), alpha_s, S, code, rr);
+        codes[half] = code;
+        if constexpr (SR) {
+            const uint64_t e0 = (uint64_t)((c0 + c) * R + r0 + rb), s = 2 * offset + 1;
+            wb[half][0] = enc8_e2m1_sr(f, rr, sr_group(e0 / 8, s, seed));
+            wb[half][1] = enc8_e2m1_sr(f + 8, rr, sr_group(e0 / 8 + 1, s, seed));
+        } else {
+            wb[half][0] = enc8_e2m1(f, rr);
+            wb[half][1] = enc8_e2m1(f + 8, rr);
+        }
+    }
+    uint8_t* rowp = pt + (c0 + c) * (R / 2) + r0 / 2;  // this column's row of X^T, from row r0
+    const bool wide = rows_in == 128 && (R % 32) == 0;  // uniform over the workgroup
+    if (wide) {
+        // even q sends its second block, odd q its first; both then hold two adjacent blocks
+        const bool odd = q & 1;
+        const uint32_t s0 = odd ? wb[0][0] : wb[1][0], s1 = odd ? wb[0][1] : wb[1][1];
+        const uint32_t r0w = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s0, kDppXor1, 0xF, 0xF, false);
+        const uint32_t r1w = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s1, kDppXor1, 0xF, 0xF, false);
+        u32x4 o;
+        if (odd)
+            o = u32x4{r0w, r1w, wb[1][0], wb[1][1]};  // blocks q + 3, q + 4 (= 2h + 4, 2h + 5)
+        else
+            o = u32x4{wb[0][0], wb[0][1], r0w, r1w};  // blocks q, q + 1
+        if (in)
+            st16_stream(rowp + (odd ? 32 + 8 * (q - 1) : 8 * q), o);
+    } else if (in) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int rb = 64 * half + 16 * q;
+            if (rb < rows_in) {
+                u32x2 v2;
+                v2[0] = wb[half][0];
+                v2[1] = wb[half][1];
+                st8_stream(rowp + rb / 2, v2);
+            }
+        }
+    }
+    if (in) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int rb = 64 * half + 16 * q;
+            if (rb < rows_in)
+                ct[(c0 + c) * (R / 16) + (r0 + rb) / 16] = (uint8_t)codes[half];
+        }
+    }
+}
+
+// Colwise copy of 16x16 blocks (BR = 16; the 1x16 copy is k_nvfp4_colt):
+// the same blocks as rowwise, so the colwise nibbles are the rowwise ones
+// transposed. Slab of 32 rows x 256 columns in LDS.
+template <typename T, int BR>
 __global__ __launch_bounds__(kWG) void k_nvfp4_col(const T* __restrict__ x, int64_t R, int64_t C, ScaleSrc src,
                                                    uint8_t* __restrict__ pt, uint8_t* __restrict__ ct,
-                                                   float* S_out, float* amax_out, uint64_t seed = 0,
-                                                   uint64_t offset = 0)
+                                                   float* S_out, float* amax_out)
 {
     __shared__ float lds[4];
     constexpr int TC = 256, E = In<T>::kE, LPR = TC / E, RPR = kWG / LPR;
@@ -340,15 +519,8 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_col(const T* __restrict__ x, int6
         uint32_t code;
         float r;
         nvfp4_block(a, alpha_s, S, code, r);
-        if constexpr (SR) {
-            // elements (c0 + c, r0 + 16b + k) of X^T: index e0 + k, plane 1
-            const uint64_t e0 = (uint64_t)((c0 + c) * R + r0 + 16 * b), s = 2 * offset + 1;
-            w[2 * b] = enc8_e2m1_sr(f, r, sr_group(e0 / 8, s, seed));
-            w[2 * b + 1] = enc8_e2m1_sr(f + 8, r, sr_group(e0 / 8 + 1, s, seed));
-        } else {
-            w[2 * b] = enc8_e2m1(f, r);
-            w[2 * b + 1] = enc8_e2m1(f + 8, r);
-        }
+        w[2 * b] = enc8_e2m1(f, r);
+        w[2 * b + 1] = enc8_e2m1(f + 8, r);
         if (in && b < nb) {
             const int64_t rb = (r0 + 16 * b) / 16;
             if constexpr (BR == 1)
@@ -374,7 +546,7 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_col(const T* __restrict__ x, int6
 
 template <typename T>
 void launch_t(const void* xv, int64_t R, int64_t C, int br, ScaleSrc src, uint8_t* p, uint8_t* codes, uint8_t* pt,
-              uint8_t* codest, float* S_out, float* amax_out, SrArgs sr, hipStream_t stream)
+              uint8_t* codest, float* S_out, float* amax_out, SrArgs sr, RhtArgs rht, hipStream_t stream)
 {
     const T* x = (const T*)xv;
     constexpr int E = In<T>::kE;
@@ -399,16 +571,24 @@ void launch_t(const void* xv, int64_t R, int64_t C, int br, ScaleSrc src, uint8_
         }
     }
     if (pt && R > 0 && C > 0) {
-        const int64_t grid = cdiv(R, 32) * cdiv(C, 256);
         float* s2 = wrote_scalars ? nullptr : S_out;
         float* a2 = wrote_scalars ? nullptr : amax_out;
-        if (sr.on)
-            k_nvfp4_col<T, 1, true><<<(unsigned)grid, kWG, 0, stream>>>(x, R, C, src, pt, codest, s2, a2, sr.seed,
-                                                                        sr.offset);
-        else if (br == 1)
-            k_nvfp4_col<T, 1><<<(unsigned)grid, kWG, 0, stream>>>(x, R, C, src, pt, codest, s2, a2);
-        else
+        if (br == 1) {
+            const unsigned g1 = (unsigned)(cdiv(R, 128) * cdiv(C, 64));
+            const uint64_t sd = sr.seed, of = sr.offset;
+            const uint32_t sg = rht.signs;
+            if (rht.on && sr.on)
+                k_nvfp4_colt<T, true, true><<<g1, kWG, 0, stream>>>(x, R, C, src, pt, codest, s2, a2, sd, of, sg);
+            else if (rht.on)
+                k_nvfp4_colt<T, false, true><<<g1, kWG, 0, stream>>>(x, R, C, src, pt, codest, s2, a2, sd, of, sg);
+            else if (sr.on)
+                k_nvfp4_colt<T, true, false><<<g1, kWG, 0, stream>>>(x, R, C, src, pt, codest, s2, a2, sd, of, sg);
+            else
+                k_nvfp4_colt<T, false, false><<<g1, kWG, 0, stream>>>(x, R, C, src, pt, codest, s2, a2, sd, of, sg);
+        } else {
+            const int64_t grid = cdiv(R, 32) * cdiv(C, 256);
             k_nvfp4_col<T, 16><<<(unsigned)grid, kWG, 0, stream>>>(x, R, C, src, pt, codest, s2, a2);
+        }
         wrote_scalars = true;
     }
     if (!wrote_scalars) {
@@ -421,12 +601,28 @@ void launch_t(const void* xv, int64_t R, int64_t C, int br, ScaleSrc src, uint8_
 
 hipError_t launch_nvfp4(const void* x, int in_bf16, int64_t R, int64_t C, int br, ScaleSrc src, uint8_t* p,
                         uint8_t* codes, uint8_t* pt, uint8_t* codest, float* S_out, float* amax_out, SrArgs sr,
-                        hipStream_t stream)
+                        RhtArgs rht, hipStream_t stream)
 {
     if (in_bf16)
-        launch_t<uint16_t>(x, R, C, br, src, p, codes, pt, codest, S_out, amax_out, sr, stream);
+        launch_t<uint16_t>(x, R, C, br, src, p, codes, pt, codest, S_out, amax_out, sr, rht, stream);
     else
-        launch_t<float>(x, R, C, br, src, p, codes, pt, codest, S_out, amax_out, sr, stream);
+        launch_t<float>(x, R, C, br, src, p, codes, pt, codest, S_out, amax_out, sr, rht, stream);
+    return hipGetLastError();
+}
+
+int rht_amax_grid(int64_t R, int64_t C)
+{
+    const int64_t nstrips = (R / 16) * cdiv(C, (int64_t)kWG * 4);  // upper bound over input types
+    return (int)std::max<int64_t>(1, std::min<int64_t>(nstrips, kMaxPartials));
+}
+
+hipError_t launch_rht_amax_partial(const void* x, int in_bf16, int64_t R, int64_t C, uint32_t signs,
+                                   float* partials, int grid, hipStream_t stream)
+{
+    if (in_bf16)
+        k_rht_amax_partial<uint16_t><<<grid, kWG, 0, stream>>>((const uint16_t*)x, R, C, signs, partials);
+    else
+        k_rht_amax_partial<float><<<grid, kWG, 0, stream>>>((const float*)x, R, C, signs, partials);
     return hipGetLastError();
 }
 

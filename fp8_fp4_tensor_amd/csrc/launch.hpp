@@ -110,10 +110,23 @@ struct SrArgs {
     uint64_t seed = 0, offset = 0;
 };
 
-// NVFP4 block pass (after the amax pass): 1x16 or 16x16 blocks; sr.on only with 1x16.
+// Random Hadamard transform of 16-element chunks along the rows of X^T.
+struct RhtArgs {
+    int on = 0;
+    uint32_t signs = 0;
+};
+
+// NVFP4 block pass (after the amax pass): 1x16 or 16x16 blocks; sr.on only
+// with 1x16; rht.on only with 1x16 and the colwise plane alone.
 hipError_t launch_nvfp4(const void* x, int in_bf16, int64_t R, int64_t C, int br, ScaleSrc src, uint8_t* p,
                         uint8_t* codes, uint8_t* pt, uint8_t* codest, float* S_out, float* amax_out, SrArgs sr,
-                        hipStream_t stream);
+                        RhtArgs rht, hipStream_t stream);
+
+// partials[g] = max|RHT(X^T)| over workgroup g's share of 16-row strips;
+// grid = rht_amax_grid(R, C) (<= kMaxPartials). R % 16 == 0, C % 16 == 0.
+int rht_amax_grid(int64_t R, int64_t C);
+hipError_t launch_rht_amax_partial(const void* x, int in_bf16, int64_t R, int64_t C, uint32_t signs,
+                                   float* partials, int grid, hipStream_t stream);
 
 // MXFP8 colwise copy (transposed codes and E8M0 codes) from the rowwise copy.
 hipError_t launch_mx_requant(const uint8_t* q, const uint8_t* e, int64_t R, int64_t C, uint8_t* qt, uint8_t* et,

@@ -24,6 +24,7 @@ FQ_PER_TENSOR_CURRENT, FQ_PER_TENSOR_DELAYED, FQ_BLOCK_FP32, FQ_MX, FQ_NVFP4 = r
 FQ_ROWWISE, FQ_COLWISE = 1, 2
 FQ_ROUND_NEAREST_EVEN, FQ_ROUND_STOCHASTIC = 0, 1
 FQ_SCALE_DEFAULT, FQ_SCALE_POW2 = 0, 1
+FQ_TRANSFORM_NONE, FQ_TRANSFORM_RHT16 = 0, 1
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfq.so")
 
@@ -32,7 +33,8 @@ class FqDesc(ctypes.Structure):
     _fields_ = [("recipe", ctypes.c_int32), ("in_dtype", ctypes.c_int32), ("format", ctypes.c_int32),
                 ("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("block_rows", ctypes.c_int32),
                 ("block_cols", ctypes.c_int32), ("outputs", ctypes.c_uint32), ("rounding", ctypes.c_int32),
-                ("scale_mode", ctypes.c_int32), ("seed", ctypes.c_uint64), ("offset", ctypes.c_uint64)]
+                ("scale_mode", ctypes.c_int32), ("seed", ctypes.c_uint64), ("offset", ctypes.c_uint64),
+                ("transform", ctypes.c_int32), ("rht_signs", ctypes.c_uint32)]
 
 
 class FqPlane(ctypes.Structure):
@@ -110,9 +112,9 @@ def _stream(stream) -> ctypes.c_void_p:
 # ---------------------------------------------------------------- descriptors
 def desc(recipe: int, in_dtype: int, fmt: int, rows: int, cols: int, block=(0, 0),
          outputs: int = FQ_ROWWISE, rounding: int = FQ_ROUND_NEAREST_EVEN, seed: int = 0, offset: int = 0,
-         scale_mode: int = FQ_SCALE_DEFAULT) -> FqDesc:
+         scale_mode: int = FQ_SCALE_DEFAULT, transform: int = FQ_TRANSFORM_NONE, rht_signs: int = 0) -> FqDesc:
     return FqDesc(recipe, in_dtype, fmt, rows, cols, block[0], block[1], outputs, rounding, scale_mode, seed,
-                  offset)
+                  offset, transform, rht_signs)
 
 
 def in_dtype_of(x: torch.Tensor) -> int:

@@ -124,6 +124,25 @@ enum { FQ_ROWWISE = 1, FQ_COLWISE = 2 };
 typedef enum { FQ_ROUND_NEAREST_EVEN = 0, FQ_ROUND_STOCHASTIC = 1 } fq_rounding;
 
 /*
+ * Transform applied before quantization.
+ *   FQ_TRANSFORM_NONE   (default).
+ *   FQ_TRANSFORM_RHT16  random Hadamard transform of the weight-gradient GEMM
+ *                       inputs ([LP] section 2.4 item 3): NVFP4 with 1x16
+ *                       blocks and outputs == FQ_COLWISE only. Each row of
+ *                       X^T (the GEMM's contraction runs along it) is
+ *                       transformed in 16-element chunks, y = (1/4) H16
+ *                       diag(s) x, H16 the Sylvester Hadamard matrix, s_i =
+ *                       -1 where bit i of rht_signs is set; computed in fp32
+ *                       by the fast Walsh-Hadamard butterfly (stages 1, 2, 4,
+ *                       8). The transformed tensor is then quantized: its
+ *                       amax sets the tensor scale (fq_amax returns that
+ *                       amax for this desc), and dequantization returns
+ *                       transformed values. The same rht_signs must be used
+ *                       for both operands of the GEMM.
+ */
+typedef enum { FQ_TRANSFORM_NONE = 0, FQ_TRANSFORM_RHT16 = 1 } fq_transform;
+
+/*
  * Scale encoding of FQ_BLOCK_FP32 (other recipes: FQ_SCALE_DEFAULT only).
  *   FQ_SCALE_DEFAULT  s_B = a_B/448 in fp32.
  *   FQ_SCALE_POW2     s_B = 2^(floor(log2 a_B) - 8), the MX rule on the tile
@@ -145,6 +164,7 @@ typedef enum { FQ_SCALE_DEFAULT = 0, FQ_SCALE_POW2 = 1 } fq_scale_mode;
  *   rounding, seed, offset:   element rounding (fq_rounding above); seed and
  *                             offset are read only for FQ_ROUND_STOCHASTIC.
  *   scale_mode:               fq_scale_mode above.
+ *   transform, rht_signs:     fq_transform above.
  *
  * Supported combinations (anything else is FQ_E_UNSUPPORTED):
  *   CURRENT, DELAYED  E4M3 or E5M2, f32 or bf16 input, any shape
@@ -154,6 +174,7 @@ typedef enum { FQ_SCALE_DEFAULT = 0, FQ_SCALE_POW2 = 1 } fq_scale_mode;
  *                     rows % 32 == 0
  *   scale_mode POW2   BLOCK_FP32 only
  *   rounding STOCHASTIC  NVFP4 with 1x16 blocks only
+ *   transform RHT16   NVFP4 with 1x16 blocks, outputs == FQ_COLWISE
  *   NVFP4             E2M1, rows % br == 0, cols % 16 == 0;
  *                     colwise needs rows % 16 == 0
  */
@@ -170,6 +191,8 @@ typedef struct {
     int32_t scale_mode; /* fq_scale_mode */
     uint64_t seed;      /* stochastic rounding: the Philox key */
     uint64_t offset;    /* stochastic rounding: stream number (e.g. the step) */
+    int32_t transform;  /* fq_transform */
+    uint32_t rht_signs; /* FQ_TRANSFORM_RHT16: sign mask, bits 0..15 */
 } fq_desc;
 
 /* One quantized copy: data codes and per-block scales (device memory). */

@@ -132,9 +132,29 @@ def test_mx_variant_sizes():
 
 
 def test_desc_layout():
-    # the C struct: three int32, two int64, two int32, uint32, two int32, two uint64
-    assert ctypes.sizeof(fq.FqDesc) == 72
+    # the C struct: three int32, two int64, two int32, uint32, two int32, two uint64, int32, uint32
+    assert ctypes.sizeof(fq.FqDesc) == 80
     assert fq.FqDesc.seed.offset == 56 and fq.FqDesc.offset.offset == 64
+    assert fq.FqDesc.transform.offset == 72 and fq.FqDesc.rht_signs.offset == 76
+
+
+@pytest.mark.parametrize("recipe,fmt,block,outputs,transform,want", [
+    (fq.FQ_NVFP4, fq.FQ_E2M1, (1, 16), fq.FQ_COLWISE, fq.FQ_TRANSFORM_RHT16, fq.FQ_OK),
+    (fq.FQ_NVFP4, fq.FQ_E2M1, (1, 16), fq.FQ_ROWWISE, fq.FQ_TRANSFORM_RHT16, fq.FQ_E_UNSUPPORTED),
+    (fq.FQ_NVFP4, fq.FQ_E2M1, (1, 16), 3, fq.FQ_TRANSFORM_RHT16, fq.FQ_E_UNSUPPORTED),
+    (fq.FQ_NVFP4, fq.FQ_E2M1, (16, 16), fq.FQ_COLWISE, fq.FQ_TRANSFORM_RHT16, fq.FQ_E_UNSUPPORTED),
+    (fq.FQ_MX, fq.FQ_E4M3, (1, 32), fq.FQ_COLWISE, fq.FQ_TRANSFORM_RHT16, fq.FQ_E_UNSUPPORTED),
+    (fq.FQ_BLOCK_FP32, fq.FQ_E4M3, (1, 128), fq.FQ_COLWISE, fq.FQ_TRANSFORM_RHT16, fq.FQ_E_UNSUPPORTED),
+    (fq.FQ_NVFP4, fq.FQ_E2M1, (1, 16), fq.FQ_COLWISE, 2, fq.FQ_E_INVALID),
+])
+def test_transform_validation(L, recipe, fmt, block, outputs, transform, want):
+    d = fq.desc(recipe, fq.FQ_IN_BF16, fmt, 256, 256, block, outputs, transform=transform, rht_signs=0x1234)
+    z = [ctypes.c_size_t() for _ in range(5)]
+    assert L.fq_sizes(ctypes.byref(d), *[ctypes.byref(v) for v in z]) == want
+    if want != fq.FQ_OK:
+        q = fq.FqQuantized(fq.FqPlane(B, B), fq.FqPlane(B, B), B, B)
+        assert L.fq_quantize(ctypes.byref(d), B, ctypes.byref(q), B, 1 << 20, None) == want
+        assert L.fq_amax(ctypes.byref(d), B, B, B, 1 << 20, None) == want
 
 
 def test_null_desc(L):
