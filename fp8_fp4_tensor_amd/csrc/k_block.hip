@@ -34,6 +34,11 @@ namespace {
 
 constexpr int kLoads = 4;
 constexpr int kMaxGrid = 16384;
+constexpr int kBlock128Tiles = 2;  // 128x128 tiles per workgroup, side by side
+
+// LDS column offset of the codes of row r: 8-byte units XOR-swizzled by the
+// row's 16-row group, so reads of one column over rows 16 apart hit distinct banks.
+__device__ __forceinline__ int code_swizzle(int r) { return 8 * ((r >> 4) & 7); }
 
 // Tile multiplier and stored scale from the tile amax.
 template <bool POW2>
@@ -130,24 +135,30 @@ __global__ __launch_bounds__(kWG) void k_block_1x128_col(const T* __restrict__ x
     st[(c0 + c) * (R / 128) + r0 / 128] = s;
 }
 
-// 128x128 tiles, one workgroup each. q/s rowwise (may be null), qt/st
-// colwise (may be null).
-template <typename T, bool POW2>
+// 128x128 tiles; a workgroup takes NT horizontally adjacent tiles (the rows
+// it reads and writes are then NT * 256 and NT * 128 contiguous bytes), kept
+// in registers between the tile maxima and the cast. q/s rowwise (may be
+// null), qt/st colwise (may be null): the colwise copy is the byte transpose
+// of the same codes, through LDS.
+template <typename T, bool POW2, int NT>
 __global__ __launch_bounds__(kWG) void k_block_128x128(const T* __restrict__ x, int64_t R, int64_t C,
                                                        uint8_t* __restrict__ q, float* __restrict__ s_out,
                                                        uint8_t* __restrict__ qt, float* __restrict__ st)
 {
-    constexpr int E = In<T>::kE, LPR = 128 / E, RPR = kWG / LPR, ROUNDS = 128 / RPR;
-    __shared__ float lds[4];
-    __shared__ __align__(16) uint8_t codes[128][128 + 16];
-    const int64_t ntc = C / 128, ntr = R / 128;
-    const int64_t tr = blockIdx.x / ntc, tc = blockIdx.x % ntc;
-    const int64_t r0 = tr * 128, c0 = tc * 128;
+    constexpr int E = In<T>::kE, W = 128 * NT, LPR = W / E, RPR = kWG / LPR, ROUNDS = 128 / RPR;
+    constexpr int LPT = 128 / E, NG = kWG / LPT;  // lanes per tile row; lane groups per workgroup
+    __shared__ float red[NG];
+    __shared__ __align__(16) uint8_t codes[128][W + 16];
+    const int64_t ntc = C / 128, ntr = R / 128, nwc = cdiv(ntc, NT);
+    const int64_t tr = blockIdx.x / nwc, tw = blockIdx.x % nwc;
+    const int64_t r0 = tr * 128, c0 = tw * W;
     const int cc = (threadIdx.x % LPR) * E, rr0 = threadIdx.x / LPR;
+    const int j = cc / 128;                  // this thread's tile in the workgroup
+    const bool tin = tw * NT + j < ntc;      // that tile exists (the last workgroup of a row may hold fewer)
     u32x4 v[ROUNDS];
 #pragma unroll
     for (int k = 0; k < ROUNDS; ++k)
-        v[k] = ld16_stream(x + (r0 + rr0 + k * RPR) * C + c0 + cc);
+        v[k] = tin ? ld16_stream(x + (r0 + rr0 + k * RPR) * C + c0 + cc) : u32x4{0u, 0u, 0u, 0u};
     float m = 0.0f;
 #pragma unroll
     for (int k = 0; k < ROUNDS; ++k) {
@@ -155,7 +166,16 @@ __global__ __launch_bounds__(kWG) void k_block_128x128(const T* __restrict__ x, 
         In<T>::unpack(v[k], f);
         m = fmaxf(m, absmax<E>(f));
     }
-    const float a = max_workgroup(m, lds);
+    // tile maxima: lanes of one tile row segment (LPT lanes), then the NG / NT
+    // groups of the same tile (group g holds tile g % NT)
+    m = max_lanes<LPT>(m);
+    if (threadIdx.x % LPT == 0)
+        red[threadIdx.x / LPT] = m;
+    __syncthreads();
+    float a = 0.0f;
+#pragma unroll
+    for (int g = 0; g < NG; g += NT)
+        a = fmaxf(a, red[g + j]);
     float alpha, s;
     tile_scales<POW2>(a, alpha, s);
 #pragma unroll
@@ -167,19 +187,20 @@ __global__ __launch_bounds__(kWG) void k_block_128x128(const T* __restrict__ x, 
             u32x2 w;
             w[0] = enc4<kE4M3>(f[0], f[1], f[2], f[3], alpha);
             w[1] = enc4<kE4M3>(f[4], f[5], f[6], f[7], alpha);
-            if (q)
+            if (q && tin)
                 st8_stream(q + (r0 + rr) * C + c0 + cc, w);
             if (qt)
-                *reinterpret_cast<u32x2*>(&codes[rr][cc]) = w;
+                *reinterpret_cast<u32x2*>(&codes[rr][cc ^ code_swizzle(rr)]) = w;
         } else {
             const uint32_t w = enc4<kE4M3>(f[0], f[1], f[2], f[3], alpha);
-            if (q)
+            if (q && tin)
                 st4_stream(q + (r0 + rr) * C + c0 + cc, w);
             if (qt)
-                *reinterpret_cast<uint32_t*>(&codes[rr][cc]) = w;
+                *reinterpret_cast<uint32_t*>(&codes[rr][cc ^ code_swizzle(rr)]) = w;
         }
     }
-    if (threadIdx.x == 0) {
+    if (tin && rr0 == 0 && cc % 128 == 0) {
+        const int64_t tc = tw * NT + j;
         if (s_out)
             s_out[tr * ntc + tc] = s;
         if (st)
@@ -187,19 +208,25 @@ __global__ __launch_bounds__(kWG) void k_block_128x128(const T* __restrict__ x, 
     }
     if (qt) {
         __syncthreads();
-        // thread -> column c of the tile, 64 rows starting at 64h
-        const int c = threadIdx.x & 127, h = threadIdx.x >> 7;
-        uint8_t* out = qt + (c0 + c) * R + r0 + 64 * h;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        // colwise: X^T rows c0 .. c0 + W - 1, 128 bytes each (rows r0 .. r0 + 127
+        // of the codes). Eight lanes per X^T row, lane k taking codes rows
+        // 16k .. 16k + 15, so each store instruction writes eight whole lines;
+        // the swizzle puts the eight lanes' byte reads in distinct banks.
+        const int k = threadIdx.x & 7;
+        for (int c = threadIdx.x >> 3; c < W; c += kWG / 8) {
             u32x4 w;
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
-                const int r = 64 * h + 16 * k + 4 * d;
-                w[d] = (uint32_t)codes[r][c] | ((uint32_t)codes[r + 1][c] << 8) |
-                       ((uint32_t)codes[r + 2][c] << 16) | ((uint32_t)codes[r + 3][c] << 24);
+                uint32_t word = 0;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int r = 16 * k + 4 * d + b;
+                    word |= (uint32_t)codes[r][c ^ code_swizzle(r)] << (8 * b);
+                }
+                w[d] = word;
             }
-            st16_stream(out + 16 * k, w);
+            if (c0 + c < C)
+                st16_stream(qt + (c0 + c) * R + r0 + 16 * k, w);
         }
     }
 }
@@ -244,20 +271,28 @@ hipError_t launch_block_1x128_colwise(const void* x, int in_bf16, int pow2, int6
     return hipGetLastError();
 }
 
+template <typename T, bool POW2>
+void block_128x128_t(const T* x, int64_t R, int64_t C, uint8_t* q, float* s, uint8_t* qt, float* st,
+                     hipStream_t stream)
+{
+    constexpr int NT = kBlock128Tiles;
+    const unsigned grid = (unsigned)(cdiv(C / 128, NT) * (R / 128));
+    k_block_128x128<T, POW2, NT><<<grid, kWG, 0, stream>>>(x, R, C, q, s, qt, st);
+}
+
 hipError_t launch_block_128x128(const void* x, int in_bf16, int pow2, int64_t R, int64_t C, uint8_t* q, float* s,
                                 uint8_t* qt, float* st, hipStream_t stream)
 {
-    const unsigned grid = (unsigned)((C / 128) * (R / 128));
     const uint16_t* xb = (const uint16_t*)x;
     const float* xf = (const float*)x;
     if (in_bf16 && pow2)
-        k_block_128x128<uint16_t, true><<<grid, kWG, 0, stream>>>(xb, R, C, q, s, qt, st);
+        block_128x128_t<uint16_t, true>(xb, R, C, q, s, qt, st, stream);
     else if (in_bf16)
-        k_block_128x128<uint16_t, false><<<grid, kWG, 0, stream>>>(xb, R, C, q, s, qt, st);
+        block_128x128_t<uint16_t, false>(xb, R, C, q, s, qt, st, stream);
     else if (pow2)
-        k_block_128x128<float, true><<<grid, kWG, 0, stream>>>(xf, R, C, q, s, qt, st);
+        block_128x128_t<float, true>(xf, R, C, q, s, qt, st, stream);
     else
-        k_block_128x128<float, false><<<grid, kWG, 0, stream>>>(xf, R, C, q, s, qt, st);
+        block_128x128_t<float, false>(xf, R, C, q, s, qt, st, stream);
     return hipGetLastError();
 }
 
