@@ -17,10 +17,9 @@
 //                      tile max is a 4-step DPP reduction inside a row of
 //                      lanes. One read, no LDS.
 //   k_block_1x128_col  the colwise copy: 1x128 tiles of X^T, i.e. 128-row
-//                      runs down each column. A 128-row x 256-column slab is
-//                      staged in LDS with coalesced row loads; each thread
-//                      then owns one column: reduces it, casts it and writes
-//                      its 128 codes as one contiguous 128-byte line of X^T.
+//                      runs down each column. A 128-row x 64-column tile is
+//                      staged in LDS (swizzled); four lanes share a column
+//                      (DPP max) and write its 128 codes, one line of X^T.
 //   k_block_128x128    one workgroup per tile, kept in registers between the
 //                      tile max and the cast; the colwise copy is the byte
 //                      transpose of the same codes, through LDS.
@@ -88,51 +87,49 @@ __global__ __launch_bounds__(kWG) void k_block_1x128(const T* __restrict__ x, in
     }
 }
 
-// Colwise 1x128: tiles of X^T. Slab of 128 rows x TC columns in LDS.
+// Colwise 1x128: tiles of X^T (128 rows of one column of X). One 128-row x
+// 64-column tile per workgroup, staged in LDS with its 16-byte chunks
+// XOR-swizzled by 32-row group. Thread t takes column c = t >> 2 and rows
+// 32q .. 32q + 31, q = t & 3: the column max is a quad of lanes (two DPP
+// steps), and each lane writes 32 contiguous bytes of the 128-byte line of
+// X^T (ordinary stores: the four lanes' pieces of a line meet in L2).
 template <typename T, bool POW2>
 __global__ __launch_bounds__(kWG) void k_block_1x128_col(const T* __restrict__ x, int64_t R, int64_t C,
                                                          uint8_t* __restrict__ qt, float* __restrict__ st)
 {
-    constexpr int TC = sizeof(T) == 2 ? 256 : 128;           // columns per slab (64 KiB of LDS)
-    constexpr int E = In<T>::kE, LPR = TC / E;               // lanes per slab row
-    constexpr int RPR = kWG / LPR;                           // slab rows per load round
-    extern __shared__ __align__(16) unsigned char smem[];
-    T* tile = reinterpret_cast<T*>(smem);                    // [128][TC]
-    const int64_t ntc = cdiv(C, TC);
+    constexpr int TC = 64, E = In<T>::kE, CPR = TC / E, SW = 16 / E;  // chunks per row; swizzle step
+    __shared__ __align__(16) T tile[128][TC];
+    const int64_t ntc = C / TC;  // C % 128 == 0
     const int64_t r0 = (int64_t)(blockIdx.x / ntc) * 128, c0 = (int64_t)(blockIdx.x % ntc) * TC;
-    const int cc = (threadIdx.x % LPR) * E;
-    // stage the slab: coalesced 16-byte loads along rows
-#pragma unroll 4
-    for (int rr = threadIdx.x / LPR; rr < 128; rr += RPR) {
-        u32x4 v = u32x4{0u, 0u, 0u, 0u};
-        if (c0 + cc < C)
-            v = ld16_stream(x + (r0 + rr) * C + c0 + cc);
-        *reinterpret_cast<u32x4*>(tile + rr * TC + cc) = v;
+    for (int i = threadIdx.x; i < 128 * CPR; i += kWG) {
+        const int r = i / CPR, j = i % CPR;
+        const u32x4 v = ld16_stream(x + (r0 + r) * C + c0 + j * E);
+        *reinterpret_cast<u32x4*>(&tile[r][(j ^ (SW * ((r >> 5) & 3))) * E]) = v;
     }
     __syncthreads();
-    const int c = threadIdx.x;
-    if (c >= TC || c0 + c >= C)
-        return;
-    float a = 0.0f;
-    for (int r = 0; r < 128; ++r)
-        a = fmaxf(a, fabsf(In<T>::load1(tile, (int64_t)r * TC + c)));
+    const int c = threadIdx.x >> 2, q = threadIdx.x & 3;
+    const int col = ((c / E) ^ (SW * q)) * E + (c % E);  // column c's place in rows 32q .. 32q + 31
+    float f[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k)
+        f[k] = In<T>::load1(&tile[32 * q + k][0], col);
+    const float a = max_lanes4(absmax<32>(f));
     float alpha, s;
     tile_scales<POW2>(a, alpha, s);
-    uint8_t* out = qt + (c0 + c) * R + r0;
-#pragma unroll 2
-    for (int r = 0; r < 128; r += 16) {
-        float f[16];
-#pragma unroll
-        for (int k = 0; k < 16; ++k)
-            f[k] = In<T>::load1(tile, (int64_t)(r + k) * TC + c);
-        u32x4 w;
-        w[0] = enc4<kE4M3>(f[0], f[1], f[2], f[3], alpha);
-        w[1] = enc4<kE4M3>(f[4], f[5], f[6], f[7], alpha);
-        w[2] = enc4<kE4M3>(f[8], f[9], f[10], f[11], alpha);
-        w[3] = enc4<kE4M3>(f[12], f[13], f[14], f[15], alpha);
-        st16_stream(out + r, w);
-    }
-    st[(c0 + c) * (R / 128) + r0 / 128] = s;
+    u32x4 w0, w1;
+    w0[0] = enc4<kE4M3>(f[0], f[1], f[2], f[3], alpha);
+    w0[1] = enc4<kE4M3>(f[4], f[5], f[6], f[7], alpha);
+    w0[2] = enc4<kE4M3>(f[8], f[9], f[10], f[11], alpha);
+    w0[3] = enc4<kE4M3>(f[12], f[13], f[14], f[15], alpha);
+    w1[0] = enc4<kE4M3>(f[16], f[17], f[18], f[19], alpha);
+    w1[1] = enc4<kE4M3>(f[20], f[21], f[22], f[23], alpha);
+    w1[2] = enc4<kE4M3>(f[24], f[25], f[26], f[27], alpha);
+    w1[3] = enc4<kE4M3>(f[28], f[29], f[30], f[31], alpha);
+    uint8_t* out = qt + (c0 + c) * R + r0 + 32 * q;
+    *reinterpret_cast<u32x4*>(out) = w0;
+    *reinterpret_cast<u32x4*>(out + 16) = w1;
+    if (q == 0)
+        st[(c0 + c) * (R / 128) + r0 / 128] = s;
 }
 
 // 128x128 tiles; a workgroup takes NT horizontally adjacent tiles (the rows
@@ -256,18 +253,17 @@ hipError_t launch_block_1x128(const void* x, int in_bf16, int pow2, int64_t R, i
 hipError_t launch_block_1x128_colwise(const void* x, int in_bf16, int pow2, int64_t R, int64_t C, uint8_t* qt,
                                       float* st, hipStream_t stream)
 {
-    const int tc = in_bf16 ? 256 : 128;
-    const unsigned grid = (unsigned)(cdiv(C, tc) * (R / 128));
+    const unsigned grid = (unsigned)((C / 64) * (R / 128));
     const uint16_t* xb = (const uint16_t*)x;
     const float* xf = (const float*)x;
     if (in_bf16 && pow2)
-        k_block_1x128_col<uint16_t, true><<<grid, kWG, 128 * 256 * 2, stream>>>(xb, R, C, qt, st);
+        k_block_1x128_col<uint16_t, true><<<grid, kWG, 0, stream>>>(xb, R, C, qt, st);
     else if (in_bf16)
-        k_block_1x128_col<uint16_t, false><<<grid, kWG, 128 * 256 * 2, stream>>>(xb, R, C, qt, st);
+        k_block_1x128_col<uint16_t, false><<<grid, kWG, 0, stream>>>(xb, R, C, qt, st);
     else if (pow2)
-        k_block_1x128_col<float, true><<<grid, kWG, 128 * 128 * 4, stream>>>(xf, R, C, qt, st);
+        k_block_1x128_col<float, true><<<grid, kWG, 0, stream>>>(xf, R, C, qt, st);
     else
-        k_block_1x128_col<float, false><<<grid, kWG, 128 * 128 * 4, stream>>>(xf, R, C, qt, st);
+        k_block_1x128_col<float, false><<<grid, kWG, 0, stream>>>(xf, R, C, qt, st);
     return hipGetLastError();
 }
 

@@ -107,8 +107,9 @@ __global__ __launch_bounds__(kWG) void k_mxfp4_col(const T* __restrict__ x, int6
     w[1] = enc8_e2m1(f + 8, m);
     w[2] = enc8_e2m1(f + 16, m);
     w[3] = enc8_e2m1(f + 24, m);
-    // row c0 + c of X^T: R/2 bytes, a multiple of 16 (R % 32 == 0)
-    st16_stream(pt + (c0 + c) * (R / 2) + r0 / 2, w);
+    // row c0 + c of X^T: R/2 bytes, a multiple of 16 (R % 32 == 0); an
+    // ordinary store, so a line's 16-byte pieces meet in L2
+    *reinterpret_cast<u32x4*>(pt + (c0 + c) * (R / 2) + r0 / 2) = w;
     ct[(c0 + c) * (R / 32) + r0 / 32] = (uint8_t)code;
 }
 
