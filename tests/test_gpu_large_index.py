@@ -1,0 +1,115 @@
+"""GPU parity beyond 2^31 elements: 64-bit indexing in every kernel family.
+
+The input is 65664 x 32768 bf16 (2.15e9 elements, 4.3 GB), built on the GPU
+row chunk by row chunk from an integer formula whose values are exact in
+bf16: x[r, c] = (((1103 r + 2221 c) mod 256) - 128) / 64 * 2^((r + c // 128) mod 8).
+The oracle regenerates sampled rows (and columns) exactly in numpy and checks
+them bit for bit, including rows whose elements lie past index 2^31. The
+tensor amax is 256 by construction (k = -128 at scale 2^7 occurs)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from fp8_fp4_tensor_amd import fq
+from gpu_util import f32, host, same_bytes
+
+pytestmark = pytest.mark.gpu
+
+R, C = 65664, 32768          # R % 128 == 0; R * C > 2^31
+AMAX = 256.0
+
+
+def values(r, c):
+    """The input at rows r (column vector) and columns c (row vector), fp32 (exact bf16)."""
+    r = np.asarray(r, np.int64)
+    c = np.asarray(c, np.int64)
+    k = ((1103 * r + 2221 * c) % 256) - 128
+    return (k.astype(np.float32) / np.float32(64.0)) * np.exp2(((r + c // 128) % 8).astype(np.float32))
+
+
+def bf16_bits(v):
+    return (np.ascontiguousarray(v, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.fixture(scope="module")
+def big():
+    x = torch.empty((R, C), dtype=torch.bfloat16, device="cuda")
+    c = torch.arange(C, device="cuda", dtype=torch.int32)
+    step = 2048
+    for r0 in range(0, R, step):
+        r = torch.arange(r0, min(r0 + step, R), device="cuda", dtype=torch.int32)[:, None]
+        k = ((1103 * r + 2221 * c) % 256) - 128
+        e = ((r + c // 128) % 8).to(torch.float32)
+        x[r0:r0 + step] = (k.to(torch.float32) / 64.0 * torch.exp2(e)).to(torch.bfloat16)
+    torch.cuda.synchronize()
+    # spot check the construction against the numpy formula
+    rows = [0, R - 1]
+    assert np.array_equal(host(x[rows].view(torch.int16)).view(np.uint16),
+                          bf16_bits(values(np.array(rows)[:, None], np.arange(C)[None, :])))
+    yield x
+    del x
+    torch.cuda.empty_cache()
+
+
+SAMPLE_ROWS = np.array([0, 65536, R - 2, R - 1])       # rows past element 2^31 = row 65536
+
+
+def sample(xg_rows):
+    return bf16_bits(values(SAMPLE_ROWS[:, None], np.arange(C)[None, :]))
+
+
+def quantize(d, x):
+    out = fq.alloc_quantized(d)
+    fq.fq_quantize(d, x, out, fq.alloc_workspace(d))
+    torch.cuda.synchronize()
+    return out
+
+
+def test_large_current(big):
+    d = fq.desc(fq.FQ_PER_TENSOR_CURRENT, fq.FQ_IN_BF16, fq.FQ_E4M3, R, C, (0, 0), fq.FQ_ROWWISE)
+    out = quantize(d, big)
+    same_bytes(host(out.amax), f32(AMAX), "tensor amax")
+    want = orc.quantize_with_amax(sample(None), orc.E4M3, AMAX, shape=(len(SAMPLE_ROWS), C))
+    same_bytes(host(out.tensor_scale), f32(want["s"]), "scale")
+    same_bytes(host(out.row_data[SAMPLE_ROWS]), want["q_row"], "codes of sampled rows")
+    del out
+
+
+@pytest.mark.parametrize("block", [(1, 128), (128, 128)])
+def test_large_block(big, block):
+    d = fq.desc(fq.FQ_BLOCK_FP32, fq.FQ_IN_BF16, fq.FQ_E4M3, R, C, block, fq.FQ_ROWWISE)
+    out = quantize(d, big)
+    br = block[0]
+    rows = SAMPLE_ROWS if br == 1 else np.arange(R - 128, R)     # the last tile row
+    xs = bf16_bits(values(rows[:, None], np.arange(C)[None, :]))
+    want = orc.quantize_block(xs, block)
+    same_bytes(host(out.row_data[rows]), want["q_row"], "codes")
+    srow = rows if br == 1 else [R // 128 - 1]
+    same_bytes(host(out.row_scale.view(R // br, C // 128)[srow]), want["s_row"], "scales")
+    del out
+
+
+def test_large_mx_both_planes(big):
+    d = fq.desc(fq.FQ_MX, fq.FQ_IN_BF16, fq.FQ_E4M3, R, C, (1, 32), fq.FQ_ROWWISE | fq.FQ_COLWISE)
+    out = quantize(d, big)
+    want = orc.quantize_mx(sample(None), outputs=orc.ROWWISE)
+    same_bytes(host(out.row_data[SAMPLE_ROWS]), want["q_row"], "rowwise codes")
+    same_bytes(host(out.row_scale.view(R, C // 32)[SAMPLE_ROWS]), want["e_row"], "rowwise E8M0")
+    cols = np.array([0, 12345, C - 1])
+    xc = bf16_bits(values(np.arange(R)[:, None], cols[None, :]).T.copy())   # X^T rows = columns of X
+    wc = orc.quantize_mx(xc, outputs=orc.ROWWISE)
+    same_bytes(host(out.col_data[cols]), wc["q_row"], "colwise codes (columns of X)")
+    same_bytes(host(out.col_scale.view(C, R // 32)[cols]), wc["e_row"], "colwise E8M0")
+    del out
+
+
+def test_large_nvfp4(big):
+    d = fq.desc(fq.FQ_NVFP4, fq.FQ_IN_BF16, fq.FQ_E2M1, R, C, (1, 16), fq.FQ_ROWWISE)
+    out = quantize(d, big)
+    same_bytes(host(out.amax), f32(AMAX), "tensor amax")
+    want = orc.quantize_nvfp4(sample(None), (1, 16), amax=AMAX)
+    same_bytes(host(out.tensor_scale), f32(want["S"]), "tensor scale")
+    same_bytes(host(out.row_data[SAMPLE_ROWS]), want["p_row"], "packed FP4")
+    same_bytes(host(out.row_scale.view(R, C // 16)[SAMPLE_ROWS]), want["c_row"], "E4M3 block scales")
+    del out
