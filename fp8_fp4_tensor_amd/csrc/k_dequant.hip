@@ -9,11 +9,11 @@
 // (value = element x block scale; E4M3 or E5M2 elements) and section
 // "NVFP4"; [LP] "从 BF16 到 FP8/FP4" section 2.4 (MXFP4).
 //
-// Bandwidth layout: a thread step is 16 elements (16 code bytes, or 8 packed
-// FP4 bytes) read with one vector load and written as 64 (fp32) or 32 (bf16)
-// contiguous bytes. Per-tensor codes are treated as a flat array; block
-// recipes walk rows (a workgroup per row, threads across it), so every
-// 16-element step lies inside one block and takes one scale, with no
+// Bandwidth layout: a lane chunk is the elements of 16 output bytes (8 for
+// bf16, 4 for fp32), so each store instruction of a wave writes 1 KiB of
+// contiguous output; lanes keep several chunks' loads in flight. Per-tensor
+// codes are treated as a flat array; block recipes give a workgroup a row,
+// and every chunk lies inside one block and takes one scale, with no
 // division per element. Codes decode exactly with the gfx950 converters.
 #include <algorithm>
 
@@ -30,29 +30,57 @@ constexpr int kGrid = 8192;
 
 enum : int { kDqE4M3 = 0, kDqE5M2 = 1, kDqFp4 = 2 };
 
-// 16 codes (one dword per four FP8 codes, or two FP4 nibbles per byte) -> 16 floats
-template <int CODE>
-__device__ __forceinline__ void decode16(const uint32_t* w, float* f)
+// A lane chunk is G elements whose output is exactly 16 bytes: G = 8 for
+// bf16 output, 4 for fp32. Consecutive lanes take consecutive chunks, so a
+// wave's store instruction writes 1 KiB of contiguous output (whole lines;
+// streaming stores of lines a lane only partly covers each became
+// partial-line writes and ran 2-4x slower). Chunks lie inside one block.
+template <bool BF16>
+constexpr int chunk_elems() { return BF16 ? 8 : 4; }
+constexpr int kChunks = 4;  // chunks per lane with loads in flight
+
+// G codes starting at element e (FP8: G bytes; FP4: G/2 bytes), zero-extended into w
+template <int CODE, int G>
+__device__ __forceinline__ void load_chunk(const uint8_t* q, int64_t e, uint32_t* w)
 {
     if constexpr (CODE == kDqFp4) {
-#pragma unroll
-        for (int d = 0; d < 2; ++d) {
-            const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[d], 1.0f, 0);
-            const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[d], 1.0f, 1);
-            const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[d], 1.0f, 2);
-            const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[d], 1.0f, 3);
-            f[8 * d] = v0[0];
-            f[8 * d + 1] = v0[1];
-            f[8 * d + 2] = v1[0];
-            f[8 * d + 3] = v1[1];
-            f[8 * d + 4] = v2[0];
-            f[8 * d + 5] = v2[1];
-            f[8 * d + 6] = v3[0];
-            f[8 * d + 7] = v3[1];
+        if constexpr (G == 8)
+            w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(q + e / 2));
+        else
+            w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(q + e / 2));
+    } else {
+        if constexpr (G == 8) {
+            const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(q + e));
+            w[0] = v[0];
+            w[1] = v[1];
+        } else {
+            w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(q + e));
+        }
+    }
+}
+
+// G codes -> G floats, exact (gfx950 converters; FP4 byte_sel must be a constant)
+template <int CODE, int G>
+__device__ __forceinline__ void decode_chunk(const uint32_t* w, float* f)
+{
+    if constexpr (CODE == kDqFp4) {
+        f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[0], 1.0f, 0);
+        f[0] = v[0];
+        f[1] = v[1];
+        v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[0], 1.0f, 1);
+        f[2] = v[0];
+        f[3] = v[1];
+        if constexpr (G == 8) {
+            v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[0], 1.0f, 2);
+            f[4] = v[0];
+            f[5] = v[1];
+            v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[0], 1.0f, 3);
+            f[6] = v[0];
+            f[7] = v[1];
         }
     } else {
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
+        for (int d = 0; d < G / 4; ++d) {
             f32x2 lo, hi;
             if constexpr (CODE == kDqE4M3) {
                 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[d], false);
@@ -69,45 +97,24 @@ __device__ __forceinline__ void decode16(const uint32_t* w, float* f)
     }
 }
 
-// 16 codes of a step: FP8 codes are 16 bytes, FP4 codes 8 bytes
-template <int CODE>
-__device__ __forceinline__ void load_codes(const uint8_t* q, int64_t step, uint32_t* w)
-{
-    if constexpr (CODE == kDqFp4) {
-        const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(q + step * 8));
-        w[0] = v[0];
-        w[1] = v[1];
-    } else {
-        const u32x4 v = ld16_stream(q + step * 16);
-        w[0] = v[0];
-        w[1] = v[1];
-        w[2] = v[2];
-        w[3] = v[3];
-    }
-}
-
-// 16 values times sc -> y[step*16 .. +16), fp32 or bf16
+// G values times sc -> 16 bytes of y at element e (bf16: one RTNE rounding of the fp32 product)
 template <bool BF16>
-__device__ __forceinline__ void store16(void* y, int64_t step, const float* f, float sc)
+__device__ __forceinline__ void store_chunk(void* y, int64_t e, const float* f, float sc)
 {
     if constexpr (BF16) {
-        uint32_t h[8];
+        uint32_t h[4];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
+        for (int k = 0; k < 4; ++k) {
             bf16x2 b;
             b[0] = (__bf16)(f[2 * k] * sc);
             b[1] = (__bf16)(f[2 * k + 1] * sc);
             h[k] = __builtin_bit_cast(uint32_t, b);
         }
-        uint8_t* p = reinterpret_cast<uint8_t*>(y) + step * 32;
-        st16_stream(p, u32x4{h[0], h[1], h[2], h[3]});
-        st16_stream(p + 16, u32x4{h[4], h[5], h[6], h[7]});
+        st16_stream(reinterpret_cast<uint8_t*>(y) + e * 2, u32x4{h[0], h[1], h[2], h[3]});
     } else {
-        uint8_t* p = reinterpret_cast<uint8_t*>(y) + step * 64;
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            st16_stream(p + 16 * k, u32x4{__float_as_uint(f[4 * k] * sc), __float_as_uint(f[4 * k + 1] * sc),
-                                          __float_as_uint(f[4 * k + 2] * sc), __float_as_uint(f[4 * k + 3] * sc)});
+        st16_stream(reinterpret_cast<uint8_t*>(y) + e * 4,
+                    u32x4{__float_as_uint(f[0] * sc), __float_as_uint(f[1] * sc), __float_as_uint(f[2] * sc),
+                          __float_as_uint(f[3] * sc)});
     }
 }
 
@@ -120,52 +127,78 @@ __device__ __forceinline__ void store1(void* y, int64_t i, float v)
         reinterpret_cast<float*>(y)[i] = v;
 }
 
-// Per-tensor: flat codes, one scale.
+// Per-tensor: flat codes, one scale; kChunks chunks per lane per round, the
+// round's loads issued before any decode.
 template <int CODE, bool BF16>
 __global__ __launch_bounds__(kWG) void k_dq_tensor(const uint8_t* __restrict__ q, int64_t n, const float* s,
                                                    void* __restrict__ y)
 {
+    constexpr int G = chunk_elems<BF16>();
     const float sc = *s;
-    const int64_t nsteps = n / 16;
-    for (int64_t i = (int64_t)blockIdx.x * kWG + threadIdx.x; i < nsteps; i += (int64_t)gridDim.x * kWG) {
-        uint32_t w[4];
-        float f[16];
-        load_codes<CODE>(q, i, w);
-        decode16<CODE>(w, f);
-        store16<BF16>(y, i, f, sc);
+    const int64_t nch = n / G, nthreads = (int64_t)gridDim.x * kWG;
+    const int64_t t = (int64_t)blockIdx.x * kWG + threadIdx.x;
+    for (int64_t base = t; base < nch; base += nthreads * kChunks) {
+        uint32_t w[kChunks][2];
+#pragma unroll
+        for (int k = 0; k < kChunks; ++k)
+            if (base + k * nthreads < nch)
+                load_chunk<CODE, G>(q, (base + k * nthreads) * G, w[k]);
+#pragma unroll
+        for (int k = 0; k < kChunks; ++k) {
+            const int64_t i = base + k * nthreads;
+            if (i < nch) {
+                float f[G];
+                decode_chunk<CODE, G>(w[k], f);
+                store_chunk<BF16>(y, i * G, f, sc);
+            }
+        }
     }
-    for (int64_t i = nsteps * 16 + (int64_t)blockIdx.x * kWG + threadIdx.x; i < n; i += (int64_t)gridDim.x * kWG) {
+    for (int64_t i = nch * G + t; i < n; i += nthreads) {
         const float v = CODE == kDqE4M3 ? dec_e4m3(q[i]) : dec_e5m2(q[i]);
         store1<BF16>(y, i, v * sc);
     }
 }
 
-// Block scales (fp32, MX E8M0, NVFP4 E4M3 x S): a workgroup per row.
+// Block scales (fp32, MX E8M0, NVFP4 E4M3 x S): a workgroup per row, lanes
+// across it in chunks; a chunk lies inside one block (C % 16 == 0, blocks 16,
+// 32 or 128 wide), so it takes one scale.
 // SKIND: 0 fp32 scale plane, 1 E8M0 codes, 2 E4M3 codes times the tensor scale.
 template <int CODE, int SKIND, bool BF16>
 __global__ __launch_bounds__(kWG) void k_dq_rows(const uint8_t* __restrict__ q, const void* __restrict__ scales,
                                                  const float* S, int64_t R, int64_t C, int br, int bc,
                                                  void* __restrict__ y)
 {
-    const int64_t steps_per_row = C / 16, nbc = C / bc;
+    constexpr int G = chunk_elems<BF16>();
+    const int64_t cpr = C / G, nbc = C / bc;
     const float Sv = SKIND == 2 ? *S : 1.0f;
     for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
         const int64_t srow = (r / br) * nbc;
-        for (int64_t j = threadIdx.x; j < steps_per_row; j += kWG) {
-            const int64_t step = r * steps_per_row + j;
-            const int64_t si = srow + (16 * j) / bc;
-            float sc;
-            if constexpr (SKIND == 0)
-                sc = reinterpret_cast<const float*>(scales)[si];
-            else if constexpr (SKIND == 1)
-                sc = e8m0_value(reinterpret_cast<const uint8_t*>(scales)[si]);
-            else
-                sc = dec_e4m3(reinterpret_cast<const uint8_t*>(scales)[si]) * Sv;
-            uint32_t w[4];
-            float f[16];
-            load_codes<CODE>(q, step, w);
-            decode16<CODE>(w, f);
-            store16<BF16>(y, step, f, sc);
+        for (int64_t j0 = threadIdx.x; j0 < cpr; j0 += kWG * kChunks) {
+            uint32_t w[kChunks][2];
+            float sc[kChunks];
+#pragma unroll
+            for (int k = 0; k < kChunks; ++k) {
+                const int64_t j = j0 + k * kWG;
+                if (j < cpr) {
+                    load_chunk<CODE, G>(q, r * C + j * G, w[k]);
+                    const int64_t si = srow + (j * G) / bc;
+                    if constexpr (SKIND == 0)
+                        sc[k] = reinterpret_cast<const float*>(scales)[si];
+                    else if constexpr (SKIND == 1)
+                        sc[k] = e8m0_value(reinterpret_cast<const uint8_t*>(scales)[si]);
+                    else
+                        sc[k] = dec_e4m3(reinterpret_cast<const uint8_t*>(scales)[si]) * Sv;
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < kChunks; ++k) {
+                const int64_t j = j0 + k * kWG;
+                if (j < cpr) {
+                    float f[G];
+                    decode_chunk<CODE, G>(w[k], f);
+                    store_chunk<BF16>(y, r * C + j * G, f, sc[k]);
+                }
+            }
         }
     }
 }
@@ -188,7 +221,7 @@ void rows_t(const uint8_t* q, const void* s, const float* S, int64_t R, int64_t 
 hipError_t launch_dequant_tensor(const uint8_t* q, int fmt, int64_t n, const float* s, void* y, int bf,
                                  hipStream_t stream)
 {
-    const int grid = grid_for(n / 16 + 1);
+    const int grid = grid_for(cdiv(n / 4, kChunks) + 1);
     if (fmt == kE4M3) {
         if (bf)
             k_dq_tensor<kDqE4M3, true><<<grid, kWG, 0, stream>>>(q, n, s, y);
