@@ -190,6 +190,95 @@ __global__ __launch_bounds__(kWG) void k_cast_tensor_2d(const T* __restrict__ x,
     }
 }
 
+// Per-tensor cast with the colwise copy, for R % 16 == 0 and C % 16 == 0:
+// 128x128 tiles, workgroups striding over tiles; 16-byte loads, rowwise
+// codes stored from registers, and the transposed codes through an LDS tile
+// XOR-swizzled in 8-byte units by 16-row group, written with eight lanes per
+// 128-byte row of X^T (edge tiles: rows of X^T of rows_in bytes). Optionally
+// one amax partial per workgroup (delayed scaling).
+__device__ __forceinline__ int tile_swizzle(int r) { return 8 * ((r >> 4) & 7); }
+
+template <typename T, int FMT>
+__global__ __launch_bounds__(kWG) void k_cast_tensor_tile(const T* __restrict__ x, int64_t R, int64_t C,
+                                                          ScaleSrc src, uint8_t* __restrict__ q,
+                                                          uint8_t* __restrict__ qt, float* s_out, float* amax_out,
+                                                          float* partials_out)
+{
+    constexpr int E = In<T>::kE, LPR = 128 / E, RPR = kWG / LPR, ROUNDS = 128 / RPR;
+    __shared__ float lds[4];
+    __shared__ __align__(16) uint8_t codes[128][128 + 16];
+    float alpha, s, a;
+    resolve_scale<FMT>(src, lds, alpha, s, a);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (s_out)
+            *s_out = s;
+        if (amax_out)
+            *amax_out = a;
+    }
+    const int64_t ntc = cdiv(C, 128), ntiles = cdiv(R, 128) * ntc;
+    const int cc = (threadIdx.x % LPR) * E, rr0 = threadIdx.x / LPR;
+    float m = 0.0f;
+    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const int64_t r0 = (t / ntc) * 128, c0 = (t % ntc) * 128;
+        const int rows_in = (int)min((int64_t)128, R - r0), cols_in = (int)min((int64_t)128, C - c0);
+        __syncthreads();  // the previous tile's LDS reads are done
+        u32x4 v[ROUNDS];
+#pragma unroll
+        for (int k = 0; k < ROUNDS; ++k) {
+            const int rr = rr0 + k * RPR;
+            v[k] = (rr < rows_in && cc < cols_in) ? ld16_stream(x + (r0 + rr) * C + c0 + cc) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int k = 0; k < ROUNDS; ++k) {
+            const int rr = rr0 + k * RPR;
+            float f[E];
+            In<T>::unpack(v[k], f);
+            if (partials_out)
+                m = fmaxf(m, absmax<E>(f));
+            const bool in = rr < rows_in && cc < cols_in;
+            if constexpr (E == 8) {
+                u32x2 w;
+                w[0] = enc4<FMT>(f[0], f[1], f[2], f[3], alpha);
+                w[1] = enc4<FMT>(f[4], f[5], f[6], f[7], alpha);
+                if (q && in)
+                    st8_stream(q + (r0 + rr) * C + c0 + cc, w);
+                if (qt)
+                    *reinterpret_cast<u32x2*>(&codes[rr][cc ^ tile_swizzle(rr)]) = w;
+            } else {
+                const uint32_t w = enc4<FMT>(f[0], f[1], f[2], f[3], alpha);
+                if (q && in)
+                    st4_stream(q + (r0 + rr) * C + c0 + cc, w);
+                if (qt)
+                    *reinterpret_cast<uint32_t*>(&codes[rr][cc ^ tile_swizzle(rr)]) = w;
+            }
+        }
+        if (!qt)
+            continue;
+        __syncthreads();
+        const int kq = threadIdx.x & 7;
+        for (int c = threadIdx.x >> 3; c < cols_in; c += kWG / 8) {
+            u32x4 w;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                uint32_t word = 0;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int r = 16 * kq + 4 * d + b;
+                    word |= (uint32_t)codes[r][c ^ tile_swizzle(r)] << (8 * b);
+                }
+                w[d] = word;
+            }
+            if (16 * kq < rows_in)
+                st16_stream(qt + (c0 + c) * R + r0 + 16 * kq, w);
+        }
+    }
+    if (partials_out) {
+        m = max_workgroup(m, lds);
+        if (threadIdx.x == 0)
+            partials_out[blockIdx.x] = m;
+    }
+}
+
 __global__ __launch_bounds__(kWG) void k_amax_finish(const float* __restrict__ partials, int n, float* out)
 {
     __shared__ float lds[4];
@@ -310,10 +399,36 @@ static void cast_2d_t(const void* x, int64_t R, int64_t C, ScaleSrc src, uint8_t
                                                        partials_out);
 }
 
+template <typename T, int FMT>
+void cast_tile_t(const void* x, int64_t R, int64_t C, ScaleSrc src, uint8_t* q, uint8_t* qt, float* s_out,
+                 float* amax_out, float* partials_out, int grid, hipStream_t stream)
+{
+    k_cast_tensor_tile<T, FMT><<<grid, kWG, 0, stream>>>((const T*)x, R, C, src, q, qt, s_out, amax_out,
+                                                         partials_out);
+}
+
 hipError_t launch_cast_tensor_2d(const void* x, int in_bf16, int fmt, int64_t R, int64_t C, ScaleSrc src,
                                  uint8_t* q, uint8_t* qt, float* s_out, float* amax_out, float* partials_out,
                                  int grid, hipStream_t stream)
 {
+    if (R % 16 == 0 && C % 16 == 0) {
+        // vector tiles; with partials_out the caller's grid is the partial count
+        const int64_t ntiles = cdiv(R, 128) * cdiv(C, 128);
+        if (grid <= 0)
+            grid = (int)std::max<int64_t>(1, std::min<int64_t>(ntiles, kCastMaxGrid));
+        if (in_bf16) {
+            if (fmt == kE4M3)
+                cast_tile_t<uint16_t, kE4M3>(x, R, C, src, q, qt, s_out, amax_out, partials_out, grid, stream);
+            else
+                cast_tile_t<uint16_t, kE5M2>(x, R, C, src, q, qt, s_out, amax_out, partials_out, grid, stream);
+        } else {
+            if (fmt == kE4M3)
+                cast_tile_t<float, kE4M3>(x, R, C, src, q, qt, s_out, amax_out, partials_out, grid, stream);
+            else
+                cast_tile_t<float, kE5M2>(x, R, C, src, q, qt, s_out, amax_out, partials_out, grid, stream);
+        }
+        return hipGetLastError();
+    }
     const int64_t ntiles = cdiv(R, 64) * cdiv(C, 64);
     if (grid <= 0)
         grid = (int)std::max<int64_t>(1, std::min<int64_t>(ntiles, kCastMaxGrid));

@@ -86,6 +86,21 @@ def test_colwise_transpose(shape, fmt):
     check_current(W.normal(shape, 1.0, 12, W.F32), fmt, outputs=fq.FQ_COLWISE)
 
 
+@pytest.mark.parametrize("shape", [(16, 16), (128, 128), (144, 272), (256, 384), (1040, 96), (32, 2064)])
+@pytest.mark.parametrize("fmt", [fq.FQ_E4M3, fq.FQ_E5M2])
+def test_colwise_tiles(shape, fmt):
+    """Shapes with R % 16 == 0 and C % 16 == 0 take the vector tile path (edge
+    tiles of 16 rows or columns included)."""
+    x = W.normal(shape, 1.0, 31 + shape[1], W.BF16)
+    check_current(x, fmt, outputs=fq.FQ_ROWWISE | fq.FQ_COLWISE)
+    check_current(W.normal(shape, 2.0, 32, W.F32), fmt, outputs=fq.FQ_COLWISE)
+
+
+def test_full_size_current_both_planes():
+    w = W.BY_NAME["current_e4m3_act_8192x4096"]
+    check_current(w.make(), fq.FQ_E4M3, outputs=fq.FQ_ROWWISE | fq.FQ_COLWISE)
+
+
 def all_finite_bf16():
     b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     f = (b.astype(np.uint32) << 16).view(np.float32)
@@ -203,6 +218,13 @@ def test_delayed_small_ring(fmt):
     xs = [(rng.standard_normal((37, 61)) * 10.0 ** rng.uniform(-3, 3)).astype(np.float32) for _ in range(11)]
     delayed_steps(xs, fmt, 4)
     delayed_steps([W.to_bf16_bits(x) for x in xs], fmt, 3, outputs=fq.FQ_ROWWISE | fq.FQ_COLWISE)
+
+
+def test_delayed_colwise_tiles():
+    rng = np.random.default_rng(5)
+    xs = [(rng.standard_normal((160, 272)) * 10.0 ** rng.uniform(-2, 2)).astype(np.float32) for _ in range(6)]
+    delayed_steps([W.to_bf16_bits(x) for x in xs], fq.FQ_E4M3, 3, outputs=fq.FQ_ROWWISE | fq.FQ_COLWISE)
+    delayed_steps(xs, fq.FQ_E5M2, 4, outputs=fq.FQ_COLWISE)
 
 
 def test_delayed_window_wrap_1024():
