@@ -391,6 +391,52 @@ __global__ __launch_bounds__(kWG) void k_mx_bf16(const uint16_t* __restrict__ x,
     }
 }
 
+// ---------------------------------------------------------------- rowwise only, flat
+// MX rowwise copy alone from bf16: the tensor is streamed as a flat array
+// (C % 32 == 0, so a 1x32 block is 32 consecutive elements: a quad of
+// lanes), each wave reading 1 KiB per load instruction with four loads in
+// flight per lane; the same packed-bf16 amax, clamp and scaled converter as
+// k_mx_bf16. Block codes are byte stores (ordinary: a wave's 16 codes meet in L2).
+template <int FMT>
+__global__ __launch_bounds__(kWG) void k_mx_row_bf16(const uint16_t* __restrict__ x, int64_t n,
+                                                     uint8_t* __restrict__ q, uint8_t* __restrict__ e)
+{
+    constexpr int kL = 4;
+    const int lane = threadIdx.x & 63;
+    const int64_t nunits = cdiv(n, 512);
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6), nwaves = (int64_t)gridDim.x * 4;
+    for (int64_t u0 = wave * kL; u0 < nunits; u0 += nwaves * kL) {
+        u32x4 v[kL];
+#pragma unroll
+        for (int j = 0; j < kL; ++j) {
+            const int64_t el = (u0 + j) * 512 + lane * 8;
+            v[j] = (u0 + j < nunits && el < n) ? ld16_stream(x + el) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int j = 0; j < kL; ++j) {
+            if (u0 + j >= nunits)
+                break;
+            const int64_t el = (u0 + j) * 512 + lane * 8;
+            uint32_t m = pk_max16(pk_max16(v[j][0] & 0x7fff7fffu, v[j][1] & 0x7fff7fffu),
+                                  pk_max16(v[j][2] & 0x7fff7fffu, v[j][3] & 0x7fff7fffu));
+            m = max(m & 0xFFFFu, m >> 16);
+            m = max(m, dppu<kDppXor1>(m));
+            m = max(m, dppu<kDppXor2>(m));  // the 1x32 block: a quad of lanes
+            const uint32_t code = mx_code_bf16<FMT>(m);
+            const uint32_t lim = mx_limit_bf16<FMT>(code), lim2 = lim | (lim << 16);
+            const float scale = e8m0_value(code);
+            u32x2 w;
+            w[0] = cvt4_scaled<FMT>(clamp_pair(v[j][0], lim2), clamp_pair(v[j][1], lim2), scale);
+            w[1] = cvt4_scaled<FMT>(clamp_pair(v[j][2], lim2), clamp_pair(v[j][3], lim2), scale);
+            if (el < n) {
+                st8_stream(q + el, w);
+                if ((lane & 3) == 0)
+                    e[el / 32] = (uint8_t)code;
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------- MXFP4 from bf16
 // MXFP4 (E2M1 elements, two per byte) with the same tile walk as k_mx_bf16:
 // both planes from one read. Magnitudes are clamped as bf16 patterns to
@@ -640,6 +686,12 @@ void launch_mx_t(const void* x, int in_bf16, int64_t R, int64_t C, uint8_t* q, u
                  uint8_t* et, hipStream_t stream)
 {
     const int64_t ntiles = cdiv(C, 128) * cdiv(R, 128);
+    if (in_bf16 && !qt) {
+        const int64_t n = R * C;
+        const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(n, (int64_t)kWG * 8 * 4), 16384));
+        k_mx_row_bf16<FMT><<<grid, kWG, 0, stream>>>((const uint16_t*)x, n, q, e);
+        return;
+    }
     if (in_bf16) {
         const size_t lds = qt ? 128 * tile_pitch<uint16_t>() * 2 : 0;
         static ResidentGrid cache;

@@ -142,7 +142,9 @@ def test_mx_wide_range():
 
 @pytest.mark.parametrize("w", [w for w in W.LARGE if w.recipe == "mx"], ids=lambda w: w.name)
 def test_full_size_mx(w):
-    check_mx(w.make(), BOTH)
+    x = w.make()
+    check_mx(x, BOTH)
+    check_mx(x, fq.FQ_ROWWISE)
 
 
 # ---------------------------------------------------------------- NVFP4
