@@ -299,7 +299,7 @@ fq_status fq_amax(const fq_desc* d, const void* x, float* amax_out, void* ws, si
         if (d->transform != FQ_TRANSFORM_NONE)
             return FQ_E_INVALID;
         g = amax_grid(n, elem_bytes(d), kMaxPartials);
-        s = hip_status(launch_amax_partial(x, d->in_dtype == FQ_IN_BF16, n, partials, g, st));
+        s = hip_status(launch_amax_partial(x, d->in_dtype == FQ_IN_BF16, n, partials, g, st, 8));
     }
     if (s != FQ_OK)
         return s;
@@ -330,7 +330,7 @@ fq_status fq_quantize(const fq_desc* d, const void* x, const fq_quantized* o, vo
     case FQ_PER_TENSOR_CURRENT: {
         float* partials = (float*)ws;
         const int g = amax_grid(n, elem_bytes(d), kMaxPartials);
-        if ((s = hip_status(launch_amax_partial(x, bf, n, partials, g, st))) != FQ_OK)
+        if ((s = hip_status(launch_amax_partial(x, bf, n, partials, g, st, 8))) != FQ_OK)
             return s;
         ScaleSrc src;
         src.partials = partials;

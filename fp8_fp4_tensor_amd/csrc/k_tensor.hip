@@ -29,7 +29,7 @@ namespace {
 constexpr int kLoads = 4;
 constexpr int kCastMaxGrid = 16384;
 
-template <typename T>
+template <typename T, int L>
 __global__ __launch_bounds__(kWG) void k_amax_partial(const T* __restrict__ x, int64_t n,
                                                       float* __restrict__ partials)
 {
@@ -40,13 +40,13 @@ __global__ __launch_bounds__(kWG) void k_amax_partial(const T* __restrict__ x, i
     const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int64_t nwaves = (int64_t)gridDim.x * 4;
     float m = 0.0f;
-    for (int64_t u0 = wave * kLoads; u0 < nunits; u0 += nwaves * kLoads) {
-        u32x4 v[kLoads];
+    for (int64_t u0 = wave * L; u0 < nunits; u0 += nwaves * L) {
+        u32x4 v[L];
 #pragma unroll
-        for (int j = 0; j < kLoads; ++j)
+        for (int j = 0; j < L; ++j)
             v[j] = (u0 + j < nunits) ? ld16(x + (u0 + j) * U + lane * E) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int j = 0; j < kLoads; ++j)
+        for (int j = 0; j < L; ++j)
             m = fmaxf(m, In<T>::absmax16(v[j]));
     }
     for (int64_t i = nunits * U + (int64_t)blockIdx.x * kWG + threadIdx.x; i < n; i += (int64_t)gridDim.x * kWG)
@@ -79,7 +79,7 @@ __device__ __forceinline__ void resolve_scale(const ScaleSrc& src, float* lds, f
 
 // q = Q(fp32(alpha * x)) over a flat tensor; optionally one amax partial per
 // workgroup (delayed scaling casts and records the amax in the same read).
-template <typename T, int FMT>
+template <typename T, int FMT, int L>
 __global__ __launch_bounds__(kWG) void k_cast_tensor(const T* __restrict__ x, int64_t n, ScaleSrc src,
                                                      uint8_t* __restrict__ q, float* s_out, float* amax_out,
                                                      float* partials_out)
@@ -92,10 +92,10 @@ __global__ __launch_bounds__(kWG) void k_cast_tensor(const T* __restrict__ x, in
     const int64_t nwaves = (int64_t)gridDim.x * 4;
     // the first step's loads go out before the scale is resolved, so the
     // partials' round trip overlaps them
-    u32x4 v[kLoads];
-    int64_t u0 = wave * kLoads;
+    u32x4 v[L];
+    int64_t u0 = wave * L;
 #pragma unroll
-    for (int j = 0; j < kLoads; ++j)
+    for (int j = 0; j < L; ++j)
         v[j] = (u0 + j < nunits) ? ld16_stream(x + (u0 + j) * U + lane * E) : u32x4{0u, 0u, 0u, 0u};
     float alpha, s, a;
     resolve_scale<FMT>(src, lds, alpha, s, a);
@@ -107,14 +107,14 @@ __global__ __launch_bounds__(kWG) void k_cast_tensor(const T* __restrict__ x, in
     }
     const bool want_amax = partials_out != nullptr;
     float m = 0.0f;
-    for (; u0 < nunits; u0 += nwaves * kLoads) {
-        if (u0 != wave * kLoads) {
+    for (; u0 < nunits; u0 += nwaves * L) {
+        if (u0 != wave * L) {
 #pragma unroll
-            for (int j = 0; j < kLoads; ++j)
+            for (int j = 0; j < L; ++j)
                 v[j] = (u0 + j < nunits) ? ld16_stream(x + (u0 + j) * U + lane * E) : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
-        for (int j = 0; j < kLoads; ++j) {
+        for (int j = 0; j < L; ++j) {
             if (u0 + j < nunits) {
                 float f[E];
                 In<T>::unpack(v[j], f);
@@ -348,12 +348,17 @@ int amax_grid(int64_t n, int elem_bytes, int max_grid)
     return (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(n, per), max_grid));
 }
 
-hipError_t launch_amax_partial(const void* x, int in_bf16, int64_t n, float* partials, int grid, hipStream_t stream)
+hipError_t launch_amax_partial(const void* x, int in_bf16, int64_t n, float* partials, int grid, hipStream_t stream,
+                               int depth)
 {
-    if (in_bf16)
-        k_amax_partial<uint16_t><<<grid, kWG, 0, stream>>>((const uint16_t*)x, n, partials);
+    if (in_bf16 && depth == 8)
+        k_amax_partial<uint16_t, 8><<<grid, kWG, 0, stream>>>((const uint16_t*)x, n, partials);
+    else if (in_bf16)
+        k_amax_partial<uint16_t, kLoads><<<grid, kWG, 0, stream>>>((const uint16_t*)x, n, partials);
+    else if (depth == 8)
+        k_amax_partial<float, 8><<<grid, kWG, 0, stream>>>((const float*)x, n, partials);
     else
-        k_amax_partial<float><<<grid, kWG, 0, stream>>>((const float*)x, n, partials);
+        k_amax_partial<float, kLoads><<<grid, kWG, 0, stream>>>((const float*)x, n, partials);
     return hipGetLastError();
 }
 
@@ -367,14 +372,22 @@ template <typename T, int FMT>
 static void cast_tensor_t(const void* x, int64_t n, ScaleSrc src, uint8_t* q, float* s_out, float* amax_out,
                           float* partials_out, int grid, hipStream_t stream)
 {
-    k_cast_tensor<T, FMT><<<grid, kWG, 0, stream>>>((const T*)x, n, src, q, s_out, amax_out, partials_out);
+    // eight loads per lane in flight for the current-scaling cast (measured
+    // faster inside a full step), four when the cast also writes amax partials
+    if (partials_out)
+        k_cast_tensor<T, FMT, kLoads><<<grid, kWG, 0, stream>>>((const T*)x, n, src, q, s_out, amax_out,
+                                                                 partials_out);
+    else
+        k_cast_tensor<T, FMT, 8><<<grid, kWG, 0, stream>>>((const T*)x, n, src, q, s_out, amax_out, partials_out);
 }
 
 hipError_t launch_cast_tensor(const void* x, int in_bf16, int fmt, int64_t n, ScaleSrc src, uint8_t* q,
                               float* s_out, float* amax_out, float* partials_out, int grid, hipStream_t stream)
 {
     if (grid <= 0) {
-        const int64_t per = in_bf16 ? elems_per_wg_step<uint16_t>() : elems_per_wg_step<float>();
+        // the depth-8 cast (no partials): a workgroup step covers 8 loads per lane
+        const int64_t per = (in_bf16 ? elems_per_wg_step<uint16_t>() : elems_per_wg_step<float>()) *
+                            (partials_out ? 1 : 8 / kLoads);
         grid = (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(n, per), kCastMaxGrid));
     }
     if (in_bf16) {

@@ -60,7 +60,7 @@ int amax_grid(int64_t n, int elem_bytes, int max_grid);
 
 // partials[g] = max|x| over workgroup g's share; grid from amax_grid().
 hipError_t launch_amax_partial(const void* x, int in_bf16, int64_t n, float* partials, int grid,
-                               hipStream_t stream);
+                               hipStream_t stream, int depth = 4);  // depth: 16-byte loads per lane, 4 or 8
 // out[0] = max(partials[0..n)).
 hipError_t launch_amax_finish(const float* partials, int n, float* out, hipStream_t stream);
 
