@@ -468,19 +468,27 @@ __global__ __launch_bounds__(kWG) void k_mxfp4_bf16(const uint16_t* __restrict__
     const int64_t ntc = cdiv(C, 128), ntiles = ntc * cdiv(R, 128);
     const int cc = (threadIdx.x & 15) * 8, rr0 = threadIdx.x >> 4;
     const int64_t nbc = C / 32, nbr = R / 32;
+    // Tile t's loads are issued one iteration early, as soon as the previous
+    // tile's registers are free, so they fly while that tile's colwise half
+    // runs (measured 57.5 -> 54 us at 8192x8192, although the extra live
+    // registers cost one resident workgroup per CU).
+    u32x4 v[ROUNDS];
+    auto load_tile = [&](int64_t t) {
+        const int64_t r0 = (t / ntc) * 128, c0 = (t % ntc) * 128;
+        const bool col_in = c0 + cc < C;
+        const uint16_t* src = x + (r0 + rr0) * C + c0 + cc;
+        const int64_t step = 16 * C;
+#pragma unroll
+        for (int k = 0; k < ROUNDS; ++k) {
+            v[k] = (col_in && r0 + rr0 + 16 * k < R) ? ld16_stream(src) : u32x4{0u, 0u, 0u, 0u};
+            src += step;
+        }
+    };
+    if ((int64_t)blockIdx.x < ntiles)
+        load_tile(blockIdx.x);
     for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
         const int64_t r0 = (t / ntc) * 128, c0 = (t % ntc) * 128;
         const bool col_in = c0 + cc < C;
-        u32x4 v[ROUNDS];
-        {
-            const uint16_t* src = x + (r0 + rr0) * C + c0 + cc;
-            const int64_t step = 16 * C;
-#pragma unroll
-            for (int k = 0; k < ROUNDS; ++k) {
-                v[k] = (col_in && r0 + rr0 + 16 * k < R) ? ld16_stream(src) : u32x4{0u, 0u, 0u, 0u};
-                src += step;
-            }
-        }
         const bool full_row_codes = c0 + 128 <= C && (nbc & 3) == 0;
         if (qt)
             __syncthreads();  // the previous tile's LDS reads are done
@@ -520,6 +528,8 @@ __global__ __launch_bounds__(kWG) void k_mxfp4_bf16(const uint16_t* __restrict__
                 }
             }
         }
+        if (t + gridDim.x < ntiles)
+            load_tile(t + gridDim.x);
         if (!qt)
             continue;
         __syncthreads();
@@ -610,6 +620,26 @@ __global__ __launch_bounds__(kWG) void k_mx_requant(const uint8_t* __restrict__ 
     __shared__ __align__(16) uint8_t ocode[128 * 4];
     const int64_t ntc = cdiv(C, 128), ntiles = ntc * cdiv(R, 128);
     const int64_t nbc = C / 32, nbr = R / 32;
+    // a tile's codes and E8M0 codes are loaded into registers one iteration
+    // early, so they fly while the previous tile is requantized
+    u32x4 v[4];
+    uint32_t ew = 0;
+    auto load_tile = [&](int64_t t) {
+        const int64_t r0 = (t / ntc) * 128, c0 = (t % ntc) * 128;
+        const int64_t nrows_in = min((int64_t)128, R - r0), ncols_in = min((int64_t)128, C - c0);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int i = k * kWG + threadIdx.x, row = i >> 3, seg = (i & 7) * 16;
+            v[k] = (row < nrows_in && seg < ncols_in) ? ld16_stream(q + (r0 + row) * C + c0 + seg)
+                                                      : u32x4{0u, 0u, 0u, 0u};
+        }
+        ew = 0;
+        if (threadIdx.x < nrows_in)
+            for (int j = 0; j < ncols_in / 32; ++j)
+                ew |= (uint32_t)e[(r0 + threadIdx.x) * nbc + c0 / 32 + j] << (8 * j);
+    };
+    if ((int64_t)blockIdx.x < ntiles)
+        load_tile(blockIdx.x);
     for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
         const int64_t r0 = (t / ntc) * 128, c0 = (t % ntc) * 128;
         const int64_t nrows_in = min((int64_t)128, R - r0), ncols_in = min((int64_t)128, C - c0);
@@ -617,20 +647,13 @@ __global__ __launch_bounds__(kWG) void k_mx_requant(const uint8_t* __restrict__ 
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int i = k * kWG + threadIdx.x, row = i >> 3, seg = (i & 7) * 16;
-            u32x4 v = u32x4{0u, 0u, 0u, 0u};
-            if (row < nrows_in && seg < ncols_in)
-                v = ld16_stream(q + (r0 + row) * C + c0 + seg);
-            *reinterpret_cast<u32x4*>(qtile + row * QP + seg) = v;
+            *reinterpret_cast<u32x4*>(qtile + row * QP + seg) = v[k];
         }
-        if (threadIdx.x < 128) {
-            const int row = threadIdx.x;
-            uint32_t w = 0;
-            if (row < nrows_in)
-                for (int j = 0; j < ncols_in / 32; ++j)
-                    w |= (uint32_t)e[(r0 + row) * nbc + c0 / 32 + j] << (8 * j);
-            *reinterpret_cast<uint32_t*>(etile + row * 4) = w;
-        }
+        if (threadIdx.x < 128)
+            *reinterpret_cast<uint32_t*>(etile + threadIdx.x * 4) = ew;
         __syncthreads();
+        if (t + gridDim.x < ntiles)
+            load_tile(t + gridDim.x);
         const int pc = threadIdx.x & 63, rb = threadIdx.x >> 6;
         const int cb = (2 * pc) >> 5;  // the 32-column block of both columns
         float f0[32], f1[32];
