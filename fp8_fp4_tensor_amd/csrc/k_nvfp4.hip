@@ -47,9 +47,35 @@ namespace {
 
 constexpr int kLoads = 4;
 constexpr int kMaxGrid = 16384;
+// Rowwise 1x16 pass 2: fewer, longer-lived workgroups, so the per-workgroup
+// set-up (tensor scale from the partials, the multiplier table) is paid less
+// often: at 8192x14336 both passes take 82 us with 4096 workgroups,
+// 89 us with 14336 (one per four 1 KiB units per wave), 85 us with 2048.
+// The same cap serves the stochastic-rounding kernel (101 us against
+// 110 us with 16384 workgroups of 256 blocks).
+constexpr int kMaxGrid1x16 = 4096;
 
-// Tensor-level scale from the amax source (uniform control flow).
-__device__ __forceinline__ void nvfp4_tensor(const ScaleSrc& src, float* lds, float& alpha_s, float& S, float& A)
+// fp32(a / 6) for a >= 0, correctly rounded: q = a * RN(1/6), the residual
+// a - 6q (exact), one correction step. An exhaustive check over every fp32
+// a >= 2^-125 finds it equal to the division; below that (quotients in the
+// subnormal range, where the residual is no longer exact) the division runs.
+__device__ __forceinline__ float div6(float a)
+{
+    if (__builtin_expect(a >= 0x1p-125f, 1)) {
+        constexpr float zh = 0x1.555556p-3f;  // RN(1/6)
+        const float q = a * zh;
+        return __builtin_fmaf(__builtin_fmaf(-q, 6.0f, a), zh, q);
+    }
+    return a / 6.0f;
+}
+
+// Tensor-level scale from the amax source, and the table of element
+// multipliers r(c) = 1 / (dec(c) * S) for every block scale code c (a code
+// is at most 0x7E: b * alpha_s is clamped to [0, 448]), so a block's
+// multiplier is a lookup instead of a division. Uniform control flow; ends
+// with a workgroup barrier.
+__device__ __forceinline__ void nvfp4_tensor(const ScaleSrc& src, float* lds, float* rtab, float& alpha_s, float& S,
+                                             float& A)
 {
     if (src.amax_in) {
         A = *src.amax_in;
@@ -60,15 +86,20 @@ __device__ __forceinline__ void nvfp4_tensor(const ScaleSrc& src, float* lds, fl
         A = max_workgroup(m, lds);
     }
     tensor_scales(A / 6.0f, 448.0f, alpha_s, S);
+    if (threadIdx.x < 128) {
+        const float d = dec_e4m3(threadIdx.x) * S;
+        rtab[threadIdx.x] = (d == 0.0f) ? 0.0f : fminf(1.0f / d, kFLT_MAX);
+    }
+    __syncthreads();
 }
 
-// Block scale code and element multiplier from a block amax.
-__device__ __forceinline__ void nvfp4_block(float a, float alpha_s, float S, uint32_t& code, float& r)
+// Block scale code and element multiplier from a block amax:
+// b = a/6, c = Q_E4M3(b * alpha_s), r = 1 / (dec(c) * S) (0 when that is 0).
+__device__ __forceinline__ void nvfp4_block(float a, float alpha_s, const float* rtab, uint32_t& code, float& r)
 {
-    const float b = a / 6.0f;
+    const float b = div6(a);
     code = enc_e4m3_one(clampf(b * alpha_s, 448.0f));
-    const float d = dec_e4m3(code) * S;
-    r = (d == 0.0f) ? 0.0f : fminf(1.0f / d, kFLT_MAX);
+    r = rtab[code];
 }
 
 // E values times r -> E/2 packed bytes (E = 8: a dword; E = 4: 16 bits).
@@ -233,6 +264,7 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_1x16_sr(const T* __restrict__ x, 
                                                        uint8_t* __restrict__ codes, float* S_out, float* amax_out)
 {
     __shared__ float lds[4];
+    __shared__ float rtab[128];
     constexpr int E = In<T>::kE, NL = 16 / E;
     const int64_t first = (int64_t)blockIdx.x * kWG + threadIdx.x, stride = (int64_t)gridDim.x * kWG;
     u32x4 v[NL];
@@ -240,7 +272,7 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_1x16_sr(const T* __restrict__ x, 
     for (int k = 0; k < NL; ++k)
         v[k] = first < nblk ? ld16_stream(x + first * 16 + k * E) : u32x4{0u, 0u, 0u, 0u};
     float alpha_s, S, A;
-    nvfp4_tensor(src, lds, alpha_s, S, A);
+    nvfp4_tensor(src, lds, rtab, alpha_s, S, A);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         if (S_out)
             *S_out = S;
@@ -258,7 +290,7 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_1x16_sr(const T* __restrict__ x, 
             v[k] = nb < nblk ? ld16_stream(x + nb * 16 + k * E) : u32x4{0u, 0u, 0u, 0u};
         uint32_t code;
         float r;
-        nvfp4_block(absmax<16>(f), alpha_s, S, code, r);
+        nvfp4_block(absmax<16>(f), alpha_s, rtab, code, r);
         const uint64_t s = 2 * offset;  // plane 0
         u32x2 out;
         out[0] = enc8_e2m1_sr(f, r, sr_group(2 * (uint64_t)b, s, seed));
@@ -274,6 +306,7 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_1x16(const T* __restrict__ x, int
                                                     float* S_out, float* amax_out)
 {
     __shared__ float lds[4];
+    __shared__ float rtab[128];
     constexpr int E = In<T>::kE, U = 64 * E, LPB = 16 / E;
     const int lane = threadIdx.x & 63;
     const int64_t nunits = cdiv(n, U);
@@ -288,7 +321,7 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_1x16(const T* __restrict__ x, int
         v[j] = (u0 + j < nunits && e < n) ? ld16_stream(x + e) : u32x4{0u, 0u, 0u, 0u};
     }
     float alpha_s, S, A;
-    nvfp4_tensor(src, lds, alpha_s, S, A);
+    nvfp4_tensor(src, lds, rtab, alpha_s, S, A);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         if (S_out)
             *S_out = S;
@@ -313,7 +346,7 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_1x16(const T* __restrict__ x, int
             const float a = max_lanes<LPB>(absmax<E>(f));
             uint32_t code;
             float r;
-            nvfp4_block(a, alpha_s, S, code, r);
+            nvfp4_block(a, alpha_s, rtab, code, r);
             if (e < n) {
                 Fp4Store<E>::store(p + e / 2, f, r);
                 if ((lane & (LPB - 1)) == 0)
@@ -329,6 +362,7 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_16x16(const T* __restrict__ x, in
                                                      float* S_out, float* amax_out)
 {
     __shared__ float lds[4];
+    __shared__ float rtab[128];
     constexpr int E = In<T>::kE, LPB = 16 / E, WC = kWG * E;  // columns per workgroup
     const int64_t nwc = cdiv(C, WC);
     const int64_t r0 = (int64_t)(blockIdx.x / nwc) * 16;
@@ -339,7 +373,7 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_16x16(const T* __restrict__ x, in
     for (int i = 0; i < 16; ++i)
         v[i] = in ? ld16_stream(x + (r0 + i) * C + c) : u32x4{0u, 0u, 0u, 0u};
     float alpha_s, S, A;
-    nvfp4_tensor(src, lds, alpha_s, S, A);
+    nvfp4_tensor(src, lds, rtab, alpha_s, S, A);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         if (S_out)
             *S_out = S;
@@ -356,7 +390,7 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_16x16(const T* __restrict__ x, in
     const float a = max_lanes<LPB>(m);
     uint32_t code;
     float r;
-    nvfp4_block(a, alpha_s, S, code, r);
+    nvfp4_block(a, alpha_s, rtab, code, r);
     if (!in)
         return;
 #pragma unroll
@@ -388,6 +422,7 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_colt(const T* __restrict__ x, int
 {
     constexpr int TC = 64, E = In<T>::kE, CPR = TC / E, SW = 16 / E;  // 16-byte chunks per row; swizzle step
     __shared__ float lds[4];
+    __shared__ float rtab[128];
     __shared__ __align__(16) T tile[128][TC];
     const int64_t ntc = C / TC + (C % TC != 0);
     const int64_t r0 = (int64_t)(blockIdx.x / ntc) * 128, c0 = (int64_t)(blockIdx.x % ntc) * TC;
@@ -401,7 +436,7 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_colt(const T* __restrict__ x, int
         *reinterpret_cast<u32x4*>(&tile[r][(j ^ (SW * ((r >> 4) & 3))) * E]) = v;
     }
     float alpha_s, S, A;
-    nvfp4_tensor(src, lds, alpha_s, S, A);  // includes a workgroup barrier
+    nvfp4_tensor(src, lds, rtab, alpha_s, S, A);  // includes a workgroup barrier
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         if (S_out)
             *S_out = S;
@@ -426,7 +461,7 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_colt(const T* __restrict__ x, int
             rht16(f, signs);
         uint32_t code;
         float rr;
-        nvfp4_block(absmax<16>(f), alpha_s, S, code, rr);
+        nvfp4_block(absmax<16>(f), alpha_s, rtab, code, rr);
         codes[half] = code;
         if constexpr (SR) {
             const uint64_t e0 = (uint64_t)((c0 + c) * R + r0 + rb), s = 2 * offset + 1;
@@ -483,10 +518,11 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_col(const T* __restrict__ x, int6
                                                    float* S_out, float* amax_out)
 {
     __shared__ float lds[4];
+    __shared__ float rtab[128];
     constexpr int TC = 256, E = In<T>::kE, LPR = TC / E, RPR = kWG / LPR;
     __shared__ __align__(16) T tile[32][TC];
     float alpha_s, S, A;
-    nvfp4_tensor(src, lds, alpha_s, S, A);
+    nvfp4_tensor(src, lds, rtab, alpha_s, S, A);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         if (S_out)
             *S_out = S;
@@ -518,7 +554,7 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_col(const T* __restrict__ x, int6
             a = max_lanes<16>(a);
         uint32_t code;
         float r;
-        nvfp4_block(a, alpha_s, S, code, r);
+        nvfp4_block(a, alpha_s, rtab, code, r);
         w[2 * b] = enc8_e2m1(f, r);
         w[2 * b + 1] = enc8_e2m1(f + 8, r);
         if (in && b < nb) {
@@ -557,14 +593,14 @@ void launch_t(const void* xv, int64_t R, int64_t C, int br, ScaleSrc src, uint8_
     if (p) {
         if (sr.on) {
             const int64_t nblk = R * C / 16;
-            const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(nblk, kWG), kMaxGrid));
+            const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(nblk, kWG), kMaxGrid1x16));
             k_nvfp4_1x16_sr<T><<<grid, kWG, 0, stream>>>(x, nblk, src, sr.seed, sr.offset, p, codes, S_out,
                                                          amax_out);
             wrote_scalars = true;
         } else if (br == 1) {
             const int64_t n = R * C;
             const int64_t per_wg = (int64_t)kWG * E * kLoads;
-            const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(n, per_wg), kMaxGrid));
+            const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(n, per_wg), kMaxGrid1x16));
             k_nvfp4_1x16<T><<<grid, kWG, 0, stream>>>(x, n, src, p, codes, S_out, amax_out);
             wrote_scalars = true;
         } else if (R > 0 && C > 0) {

@@ -10,6 +10,13 @@
       (256 MiB read and 256 MiB written), so the result is in true bytes.
       The file records a hash of the kernel's sources; bench.py reports the
       traffic only while the sources are unchanged.
+
+  python -m fp8_fp4_tensor_amd.profsum insts OUT.md "COMMAND" WORKLOAD=CSV ...
+      instruction counts per element from --pmc runs of bench.py --only
+      WORKLOAD (SQ_INSTS_VALU, SQ_INSTS_SALU, SQ_INSTS_LDS, SQ_INSTS_VMEM_RD,
+      SQ_INSTS_VMEM_WR, SQ_WAVES; wave-level counts summed over the chip).
+      A wave instruction does the work of 64 lanes, so VALU x 64 / elements
+      is the vector lane-operations per element.
 """
 import collections
 import csv
@@ -109,10 +116,60 @@ def traffic(fetch_csv, write_csv, kernel, workload, shape, out_json, commands):
     print(json.dumps(out, indent=1))
 
 
+INST_COUNTERS = ["SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_INSTS_VMEM_RD", "SQ_INSTS_VMEM_WR",
+                 "SQ_WAVES"]
+
+
+def _per_kernel_counters(rows):
+    """{short kernel name: {counter: mean per dispatch}} (instances summed per dispatch)."""
+    acc = collections.defaultdict(lambda: collections.defaultdict(float))
+    names = {}
+    for r in rows:
+        acc[(r["Dispatch_Id"])][r["Counter_Name"]] += float(r["Counter_Value"])
+        names[r["Dispatch_Id"]] = short_name(r["Kernel_Name"])
+    out = collections.defaultdict(lambda: collections.defaultdict(list))
+    for d, cs in acc.items():
+        for c, v in cs.items():
+            out[names[d]][c].append(v)
+    return {k: {c: sum(v) / len(v) for c, v in cs.items()} | {"dispatches": len(next(iter(cs.values())))}
+            for k, cs in out.items()}
+
+
+def insts(out_md, command, *pairs):
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    from fp8_fp4_tensor_amd import workloads as W
+    lines = ["# Instructions per element (rocprofv3 --pmc, SQ counters)", "",
+             f"Command (per workload): `{command}`", "",
+             "Wave-level instruction counts summed over the chip, per dispatch; a VALU",
+             "instruction covers 64 lanes, so VALU x 64 / elements = vector lane-operations",
+             "per element of the input tensor. (256 CUs x 64 lanes x 2.4 GHz = 39.3 T",
+             "lane-ops/s; at 6.4 TB/s and 3 bytes per element the budget is ~18.)", "",
+             "| workload | kernel | dispatches | VALU lane-ops / elem | SALU / 1K elem | LDS / 1K elem "
+             "| VMEM rd / 1K elem | VMEM wr / 1K elem | waves |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for pair in pairs:
+        wname, csv_path = pair.split("=", 1)
+        w = W.BY_NAME[wname]
+        n = w.shape[0] * w.shape[1]
+        for k, cs in sorted(_per_kernel_counters(_rows(csv_path)).items()):
+            if not k.startswith("k_"):
+                continue
+            g = cs.get
+            lines.append(f"| {wname} | `{k}` | {cs['dispatches']} | {g('SQ_INSTS_VALU', 0) * 64 / n:.2f} | "
+                         f"{g('SQ_INSTS_SALU', 0) * 1e3 / n:.2f} | {g('SQ_INSTS_LDS', 0) * 1e3 / n:.2f} | "
+                         f"{g('SQ_INSTS_VMEM_RD', 0) * 1e3 / n:.2f} | {g('SQ_INSTS_VMEM_WR', 0) * 1e3 / n:.2f} | "
+                         f"{g('SQ_WAVES', 0):.0f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "trace":
         trace(*sys.argv[2:6])
     elif sys.argv[1] == "traffic":
         traffic(*sys.argv[2:9])
+    elif sys.argv[1] == "insts":
+        insts(*sys.argv[2:])
     else:
         raise SystemExit(__doc__)
