@@ -4,8 +4,11 @@ The input is 65664 x 32768 bf16 (2.15e9 elements, 4.3 GB), built on the GPU
 row chunk by row chunk from an integer formula whose values are exact in
 bf16: x[r, c] = (((1103 r + 2221 c) mod 256) - 128) / 64 * 2^((r + c // 128) mod 8).
 The oracle regenerates sampled rows (and columns) exactly in numpy and checks
-them bit for bit, including rows whose elements lie past index 2^31. The
-tensor amax is 256 by construction (k = -128 at scale 2^7 occurs)."""
+them bit for bit, including rows whose elements lie past index 2^31, and
+colwise planes (rows of X^T) past that index: per-tensor, blockwise, MXFP8,
+MXFP4, NVFP4 (with and without the RHT), dequantization and the MX
+requantization. The tensor amax is 256 by construction (k = -128 at scale
+2^7 occurs)."""
 import numpy as np
 import pytest
 import torch
@@ -53,10 +56,16 @@ def big():
 
 
 SAMPLE_ROWS = np.array([0, 65536, R - 2, R - 1])       # rows past element 2^31 = row 65536
+SAMPLE_COLS = np.array([0, 12345, C - 2, C - 1])        # colwise planes: X^T rows past element 2^31
 
 
 def sample(xg_rows):
     return bf16_bits(values(SAMPLE_ROWS[:, None], np.arange(C)[None, :]))
+
+
+def sample_cols():
+    """Columns SAMPLE_COLS of X as rows ([len, R]): the rows of X^T that colwise planes hold."""
+    return bf16_bits(values(np.arange(R)[:, None], SAMPLE_COLS[None, :]).T.copy())
 
 
 def quantize(d, x):
@@ -113,3 +122,88 @@ def test_large_nvfp4(big):
     same_bytes(host(out.row_data[SAMPLE_ROWS]), want["p_row"], "packed FP4")
     same_bytes(host(out.row_scale.view(R, C // 16)[SAMPLE_ROWS]), want["c_row"], "E4M3 block scales")
     del out
+
+
+def test_large_current_colwise_and_dequant(big):
+    d = fq.desc(fq.FQ_PER_TENSOR_CURRENT, fq.FQ_IN_BF16, fq.FQ_E4M3, R, C, (0, 0), fq.FQ_ROWWISE | fq.FQ_COLWISE)
+    out = quantize(d, big)
+    want_c = orc.quantize_with_amax(sample_cols(), orc.E4M3, AMAX, shape=(len(SAMPLE_COLS), R))
+    same_bytes(host(out.col_data[SAMPLE_COLS]), want_c["q_row"], "colwise codes (columns of X)")
+    want_r = orc.quantize_with_amax(sample(None), orc.E4M3, AMAX, shape=(len(SAMPLE_ROWS), C))
+    same_bytes(host(out.row_data[SAMPLE_ROWS]), want_r["q_row"], "rowwise codes")
+    y = torch.empty((R, C), dtype=torch.bfloat16, device="cuda")
+    fq.fq_dequantize(d, out, fq.FQ_ROWWISE, y)
+    torch.cuda.synchronize()
+    same_bytes(host(y[SAMPLE_ROWS].view(torch.int16)).view(np.uint16),
+               orc.f32_to_bf16(orc.dequant_tensor(want_r["q_row"], orc.E4M3, want_r["s"])), "dequantized rows (bf16)")
+    del out, y
+
+
+def test_large_block_1x128_colwise(big):
+    d = fq.desc(fq.FQ_BLOCK_FP32, fq.FQ_IN_BF16, fq.FQ_E4M3, R, C, (1, 128), fq.FQ_COLWISE)
+    out = quantize(d, big)
+    want = orc.quantize_block(sample_cols(), (1, 128))
+    same_bytes(host(out.col_data[SAMPLE_COLS]), want["q_row"], "colwise codes (columns of X)")
+    same_bytes(host(out.col_scale.view(C, R // 128)[SAMPLE_COLS]), want["s_row"], "colwise scales")
+    del out
+
+
+def test_large_nvfp4_colwise(big):
+    d = fq.desc(fq.FQ_NVFP4, fq.FQ_IN_BF16, fq.FQ_E2M1, R, C, (1, 16), fq.FQ_COLWISE)
+    out = quantize(d, big)
+    same_bytes(host(out.amax), f32(AMAX), "tensor amax")
+    want = orc.quantize_nvfp4(sample_cols(), (1, 16), amax=AMAX)
+    same_bytes(host(out.tensor_scale), f32(want["S"]), "tensor scale")
+    same_bytes(host(out.col_data[SAMPLE_COLS]), want["p_row"], "packed FP4 of X^T rows")
+    same_bytes(host(out.col_scale.view(C, R // 16)[SAMPLE_COLS]), want["c_row"], "E4M3 block scales")
+    del out
+
+
+def test_large_nvfp4_colwise_rht_given_amax(big):
+    """The RHT works along X^T rows, so sampled columns of X transform alone;
+    a given amax (as after a cross-device max) replaces the tensor's own."""
+    signs = 0x5AC3
+    d = fq.desc(fq.FQ_NVFP4, fq.FQ_IN_BF16, fq.FQ_E2M1, R, C, (1, 16), fq.FQ_COLWISE,
+                transform=fq.FQ_TRANSFORM_RHT16, rht_signs=signs)
+    out = fq.alloc_quantized(d)
+    amax = torch.tensor([300.0], dtype=torch.float32, device="cuda")
+    fq.fq_quantize_with_amax(d, big, amax, out)
+    torch.cuda.synchronize()
+    cols = np.concatenate([np.arange(4), 12345 + np.arange(4), C - 8 + np.arange(8)])   # 16 columns
+    xs = bf16_bits(values(np.arange(R)[:, None], cols[None, :]))     # [R, 16]: those columns of X
+    want = orc.quantize_nvfp4_rht(xs, signs, amax=300.0)
+    same_bytes(host(out.col_data[cols]), want["p_col"], "packed FP4 of transformed X^T rows")
+    same_bytes(host(out.col_scale.view(C, R // 16)[cols]), want["c_col"], "E4M3 block scales")
+    del out
+
+
+def test_large_mxfp4_both_planes(big):
+    d = fq.desc(fq.FQ_MX, fq.FQ_IN_BF16, fq.FQ_E2M1, R, C, (1, 32), fq.FQ_ROWWISE | fq.FQ_COLWISE)
+    out = quantize(d, big)
+    want = orc.quantize_mx(sample(None), outputs=orc.ROWWISE, fmt=orc.E2M1)
+    same_bytes(host(out.row_data[SAMPLE_ROWS]), want["q_row"], "rowwise packed FP4")
+    same_bytes(host(out.row_scale.view(R, C // 32)[SAMPLE_ROWS]), want["e_row"], "rowwise E8M0")
+    wc = orc.quantize_mx(sample_cols(), outputs=orc.ROWWISE, fmt=orc.E2M1)
+    same_bytes(host(out.col_data[SAMPLE_COLS]), wc["q_row"], "colwise packed FP4 (columns of X)")
+    same_bytes(host(out.col_scale.view(C, R // 32)[SAMPLE_COLS]), wc["e_row"], "colwise E8M0")
+    del out
+
+
+def test_large_mx_requantize(big):
+    d = fq.desc(fq.FQ_MX, fq.FQ_IN_BF16, fq.FQ_E4M3, R, C, (1, 32), fq.FQ_ROWWISE)
+    src = quantize(d, big)
+    dst = fq.alloc_quantized(fq.desc(fq.FQ_MX, fq.FQ_IN_BF16, fq.FQ_E4M3, R, C, (1, 32), fq.FQ_COLWISE))
+    fq.fq_requantize_transpose(d, src, dst)
+    torch.cuda.synchronize()
+    # the requantized columns from the oracle's rowwise codes of those columns' rows: every row
+    # is needed, so rebuild the rowwise codes of the sampled columns' 32-column blocks
+    blocks = np.unique(SAMPLE_COLS // 32)
+    cols = (blocks[:, None] * 32 + np.arange(32)[None, :]).reshape(-1)
+    xs = bf16_bits(values(np.arange(R)[:, None], cols[None, :]))      # [R, 32 * len(blocks)]
+    rw = orc.quantize_mx(xs, outputs=orc.ROWWISE)
+    want = orc.requant_mx_colwise(rw["q_row"], rw["e_row"])
+    pos = np.searchsorted(cols, SAMPLE_COLS)
+    same_bytes(host(dst.col_data[SAMPLE_COLS]), want["q_col"][pos], "requantized colwise codes")
+    same_bytes(host(dst.col_scale.view(C, R // 32)[SAMPLE_COLS]), want["e_col"].reshape(len(cols), R // 32)[pos],
+               "requantized colwise E8M0")
+    del src, dst
