@@ -15,7 +15,9 @@ namespace {
 
 using namespace fq;
 
-constexpr int64_t kMaxElems = int64_t(1) << 40;
+// At most 2^36 elements (128 GiB of bf16): every tiled kernel's grid then
+// stays below 2^32 work-items (the widest, 128x64 tiles, needs 2^31).
+constexpr int64_t kMaxElems = int64_t(1) << 36;
 constexpr int32_t kMaxHistory = 1 << 24;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }

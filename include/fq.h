@@ -156,7 +156,7 @@ typedef enum { FQ_SCALE_DEFAULT = 0, FQ_SCALE_POW2 = 1 } fq_scale_mode;
 /*
  * What to quantize and how.
  *   recipe, in_dtype, format: the enums above.
- *   rows, cols:               tensor shape, each >= 0, rows*cols < 2^40.
+ *   rows, cols:               tensor shape, each >= 0, rows*cols <= 2^36.
  *   block_rows, block_cols:   FQ_BLOCK_FP32 (1,128) or (128,128);
  *                             FQ_MX (1,32); FQ_NVFP4 (1,16) or (16,16);
  *                             ignored by the per-tensor recipes.
@@ -324,7 +324,8 @@ fq_status fq_dequantize(const fq_desc *desc, const fq_quantized *in, int32_t whi
  * The colwise copy from the rowwise copy alone: de-quantize in->rowwise and
  * re-quantize in the other direction into out->colwise ([MP] section "FP8
  * 通信": the expert-parallel backward pass receives only rowwise FP8 data and
- * needs the colwise copy). Recipe FQ_MX only: its power-of-two scales restore
+ * needs the colwise copy). Recipe FQ_MX with E4M3 elements (MXFP8) only,
+ * round to nearest even, no transform: its power-of-two scales restore
  * the values exactly, so the result is the MX recipe applied down the columns
  * of those restored values (32x1 blocks, stored transposed: codes [cols,
  * rows], E8M0 codes [cols, rows/32]). It equals quantizing the original

@@ -86,6 +86,7 @@ def test_sizes_per_recipe():
     (fq.FQ_NVFP4, fq.FQ_E2M1, 16, 24, (1, 16), 1, fq.FQ_E_SHAPE),
     (fq.FQ_NVFP4, fq.FQ_E2M1, 16, 32, (1, 8), 1, fq.FQ_E_UNSUPPORTED),
     (0, 0, 1 << 21, 1 << 20, (0, 0), 1, fq.FQ_E_SHAPE),
+    (0, 0, (1 << 18) + 1, 1 << 18, (0, 0), 1, fq.FQ_E_SHAPE),
 ])
 def test_desc_validation(L, recipe, fmt, R, C, block, outputs, want):
     d = fq.desc(recipe, fq.FQ_IN_BF16, fmt, R, C, block, outputs)
