@@ -22,7 +22,8 @@ def L():
 
 
 def declared_functions():
-    text = open(HEADER, encoding="utf-8").read()
+    with open(HEADER, encoding="utf-8") as f:
+        text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(fq_[a-z_]+)\s*\(", text)))
 
