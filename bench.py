@@ -134,7 +134,22 @@ def cpu_baseline(workloads, row_fraction):
         del x
     return {"value": round(total_bytes / total_t / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"every workload of one step on its first {row_fraction:.0%} of rows "
-                      f"({total_bytes / 1e9:.2f} GB algorithmic, {total_t:.1f} s, one thread)"}
+                      f"({total_bytes / 1e9:.2f} GB algorithmic, {total_t:.1f} s, one thread of "
+                      f"{host_cpu()})"}
+
+
+def host_cpu():
+    """The host CPU's model name and logical CPU count, for the baseline's record."""
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"{model}, {os.cpu_count()} logical CPUs"
 
 
 def plane_bytes(w, which):
