@@ -11,6 +11,10 @@
       The file records a hash of the kernel's sources; bench.py reports the
       traffic only while the sources are unchanged.
 
+  python -m fp8_fp4_tensor_amd.profsum traffic-all FETCH_CSV WRITE_CSV OUT.md "COMMANDS"
+      HBM bytes per dispatch of every kernel in the two --pmc runs, scaled
+      like `traffic`.
+
   python -m fp8_fp4_tensor_amd.profsum insts OUT.md "COMMAND" WORKLOAD=CSV ...
       instruction counts per element from --pmc runs of bench.py --only
       WORKLOAD (SQ_INSTS_VALU, SQ_INSTS_SALU, SQ_INSTS_LDS, SQ_INSTS_VMEM_RD,
@@ -116,6 +120,25 @@ def traffic(fetch_csv, write_csv, kernel, workload, shape, out_json, commands):
     print(json.dumps(out, indent=1))
 
 
+def traffic_all(fetch_csv, write_csv, out_md, commands):
+    fr, wr = _per_kernel_counters(_rows(fetch_csv)), _per_kernel_counters(_rows(write_csv))
+    f_scale = COPY_BYTES / (fr[COPY_KERNEL]["FETCH_SIZE"] * 1024.0)
+    w_scale = COPY_BYTES / (wr[COPY_KERNEL]["WRITE_SIZE"] * 1024.0)
+    lines = ["# HBM traffic per dispatch, every kernel (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)", "",
+             f"Commands: `{commands}`", "",
+             f"Counters scaled by what they read for the plain 256 MiB device copy: FETCH_SIZE x {f_scale:.3f}, "
+             f"WRITE_SIZE x {w_scale:.3f}. A kernel name that serves several workloads shows their mean.", "",
+             "| kernel | dispatches | read MB | written MB |", "|---|---|---|---|"]
+    for k in sorted(set(fr) & set(wr)):
+        if not k.startswith("k_"):
+            continue
+        lines.append(f"| `{k}` | {fr[k]['dispatches']} | {fr[k]['FETCH_SIZE'] * 1024 * f_scale / 1e6:.2f} | "
+                     f"{wr[k]['WRITE_SIZE'] * 1024 * w_scale / 1e6:.2f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 INST_COUNTERS = ["SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_INSTS_VMEM_RD", "SQ_INSTS_VMEM_WR",
                  "SQ_WAVES"]
 
@@ -169,6 +192,8 @@ if __name__ == "__main__":
         trace(*sys.argv[2:6])
     elif sys.argv[1] == "traffic":
         traffic(*sys.argv[2:9])
+    elif sys.argv[1] == "traffic-all":
+        traffic_all(*sys.argv[2:6])
     elif sys.argv[1] == "insts":
         insts(*sys.argv[2:])
     else:
