@@ -54,6 +54,9 @@ constexpr int kMaxGrid = 16384;
 // The same cap serves the stochastic-rounding kernel (101 us against
 // 110 us with 16384 workgroups of 256 blocks).
 constexpr int kMaxGrid1x16 = 4096;
+// Colwise 1x16 (k_nvfp4_colt): workgroups stride over 128 x 64 tiles, the
+// set-up paid once per workgroup.
+constexpr int kMaxGridColt = 2048;
 
 // fp32(a / 6) for a >= 0, correctly rounded: q = a * RN(1/6), the residual
 // a - 6q (exact), one correction step. An exhaustive check over every fp32
@@ -165,27 +168,31 @@ __device__ __forceinline__ Philox4 sr_group(uint64_t h, uint64_t s, uint64_t see
 // kept); with a word whose bits 31..16 are u and 15..0 zero this is exactly
 // "round up iff u + g * 2^16 >= 2^16". Its second value would read bits
 // 30..9 of the same word, so each element gets a call of its own, with 0 as
-// the second value (code 0 for any random word). Only byte 0 of each result
-// is used: the compiler does not carry the other bytes of the destination
-// through, so they are undefined.
-__device__ __forceinline__ uint32_t sr_nibble(float y, uint32_t word_hi16)
+// the second value: bits 3..0 of the result are the element's code and bits
+// 7..4 are 0 (code 0 for any random word). Only byte 0 of a result is
+// defined: the compiler does not carry the other bytes of the destination
+// through this builtin.
+__device__ __forceinline__ uint32_t sr_byte0(float y, uint32_t word_hi16)
 {
     typedef float f32x2 __attribute__((ext_vector_type(2)));
-    return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, f32x2{y, 0.0f}, word_hi16, 1.0f, 0) & 0xFu;
+    return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, f32x2{y, 0.0f}, word_hi16, 1.0f, 0);
 }
 
 // 8 values (times r, stochastically rounded with one group's random bits:
 // element 2k takes bits 15..0 of word k, element 2k+1 bits 31..16) -> one
-// dword of packed E2M1, element j in bits 4j..4j+3
+// dword of packed E2M1, element j in bits 4j..4j+3. Byte 0 of
+// lo | hi << 4 is the pair's byte (the other bytes are undefined); v_perm
+// gathers the four byte 0s.
 __device__ __forceinline__ uint32_t enc8_e2m1_sr(const float* f, float r, const Philox4& ph)
 {
-    uint32_t w = 0;
+    uint32_t t[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        w |= sr_nibble(f[2 * k] * r, ph.w[k] << 16) << (8 * k);
-        w |= sr_nibble(f[2 * k + 1] * r, ph.w[k] & 0xFFFF0000u) << (8 * k + 4);
-    }
-    return w;
+    for (int k = 0; k < 4; ++k)
+        t[k] = sr_byte0(f[2 * k] * r, ph.w[k] << 16) | (sr_byte0(f[2 * k + 1] * r, ph.w[k] & 0xFFFF0000u) << 4);
+    // v_perm_b32(a, b, sel): selector byte i picks byte sel_i of {a:b} (0..3 from b, 4..7 from a), 0x0c gives 0
+    const uint32_t lo = __builtin_amdgcn_perm(t[1], t[0], 0x0c0c0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(t[3], t[2], 0x04000c0cu);
+    return lo | hi;
 }
 
 // ---------------------------------------------------------------- random Hadamard transform
@@ -404,9 +411,9 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_16x16(const T* __restrict__ x, in
         codes[(r0 / 16) * (C / 16) + c / 16] = (uint8_t)code;
 }
 
-// Colwise 1x16 copy (1x16 blocks of X^T = 16 rows of one column of X), one
-// 128-row x 64-column tile per workgroup, so each row of X^T gets 64
-// contiguous bytes per tile. Thread t: column c = t >> 2 of the tile and
+// Colwise 1x16 copy (1x16 blocks of X^T = 16 rows of one column of X) in
+// 128-row x 64-column tiles (workgroups stride over them), so each row of
+// X^T gets 64 contiguous bytes per tile. Thread t: column c = t >> 2 of the tile and
 // q = t & 3, which owns the blocks at rows 16q and 64 + 16q. The tile sits in
 // LDS with its 16-byte chunks XOR-swizzled by the row's 16-row group, so the
 // four rows 16 apart that a wave reads at each step hit distinct banks.
@@ -425,17 +432,7 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_colt(const T* __restrict__ x, int
     __shared__ float lds[4];
     __shared__ float rtab[128];
     __shared__ __align__(16) T tile[128][TC];
-    const int64_t ntc = C / TC + (C % TC != 0);
-    const int64_t r0 = (int64_t)(blockIdx.x / ntc) * 128, c0 = (int64_t)(blockIdx.x % ntc) * TC;
-    const int64_t rows_in = min((int64_t)128, R - r0);
-    // stage the tile: chunk j of row r goes to chunk j ^ (SW * ((r >> 4) & 3))
-    for (int i = threadIdx.x; i < 128 * CPR; i += kWG) {
-        const int r = i / CPR, j = i % CPR;
-        u32x4 v = u32x4{0u, 0u, 0u, 0u};
-        if (r < rows_in && c0 + j * E < C)
-            v = ld16_stream(x + (r0 + r) * C + c0 + j * E);
-        *reinterpret_cast<u32x4*>(&tile[r][(j ^ (SW * ((r >> 4) & 3))) * E]) = v;
-    }
+    const int64_t ntc = C / TC + (C % TC != 0), ntiles = ntc * cdiv(R, 128);
     float alpha_s, S, A;
     nvfp4_tensor(src, lds, rtab, alpha_s, S, A);  // includes a workgroup barrier
     if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -444,68 +441,81 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_colt(const T* __restrict__ x, int
         if (amax_out)
             *amax_out = A;
     }
-    __syncthreads();
     const int c = threadIdx.x >> 2, q = threadIdx.x & 3;
-    const bool in = c0 + c < C;
-    uint32_t wb[2][2];
-    uint32_t codes[2];
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        const int rb = 64 * half + 16 * q;  // first row of this block in the tile
-        float f[16];
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const int r = rb + k;
-            f[k] = In<T>::load1(&tile[r][0], ((c / E) ^ (SW * q)) * E + (c % E));
+    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const int64_t r0 = (t / ntc) * 128, c0 = (t % ntc) * TC;
+        const int64_t rows_in = min((int64_t)128, R - r0);
+        __syncthreads();  // the previous tile's LDS reads are done
+        // stage the tile: chunk j of row r goes to chunk j ^ (SW * ((r >> 4) & 3))
+        for (int i = threadIdx.x; i < 128 * CPR; i += kWG) {
+            const int r = i / CPR, j = i % CPR;
+            u32x4 v = u32x4{0u, 0u, 0u, 0u};
+            if (r < rows_in && c0 + j * E < C)
+                v = ld16_stream(x + (r0 + r) * C + c0 + j * E);
+            *reinterpret_cast<u32x4*>(&tile[r][(j ^ (SW * ((r >> 4) & 3))) * E]) = v;
         }
-        if constexpr (RHT)
-            rht16(f, signs);
-        uint32_t code;
-        float rr;
-        nvfp4_block(absmax<16>(f), alpha_s, rtab, code, rr);
-        codes[half] = code;
-        if constexpr (SR) {
-            const uint64_t e0 = (uint64_t)((c0 + c) * R + r0 + rb), s = 2 * offset + 1;
-            wb[half][0] = enc8_e2m1_sr(f, rr, sr_group(e0 / 8, s, seed));
-            wb[half][1] = enc8_e2m1_sr(f + 8, rr, sr_group(e0 / 8 + 1, s, seed));
-        } else {
-            wb[half][0] = enc8_e2m1(f, rr);
-            wb[half][1] = enc8_e2m1(f + 8, rr);
-        }
-    }
-    uint8_t* rowp = pt + (c0 + c) * (R / 2) + r0 / 2;  // this column's row of X^T, from row r0
-    const bool wide = rows_in == 128 && (R % 32) == 0;  // uniform over the workgroup
-    if (wide) {
-        // even q sends its second block, odd q its first; both then hold two adjacent blocks
-        const bool odd = q & 1;
-        const uint32_t s0 = odd ? wb[0][0] : wb[1][0], s1 = odd ? wb[0][1] : wb[1][1];
-        const uint32_t r0w = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s0, kDppXor1, 0xF, 0xF, false);
-        const uint32_t r1w = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s1, kDppXor1, 0xF, 0xF, false);
-        u32x4 o;
-        if (odd)
-            o = u32x4{r0w, r1w, wb[1][0], wb[1][1]};  // blocks q + 3, q + 4 (= 2h + 4, 2h + 5)
-        else
-            o = u32x4{wb[0][0], wb[0][1], r0w, r1w};  // blocks q, q + 1
-        if (in)
-            st16_stream(rowp + (odd ? 32 + 8 * (q - 1) : 8 * q), o);
-    } else if (in) {
+        __syncthreads();
+        const bool in = c0 + c < C;
+        uint32_t wb[2][2];
+        uint32_t codes[2];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-            const int rb = 64 * half + 16 * q;
-            if (rb < rows_in) {
-                u32x2 v2;
-                v2[0] = wb[half][0];
-                v2[1] = wb[half][1];
-                st8_stream(rowp + rb / 2, v2);
+            const int rb = 64 * half + 16 * q;  // first row of this block in the tile
+            float f[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                const int r = rb + k;
+                f[k] = In<T>::load1(&tile[r][0], ((c / E) ^ (SW * q)) * E + (c % E));
+            }
+            if constexpr (RHT)
+                rht16(f, signs);
+            uint32_t code;
+            float rr;
+            nvfp4_block(absmax<16>(f), alpha_s, rtab, code, rr);
+            codes[half] = code;
+            if constexpr (SR) {
+                const uint64_t e0 = (uint64_t)((c0 + c) * R + r0 + rb), s = 2 * offset + 1;
+                wb[half][0] = enc8_e2m1_sr(f, rr, sr_group(e0 / 8, s, seed));
+                wb[half][1] = enc8_e2m1_sr(f + 8, rr, sr_group(e0 / 8 + 1, s, seed));
+            } else {
+                wb[half][0] = enc8_e2m1(f, rr);
+                wb[half][1] = enc8_e2m1(f + 8, rr);
             }
         }
-    }
-    if (in) {
+        uint8_t* rowp = pt + (c0 + c) * (R / 2) + r0 / 2;  // this column's row of X^T, from row r0
+        const bool wide = rows_in == 128 && (R % 32) == 0;  // uniform over the workgroup
+        if (wide) {
+            // even q sends its second block, odd q its first; both then hold two adjacent blocks
+            const bool odd = q & 1;
+            const uint32_t s0 = odd ? wb[0][0] : wb[1][0], s1 = odd ? wb[0][1] : wb[1][1];
+            const uint32_t r0w = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s0, kDppXor1, 0xF, 0xF, false);
+            const uint32_t r1w = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s1, kDppXor1, 0xF, 0xF, false);
+            u32x4 o;
+            if (odd)
+                o = u32x4{r0w, r1w, wb[1][0], wb[1][1]};  // blocks q + 3, q + 4 (= 2h + 4, 2h + 5)
+            else
+                o = u32x4{wb[0][0], wb[0][1], r0w, r1w};  // blocks q, q + 1
+            if (in)
+                st16_stream(rowp + (odd ? 32 + 8 * (q - 1) : 8 * q), o);
+        } else if (in) {
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int rb = 64 * half + 16 * q;
-            if (rb < rows_in)
-                ct[(c0 + c) * (R / 16) + (r0 + rb) / 16] = (uint8_t)codes[half];
+            for (int half = 0; half < 2; ++half) {
+                const int rb = 64 * half + 16 * q;
+                if (rb < rows_in) {
+                    u32x2 v2;
+                    v2[0] = wb[half][0];
+                    v2[1] = wb[half][1];
+                    st8_stream(rowp + rb / 2, v2);
+                }
+            }
+        }
+        if (in) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int rb = 64 * half + 16 * q;
+                if (rb < rows_in)
+                    ct[(c0 + c) * (R / 16) + (r0 + rb) / 16] = (uint8_t)codes[half];
+            }
         }
     }
 }
@@ -614,7 +624,7 @@ void launch_t(const void* xv, int64_t R, int64_t C, int br, ScaleSrc src, uint8_
         float* s2 = wrote_scalars ? nullptr : S_out;
         float* a2 = wrote_scalars ? nullptr : amax_out;
         if (br == 1) {
-            const unsigned g1 = (unsigned)(cdiv(R, 128) * cdiv(C, 64));
+            const unsigned g1 = (unsigned)std::min<int64_t>(cdiv(R, 128) * cdiv(C, 64), kMaxGridColt);
             const uint64_t sd = sr.seed, of = sr.offset;
             const uint32_t sg = rht.signs;
             if (rht.on && sr.on)
