@@ -93,6 +93,19 @@ __device__ __forceinline__ float max_wave(float v)
     return fmaxf(v, __shfl_xor(v, 32));
 }
 
+// This thread's max over amax partials p[0 .. n-1], n <= 4 * kWG: the four
+// loads are issued together, so one memory latency covers them.
+__device__ __forceinline__ float partials_max(const float* p, int n)
+{
+    float v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int i = (int)threadIdx.x + k * kWG;
+        v[k] = i < n ? p[i] : 0.0f;
+    }
+    return fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+}
+
 // Max over a 256-thread workgroup; every thread receives it. `lds` holds 4
 // floats. Contains __syncthreads(): call from uniform control flow.
 __device__ __forceinline__ float max_workgroup(float v, float* lds)

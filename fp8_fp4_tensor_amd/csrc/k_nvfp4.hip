@@ -83,9 +83,7 @@ __device__ __forceinline__ void nvfp4_tensor(const ScaleSrc& src, float* lds, fl
     if (src.amax_in) {
         A = *src.amax_in;
     } else {
-        float m = 0.0f;
-        for (int i = threadIdx.x; i < src.n_partials; i += kWG)
-            m = fmaxf(m, src.partials[i]);
+        const float m = partials_max(src.partials, src.n_partials);
         A = max_workgroup(m, lds);
     }
     tensor_scales(A / 6.0f, 448.0f, alpha_s, S);

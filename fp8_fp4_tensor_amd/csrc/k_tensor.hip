@@ -69,9 +69,7 @@ __device__ __forceinline__ void resolve_scale(const ScaleSrc& src, float* lds, f
     if (src.amax_in) {
         a = *src.amax_in;
     } else {
-        float m = 0.0f;
-        for (int i = threadIdx.x; i < src.n_partials; i += kWG)
-            m = fmaxf(m, src.partials[i]);
+        const float m = partials_max(src.partials, src.n_partials);
         a = max_workgroup(m, lds);
     }
     tensor_scales(a, Fmt<FMT>::kMax, alpha, s);
@@ -301,9 +299,9 @@ __global__ __launch_bounds__(kFinishThreads) void k_delayed_finish(const float* 
                                                                    float* s, float fmax_v, float* amax_out)
 {
     __shared__ float lds[2][kFinishThreads / 64];
-    float mp = 0.0f, mh = 0.0f;
-    for (int i = threadIdx.x; i < n; i += kFinishThreads)
-        mp = fmaxf(mp, partials[i]);
+    static_assert(kFinishThreads == kWG, "partials_max assumes kWG threads");
+    float mp = partials_max(partials, n), mh = 0.0f;
+#pragma unroll 4
     for (int i = threadIdx.x; i < H; i += kFinishThreads)
         if (i != slot)
             mh = fmaxf(mh, hist[i]);

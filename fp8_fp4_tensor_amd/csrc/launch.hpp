@@ -43,6 +43,7 @@ struct ResidentGrid {
 // without atomics: every workgroup of the second pass (or the delayed-scaling
 // finish) re-reduces them from L2.
 constexpr int kMaxPartials = 1024;
+static_assert(kMaxPartials <= 4 * 256, "consumers read the partials with four loads per thread");
 constexpr size_t kPartialsBytes = kMaxPartials * sizeof(float);
 
 // Where a per-tensor cast takes its amax from.
