@@ -163,16 +163,17 @@ __global__ __launch_bounds__(kWG) void k_dq_tensor(const uint8_t* __restrict__ q
 // across it in chunks; a chunk lies inside one block (C % 16 == 0, blocks 16,
 // 32 or 128 wide), so it takes one scale.
 // SKIND: 0 fp32 scale plane, 1 E8M0 codes, 2 E4M3 codes times the tensor scale.
+// Block sizes are powers of two, passed as shifts (no integer division).
 template <int CODE, int SKIND, bool BF16>
 __global__ __launch_bounds__(kWG) void k_dq_rows(const uint8_t* __restrict__ q, const void* __restrict__ scales,
-                                                 const float* S, int64_t R, int64_t C, int br, int bc,
+                                                 const float* S, int64_t R, int64_t C, int br_shift, int bc_shift,
                                                  void* __restrict__ y)
 {
     constexpr int G = chunk_elems<BF16>();
-    const int64_t cpr = C / G, nbc = C / bc;
+    const int64_t cpr = C / G, nbc = C >> bc_shift;
     const float Sv = SKIND == 2 ? *S : 1.0f;
     for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
-        const int64_t srow = (r / br) * nbc;
+        const int64_t srow = (r >> br_shift) * nbc;
         for (int64_t j0 = threadIdx.x; j0 < cpr; j0 += kWG * kChunks) {
             uint32_t w[kChunks][2];
             float sc[kChunks];
@@ -181,7 +182,7 @@ __global__ __launch_bounds__(kWG) void k_dq_rows(const uint8_t* __restrict__ q, 
                 const int64_t j = j0 + k * kWG;
                 if (j < cpr) {
                     load_chunk<CODE, G>(q, r * C + j * G, w[k]);
-                    const int64_t si = srow + (j * G) / bc;
+                    const int64_t si = srow + ((j * G) >> bc_shift);
                     if constexpr (SKIND == 0)
                         sc[k] = reinterpret_cast<const float*>(scales)[si];
                     else if constexpr (SKIND == 1)
@@ -210,10 +211,11 @@ void rows_t(const uint8_t* q, const void* s, const float* S, int64_t R, int64_t 
             hipStream_t stream)
 {
     const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(R, kGrid));
+    const int brs = __builtin_ctz((unsigned)br), bcs = __builtin_ctz((unsigned)bc);  // powers of two
     if (bf)
-        k_dq_rows<CODE, SKIND, true><<<grid, kWG, 0, stream>>>(q, s, S, R, C, br, bc, y);
+        k_dq_rows<CODE, SKIND, true><<<grid, kWG, 0, stream>>>(q, s, S, R, C, brs, bcs, y);
     else
-        k_dq_rows<CODE, SKIND, false><<<grid, kWG, 0, stream>>>(q, s, S, R, C, br, bc, y);
+        k_dq_rows<CODE, SKIND, false><<<grid, kWG, 0, stream>>>(q, s, S, R, C, brs, bcs, y);
 }
 
 }  // namespace
