@@ -90,8 +90,11 @@ def lib():
     return L
 
 
-def status_str(status: int) -> str:
+def fq_status_str(status: int) -> str:
     return lib().fq_status_str(int(status)).decode()
+
+
+status_str = fq_status_str
 
 
 def _check(status: int, where: str):

@@ -36,6 +36,11 @@ def test_every_declared_symbol_is_exported(L):
         assert hasattr(L, n), n
 
 
+def test_binding_has_every_entry_point_by_name():
+    for n in declared_functions():
+        assert callable(getattr(fq, n, None)), n
+
+
 def test_status_strings(L):
     for s in range(7):
         assert fq.status_str(s).startswith("FQ_")
