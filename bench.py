@@ -268,6 +268,35 @@ def time_extras(torch, fq, L, stream_p, jobs, steps):
     return out
 
 
+def time_small(torch, fq, L, stream_p, steps):
+    """The small per-tensor workload (2^20 fp32 with outliers, current
+    scaling to E4M3): a few MiB, so launch latency bounds it; each call
+    bracketed by events, not part of the step."""
+    from fp8_fp4_tensor_amd import workloads as W
+    w = W.SMALL_CURRENT
+    R, C = w.shape
+    x = torch.from_numpy(w.make()).cuda()
+    d = fq.desc(fq.FQ_PER_TENSOR_CURRENT, fq.FQ_IN_F32, fq.FQ_E4M3, R, C, (0, 0), fq.FQ_ROWWISE)
+    out = fq.alloc_quantized(d)
+    ws = fq.alloc_workspace(d)
+    cq = out.c()
+    args = (ctypes.byref(d), ctypes.c_void_p(x.data_ptr()), ctypes.byref(cq), ctypes.c_void_p(ws.data_ptr()),
+            ws.numel(), stream_p)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for k in range(-3, steps):
+        if k >= 0:
+            ev[k][0].record()
+        rc = L.fq_quantize(*args)
+        if k >= 0:
+            ev[k][1].record()
+        if rc != fq.FQ_OK:
+            raise fq.FqError(rc, w.name)
+    torch.cuda.synchronize()
+    us = 1e3 * sum(a.elapsed_time(b) for a, b in ev) / steps
+    nbytes = algorithmic_bytes(w)
+    return {w.name: {"us_per_call": round(us, 2), "bytes": nbytes, "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -410,6 +439,7 @@ def main():
     }
     if not args.no_extras:
         result["dequant_requant"] = time_extras(torch, fq, L, sp, jobs, args.steps)
+        result["small"] = time_small(torch, fq, L, sp, args.steps)
     if not args.no_cpu_baseline:
         print("bench: timing the oracle on the host", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline([j["w"] for j in jobs], args.cpu_rows)
