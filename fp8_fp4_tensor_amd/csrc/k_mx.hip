@@ -29,8 +29,14 @@
 namespace fq {
 namespace {
 
-constexpr int kOP = 128 + 16;  // pitch of the LDS tile of transposed codes
+constexpr int kOP = 128;  // pitch of the LDS tile of transposed codes
 static_assert(128 * kOP + 128 * 4 <= 128 * 128 * 2, "the code tile must fit in the input tile it reuses");
+
+// Byte offset of 16-byte chunk ch (0..7) of row `row` in the tile of
+// transposed codes: 128-byte rows, chunks XOR-swizzled by (row / 2) % 8, so
+// the eight rows two apart that eight lanes write at once hit distinct banks
+// (a row's eight chunks, read by eight lanes, stay distinct too).
+__device__ __forceinline__ int otile_off(int row, int ch) { return row * kOP + ((ch ^ ((row >> 1) & 7)) << 4); }
 
 template <typename T>
 constexpr int tile_pitch()
@@ -155,8 +161,8 @@ __global__ __launch_bounds__(kWG) void k_mx(const T* __restrict__ x, int64_t R, 
         uint8_t* ocode = smem + 128 * kOP;  // [128][4] E8M0 codes of X^T
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            *reinterpret_cast<u32x4*>(otile + (2 * pc + j) * kOP + 32 * rb) = w[2 * j];
-            *reinterpret_cast<u32x4*>(otile + (2 * pc + j) * kOP + 32 * rb + 16) = w[2 * j + 1];
+            *reinterpret_cast<u32x4*>(otile + otile_off(2 * pc + j, 2 * rb)) = w[2 * j];
+            *reinterpret_cast<u32x4*>(otile + otile_off(2 * pc + j, 2 * rb + 1)) = w[2 * j + 1];
             ocode[(2 * pc + j) * 4 + rb] = (uint8_t)codes2[j];
         }
         __syncthreads();
@@ -169,7 +175,7 @@ __global__ __launch_bounds__(kWG) void k_mx(const T* __restrict__ x, int64_t R, 
             const int row = i >> 3, seg = (i & 7) * 16;
             if (row < nrows && seg < nbytes)
                 st16_stream(qt + (c0 + row) * R + r0 + seg,
-                            *reinterpret_cast<const u32x4*>(otile + row * kOP + seg));
+                            *reinterpret_cast<const u32x4*>(otile + otile_off(row, seg >> 4)));
         }
         if (threadIdx.x < nrows) {
             const int row = threadIdx.x;
@@ -359,8 +365,8 @@ __global__ __launch_bounds__(kWG) void k_mx_bf16(const uint16_t* __restrict__ x,
         uint8_t* ocode = smem + 128 * kOP;  // [128][4] E8M0 codes of X^T
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            *reinterpret_cast<u32x4*>(otile + (2 * pc + j) * kOP + 32 * rb) = w[2 * j];
-            *reinterpret_cast<u32x4*>(otile + (2 * pc + j) * kOP + 32 * rb + 16) = w[2 * j + 1];
+            *reinterpret_cast<u32x4*>(otile + otile_off(2 * pc + j, 2 * rb)) = w[2 * j];
+            *reinterpret_cast<u32x4*>(otile + otile_off(2 * pc + j, 2 * rb + 1)) = w[2 * j + 1];
         }
         ocode[(2 * pc) * 4 + rb] = (uint8_t)code0;
         ocode[(2 * pc + 1) * 4 + rb] = (uint8_t)code1;
@@ -374,7 +380,7 @@ __global__ __launch_bounds__(kWG) void k_mx_bf16(const uint16_t* __restrict__ x,
             for (int k = 0; k < 4; ++k) {
                 const int row = row0 + 32 * k;
                 if (row < nrows && seg < nbytes)
-                    st16_stream(dst, *reinterpret_cast<const u32x4*>(otile + row * kOP + seg));
+                    st16_stream(dst, *reinterpret_cast<const u32x4*>(otile + otile_off(row, seg >> 4)));
                 dst += step;
             }
         }
@@ -676,8 +682,8 @@ __global__ __launch_bounds__(kWG) void k_mx_requant(const uint8_t* __restrict__ 
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            *reinterpret_cast<u32x4*>(otile + (2 * pc + j) * kOP + 32 * rb) = w[2 * j];
-            *reinterpret_cast<u32x4*>(otile + (2 * pc + j) * kOP + 32 * rb + 16) = w[2 * j + 1];
+            *reinterpret_cast<u32x4*>(otile + otile_off(2 * pc + j, 2 * rb)) = w[2 * j];
+            *reinterpret_cast<u32x4*>(otile + otile_off(2 * pc + j, 2 * rb + 1)) = w[2 * j + 1];
         }
         ocode[(2 * pc) * 4 + rb] = (uint8_t)code0;
         ocode[(2 * pc + 1) * 4 + rb] = (uint8_t)code1;
@@ -687,7 +693,7 @@ __global__ __launch_bounds__(kWG) void k_mx_requant(const uint8_t* __restrict__ 
         for (int k = 0; k < 4; ++k) {
             const int i = k * kWG + threadIdx.x, row = i >> 3, seg = (i & 7) * 16;
             if (row < nrows && seg < nbytes)
-                st16_stream(qt + (c0 + row) * R + r0 + seg, *reinterpret_cast<const u32x4*>(otile + row * kOP + seg));
+                st16_stream(qt + (c0 + row) * R + r0 + seg, *reinterpret_cast<const u32x4*>(otile + otile_off(row, seg >> 4)));
         }
         if (threadIdx.x < nrows) {
             const int row = threadIdx.x;
