@@ -167,12 +167,13 @@ def plane_bytes(w, which):
     return n // 2 + n // (br * bc) + 4
 
 
-def time_extras(torch, fq, L, stream_p, jobs, steps):
+def time_extras(torch, fq, L, stream_p, jobs, steps, flush):
     """Dequantize (rowwise plane to bf16), MXFP8 rowwise-to-colwise requantize,
     NVFP4 1x16 with stochastic rounding, the NVFP4 colwise copy with the RHT and
     stochastic rounding, MX with E5M2 and E2M1 elements and blockwise with
     power-of-two scales, at the large workloads' shapes, each call bracketed by
-    events; not part of the step."""
+    events and started cold (flush() runs before it, outside the events); not
+    part of the step."""
     out = {}
     for j in jobs:
         w = j["w"]
@@ -180,6 +181,7 @@ def time_extras(torch, fq, L, stream_p, jobs, steps):
         y = torch.empty((R, C), dtype=torch.bfloat16, device="cuda")
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         for k in range(-1, steps):
+            flush()
             if k >= 0:
                 ev[k][0].record()
             rc = L.fq_dequantize(ctypes.byref(j["d"]), ctypes.byref(j["cq"]), fq.FQ_ROWWISE,
@@ -200,6 +202,7 @@ def time_extras(torch, fq, L, stream_p, jobs, steps):
             dsr = fq.desc(d.recipe, d.in_dtype, d.format, R, C, (1, 16), d.outputs,
                           rounding=fq.FQ_ROUND_STOCHASTIC, seed=2024, offset=0)
             for k in range(-1, steps):
+                flush()
                 dsr.offset = k + 1
                 if k >= 0:
                     ev[k][0].record()
@@ -235,6 +238,7 @@ def time_extras(torch, fq, L, stream_p, jobs, steps):
             wsp = None if wsv is None else ctypes.c_void_p(wsv.data_ptr())
             wsn = 0 if wsv is None else wsv.numel()
             for k in range(-1, steps):
+                flush()
                 if k >= 0:
                     ev[k][0].record()
                 rc = L.fq_quantize(ctypes.byref(dv), j["xp"], ctypes.byref(cov), wsp, wsn, stream_p)
@@ -252,6 +256,7 @@ def time_extras(torch, fq, L, stream_p, jobs, steps):
             dst = fq.alloc_quantized(d)
             cdst = dst.c()
             for k in range(-1, steps):
+                flush()
                 if k >= 0:
                     ev[k][0].record()
                 rc = L.fq_requantize_transpose(ctypes.byref(j["d"]), ctypes.byref(j["cq"]), ctypes.byref(cdst),
@@ -268,7 +273,7 @@ def time_extras(torch, fq, L, stream_p, jobs, steps):
     return out
 
 
-def time_small(torch, fq, L, stream_p, steps):
+def time_small(torch, fq, L, stream_p, steps, flush):
     """The small per-tensor workload (2^20 fp32 with outliers, current
     scaling to E4M3): a few MiB, so launch latency bounds it; each call
     bracketed by events, not part of the step."""
@@ -284,6 +289,7 @@ def time_small(torch, fq, L, stream_p, steps):
             ws.numel(), stream_p)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for k in range(-3, steps):
+        flush()
         if k >= 0:
             ev[k][0].record()
         rc = L.fq_quantize(*args)
@@ -438,8 +444,16 @@ def main():
         "copy_reference_GBps": round(copy_gbs, 1),
     }
     if not args.no_extras:
-        result["dequant_requant"] = time_extras(torch, fq, L, sp, jobs, args.steps)
-        result["small"] = time_small(torch, fq, L, sp, args.steps)
+        # each extra call starts cold, like the step's: 512 MiB written between
+        # calls (outside the events) evicts the 256 MB memory-side cache and L2
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+
+        def flush():
+            scratch.zero_()
+
+        result["dequant_requant"] = time_extras(torch, fq, L, sp, jobs, args.steps, flush)
+        result["small"] = time_small(torch, fq, L, sp, args.steps, flush)
+        del scratch
     if not args.no_cpu_baseline:
         print("bench: timing the oracle on the host", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline([j["w"] for j in jobs], args.cpu_rows)
