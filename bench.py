@@ -444,12 +444,14 @@ def main():
         "copy_reference_GBps": round(copy_gbs, 1),
     }
     if not args.no_extras:
-        # each extra call starts cold, like the step's: 512 MiB written between
+        # each extra call starts cold, like the step's: 512 MiB read between
         # calls (outside the events) evicts the 256 MB memory-side cache and L2
-        scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        # and leaves clean lines (a write would leave dirty ones for the timed
+        # call to write back)
+        scratch = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda")
 
         def flush():
-            scratch.zero_()
+            torch.amax(scratch)
 
         result["dequant_requant"] = time_extras(torch, fq, L, sp, jobs, args.steps, flush)
         result["small"] = time_small(torch, fq, L, sp, args.steps, flush)
