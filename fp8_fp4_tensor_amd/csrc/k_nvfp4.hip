@@ -46,7 +46,6 @@ namespace fq {
 namespace {
 
 constexpr int kLoads = 4;
-constexpr int kMaxGrid = 16384;
 // Rowwise 1x16 pass 2: fewer, longer-lived workgroups, so the per-workgroup
 // set-up (tensor scale from the partials, the multiplier table) is paid less
 // often: at 8192x14336 both passes take 82 us with 4096 workgroups,
@@ -363,7 +362,8 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_1x16(const T* __restrict__ x, int
 }
 
 template <typename T>
-__global__ __launch_bounds__(kWG) void k_nvfp4_16x16(const T* __restrict__ x, int64_t R, int64_t C, ScaleSrc src,
+__global__ __launch_bounds__(kWG) void k_nvfp4_16x16(const T* __restrict__ x, int64_t /*R: the grid covers it*/,
+                                                     int64_t C, ScaleSrc src,
                                                      uint8_t* __restrict__ p, uint8_t* __restrict__ codes,
                                                      float* S_out, float* amax_out)
 {
