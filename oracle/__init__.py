@@ -34,6 +34,17 @@ What pins each function (tests/test_oracle_*.py):
                        tiny tensors. The fp32 association of the two-level
                        scale is a reading of the pages: parity unpinned at
                        the last-ulp level of that association.
+  variants             MX E5M2 / MXFP4 scale closed forms and brute force;
+                       pow2 blockwise against closed forms, brute force and
+                       MX blocks sharing the tile exponent.
+  sr, rht              Philox against torch's engine; the rounding's
+                       defining properties; the transform against a
+                       Hadamard matrix built by Kronecker products.
+  dequant              exact decode times scale; bf16 rounding against torch.
+  requant (MX, pow2    brute force on tiny tensors in float64; exact
+  blockwise 1x128)     transposition on grid values; equality with the
+                       colwise copy quantized from the source wherever no
+                       special value intervenes ([MP] "FP8 通信"); error bound.
 """
 import ctypes
 import os
@@ -105,6 +116,7 @@ def _load():
         "orc_encode_e2m1_sr_array": (None, [_p, _p, _i64, _p]),
         "orc_f32_to_bf16_array": (None, [_p, _i64, _p]),
         "orc_requant_mx_colwise": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p]),
+        "orc_requant_block_colwise": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p]),
         "orc_dequant_tensor": (None, [_p, _i64, ctypes.c_int, _f32, _p]),
         "orc_dequant_block": (None, [_p, _p, _i64, _i64, ctypes.c_int, ctypes.c_int, _p]),
         "orc_dequant_mx": (None, [_p, _p, _i64, _i64, _p]),
@@ -448,3 +460,16 @@ def requant_mx_colwise(q_row, e_row):
     _check(_load().orc_requant_mx_colwise(q_row.ctypes.data, e_row.ctypes.data, R, C, q_col.ctypes.data,
                                           e_col.ctypes.data), "requant_mx_colwise")
     return dict(q_col=q_col.reshape(C, R), e_col=e_col.reshape(C, R // 32))
+
+
+def requant_block_colwise(q_row, s_row):
+    """Blockwise 1x128 with power-of-two scales: the colwise copy (codes
+    [C,R], fp32 scales [C,R/128]) from the rowwise copy alone."""
+    q_row = np.ascontiguousarray(q_row, dtype=np.uint8)
+    s_row = np.ascontiguousarray(s_row, dtype=np.float32)
+    R, C = q_row.shape
+    q_col = np.empty(R * C, np.uint8)
+    s_col = np.empty(C * (R // 128), np.float32)
+    _check(_load().orc_requant_block_colwise(q_row.ctypes.data, s_row.ctypes.data, R, C, q_col.ctypes.data,
+                                             s_col.ctypes.data), "requant_block_colwise")
+    return dict(q_col=q_col.reshape(C, R), s_col=s_col.reshape(C, R // 128))

@@ -1045,3 +1045,31 @@ int orc_requant_mx_colwise(const uint8_t *q_row, const uint8_t *e_row, int64_t R
     free(xhat);
     return 0;
 }
+
+/*
+ * The same step for the blockwise recipe with 1x128 tiles and power-of-two
+ * scales, the DeepSeek-V3-like activation layout whose 1-D tiles run along
+ * the token's hidden vector ([MP] section "FP8 通信": an FP8 expert-parallel
+ * dispatch sends only the rowwise copy, and the scales must be powers of two
+ * for the re-quantization to match a single quantization up to special
+ * values such as subnormals; [MP] "Blockwise scaling": the colwise copy of a
+ * 1-D tiling quantizes X^T with the same tiles). From q_row [R,C] and the
+ * tile scales s_row [R, C/128]: x_hat = dec(q) * s (exact in fp32, the scale
+ * being a power of two), then X_hat^T is quantized with 1x128 tiles and
+ * power-of-two scales: q_col [C,R], s_col [C, R/128].
+ */
+int orc_requant_block_colwise(const uint8_t *q_row, const float *s_row, int64_t R, int64_t C, uint8_t *q_col,
+                              float *s_col)
+{
+    float *xhat, *xt;
+    if (R <= 0 || C <= 0 || C % 128 || R % 128)
+        return -3;
+    xhat = (float *)malloc(sizeof(float) * (size_t)(R * C));
+    orc_dequant_block(q_row, s_row, R, C, 1, 128, xhat);
+    xt = (float *)malloc(sizeof(float) * (size_t)(R * C));
+    transpose_f32(xhat, R, C, xt);
+    block_rowwise(xt, ORC_IN_F32, C, R, 1, 128, 1, q_col, s_col);
+    free(xt);
+    free(xhat);
+    return 0;
+}

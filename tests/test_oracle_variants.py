@@ -165,3 +165,83 @@ def test_block_pow2_brute_force_tiny(orc):
                 assert r["q_row"][i, j * 128 + k] == want
     z = orc.quantize_block(np.zeros((1, 128), np.float32), (1, 128), pow2=True)
     assert z["s_row"][0, 0] == np.float32(2.0 ** -127) and not z["q_row"].any()
+
+
+# ------------------------------------------------------------ blockwise 1x128 pow2 requantization
+def test_block_requant_brute_force_tiny(orc):
+    """The colwise copy from the rowwise codes and scales alone, recomputed
+    here in float64: restore dec(q) * s (exact), take each 128-row column
+    block's amax, e = floor(log2 a) - 8, and the brute-force nearest code of
+    x_hat * 2^-e, stored transposed."""
+    rng = np.random.default_rng(81)
+    R, C = 128, 256
+    x = (rng.standard_normal((R, C)) * np.exp2(rng.integers(-10, 10, (R, C)))).astype(np.float32)
+    single = orc.quantize_block(x, (1, 128), pow2=True)
+    rq = orc.requant_block_colwise(single["q_row"], single["s_row"])
+    xhat = dec(orc, E4M3, single["q_row"]) * np.repeat(single["s_row"].astype(np.float64), 128, axis=1)
+    for c in range(0, C, 17):
+        col = xhat[:, c]
+        e = int(np.floor(np.log2(np.abs(col).max()))) - 8
+        assert rq["s_col"][c, 0] == np.float32(2.0 ** e)
+        for r in range(R):
+            y = col[r] * 2.0 ** -e                      # exact in float64
+            want = nearest_positive(orc, E4M3, y) | (0x80 if np.signbit(y) else 0)
+            assert rq["q_col"][c, r] == want, (c, r)
+
+
+def test_block_requant_exact_on_grid(orc):
+    """Values on the E4M3 grid whose every row tile and column block holds a
+    +-256: every scale is 1 both ways, so the requantized colwise copy is
+    the transpose of the rowwise codes, which is also the colwise copy
+    quantized from the source."""
+    rng = np.random.default_rng(83)
+    R, C = 256, 384
+    grid = np.array([orc.decode(E4M3, c) for c in range(0x08, 0x7F)])   # normal positives, 2^-6 .. 448
+    grid = grid[grid < 256]
+    x = (rng.choice(grid, (R, C)) * rng.choice([-1.0, 1.0], (R, C))).astype(np.float32)
+    for r in range(R):
+        x[r, (r * 3) % C] = 256.0 if r % 2 else -256.0      # every row tile of row r, and column block, gets one
+        x[r, (r * 3 + 128) % C] = 256.0
+        x[r, (r * 3 + 256) % C] = -256.0
+    single = orc.quantize_block(x, (1, 128), outputs=ROW | COL, pow2=True)
+    assert (single["s_row"] == 1.0).all() and (single["s_col"] == 1.0).all()
+    rq = orc.requant_block_colwise(single["q_row"], single["s_row"])
+    assert np.array_equal(rq["q_col"], single["q_row"].T)
+    assert np.array_equal(rq["q_col"], single["q_col"]) and (rq["s_col"] == 1.0).all()
+
+
+def test_block_requant_equals_single_quantization_where_exact(orc):
+    """[MP] "FP8 通信": with power-of-two scales, the re-quantized colwise copy
+    equals the colwise copy quantized from the source except at special
+    values. Where an element's column block gets the same scale both ways and
+    its scaled value is a normal, unsaturated E4M3 value in the row scaling
+    and in the column scaling, the codes are equal."""
+    R, C = 256, 384
+    x = W.normal((R, C), 1.0, 85, W.BF16)
+    xf = W.bf16_bits_to_f32(x).reshape(R, C)
+    single = orc.quantize_block(x, (1, 128), outputs=ROW | COL, pow2=True)
+    rq = orc.requant_block_colwise(single["q_row"], single["s_row"])
+    s1 = np.repeat(single["s_col"].astype(np.float64), 128, axis=1)        # [C, R]
+    s2 = np.repeat(rq["s_col"].astype(np.float64), 128, axis=1)
+    sr = np.repeat(single["s_row"].astype(np.float64), 128, axis=1).T      # row-tile scale of each element, [C, R]
+    xt = np.abs(xf.T).astype(np.float64)
+    y_row, y_col = xt / sr, xt / s1
+    exact = (s1 == s2) & (y_row >= 2.0 ** -6) & (y_col >= 2.0 ** -6) & (y_row <= 448) & (y_col <= 448)
+    assert exact.mean() > 0.8
+    assert np.array_equal(single["q_col"][exact], rq["q_col"][exact])
+    assert (single["q_col"] == rq["q_col"]).mean() > 0.9
+
+
+def test_block_requant_error_bound_and_zero(orc):
+    x = W.normal((128, 256), 0.02, 87, W.BF16)
+    single = orc.quantize_block(x, (1, 128), pow2=True)
+    rq = orc.requant_block_colwise(single["q_row"], single["s_row"])
+    xhat = orc.dequant_block(single["q_row"], single["s_row"], (1, 128)).T
+    back = orc.dequant_block(rq["q_col"], rq["s_col"], (1, 128))
+    ys = np.abs(xhat) / np.repeat(rq["s_col"].astype(np.float64), 128, axis=1)
+    ok = (ys >= 2.0 ** -6) & (ys <= 448)
+    assert ok.mean() > 0.9
+    assert (np.abs(back - xhat)[ok] / np.abs(xhat)[ok]).max() <= 2.0 ** -4 * (1 + 1e-6)
+    z = orc.quantize_block(np.zeros((128, 128), np.float32), (1, 128), pow2=True)
+    rz = orc.requant_block_colwise(z["q_row"], z["s_row"])
+    assert not rz["q_col"].any() and (rz["s_col"] == np.float32(2.0 ** -127)).all()
