@@ -212,13 +212,32 @@ def plane_bytes(w, which):
 
 
 def time_extras(torch, fq, L, stream_p, jobs, steps, flush):
-    """Dequantize (rowwise plane to bf16), MXFP8 rowwise-to-colwise requantize,
-    NVFP4 1x16 with stochastic rounding, the NVFP4 colwise copy with the RHT and
+    """Dequantize (rowwise plane to bf16), MXFP8 and pow2 blockwise 1x128
+    rowwise-to-colwise requantize, NVFP4 1x16 with stochastic rounding, the NVFP4 colwise copy with the RHT and
     stochastic rounding, MX with E5M2 and E2M1 elements and blockwise with
     power-of-two scales, at the large workloads' shapes, each call bracketed by
     events and started cold (flush() runs before it, outside the events); not
     part of the step."""
     out = {}
+
+    def time_requant(d_src, c_src, d_dst, nbytes, name, ev):
+        """Colwise copy from the rowwise copy (c_src) into fresh planes of d_dst."""
+        dst = fq.alloc_quantized(d_dst)
+        cdst = dst.c()
+        for k in range(-1, steps):
+            flush()
+            if k >= 0:
+                ev[k][0].record()
+            rc = L.fq_requantize_transpose(ctypes.byref(d_src), ctypes.byref(c_src), ctypes.byref(cdst), stream_p)
+            if k >= 0:
+                ev[k][1].record()
+            if rc != fq.FQ_OK:
+                raise fq.FqError(rc, "requantize " + name)
+        torch.cuda.synchronize()
+        us = 1e3 * sum(a.elapsed_time(b) for a, b in ev) / steps
+        out["requant_colwise/" + name] = {"us_per_call": round(us, 2), "bytes": nbytes,
+                                          "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1)}
+
     for j in jobs:
         w = j["w"]
         R, C = w.shape
@@ -294,26 +313,16 @@ def time_extras(torch, fq, L, stream_p, jobs, steps, flush):
             us = 1e3 * sum(a.elapsed_time(b) for a, b in ev) / steps
             out[vname + "/" + w.name] = {"us_per_call": round(us, 2), "bytes": nbytes,
                                          "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1)}
+            if vname == "block_pow2" and tuple(w.block) == (1, 128) and dv.outputs & fq.FQ_ROWWISE:
+                # the blockwise requantize from this pow2 rowwise copy: codes and
+                # fp32 tile scales read, the same written transposed
+                dc = fq.desc(fq.FQ_BLOCK_FP32, fq.FQ_IN_BF16, fq.FQ_E4M3, R, C, (1, 128), fq.FQ_COLWISE,
+                             scale_mode=fq.FQ_SCALE_POW2)
+                time_requant(dv, cov, dc, 2 * (R * C + 4 * (R * C // 128)), "block_pow2_" + w.name, ev)
             del ov
         if w.recipe == "mx":
             d = fq.desc(fq.FQ_MX, fq.FQ_IN_BF16, fq.FQ_E4M3, R, C, (1, 32), fq.FQ_COLWISE)
-            dst = fq.alloc_quantized(d)
-            cdst = dst.c()
-            for k in range(-1, steps):
-                flush()
-                if k >= 0:
-                    ev[k][0].record()
-                rc = L.fq_requantize_transpose(ctypes.byref(j["d"]), ctypes.byref(j["cq"]), ctypes.byref(cdst),
-                                               stream_p)
-                if k >= 0:
-                    ev[k][1].record()
-                if rc != fq.FQ_OK:
-                    raise fq.FqError(rc, "requantize " + w.name)
-            torch.cuda.synchronize()
-            us = 1e3 * sum(a.elapsed_time(b) for a, b in ev) / steps
-            nbytes = 2 * (R * C + R * C // 32)
-            out["requant_colwise/" + w.name] = {"us_per_call": round(us, 2), "bytes": nbytes,
-                                                "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1)}
+            time_requant(j["d"], j["cq"], d, 2 * (R * C + R * C // 32), w.name, ev)
     return out
 
 

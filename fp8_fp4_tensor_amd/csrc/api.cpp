@@ -514,13 +514,18 @@ fq_status fq_requantize_transpose(const fq_desc* d, const fq_quantized* in, cons
         return FQ_E_INVALID;
     if (d->transform != FQ_TRANSFORM_NONE && d->transform != FQ_TRANSFORM_RHT16)
         return FQ_E_INVALID;
-    if (d->recipe != FQ_MX || d->format != FQ_E4M3 || d->block_rows != 1 || d->block_cols != 32 ||
-        d->scale_mode != FQ_SCALE_DEFAULT || d->transform != FQ_TRANSFORM_NONE ||
-        d->rounding != FQ_ROUND_NEAREST_EVEN)
+    // MXFP8, or blockwise 1x128 with power-of-two scales ([MP] "FP8 通信":
+    // only power-of-two scales make the restored values exact)
+    const bool common = d->format == FQ_E4M3 && d->block_rows == 1 && d->transform == FQ_TRANSFORM_NONE &&
+                        d->rounding == FQ_ROUND_NEAREST_EVEN;
+    const bool mx = common && d->recipe == FQ_MX && d->block_cols == 32 && d->scale_mode == FQ_SCALE_DEFAULT;
+    const bool blk = common && d->recipe == FQ_BLOCK_FP32 && d->block_cols == 128 && d->scale_mode == FQ_SCALE_POW2;
+    if (!mx && !blk)
         return FQ_E_UNSUPPORTED;
     if (d->cols > 0 && d->rows > kMaxElems / d->cols)
         return FQ_E_SHAPE;
-    if (d->rows % 32 || d->cols % 32)
+    const int64_t unit = mx ? 32 : 128;
+    if (d->rows % unit || d->cols % unit)
         return FQ_E_SHAPE;
     if (!in || !out)
         return FQ_E_INVALID;
@@ -532,6 +537,9 @@ fq_status fq_requantize_transpose(const fq_desc* d, const fq_quantized* in, cons
     if (!aligned(in->rowwise.data, 16) || !aligned(in->rowwise.scale, 16) || !aligned(out->colwise.data, 16) ||
         !aligned(out->colwise.scale, 16))
         return FQ_E_ALIGN;
+    if (blk)
+        return hip_status(launch_block_requant((const uint8_t*)in->rowwise.data, (const float*)in->rowwise.scale, R,
+                                               C, (uint8_t*)out->colwise.data, (float*)out->colwise.scale, st));
     return hip_status(launch_mx_requant((const uint8_t*)in->rowwise.data, (const uint8_t*)in->rowwise.scale, R, C,
                                         (uint8_t*)out->colwise.data, (uint8_t*)out->colwise.scale, st));
 }

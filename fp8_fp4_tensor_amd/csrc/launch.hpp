@@ -129,6 +129,12 @@ int rht_amax_grid(int64_t R, int64_t C);
 hipError_t launch_rht_amax_partial(const void* x, int in_bf16, int64_t R, int64_t C, uint32_t signs,
                                    float* partials, int grid, hipStream_t stream);
 
+// Blockwise 1x128 with power-of-two scales: colwise copy (transposed codes,
+// fp32 scales [C, R/128]) from the rowwise codes and scales. R % 128 == 0,
+// C % 128 == 0.
+hipError_t launch_block_requant(const uint8_t* q, const float* s, int64_t R, int64_t C, uint8_t* qt, float* st,
+                                hipStream_t stream);
+
 // MXFP8 colwise copy (transposed codes and E8M0 codes) from the rowwise copy.
 hipError_t launch_mx_requant(const uint8_t* q, const uint8_t* e, int64_t R, int64_t C, uint8_t* qt, uint8_t* et,
                              hipStream_t stream);

@@ -324,14 +324,20 @@ fq_status fq_dequantize(const fq_desc *desc, const fq_quantized *in, int32_t whi
  * The colwise copy from the rowwise copy alone: de-quantize in->rowwise and
  * re-quantize in the other direction into out->colwise ([MP] section "FP8
  * 通信": the expert-parallel backward pass receives only rowwise FP8 data and
- * needs the colwise copy). Recipe FQ_MX with E4M3 elements (MXFP8) only,
- * round to nearest even, no transform: its power-of-two scales restore
- * the values exactly, so the result is the MX recipe applied down the columns
- * of those restored values (32x1 blocks, stored transposed: codes [cols,
- * rows], E8M0 codes [cols, rows/32]). It equals quantizing the original
- * tensor down the columns except where an element is subnormal or saturated
- * in one of the two scalings. Requires rows % 32 == 0 and cols % 32 == 0.
- * desc->outputs is ignored. Reads one code byte and writes one per element.
+ * needs the colwise copy; power-of-two scales are required so that the
+ * double quantization matches a single one up to special values). Round to
+ * nearest even, no transform, E4M3 elements, and one of:
+ *   FQ_MX, blocks (1,32) (MXFP8): the MX recipe applied down the columns of
+ *     the restored values (32x1 blocks, stored transposed: codes [cols,
+ *     rows], E8M0 codes [cols, rows/32]); rows % 32 == 0, cols % 32 == 0.
+ *   FQ_BLOCK_FP32, blocks (1,128), FQ_SCALE_POW2: the blockwise recipe with
+ *     power-of-two scales applied to X_hat^T with 1x128 tiles (codes [cols,
+ *     rows], fp32 scales [cols, rows/128]); in->rowwise.scale holds the
+ *     [rows, cols/128] fp32 tile scales; rows % 128 == 0, cols % 128 == 0.
+ * The restored values dec(q) * scale are exact in fp32. The result equals
+ * quantizing the original tensor down the columns except where an element
+ * is subnormal or saturated in one of the two scalings. desc->outputs is
+ * ignored. Reads one code byte and writes one per element.
  */
 fq_status fq_requantize_transpose(const fq_desc *desc, const fq_quantized *in, const fq_quantized *out,
                                   hipStream_t stream);

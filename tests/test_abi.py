@@ -255,3 +255,28 @@ def test_requantize_checks(L):
     nocol = fq.FqQuantized(fq.FqPlane(B, B), fq.FqPlane(None, None), None, None)
     assert L.fq_requantize_transpose(ctypes.byref(d), ctypes.byref(ok), ctypes.byref(nocol), None) \
         == fq.FQ_E_INVALID
+
+
+def test_requantize_checks_blockwise(L):
+    """Blockwise requantization: 1x128 tiles with power-of-two scales only
+    (the restored values are exact only then), 128-aligned shapes."""
+    ok = fq.FqQuantized(fq.FqPlane(B, B), fq.FqPlane(B, B), None, None)
+    pow2 = dict(scale_mode=fq.FQ_SCALE_POW2)
+    for bad in (fq.desc(fq.FQ_BLOCK_FP32, fq.FQ_IN_BF16, fq.FQ_E4M3, 128, 128, (1, 128)),
+                fq.desc(fq.FQ_BLOCK_FP32, fq.FQ_IN_BF16, fq.FQ_E4M3, 128, 128, (128, 128), **pow2),
+                fq.desc(fq.FQ_BLOCK_FP32, fq.FQ_IN_BF16, fq.FQ_E4M3, 128, 128, (1, 128), rounding=1, **pow2),
+                fq.desc(fq.FQ_MX, fq.FQ_IN_BF16, fq.FQ_E4M3, 128, 128, (1, 32), **pow2)):
+        assert L.fq_requantize_transpose(ctypes.byref(bad), ctypes.byref(ok), ctypes.byref(ok), None) \
+            in (fq.FQ_E_UNSUPPORTED, fq.FQ_E_INVALID)
+    for R, C in ((64, 128), (128, 96), (192, 128)):
+        d = fq.desc(fq.FQ_BLOCK_FP32, fq.FQ_IN_BF16, fq.FQ_E4M3, R, C, (1, 128), **pow2)
+        assert L.fq_requantize_transpose(ctypes.byref(d), ctypes.byref(ok), ctypes.byref(ok), None) \
+            == fq.FQ_E_SHAPE
+    d = fq.desc(fq.FQ_BLOCK_FP32, fq.FQ_IN_BF16, fq.FQ_E4M3, 256, 128, (1, 128), **pow2)
+    mis = fq.FqQuantized(fq.FqPlane(B, B + 4), fq.FqPlane(B, B), None, None)
+    assert L.fq_requantize_transpose(ctypes.byref(d), ctypes.byref(mis), ctypes.byref(ok), None) == fq.FQ_E_ALIGN
+    nocol = fq.FqQuantized(fq.FqPlane(B, B), fq.FqPlane(B, None), None, None)
+    assert L.fq_requantize_transpose(ctypes.byref(d), ctypes.byref(ok), ctypes.byref(nocol), None) \
+        == fq.FQ_E_INVALID
+    empty = fq.desc(fq.FQ_BLOCK_FP32, fq.FQ_IN_BF16, fq.FQ_E4M3, 0, 128, (1, 128), **pow2)
+    assert L.fq_requantize_transpose(ctypes.byref(empty), ctypes.byref(ok), ctypes.byref(ok), None) == fq.FQ_OK

@@ -214,12 +214,17 @@ def test_dequant_per_tensor(fmt):
 
 # ---------------------------------------------------------------- MX requantize (rowwise -> colwise)
 def check_requant(x):
+    """The GPU's rowwise copy must equal the oracle's; the oracle then
+    requantizes its own rowwise copy, the GPU its own."""
     R, C = x.shape
     d, out = run(fq.FQ_MX, fq.FQ_E4M3, x, (1, 32), fq.FQ_ROWWISE)
+    single = orc.quantize_mx(x, outputs=fq.FQ_ROWWISE)
+    same_bytes(host(out.row_data), single["q_row"], "rowwise codes")
+    same_bytes(host(out.row_scale), single["e_row"], "rowwise E8M0")
     dst = fq.alloc_quantized(fq.desc(fq.FQ_MX, fq.FQ_IN_BF16, fq.FQ_E4M3, R, C, (1, 32), fq.FQ_COLWISE))
     fq.fq_requantize_transpose(d, out, dst)
     torch.cuda.synchronize()
-    want = orc.requant_mx_colwise(host(out.row_data), host(out.row_scale).reshape(R, C // 32))
+    want = orc.requant_mx_colwise(single["q_row"], single["e_row"])
     same_bytes(host(dst.col_data), want["q_col"], "requantized colwise codes")
     same_bytes(host(dst.col_scale), want["e_col"], "requantized colwise E8M0")
 

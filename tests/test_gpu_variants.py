@@ -1,8 +1,9 @@
 """GPU parity of the format variants against the oracle (bit-exact codes and
 scales, plus fp32/bf16 dequantization): MX with E5M2 elements, MXFP4 (E2M1
 elements packed two per byte), and blockwise E4M3 with power-of-two tile
-scales. Small, ragged-tile, wide-range, every-bf16-pattern, all-zero and
-full-size cases, fp32 and bf16 inputs."""
+scales, including its requantization in the other direction (the colwise
+copy from the rowwise copy alone). Small, ragged-tile, wide-range,
+every-bf16-pattern, all-zero and full-size cases, fp32 and bf16 inputs."""
 import numpy as np
 import pytest
 import torch
@@ -135,3 +136,44 @@ def test_block_pow2_all_bf16_patterns_and_zero():
 @pytest.mark.parametrize("w", [w for w in W.LARGE if w.recipe == "block"], ids=lambda w: w.name)
 def test_full_size_block_pow2(w):
     check_block_pow2(w.make(), w.block, fq.FQ_ROWWISE)
+
+
+# ---------------------------------------------------------------- blockwise 1x128 pow2 requantize
+def check_block_requant(x):
+    """The GPU's rowwise copy must equal the oracle's; the oracle then
+    requantizes its own rowwise copy, the GPU its own."""
+    R, C = x.shape
+    d, out = quantize(fq.FQ_BLOCK_FP32, fq.FQ_E4M3, x, (1, 128), fq.FQ_ROWWISE, fq.FQ_SCALE_POW2)
+    single = orc.quantize_block(x, (1, 128), pow2=True)
+    same_bytes(host(out.row_data), single["q_row"], "pow2 rowwise codes")
+    same_bytes(host(out.row_scale), single["s_row"], "pow2 rowwise scales")
+    dst = fq.alloc_quantized(fq.desc(fq.FQ_BLOCK_FP32, in_dtype(x), fq.FQ_E4M3, R, C, (1, 128), fq.FQ_COLWISE,
+                                     scale_mode=fq.FQ_SCALE_POW2))
+    dst.col_data.fill_(0xA5)
+    dst.col_scale.fill_(-3.0)
+    fq.fq_requantize_transpose(d, out, dst)
+    torch.cuda.synchronize()
+    want = orc.requant_block_colwise(single["q_row"], single["s_row"])
+    same_bytes(host(dst.col_data), want["q_col"], "requantized colwise codes")
+    same_bytes(host(dst.col_scale), want["s_col"], "requantized colwise scales")
+
+
+@pytest.mark.parametrize("shape", [(128, 128), (256, 384), (384, 128), (128, 1152)])
+@pytest.mark.parametrize("dt", [W.BF16, W.F32])
+def test_block_requant_small(shape, dt):
+    check_block_requant(W.normal(shape, 0.02, 5 * shape[0] + shape[1], dt))
+
+
+def test_block_requant_wide_range_and_zero():
+    check_block_requant(W.uniform_bits_bf16((256, 256), 17, max_abs=3e38))
+    check_block_requant(W.student_t((384, 256), 3.0, 19, W.BF16))
+    check_block_requant(np.zeros((128, 256), np.uint16))
+    z = np.zeros((256, 128), np.float32)
+    z[5, 7] = -3.0e-30
+    check_block_requant(z)
+
+
+@pytest.mark.parametrize("w", [w for w in W.LARGE if w.recipe == "block" and w.block == (1, 128)],
+                         ids=lambda w: w.name)
+def test_full_size_block_requant(w):
+    check_block_requant(w.make())
