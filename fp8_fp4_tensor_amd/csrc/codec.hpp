@@ -214,6 +214,18 @@ __device__ __forceinline__ float e8m0_value(uint32_t code)
     return code == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(code << 23);
 }
 
+// ---------------------------------------------------------------- tiles
+// Tile t of a grid of tiles ntc wide -> its tile row tr and column tc.
+// Tensors hold at most 2^36 elements, so tile indices and counts stay below
+// 2^32 and one 32-bit division does (a 64-bit one costs about a hundred
+// scalar instructions per tile).
+__device__ __forceinline__ void tile_coords(int64_t t, int64_t ntc, int64_t& tr, int64_t& tc)
+{
+    const uint32_t q = (uint32_t)t / (uint32_t)ntc;
+    tr = q;
+    tc = t - (int64_t)q * ntc;
+}
+
 // ---------------------------------------------------------------- memory
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));

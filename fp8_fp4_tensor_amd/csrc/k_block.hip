@@ -23,10 +23,6 @@
 //   k_block_128x128    one workgroup per tile, kept in registers between the
 //                      tile max and the cast; the colwise copy is the byte
 //                      transpose of the same codes, through LDS.
-//   k_block_requant    1x128 tiles with power-of-two scales: the colwise copy
-//                      from the rowwise codes and scales alone (no source
-//                      tensor), as an FP8 expert-parallel dispatch needs in
-//                      the backward pass ([MP] "FP8 通信").
 #include <algorithm>
 
 #include "codec.hpp"
@@ -232,101 +228,6 @@ __global__ __launch_bounds__(kWG) void k_block_128x128(const T* __restrict__ x, 
     }
 }
 
-// Byte offset of 16-byte chunk ch (0..7) of row `row` in an LDS tile of
-// transposed codes (128-byte rows): chunks XOR-swizzled by (row / 2) % 8, so
-// the eight rows two apart that eight lanes write at once hit distinct banks.
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ int tr_off(int row, int ch) { return row * 128 + ((ch ^ ((row >> 1) & 7)) << 4); }
-
-// Requantize blockwise 1x128 (power-of-two scales) in the other direction.
-// A 128x128 tile of rowwise codes and its 128 row scales are staged in LDS
-// (the next tile's loads already in flight into registers). Thread (p, rb)
-// restores columns 2p, 2p+1 over rows 32rb..32rb+31 exactly in fp32 (an
-// E4M3 value times a power of two); the four waves' column maxima meet in
-// LDS to give each 128x1 block its E8M0-rule scale; the re-encoded codes go
-// through a transposed LDS tile and out as whole 128-byte lines of X^T, and
-// each X^T row's tile scale as one fp32. R and C are multiples of 128.
-__global__ __launch_bounds__(kWG) void k_block_requant(const uint8_t* __restrict__ q, const float* __restrict__ s,
-                                                       int64_t R, int64_t C, uint8_t* __restrict__ qt,
-                                                       float* __restrict__ st)
-{
-    constexpr int QP = 128 + 16;  // pitch of the staged code tile (bytes)
-    __shared__ __align__(16) uint8_t qtile[128 * QP];
-    __shared__ __align__(16) uint8_t otile[128 * 128];
-    __shared__ float stile[128];
-    __shared__ float pmax[4][128];
-    const int64_t ntc = C / 128, ntiles = ntc * (R / 128), nsr = R / 128;
-    u32x4 v[4];
-    float sv = 0.0f;
-    auto load_tile = [&](int64_t t) {
-        const int64_t r0 = (t / ntc) * 128, c0 = (t % ntc) * 128;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int i = k * kWG + threadIdx.x, row = i >> 3, seg = (i & 7) * 16;
-            v[k] = ld16_stream(q + (r0 + row) * C + c0 + seg);
-        }
-        if (threadIdx.x < 128)
-            sv = s[(r0 + threadIdx.x) * ntc + c0 / 128];
-    };
-    if ((int64_t)blockIdx.x < ntiles)
-        load_tile(blockIdx.x);
-    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        const int64_t r0 = (t / ntc) * 128, c0 = (t % ntc) * 128;
-        __syncthreads();  // the previous tile's LDS reads are done
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int i = k * kWG + threadIdx.x, row = i >> 3, seg = (i & 7) * 16;
-            *reinterpret_cast<u32x4*>(qtile + row * QP + seg) = v[k];
-        }
-        if (threadIdx.x < 128)
-            stile[threadIdx.x] = sv;
-        __syncthreads();
-        if (t + gridDim.x < ntiles)
-            load_tile(t + gridDim.x);
-        const int pc = threadIdx.x & 63, rb = threadIdx.x >> 6;
-        float f0[32], f1[32];
-#pragma unroll
-        for (int k = 0; k < 32; ++k) {
-            const int row = 32 * rb + k;
-            const uint32_t two = *reinterpret_cast<const uint16_t*>(qtile + row * QP + 2 * pc);
-            const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)two, false);
-            const float sc = stile[row];
-            f0[k] = d[0] * sc;
-            f1[k] = d[1] * sc;
-        }
-        pmax[rb][2 * pc] = absmax<32>(f0);
-        pmax[rb][2 * pc + 1] = absmax<32>(f1);
-        __syncthreads();
-        const float a0 = fmaxf(fmaxf(pmax[0][2 * pc], pmax[1][2 * pc]), fmaxf(pmax[2][2 * pc], pmax[3][2 * pc]));
-        const float a1 = fmaxf(fmaxf(pmax[0][2 * pc + 1], pmax[1][2 * pc + 1]),
-                               fmaxf(pmax[2][2 * pc + 1], pmax[3][2 * pc + 1]));
-        const uint32_t code0 = mx_code<kE4M3>(a0), code1 = mx_code<kE4M3>(a1);
-        const float m0 = mx_multiplier(code0), m1 = mx_multiplier(code1);
-        u32x4 w[4];
-#pragma unroll
-        for (int d = 0; d < 8; ++d) {
-            w[d >> 2][d & 3] = enc4<kE4M3>(f0[4 * d], f0[4 * d + 1], f0[4 * d + 2], f0[4 * d + 3], m0);
-            w[2 + (d >> 2)][d & 3] = enc4<kE4M3>(f1[4 * d], f1[4 * d + 1], f1[4 * d + 2], f1[4 * d + 3], m1);
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            *reinterpret_cast<u32x4*>(otile + tr_off(2 * pc + j, 2 * rb)) = w[2 * j];
-            *reinterpret_cast<u32x4*>(otile + tr_off(2 * pc + j, 2 * rb + 1)) = w[2 * j + 1];
-        }
-        if (rb == 0) {
-            st[(c0 + 2 * pc) * nsr + r0 / 128] = e8m0_value(code0);
-            st[(c0 + 2 * pc + 1) * nsr + r0 / 128] = e8m0_value(code1);
-        }
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int i = k * kWG + threadIdx.x, row = i >> 3, seg = (i & 7) * 16;
-            st16_stream(qt + (c0 + row) * R + r0 + seg, *reinterpret_cast<const u32x4*>(otile + tr_off(row, seg >> 4)));
-        }
-    }
-}
-
 }  // namespace
 
 hipError_t launch_block_1x128(const void* x, int in_bf16, int pow2, int64_t R, int64_t C, uint8_t* q, float* s,
@@ -388,16 +289,6 @@ hipError_t launch_block_128x128(const void* x, int in_bf16, int pow2, int64_t R,
         block_128x128_t<float, true>(xf, R, C, q, s, qt, st, stream);
     else
         block_128x128_t<float, false>(xf, R, C, q, s, qt, st, stream);
-    return hipGetLastError();
-}
-
-hipError_t launch_block_requant(const uint8_t* q, const float* s, int64_t R, int64_t C, uint8_t* qt, float* st,
-                                hipStream_t stream)
-{
-    const int64_t ntiles = (C / 128) * (R / 128);
-    static ResidentGrid cache;
-    const int64_t grid = std::min<int64_t>(ntiles, cache.get(k_block_requant, kWG, 0));
-    k_block_requant<<<(unsigned)grid, kWG, 0, stream>>>(q, s, R, C, qt, st);
     return hipGetLastError();
 }
 

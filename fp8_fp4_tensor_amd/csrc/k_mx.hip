@@ -74,7 +74,9 @@ __global__ __launch_bounds__(kWG) void k_mx(const T* __restrict__ x, int64_t R, 
     const int cc = (threadIdx.x % LPR) * E, rr0 = threadIdx.x / LPR;
     const int64_t nbc = C / 32, nbr = R / 32;
     for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        const int64_t r0 = (t / ntc) * 128, c0 = (t % ntc) * 128;
+        int64_t tr, tc;
+        tile_coords(t, ntc, tr, tc);
+        const int64_t r0 = tr * 128, c0 = tc * 128;
         u32x4 v[ROUNDS];
         mx_load_tile<T, ROUNDS>(x, R, C, r0, c0, cc, rr0, RPR, v);
         const bool col_in = c0 + cc < C;
@@ -205,7 +207,6 @@ __global__ __launch_bounds__(kWG) void k_mx(const T* __restrict__ x, int64_t R, 
 // about a third of the VALU work of widening, multiplying and clamping in
 // fp32.
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -271,7 +272,9 @@ __global__ __launch_bounds__(kWG) void k_mx_bf16(const uint16_t* __restrict__ x,
     const int cc = (threadIdx.x & 15) * 8, rr0 = threadIdx.x >> 4;
     const int64_t nbc = C / 32, nbr = R / 32;
     for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        const int64_t r0 = (t / ntc) * 128, c0 = (t % ntc) * 128;
+        int64_t tr, tc;
+        tile_coords(t, ntc, tr, tc);
+        const int64_t r0 = tr * 128, c0 = tc * 128;
         const bool col_in = c0 + cc < C;
         u32x4 v[ROUNDS];
         {
@@ -480,7 +483,9 @@ __global__ __launch_bounds__(kWG) void k_mxfp4_bf16(const uint16_t* __restrict__
     // registers cost one resident workgroup per CU).
     u32x4 v[ROUNDS];
     auto load_tile = [&](int64_t t) {
-        const int64_t r0 = (t / ntc) * 128, c0 = (t % ntc) * 128;
+        int64_t tr, tc;
+        tile_coords(t, ntc, tr, tc);
+        const int64_t r0 = tr * 128, c0 = tc * 128;
         const bool col_in = c0 + cc < C;
         const uint16_t* src = x + (r0 + rr0) * C + c0 + cc;
         const int64_t step = 16 * C;
@@ -493,7 +498,9 @@ __global__ __launch_bounds__(kWG) void k_mxfp4_bf16(const uint16_t* __restrict__
     if ((int64_t)blockIdx.x < ntiles)
         load_tile(blockIdx.x);
     for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        const int64_t r0 = (t / ntc) * 128, c0 = (t % ntc) * 128;
+        int64_t tr, tc;
+        tile_coords(t, ntc, tr, tc);
+        const int64_t r0 = tr * 128, c0 = tc * 128;
         const bool col_in = c0 + cc < C;
         const bool full_row_codes = c0 + 128 <= C && (nbc & 3) == 0;
         if (qt)
@@ -609,108 +616,6 @@ __global__ __launch_bounds__(kWG) void k_mxfp4_bf16(const uint16_t* __restrict__
     }
 }
 
-// ---------------------------------------------------------------- requantize
-// The colwise MXFP8 copy from the rowwise copy alone ([MP] "FP8 通信": the
-// EP backward step de-quantizes the rowwise FP8 data and re-quantizes it in
-// the other direction). Per 128x128 tile: the rowwise codes (16 KiB) and the
-// tile rows' E8M0 codes go to LDS; each thread takes a column pair and 32
-// rows, restores the values exactly (dec(q) * 2^(code-127) is exact in fp32
-// for power-of-two scales), quantizes each 32x1 column block with the MX
-// rule, and the transposed codes leave through an LDS tile as whole lines.
-// HBM traffic is one code byte in and one out per element, plus scales.
-__global__ __launch_bounds__(kWG) void k_mx_requant(const uint8_t* __restrict__ q, const uint8_t* __restrict__ e,
-                                                    int64_t R, int64_t C, uint8_t* __restrict__ qt,
-                                                    uint8_t* __restrict__ et)
-{
-    constexpr int QP = 128 + 16;  // pitch of the code tile (bytes)
-    __shared__ __align__(16) uint8_t qtile[128 * QP];
-    __shared__ __align__(16) uint8_t etile[128 * 4];
-    __shared__ __align__(16) uint8_t otile[128 * kOP];
-    __shared__ __align__(16) uint8_t ocode[128 * 4];
-    const int64_t ntc = cdiv(C, 128), ntiles = ntc * cdiv(R, 128);
-    const int64_t nbc = C / 32, nbr = R / 32;
-    // a tile's codes and E8M0 codes are loaded into registers one iteration
-    // early, so they fly while the previous tile is requantized
-    u32x4 v[4];
-    uint32_t ew = 0;
-    auto load_tile = [&](int64_t t) {
-        const int64_t r0 = (t / ntc) * 128, c0 = (t % ntc) * 128;
-        const int64_t nrows_in = min((int64_t)128, R - r0), ncols_in = min((int64_t)128, C - c0);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int i = k * kWG + threadIdx.x, row = i >> 3, seg = (i & 7) * 16;
-            v[k] = (row < nrows_in && seg < ncols_in) ? ld16_stream(q + (r0 + row) * C + c0 + seg)
-                                                      : u32x4{0u, 0u, 0u, 0u};
-        }
-        ew = 0;
-        if (threadIdx.x < nrows_in)
-            for (int j = 0; j < ncols_in / 32; ++j)
-                ew |= (uint32_t)e[(r0 + threadIdx.x) * nbc + c0 / 32 + j] << (8 * j);
-    };
-    if ((int64_t)blockIdx.x < ntiles)
-        load_tile(blockIdx.x);
-    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        const int64_t r0 = (t / ntc) * 128, c0 = (t % ntc) * 128;
-        const int64_t nrows_in = min((int64_t)128, R - r0), ncols_in = min((int64_t)128, C - c0);
-        __syncthreads();  // the previous tile's LDS reads are done
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int i = k * kWG + threadIdx.x, row = i >> 3, seg = (i & 7) * 16;
-            *reinterpret_cast<u32x4*>(qtile + row * QP + seg) = v[k];
-        }
-        if (threadIdx.x < 128)
-            *reinterpret_cast<uint32_t*>(etile + threadIdx.x * 4) = ew;
-        __syncthreads();
-        if (t + gridDim.x < ntiles)
-            load_tile(t + gridDim.x);
-        const int pc = threadIdx.x & 63, rb = threadIdx.x >> 6;
-        const int cb = (2 * pc) >> 5;  // the 32-column block of both columns
-        float f0[32], f1[32];
-#pragma unroll
-        for (int k = 0; k < 32; ++k) {
-            const int row = 32 * rb + k;
-            const uint32_t two = *reinterpret_cast<const uint16_t*>(qtile + row * QP + 2 * pc);
-            const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)two, false);
-            const float sc = e8m0_value(etile[row * 4 + cb]);
-            f0[k] = d[0] * sc;
-            f1[k] = d[1] * sc;
-        }
-        const uint32_t code0 = mx_code(absmax<32>(f0)), code1 = mx_code(absmax<32>(f1));
-        const float m0 = mx_multiplier(code0), m1 = mx_multiplier(code1);
-        u32x4 w[4];
-#pragma unroll
-        for (int d = 0; d < 8; ++d) {
-            w[d >> 2][d & 3] = enc4<kE4M3>(f0[4 * d], f0[4 * d + 1], f0[4 * d + 2], f0[4 * d + 3], m0);
-            w[2 + (d >> 2)][d & 3] = enc4<kE4M3>(f1[4 * d], f1[4 * d + 1], f1[4 * d + 2], f1[4 * d + 3], m1);
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            *reinterpret_cast<u32x4*>(otile + otile_off(2 * pc + j, 2 * rb)) = w[2 * j];
-            *reinterpret_cast<u32x4*>(otile + otile_off(2 * pc + j, 2 * rb + 1)) = w[2 * j + 1];
-        }
-        ocode[(2 * pc) * 4 + rb] = (uint8_t)code0;
-        ocode[(2 * pc + 1) * 4 + rb] = (uint8_t)code1;
-        __syncthreads();
-        const int64_t nrows = ncols_in, nbytes = nrows_in;  // rows and bytes of the X^T tile
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int i = k * kWG + threadIdx.x, row = i >> 3, seg = (i & 7) * 16;
-            if (row < nrows && seg < nbytes)
-                st16_stream(qt + (c0 + row) * R + r0 + seg, *reinterpret_cast<const u32x4*>(otile + otile_off(row, seg >> 4)));
-        }
-        if (threadIdx.x < nrows) {
-            const int row = threadIdx.x;
-            uint8_t* dst = et + (c0 + row) * nbr + r0 / 32;
-            if (nbytes == 128 && (nbr & 3) == 0) {
-                *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(ocode + row * 4);
-            } else {
-                for (int j = 0; j < nbytes / 32; ++j)
-                    dst[j] = ocode[row * 4 + j];
-            }
-        }
-    }
-}
-
 }  // namespace
 
 template <int FMT>
@@ -755,20 +660,6 @@ hipError_t launch_mx(const void* x, int in_bf16, int fmt, int64_t R, int64_t C, 
         launch_mx_t<kE5M2>(x, in_bf16, R, C, q, e, qt, et, stream);
     else
         launch_mx_t<kE4M3>(x, in_bf16, R, C, q, e, qt, et, stream);
-    return hipGetLastError();
-}
-
-}  // namespace fq
-
-namespace fq {
-
-hipError_t launch_mx_requant(const uint8_t* q, const uint8_t* e, int64_t R, int64_t C, uint8_t* qt, uint8_t* et,
-                             hipStream_t stream)
-{
-    const int64_t ntiles = cdiv(C, 128) * cdiv(R, 128);
-    static ResidentGrid cache;
-    const int64_t grid = std::min<int64_t>(ntiles, cache.get(k_mx_requant, kWG, 0));
-    k_mx_requant<<<(unsigned)grid, kWG, 0, stream>>>(q, e, R, C, qt, et);
     return hipGetLastError();
 }
 

@@ -441,7 +441,9 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_colt(const T* __restrict__ x, int
     }
     const int c = threadIdx.x >> 2, q = threadIdx.x & 3;
     for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        const int64_t r0 = (t / ntc) * 128, c0 = (t % ntc) * TC;
+        int64_t tr, tc;
+        tile_coords(t, ntc, tr, tc);
+        const int64_t r0 = tr * 128, c0 = tc * TC;
         const int64_t rows_in = min((int64_t)128, R - r0);
         __syncthreads();  // the previous tile's LDS reads are done
         // stage the tile: chunk j of row r goes to chunk j ^ (SW * ((r >> 4) & 3))

@@ -156,7 +156,9 @@ __global__ __launch_bounds__(kWG) void k_cast_tensor_2d(const T* __restrict__ x,
     const int64_t tcols = (C + 63) / 64, ntiles = ((R + 63) / 64) * tcols;
     float m = 0.0f;
     for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        const int64_t r0 = (t / tcols) * 64, c0 = (t % tcols) * 64;
+        int64_t tr, tc;
+        tile_coords(t, tcols, tr, tc);
+        const int64_t r0 = tr * 64, c0 = tc * 64;
         __syncthreads();
         for (int i = threadIdx.x; i < 64 * 64; i += kWG) {
             const int r = i >> 6, c = i & 63;
@@ -217,7 +219,9 @@ __global__ __launch_bounds__(kWG) void k_cast_tensor_tile(const T* __restrict__ 
     const int cc = (threadIdx.x % LPR) * E, rr0 = threadIdx.x / LPR;
     float m = 0.0f;
     for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        const int64_t r0 = (t / ntc) * 128, c0 = (t % ntc) * 128;
+        int64_t tr, tc;
+        tile_coords(t, ntc, tr, tc);
+        const int64_t r0 = tr * 128, c0 = tc * 128;
         const int rows_in = (int)min((int64_t)128, R - r0), cols_in = (int)min((int64_t)128, C - c0);
         __syncthreads();  // the previous tile's LDS reads are done
         u32x4 v[ROUNDS];
