@@ -15,7 +15,11 @@
 //                      128-element runs of the flat tensor: one tile is 16
 //                      lanes x 16 bytes of bf16 (32 lanes for fp32), and the
 //                      tile max is a 4-step DPP reduction inside a row of
-//                      lanes. One read, no LDS.
+//                      lanes. A lane keeps four loads (four tiles of its
+//                      lane group) in flight; lane i of each quad does the
+//                      scale division for load i and the quad shares the
+//                      results by DPP, a quarter of the division work. One
+//                      read, no LDS.
 //   k_block_1x128_col  the colwise copy: 1x128 tiles of X^T, i.e. 128-row
 //                      runs down each column. A 128-row x 64-column tile is
 //                      staged in LDS (swizzled); four lanes share a column
@@ -61,6 +65,8 @@ __global__ __launch_bounds__(kWG) void k_block_1x128(const T* __restrict__ x, in
     const int64_t nunits = cdiv(n, U);
     const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int64_t nwaves = (int64_t)gridDim.x * 4;
+    static_assert(kLoads == 4 && LPB >= 4, "a quad of lanes shares the scale arithmetic of the four loads");
+    const int jsel = lane & 3;
     for (int64_t u0 = wave * kLoads; u0 < nunits; u0 += nwaves * kLoads) {
         u32x4 v[kLoads];
 #pragma unroll
@@ -68,6 +74,20 @@ __global__ __launch_bounds__(kWG) void k_block_1x128(const T* __restrict__ x, in
             const int64_t e = (u0 + j) * U + lane * E;
             v[j] = (u0 + j < nunits && e < n) ? ld16_stream(x + e) : u32x4{0u, 0u, 0u, 0u};
         }
+        // the tile maxima of the four loads; lane i of each quad then takes
+        // the scale arithmetic of load i, and the quad shares the results
+        float a[kLoads];
+#pragma unroll
+        for (int j = 0; j < kLoads; ++j)
+            a[j] = max_lanes<LPB>(In<T>::absmax16(v[j]));
+        const float asel = jsel == 0 ? a[0] : jsel == 1 ? a[1] : jsel == 2 ? a[2] : a[3];
+        float alpha_sel, s_sel;
+        tile_scales<POW2>(asel, alpha_sel, s_sel);
+        float alpha[kLoads];
+        alpha[0] = dpp<0x00>(alpha_sel);
+        alpha[1] = dpp<0x55>(alpha_sel);
+        alpha[2] = dpp<0xAA>(alpha_sel);
+        alpha[3] = dpp<0xFF>(alpha_sel);
 #pragma unroll
         for (int j = 0; j < kLoads; ++j) {
             if (u0 + j >= nunits)
@@ -75,13 +95,10 @@ __global__ __launch_bounds__(kWG) void k_block_1x128(const T* __restrict__ x, in
             const int64_t e = (u0 + j) * U + lane * E;
             float f[E];
             In<T>::unpack(v[j], f);
-            const float a = max_lanes<LPB>(absmax<E>(f));
-            float alpha, s;
-            tile_scales<POW2>(a, alpha, s);
             if (e < n) {
-                Enc8<kE4M3, E>::store(q + e, f, alpha);
-                if ((lane & (LPB - 1)) == 0)
-                    s_out[e / 128] = s;
+                Enc8<kE4M3, E>::store(q + e, f, alpha[j]);
+                if ((lane & (LPB - 1)) == j)
+                    s_out[e / 128] = s_sel;
             }
         }
     }
