@@ -95,11 +95,14 @@ __device__ __forceinline__ void nvfp4_tensor(const ScaleSrc& src, float* lds, fl
 
 // Block scale code and element multiplier from a block amax:
 // b = a/6, c = Q_E4M3(b * alpha_s), r = 1 / (dec(c) * S) (0 when that is 0).
+// For finite inputs c is a non-negative code, at most 0x7E; a NaN product
+// (non-finite input) would clamp to -448 and give 0xFE, so the table index
+// keeps the low seven bits and stays inside the table whatever the input.
 __device__ __forceinline__ void nvfp4_block(float a, float alpha_s, const float* rtab, uint32_t& code, float& r)
 {
     const float b = div6(a);
     code = enc_e4m3_one(clampf(b * alpha_s, 448.0f));
-    r = rtab[code];
+    r = rtab[code & 0x7Fu];
 }
 
 // E values times r -> E/2 packed bytes (E = 8: a dword; E = 4: 16 bits).
