@@ -6,9 +6,9 @@ bf16: x[r, c] = (((1103 r + 2221 c) mod 256) - 128) / 64 * 2^((r + c // 128) mod
 The oracle regenerates sampled rows (and columns) exactly in numpy and checks
 them bit for bit, including rows whose elements lie past index 2^31, and
 colwise planes (rows of X^T) past that index: per-tensor, blockwise, MXFP8,
-MXFP4, NVFP4 (with and without the RHT), dequantization and the MX
-requantization. The tensor amax is 256 by construction (k = -128 at scale
-2^7 occurs)."""
+MXFP4, NVFP4 (with and without the RHT), dequantization and the MX and
+power-of-two blockwise requantizations. The tensor amax is 256 by
+construction (k = -128 at scale 2^7 occurs)."""
 import numpy as np
 import pytest
 import torch
@@ -206,4 +206,24 @@ def test_large_mx_requantize(big):
     same_bytes(host(dst.col_data[SAMPLE_COLS]), want["q_col"][pos], "requantized colwise codes")
     same_bytes(host(dst.col_scale.view(C, R // 32)[SAMPLE_COLS]), want["e_col"].reshape(len(cols), R // 32)[pos],
                "requantized colwise E8M0")
+    del src, dst
+
+
+def test_large_block_pow2_requantize(big):
+    pow2 = dict(scale_mode=fq.FQ_SCALE_POW2)
+    d = fq.desc(fq.FQ_BLOCK_FP32, fq.FQ_IN_BF16, fq.FQ_E4M3, R, C, (1, 128), fq.FQ_ROWWISE, **pow2)
+    src = quantize(d, big)
+    dst = fq.alloc_quantized(fq.desc(fq.FQ_BLOCK_FP32, fq.FQ_IN_BF16, fq.FQ_E4M3, R, C, (1, 128), fq.FQ_COLWISE,
+                                     **pow2))
+    fq.fq_requantize_transpose(d, src, dst)
+    torch.cuda.synchronize()
+    # the oracle's rowwise copy of the sampled columns' 1x128 tiles (every row), then its requantization
+    blocks = np.unique(SAMPLE_COLS // 128)
+    cols = (blocks[:, None] * 128 + np.arange(128)[None, :]).reshape(-1)
+    xs = bf16_bits(values(np.arange(R)[:, None], cols[None, :]))      # [R, 128 * len(blocks)]
+    rw = orc.quantize_block(xs, (1, 128), pow2=True)
+    want = orc.requant_block_colwise(rw["q_row"], rw["s_row"])
+    pos = np.searchsorted(cols, SAMPLE_COLS)
+    same_bytes(host(dst.col_data[SAMPLE_COLS]), want["q_col"][pos], "requantized colwise codes")
+    same_bytes(host(dst.col_scale.view(C, R // 128)[SAMPLE_COLS]), want["s_col"][pos], "requantized colwise scales")
     del src, dst
