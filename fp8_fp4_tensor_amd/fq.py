@@ -252,7 +252,8 @@ def fq_dequantize(d: FqDesc, qt: Quantized, which: int, y: torch.Tensor, stream=
 
 
 def fq_requantize_transpose(d: FqDesc, src: Quantized, dst: Quantized, stream=None):
-    """MXFP8: dst's colwise planes from src's rowwise planes (no bf16 source)."""
+    """MXFP8, or blockwise 1x128 with power-of-two scales: dst's colwise planes
+    from src's rowwise planes (no high-precision source)."""
     a, b = src.c(), dst.c()
     _check(lib().fq_requantize_transpose(ctypes.byref(d), ctypes.byref(a), ctypes.byref(b), _stream(stream)),
            "fq_requantize_transpose")
