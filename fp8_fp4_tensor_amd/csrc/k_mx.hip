@@ -12,7 +12,8 @@
 // E4M3, 15 = floor(log2 57344) for E5M2), held to the E8M0 range;
 // q = Q(x * 2^-e), exact multiply, saturating.
 //
-// One workgroup per 128x128 tile. Rowwise: each lane holds 16 bytes of a
+// One workgroup per 128x128 tile (bf16 input: two tiles side by side per
+// 512-thread workgroup, kMxTiles). Rowwise: each lane holds 16 bytes of a
 // row, a quad of lanes is one 1x32 block (bf16), reduced with two DPP steps;
 // codes and E8M0 scales are written straight from registers. Colwise: the
 // tile's raw inputs go to LDS in the same pass; then each thread owns one
@@ -31,6 +32,12 @@ namespace {
 
 constexpr int kOP = 128;  // pitch of the LDS tile of transposed codes
 static_assert(128 * kOP + 128 * 4 <= 128 * 128 * 2, "the code tile must fit in the input tile it reuses");
+// bf16 MX tile walk: 128x128 tiles per workgroup, side by side (a 128-row x
+// 256-column region, 512 threads): rows are read as 512-byte segments and
+// the rowwise E8M0 codes of a row leave as 8 contiguous bytes
+constexpr int kMxTiles = 2;
+static_assert(kMxTiles * 128 * kOP + kMxTiles * 128 * 4 <= 128 * (128 * kMxTiles + 8) * 2,
+              "the transposed code tile must fit in the input region it reuses");
 
 // Byte offset of 16-byte chunk ch (0..7) of row `row` in the tile of
 // transposed codes: 128-byte rows, chunks XOR-swizzled by (row / 2) % 8, so
@@ -260,21 +267,23 @@ __device__ __forceinline__ uint32_t dppu(uint32_t v)
 }
 
 template <int FMT>
-__global__ __launch_bounds__(kWG) void k_mx_bf16(const uint16_t* __restrict__ x, int64_t R, int64_t C,
+__global__ __launch_bounds__(kMxTiles * kWG) void k_mx_bf16(const uint16_t* __restrict__ x, int64_t R, int64_t C,
                                                  uint8_t* __restrict__ q, uint8_t* __restrict__ e,
                                                  uint8_t* __restrict__ qt, uint8_t* __restrict__ et)
 {
-    constexpr int ROUNDS = 8, P = 128 + 8;  // 16 lanes x 8 bf16 per tile row; LDS pitch in bf16
+    // kMxTiles 128x128 tiles side by side: TW columns, 16 lanes x 8 bf16 per
+    // tile row; LDS pitch P in bf16
+    constexpr int W = kMxTiles, NT = W * kWG, TW = 128 * W, ROUNDS = 8, P = TW + 8;
     extern __shared__ __align__(16) unsigned char smem[];
     uint16_t* tile = reinterpret_cast<uint16_t*>(smem);
     const int lane = threadIdx.x & 63;
-    const int64_t ntc = cdiv(C, 128), ntiles = ntc * cdiv(R, 128);
-    const int cc = (threadIdx.x & 15) * 8, rr0 = threadIdx.x >> 4;
+    const int64_t ntc = cdiv(C, TW), ntiles = ntc * cdiv(R, 128);
+    const int cc = (threadIdx.x & (16 * W - 1)) * 8, rr0 = threadIdx.x / (16 * W);
     const int64_t nbc = C / 32, nbr = R / 32;
     for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
         int64_t tr, tc;
         tile_coords(t, ntc, tr, tc);
-        const int64_t r0 = tr * 128, c0 = tc * 128;
+        const int64_t r0 = tr * 128, c0 = tc * TW;
         const bool col_in = c0 + cc < C;
         u32x4 v[ROUNDS];
         {
@@ -286,7 +295,8 @@ __global__ __launch_bounds__(kWG) void k_mx_bf16(const uint16_t* __restrict__ x,
                 src += step;
             }
         }
-        const bool full_row_codes = c0 + 128 <= C && (nbc & 3) == 0;
+        // whole u32 E8M0 words for this lane's 128-column tile
+        const bool full_row_codes = c0 + (cc & ~127) + 128 <= C && (nbc & 3) == 0;
         if (qt)
             __syncthreads();  // the previous tile's LDS reads are done
         {
@@ -309,7 +319,7 @@ __global__ __launch_bounds__(kWG) void k_mx_bf16(const uint16_t* __restrict__ x,
                     u32x2 w;
                     w[0] = cvt4_scaled<FMT>(clamp_pair(v[k][0], lim2), clamp_pair(v[k][1], lim2), scale);
                     w[1] = cvt4_scaled<FMT>(clamp_pair(v[k][2], lim2), clamp_pair(v[k][3], lim2), scale);
-                    // the row's four block codes into its first lane (DPP row_shl 4, 8, 12)
+                    // a tile row's four block codes into its first lane (DPP row_shl 4, 8, 12)
                     const int rbase = lane & ~15;
                     const uint32_t word = code | (dppu<0x104>(code) << 8) | (dppu<0x108>(code) << 16) |
                                           (dppu<0x10C>(code) << 24);
@@ -317,7 +327,7 @@ __global__ __launch_bounds__(kWG) void k_mx_bf16(const uint16_t* __restrict__ x,
                         st8_stream(dst, w);
                         if (full_row_codes) {
                             if (lane == rbase)
-                                *reinterpret_cast<uint32_t*>(edst) = word;
+                                *reinterpret_cast<uint32_t*>(edst + (cc & ~127) / 32) = word;
                         } else if ((lane & 3) == 0) {
                             edst[cc / 32] = (uint8_t)code;
                         }
@@ -333,7 +343,7 @@ __global__ __launch_bounds__(kWG) void k_mx_bf16(const uint16_t* __restrict__ x,
             continue;
         __syncthreads();
         // colwise: thread (p, rb) takes tile columns 2p, 2p+1, rows 32rb..+31
-        const int pc = threadIdx.x & 63, rb = threadIdx.x >> 6;
+        const int pc = threadIdx.x & (64 * W - 1), rb = threadIdx.x / (64 * W);
         u32x4 w[4];
         uint32_t code0, code1;
         {
@@ -364,8 +374,8 @@ __global__ __launch_bounds__(kWG) void k_mx_bf16(const uint16_t* __restrict__ x,
             }
         }
         __syncthreads();
-        uint8_t* otile = smem;              // [128][kOP] codes of X^T
-        uint8_t* ocode = smem + 128 * kOP;  // [128][4] E8M0 codes of X^T
+        uint8_t* otile = smem;             // [TW][kOP] codes of X^T
+        uint8_t* ocode = smem + TW * kOP;  // [TW][4] E8M0 codes of X^T
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             *reinterpret_cast<u32x4*>(otile + otile_off(2 * pc + j, 2 * rb)) = w[2 * j];
@@ -374,14 +384,14 @@ __global__ __launch_bounds__(kWG) void k_mx_bf16(const uint16_t* __restrict__ x,
         ocode[(2 * pc) * 4 + rb] = (uint8_t)code0;
         ocode[(2 * pc + 1) * 4 + rb] = (uint8_t)code1;
         __syncthreads();
-        const int64_t nrows = min((int64_t)128, C - c0), nbytes = min((int64_t)128, R - r0);
+        const int64_t nrows = min((int64_t)TW, C - c0), nbytes = min((int64_t)128, R - r0);
         {
             const int row0 = threadIdx.x >> 3, seg = (threadIdx.x & 7) * 16;
             uint8_t* dst = qt + (c0 + row0) * R + r0 + seg;
-            const int64_t step = 32 * R;
+            const int64_t step = (NT / 8) * R;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const int row = row0 + 32 * k;
+                const int row = row0 + (NT / 8) * k;
                 if (row < nrows && seg < nbytes)
                     st16_stream(dst, *reinterpret_cast<const u32x4*>(otile + otile_off(row, seg >> 4)));
                 dst += step;
@@ -630,10 +640,11 @@ void launch_mx_t(const void* x, int in_bf16, int64_t R, int64_t C, uint8_t* q, u
         return;
     }
     if (in_bf16) {
-        const size_t lds = qt ? 128 * tile_pitch<uint16_t>() * 2 : 0;
+        const size_t lds = qt ? 128 * (128 * kMxTiles + 8) * 2 : 0;
         static ResidentGrid cache;
-        const int64_t grid = std::min<int64_t>(ntiles, cache.get(k_mx_bf16<FMT>, kWG, lds));
-        k_mx_bf16<FMT><<<(unsigned)grid, kWG, lds, stream>>>((const uint16_t*)x, R, C, q, e, qt, et);
+        const int64_t nregions = cdiv(C, 128 * kMxTiles) * cdiv(R, 128);
+        const int64_t grid = std::min<int64_t>(nregions, cache.get(k_mx_bf16<FMT>, kMxTiles * kWG, lds));
+        k_mx_bf16<FMT><<<(unsigned)grid, kMxTiles * kWG, lds, stream>>>((const uint16_t*)x, R, C, q, e, qt, et);
     } else {
         const size_t lds = qt ? 128 * tile_pitch<float>() * 4 : 0;
         static ResidentGrid cache;
