@@ -14,8 +14,11 @@
  *     the Hopper flow with cast + cast_transpose).
  *   - All tensor pointers are DEVICE pointers, owned by the caller, and must
  *     be 16-byte aligned; scalar outputs (float*) must be 4-byte aligned.
- *     The library never allocates, frees or synchronizes, and keeps no state
- *     between calls: all state is in caller memory.
+ *     The library never allocates, frees or synchronizes. All quantization
+ *     state (delayed scaling's window and scales) is in caller memory; the
+ *     only thing the library keeps between calls is a per-device cache of
+ *     occupancy queries (how many workgroups of a kernel fit at once), which
+ *     sets launch shapes, never results.
  *   - Work is enqueued on the given HIP stream, in order; the call returns
  *     when it is enqueued. Calls on one stream with one workspace are
  *     ordered; concurrent calls need distinct workspaces and outputs.
@@ -107,12 +110,16 @@ enum { FQ_ROWWISE = 1, FQ_COLWISE = 2 };
  *                          option for FP4 values; [LP] section 2.4 item 5:
  *                          applied to gradients). A scaled value of
  *                          magnitude v < 6 between neighbouring E2M1 values
- *                          lo <= v < hi rounds to hi iff u / 2^16 <
- *                          (v - lo) / (hi - lo), u a 16-bit random number;
- *                          v >= 6 saturates; block scales stay
- *                          round-to-nearest-even. u comes from Philox4x32-10
- *                          (Salmon et al., SC 2011) with key = seed (low word
- *                          first): the element at index e of an output plane
+ *                          lo <= v < hi, with g = (v - lo) / (hi - lo) and u
+ *                          a 16-bit random number, rounds to hi iff
+ *                          u + g * 2^16 >= 2^16: the random bits are added
+ *                          below the last kept bit and the sum truncated, so
+ *                          it rounds up with probability floor(g * 2^16) /
+ *                          2^16. v >= 6 saturates; the sign is kept, also on
+ *                          zero; block scales stay round-to-nearest-even.
+ *                          u comes from Philox4x32-10 (Salmon et al., SC
+ *                          2011) with key = seed (low word first): the
+ *                          element at index e of an output plane
  *                          (row-major in that plane) uses counter
  *                          (h mod 2^32, h >> 32, s mod 2^32, s >> 32) with
  *                          h = e/8 and s = 2*offset + plane (mod 2^64), plane
@@ -251,9 +258,11 @@ typedef struct {
 /*
  * Buffer sizes in bytes for a desc. Any output pointer may be NULL. A plane
  * not selected by desc->outputs, or not used by the recipe, reports 0.
- * `workspace` is the device scratch that fq_quantize, fq_amax,
- * fq_quantize_with_amax and fq_quantize_delayed need for this desc (0 if
- * none); its contents need no initialization and are not preserved.
+ * `workspace` is device scratch large enough for every entry point that
+ * takes one (fq_quantize, fq_amax, fq_quantize_with_amax,
+ * fq_quantize_delayed) with this desc: 4096 bytes for every desc today.
+ * fq_quantize of BLOCK_FP32 and MX uses none and also accepts a NULL
+ * workspace. Its contents need no initialization and are not preserved.
  * Returns FQ_OK or the validation error the desc would raise.
  */
 fq_status fq_sizes(const fq_desc *desc, size_t *row_data, size_t *row_scale, size_t *col_data,

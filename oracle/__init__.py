@@ -30,16 +30,29 @@ What pins each function (tests/test_oracle_*.py):
   mx                   closed form code = max(E(a)-8, 0) from the fp32 bits,
                        power-of-two scale, brute force on tiny tensors.
   nvfp4                structure (block holding the tensor amax gets the
-                       E4M3 code of 448 and a +-6 element), brute force on
-                       tiny tensors. The fp32 association of the two-level
-                       scale is a reading of the pages: parity unpinned at
-                       the last-ulp level of that association.
+                       E4M3 code of 448 and a +-6 element); brute force on
+                       tiny tensors (both block shapes and planes, fp32 and
+                       bf16, E4M3-subnormal and zero blocks) recomputing A,
+                       S, every block code, d_B, r_B and nibble with the
+                       test's own float32 arithmetic and nearest-value search
+                       over torch-decoded E4M3 and the page's E2M1 list;
+                       exact power-of-two cases whose bytes follow from the
+                       construction; inputs on rounding boundaries showing
+                       that a swapped fp32 association would fail. Which
+                       association the pages mean is a reading (they fix the
+                       structure only); the pins fix that the oracle computes
+                       the stated one.
   variants             MX E5M2 / MXFP4 scale closed forms and brute force;
                        pow2 blockwise against closed forms, brute force and
                        MX blocks sharing the tile exponent.
-  sr, rht              Philox against torch's engine; the rounding's
-                       defining properties; the transform against a
-                       Hadamard matrix built by Kronecker products.
+  sr, rht              Philox against torch's engine; the rounding rule
+                       against a bit-level add-and-truncate on the fp32
+                       significand and its defining properties; the
+                       transform against a Hadamard matrix built by
+                       Kronecker products. The SR rule (which of the two
+                       16-bit discretizations of stochastic rounding) and
+                       the butterfly's stage order are readings the pages
+                       do not fix: parity unpinned at that level.
   dequant              exact decode times scale; bf16 rounding against torch.
   requant (MX, pow2    brute force on tiny tensors in float64; exact
   blockwise 1x128)     transposition on grid values; equality with the

@@ -669,14 +669,21 @@ unsigned orc_sr_bits(uint64_t seed, uint64_t offset, unsigned plane, int64_t e)
 }
 
 /*
- * READING (stochastic rounding to E2M1): a scaled value y of magnitude v
- * below the largest, 6, lies between two neighbouring E2M1 values lo <= v < hi;
- * with g = (v - lo) / (hi - lo) (exact in fp32) and u a 16-bit random number,
- * the 16 random bits are added below the last kept bit and the sum truncated:
- * v rounds to hi iff u + g * 2^16 >= 2^16, else to lo.  It goes up with
- * probability floor(g * 2^16) / 2^16, within 2^-16 of g (unbiased to that
- * resolution).  Values of magnitude 6 or more saturate to 6, as in
- * round-to-nearest.  The sign of y is kept, also on zero.
+ * READING (stochastic rounding to E2M1; the pages name the technique, not
+ * its arithmetic).  Stochastic rounding rounds v, lo <= v < hi between two
+ * neighbouring representable values, up with probability g = (v - lo) /
+ * (hi - lo) (Croci, Fasi, Higham, Mary and Mikaitis, "Stochastic rounding:
+ * implementation, error analysis and applications", R. Soc. Open Sci. 2022).
+ * With a finite random number the probability must be discretized; this
+ * oracle takes the form those authors and SR hardware use: r random bits are
+ * added to the bits below the last kept bit and the sum is truncated, here
+ * with r = 16.  So v rounds to hi iff u + g * 2^16 >= 2^16 (u the 16-bit
+ * random number, g * 2^16 exact in fp32), i.e. with probability
+ * floor(g * 2^16) / 2^16, within 2^-16 of g.  (The other discretization,
+ * "up iff u < g * 2^16", goes up with probability ceil(g * 2^16) / 2^16 and
+ * picks the low u; it is equally faithful to the definition and is not this
+ * one.)  Magnitudes of 6 or more saturate to 6, as in round-to-nearest; the
+ * sign of y is kept, also on zero.
  */
 unsigned orc_encode_e2m1_sr(float y, unsigned u)
 {

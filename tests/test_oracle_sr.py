@@ -104,6 +104,44 @@ def test_e2m1_sr_neighbours_and_exact_up_count(orc):
         assert np.all((codes >> 3) == (1 if np.signbit(y) else 0))
 
 
+def sr_add_truncate_bits(v, u):
+    """Stochastic rounding of a non-negative fp32 v < 6 to the E2M1 grid as
+    integer work on its bit pattern: the grid spacing h at v is 2^k (0.5 below
+    2, 1 below 4, 2 below 6); v/h in fixed point with 16 fraction bits is the
+    24-bit significand shifted (bits below those 16 are dropped); u is added
+    to that integer and the sum truncated to whole units of h. Returns the
+    grid values (float64) for an array of u."""
+    bits = int(np.float32(v).view(np.uint32))
+    e, m = (bits >> 23) & 0xFF, bits & 0x7FFFFF
+    sig, exp = (m | 0x800000, e - 150) if e else (m, -149)    # v = sig * 2^exp
+    k = -1 if v < 2 else (0 if v < 4 else 1)                  # h = 2^k
+    shift = exp - k + 16                                      # v/h * 2^16 = sig * 2^shift
+    t = sig << shift if shift >= 0 else sig >> -shift
+    s = t + u.astype(np.int64)
+    return (s >> 16).astype(np.float64) * 2.0 ** k
+
+
+def test_e2m1_sr_equals_bit_level_add_and_truncate(orc):
+    """The oracle's rule (up iff u + g*2^16 >= 2^16, compared in fp32) against
+    the add-and-truncate form of stochastic rounding done on the integer
+    significand: every one of the 65536 random values, for fp32 inputs
+    spread over every binade from 2^-140 to 6 and the E2M1 midpoints +-1 ulp."""
+    rng = np.random.default_rng(13)
+    u = np.arange(65536, dtype=np.uint16)
+    vs = list(np.exp2(rng.uniform(-140, np.log2(6.0), 160)).astype(np.float32))
+    for mid in (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0):
+        m = np.float32(mid)
+        vs += [np.nextafter(m, np.float32(0)), m, np.nextafter(m, np.float32(7))]
+    vs += [np.float32(v) for v in (0.5, 1.0, 2.0, 4.0, 5.9999995, 2.0 ** -149)]
+    for v in vs:
+        if not v < 6:
+            continue
+        want = sr_add_truncate_bits(v, u)
+        codes = orc.encode_e2m1_sr(np.full(65536, v, np.float32), u)
+        got = np.array([E2M1[c] for c in codes], np.float64)
+        assert np.array_equal(got, want), v
+
+
 def test_e2m1_sr_grid_values_are_fixed(orc):
     u = np.arange(0, 65536, 97, dtype=np.uint16)
     for code, val in enumerate(E2M1):
