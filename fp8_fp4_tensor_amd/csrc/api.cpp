@@ -15,8 +15,10 @@ namespace {
 
 using namespace fq;
 
-// At most 2^36 elements (128 GiB of bf16): every tiled kernel's grid then
-// stays below 2^32 work-items (the widest, 128x64 tiles, needs 2^31).
+// At most 2^36 elements (128 GiB of bf16). Kernels whose work units can be
+// small at narrow shapes (16x16 strips, 32-row slabs) stride over them with
+// a capped grid; every other tiled kernel's grid stays below 2^32
+// work-items at this size (the widest, 128x64 tiles, needs 2^31).
 constexpr int64_t kMaxElems = int64_t(1) << 36;
 constexpr int32_t kMaxHistory = 1 << 24;
 
@@ -111,8 +113,12 @@ SrArgs sr_of(const fq_desc* d)
 }
 
 struct Sizes {
-    size_t row_data = 0, row_scale = 0, col_data = 0, col_scale = 0, ws = 0;
+    size_t row_data = 0, row_scale = 0, col_data = 0, col_scale = 0;
+    size_t ws = 0;  // what fq_quantize / fq_quantize_with_amax / fq_quantize_delayed need
 };
+
+// fq_amax needs the partials for any desc, so fq_sizes reports at least that.
+constexpr size_t kAmaxWorkspace = kPartialsBytes;
 
 Sizes sizes_of(const fq_desc* d)
 {
@@ -261,7 +267,7 @@ fq_status fq_sizes(const fq_desc* d, size_t* row_data, size_t* row_scale, size_t
     if (col_scale)
         *col_scale = z.col_scale;
     if (workspace)
-        *workspace = z.ws;
+        *workspace = z.ws > kAmaxWorkspace ? z.ws : kAmaxWorkspace;
     return FQ_OK;
 }
 
@@ -283,7 +289,7 @@ fq_status fq_amax(const fq_desc* d, const void* x, float* amax_out, void* ws, si
     if (!aligned(amax_out, 4))
         return FQ_E_ALIGN;
     Sizes z;
-    z.ws = kPartialsBytes;
+    z.ws = kAmaxWorkspace;
     if ((s = check_ws(z, ws, ws_bytes)) != FQ_OK)
         return s;
     const int64_t n = d->rows * d->cols;

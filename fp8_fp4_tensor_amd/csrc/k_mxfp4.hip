@@ -28,6 +28,7 @@ namespace {
 
 constexpr int kLoads = 4;
 constexpr int kMaxGrid = 16384;
+constexpr int64_t kMaxSlabGrid = int64_t(1) << 16;  // 2^24 work-items at most
 
 // E values times m -> E/2 packed bytes
 template <int E>
@@ -83,34 +84,38 @@ __global__ __launch_bounds__(kWG) void k_mxfp4_col(const T* __restrict__ x, int6
 {
     constexpr int TC = 256, E = In<T>::kE, LPR = TC / E, RPR = kWG / LPR;
     __shared__ __align__(16) T tile[32][TC];
-    const int64_t ntc = cdiv(C, TC);
-    const int64_t r0 = (int64_t)(blockIdx.x / ntc) * 32, c0 = (int64_t)(blockIdx.x % ntc) * TC;
+    const int64_t ntc = cdiv(C, TC), nslabs = (R / 32) * ntc;
     const int cc = (threadIdx.x % LPR) * E;
-    for (int rr = threadIdx.x / LPR; rr < 32; rr += RPR) {
-        u32x4 v = u32x4{0u, 0u, 0u, 0u};
-        if (c0 + cc < C)
-            v = ld16_stream(x + (r0 + rr) * C + c0 + cc);
-        *reinterpret_cast<u32x4*>(&tile[rr][cc]) = v;
-    }
-    __syncthreads();
-    const int c = threadIdx.x;
-    if (c0 + c >= C)
-        return;
-    float f[32];
+    // workgroups stride over the 32 x 256 slabs (the grid is capped)
+    for (int64_t t = blockIdx.x; t < nslabs; t += gridDim.x) {
+        const int64_t r0 = (t / ntc) * 32, c0 = (t % ntc) * TC;
+        __syncthreads();  // the previous slab's LDS reads are done
+        for (int rr = threadIdx.x / LPR; rr < 32; rr += RPR) {
+            u32x4 v = u32x4{0u, 0u, 0u, 0u};
+            if (c0 + cc < C)
+                v = ld16_stream(x + (r0 + rr) * C + c0 + cc);
+            *reinterpret_cast<u32x4*>(&tile[rr][cc]) = v;
+        }
+        __syncthreads();
+        const int c = threadIdx.x;
+        if (c0 + c >= C)
+            continue;
+        float f[32];
 #pragma unroll
-    for (int k = 0; k < 32; ++k)
-        f[k] = In<T>::load1(&tile[0][0], (int64_t)k * TC + c);
-    const uint32_t code = mx_code<kE2M1>(absmax<32>(f));
-    const float m = mx_multiplier(code);
-    u32x4 w;
-    w[0] = enc8_e2m1(f, m);
-    w[1] = enc8_e2m1(f + 8, m);
-    w[2] = enc8_e2m1(f + 16, m);
-    w[3] = enc8_e2m1(f + 24, m);
-    // row c0 + c of X^T: R/2 bytes, a multiple of 16 (R % 32 == 0); an
-    // ordinary store, so a line's 16-byte pieces meet in L2
-    *reinterpret_cast<u32x4*>(pt + (c0 + c) * (R / 2) + r0 / 2) = w;
-    ct[(c0 + c) * (R / 32) + r0 / 32] = (uint8_t)code;
+        for (int k = 0; k < 32; ++k)
+            f[k] = In<T>::load1(&tile[0][0], (int64_t)k * TC + c);
+        const uint32_t code = mx_code<kE2M1>(absmax<32>(f));
+        const float m = mx_multiplier(code);
+        u32x4 w;
+        w[0] = enc8_e2m1(f, m);
+        w[1] = enc8_e2m1(f + 8, m);
+        w[2] = enc8_e2m1(f + 16, m);
+        w[3] = enc8_e2m1(f + 24, m);
+        // row c0 + c of X^T: R/2 bytes, a multiple of 16 (R % 32 == 0); an
+        // ordinary store, so a line's 16-byte pieces meet in L2
+        *reinterpret_cast<u32x4*>(pt + (c0 + c) * (R / 2) + r0 / 2) = w;
+        ct[(c0 + c) * (R / 32) + r0 / 32] = (uint8_t)code;
+    }
 }
 
 template <typename T>
@@ -126,7 +131,7 @@ void launch_t(const void* xv, int64_t R, int64_t C, uint8_t* p, uint8_t* codes, 
         k_mxfp4_row<T><<<grid, kWG, 0, stream>>>(x, n, p, codes);
     }
     if (pt) {
-        const int64_t grid = (R / 32) * cdiv(C, 256);
+        const int64_t grid = std::min<int64_t>((R / 32) * cdiv(C, 256), kMaxSlabGrid);
         k_mxfp4_col<T><<<(unsigned)grid, kWG, 0, stream>>>(x, R, C, pt, codest);
     }
 }

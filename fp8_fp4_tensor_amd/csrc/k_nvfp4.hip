@@ -56,6 +56,10 @@ constexpr int kMaxGrid1x16 = 4096;
 // Colwise 1x16 (k_nvfp4_colt): workgroups stride over 128 x 64 tiles, the
 // set-up paid once per workgroup.
 constexpr int kMaxGridColt = 2048;
+// 16x16 strips and colwise slabs: one per workgroup up to 2^16 of them
+// (every transformer-linear shape here), beyond that workgroups stride over
+// them, so a grid stays far below 2^32 work-items
+constexpr int64_t kMaxSlabGrid = int64_t(1) << 16;
 
 // fp32(a / 6) for a >= 0, correctly rounded: q = a * RN(1/6), the residual
 // a - 6q (exact), one correction step. An exhaustive check over every fp32
@@ -365,22 +369,25 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_1x16(const T* __restrict__ x, int
 }
 
 template <typename T>
-__global__ __launch_bounds__(kWG) void k_nvfp4_16x16(const T* __restrict__ x, int64_t /*R: the grid covers it*/,
-                                                     int64_t C, ScaleSrc src,
+__global__ __launch_bounds__(kWG) void k_nvfp4_16x16(const T* __restrict__ x, int64_t R, int64_t C, ScaleSrc src,
                                                      uint8_t* __restrict__ p, uint8_t* __restrict__ codes,
                                                      float* S_out, float* amax_out)
 {
     __shared__ float lds[4];
     __shared__ float rtab[128];
     constexpr int E = In<T>::kE, LPB = 16 / E, WC = kWG * E;  // columns per workgroup
-    const int64_t nwc = cdiv(C, WC);
-    const int64_t r0 = (int64_t)(blockIdx.x / nwc) * 16;
-    const int64_t c = (int64_t)(blockIdx.x % nwc) * WC + (int64_t)threadIdx.x * E;
-    const bool in = c < C;
+    const int64_t nwc = cdiv(C, WC), nstrips = (R / 16) * nwc;
+    // workgroups stride over the 16-row strips (one each at the usual
+    // shapes; the grid is capped); the first strip's loads go out before the
+    // tensor scale is resolved, so the partials' round trip overlaps them
+    int64_t t = blockIdx.x;
     u32x4 v[16];
+    {
+        const int64_t r0 = (t / nwc) * 16, c = (t % nwc) * WC + (int64_t)threadIdx.x * E;
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-        v[i] = in ? ld16_stream(x + (r0 + i) * C + c) : u32x4{0u, 0u, 0u, 0u};
+        for (int i = 0; i < 16; ++i)
+            v[i] = (t < nstrips && c < C) ? ld16_stream(x + (r0 + i) * C + c) : u32x4{0u, 0u, 0u, 0u};
+    }
     float alpha_s, S, A;
     nvfp4_tensor(src, lds, rtab, alpha_s, S, A);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -389,27 +396,36 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_16x16(const T* __restrict__ x, in
         if (amax_out)
             *amax_out = A;
     }
-    float m = 0.0f;
+    for (; t < nstrips; t += gridDim.x) {
+        const int64_t r0 = (t / nwc) * 16, c = (t % nwc) * WC + (int64_t)threadIdx.x * E;
+        const bool in = c < C;
+        if (t != blockIdx.x) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        float f[E];
-        In<T>::unpack(v[i], f);
-        m = fmaxf(m, absmax<E>(f));
-    }
-    const float a = max_lanes<LPB>(m);
-    uint32_t code;
-    float r;
-    nvfp4_block(a, alpha_s, rtab, code, r);
-    if (!in)
-        return;
+            for (int i = 0; i < 16; ++i)
+                v[i] = in ? ld16_stream(x + (r0 + i) * C + c) : u32x4{0u, 0u, 0u, 0u};
+        }
+        float m = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        float f[E];
-        In<T>::unpack(v[i], f);
-        Fp4Store<E>::store(p + (r0 + i) * (C / 2) + c / 2, f, r);
+        for (int i = 0; i < 16; ++i) {
+            float f[E];
+            In<T>::unpack(v[i], f);
+            m = fmaxf(m, absmax<E>(f));
+        }
+        const float a = max_lanes<LPB>(m);
+        uint32_t code;
+        float r;
+        nvfp4_block(a, alpha_s, rtab, code, r);
+        if (!in)
+            continue;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float f[E];
+            In<T>::unpack(v[i], f);
+            Fp4Store<E>::store(p + (r0 + i) * (C / 2) + c / 2, f, r);
+        }
+        if ((threadIdx.x & (LPB - 1)) == 0)
+            codes[(r0 / 16) * (C / 16) + c / 16] = (uint8_t)code;
     }
-    if ((threadIdx.x & (LPB - 1)) == 0)
-        codes[(r0 / 16) * (C / 16) + c / 16] = (uint8_t)code;
 }
 
 // Colwise 1x16 copy (1x16 blocks of X^T = 16 rows of one column of X) in
@@ -543,57 +559,63 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_col(const T* __restrict__ x, int6
         if (amax_out)
             *amax_out = A;
     }
-    const int64_t ntc = cdiv(C, TC);
-    const int64_t r0 = (int64_t)(blockIdx.x / ntc) * 32, c0 = (int64_t)(blockIdx.x % ntc) * TC;
+    const int64_t ntc = cdiv(C, TC), nslabs = cdiv(R, 32) * ntc;
     const int cc = (threadIdx.x % LPR) * E;
-    for (int rr = threadIdx.x / LPR; rr < 32; rr += RPR) {
-        u32x4 v = u32x4{0u, 0u, 0u, 0u};
-        if (c0 + cc < C && r0 + rr < R)
-            v = ld16_stream(x + (r0 + rr) * C + c0 + cc);
-        *reinterpret_cast<u32x4*>(&tile[rr][cc]) = v;
-    }
-    __syncthreads();
-    const int c = threadIdx.x;
-    const bool in = c0 + c < C;
-    const int nb = (r0 + 32 <= R) ? 2 : 1;  // R % 16 == 0
-    uint32_t w[4];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        float f[16];
-#pragma unroll
-        for (int k = 0; k < 16; ++k)
-            f[k] = In<T>::load1(&tile[0][0], (int64_t)(16 * b + k) * TC + c);
-        float a = absmax<16>(f);
-        if constexpr (BR == 16)
-            a = max_lanes<16>(a);
-        uint32_t code;
-        float r;
-        nvfp4_block(a, alpha_s, rtab, code, r);
-        w[2 * b] = enc8_e2m1(f, r);
-        w[2 * b + 1] = enc8_e2m1(f + 8, r);
-        if (in && b < nb) {
-            const int64_t rb = (r0 + 16 * b) / 16;
-            if constexpr (BR == 1)
-                ct[(c0 + c) * (R / 16) + rb] = (uint8_t)code;
-            else if ((c & 15) == 0)
-                ct[((c0 + c) / 16) * (R / 16) + rb] = (uint8_t)code;
+    // workgroups stride over the 32 x 256 slabs (the grid is capped); every
+    // thread runs every iteration, so the barriers below are uniform
+    for (int64_t t = blockIdx.x; t < nslabs; t += gridDim.x) {
+        const int64_t r0 = (t / ntc) * 32, c0 = (t % ntc) * TC;
+        __syncthreads();  // the previous slab's LDS reads are done
+        for (int rr = threadIdx.x / LPR; rr < 32; rr += RPR) {
+            u32x4 v = u32x4{0u, 0u, 0u, 0u};
+            if (c0 + cc < C && r0 + rr < R)
+                v = ld16_stream(x + (r0 + rr) * C + c0 + cc);
+            *reinterpret_cast<u32x4*>(&tile[rr][cc]) = v;
         }
-    }
-    if (!in)
-        return;
-    // row c of the colwise plane is only 8-byte aligned (R/2 is a multiple of
-    // 8). A thread writes 8 or 16 bytes of a row: ordinary stores, so the
-    // pieces of a line meet in L2 before going to memory (streaming stores of
-    // such pieces each become a partial-line write, measured 3x slower).
-    uint8_t* out = pt + (c0 + c) * (R / 2) + r0 / 2;
-    u32x2 v2;
-    v2[0] = w[0];
-    v2[1] = w[1];
-    *reinterpret_cast<u32x2*>(out) = v2;
-    if (nb == 2) {
-        v2[0] = w[2];
-        v2[1] = w[3];
-        *reinterpret_cast<u32x2*>(out + 8) = v2;
+        __syncthreads();
+        const int c = threadIdx.x;
+        const bool in = c0 + c < C;
+        const int nb = (r0 + 32 <= R) ? 2 : 1;  // R % 16 == 0
+        uint32_t w[4];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            float f[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                f[k] = In<T>::load1(&tile[0][0], (int64_t)(16 * b + k) * TC + c);
+            float a = absmax<16>(f);
+            if constexpr (BR == 16)
+                a = max_lanes<16>(a);
+            uint32_t code;
+            float r;
+            nvfp4_block(a, alpha_s, rtab, code, r);
+            w[2 * b] = enc8_e2m1(f, r);
+            w[2 * b + 1] = enc8_e2m1(f + 8, r);
+            if (in && b < nb) {
+                const int64_t rb = (r0 + 16 * b) / 16;
+                if constexpr (BR == 1)
+                    ct[(c0 + c) * (R / 16) + rb] = (uint8_t)code;
+                else if ((c & 15) == 0)
+                    ct[((c0 + c) / 16) * (R / 16) + rb] = (uint8_t)code;
+            }
+        }
+        if (!in)
+            continue;
+        // row c of the colwise plane is only 8-byte aligned (R/2 is a
+        // multiple of 8). A thread writes 8 or 16 bytes of a row: ordinary
+        // stores, so the pieces of a line meet in L2 before going to memory
+        // (streaming stores of such pieces each become a partial-line write,
+        // measured 3x slower).
+        uint8_t* out = pt + (c0 + c) * (R / 2) + r0 / 2;
+        u32x2 v2;
+        v2[0] = w[0];
+        v2[1] = w[1];
+        *reinterpret_cast<u32x2*>(out) = v2;
+        if (nb == 2) {
+            v2[0] = w[2];
+            v2[1] = w[3];
+            *reinterpret_cast<u32x2*>(out + 8) = v2;
+        }
     }
 }
 
@@ -618,7 +640,7 @@ void launch_t(const void* xv, int64_t R, int64_t C, int br, ScaleSrc src, uint8_
             k_nvfp4_1x16<T><<<grid, kWG, 0, stream>>>(x, n, src, p, codes, S_out, amax_out);
             wrote_scalars = true;
         } else if (R > 0 && C > 0) {
-            const int64_t grid = (R / 16) * cdiv(C, (int64_t)kWG * E);
+            const int64_t grid = std::min<int64_t>((R / 16) * cdiv(C, (int64_t)kWG * E), kMaxSlabGrid);
             k_nvfp4_16x16<T><<<(unsigned)grid, kWG, 0, stream>>>(x, R, C, src, p, codes, S_out, amax_out);
             wrote_scalars = true;
         }
@@ -639,7 +661,7 @@ void launch_t(const void* xv, int64_t R, int64_t C, int br, ScaleSrc src, uint8_
             else
                 k_nvfp4_colt<T, false, false><<<g1, kWG, 0, stream>>>(x, R, C, src, pt, codest, s2, a2, sd, of, sg);
         } else {
-            const int64_t grid = cdiv(R, 32) * cdiv(C, 256);
+            const int64_t grid = std::min<int64_t>(cdiv(R, 32) * cdiv(C, 256), kMaxSlabGrid);
             k_nvfp4_col<T, 16><<<(unsigned)grid, kWG, 0, stream>>>(x, R, C, src, pt, codest, s2, a2);
         }
         wrote_scalars = true;

@@ -58,11 +58,13 @@ def test_sizes_per_recipe():
     assert sizes(fq.FQ_PER_TENSOR_DELAYED, fq.FQ_E4M3, 8192, 4096).workspace == 4096
     z = sizes(fq.FQ_BLOCK_FP32, fq.FQ_E4M3, 16384, 7168, (1, 128), both)
     assert (z.row_data, z.row_scale) == (16384 * 7168, 16384 * 56 * 4)
-    assert (z.col_data, z.col_scale) == (16384 * 7168, 7168 * 128 * 4) and z.workspace == 0
+    # block and MX quantization need no workspace, but fq_amax on the same desc does
+    assert (z.col_data, z.col_scale) == (16384 * 7168, 7168 * 128 * 4) and z.workspace == 4096
     z = sizes(fq.FQ_BLOCK_FP32, fq.FQ_E4M3, 7168, 18432, (128, 128), both)
     assert (z.row_scale, z.col_scale) == (56 * 144 * 4, 144 * 56 * 4)
     z = sizes(fq.FQ_MX, fq.FQ_E4M3, 8192, 8192, (1, 32), both)
     assert (z.row_data, z.row_scale, z.col_data, z.col_scale) == (8192 ** 2, 8192 * 256, 8192 ** 2, 8192 * 256)
+    assert z.workspace == 4096
     z = sizes(fq.FQ_NVFP4, fq.FQ_E2M1, 8192, 14336, (1, 16), both)
     assert (z.row_data, z.row_scale) == (8192 * 7168, 8192 * 896)
     assert (z.col_data, z.col_scale) == (8192 * 7168, 14336 * 512) and z.workspace == 4096
@@ -216,6 +218,13 @@ def test_delayed_and_amax_checks(L):
     assert L.fq_amax(ctypes.byref(dc), B, None, B, 4096, None) == fq.FQ_E_INVALID
     assert L.fq_amax(ctypes.byref(dc), B, B + 1, B, 4096, None) == fq.FQ_E_ALIGN
     assert L.fq_amax(ctypes.byref(dc), B, B, B, 100, None) == fq.FQ_E_WORKSPACE
+    # fq_amax takes any desc; the workspace fq_sizes reports for it is enough
+    for dx in (fq.desc(fq.FQ_BLOCK_FP32, fq.FQ_IN_BF16, fq.FQ_E4M3, 128, 128, (1, 128)),
+               fq.desc(fq.FQ_MX, fq.FQ_IN_BF16, fq.FQ_E4M3, 64, 64, (1, 32))):
+        need = fq.fq_sizes(dx).workspace
+        assert need == 4096
+        assert L.fq_amax(ctypes.byref(dx), B, B, B, need - 1, None) == fq.FQ_E_WORKSPACE
+        assert L.fq_amax(ctypes.byref(dx), B, B, None, need, None) == fq.FQ_E_WORKSPACE
     db = fq.desc(fq.FQ_BLOCK_FP32, fq.FQ_IN_BF16, fq.FQ_E4M3, 128, 128, (1, 128))
     assert L.fq_quantize_with_amax(ctypes.byref(db), B, B, ctypes.byref(ok), None, 0, None) == fq.FQ_E_UNSUPPORTED
     assert L.fq_quantize_with_amax(ctypes.byref(dc), B, None, ctypes.byref(ok), None, 0, None) == fq.FQ_E_INVALID

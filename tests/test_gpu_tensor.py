@@ -139,6 +139,21 @@ def test_random_fp32_bit_patterns(fmt):
         same_bytes(host(out.row_data), want["q_row"], f"codes at amax {amax}")
 
 
+@pytest.mark.parametrize("recipe,fmt,block", [(fq.FQ_BLOCK_FP32, fq.FQ_E4M3, (1, 128)),
+                                               (fq.FQ_MX, fq.FQ_E4M3, (1, 32)),
+                                               (fq.FQ_NVFP4, fq.FQ_E2M1, (16, 16))])
+def test_fq_amax_any_desc_with_reported_workspace(recipe, fmt, block):
+    """fq_amax accepts any desc; the workspace fq_sizes reports for that desc
+    is enough, and the amax equals the oracle's."""
+    x = W.normal((256, 384), 1.0, 91, W.BF16)
+    d = fq.desc(recipe, fq.FQ_IN_BF16, fmt, 256, 384, block)
+    ws = torch.empty(fq.fq_sizes(d).workspace, dtype=torch.uint8, device="cuda")
+    a = torch.empty(1, dtype=torch.float32, device="cuda")
+    fq.fq_amax(d, dev(x), a, ws)
+    torch.cuda.synchronize()
+    same_bytes(host(a), f32(orc.amax(x)), "fq_amax")
+
+
 def test_sharded_amax_allgather_example():
     """Shards quantized with the max of their amaxes equal the whole tensor
     quantized at once (fq_amax, a max across shards, fq_quantize_with_amax)."""
