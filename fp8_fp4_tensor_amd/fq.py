@@ -81,6 +81,7 @@ def lib():
         "fq_quantize_delayed": (ctypes.c_int, [dp, _P, ctypes.POINTER(FqDelayedState), qp, _P, ctypes.c_size_t, _P]),
         "fq_dequantize": (ctypes.c_int, [dp, qp, ctypes.c_int32, _P, ctypes.c_int32, _P]),
         "fq_requantize_transpose": (ctypes.c_int, [dp, qp, qp, _P]),
+        "fq_quantize_noalloc": (ctypes.c_int, [dp, _P, qp, _P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -195,6 +196,13 @@ def fq_quantize(d: FqDesc, x: torch.Tensor, out: Quantized, ws: Optional[torch.T
     q = out.c()
     _check(lib().fq_quantize(ctypes.byref(d), _ptr(x), ctypes.byref(q), _ptr(ws),
                              0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)), "fq_quantize")
+
+
+def fq_quantize_noalloc(d: FqDesc, x: torch.Tensor, out: Quantized, stream=None):
+    """fq_quantize with the library's own per-GPU scratch array (no workspace)."""
+    q = out.c()
+    _check(lib().fq_quantize_noalloc(ctypes.byref(d), _ptr(x), ctypes.byref(q), _stream(stream)),
+           "fq_quantize_noalloc")
 
 
 def fq_amax(d: FqDesc, x: torch.Tensor, amax_out: torch.Tensor, ws: torch.Tensor, stream=None):

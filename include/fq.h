@@ -351,6 +351,21 @@ fq_status fq_dequantize(const fq_desc *desc, const fq_quantized *in, int32_t whi
 fq_status fq_requantize_transpose(const fq_desc *desc, const fq_quantized *in, const fq_quantized *out,
                                   hipStream_t stream);
 
+/*
+ * fq_quantize without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation. Same recipes, arguments, results and errors as
+ * fq_quantize. The scratch that fq_quantize takes from `workspace` (the amax
+ * partials of CURRENT and NVFP4) comes from a 4096-byte array that the
+ * library holds on each GPU it runs on, for the life of the process; the call
+ * itself allocates nothing. Returns FQ_E_WORKSPACE if a desc needs more
+ * scratch than that array holds (none does: every desc needs 4096 bytes or
+ * less, whatever its size). Calls on one stream are ordered and safe; calls
+ * that overlap in time on one GPU (unordered streams, several host threads)
+ * share that GPU's array and race: their results are undefined.
+ */
+fq_status fq_quantize_noalloc(const fq_desc *desc, const void *x, const fq_quantized *out, hipStream_t stream);
+
 /* A static, human-readable name for a status code. */
 const char *fq_status_str(fq_status status);
 
