@@ -81,6 +81,26 @@ def traffic_for(w, per_launch_alg_bytes):
     return t.get("hbm_bytes_per_launch")
 
 
+def rocprof_duration(w, kernel, per_launch_alg_bytes):
+    """The kernel's mean duration in the committed rocprofv3 kernel-trace
+    summary of the step (profiles/kernels_bench_step_all_workloads.json),
+    with the rate it gives, or None if there is none or the kernel's sources
+    changed since it was taken."""
+    path = os.path.join(PROFILES, "kernels_bench_step_all_workloads.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    from fp8_fp4_tensor_amd.profsum import source_hash
+    found = [(n, k) for n, k in t.get("kernels", {}).items() if n.split("<")[0] == kernel]
+    if len(found) != 1 or found[0][1].get("source_hash") != source_hash(KERNEL_FILES[w.recipe]):
+        return None
+    us = found[0][1]["mean_us"]
+    gbs = per_launch_alg_bytes / (us * 1e-6) / 1e9
+    return {"us_per_launch": us, "achieved": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "file": "profiles/kernels_bench_step_all_workloads.json"}
+
+
 COPY_BYTES = 256 << 20
 
 
@@ -147,39 +167,119 @@ def plain_copy(torch, stream, reps):
     return 2 * COPY_BYTES / t / 1e9
 
 
-def cpu_baseline(workloads, row_fraction):
-    """The oracle (single-threaded C) on the first rows of each workload."""
+# rows of a partition are a multiple of this, so every block (and every
+# colwise block down the columns) lies inside one partition
+PART_UNIT = {"current": 1, "delayed": 1, "mx": 32}
+
+
+def part_unit(w):
+    if w.recipe in PART_UNIT:
+        return PART_UNIT[w.recipe]
+    br = w.block[0]
+    if w.outputs & 2:                       # colwise blocks run down the columns
+        return max(br, w.block[1])
+    return br
+
+
+def row_parts(R, unit, parts):
+    """`parts` row ranges [r0, r1) of about equal size, cut at multiples of unit."""
+    units = R // unit
+    cuts = [unit * (units * k // parts) for k in range(parts + 1)]
+    cuts[-1] = R
+    return [(a, b) for a, b in zip(cuts[:-1], cuts[1:]) if b > a]
+
+
+def oracle_partitioned(w, x, parts, pool):
+    """The oracle on workload w's host input x, its rows split into `parts`
+    ranges run on `pool`'s threads (each oracle call releases the GIL).
+    Per-tensor amaxes are combined with an exact max before the cast, as the
+    sharded flow does. Returns the raw per-partition results."""
+    import oracle as orc
+
+    fmt = {"e4m3": orc.E4M3, "e5m2": orc.E5M2, "e2m1": orc.E2M1}[w.fmt]
+    rng = row_parts(x.shape[0], part_unit(w), parts)
+    xs = [x[a:b] for a, b in rng]
+
+    def amax_all():
+        return max(pool.map(orc.amax, xs))
+
+    if w.recipe == "current":
+        A = amax_all()
+        return [dict(r, amax=A) for r in pool.map(lambda xp: orc.quantize_with_amax(xp, fmt, A, outputs=w.outputs),
+                                                  xs)]
+    if w.recipe == "delayed":
+        st = orc.DelayedState(w.extra["history_len"])
+
+        def step(xp):
+            # every partition casts with the same old scale; its own copy of
+            # the state records its own amax
+            mine = st.copy()
+            return orc.quantize_delayed(xp, fmt, mine, outputs=w.outputs), mine
+        return list(pool.map(step, xs))
+    if w.recipe == "block":
+        return list(pool.map(lambda xp: orc.quantize_block(xp, w.block, outputs=w.outputs), xs))
+    if w.recipe == "mx":
+        return list(pool.map(lambda xp: orc.quantize_mx(xp, outputs=w.outputs, fmt=fmt), xs))
+    if w.recipe == "nvfp4":
+        A = amax_all()
+        return list(pool.map(lambda xp: orc.quantize_nvfp4(xp, w.block, outputs=w.outputs, amax=A), xs))
+    raise ValueError(w.recipe)
+
+
+def assemble(w, results):
+    """One tensor's outputs from per-partition results (rowwise planes stack
+    by rows; colwise planes, stored transposed, by columns)."""
     import numpy as np
 
-    import oracle as orc
+    if w.recipe == "delayed":
+        # the partition holding the largest amax made the whole tensor's update
+        best = max(results, key=lambda r: r[0]["amax"])
+        st = best[1]
+        return {"q_row": np.concatenate([r[0]["q_row"] for r in results]), "amax": best[0]["amax"],
+                "hist": st.hist, "alpha": st.alpha, "s": st.s}
+    out = {}
+    for k, v in results[0].items():
+        if v is None or np.ndim(v) == 0:
+            out[k] = v
+        elif k.endswith("_col"):
+            out[k] = np.concatenate([r[k] for r in results], axis=1)
+        else:
+            out[k] = np.concatenate([r[k] for r in results], axis=0)
+    return out
+
+
+def cpu_baseline(hosts, threads, one_thread_fraction):
+    """The oracle on the host: every workload of the step on all `threads`
+    (rows partitioned), and every workload on its first rows on one thread."""
+    import concurrent.futures
+
     from fp8_fp4_tensor_amd import workloads as W
 
-    total_bytes, total_t = 0, 0.0
-    for w in workloads:
-        R, C = w.shape
-        r = max(w.block[0] if w.block else 1, 16, int(R * row_fraction) // 128 * 128)
-        sub = W.Workload(w.name, (r, C), w.dtype, w.recipe, w.fmt, w.block, w.outputs, w.seed, w.dist, w.std,
-                         w.extra)
-        x = sub.make()
-        fmt = {"e4m3": orc.E4M3, "e5m2": orc.E5M2}.get(w.fmt)
-        t0 = time.perf_counter()
-        if w.recipe == "current":
-            orc.quantize_current(x, fmt)
-        elif w.recipe == "delayed":
-            orc.quantize_delayed(x, fmt, orc.DelayedState(w.extra["history_len"]))
-        elif w.recipe == "block":
-            orc.quantize_block(x, w.block)
-        elif w.recipe == "mx":
-            orc.quantize_mx(x, outputs=w.outputs)
-        elif w.recipe == "nvfp4":
-            orc.quantize_nvfp4(x, w.block)
-        total_t += time.perf_counter() - t0
-        total_bytes += algorithmic_bytes(sub)
-        del x
-    return {"value": round(total_bytes / total_t / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"every workload of one step on its first {row_fraction:.0%} of rows "
-                      f"({total_bytes / 1e9:.2f} GB algorithmic, {total_t:.1f} s, one thread of "
-                      f"{host_cpu()})"}
+    def run(parts, fraction):
+        total_bytes, total_t = 0, 0.0
+        with concurrent.futures.ThreadPoolExecutor(max_workers=parts) as pool:
+            for w, x in hosts:
+                R, C = w.shape
+                unit = max(part_unit(w), 128 if w.recipe == "block" else 1)
+                r = R if fraction >= 1 else max(unit, int(R * fraction) // unit * unit)
+                xs = x[:r]
+                sub = W.Workload(w.name, (r, C), w.dtype, w.recipe, w.fmt, w.block, w.outputs, w.seed, w.dist,
+                                 w.std, w.extra)
+                t0 = time.perf_counter()
+                oracle_partitioned(w, xs, parts, pool)
+                total_t += time.perf_counter() - t0
+                total_bytes += algorithmic_bytes(sub)
+        return total_bytes, total_t
+
+    nb, nt = run(threads, 1.0)
+    ob, ot = run(1, one_thread_fraction)
+    cpu = host_cpu()
+    return {"value": round(nb / nt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"every workload of one step, all rows, split by rows over {threads} threads "
+                      f"({nb / 1e9:.2f} GB algorithmic in {nt:.1f} s wall; {cpu})",
+            "one_thread": {"value": round(ob / ot / 1e9, 3), "cores": 1,
+                           "sample": f"every workload on its first {one_thread_fraction:.0%} of rows "
+                                     f"({ob / 1e9:.2f} GB in {ot:.1f} s)"}}
 
 
 def host_cpu():
@@ -326,6 +426,79 @@ def time_extras(torch, fq, L, stream_p, jobs, steps, flush):
     return out
 
 
+def time_current_split(torch, fq, L, stream_p, jobs, steps, flush):
+    """Current scaling's second read, with and without the memory-side cache:
+    fq_amax (pass 1), then fq_quantize_with_amax (pass 2) either right after
+    pass 1 (its input partly still in the 256 MB memory-side cache) or after
+    a flush (its input cold, every byte from HBM). Events bracket each pass;
+    the flush is outside them. No rocprofv3 counter on this chip separates
+    memory-side-cache hits from HBM reads, so this timing split is the
+    evidence of how much the cache serves."""
+    out = {}
+    for j in jobs:
+        w = j["w"]
+        if w.recipe != "current":
+            continue
+        d = j["d"]
+        amax = torch.empty(1, dtype=torch.float32, device="cuda")
+        ap = ctypes.c_void_p(amax.data_ptr())
+        ev = [[TimingEvent() for _ in range(4)] for _ in range(steps)]
+        for cold in (False, True):
+            for k in range(-1, steps):
+                flush()
+                e = ev[max(k, 0)]
+                if k >= 0:
+                    e[0].record()
+                rc = L.fq_amax(ctypes.byref(d), j["xp"], ap, j["wsp"], j["wsn"], stream_p)
+                if k >= 0:
+                    e[1].record()
+                if cold:
+                    flush()
+                if k >= 0:
+                    e[2].record()
+                rc |= L.fq_quantize_with_amax(ctypes.byref(d), j["xp"], ap, ctypes.byref(j["cq"]), j["wsp"],
+                                              j["wsn"], stream_p)
+                if k >= 0:
+                    e[3].record()
+                if rc != fq.FQ_OK:
+                    raise fq.FqError(rc, "current split " + w.name)
+            torch.cuda.synchronize()
+            p1 = 1e3 * sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+            p2 = 1e3 * sum(e[2].elapsed_time(e[3]) for e in ev) / steps
+            key = "pass2_cold_us" if cold else "pass2_after_pass1_us"
+            r = out.setdefault(w.name, {})
+            r[key] = round(p2, 2)
+            r.setdefault("pass1_us", round(p1, 2))
+        r = out[w.name]
+        R, C = w.shape
+        r["two_pass_hbm_only_GB/s"] = round(j["bytes"] / ((r["pass1_us"] + r["pass2_cold_us"]) * 1e-6) / 1e9, 1)
+        r["note"] = ("pass 1 = fq_amax (amax partials + their max), pass 2 = fq_quantize_with_amax; "
+                     f"{2 * R * C} B read by pass 2 alone")
+    return out
+
+
+def torch_cast_reference(torch, stream, steps, flush):
+    """torch's own bf16 -> float8_e4m3fn cast of an 8192x4096 tensor (2 bytes
+    read, 1 written per element, no amax, no scale): a 2:1 stream reference
+    from a library other than this one. Each cast starts cold."""
+    x = torch.randn(8192, 4096, device="cuda").to(torch.bfloat16)
+    y = torch.empty(8192, 4096, dtype=torch.float8_e4m3fn, device="cuda")
+    ev = [(TimingEvent(), TimingEvent()) for _ in range(steps)]
+    for k in range(-2, steps):
+        flush()
+        if k >= 0:
+            ev[k][0].record(stream)
+        y.copy_(x)
+        if k >= 0:
+            ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    us = 1e3 * sum(a.elapsed_time(b) for a, b in ev) / steps
+    nbytes = 3 * x.numel()
+    del x, y
+    return {"what": "torch bf16 -> float8_e4m3fn copy_, 8192x4096, cold input", "us": round(us, 2),
+            "bytes": nbytes, "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1)}
+
+
 def time_small(torch, fq, L, stream_p, steps, flush):
     """The small per-tensor workload (2^20 fp32 with outliers, current
     scaling to E4M3): a few MiB, so launch latency bounds it; each call
@@ -362,7 +535,12 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=float, default=0.6, help="row fraction for the oracle baseline")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="host threads of the all-core oracle baseline (default: the host's CPUs, at most 16)")
+    ap.add_argument("--cpu-rows", type=float, default=0.2,
+                    help="row fraction of the one-thread oracle baseline")
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="per-recipe figures: median over this many repeats of K calls")
     ap.add_argument("--only", default="", help="comma-separated workload names (profiling runs)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the dequantize / requantize timings reported beside the step")
@@ -411,7 +589,12 @@ def main():
         # the C arguments, built once: each call below is one ctypes call into libfq.so
         j = dict(w=w, x=xd, d=d, out=out, ws=ws, st=st, bytes=algorithmic_bytes(w), cq=out.c(),
                  xp=ctypes.c_void_p(xd.data_ptr()), wsp=ctypes.c_void_p(ws.data_ptr()) if ws is not None else None,
-                 wsn=0 if ws is None else ws.numel(), cst=st.c() if st is not None else None)
+                 wsn=0 if ws is None else ws.numel(), cst=st.c() if st is not None else None,
+                 xh=None if args.no_cpu_baseline else x)   # host copy for the oracle baseline
+        if w.recipe == "delayed":
+            # a step's outputs are its codes, the s used, the window and the
+            # scales; the optional a_t output would add a kernel
+            j["cq"].amax = None
         jobs.append(j)
         del x
     print(f"bench: {len(jobs)} workloads resident, {sum(j['x'].numel() * 2 for j in jobs) / 2**30:.2f} GiB input",
@@ -432,23 +615,29 @@ def main():
             call(j)
     torch.cuda.synchronize()
 
-    # per-recipe breakdown: K instrumented steps, every call bracketed by events
-    # (each call starts with its input cold, as in the timed region below)
-    for j in jobs:
-        j["events"] = [(TimingEvent(), TimingEvent())
-                       for _ in range(args.steps)]
-    for k in range(args.steps):
+    # per-recipe breakdown: `repeats` rounds of K instrumented steps, every
+    # call bracketed by fence-free events (each call starts with its input
+    # cold, as in the timed region below); each workload's figure is the
+    # median over the rounds of its mean time per call
+    rounds = {j["w"].name: [] for j in jobs}
+    for _ in range(max(1, args.repeats)):
         for j in jobs:
-            j["events"][k][0].record(stream)
-            call(j)
-            j["events"][k][1].record(stream)
-    torch.cuda.synchronize()
+            j["events"] = [(TimingEvent(), TimingEvent()) for _ in range(args.steps)]
+        for k in range(args.steps):
+            for j in jobs:
+                j["events"][k][0].record(stream)
+                call(j)
+                j["events"][k][1].record(stream)
+        torch.cuda.synchronize()
+        for j in jobs:
+            rounds[j["w"].name].append(1e3 * sum(a.elapsed_time(b) for a, b in j["events"]) / args.steps)
     per = {}
     for j in jobs:
-        us = 1e3 * sum(a.elapsed_time(b) for a, b in j["events"]) / args.steps
+        us = float(np.median(rounds[j["w"].name]))
         gbs = j["bytes"] / (us * 1e-6) / 1e9
         per[j["w"].name] = {"us_per_call": round(us, 2), "GB/s": round(gbs, 1),
-                            "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 1), "bytes": j["bytes"],
+                            "alg_pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 1), "bytes": j["bytes"],
+                            "us_rounds": [round(v, 2) for v in rounds[j["w"].name]],
                             "kernels": 2 if j["w"].recipe in ("current", "nvfp4", "delayed") else 1}
     # the dominant kernel: the single-kernel workload with the largest time per call
     single = [j for j in jobs if per[j["w"].name]["kernels"] == 1]
@@ -479,11 +668,15 @@ def main():
     if dom is not None:
         us = 1e3 * sum(a.elapsed_time(b) for a, b in dom_events) / args.steps
         gbs = dom["bytes"] / (us * 1e-6) / 1e9
-        roofline = {"kernel": KERNEL_NAMES[kernel_key(dom["w"])], "workload": dom["w"].name, "bound": "hbm",
+        kname = KERNEL_NAMES[kernel_key(dom["w"])]
+        roofline = {"kernel": kname, "workload": dom["w"].name, "bound": "hbm",
                     "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(gbs / HBM_PEAK_GBS, 4),
                     "traffic": traffic_for(dom["w"], dom["bytes"]),
-                    "alg_bytes_per_launch": dom["bytes"], "us_per_launch": round(us, 2)}
+                    "alg_bytes_per_launch": dom["bytes"], "us_per_launch": round(us, 2),
+                    "duration_source": "mean of fence-free HIP events around each launch inside the timed "
+                                       "region, on the launch stream",
+                    "rocprof": rocprof_duration(dom["w"], kname, dom["bytes"])}
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -492,26 +685,33 @@ def main():
         "config": {"workload": "one step = every large workload once: " + ", ".join(j["w"].name for j in jobs),
                    "bytes_per_step": step_bytes, "input": "bf16",
                    "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1)},
+        "per_recipe_basis": ("algorithmic bytes (one read of the input per pass the method makes, plus every "
+                             "byte written) / median event time per call; a second read served by the "
+                             "memory-side cache counts as a full read, so these are algorithmic-byte rates, "
+                             "not measured HBM traffic"),
         "per_recipe": per,
         "roofline": roofline,
         "copy_reference_GBps": round(copy_gbs, 1),
     }
+    # each reference or extra call starts cold, like the step's: 512 MiB read
+    # between calls (outside the events) evicts the 256 MB memory-side cache
+    # and L2 and leaves clean lines (a write would leave dirty ones for the
+    # timed call to write back)
+    scratch = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda")
+
+    def flush():
+        torch.amax(scratch)
+
+    result["torch_cast_reference"] = torch_cast_reference(torch, stream, args.steps, flush)
     if not args.no_extras:
-        # each extra call starts cold, like the step's: 512 MiB read between
-        # calls (outside the events) evicts the 256 MB memory-side cache and L2
-        # and leaves clean lines (a write would leave dirty ones for the timed
-        # call to write back)
-        scratch = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda")
-
-        def flush():
-            torch.amax(scratch)
-
+        result["current_scaling_second_read"] = time_current_split(torch, fq, L, sp, jobs, args.steps, flush)
         result["dequant_requant"] = time_extras(torch, fq, L, sp, jobs, args.steps, flush)
         result["small"] = time_small(torch, fq, L, sp, args.steps, flush)
-        del scratch
+    del scratch
     if not args.no_cpu_baseline:
         print("bench: timing the oracle on the host", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline([j["w"] for j in jobs], args.cpu_rows)
+        threads = args.cpu_threads or min(os.cpu_count() or 1, 16)
+        result["cpu_baseline"] = cpu_baseline([(j["w"], j["xh"]) for j in jobs], threads, args.cpu_rows)
     print(json.dumps(result), flush=True)
 
 

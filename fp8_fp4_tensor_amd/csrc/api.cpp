@@ -20,6 +20,7 @@ using namespace fq;
 // a capped grid; every other tiled kernel's grid stays below 2^32
 // work-items at this size (the widest, 128x64 tiles, needs 2^31).
 constexpr int64_t kMaxElems = int64_t(1) << 36;
+static_assert(kPendingBytes == FQ_DELAYED_PENDING_BYTES, "the pending records' size is part of the ABI");
 constexpr int32_t kMaxHistory = 1 << 24;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -132,9 +133,9 @@ Sizes sizes_of(const fq_desc* d)
         z.ws = kPartialsBytes;
         break;
     case FQ_PER_TENSOR_DELAYED:
+        // the amax partials live in the state's pending records
         z.row_data = row ? R * C : 0;
         z.col_data = col ? R * C : 0;
-        z.ws = kPartialsBytes;
         break;
     case FQ_BLOCK_FP32:
         z.row_data = row ? R * C : 0;
@@ -219,19 +220,52 @@ fq_status hip_status(hipError_t e) { return e == hipSuccess ? FQ_OK : FQ_E_HIP; 
 
 int elem_bytes(const fq_desc* d) { return d->in_dtype == FQ_IN_BF16 ? 2 : 4; }
 
-// Per-tensor cast (current, with a given amax, or delayed) of a validated desc.
-fq_status run_per_tensor_cast(const fq_desc* d, const void* x, ScaleSrc src, const fq_quantized* o, float* s_out,
-                              float* amax_out, float* partials_out, int grid, hipStream_t st)
+// Per-tensor current-scaling cast (amax from partials or given) of a validated desc.
+fq_status run_per_tensor_cast(const fq_desc* d, const void* x, ScaleSrc src, const fq_quantized* o, hipStream_t st)
 {
     const int bf = d->in_dtype == FQ_IN_BF16;
     const int64_t n = d->rows * d->cols;
     uint8_t* q = (d->outputs & FQ_ROWWISE) ? (uint8_t*)o->rowwise.data : nullptr;
     uint8_t* qt = (d->outputs & FQ_COLWISE) ? (uint8_t*)o->colwise.data : nullptr;
     if (qt)
-        return hip_status(launch_cast_tensor_2d(x, bf, d->format, d->rows, d->cols, src, q, qt, s_out, amax_out,
-                                                partials_out, grid, st));
-    return hip_status(launch_cast_tensor(x, bf, d->format, n, src, q, s_out, amax_out, partials_out, grid, st));
+        return hip_status(launch_cast_tensor_2d(x, bf, d->format, d->rows, d->cols, src, q, qt, o->tensor_scale,
+                                                o->amax, st));
+    return hip_status(launch_cast_tensor(x, bf, d->format, n, src, q, o->tensor_scale, o->amax, st));
 }
+
+// A delayed state's fields, present, aligned and in range.
+fq_status check_state(const fq_delayed_state* state)
+{
+    if (!state || !state->amax_history || !state->scale || !state->scale_inv || !state->pending)
+        return FQ_E_INVALID;
+    if (state->history_len < 1 || state->history_len > kMaxHistory || state->step < 0)
+        return FQ_E_INVALID;
+    if (!aligned(state->amax_history, 4) || !aligned(state->scale, 4) || !aligned(state->scale_inv, 4) ||
+        !aligned(state->pending, 16))
+        return FQ_E_ALIGN;
+    return FQ_OK;
+}
+
+float* record_of(const fq_delayed_state* state, int64_t step)
+{
+    return state->pending + (step & 1) * kRecordFloats;
+}
+
+// The tag of step t's record: (t mod L) + 1 with L = lcm(2, H), the period
+// of the window slot and of the record's parity, so every argument of a
+// step's kernels repeats with period L (a step captured in a graph replays
+// correctly L steps later), and never 0 (a zero-filled record is never
+// taken for a step's); then a constant word.
+constexpr uint32_t kRecordMagic = 0x46510D1Au;
+
+void record_tag(int64_t t, int64_t H, uint32_t tag[2])
+{
+    const int64_t L = (H % 2 == 0) ? H : 2 * H;
+    tag[0] = (uint32_t)(t % L) + 1u;
+    tag[1] = kRecordMagic;
+}
+
+float fmax_of(const fq_desc* d) { return d->format == FQ_E4M3 ? 448.0f : 57344.0f; }
 
 }  // namespace
 
@@ -343,7 +377,7 @@ fq_status fq_quantize(const fq_desc* d, const void* x, const fq_quantized* o, vo
         ScaleSrc src;
         src.partials = partials;
         src.n_partials = g;
-        return run_per_tensor_cast(d, x, src, o, o->tensor_scale, o->amax, nullptr, 0, st);
+        return run_per_tensor_cast(d, x, src, o, st);
     }
     case FQ_BLOCK_FP32: {
         if (n == 0)
@@ -419,7 +453,7 @@ fq_status fq_quantize_with_amax(const fq_desc* d, const void* x, const float* am
     ScaleSrc src;
     src.amax_in = amax_in;
     if (d->recipe == FQ_PER_TENSOR_CURRENT)
-        return run_per_tensor_cast(d, x, src, o, o->tensor_scale, o->amax, nullptr, 0, st);
+        return run_per_tensor_cast(d, x, src, o, st);
     const bool row = d->outputs & FQ_ROWWISE, col = d->outputs & FQ_COLWISE;
     return hip_status(launch_nvfp4(x, d->in_dtype == FQ_IN_BF16, d->rows, d->cols, d->block_rows, src,
                                    row ? (uint8_t*)o->rowwise.data : nullptr,
@@ -432,36 +466,67 @@ fq_status fq_quantize_with_amax(const fq_desc* d, const void* x, const float* am
 fq_status fq_quantize_delayed(const fq_desc* d, const void* x, const fq_delayed_state* state,
                               const fq_quantized* o, void* ws, size_t ws_bytes, hipStream_t st)
 {
+    (void)ws;
+    (void)ws_bytes;
     fq_status s = check_desc(d);
     if (s != FQ_OK)
         return s;
     if (d->recipe != FQ_PER_TENSOR_DELAYED)
         return FQ_E_UNSUPPORTED;
-    if (!state || !state->amax_history || !state->scale || !state->scale_inv)
-        return FQ_E_INVALID;
-    if (state->history_len < 1 || state->history_len > kMaxHistory || state->step < 0)
-        return FQ_E_INVALID;
-    if (!aligned(state->amax_history, 4) || !aligned(state->scale, 4) || !aligned(state->scale_inv, 4))
-        return FQ_E_ALIGN;
+    if ((s = check_state(state)) != FQ_OK)
+        return s;
     if ((s = check_x(d, x)) != FQ_OK)
         return s;
     if ((s = check_out(d, o, false)) != FQ_OK)
         return s;
-    const Sizes z = sizes_of(d);
-    if ((s = check_ws(z, ws, ws_bytes)) != FQ_OK)
+    const int64_t t = state->step, H = state->history_len;
+    DelayedArgs dl;
+    dl.hist = state->amax_history;
+    dl.H = (int)H;
+    dl.alpha = state->scale;
+    dl.s = state->scale_inv;
+    dl.fmax = fmax_of(d);
+    dl.rec = record_of(state, t);
+    record_tag(t, H, dl.tag);
+    dl.s_used = o->tensor_scale;
+    const bool fold = H <= kFoldMaxHistory;
+    if (fold && t >= 1) {
+        // this step first finishes step t-1 from its record
+        dl.prev = record_of(state, t - 1);
+        dl.prev_slot = (int)((t - 1) % H);
+        record_tag(t - 1, H, dl.prev_tag);
+    }
+    uint8_t* q = (d->outputs & FQ_ROWWISE) ? (uint8_t*)o->rowwise.data : nullptr;
+    uint8_t* qt = (d->outputs & FQ_COLWISE) ? (uint8_t*)o->colwise.data : nullptr;
+    if ((s = hip_status(launch_cast_delayed(x, d->in_dtype == FQ_IN_BF16, d->format, d->rows, d->cols, dl, q, qt,
+                                            st))) != FQ_OK)
         return s;
-    const int64_t n = d->rows * d->cols;
-    float* partials = (float*)ws;
-    const int g = amax_grid(n, elem_bytes(d), kMaxPartials);
-    ScaleSrc src;
-    src.alpha_in = state->scale;
-    src.s_in = state->scale_inv;
-    if ((s = run_per_tensor_cast(d, x, src, o, o->tensor_scale, nullptr, partials, g, st)) != FQ_OK)
+    if (!fold)
+        // a long window: this step's update runs now, as its own kernel
+        return hip_status(launch_delayed_finish(dl.rec, dl.tag[0], dl.tag[1], dl.hist, dl.H, (int)(t % H), dl.alpha,
+                                                dl.s, dl.fmax, o->amax, st));
+    if (o->amax)
+        return hip_status(launch_amax_finish(dl.rec, kMaxPartials, o->amax, st));
+    return FQ_OK;
+}
+
+fq_status fq_delayed_flush(const fq_desc* d, const fq_delayed_state* state, hipStream_t st)
+{
+    fq_status s = check_desc(d);
+    if (s != FQ_OK)
         return s;
-    const int slot = (int)(state->step % state->history_len);
-    const float fmax_v = d->format == FQ_E4M3 ? 448.0f : 57344.0f;
-    return hip_status(launch_delayed_finish(partials, g, state->amax_history, state->history_len, slot,
-                                            state->scale, state->scale_inv, fmax_v, o->amax, st));
+    if (d->recipe != FQ_PER_TENSOR_DELAYED)
+        return FQ_E_UNSUPPORTED;
+    if ((s = check_state(state)) != FQ_OK)
+        return s;
+    const int64_t t = state->step, H = state->history_len;
+    if (t == 0)
+        return FQ_OK;  // no step has run
+    uint32_t tag[2];
+    record_tag(t - 1, H, tag);
+    return hip_status(launch_delayed_finish(record_of(state, t - 1), tag[0], tag[1], state->amax_history, (int)H,
+                                            (int)((t - 1) % H), state->scale, state->scale_inv, fmax_of(d), nullptr,
+                                            st));
 }
 
 fq_status fq_dequantize(const fq_desc* d, const fq_quantized* in, int32_t which, void* y, int32_t y_dtype,

@@ -368,6 +368,36 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_1x16(const T* __restrict__ x, int
     }
 }
 
+// One 16-row strip of a 16x16 pass: lane E-column group at column c, loads
+// v[16] already issued. Block amax over the lane pair, then codes and nibbles.
+template <typename T>
+__device__ __forceinline__ void strip_16x16(const u32x4* v, int64_t r0, int64_t c, int64_t C, float alpha_s,
+                                            const float* rtab, uint8_t* __restrict__ p, uint8_t* __restrict__ codes)
+{
+    constexpr int E = In<T>::kE, LPB = 16 / E;
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        float f[E];
+        In<T>::unpack(v[i], f);
+        m = fmaxf(m, absmax<E>(f));
+    }
+    const float a = max_lanes<LPB>(m);
+    uint32_t code;
+    float r;
+    nvfp4_block(a, alpha_s, rtab, code, r);
+    if (c >= C)
+        return;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        float f[E];
+        In<T>::unpack(v[i], f);
+        Fp4Store<E>::store(p + (r0 + i) * (C / 2) + c / 2, f, r);
+    }
+    if ((threadIdx.x & (LPB - 1)) == 0)
+        codes[(r0 / 16) * (C / 16) + c / 16] = (uint8_t)code;
+}
+
 template <typename T>
 __global__ __launch_bounds__(kWG) void k_nvfp4_16x16(const T* __restrict__ x, int64_t R, int64_t C, ScaleSrc src,
                                                      uint8_t* __restrict__ p, uint8_t* __restrict__ codes,
@@ -375,19 +405,18 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_16x16(const T* __restrict__ x, in
 {
     __shared__ float lds[4];
     __shared__ float rtab[128];
-    constexpr int E = In<T>::kE, LPB = 16 / E, WC = kWG * E;  // columns per workgroup
+    constexpr int E = In<T>::kE, WC = kWG * E;  // columns per workgroup
     const int64_t nwc = cdiv(C, WC), nstrips = (R / 16) * nwc;
-    // workgroups stride over the 16-row strips (one each at the usual
-    // shapes; the grid is capped); the first strip's loads go out before the
-    // tensor scale is resolved, so the partials' round trip overlaps them
+    // one 16-row strip per workgroup (the grid is capped, so beyond 2^16
+    // strips workgroups go on to further strips); the first strip's loads go
+    // out before the tensor scale is resolved, so the partials' round trip
+    // overlaps them
     int64_t t = blockIdx.x;
+    int64_t r0 = (t / nwc) * 16, c = (t % nwc) * WC + (int64_t)threadIdx.x * E;
     u32x4 v[16];
-    {
-        const int64_t r0 = (t / nwc) * 16, c = (t % nwc) * WC + (int64_t)threadIdx.x * E;
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-            v[i] = (t < nstrips && c < C) ? ld16_stream(x + (r0 + i) * C + c) : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int i = 0; i < 16; ++i)
+        v[i] = c < C ? ld16_stream(x + (r0 + i) * C + c) : u32x4{0u, 0u, 0u, 0u};
     float alpha_s, S, A;
     nvfp4_tensor(src, lds, rtab, alpha_s, S, A);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -396,35 +425,14 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_16x16(const T* __restrict__ x, in
         if (amax_out)
             *amax_out = A;
     }
-    for (; t < nstrips; t += gridDim.x) {
-        const int64_t r0 = (t / nwc) * 16, c = (t % nwc) * WC + (int64_t)threadIdx.x * E;
-        const bool in = c < C;
-        if (t != blockIdx.x) {
+    strip_16x16<T>(v, r0, c, C, alpha_s, rtab, p, codes);
+    for (t += gridDim.x; t < nstrips; t += gridDim.x) {
+        r0 = (t / nwc) * 16;
+        c = (t % nwc) * WC + (int64_t)threadIdx.x * E;
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-                v[i] = in ? ld16_stream(x + (r0 + i) * C + c) : u32x4{0u, 0u, 0u, 0u};
-        }
-        float m = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float f[E];
-            In<T>::unpack(v[i], f);
-            m = fmaxf(m, absmax<E>(f));
-        }
-        const float a = max_lanes<LPB>(m);
-        uint32_t code;
-        float r;
-        nvfp4_block(a, alpha_s, rtab, code, r);
-        if (!in)
-            continue;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float f[E];
-            In<T>::unpack(v[i], f);
-            Fp4Store<E>::store(p + (r0 + i) * (C / 2) + c / 2, f, r);
-        }
-        if ((threadIdx.x & (LPB - 1)) == 0)
-            codes[(r0 / 16) * (C / 16) + c / 16] = (uint8_t)code;
+        for (int i = 0; i < 16; ++i)
+            v[i] = c < C ? ld16_stream(x + (r0 + i) * C + c) : u32x4{0u, 0u, 0u, 0u};
+        strip_16x16<T>(v, r0, c, C, alpha_s, rtab, p, codes);
     }
 }
 

@@ -18,6 +18,14 @@
 // LDS across 4 waves), and every workgroup of the cast pass re-reduces those
 // few KiB of partials itself (they stay in L2), so no atomics and no third
 // kernel are needed and the result does not depend on scheduling order.
+//
+// Delayed scaling is one pass per step: the cast uses the scale the window
+// gave after the previous step and writes this step's amax partials into a
+// record in the caller's state. The window update of step t-1 (record its
+// amax, new scale from the window's max) is folded into step t's cast: every
+// workgroup re-reduces step t-1's record and the window from L2 to get the
+// scale it casts with, and workgroup 0 alone writes the window slot and the
+// new scale back. So a step is one kernel, with no separate finish launch.
 #include <algorithm>
 
 #include "codec.hpp"
@@ -60,12 +68,6 @@ __global__ __launch_bounds__(kWG) void k_amax_partial(const T* __restrict__ x, i
 template <int FMT>
 __device__ __forceinline__ void resolve_scale(const ScaleSrc& src, float* lds, float& alpha, float& s, float& a)
 {
-    if (src.alpha_in) {
-        alpha = *src.alpha_in;
-        s = *src.s_in;
-        a = 0.0f;
-        return;
-    }
     if (src.amax_in) {
         a = *src.amax_in;
     } else {
@@ -75,12 +77,84 @@ __device__ __forceinline__ void resolve_scale(const ScaleSrc& src, float* lds, f
     tensor_scales(a, Fmt<FMT>::kMax, alpha, s);
 }
 
-// q = Q(fp32(alpha * x)) over a flat tensor; optionally one amax partial per
-// workgroup (delayed scaling casts and records the amax in the same read).
+// Delayed scaling, start of step t: finish step t-1 from its record (if
+// dl.prev and the record carries step t-1's tag), giving the scale this
+// step casts with; otherwise cast with the state's scale. Every workgroup
+// computes the same values; workgroup 0 writes them back (window slot, new
+// alpha and s, the s used). All loads (record, tag, window, state scale)
+// are issued together: one memory latency. `lds` holds 8 floats. Uniform
+// control flow (contains __syncthreads).
+__device__ __forceinline__ void delayed_prologue(const DelayedArgs& dl, float* lds, float& alpha, float& s)
+{
+    const float a0 = *dl.alpha, s0 = *dl.s;
+    float mp = 0.0f, mh = 0.0f;
+    bool apply = false;
+    if (dl.prev) {
+        const uint32_t* tag = reinterpret_cast<const uint32_t*>(dl.prev + kMaxPartials);
+        const uint32_t t0 = tag[0], t1 = tag[1];
+        float h[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int i = (int)threadIdx.x + k * kWG;
+            h[k] = (i < dl.H && i != dl.prev_slot) ? dl.hist[i] : 0.0f;
+        }
+        mp = partials_max(dl.prev, kMaxPartials);
+        mh = fmaxf(fmaxf(h[0], h[1]), fmaxf(h[2], h[3]));
+        apply = t0 == dl.prev_tag[0] && t1 == dl.prev_tag[1];
+    }
+    mp = max_wave(mp);
+    mh = max_wave(mh);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) {
+        lds[w] = mp;
+        lds[4 + w] = mh;
+    }
+    __syncthreads();
+    const float a_prev = fmaxf(fmaxf(lds[0], lds[1]), fmaxf(lds[2], lds[3]));
+    const float m = fmaxf(fmaxf(fmaxf(lds[4], lds[5]), fmaxf(lds[6], lds[7])), a_prev);
+    if (apply && m > 0.0f) {
+        tensor_scales(m, dl.fmax, alpha, s);
+    } else {
+        alpha = a0;
+        s = s0;
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (apply) {
+            dl.hist[dl.prev_slot] = a_prev;
+            if (m > 0.0f) {
+                *dl.alpha = alpha;
+                *dl.s = s;
+            }
+        }
+        if (dl.s_used)
+            *dl.s_used = s;
+    }
+}
+
+// Delayed scaling, end of step t: this workgroup's amax into the step's
+// record; workgroup 0 also zeroes the slots beyond the grid and writes the
+// tag. Uniform control flow.
+__device__ __forceinline__ void delayed_epilogue(const DelayedArgs& dl, float m, float* lds)
+{
+    m = max_workgroup(m, lds);
+    if (threadIdx.x == 0)
+        dl.rec[blockIdx.x] = m;
+    if (blockIdx.x == 0) {
+        for (int i = (int)gridDim.x + (int)threadIdx.x; i < kMaxPartials; i += kWG)
+            dl.rec[i] = 0.0f;
+        if (threadIdx.x == 0) {
+            uint32_t* tag = reinterpret_cast<uint32_t*>(dl.rec + kMaxPartials);
+            tag[0] = dl.tag[0];
+            tag[1] = dl.tag[1];
+        }
+    }
+}
+
+// q = Q(fp32(alpha * x)) over a flat tensor, current scaling.
 template <typename T, int FMT, int L>
 __global__ __launch_bounds__(kWG) void k_cast_tensor(const T* __restrict__ x, int64_t n, ScaleSrc src,
-                                                     uint8_t* __restrict__ q, float* s_out, float* amax_out,
-                                                     float* partials_out)
+                                                     uint8_t* __restrict__ q, float* s_out, float* amax_out)
 {
     __shared__ float lds[4];
     constexpr int E = In<T>::kE, U = 64 * E;
@@ -103,7 +177,46 @@ __global__ __launch_bounds__(kWG) void k_cast_tensor(const T* __restrict__ x, in
         if (amax_out)
             *amax_out = a;
     }
-    const bool want_amax = partials_out != nullptr;
+    for (; u0 < nunits; u0 += nwaves * L) {
+        if (u0 != wave * L) {
+#pragma unroll
+            for (int j = 0; j < L; ++j)
+                v[j] = (u0 + j < nunits) ? ld16_stream(x + (u0 + j) * U + lane * E) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            if (u0 + j < nunits) {
+                float f[E];
+                In<T>::unpack(v[j], f);
+                Enc8<FMT, E>::store(q + (u0 + j) * U + lane * E, f, alpha);
+            }
+        }
+    }
+    for (int64_t i = nunits * U + (int64_t)blockIdx.x * kWG + threadIdx.x; i < n; i += (int64_t)gridDim.x * kWG)
+        q[i] = enc1<FMT>(In<T>::load1(x, i), alpha);
+}
+
+// One delayed-scaling step over a flat tensor: finish step t-1 (prologue),
+// q = Q(fp32(alpha * x)) and the amax in the same read, this step's record
+// (epilogue). The first loads go out before the prologue's loads, so its
+// round trip overlaps them.
+template <typename T, int FMT, int L>
+__global__ __launch_bounds__(kWG) void k_cast_delayed(const T* __restrict__ x, int64_t n, DelayedArgs dl,
+                                                      uint8_t* __restrict__ q)
+{
+    __shared__ float lds[8];
+    constexpr int E = In<T>::kE, U = 64 * E;
+    const int lane = threadIdx.x & 63;
+    const int64_t nunits = n / U;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    u32x4 v[L];
+    int64_t u0 = wave * L;
+#pragma unroll
+    for (int j = 0; j < L; ++j)
+        v[j] = (u0 + j < nunits) ? ld16_stream(x + (u0 + j) * U + lane * E) : u32x4{0u, 0u, 0u, 0u};
+    float alpha, s;
+    delayed_prologue(dl, lds, alpha, s);
     float m = 0.0f;
     for (; u0 < nunits; u0 += nwaves * L) {
         if (u0 != wave * L) {
@@ -116,43 +229,54 @@ __global__ __launch_bounds__(kWG) void k_cast_tensor(const T* __restrict__ x, in
             if (u0 + j < nunits) {
                 float f[E];
                 In<T>::unpack(v[j], f);
-                if (want_amax)
-                    m = fmaxf(m, absmax<E>(f));
+                m = fmaxf(m, absmax<E>(f));
                 Enc8<FMT, E>::store(q + (u0 + j) * U + lane * E, f, alpha);
             }
         }
     }
     for (int64_t i = nunits * U + (int64_t)blockIdx.x * kWG + threadIdx.x; i < n; i += (int64_t)gridDim.x * kWG) {
-        const float v = In<T>::load1(x, i);
-        m = fmaxf(m, fabsf(v));
-        q[i] = enc1<FMT>(v, alpha);
+        const float v1 = In<T>::load1(x, i);
+        m = fmaxf(m, fabsf(v1));
+        q[i] = enc1<FMT>(v1, alpha);
     }
-    if (want_amax) {
-        m = max_workgroup(m, lds);
-        if (threadIdx.x == 0)
-            partials_out[blockIdx.x] = m;
+    delayed_epilogue(dl, m, lds);
+}
+
+// The scale of a per-tensor tile cast: current scaling from src (writing s
+// and the amax), or a delayed step's prologue. Uniform control flow.
+template <int FMT, bool DELAYED>
+__device__ __forceinline__ void tile_cast_scale(const ScaleSrc& src, const DelayedArgs& dl, float* lds,
+                                                float* s_out, float* amax_out, float& alpha)
+{
+    float s;
+    if constexpr (DELAYED) {
+        delayed_prologue(dl, lds, alpha, s);
+    } else {
+        float a;
+        resolve_scale<FMT>(src, lds, alpha, s, a);
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            if (s_out)
+                *s_out = s;
+            if (amax_out)
+                *amax_out = a;
+        }
     }
 }
 
 // Per-tensor cast through 64x64 tiles, for the transposed (colwise) copy:
 // rowwise bytes q[r*C + c] and transposed bytes qt[c*R + r] from one read.
-// Byte-granular and bounds-checked: any shape.
-template <typename T, int FMT>
+// Byte-granular and bounds-checked: any shape. Current scaling, or one
+// delayed-scaling step (then one amax partial per workgroup into the step's
+// record).
+template <typename T, int FMT, bool DELAYED>
 __global__ __launch_bounds__(kWG) void k_cast_tensor_2d(const T* __restrict__ x, int64_t R, int64_t C,
-                                                        ScaleSrc src, uint8_t* __restrict__ q,
-                                                        uint8_t* __restrict__ qt, float* s_out, float* amax_out,
-                                                        float* partials_out)
+                                                        ScaleSrc src, DelayedArgs dl, uint8_t* __restrict__ q,
+                                                        uint8_t* __restrict__ qt, float* s_out, float* amax_out)
 {
-    __shared__ float lds[4];
+    __shared__ float lds[8];
     __shared__ uint8_t tile[64][68];
-    float alpha, s, a;
-    resolve_scale<FMT>(src, lds, alpha, s, a);
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        if (s_out)
-            *s_out = s;
-        if (amax_out)
-            *amax_out = a;
-    }
+    float alpha;
+    tile_cast_scale<FMT, DELAYED>(src, dl, lds, s_out, amax_out, alpha);
     const int64_t tcols = (C + 63) / 64, ntiles = ((R + 63) / 64) * tcols;
     float m = 0.0f;
     for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
@@ -183,38 +307,29 @@ __global__ __launch_bounds__(kWG) void k_cast_tensor_2d(const T* __restrict__ x,
             }
         }
     }
-    if (partials_out) {
-        m = max_workgroup(m, lds);
-        if (threadIdx.x == 0)
-            partials_out[blockIdx.x] = m;
-    }
+    if constexpr (DELAYED)
+        delayed_epilogue(dl, m, lds);
 }
 
 // Per-tensor cast with the colwise copy, for R % 16 == 0 and C % 16 == 0:
 // 128x128 tiles, workgroups striding over tiles; 16-byte loads, rowwise
 // codes stored from registers, and the transposed codes through an LDS tile
 // XOR-swizzled in 8-byte units by 16-row group, written with eight lanes per
-// 128-byte row of X^T (edge tiles: rows of X^T of rows_in bytes). Optionally
-// one amax partial per workgroup (delayed scaling).
+// 128-byte row of X^T (edge tiles: rows of X^T of rows_in bytes). Current
+// scaling, or one delayed-scaling step (then one amax partial per workgroup
+// into the step's record).
 __device__ __forceinline__ int tile_swizzle(int r) { return 8 * ((r >> 4) & 7); }
 
-template <typename T, int FMT>
+template <typename T, int FMT, bool DELAYED>
 __global__ __launch_bounds__(kWG) void k_cast_tensor_tile(const T* __restrict__ x, int64_t R, int64_t C,
-                                                          ScaleSrc src, uint8_t* __restrict__ q,
-                                                          uint8_t* __restrict__ qt, float* s_out, float* amax_out,
-                                                          float* partials_out)
+                                                          ScaleSrc src, DelayedArgs dl, uint8_t* __restrict__ q,
+                                                          uint8_t* __restrict__ qt, float* s_out, float* amax_out)
 {
     constexpr int E = In<T>::kE, LPR = 128 / E, RPR = kWG / LPR, ROUNDS = 128 / RPR;
-    __shared__ float lds[4];
+    __shared__ float lds[8];
     __shared__ __align__(16) uint8_t codes[128][128 + 16];
-    float alpha, s, a;
-    resolve_scale<FMT>(src, lds, alpha, s, a);
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        if (s_out)
-            *s_out = s;
-        if (amax_out)
-            *amax_out = a;
-    }
+    float alpha;
+    tile_cast_scale<FMT, DELAYED>(src, dl, lds, s_out, amax_out, alpha);
     const int64_t ntc = cdiv(C, 128), ntiles = cdiv(R, 128) * ntc;
     const int cc = (threadIdx.x % LPR) * E, rr0 = threadIdx.x / LPR;
     float m = 0.0f;
@@ -235,7 +350,7 @@ __global__ __launch_bounds__(kWG) void k_cast_tensor_tile(const T* __restrict__ 
             const int rr = rr0 + k * RPR;
             float f[E];
             In<T>::unpack(v[k], f);
-            if (partials_out)
+            if constexpr (DELAYED)
                 m = fmaxf(m, absmax<E>(f));
             const bool in = rr < rows_in && cc < cols_in;
             if constexpr (E == 8) {
@@ -274,11 +389,8 @@ __global__ __launch_bounds__(kWG) void k_cast_tensor_tile(const T* __restrict__ 
                 st16_stream(qt + (c0 + c) * R + r0 + 16 * kq, w);
         }
     }
-    if (partials_out) {
-        m = max_workgroup(m, lds);
-        if (threadIdx.x == 0)
-            partials_out[blockIdx.x] = m;
-    }
+    if constexpr (DELAYED)
+        delayed_epilogue(dl, m, lds);
 }
 
 __global__ __launch_bounds__(kWG) void k_amax_finish(const float* __restrict__ partials, int n, float* out)
@@ -292,19 +404,23 @@ __global__ __launch_bounds__(kWG) void k_amax_finish(const float* __restrict__ p
         *out = m;
 }
 
-// Delayed scaling, second half of a step ([MP] recipe 2: record this step's
-// amax in the window; the next step's scale comes from the window's max).
-// One workgroup reads the partials and the window together, so both
-// reductions share one round of loads and one LDS exchange.
+// Delayed scaling, the window update of one step on its own ([MP] recipe 2:
+// record the step's amax in the window; the next scale comes from the
+// window's max), for windows longer than the cast's prologue reads and for
+// fq_delayed_flush. One workgroup reads the record (partials and tag) and
+// the window together; nothing changes unless the record carries `tag`.
 constexpr int kFinishThreads = 256;
 
-__global__ __launch_bounds__(kFinishThreads) void k_delayed_finish(const float* __restrict__ partials, int n,
-                                                                   float* hist, int H, int slot, float* alpha,
-                                                                   float* s, float fmax_v, float* amax_out)
+__global__ __launch_bounds__(kFinishThreads) void k_delayed_finish(const float* __restrict__ rec, uint32_t tag_lo,
+                                                                   uint32_t tag_hi, float* hist, int H, int slot,
+                                                                   float* alpha, float* s, float fmax_v,
+                                                                   float* amax_out)
 {
     __shared__ float lds[2][kFinishThreads / 64];
     static_assert(kFinishThreads == kWG, "partials_max assumes kWG threads");
-    float mp = partials_max(partials, n), mh = 0.0f;
+    const uint32_t* tag = reinterpret_cast<const uint32_t*>(rec + kMaxPartials);
+    const bool apply = tag[0] == tag_lo && tag[1] == tag_hi;
+    float mp = partials_max(rec, kMaxPartials), mh = 0.0f;
 #pragma unroll 4
     for (int i = threadIdx.x; i < H; i += kFinishThreads)
         if (i != slot)
@@ -317,7 +433,7 @@ __global__ __launch_bounds__(kFinishThreads) void k_delayed_finish(const float* 
         lds[1][w] = mh;
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if (threadIdx.x == 0 && apply) {
         float at = 0.0f, wm = 0.0f;
         for (int k = 0; k < kFinishThreads / 64; ++k) {
             at = fmaxf(at, lds[0][k]);
@@ -372,99 +488,116 @@ hipError_t launch_amax_finish(const float* partials, int n, float* out, hipStrea
 
 template <typename T, int FMT>
 static void cast_tensor_t(const void* x, int64_t n, ScaleSrc src, uint8_t* q, float* s_out, float* amax_out,
-                          float* partials_out, int grid, hipStream_t stream)
+                          int grid, hipStream_t stream)
 {
-    // eight loads per lane in flight for the current-scaling cast (measured
-    // faster inside a full step), four when the cast also writes amax partials
-    if (partials_out)
-        k_cast_tensor<T, FMT, kLoads><<<grid, kWG, 0, stream>>>((const T*)x, n, src, q, s_out, amax_out,
-                                                                 partials_out);
-    else
-        k_cast_tensor<T, FMT, 8><<<grid, kWG, 0, stream>>>((const T*)x, n, src, q, s_out, amax_out, partials_out);
+    // eight loads per lane in flight (measured faster inside a full step)
+    k_cast_tensor<T, FMT, 8><<<grid, kWG, 0, stream>>>((const T*)x, n, src, q, s_out, amax_out);
 }
 
 hipError_t launch_cast_tensor(const void* x, int in_bf16, int fmt, int64_t n, ScaleSrc src, uint8_t* q,
-                              float* s_out, float* amax_out, float* partials_out, int grid, hipStream_t stream)
+                              float* s_out, float* amax_out, hipStream_t stream)
 {
-    if (grid <= 0) {
-        // the depth-8 cast (no partials): a workgroup step covers 8 loads per lane
-        const int64_t per = (in_bf16 ? elems_per_wg_step<uint16_t>() : elems_per_wg_step<float>()) *
-                            (partials_out ? 1 : 8 / kLoads);
-        grid = (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(n, per), kCastMaxGrid));
-    }
+    // a workgroup step covers 8 loads per lane
+    const int64_t per = (in_bf16 ? elems_per_wg_step<uint16_t>() : elems_per_wg_step<float>()) * (8 / kLoads);
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(n, per), kCastMaxGrid));
     if (in_bf16) {
         if (fmt == kE4M3)
-            cast_tensor_t<uint16_t, kE4M3>(x, n, src, q, s_out, amax_out, partials_out, grid, stream);
+            cast_tensor_t<uint16_t, kE4M3>(x, n, src, q, s_out, amax_out, grid, stream);
         else
-            cast_tensor_t<uint16_t, kE5M2>(x, n, src, q, s_out, amax_out, partials_out, grid, stream);
+            cast_tensor_t<uint16_t, kE5M2>(x, n, src, q, s_out, amax_out, grid, stream);
     } else {
         if (fmt == kE4M3)
-            cast_tensor_t<float, kE4M3>(x, n, src, q, s_out, amax_out, partials_out, grid, stream);
+            cast_tensor_t<float, kE4M3>(x, n, src, q, s_out, amax_out, grid, stream);
         else
-            cast_tensor_t<float, kE5M2>(x, n, src, q, s_out, amax_out, partials_out, grid, stream);
+            cast_tensor_t<float, kE5M2>(x, n, src, q, s_out, amax_out, grid, stream);
     }
     return hipGetLastError();
 }
 
-template <typename T, int FMT>
-static void cast_2d_t(const void* x, int64_t R, int64_t C, ScaleSrc src, uint8_t* q, uint8_t* qt, float* s_out,
-                      float* amax_out, float* partials_out, int grid, hipStream_t stream)
+// Tile casts (colwise copy): vector 128x128 tiles when R and C are multiples
+// of 16, else byte-granular 64x64 tiles. A delayed step's grid is at most
+// kMaxPartials (one partial per workgroup).
+template <typename T, int FMT, bool DELAYED>
+static void cast_2d_t(const void* x, int64_t R, int64_t C, ScaleSrc src, const DelayedArgs& dl, uint8_t* q,
+                      uint8_t* qt, float* s_out, float* amax_out, hipStream_t stream)
 {
-    k_cast_tensor_2d<T, FMT><<<grid, kWG, 0, stream>>>((const T*)x, R, C, src, q, qt, s_out, amax_out,
-                                                       partials_out);
+    const int max_grid = DELAYED ? kMaxPartials : kCastMaxGrid;
+    if (R % 16 == 0 && C % 16 == 0) {
+        const int64_t ntiles = cdiv(R, 128) * cdiv(C, 128);
+        const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(ntiles, max_grid));
+        k_cast_tensor_tile<T, FMT, DELAYED><<<grid, kWG, 0, stream>>>((const T*)x, R, C, src, dl, q, qt, s_out,
+                                                                      amax_out);
+    } else {
+        const int64_t ntiles = cdiv(R, 64) * cdiv(C, 64);
+        const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(ntiles, max_grid));
+        k_cast_tensor_2d<T, FMT, DELAYED><<<grid, kWG, 0, stream>>>((const T*)x, R, C, src, dl, q, qt, s_out,
+                                                                    amax_out);
+    }
 }
 
-template <typename T, int FMT>
-void cast_tile_t(const void* x, int64_t R, int64_t C, ScaleSrc src, uint8_t* q, uint8_t* qt, float* s_out,
-                 float* amax_out, float* partials_out, int grid, hipStream_t stream)
+template <bool DELAYED>
+static void cast_2d_any(const void* x, int in_bf16, int fmt, int64_t R, int64_t C, ScaleSrc src,
+                        const DelayedArgs& dl, uint8_t* q, uint8_t* qt, float* s_out, float* amax_out,
+                        hipStream_t stream)
 {
-    k_cast_tensor_tile<T, FMT><<<grid, kWG, 0, stream>>>((const T*)x, R, C, src, q, qt, s_out, amax_out,
-                                                         partials_out);
+    if (in_bf16) {
+        if (fmt == kE4M3)
+            cast_2d_t<uint16_t, kE4M3, DELAYED>(x, R, C, src, dl, q, qt, s_out, amax_out, stream);
+        else
+            cast_2d_t<uint16_t, kE5M2, DELAYED>(x, R, C, src, dl, q, qt, s_out, amax_out, stream);
+    } else {
+        if (fmt == kE4M3)
+            cast_2d_t<float, kE4M3, DELAYED>(x, R, C, src, dl, q, qt, s_out, amax_out, stream);
+        else
+            cast_2d_t<float, kE5M2, DELAYED>(x, R, C, src, dl, q, qt, s_out, amax_out, stream);
+    }
 }
 
 hipError_t launch_cast_tensor_2d(const void* x, int in_bf16, int fmt, int64_t R, int64_t C, ScaleSrc src,
-                                 uint8_t* q, uint8_t* qt, float* s_out, float* amax_out, float* partials_out,
-                                 int grid, hipStream_t stream)
+                                 uint8_t* q, uint8_t* qt, float* s_out, float* amax_out, hipStream_t stream)
 {
-    if (R % 16 == 0 && C % 16 == 0) {
-        // vector tiles; with partials_out the caller's grid is the partial count
-        const int64_t ntiles = cdiv(R, 128) * cdiv(C, 128);
-        if (grid <= 0)
-            grid = (int)std::max<int64_t>(1, std::min<int64_t>(ntiles, kCastMaxGrid));
-        if (in_bf16) {
-            if (fmt == kE4M3)
-                cast_tile_t<uint16_t, kE4M3>(x, R, C, src, q, qt, s_out, amax_out, partials_out, grid, stream);
-            else
-                cast_tile_t<uint16_t, kE5M2>(x, R, C, src, q, qt, s_out, amax_out, partials_out, grid, stream);
-        } else {
-            if (fmt == kE4M3)
-                cast_tile_t<float, kE4M3>(x, R, C, src, q, qt, s_out, amax_out, partials_out, grid, stream);
-            else
-                cast_tile_t<float, kE5M2>(x, R, C, src, q, qt, s_out, amax_out, partials_out, grid, stream);
-        }
+    cast_2d_any<false>(x, in_bf16, fmt, R, C, src, DelayedArgs{}, q, qt, s_out, amax_out, stream);
+    return hipGetLastError();
+}
+
+// The flat delayed cast: loads per lane in flight, and the grid (one
+// partial per workgroup, at most kMaxPartials).
+constexpr int kDelayedLoads = 8;
+
+template <typename T, int FMT>
+static void cast_delayed_t(const void* x, int64_t n, const DelayedArgs& dl, uint8_t* q, hipStream_t stream)
+{
+    const int64_t per = (int64_t)kWG * In<T>::kE * kDelayedLoads;
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(n, per), kMaxPartials));
+    k_cast_delayed<T, FMT, kDelayedLoads><<<grid, kWG, 0, stream>>>((const T*)x, n, dl, q);
+}
+
+hipError_t launch_cast_delayed(const void* x, int in_bf16, int fmt, int64_t R, int64_t C, const DelayedArgs& dl,
+                               uint8_t* q, uint8_t* qt, hipStream_t stream)
+{
+    if (qt) {
+        cast_2d_any<true>(x, in_bf16, fmt, R, C, ScaleSrc{}, dl, q, qt, nullptr, nullptr, stream);
         return hipGetLastError();
     }
-    const int64_t ntiles = cdiv(R, 64) * cdiv(C, 64);
-    if (grid <= 0)
-        grid = (int)std::max<int64_t>(1, std::min<int64_t>(ntiles, kCastMaxGrid));
+    const int64_t n = R * C;
     if (in_bf16) {
         if (fmt == kE4M3)
-            cast_2d_t<uint16_t, kE4M3>(x, R, C, src, q, qt, s_out, amax_out, partials_out, grid, stream);
+            cast_delayed_t<uint16_t, kE4M3>(x, n, dl, q, stream);
         else
-            cast_2d_t<uint16_t, kE5M2>(x, R, C, src, q, qt, s_out, amax_out, partials_out, grid, stream);
+            cast_delayed_t<uint16_t, kE5M2>(x, n, dl, q, stream);
     } else {
         if (fmt == kE4M3)
-            cast_2d_t<float, kE4M3>(x, R, C, src, q, qt, s_out, amax_out, partials_out, grid, stream);
+            cast_delayed_t<float, kE4M3>(x, n, dl, q, stream);
         else
-            cast_2d_t<float, kE5M2>(x, R, C, src, q, qt, s_out, amax_out, partials_out, grid, stream);
+            cast_delayed_t<float, kE5M2>(x, n, dl, q, stream);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_delayed_finish(const float* partials, int n_partials, float* hist, int H, int slot, float* alpha,
-                                 float* s, float fmax_v, float* amax_out, hipStream_t stream)
+hipError_t launch_delayed_finish(const float* rec, uint32_t tag_lo, uint32_t tag_hi, float* hist, int H, int slot,
+                                 float* alpha, float* s, float fmax_v, float* amax_out, hipStream_t stream)
 {
-    k_delayed_finish<<<1, kFinishThreads, 0, stream>>>(partials, n_partials, hist, H, slot, alpha, s, fmax_v,
+    k_delayed_finish<<<1, kFinishThreads, 0, stream>>>(rec, tag_lo, tag_hi, hist, H, slot, alpha, s, fmax_v,
                                                         amax_out);
     return hipGetLastError();
 }

@@ -46,13 +46,38 @@ constexpr int kMaxPartials = 1024;
 static_assert(kMaxPartials <= 4 * 256, "consumers read the partials with four loads per thread");
 constexpr size_t kPartialsBytes = kMaxPartials * sizeof(float);
 
-// Where a per-tensor cast takes its amax from.
+// Where a per-tensor cast takes its amax from (current scaling).
 struct ScaleSrc {
-    const float* partials = nullptr;  // reduce partials[0..n_partials) (current scaling)
+    const float* partials = nullptr;  // reduce partials[0..n_partials)
     int n_partials = 0;
     const float* amax_in = nullptr;   // or a given amax (quantize_with_amax)
-    const float* alpha_in = nullptr;  // or a given alpha and s (delayed scaling)
-    const float* s_in = nullptr;
+};
+
+// Delayed scaling keeps one record per step in the caller's state: the
+// step's amax partials (one per workgroup of its cast, zero beyond the grid)
+// followed by a two-word tag naming the step (never all zero). Two records
+// alternate by step parity, so step t reads step t-1's record while it
+// writes its own.
+constexpr int kRecordFloats = kMaxPartials + 8;
+constexpr size_t kPendingBytes = 2 * kRecordFloats * sizeof(float);
+// Windows up to this length are finished inside the next step's cast (each
+// thread of a workgroup reads at most four window slots, in one batch of
+// loads); longer windows take a separate one-workgroup finish kernel.
+constexpr int kFoldMaxHistory = 4 * 256;
+
+// One delayed-scaling cast (step t).
+struct DelayedArgs {
+    float* hist = nullptr;            // the window, H floats
+    int H = 0;
+    const float* prev = nullptr;      // step t-1's record to finish first, or null (t = 0, or H > kFoldMaxHistory)
+    int prev_slot = 0;                // (t-1) mod H
+    uint32_t prev_tag[2] = {0u, 0u};  // the tag that record carries if it is step t-1's
+    float* alpha = nullptr;           // the state's scale (alpha) and scale_inv (s): read, and
+    float* s = nullptr;               // written by workgroup 0 when it finishes step t-1
+    float fmax = 0.0f;
+    float* rec = nullptr;             // this step's record
+    uint32_t tag[2] = {0u, 0u};       // this step's tag
+    float* s_used = nullptr;          // optional: the s that dequantizes this step's codes
 };
 
 // Number of workgroups of an amax pass over n elements of the given size,
@@ -65,23 +90,27 @@ hipError_t launch_amax_partial(const void* x, int in_bf16, int64_t n, float* par
 // out[0] = max(partials[0..n)).
 hipError_t launch_amax_finish(const float* partials, int n, float* out, hipStream_t stream);
 
-// Per-tensor cast of a flat tensor (rowwise bytes only). Optional
-// partials_out receives one amax partial per workgroup (delayed scaling);
-// pass grid = amax_grid(n) then. grid <= 0 picks a default.
+// Per-tensor cast of a flat tensor (rowwise bytes only), current scaling.
 hipError_t launch_cast_tensor(const void* x, int in_bf16, int fmt, int64_t n, ScaleSrc src, uint8_t* q,
-                              float* s_out, float* amax_out, float* partials_out, int grid, hipStream_t stream);
+                              float* s_out, float* amax_out, hipStream_t stream);
 
-// Per-tensor cast of a [R, C] tensor through 64x64 tiles, writing rowwise
-// bytes q (may be null) and transposed bytes qt (may be null). Optional
-// partials_out receives one amax per workgroup; grid <= 0 picks a default
-// (pass amax_grid-sized grids, <= kMaxPartials, when partials_out is set).
+// Per-tensor cast of a [R, C] tensor writing rowwise bytes q (may be null)
+// and transposed bytes qt (may be null), current scaling.
 hipError_t launch_cast_tensor_2d(const void* x, int in_bf16, int fmt, int64_t R, int64_t C, ScaleSrc src,
-                                 uint8_t* q, uint8_t* qt, float* s_out, float* amax_out, float* partials_out,
-                                 int grid, hipStream_t stream);
+                                 uint8_t* q, uint8_t* qt, float* s_out, float* amax_out, hipStream_t stream);
 
-// Delayed scaling, after the cast wrote partials: a_t = max(partials),
-// hist[slot] = a_t, m = max(hist), new alpha/s if m > 0.
-hipError_t launch_delayed_finish(const float* partials, int n_partials, float* hist, int H, int slot,
+// One delayed-scaling step: finish step t-1 from its record (if dl.prev),
+// cast with the resulting scale, write this step's record. Rowwise bytes q
+// and/or transposed bytes qt of the [R, C] tensor.
+hipError_t launch_cast_delayed(const void* x, int in_bf16, int fmt, int64_t R, int64_t C, const DelayedArgs& dl,
+                               uint8_t* q, uint8_t* qt, hipStream_t stream);
+
+// Finish a delayed step from its record (one workgroup): if rec carries the
+// tag (tag_lo, tag_hi), a = max(its partials), hist[slot] = a, m =
+// max(hist), and alpha = Fmax/m, s = m/Fmax if m > 0; amax_out (optional)
+// receives a. A record with another tag (zero-filled, or another step's)
+// changes nothing.
+hipError_t launch_delayed_finish(const float* rec, uint32_t tag_lo, uint32_t tag_hi, float* hist, int H, int slot,
                                  float* alpha, float* s, float fmax_v, float* amax_out, hipStream_t stream);
 
 // Blockwise fp32 scales, E4M3. 1x128: flat blocks; 128x128: tiles.

@@ -46,9 +46,12 @@ class FqQuantized(ctypes.Structure):
                 ("amax", ctypes.c_void_p)]
 
 
+FQ_DELAYED_PENDING_BYTES = 8256
+
+
 class FqDelayedState(ctypes.Structure):
     _fields_ = [("amax_history", ctypes.c_void_p), ("history_len", ctypes.c_int32), ("scale", ctypes.c_void_p),
-                ("scale_inv", ctypes.c_void_p), ("step", ctypes.c_int64)]
+                ("scale_inv", ctypes.c_void_p), ("pending", ctypes.c_void_p), ("step", ctypes.c_int64)]
 
 
 class FqError(RuntimeError):
@@ -79,6 +82,7 @@ def lib():
         "fq_amax": (ctypes.c_int, [dp, _P, _P, _P, ctypes.c_size_t, _P]),
         "fq_quantize_with_amax": (ctypes.c_int, [dp, _P, _P, qp, _P, ctypes.c_size_t, _P]),
         "fq_quantize_delayed": (ctypes.c_int, [dp, _P, ctypes.POINTER(FqDelayedState), qp, _P, ctypes.c_size_t, _P]),
+        "fq_delayed_flush": (ctypes.c_int, [dp, ctypes.POINTER(FqDelayedState), _P]),
         "fq_dequantize": (ctypes.c_int, [dp, qp, ctypes.c_int32, _P, ctypes.c_int32, _P]),
         "fq_requantize_transpose": (ctypes.c_int, [dp, qp, qp, _P]),
         "fq_quantize_noalloc": (ctypes.c_int, [dp, _P, qp, _P]),
@@ -225,31 +229,45 @@ class DelayedState:
         self.amax_history = torch.zeros(history_len, dtype=torch.float32, device=device)
         self.scale = torch.ones(1, dtype=torch.float32, device=device)
         self.scale_inv = torch.ones(1, dtype=torch.float32, device=device)
+        self.pending = torch.zeros(FQ_DELAYED_PENDING_BYTES // 4, dtype=torch.float32, device=device)
         self.step = 0
 
     def c(self) -> FqDelayedState:
         return FqDelayedState(_ptr(self.amax_history), self.amax_history.numel(), _ptr(self.scale),
-                              _ptr(self.scale_inv), self.step)
+                              _ptr(self.scale_inv), _ptr(self.pending), self.step)
 
     def state_dict(self):
+        """The state as it stands (call fq_delayed_flush first to make the
+        window and scales current and the pending records unnecessary)."""
         return {"amax_history": self.amax_history.clone(), "scale": self.scale.clone(),
-                "scale_inv": self.scale_inv.clone(), "step": self.step}
+                "scale_inv": self.scale_inv.clone(), "pending": self.pending.clone(), "step": self.step}
 
     def load_state_dict(self, sd):
         self.amax_history.copy_(sd["amax_history"])
         self.scale.copy_(sd["scale"])
         self.scale_inv.copy_(sd["scale_inv"])
+        if "pending" in sd:
+            self.pending.copy_(sd["pending"])
+        else:
+            self.pending.zero_()
         self.step = int(sd["step"])
 
 
-def fq_quantize_delayed(d: FqDesc, x: torch.Tensor, state: DelayedState, out: Quantized, ws: torch.Tensor,
-                        stream=None, advance: bool = True):
+def fq_quantize_delayed(d: FqDesc, x: torch.Tensor, state: DelayedState, out: Quantized,
+                        ws: Optional[torch.Tensor] = None, stream=None, advance: bool = True):
     q = out.c()
     st = state.c()
     _check(lib().fq_quantize_delayed(ctypes.byref(d), _ptr(x), ctypes.byref(st), ctypes.byref(q), _ptr(ws),
-                                     ws.numel() * ws.element_size(), _stream(stream)), "fq_quantize_delayed")
+                                     0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)),
+           "fq_quantize_delayed")
     if advance:
         state.step += 1
+
+
+def fq_delayed_flush(d: FqDesc, state: DelayedState, stream=None):
+    """Bring state's window and scales up to date after its last step."""
+    st = state.c()
+    _check(lib().fq_delayed_flush(ctypes.byref(d), ctypes.byref(st), _stream(stream)), "fq_delayed_flush")
 
 
 def fq_dequantize(d: FqDesc, qt: Quantized, which: int, y: torch.Tensor, stream=None):

@@ -65,6 +65,19 @@ def trace(stats_csv, trace_csv, out_md, command):
         prev = e
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
+    # the same mean durations as JSON, each with the hash of its kernel's
+    # sources (bench.py quotes a duration only while they are unchanged)
+    kernels = {}
+    for r in stats:
+        short = short_name(r["Name"])
+        family = short.split("<")[0]
+        entry = {"calls": int(r["Calls"]), "mean_us": round(float(r["AverageNs"]) / 1e3, 3)}
+        if family in KERNEL_SOURCES:
+            entry["source_hash"] = source_hash(KERNEL_SOURCES[family])
+        kernels[short] = entry
+    with open(os.path.splitext(out_md)[0] + ".json", "w") as f:
+        json.dump({"command": command, "kernels": kernels}, f, indent=1)
+        f.write("\n")
 
 
 def _mean_counter(rows, kernel_substr, counter):

@@ -242,16 +242,23 @@ typedef struct {
 /*
  * Delayed-scaling state, all fields but `step` in device memory.
  *   amax_history  history_len floats; zero-filled by the caller before step 0.
- *   scale         alpha, the multiplier the next cast uses; 1.0 before step 0.
+ *   scale         alpha, the multiplier casts use; 1.0 before step 0.
  *   scale_inv     s, its dequantization multiplier; 1.0 before step 0.
+ *   pending       FQ_DELAYED_PENDING_BYTES, 16-byte aligned, zero-filled
+ *                 before step 0: carries a step's amax (as per-workgroup
+ *                 partial maxima, tagged with the step) to the next call,
+ *                 which records it in the window.
  *   step          host counter t; the caller advances it after each call.
- * Checkpointing the state is copying these buffers and the counter.
+ * See fq_quantize_delayed for when the window and scales are up to date, and
+ * fq_delayed_flush for checkpointing.
  */
+#define FQ_DELAYED_PENDING_BYTES 8256
 typedef struct {
     float *amax_history;
     int32_t history_len;
     float *scale;
     float *scale_inv;
+    float *pending;
     int64_t step;
 } fq_delayed_state;
 
@@ -304,17 +311,39 @@ fq_status fq_quantize_with_amax(const fq_desc *desc, const void *x, const float 
  * One step t = state->step of per-tensor delayed scaling (desc->recipe must
  * be FQ_PER_TENSOR_DELAYED) ([MP] recipe 2: one read of the tensor casts it
  * with the old scale while its amax is recorded in the window):
- *   q = Q(fp32(alpha_old * x))               alpha_old = *state->scale
+ *   q = Q(fp32(alpha_old * x))               alpha_old = the scale after step t-1
  *   a_t = max|x|;  amax_history[t mod H] = a_t
  *   m = max(amax_history)
- *   if m > 0: *scale = Fmax/m, *scale_inv = m/Fmax   (else both unchanged)
- * out->tensor_scale (optional here) receives s_old, the multiplier that
- * dequantizes this step's bytes; out->amax (optional) receives a_t.
- * The caller increments state->step afterwards.
+ *   if m > 0: scale = Fmax/m, scale_inv = m/Fmax   (else both unchanged)
+ * The codes, and out->tensor_scale (optional: s_old, the multiplier that
+ * dequantizes them), are this step's when the call's work completes. The
+ * window update of step t runs at the start of step t+1's call, in the same
+ * kernel as its cast, from a_t carried in state->pending: so after the call
+ * for step t, amax_history and scale/scale_inv are those after step t-1,
+ * unless history_len > 1024, in which case the update runs as a second kernel
+ * of this call. out->amax (optional) receives a_t (one more small kernel).
+ * The workspace is unused (may be NULL). The caller increments state->step
+ * afterwards; calls for one state must be ordered (one stream, or events).
+ * Every kernel argument of the call for step t repeats with period
+ * lcm(2, history_len) in t, so a call captured in a HIP graph at step t
+ * replays correctly at steps t + k * lcm(2, history_len).
  */
 fq_status fq_quantize_delayed(const fq_desc *desc, const void *x, const fq_delayed_state *state,
                               const fq_quantized *out, void *workspace, size_t workspace_bytes,
                               hipStream_t stream);
+
+/*
+ * Bring a delayed-scaling state up to date after the call for step
+ * state->step - 1 (state->step as the caller advanced it): record that
+ * step's amax in the window and set scale/scale_inv from the window, as the
+ * next call would; a no-op if state->step == 0. Idempotent: the next call,
+ * or a second flush, repeats the same update and changes nothing. After a
+ * flush, (amax_history, scale, scale_inv, step) is the whole state:
+ * checkpoint those; on resume, zero-fill `pending` (a zero-filled record is
+ * never taken for a step's) or restore it too.
+ * Uses desc->recipe (FQ_PER_TENSOR_DELAYED) and desc->format.
+ */
+fq_status fq_delayed_flush(const fq_desc *desc, const fq_delayed_state *state, hipStream_t stream);
 
 /*
  * y = the values that `in` represents ([CS] "Current Scaling": the code value

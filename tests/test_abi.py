@@ -200,18 +200,23 @@ def test_pointer_checks(L):
 def test_delayed_and_amax_checks(L):
     d = fq.desc(fq.FQ_PER_TENSOR_DELAYED, fq.FQ_IN_BF16, fq.FQ_E4M3, 64, 64)
     ok = fq.FqQuantized(fq.FqPlane(B, None), fq.FqPlane(None, None), None, None)
-    st = fq.FqDelayedState(B, 0, B, B, 0)
-    assert L.fq_quantize_delayed(ctypes.byref(d), B, ctypes.byref(st), ctypes.byref(ok), B, 4096, None) \
-        == fq.FQ_E_INVALID
-    st = fq.FqDelayedState(B, 1024, B, B, -1)
-    assert L.fq_quantize_delayed(ctypes.byref(d), B, ctypes.byref(st), ctypes.byref(ok), B, 4096, None) \
-        == fq.FQ_E_INVALID
-    st = fq.FqDelayedState(B, 1024, B + 2, B, 0)
-    assert L.fq_quantize_delayed(ctypes.byref(d), B, ctypes.byref(st), ctypes.byref(ok), B, 4096, None) \
-        == fq.FQ_E_ALIGN
-    st = fq.FqDelayedState(B, 1024, B, B, 0)
-    assert L.fq_quantize_delayed(ctypes.byref(d), B, ctypes.byref(st), ctypes.byref(ok), B, 16, None) \
-        == fq.FQ_E_WORKSPACE
+    call = lambda st, ws=None, n=0: L.fq_quantize_delayed(ctypes.byref(d), B, ctypes.byref(st), ctypes.byref(ok),
+                                                          ws, n, None)
+    assert call(fq.FqDelayedState(B, 0, B, B, B, 0)) == fq.FQ_E_INVALID            # empty window
+    assert call(fq.FqDelayedState(B, 1024, B, B, B, -1)) == fq.FQ_E_INVALID        # negative step
+    assert call(fq.FqDelayedState(B, 1024, B + 2, B, B, 0)) == fq.FQ_E_ALIGN       # scale
+    assert call(fq.FqDelayedState(B, 1024, B, B, None, 0)) == fq.FQ_E_INVALID      # no pending records
+    assert call(fq.FqDelayedState(B, 1024, B, B, B + 4, 0)) == fq.FQ_E_ALIGN       # pending 16-byte aligned
+    st = fq.FqDelayedState(B, 1024, B, B, B, 0)
+    # fq_delayed_flush checks the same state and the recipe
+    assert L.fq_delayed_flush(ctypes.byref(d), ctypes.byref(fq.FqDelayedState(B, 1024, B, B, None, 3)),
+                              None) == fq.FQ_E_INVALID
+    assert L.fq_delayed_flush(ctypes.byref(d), ctypes.byref(fq.FqDelayedState(B, 1024, B, B, B + 8, 3)),
+                              None) == fq.FQ_E_ALIGN
+    assert L.fq_delayed_flush(ctypes.byref(d), ctypes.byref(st), None) == fq.FQ_OK  # step 0: nothing to do
+    dcur = fq.desc(fq.FQ_PER_TENSOR_CURRENT, fq.FQ_IN_BF16, fq.FQ_E4M3, 64, 64)
+    assert L.fq_delayed_flush(ctypes.byref(dcur), ctypes.byref(st), None) == fq.FQ_E_UNSUPPORTED
+    assert fq.fq_sizes(d).workspace == 4096 and ctypes.sizeof(fq.FqDelayedState) == 48
     dc = fq.desc(fq.FQ_PER_TENSOR_CURRENT, fq.FQ_IN_BF16, fq.FQ_E4M3, 64, 64)
     assert L.fq_quantize_delayed(ctypes.byref(dc), B, ctypes.byref(st), ctypes.byref(ok), B, 4096, None) \
         == fq.FQ_E_UNSUPPORTED

@@ -99,3 +99,59 @@ def test_traffic_for_ignores_a_stale_summary(tmp_path, monkeypatch):
     assert bench.traffic_for(w, 0) == 123
     path.write_text(json.dumps({"source_hash": "0" * 16, "hbm_bytes_per_launch": 123}))
     assert bench.traffic_for(w, 0) is None
+
+
+SMALL = [
+    W.Workload("cur", (96, 256), W.BF16, "current", "e4m3", seed=11),
+    W.Workload("del", (96, 256), W.BF16, "delayed", "e5m2", seed=12, std=1e-3, extra={"history_len": 8}),
+    W.Workload("b1", (96, 256), W.BF16, "block", "e4m3", block=(1, 128), seed=13),
+    W.Workload("b128", (384, 256), W.BF16, "block", "e4m3", block=(128, 128), seed=14, std=0.02),
+    W.Workload("mx", (160, 128), W.BF16, "mx", "e4m3", block=(1, 32), outputs=3, seed=15, dist="student_t",
+               extra={"nu": 3.0}),
+    W.Workload("nv1", (96, 256), W.BF16, "nvfp4", "e2m1", block=(1, 16), seed=16),
+    W.Workload("nv16", (96, 256), W.BF16, "nvfp4", "e2m1", block=(16, 16), seed=17, std=0.02),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_partitioned_oracle_equals_one_thread(w):
+    """The all-core oracle baseline splits rows over threads (cut at block
+    heights) and combines per-tensor amaxes with an exact max; its bytes,
+    scales and delayed-scaling state equal one oracle call on the whole
+    tensor."""
+    import concurrent.futures
+
+    import numpy as np
+
+    import oracle as orc
+
+    x = w.make()
+    fmt = {"e4m3": orc.E4M3, "e5m2": orc.E5M2, "e2m1": orc.E2M1}[w.fmt]
+    # one oracle call on the whole tensor
+    if w.recipe == "current":
+        whole = orc.quantize_current(x, fmt, outputs=w.outputs)
+    elif w.recipe == "delayed":
+        st = orc.DelayedState(w.extra["history_len"])
+        whole = orc.quantize_delayed(x, fmt, st, outputs=w.outputs)
+        whole.update(hist=st.hist, alpha=st.alpha, s=st.s)
+    elif w.recipe == "block":
+        whole = orc.quantize_block(x, w.block, outputs=w.outputs)
+    elif w.recipe == "mx":
+        whole = orc.quantize_mx(x, outputs=w.outputs, fmt=fmt)
+    else:
+        whole = orc.quantize_nvfp4(x, w.block, outputs=w.outputs)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=3) as pool:
+        parts = bench.assemble(w, bench.oracle_partitioned(w, x, 3, pool))
+        assert len(bench.row_parts(w.shape[0], bench.part_unit(w), 3)) == 3
+    for k, v in parts.items():
+        if v is None or k not in whole:
+            continue
+        a, b = np.atleast_1d(np.asarray(whole[k])), np.atleast_1d(np.asarray(v))
+        assert a.shape == b.shape and np.array_equal(a.view(np.uint8), b.view(np.uint8)), (w.name, k)
+    assert {k for k, v in whole.items() if v is not None} <= set(parts)
+
+
+def test_row_parts_cut_at_the_unit():
+    assert bench.row_parts(384, 128, 3) == [(0, 128), (128, 256), (256, 384)]
+    assert bench.row_parts(100, 1, 3) == [(0, 33), (33, 66), (66, 100)]
+    assert bench.row_parts(96, 32, 5) == [(0, 32), (32, 64), (64, 96)]

@@ -101,6 +101,7 @@ def test_empty_delayed_step(shape, fmt):
         out0.amax.fill_(SENTINEL)
         fq.fq_quantize_delayed(d0, torch.empty(16, dtype=torch.float32, device="cuda"), st, out0, ws0)
         orc.quantize_delayed(zero, ofmt, ost)
+        fq.fq_delayed_flush(d0, st)
         torch.cuda.synchronize()
         assert host(out0.amax)[0] == 0.0
         assert np.array_equal(host(st.amax_history).view(np.uint32), ost.hist.view(np.uint32)), t

@@ -126,14 +126,31 @@ def test_guards_hold(case, dt):
     run_case(case, W.normal(shape, 2.0, shape[0] * 131 + shape[1], dt), g)
 
 
-def test_guards_hold_delayed():
+def guarded_state(g, H):
+    """A delayed-scaling state whose window, scales and pending records each
+    sit between guard regions."""
+    st = fq.DelayedState(H)
+    st.amax_history = g.alloc(4 * H, torch.float32)
+    st.amax_history.zero_()
+    st.scale = g.alloc(4, torch.float32)
+    st.scale_inv = g.alloc(4, torch.float32)
+    st.scale.fill_(1.0)
+    st.scale_inv.fill_(1.0)
+    st.pending = g.alloc(fq.FQ_DELAYED_PENDING_BYTES, torch.float32)
+    st.pending.zero_()
+    return st
+
+
+@pytest.mark.parametrize("H", [8, 2000], ids=["window-8", "window-2000"])
+def test_guards_hold_delayed(H):
     g = Guarded()
-    st = fq.DelayedState(8)
+    st = guarded_state(g, H)
     for R, C, outputs in ((37, 61, BOTH), (160, 272, BOTH), (3, 100003, fq.FQ_ROWWISE)):
         d = fq.desc(fq.FQ_PER_TENSOR_DELAYED, fq.FQ_IN_F32, fq.FQ_E4M3, R, C, outputs=outputs)
         q, ws = guarded_quantized(g, d)
         for t in range(3):
             fq.fq_quantize_delayed(d, dev(W.normal((R, C), 1.0 + t, 7 + t, W.F32)), st, q, ws)
+        fq.fq_delayed_flush(d, st)
         g.check(f"delayed {R}x{C}")
 
 

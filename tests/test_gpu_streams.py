@@ -49,6 +49,7 @@ def test_delayed_steps_on_a_side_stream():
         on_stream(s, lambda: fq.fq_quantize_delayed(d, xd, st, out, ws, stream=s))
         want = orc.quantize_delayed(x, orc.E5M2, ost)
         same_bytes(host(out.row_data), want["q_row"], f"step {t} codes")
+    on_stream(s, lambda: fq.fq_delayed_flush(d, st, stream=s))
     same_bytes(host(st.scale), np.float32(ost.alpha), "next alpha")
 
 

@@ -202,18 +202,27 @@ def test_full_size_current(w):
 
 
 # ---------------------------------------------------------------- delayed
+def check_state(st, ost, what):
+    same_bytes(host(st.amax_history), ost.hist, f"{what} history")
+    same_bytes(host(st.scale), f32(ost.alpha), f"{what} alpha")
+    same_bytes(host(st.scale_inv), f32(ost.s), f"{what} s")
+
+
 def delayed_steps(xs, fmt, H, outputs=fq.FQ_ROWWISE, check_every=1):
+    """Steps on the GPU and in the oracle; at checked steps the codes, the s
+    used, a_t, and (after fq_delayed_flush) the window and scales. Between
+    checks the window update of each step runs inside the next step's cast."""
     R, C = shape2(xs[0])
     d = fq.desc(fq.FQ_PER_TENSOR_DELAYED, in_dtype(xs[0]), fmt, R, C, outputs=outputs)
     out = fq.alloc_quantized(d)
-    ws = fq.alloc_workspace(d)
     st = fq.DelayedState(H)
     ost = orc.DelayedState(H)
     for t, x in enumerate(xs):
         s_before = ost.s
-        fq.fq_quantize_delayed(d, dev(x), st, out, ws)
+        fq.fq_quantize_delayed(d, dev(x), st, out)
         want = orc.quantize_delayed(x.reshape(-1), FMTS[fmt], ost, outputs=outputs, shape=(R, C))
         if t % check_every == 0 or t == len(xs) - 1:
+            fq.fq_delayed_flush(d, st)
             torch.cuda.synchronize()
             if outputs & fq.FQ_ROWWISE:
                 same_bytes(host(out.row_data), want["q_row"], f"step {t} codes")
@@ -221,9 +230,7 @@ def delayed_steps(xs, fmt, H, outputs=fq.FQ_ROWWISE, check_every=1):
                 same_bytes(host(out.col_data), want["q_col"], f"step {t} colwise codes")
             same_bytes(host(out.tensor_scale), f32(s_before), f"step {t} s used")
             same_bytes(host(out.amax), f32(want["amax"]), f"step {t} amax")
-            same_bytes(host(st.amax_history), ost.hist, f"step {t} history")
-            same_bytes(host(st.scale), f32(ost.alpha), f"step {t} alpha")
-            same_bytes(host(st.scale_inv), f32(ost.s), f"step {t} s")
+            check_state(st, ost, f"step {t}")
     return st, ost
 
 
@@ -232,14 +239,16 @@ def test_delayed_small_ring(fmt):
     rng = np.random.default_rng(4)
     xs = [(rng.standard_normal((37, 61)) * 10.0 ** rng.uniform(-3, 3)).astype(np.float32) for _ in range(11)]
     delayed_steps(xs, fmt, 4)
+    delayed_steps(xs, fmt, 4, check_every=5)
     delayed_steps([W.to_bf16_bits(x) for x in xs], fmt, 3, outputs=fq.FQ_ROWWISE | fq.FQ_COLWISE)
+    delayed_steps(xs, fmt, 1, check_every=3)                       # a window of one step
 
 
 def test_delayed_colwise_tiles():
     rng = np.random.default_rng(5)
     xs = [(rng.standard_normal((160, 272)) * 10.0 ** rng.uniform(-2, 2)).astype(np.float32) for _ in range(6)]
     delayed_steps([W.to_bf16_bits(x) for x in xs], fq.FQ_E4M3, 3, outputs=fq.FQ_ROWWISE | fq.FQ_COLWISE)
-    delayed_steps(xs, fq.FQ_E5M2, 4, outputs=fq.FQ_COLWISE)
+    delayed_steps(xs, fq.FQ_E5M2, 4, outputs=fq.FQ_COLWISE, check_every=4)
 
 
 def test_delayed_window_wrap_1024():
@@ -251,25 +260,127 @@ def test_delayed_window_wrap_1024():
     assert ost.alpha != orc.tensor_scales(1000.0, 448.0)[0]
 
 
-def test_delayed_checkpoint_resume():
+def test_delayed_long_window_separate_finish():
+    """A window longer than 1024 steps: each step's update runs as its own
+    kernel in the same call, so the state is current after every call
+    (checked here without a flush), and a flush changes nothing."""
+    rng = np.random.default_rng(9)
+    xs = [(rng.standard_normal((64, 96)) * 10.0 ** rng.uniform(-2, 2)).astype(np.float32) for _ in range(7)]
+    H = 2048
+    d = fq.desc(fq.FQ_PER_TENSOR_DELAYED, fq.FQ_IN_F32, fq.FQ_E5M2, 64, 96)
+    out = fq.alloc_quantized(d)
+    st, ost = fq.DelayedState(H), orc.DelayedState(H)
+    for t, x in enumerate(xs):
+        fq.fq_quantize_delayed(d, dev(x), st, out)
+        want = orc.quantize_delayed(x, orc.E5M2, ost)
+        torch.cuda.synchronize()
+        same_bytes(host(out.row_data), want["q_row"], f"step {t} codes")
+        check_state(st, ost, f"step {t} unflushed")
+    fq.fq_delayed_flush(d, st)
+    torch.cuda.synchronize()
+    check_state(st, ost, "flushed")
+    delayed_steps(xs, fq.FQ_E4M3, 1500, outputs=fq.FQ_ROWWISE | fq.FQ_COLWISE, check_every=3)
+
+
+def test_delayed_state_lags_one_step_until_flushed():
+    """Without a flush, the window and scales after the call for step t are
+    those after step t-1 (step t's update runs in step t+1's cast); a flush
+    brings them to step t, a second flush changes nothing, and the steps that
+    follow are unaffected by the flushes."""
+    rng = np.random.default_rng(10)
+    xs = [W.to_bf16_bits((rng.standard_normal((128, 256)) * 3.0 ** t).astype(np.float32)) for t in range(6)]
+    d = fq.desc(fq.FQ_PER_TENSOR_DELAYED, fq.FQ_IN_BF16, fq.FQ_E4M3, 128, 256)
+    out = fq.alloc_quantized(d)
+    out.amax = None                      # no amax output: the step is one kernel
+    st, ost = fq.DelayedState(4), orc.DelayedState(4)
+    prev = ost.copy()
+    for t, x in enumerate(xs):
+        fq.fq_quantize_delayed(d, dev(x), st, out)
+        want = orc.quantize_delayed(x, orc.E4M3, ost)
+        torch.cuda.synchronize()
+        same_bytes(host(out.row_data), want["q_row"], f"step {t} codes")
+        check_state(st, prev, f"step {t} before the flush")
+        if t % 2:
+            fq.fq_delayed_flush(d, st)
+            fq.fq_delayed_flush(d, st)
+            torch.cuda.synchronize()
+            check_state(st, ost, f"step {t} after the flush")
+        prev = ost.copy()
+
+
+@pytest.mark.parametrize("flushed", [False, True], ids=["with-pending", "flushed"])
+def test_delayed_checkpoint_resume(flushed):
+    """Resume from a saved state: either everything including the pending
+    records, or (after fq_delayed_flush) the window, scales and step with the
+    pending records zero-filled."""
     rng = np.random.default_rng(6)
     xs = [W.to_bf16_bits((rng.standard_normal((64, 256)) * (t + 1)).astype(np.float32)) for t in range(12)]
     d = fq.desc(fq.FQ_PER_TENSOR_DELAYED, fq.FQ_IN_BF16, fq.FQ_E5M2, 64, 256)
-    ws = fq.alloc_workspace(d)
-    run = lambda st, x: (fq.fq_quantize_delayed(d, dev(x), st, out, ws), host(out.row_data).copy())[1]
+    run = lambda st, x: (fq.fq_quantize_delayed(d, dev(x), st, out), host(out.row_data).copy())[1]
     out = fq.alloc_quantized(d)
     ref = fq.DelayedState(8)
     ref_bytes = [run(ref, x) for x in xs]
     a = fq.DelayedState(8)
     for x in xs[:5]:
         run(a, x)
+    if flushed:
+        fq.fq_delayed_flush(d, a)
     saved = a.state_dict()
+    if flushed:
+        del saved["pending"]
     b = fq.DelayedState(8)
     b.load_state_dict(saved)
     got = [run(b, x) for x in xs[5:]]
     for t, g in enumerate(got):
         assert np.array_equal(g, ref_bytes[5 + t])
+    fq.fq_delayed_flush(d, b)
+    fq.fq_delayed_flush(d, ref)
+    torch.cuda.synchronize()
     assert torch.equal(b.amax_history, ref.amax_history) and torch.equal(b.scale, ref.scale)
+
+
+def test_delayed_steps_in_a_graph():
+    """One delayed step captured per parity (the step number selects the
+    window slot and the record), replayed in order with new inputs copied in
+    between, equals eager steps."""
+    R, C = 256, 512
+    d = fq.desc(fq.FQ_PER_TENSOR_DELAYED, fq.FQ_IN_BF16, fq.FQ_E4M3, R, C)
+    x = torch.empty((R, C), dtype=torch.bfloat16, device="cuda")
+    out = fq.alloc_quantized(d)
+    out.amax = None
+    st, ost = fq.DelayedState(4), orc.DelayedState(4)
+    # steps 0 and 1 eagerly (warm-up), then steps 2 and 3 captured
+    xs = [W.normal((R, C), 1.0 + t, 900 + t, W.BF16) for t in range(10)]
+    for t in range(2):
+        x.copy_(dev(xs[t]))
+        fq.fq_quantize_delayed(d, x, st, out)
+        orc.quantize_delayed(xs[t], orc.E4M3, ost)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graphs = []
+    for t in (2, 3):
+        g = torch.cuda.CUDAGraph()
+        st.step = t
+        with torch.cuda.graph(g, stream=s):
+            fq.fq_quantize_delayed(d, x, st, out, advance=False)
+        graphs.append(g)
+    for t in range(2, 10):
+        if t >= 4:
+            st.step = t                   # slot t mod 4 and record t mod 2 repeat with period 4
+        x.copy_(dev(xs[t]))
+        torch.cuda.synchronize()
+        if t % 4 in (2, 3):
+            graphs[t % 2].replay()
+        else:
+            fq.fq_quantize_delayed(d, x, st, out, advance=False)
+        want = orc.quantize_delayed(xs[t], orc.E4M3, ost)
+        torch.cuda.synchronize()
+        same_bytes(host(out.row_data), want["q_row"], f"step {t} codes")
+    st.step = 10
+    fq.fq_delayed_flush(d, st)
+    torch.cuda.synchronize()
+    check_state(st, ost, "after 10 steps")
 
 
 @pytest.mark.parametrize("w", [w for w in W.LARGE if w.recipe == "delayed"], ids=lambda w: w.name)
