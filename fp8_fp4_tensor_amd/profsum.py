@@ -105,6 +105,7 @@ def source_hash(files):
 
 KERNEL_SOURCES = {"k_block_128x128": ["k_block.hip", "codec.hpp"], "k_block_1x128": ["k_block.hip", "codec.hpp"],
                   "k_mx_bf16": ["k_mx.hip", "codec.hpp"], "k_cast_tensor": ["k_tensor.hip", "codec.hpp"],
+                  "k_cast_delayed": ["k_tensor.hip", "codec.hpp"],
                   "k_nvfp4_1x16": ["k_nvfp4.hip", "k_tensor.hip", "codec.hpp"],
                   "k_nvfp4_16x16": ["k_nvfp4.hip", "k_tensor.hip", "codec.hpp"]}
 
