@@ -257,7 +257,7 @@ def cpu_baseline(hosts, threads, one_thread_fraction):
     from fp8_fp4_tensor_amd import workloads as W
 
     def run(parts, fraction):
-        total_bytes, total_t = 0, 0.0
+        total_bytes, total_t, per = 0, 0.0, {}
         with concurrent.futures.ThreadPoolExecutor(max_workers=parts) as pool:
             for w, x in hosts:
                 R, C = w.shape
@@ -268,19 +268,23 @@ def cpu_baseline(hosts, threads, one_thread_fraction):
                                  w.std, w.extra)
                 t0 = time.perf_counter()
                 oracle_partitioned(w, xs, parts, pool)
-                total_t += time.perf_counter() - t0
+                dt = time.perf_counter() - t0
+                total_t += dt
                 total_bytes += algorithmic_bytes(sub)
-        return total_bytes, total_t
+                per[w.name] = round(algorithmic_bytes(sub) / dt / 1e9, 3)
+        return total_bytes, total_t, per
 
-    nb, nt = run(threads, 1.0)
-    ob, ot = run(1, one_thread_fraction)
+    nb, nt, nper = run(threads, 1.0)
+    ob, ot, oper = run(1, one_thread_fraction)
     cpu = host_cpu()
     return {"value": round(nb / nt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"every workload of one step, all rows, split by rows over {threads} threads "
                       f"({nb / 1e9:.2f} GB algorithmic in {nt:.1f} s wall; {cpu})",
+            "per_workload_GBps": nper,
             "one_thread": {"value": round(ob / ot / 1e9, 3), "cores": 1,
                            "sample": f"every workload on its first {one_thread_fraction:.0%} of rows "
-                                     f"({ob / 1e9:.2f} GB in {ot:.1f} s)"}}
+                                     f"({ob / 1e9:.2f} GB in {ot:.1f} s)",
+                           "per_workload_GBps": oper}}
 
 
 def host_cpu():
