@@ -31,6 +31,17 @@ HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 
 
+def launches_per_call(w):
+    """Kernels one call enqueues: two passes for current scaling and NVFP4;
+    one for delayed scaling while the window is short enough to be finished
+    inside the next step's cast, else a separate finish kernel as well."""
+    if w.recipe in ("current", "nvfp4"):
+        return 2
+    if w.recipe == "delayed" and w.extra["history_len"] > 1024:
+        return 2
+    return 1
+
+
 def algorithmic_bytes(w) -> int:
     R, C = w.shape
     n = R * C
@@ -643,7 +654,7 @@ def main():
         per[j["w"].name] = {"us_per_call": round(us, 2), "GB/s": round(gbs, 1),
                             "alg_pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 1), "bytes": j["bytes"],
                             "us_rounds": [round(v, 2) for v in rounds[j["w"].name]],
-                            "kernels": 2 if j["w"].recipe in ("current", "nvfp4", "delayed") else 1}
+                            "kernels": launches_per_call(j["w"])}
     # the dominant kernel: the single-kernel workload with the largest time per call
     single = [j for j in jobs if per[j["w"].name]["kernels"] == 1]
     dom = max(single, key=lambda j: per[j["w"].name]["us_per_call"]) if single else None

@@ -155,3 +155,13 @@ def test_row_parts_cut_at_the_unit():
     assert bench.row_parts(384, 128, 3) == [(0, 128), (128, 256), (256, 384)]
     assert bench.row_parts(100, 1, 3) == [(0, 33), (33, 66), (66, 100)]
     assert bench.row_parts(96, 32, 5) == [(0, 32), (32, 64), (64, 96)]
+
+
+def test_launches_per_call():
+    """A delayed step with a window of at most 1024 slots is one kernel (its
+    finish rides in the next step's cast); the two-pass recipes are two."""
+    by = {w.name: bench.launches_per_call(w) for w in W.LARGE}
+    assert by["delayed_e4m3_act_8192x4096"] == 1 and by["current_e4m3_act_8192x4096"] == 2
+    assert by["nvfp4_1x16_act_8192x14336"] == 2 and by["block128x128_wgt_7168x18432"] == 1
+    long = W.Workload("dl", (96, 256), W.BF16, "delayed", "e4m3", extra={"history_len": 2048})
+    assert bench.launches_per_call(long) == 2
