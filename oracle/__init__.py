@@ -49,10 +49,13 @@ What pins each function (tests/test_oracle_*.py):
                        against a bit-level add-and-truncate on the fp32
                        significand and its defining properties; the
                        transform against a Hadamard matrix built by
-                       Kronecker products. The SR rule (which of the two
-                       16-bit discretizations of stochastic rounding) and
-                       the butterfly's stage order are readings the pages
-                       do not fix: parity unpinned at that level.
+                       Kronecker products, and its fp32 rounding against
+                       those factors applied as float32 matrix products
+                       in the stated stage order. The SR rule (which of the
+                       two 16-bit discretizations of stochastic rounding)
+                       and the butterfly's stage order are readings the
+                       pages do not fix: parity unpinned at that level
+                       (each is pinned to the stated reading).
   dequant              exact decode times scale; bf16 rounding against torch.
   requant (MX, pow2    brute force on tiny tensors in float64; exact
   blockwise 1x128)     transposition on grid values; equality with the

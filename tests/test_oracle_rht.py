@@ -129,3 +129,42 @@ def test_rht_spreads_block_outliers(orc):
     assert before > 3.0 and after < 1.6, (before, after)
     # the transformed blocks carry the same energy (orthogonal transform)
     assert np.allclose((yt ** 2).sum(axis=1), (xt ** 2).sum(axis=1), rtol=1e-5)
+
+
+def stage_factor(h):
+    """The butterfly stage that pairs index i with i + h (bit h of i clear)
+    as a matrix: I_(16/2h) kron H2 kron I_h, entries 0 and +-1."""
+    return np.kron(np.kron(np.eye(16 // (2 * h)), np.array([[1.0, 1.0], [1.0, -1.0]])), np.eye(h))
+
+
+def factored_rht_f32(x, signs, order):
+    """(1/4) H16 diag(s) x with H16 applied as its four Kronecker factors,
+    one float32 matrix product per factor in the given order. Each output of
+    a factor has two nonzero terms, so each product rounds a + b or a - b
+    once to float32, as one butterfly stage does. (The zero entries add +0
+    terms, so the sign of an exact zero result may differ from a butterfly's;
+    values compare equal.)"""
+    w = (x.reshape(-1, 16) * sign_vec(signs).astype(np.float32)).astype(np.float32)
+    for h in order:
+        w = np.matmul(w, stage_factor(h).T.astype(np.float32)).astype(np.float32)
+    return (w * np.float32(0.25)).reshape(x.shape)
+
+
+def test_stage_factors_multiply_to_h16():
+    P = np.eye(16)
+    for h in (1, 2, 4, 8):
+        P = stage_factor(h) @ P
+    assert np.array_equal(P, H16)
+
+
+def test_rht_fp32_stage_order(orc):
+    """The oracle's fp32 arithmetic is the stated reading: stages h = 1, 2,
+    4, 8 in that order (a different order rounds differently on inputs that
+    span many binades, and the test checks that it would be caught)."""
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal(16 * 8192) * np.exp2(rng.integers(-30, 30, 16 * 8192))).astype(np.float32)
+    for signs in (0x0000, 0xB00F, 0x6C1B):
+        y = orc.rht16(x, signs)
+        assert np.array_equal(y, factored_rht_f32(x, signs, (1, 2, 4, 8)))
+        assert not np.array_equal(y, factored_rht_f32(x, signs, (8, 4, 2, 1)))
+        assert not np.array_equal(y, factored_rht_f32(x, signs, (2, 1, 4, 8)))
