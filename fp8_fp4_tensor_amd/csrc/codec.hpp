@@ -106,6 +106,19 @@ __device__ __forceinline__ float partials_max(const float* p, int n)
     return fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
 }
 
+// A workgroup barrier that orders LDS accesses only. __syncthreads() also
+// waits for the wave's outstanding global loads and stores (on gfx9 stores
+// count in the same counter as loads); this one waits for its LDS operations
+// alone, so a tile's global stores stay in flight while the next tile is
+// staged. Only for kernels that never read back, within the launch, global
+// memory they wrote. Call from uniform control flow.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Max over a 256-thread workgroup; every thread receives it. `lds` holds 4
 // floats. Contains __syncthreads(): call from uniform control flow.
 __device__ __forceinline__ float max_workgroup(float v, float* lds)

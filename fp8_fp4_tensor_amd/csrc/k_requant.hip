@@ -14,7 +14,8 @@
 //
 // Both walk 128x128 tiles of codes with a resident grid, the next tile's
 // loads in flight while the current one is requantized, and write X^T as
-// whole 128-byte lines through a transposed LDS tile.
+// whole 128-byte lines through a transposed LDS tile; a tile's stores drain
+// while the next tile is staged and requantized.
 #include <algorithm>
 
 #include "codec.hpp"
@@ -33,23 +34,32 @@ __device__ __forceinline__ int tr_off(int row, int ch) { return row * 128 + ((ch
 // The colwise MXFP8 copy from the rowwise copy alone ([MP] "FP8 通信": the
 // EP backward step de-quantizes the rowwise FP8 data and re-quantizes it in
 // the other direction). Per 128x128 tile: the rowwise codes (16 KiB) and the
-// tile rows' E8M0 codes go to LDS; each thread takes a column pair and 32
+// tile rows' scales (as fp32) go to LDS; each thread takes a column pair and 32
 // rows, restores the values exactly (dec(q) * 2^(code-127) is exact in fp32
 // for power-of-two scales), quantizes each 32x1 column block with the MX
 // rule, and the transposed codes leave through an LDS tile as whole lines.
 // HBM traffic is one code byte in and one out per element, plus scales.
+//
+// FULL: R and C are multiples of 128, so every load and store is
+// unconditional. The first tile is peeled off the loop, so that the loop is
+// entered, like each of its iterations, with the next tile's loads followed
+// by this tile's stores in flight; the compiler then waits for the loads
+// alone before staging a tile, and with LDS-only barriers a tile's stores
+// drain while the next one is requantized.
+template <bool FULL>
 __global__ __launch_bounds__(kWG) void k_mx_requant(const uint8_t* __restrict__ q, const uint8_t* __restrict__ e,
                                                     int64_t R, int64_t C, uint8_t* __restrict__ qt,
                                                     uint8_t* __restrict__ et)
 {
     constexpr int QP = 128 + 16;  // pitch of the code tile (bytes)
+    constexpr int SP = 128 + 4;   // pitch of the scale table (floats): its four rows start in distinct banks
     __shared__ __align__(16) uint8_t qtile[128 * QP];
-    __shared__ __align__(16) uint8_t etile[128 * 4];
+    __shared__ __align__(16) float escale[4 * SP];  // [column block][tile row]: the row scales as fp32
     __shared__ __align__(16) uint8_t otile[128 * 128];
     __shared__ __align__(16) uint8_t ocode[128 * 4];
     const int64_t ntc = cdiv(C, 128), ntiles = ntc * cdiv(R, 128);
     const int64_t nbc = C / 32, nbr = R / 32;
-    // a tile's codes and E8M0 codes are loaded into registers one iteration
+    // a tile's codes and E8M0 codes are loaded into registers one tile
     // early, so they fly while the previous tile is requantized
     u32x4 v[4];
     uint32_t ew = 0;
@@ -57,34 +67,48 @@ __global__ __launch_bounds__(kWG) void k_mx_requant(const uint8_t* __restrict__ 
         int64_t tr, tc;
         tile_coords(t, ntc, tr, tc);
         const int64_t r0 = tr * 128, c0 = tc * 128;
-        const int64_t nrows_in = min((int64_t)128, R - r0), ncols_in = min((int64_t)128, C - c0);
+        if (FULL) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int i = k * kWG + threadIdx.x, row = i >> 3, seg = (i & 7) * 16;
-            v[k] = (row < nrows_in && seg < ncols_in) ? ld16_stream(q + (r0 + row) * C + c0 + seg)
-                                                      : u32x4{0u, 0u, 0u, 0u};
+            for (int k = 0; k < 4; ++k) {
+                const int i = k * kWG + threadIdx.x, row = i >> 3, seg = (i & 7) * 16;
+                v[k] = ld16_stream(q + (r0 + row) * C + c0 + seg);
+            }
+            // four E8M0 codes of a tile row: 4-byte aligned (nbc % 4 == 0)
+            if (threadIdx.x < 128)
+                ew = *reinterpret_cast<const uint32_t*>(e + (r0 + threadIdx.x) * nbc + c0 / 32);
+        } else {
+            const int64_t nrows_in = min((int64_t)128, R - r0), ncols_in = min((int64_t)128, C - c0);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int i = k * kWG + threadIdx.x, row = i >> 3, seg = (i & 7) * 16;
+                v[k] = (row < nrows_in && seg < ncols_in) ? ld16_stream(q + (r0 + row) * C + c0 + seg)
+                                                          : u32x4{0u, 0u, 0u, 0u};
+            }
+            ew = 0;
+            if (threadIdx.x < nrows_in)
+                for (int j = 0; j < ncols_in / 32; ++j)
+                    ew |= (uint32_t)e[(r0 + threadIdx.x) * nbc + c0 / 32 + j] << (8 * j);
         }
-        ew = 0;
-        if (threadIdx.x < nrows_in)
-            for (int j = 0; j < ncols_in / 32; ++j)
-                ew |= (uint32_t)e[(r0 + threadIdx.x) * nbc + c0 / 32 + j] << (8 * j);
     };
-    if ((int64_t)blockIdx.x < ntiles)
-        load_tile(blockIdx.x);
-    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    // Tile t, whose loads are in v and ew. LDS hazards between consecutive
+    // tiles: the staging writes of tile t+1 follow the second barrier of
+    // tile t (after every read of qtile and escale), and its otile / ocode
+    // writes follow its own first barrier (after every read of tile t's).
+    auto step = [&](int64_t t) {
         int64_t tr, tc;
         tile_coords(t, ntc, tr, tc);
         const int64_t r0 = tr * 128, c0 = tc * 128;
-        const int64_t nrows_in = min((int64_t)128, R - r0), ncols_in = min((int64_t)128, C - c0);
-        __syncthreads();  // the previous tile's LDS reads are done
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int i = k * kWG + threadIdx.x, row = i >> 3, seg = (i & 7) * 16;
             *reinterpret_cast<u32x4*>(qtile + row * QP + seg) = v[k];
         }
-        if (threadIdx.x < 128)
-            *reinterpret_cast<uint32_t*>(etile + threadIdx.x * 4) = ew;
-        __syncthreads();
+        if (threadIdx.x < 128) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                escale[j * SP + threadIdx.x] = e8m0_value((ew >> (8 * j)) & 0xFFu);
+        }
+        lds_barrier();
         if (t + gridDim.x < ntiles)
             load_tile(t + gridDim.x);
         const int pc = threadIdx.x & 63, rb = threadIdx.x >> 6;
@@ -95,7 +119,7 @@ __global__ __launch_bounds__(kWG) void k_mx_requant(const uint8_t* __restrict__ 
             const int row = 32 * rb + k;
             const uint32_t two = *reinterpret_cast<const uint16_t*>(qtile + row * QP + 2 * pc);
             const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)two, false);
-            const float sc = e8m0_value(etile[row * 4 + cb]);
+            const float sc = escale[cb * SP + row];
             f0[k] = d[0] * sc;
             f1[k] = d[1] * sc;
         }
@@ -114,25 +138,43 @@ __global__ __launch_bounds__(kWG) void k_mx_requant(const uint8_t* __restrict__ 
         }
         ocode[(2 * pc) * 4 + rb] = (uint8_t)code0;
         ocode[(2 * pc + 1) * 4 + rb] = (uint8_t)code1;
-        __syncthreads();
-        const int64_t nrows = ncols_in, nbytes = nrows_in;  // rows and bytes of the X^T tile
+        lds_barrier();
+        if (FULL) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int i = k * kWG + threadIdx.x, row = i >> 3, seg = (i & 7) * 16;
-            if (row < nrows && seg < nbytes)
-                st16_stream(qt + (c0 + row) * R + r0 + seg, *reinterpret_cast<const u32x4*>(otile + tr_off(row, seg >> 4)));
-        }
-        if (threadIdx.x < nrows) {
-            const int row = threadIdx.x;
-            uint8_t* dst = et + (c0 + row) * nbr + r0 / 32;
-            if (nbytes == 128 && (nbr & 3) == 0) {
-                *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(ocode + row * 4);
-            } else {
+            for (int k = 0; k < 4; ++k) {
+                const int i = k * kWG + threadIdx.x, row = i >> 3, seg = (i & 7) * 16;
+                st16_stream(qt + (c0 + row) * R + r0 + seg,
+                            *reinterpret_cast<const u32x4*>(otile + tr_off(row, seg >> 4)));
+            }
+            // four E8M0 codes of an X^T tile row: 4-byte aligned (nbr % 4 == 0)
+            if (threadIdx.x < 128)
+                *reinterpret_cast<uint32_t*>(et + (c0 + threadIdx.x) * nbr + r0 / 32) =
+                    *reinterpret_cast<const uint32_t*>(ocode + threadIdx.x * 4);
+        } else {
+            const int64_t nrows_in = min((int64_t)128, R - r0), ncols_in = min((int64_t)128, C - c0);
+            const int64_t nrows = ncols_in, nbytes = nrows_in;  // rows and bytes of the X^T tile
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int i = k * kWG + threadIdx.x, row = i >> 3, seg = (i & 7) * 16;
+                if (row < nrows && seg < nbytes)
+                    st16_stream(qt + (c0 + row) * R + r0 + seg,
+                                *reinterpret_cast<const u32x4*>(otile + tr_off(row, seg >> 4)));
+            }
+            if (threadIdx.x < nrows) {
+                const int row = threadIdx.x;
+                uint8_t* dst = et + (c0 + row) * nbr + r0 / 32;
                 for (int j = 0; j < nbytes / 32; ++j)
                     dst[j] = ocode[row * 4 + j];
             }
         }
-    }
+    };
+    int64_t t = blockIdx.x;
+    if (t >= ntiles)
+        return;
+    load_tile(t);
+    step(t);
+    for (t += gridDim.x; t < ntiles; t += gridDim.x)
+        step(t);
 }
 
 // Requantize blockwise 1x128 (power-of-two scales) in the other direction.
@@ -142,7 +184,8 @@ __global__ __launch_bounds__(kWG) void k_mx_requant(const uint8_t* __restrict__ 
 // E4M3 value times a power of two); the four waves' column maxima meet in
 // LDS to give each 128x1 block its E8M0-rule scale; the re-encoded codes go
 // through a transposed LDS tile and out as whole 128-byte lines of X^T, and
-// each X^T row's tile scale as one fp32. R and C are multiples of 128.
+// each X^T row's tile scale as one fp32. R and C are multiples of 128. The
+// first tile is peeled and the barriers order LDS only, as in k_mx_requant.
 __global__ __launch_bounds__(kWG) void k_block_requant(const uint8_t* __restrict__ q, const float* __restrict__ s,
                                                        int64_t R, int64_t C, uint8_t* __restrict__ qt,
                                                        float* __restrict__ st)
@@ -167,13 +210,13 @@ __global__ __launch_bounds__(kWG) void k_block_requant(const uint8_t* __restrict
         if (threadIdx.x < 128)
             sv = s[(r0 + threadIdx.x) * ntc + c0 / 128];
     };
-    if ((int64_t)blockIdx.x < ntiles)
-        load_tile(blockIdx.x);
-    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    // LDS hazards between consecutive tiles: qtile / stile writes of tile
+    // t+1 follow the third barrier of tile t, pmax writes follow its first
+    // barrier, otile writes its second.
+    auto step = [&](int64_t t) {
         int64_t tr, tc;
         tile_coords(t, ntc, tr, tc);
         const int64_t r0 = tr * 128, c0 = tc * 128;
-        __syncthreads();  // the previous tile's LDS reads are done
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int i = k * kWG + threadIdx.x, row = i >> 3, seg = (i & 7) * 16;
@@ -181,7 +224,7 @@ __global__ __launch_bounds__(kWG) void k_block_requant(const uint8_t* __restrict
         }
         if (threadIdx.x < 128)
             stile[threadIdx.x] = sv;
-        __syncthreads();
+        lds_barrier();
         if (t + gridDim.x < ntiles)
             load_tile(t + gridDim.x);
         const int pc = threadIdx.x & 63, rb = threadIdx.x >> 6;
@@ -197,7 +240,7 @@ __global__ __launch_bounds__(kWG) void k_block_requant(const uint8_t* __restrict
         }
         pmax[rb][2 * pc] = absmax<32>(f0);
         pmax[rb][2 * pc + 1] = absmax<32>(f1);
-        __syncthreads();
+        lds_barrier();
         const float a0 = fmaxf(fmaxf(pmax[0][2 * pc], pmax[1][2 * pc]), fmaxf(pmax[2][2 * pc], pmax[3][2 * pc]));
         const float a1 = fmaxf(fmaxf(pmax[0][2 * pc + 1], pmax[1][2 * pc + 1]),
                                fmaxf(pmax[2][2 * pc + 1], pmax[3][2 * pc + 1]));
@@ -218,13 +261,20 @@ __global__ __launch_bounds__(kWG) void k_block_requant(const uint8_t* __restrict
             st[(c0 + 2 * pc) * nsr + r0 / 128] = e8m0_value(code0);
             st[(c0 + 2 * pc + 1) * nsr + r0 / 128] = e8m0_value(code1);
         }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int i = k * kWG + threadIdx.x, row = i >> 3, seg = (i & 7) * 16;
             st16_stream(qt + (c0 + row) * R + r0 + seg, *reinterpret_cast<const u32x4*>(otile + tr_off(row, seg >> 4)));
         }
-    }
+    };
+    int64_t t = blockIdx.x;
+    if (t >= ntiles)
+        return;
+    load_tile(t);
+    step(t);
+    for (t += gridDim.x; t < ntiles; t += gridDim.x)
+        step(t);
 }
 
 }  // namespace
@@ -233,9 +283,15 @@ hipError_t launch_mx_requant(const uint8_t* q, const uint8_t* e, int64_t R, int6
                              hipStream_t stream)
 {
     const int64_t ntiles = cdiv(C, 128) * cdiv(R, 128);
-    static ResidentGrid cache;
-    const int64_t grid = std::min<int64_t>(ntiles, cache.get(k_mx_requant, kWG, 0));
-    k_mx_requant<<<(unsigned)grid, kWG, 0, stream>>>(q, e, R, C, qt, et);
+    if (R % 128 == 0 && C % 128 == 0) {
+        static ResidentGrid cache;
+        const int64_t grid = std::min<int64_t>(ntiles, cache.get(k_mx_requant<true>, kWG, 0));
+        k_mx_requant<true><<<(unsigned)grid, kWG, 0, stream>>>(q, e, R, C, qt, et);
+    } else {
+        static ResidentGrid cache;
+        const int64_t grid = std::min<int64_t>(ntiles, cache.get(k_mx_requant<false>, kWG, 0));
+        k_mx_requant<false><<<(unsigned)grid, kWG, 0, stream>>>(q, e, R, C, qt, et);
+    }
     return hipGetLastError();
 }
 
