@@ -1,7 +1,8 @@
 """Summaries of rocprofv3 runs of bench.py, for the profiles/ directory.
 
   python -m fp8_fp4_tensor_amd.profsum trace  STATS_CSV TRACE_CSV OUT.md "COMMAND"
-      per-kernel durations (calls, mean, min, max) from a --kernel-trace --stats run.
+      per-kernel durations (calls, mean, min, max) from a --kernel-trace --stats run,
+      and the dispatches of the fastest complete step in order.
 
   python -m fp8_fp4_tensor_amd.profsum traffic FETCH_CSV WRITE_CSV KERNEL WORKLOAD ROWSxCOLS OUT.json "COMMANDS"
       HBM bytes per launch of KERNEL from two --pmc runs (FETCH_SIZE, then
@@ -52,8 +53,21 @@ def trace(stats_csv, trace_csv, out_md, command):
         short = short_name(name)
         lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
-    # one step in dispatch order, from the trace: durations and gaps
     rows = sorted(_rows(trace_csv), key=lambda r: int(r["Start_Timestamp"]))
+    step = fastest_step(rows)
+    if step:
+        span = (int(step[-1]["End_Timestamp"]) - int(step[0]["Start_Timestamp"])) / 1e3
+        lines += ["", f"The fastest complete step of the library's kernels ({span:.1f} us from the first "
+                  "start to the last end; a step of the timed region, where no event sits between calls), "
+                  "dispatches in order with the gap after the previous kernel:", "",
+                  "| kernel | grid (work-items) | us | gap us |", "|---|---|---|---|"]
+        prev = None
+        for r in step:
+            s, e = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+            gap = "" if prev is None else f"{(s - prev) / 1e3:.2f}"
+            lines.append(f"| `{short_name(r['Kernel_Name'])}` | {r.get('Grid_Size_X', '')} | {(e - s) / 1e3:.2f} | {gap} |")
+            prev = e
+    # the end of the run in dispatch order: durations and gaps
     lines += ["", "Last dispatches in order (duration, gap after the previous kernel):", "",
               "| kernel | us | gap us |", "|---|---|---|"]
     prev = None
@@ -78,6 +92,26 @@ def trace(stats_csv, trace_csv, out_md, command):
     with open(os.path.splitext(out_md)[0] + ".json", "w") as f:
         json.dump({"command": command, "kernels": kernels}, f, indent=1)
         f.write("\n")
+
+
+def fastest_step(rows, last="k_nvfp4_16x16"):
+    """The library's dispatches of one bench step, from a time-ordered kernel
+    trace: the library's kernels (names in namespace fq) are cut into steps
+    after each dispatch of `last` (the step's final kernel); of the steps
+    with the most common length, the one with the shortest span from its
+    first start to its last end. Empty if `last` never ran."""
+    ours = [r for r in rows if "fq::" in r["Kernel_Name"]]
+    steps, cur = [], []
+    for r in ours:
+        cur.append(r)
+        if short_name(r["Kernel_Name"]).split("<")[0] == last:
+            steps.append(cur)
+            cur = []
+    if not steps:
+        return []
+    n = collections.Counter(len(st) for st in steps).most_common(1)[0][0]
+    full = [st for st in steps if len(st) == n]
+    return min(full, key=lambda st: int(st[-1]["End_Timestamp"]) - int(st[0]["Start_Timestamp"]))
 
 
 def _mean_counter(rows, kernel_substr, counter):

@@ -165,3 +165,20 @@ def test_launches_per_call():
     assert by["nvfp4_1x16_act_8192x14336"] == 2 and by["block128x128_wgt_7168x18432"] == 1
     long = W.Workload("dl", (96, 256), W.BF16, "delayed", "e4m3", extra={"history_len": 2048})
     assert bench.launches_per_call(long) == 2
+
+
+def test_fastest_step_from_a_trace():
+    """The step table of the trace summaries: the library's dispatches cut
+    after each final kernel of a step, the shortest full step kept; other
+    kernels (torch's) and an incomplete tail are left out."""
+    def row(name, s, e):
+        return {"Kernel_Name": name, "Start_Timestamp": str(s), "End_Timestamp": str(e)}
+    a = "void fq::(anonymous namespace)::k_amax_partial<unsigned short, 8>(x)"
+    z = "void fq::(anonymous namespace)::k_nvfp4_16x16<unsigned short>(x)"
+    rows = [row(a, 0, 10), row("at::native::copy(x)", 11, 12), row(z, 20, 40),    # span 40
+            row(a, 100, 105), row(z, 105, 120),                                     # span 20
+            row(a, 200, 230), row(z, 240, 300),                                     # span 100
+            row(a, 400, 401)]                                                       # no final kernel
+    step = profsum.fastest_step(rows)
+    assert [r["Start_Timestamp"] for r in step] == ["100", "105"]
+    assert profsum.fastest_step([row(a, 0, 1)]) == []
