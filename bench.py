@@ -442,18 +442,19 @@ def time_extras(torch, fq, L, stream_p, jobs, steps, flush):
     return out
 
 
-def time_current_split(torch, fq, L, stream_p, jobs, steps, flush):
-    """Current scaling's second read, with and without the memory-side cache:
-    fq_amax (pass 1), then fq_quantize_with_amax (pass 2) either right after
-    pass 1 (its input partly still in the 256 MB memory-side cache) or after
-    a flush (its input cold, every byte from HBM). Events bracket each pass;
-    the flush is outside them. No rocprofv3 counter on this chip separates
+def time_second_read(torch, fq, L, stream_p, jobs, steps, flush):
+    """The second read of the two-pass recipes (current scaling and NVFP4),
+    with and without the memory-side cache: fq_amax (pass 1), then
+    fq_quantize_with_amax (pass 2) either right after pass 1 (its input
+    partly still in the 256 MB memory-side cache) or after a flush (its
+    input cold, every byte from HBM). Events bracket each pass; the flush is
+    outside them. No rocprofv3 counter on this chip separates
     memory-side-cache hits from HBM reads, so this timing split is the
     evidence of how much the cache serves."""
     out = {}
     for j in jobs:
         w = j["w"]
-        if w.recipe != "current":
+        if w.recipe not in ("current", "nvfp4"):
             continue
         d = j["d"]
         amax = torch.empty(1, dtype=torch.float32, device="cuda")
@@ -477,7 +478,7 @@ def time_current_split(torch, fq, L, stream_p, jobs, steps, flush):
                 if k >= 0:
                     e[3].record()
                 if rc != fq.FQ_OK:
-                    raise fq.FqError(rc, "current split " + w.name)
+                    raise fq.FqError(rc, "second read " + w.name)
             torch.cuda.synchronize()
             p1 = 1e3 * sum(e[0].elapsed_time(e[1]) for e in ev) / steps
             p2 = 1e3 * sum(e[2].elapsed_time(e[3]) for e in ev) / steps
@@ -728,7 +729,7 @@ def main():
 
     result["torch_cast_reference"] = torch_cast_reference(torch, stream, args.steps, flush)
     if not args.no_extras:
-        result["current_scaling_second_read"] = time_current_split(torch, fq, L, sp, jobs, args.steps, flush)
+        result["second_read"] = time_second_read(torch, fq, L, sp, jobs, args.steps, flush)
         result["dequant_requant"] = time_extras(torch, fq, L, sp, jobs, args.steps, flush)
         result["small"] = time_small(torch, fq, L, sp, args.steps, flush)
     del scratch
