@@ -442,6 +442,27 @@ def time_extras(torch, fq, L, stream_p, jobs, steps, flush):
     return out
 
 
+def time_clean_cold(torch, jobs, call, steps, flush):
+    """Every workload's call from a clean cold cache (flush() outside the
+    events, as for torch's cast reference), where in the step it follows
+    kernels that have just written their outputs: the same call without the
+    write-back of the previous workload's dirty lines."""
+    out = {}
+    for j in jobs:
+        ev = [(TimingEvent(), TimingEvent()) for _ in range(steps)]
+        for k in range(-1, steps):
+            flush()
+            if k >= 0:
+                ev[k][0].record()
+            call(j)
+            if k >= 0:
+                ev[k][1].record()
+        torch.cuda.synchronize()
+        us = 1e3 * sum(a.elapsed_time(b) for a, b in ev) / steps
+        out[j["w"].name] = {"us_per_call": round(us, 2), "GB/s": round(j["bytes"] / (us * 1e-6) / 1e9, 1)}
+    return out
+
+
 def time_second_read(torch, fq, L, stream_p, jobs, steps, flush):
     """The second read of the two-pass recipes (current scaling and NVFP4),
     with and without the memory-side cache: fq_amax (pass 1), then
@@ -729,6 +750,7 @@ def main():
 
     result["torch_cast_reference"] = torch_cast_reference(torch, stream, args.steps, flush)
     if not args.no_extras:
+        result["clean_cold"] = time_clean_cold(torch, jobs, call, args.steps, flush)
         result["second_read"] = time_second_read(torch, fq, L, sp, jobs, args.steps, flush)
         result["dequant_requant"] = time_extras(torch, fq, L, sp, jobs, args.steps, flush)
         result["small"] = time_small(torch, fq, L, sp, args.steps, flush)
