@@ -229,7 +229,8 @@ def check_requant(x):
     same_bytes(host(dst.col_scale), want["e_col"], "requantized colwise E8M0")
 
 
-@pytest.mark.parametrize("shape", [(32, 32), (64, 96), (96, 64), (160, 288), (256, 384)])
+# ragged tiles, one full tile, and full tiles with several per workgroup walk
+@pytest.mark.parametrize("shape", [(32, 32), (64, 96), (96, 64), (160, 288), (256, 384), (256, 512), (512, 1024)])
 def test_mx_requant_small(shape):
     check_requant(W.student_t(shape, 3.0, shape[0] * 7 + shape[1], W.BF16))
 
