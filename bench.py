@@ -330,10 +330,11 @@ def plane_bytes(w, which):
 def time_extras(torch, fq, L, stream_p, jobs, steps, flush):
     """Dequantize (rowwise plane to bf16), MXFP8 and pow2 blockwise 1x128
     rowwise-to-colwise requantize, NVFP4 1x16 with stochastic rounding, the NVFP4 colwise copy with the RHT and
-    stochastic rounding, MX with E5M2 and E2M1 elements and blockwise with
-    power-of-two scales, at the large workloads' shapes, each call bracketed by
-    events and started cold (flush() runs before it, outside the events); not
-    part of the step."""
+    stochastic rounding, MX with E5M2 and E2M1 elements, blockwise with
+    power-of-two scales, and the rowwise-only recipes with both planes
+    (rowcol), at the large workloads' shapes, each call bracketed by events
+    and started cold (flush() runs before it, outside the events); not part
+    of the step."""
     out = {}
 
     def time_requant(d_src, c_src, d_dst, nbytes, name, ev):
@@ -410,6 +411,15 @@ def time_extras(torch, fq, L, stream_p, jobs, steps, flush):
                                  rounding=fq.FQ_ROUND_STOCHASTIC, seed=2024, offset=1,
                                  transform=fq.FQ_TRANSFORM_RHT16, rht_signs=0xA5C3),
                          2 * 2 * R * C + R * C // 2 + R * C // 16 + 4)]
+        if w.recipe in ("current", "block", "nvfp4") and w.outputs == fq.FQ_ROWWISE:
+            # the same recipe with both planes (the colwise copy for the
+            # backward GEMMs): bytes from the library's own plane sizes
+            d = j["d"]
+            drc = fq.desc(d.recipe, d.in_dtype, d.format, R, C, w.block or (0, 0), fq.FQ_ROWWISE | fq.FQ_COLWISE)
+            z = fq.fq_sizes(drc)
+            two_pass = w.recipe in ("current", "nvfp4")
+            variants.append(("rowcol", drc, (2 if two_pass else 1) * 2 * R * C + z.row_data + z.row_scale
+                             + z.col_data + z.col_scale + (4 if two_pass else 0)))
         for vname, dv, nbytes in variants:
             ov = fq.alloc_quantized(dv)
             cov = ov.c()

@@ -24,6 +24,9 @@
 //                      runs down each column. A 128-row x 64-column tile is
 //                      staged in LDS (swizzled); four lanes share a column
 //                      (DPP max) and write its 128 codes, one line of X^T.
+//   k_block_1x128_rowcol  both planes from one read: a 128x128 tile per
+//                      workgroup, rowwise from registers as k_block_1x128,
+//                      colwise from the tile staged in LDS as k_block_1x128_col.
 //   k_block_128x128    one workgroup per tile, kept in registers between the
 //                      tile max and the cast; the colwise copy is the byte
 //                      transpose of the same codes, through LDS.
@@ -147,6 +150,94 @@ __global__ __launch_bounds__(kWG) void k_block_1x128_col(const T* __restrict__ x
     *reinterpret_cast<u32x4*>(out + 16) = w1;
     if (q == 0)
         st[(c0 + c) * (R / 128) + r0 / 128] = s;
+}
+
+// Both planes of 1x128 tiles from one read: a 128x128 tile of X per
+// workgroup. The LPR lanes that load a tile row hold one 1x128 tile of X:
+// the rowwise codes and scale come straight from registers, as in
+// k_block_1x128 (a row's max by DPP; lane j of a row does the scale
+// arithmetic of round j and the others read it with a lane permute). The
+// tile is also staged in LDS, swizzled as in k_block_1x128_col, and after one
+// barrier (LDS only, so the rowwise stores drain meanwhile) quads of lanes
+// take the colwise tiles (128 rows of one column: a 1x128 tile of X^T), 64
+// columns per pass, exactly as k_block_1x128_col does. R % 128 == 0,
+// C % 128 == 0; LDS: 128 rows x 128 elements.
+template <typename T, bool POW2>
+__global__ __launch_bounds__(kWG) void k_block_1x128_rowcol(const T* __restrict__ x, int64_t R, int64_t C,
+                                                            uint8_t* __restrict__ q, float* __restrict__ s_out,
+                                                            uint8_t* __restrict__ qt, float* __restrict__ st)
+{
+    constexpr int TC = 128, E = In<T>::kE, CPR = TC / E, SW = 16 / E;  // chunks per row; swizzle step
+    constexpr int LPR = CPR, RPR = kWG / LPR, ROUNDS = 128 / RPR;      // lanes per row, rows per round
+    static_assert(ROUNDS <= LPR, "each round's scale is computed by a lane of the row");
+    extern __shared__ __align__(16) unsigned char smem[];
+    T (*tile)[TC] = reinterpret_cast<T (*)[TC]>(smem);
+    const int64_t ntc = C / TC;
+    const int64_t r0 = (int64_t)(blockIdx.x / ntc) * 128, c0 = (int64_t)(blockIdx.x % ntc) * TC;
+    const int lane = threadIdx.x & 63;
+    const int j = threadIdx.x % LPR, rr0 = threadIdx.x / LPR;  // this lane's chunk of its rows; first row
+    u32x4 v[ROUNDS];
+#pragma unroll
+    for (int k = 0; k < ROUNDS; ++k)
+        v[k] = ld16_stream(x + (r0 + rr0 + k * RPR) * C + c0 + j * E);
+    // stage for the colwise pass: chunk j of row r at chunk j ^ (SW * ((r >> 5) & 3))
+#pragma unroll
+    for (int k = 0; k < ROUNDS; ++k) {
+        const int r = rr0 + k * RPR;
+        *reinterpret_cast<u32x4*>(&tile[r][(j ^ (SW * ((r >> 5) & 3))) * E]) = v[k];
+    }
+    // rowwise: round k's row max in every lane of the row; lane j computes
+    // the scales of round j % ROUNDS and lends them to the row's other lanes
+    float a[ROUNDS];
+#pragma unroll
+    for (int k = 0; k < ROUNDS; ++k)
+        a[k] = max_lanes<LPR>(In<T>::absmax16(v[k]));
+    float asel = a[0];
+#pragma unroll
+    for (int k = 1; k < ROUNDS; ++k)
+        asel = (j % ROUNDS) == k ? a[k] : asel;
+    float alpha_sel, s_sel;
+    tile_scales<POW2>(asel, alpha_sel, s_sel);
+    const int base = lane & ~(LPR - 1);
+#pragma unroll
+    for (int k = 0; k < ROUNDS; ++k) {
+        const float alpha = __shfl(alpha_sel, base + k);
+        const int64_t row = r0 + rr0 + k * RPR;
+        float f[E];
+        In<T>::unpack(v[k], f);
+        Enc8<kE4M3, E>::store(q + row * C + c0 + j * E, f, alpha);
+        if (j == k)
+            s_out[row * ntc + c0 / 128] = s_sel;
+    }
+    lds_barrier();
+    // colwise: thread t takes column c = (t >> 2) + 64h and rows 32cq .. 32cq + 31
+    const int cq = threadIdx.x & 3;
+#pragma unroll
+    for (int h = 0; h < TC / 64; ++h) {
+        const int c = (threadIdx.x >> 2) + 64 * h;
+        const int col = ((c / E) ^ (SW * cq)) * E + (c % E);  // column c's place in rows 32cq .. 32cq + 31
+        float f[32];
+#pragma unroll
+        for (int k = 0; k < 32; ++k)
+            f[k] = In<T>::load1(&tile[32 * cq + k][0], col);
+        const float am = max_lanes4(absmax<32>(f));
+        float alpha, s;
+        tile_scales<POW2>(am, alpha, s);
+        u32x4 w0, w1;
+        w0[0] = enc4<kE4M3>(f[0], f[1], f[2], f[3], alpha);
+        w0[1] = enc4<kE4M3>(f[4], f[5], f[6], f[7], alpha);
+        w0[2] = enc4<kE4M3>(f[8], f[9], f[10], f[11], alpha);
+        w0[3] = enc4<kE4M3>(f[12], f[13], f[14], f[15], alpha);
+        w1[0] = enc4<kE4M3>(f[16], f[17], f[18], f[19], alpha);
+        w1[1] = enc4<kE4M3>(f[20], f[21], f[22], f[23], alpha);
+        w1[2] = enc4<kE4M3>(f[24], f[25], f[26], f[27], alpha);
+        w1[3] = enc4<kE4M3>(f[28], f[29], f[30], f[31], alpha);
+        uint8_t* out = qt + (c0 + c) * R + r0 + 32 * cq;
+        *reinterpret_cast<u32x4*>(out) = w0;
+        *reinterpret_cast<u32x4*>(out + 16) = w1;
+        if (cq == 0)
+            st[(c0 + c) * (R / 128) + r0 / 128] = s;
+    }
 }
 
 // 128x128 tiles; a workgroup takes NT horizontally adjacent tiles (the rows
@@ -281,6 +372,31 @@ hipError_t launch_block_1x128_colwise(const void* x, int in_bf16, int pow2, int6
         k_block_1x128_col<float, true><<<grid, kWG, 0, stream>>>(xf, R, C, qt, st);
     else
         k_block_1x128_col<float, false><<<grid, kWG, 0, stream>>>(xf, R, C, qt, st);
+    return hipGetLastError();
+}
+
+template <typename T, bool POW2>
+static void block_1x128_rowcol_t(const T* x, int64_t R, int64_t C, uint8_t* q, float* s, uint8_t* qt, float* st,
+                                 hipStream_t stream)
+{
+    const unsigned grid = (unsigned)((R / 128) * (C / 128));
+    const size_t lds = 128 * 128 * sizeof(T);
+    k_block_1x128_rowcol<T, POW2><<<grid, kWG, lds, stream>>>(x, R, C, q, s, qt, st);
+}
+
+hipError_t launch_block_1x128_rowcol(const void* x, int in_bf16, int pow2, int64_t R, int64_t C, uint8_t* q,
+                                     float* s, uint8_t* qt, float* st, hipStream_t stream)
+{
+    const uint16_t* xb = (const uint16_t*)x;
+    const float* xf = (const float*)x;
+    if (in_bf16 && pow2)
+        block_1x128_rowcol_t<uint16_t, true>(xb, R, C, q, s, qt, st, stream);
+    else if (in_bf16)
+        block_1x128_rowcol_t<uint16_t, false>(xb, R, C, q, s, qt, st, stream);
+    else if (pow2)
+        block_1x128_rowcol_t<float, true>(xf, R, C, q, s, qt, st, stream);
+    else
+        block_1x128_rowcol_t<float, false>(xf, R, C, q, s, qt, st, stream);
     return hipGetLastError();
 }
 

@@ -119,6 +119,9 @@ hipError_t launch_block_1x128(const void* x, int in_bf16, int pow2, int64_t R, i
                               hipStream_t stream);
 hipError_t launch_block_1x128_colwise(const void* x, int in_bf16, int pow2, int64_t R, int64_t C, uint8_t* qt,
                                       float* st, hipStream_t stream);
+// Both planes of 1x128 tiles from one read. R % 128 == 0, C % 128 == 0.
+hipError_t launch_block_1x128_rowcol(const void* x, int in_bf16, int pow2, int64_t R, int64_t C, uint8_t* q,
+                                     float* s, uint8_t* qt, float* st, hipStream_t stream);
 hipError_t launch_block_128x128(const void* x, int in_bf16, int pow2, int64_t R, int64_t C, uint8_t* q, float* s,
                                 uint8_t* qt, float* st, hipStream_t stream);
 

@@ -99,6 +99,12 @@ def test_full_size_block(w):
     check_block(w.make(), w.block, fq.FQ_ROWWISE)
 
 
+def test_full_size_block_1x128_both_planes():
+    """The activation workload with its colwise copy too (one read for both)."""
+    w = W.BY_NAME["block1x128_act_16384x7168"]
+    check_block(w.make(), w.block, BOTH)
+
+
 # ---------------------------------------------------------------- MXFP8
 def check_mx(x, outputs, dq=False):
     d, out = run(fq.FQ_MX, fq.FQ_E4M3, x, (1, 32), outputs)

@@ -148,6 +148,20 @@ def test_large_block_1x128_colwise(big):
     del out
 
 
+def test_large_block_1x128_both_planes(big):
+    """Both planes from one read (the fused row + col tile kernel): sampled
+    rows of X and sampled rows of X^T, past element 2^31 in each plane."""
+    d = fq.desc(fq.FQ_BLOCK_FP32, fq.FQ_IN_BF16, fq.FQ_E4M3, R, C, (1, 128), fq.FQ_ROWWISE | fq.FQ_COLWISE)
+    out = quantize(d, big)
+    want_r = orc.quantize_block(sample(big), (1, 128))
+    same_bytes(host(out.row_data[SAMPLE_ROWS]), want_r["q_row"], "rowwise codes")
+    same_bytes(host(out.row_scale.view(R, C // 128)[SAMPLE_ROWS]), want_r["s_row"], "rowwise scales")
+    want_c = orc.quantize_block(sample_cols(), (1, 128))
+    same_bytes(host(out.col_data[SAMPLE_COLS]), want_c["q_row"], "colwise codes (columns of X)")
+    same_bytes(host(out.col_scale.view(C, R // 128)[SAMPLE_COLS]), want_c["s_row"], "colwise scales")
+    del out
+
+
 def test_large_nvfp4_colwise(big):
     d = fq.desc(fq.FQ_NVFP4, fq.FQ_IN_BF16, fq.FQ_E2M1, R, C, (1, 16), fq.FQ_COLWISE)
     out = quantize(d, big)
