@@ -550,15 +550,24 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_colt(const T* __restrict__ x, int
 // Colwise copy of 16x16 blocks (BR = 16; the 1x16 copy is k_nvfp4_colt):
 // the same blocks as rowwise, so the colwise nibbles are the rowwise ones
 // transposed. Slab of 32 rows x 256 columns in LDS.
-template <typename T, int BR>
+//
+// ROW (BR = 16): the rowwise copy too, from the same read. The staged chunks
+// stay in registers; each block's multiplier goes to LDS once its column
+// pass has it, and after one more barrier every lane encodes its chunks
+// rowwise (the rowwise pass's packing, Fp4Store) and writes the block codes
+// of both planes.
+template <typename T, int BR, bool ROW = false>
 __global__ __launch_bounds__(kWG) void k_nvfp4_col(const T* __restrict__ x, int64_t R, int64_t C, ScaleSrc src,
                                                    uint8_t* __restrict__ pt, uint8_t* __restrict__ ct,
-                                                   float* S_out, float* amax_out)
+                                                   float* S_out, float* amax_out, uint8_t* __restrict__ p = nullptr,
+                                                   uint8_t* __restrict__ codes = nullptr)
 {
+    static_assert(!ROW || BR == 16, "the rowwise copy from the colwise pass needs 16x16 blocks");
     __shared__ float lds[4];
     __shared__ float rtab[128];
-    constexpr int TC = 256, E = In<T>::kE, LPR = TC / E, RPR = kWG / LPR;
+    constexpr int TC = 256, E = In<T>::kE, LPR = TC / E, RPR = kWG / LPR, NR = 32 / RPR;
     __shared__ __align__(16) T tile[32][TC];
+    __shared__ float rblk[2][TC / 16];  // ROW: the multiplier of each block of the slab
     float alpha_s, S, A;
     nvfp4_tensor(src, lds, rtab, alpha_s, S, A);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -574,11 +583,14 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_col(const T* __restrict__ x, int6
     for (int64_t t = blockIdx.x; t < nslabs; t += gridDim.x) {
         const int64_t r0 = (t / ntc) * 32, c0 = (t % ntc) * TC;
         __syncthreads();  // the previous slab's LDS reads are done
-        for (int rr = threadIdx.x / LPR; rr < 32; rr += RPR) {
-            u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        u32x4 v[NR];
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            const int rr = threadIdx.x / LPR + k * RPR;
+            v[k] = u32x4{0u, 0u, 0u, 0u};
             if (c0 + cc < C && r0 + rr < R)
-                v = ld16_stream(x + (r0 + rr) * C + c0 + cc);
-            *reinterpret_cast<u32x4*>(&tile[rr][cc]) = v;
+                v[k] = ld16_stream(x + (r0 + rr) * C + c0 + cc);
+            *reinterpret_cast<u32x4*>(&tile[rr][cc]) = v[k];
         }
         __syncthreads();
         const int c = threadIdx.x;
@@ -599,30 +611,49 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_col(const T* __restrict__ x, int6
             nvfp4_block(a, alpha_s, rtab, code, r);
             w[2 * b] = enc8_e2m1(f, r);
             w[2 * b + 1] = enc8_e2m1(f + 8, r);
+            if constexpr (ROW) {
+                if ((c & 15) == 0)
+                    rblk[b][c / 16] = r;
+            }
             if (in && b < nb) {
                 const int64_t rb = (r0 + 16 * b) / 16;
-                if constexpr (BR == 1)
+                if constexpr (BR == 1) {
                     ct[(c0 + c) * (R / 16) + rb] = (uint8_t)code;
-                else if ((c & 15) == 0)
+                } else if ((c & 15) == 0) {
                     ct[((c0 + c) / 16) * (R / 16) + rb] = (uint8_t)code;
+                    if constexpr (ROW)
+                        codes[rb * (C / 16) + (c0 + c) / 16] = (uint8_t)code;
+                }
             }
         }
-        if (!in)
-            continue;
-        // row c of the colwise plane is only 8-byte aligned (R/2 is a
-        // multiple of 8). A thread writes 8 or 16 bytes of a row: ordinary
-        // stores, so the pieces of a line meet in L2 before going to memory
-        // (streaming stores of such pieces each become a partial-line write,
-        // measured 3x slower).
-        uint8_t* out = pt + (c0 + c) * (R / 2) + r0 / 2;
-        u32x2 v2;
-        v2[0] = w[0];
-        v2[1] = w[1];
-        *reinterpret_cast<u32x2*>(out) = v2;
-        if (nb == 2) {
-            v2[0] = w[2];
-            v2[1] = w[3];
-            *reinterpret_cast<u32x2*>(out + 8) = v2;
+        if (in) {
+            // row c of the colwise plane is only 8-byte aligned (R/2 is a
+            // multiple of 8). A thread writes 8 or 16 bytes of a row: ordinary
+            // stores, so the pieces of a line meet in L2 before going to memory
+            // (streaming stores of such pieces each become a partial-line write,
+            // measured 3x slower).
+            uint8_t* out = pt + (c0 + c) * (R / 2) + r0 / 2;
+            u32x2 v2;
+            v2[0] = w[0];
+            v2[1] = w[1];
+            *reinterpret_cast<u32x2*>(out) = v2;
+            if (nb == 2) {
+                v2[0] = w[2];
+                v2[1] = w[3];
+                *reinterpret_cast<u32x2*>(out + 8) = v2;
+            }
+        }
+        if constexpr (ROW) {
+            lds_barrier();  // the slab's block multipliers are in rblk
+#pragma unroll
+            for (int k = 0; k < NR; ++k) {
+                const int rr = threadIdx.x / LPR + k * RPR;
+                if (c0 + cc < C && r0 + rr < R) {
+                    float f[E];
+                    In<T>::unpack(v[k], f);
+                    Fp4Store<E>::store(p + (r0 + rr) * (C / 2) + (c0 + cc) / 2, f, rblk[rr / 16][cc / 16]);
+                }
+            }
         }
     }
 }
@@ -633,6 +664,13 @@ void launch_t(const void* xv, int64_t R, int64_t C, int br, ScaleSrc src, uint8_
 {
     const T* x = (const T*)xv;
     constexpr int E = In<T>::kE;
+    if (p && pt && br == 16 && R > 0 && C > 0) {
+        // both planes of 16x16 blocks from one read
+        const int64_t grid = std::min<int64_t>(cdiv(R, 32) * cdiv(C, 256), kMaxSlabGrid);
+        k_nvfp4_col<T, 16, true><<<(unsigned)grid, kWG, 0, stream>>>(x, R, C, src, pt, codest, S_out, amax_out, p,
+                                                                      codes);
+        return;
+    }
     bool wrote_scalars = false;
     if (p) {
         if (sr.on) {

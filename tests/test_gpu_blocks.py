@@ -208,6 +208,12 @@ def test_full_size_nvfp4(w):
     check_nvfp4(w.make(), w.block, fq.FQ_ROWWISE)
 
 
+def test_full_size_nvfp4_16x16_both_planes():
+    """The weight workload with its colwise copy too (one block pass for both)."""
+    w = W.BY_NAME["nvfp4_16x16_wgt_14336x4096"]
+    check_nvfp4(w.make(), w.block, BOTH)
+
+
 # ---------------------------------------------------------------- per-tensor dequant
 @pytest.mark.parametrize("fmt", [fq.FQ_E4M3, fq.FQ_E5M2])
 def test_dequant_per_tensor(fmt):

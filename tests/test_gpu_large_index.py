@@ -124,6 +124,26 @@ def test_large_nvfp4(big):
     del out
 
 
+def test_large_nvfp4_16x16_both_planes(big):
+    """Both planes of 16x16 blocks from one block pass: the last block row of
+    X and the last block column (the last 16 rows of X^T), past element 2^31
+    in each plane."""
+    d = fq.desc(fq.FQ_NVFP4, fq.FQ_IN_BF16, fq.FQ_E2M1, R, C, (16, 16), fq.FQ_ROWWISE | fq.FQ_COLWISE)
+    out = quantize(d, big)
+    same_bytes(host(out.amax), f32(AMAX), "tensor amax")
+    rows = np.arange(R - 16, R)
+    want_r = orc.quantize_nvfp4(bf16_bits(values(rows[:, None], np.arange(C)[None, :])), (16, 16), amax=AMAX)
+    same_bytes(host(out.tensor_scale), f32(want_r["S"]), "tensor scale")
+    same_bytes(host(out.row_data[rows]), want_r["p_row"], "packed FP4, last block row")
+    same_bytes(host(out.row_scale.view(R // 16, C // 16)[-1:]), want_r["c_row"], "E4M3 codes, last block row")
+    cols = np.arange(C - 16, C)
+    xc = bf16_bits(values(np.arange(R)[:, None], cols[None, :]))
+    want_c = orc.quantize_nvfp4(xc, (16, 16), outputs=orc.COLWISE, amax=AMAX)
+    same_bytes(host(out.col_data[cols]), want_c["p_col"], "packed FP4 of X^T, last block row")
+    same_bytes(host(out.col_scale.view(C // 16, R // 16)[-1:]), want_c["c_col"], "E4M3 codes of X^T")
+    del out
+
+
 def test_large_current_colwise_and_dequant(big):
     d = fq.desc(fq.FQ_PER_TENSOR_CURRENT, fq.FQ_IN_BF16, fq.FQ_E4M3, R, C, (0, 0), fq.FQ_ROWWISE | fq.FQ_COLWISE)
     out = quantize(d, big)
