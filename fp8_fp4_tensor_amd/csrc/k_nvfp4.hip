@@ -38,6 +38,7 @@
 //                  Philox4x32-10 calls (8 x 16 random bits each); the colwise
 //                  kernel takes the same path per 16-row block.
 #include <algorithm>
+#include <type_traits>
 
 #include "codec.hpp"
 #include "launch.hpp"
@@ -547,6 +548,92 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_colt(const T* __restrict__ x, int
     }
 }
 
+// Both planes of 1x16 blocks from one block pass (bf16, round to nearest,
+// no transform): a 128x128 tile per workgroup. Rowwise from registers as in
+// k_nvfp4_1x16 (a block is the 16-byte chunks of a lane pair; a tile row
+// leaves as 64 contiguous bytes of nibbles). The tile is staged in LDS with
+// its 16-byte chunks XOR-swizzled by the row's 64-row half, and after one
+// LDS-only barrier thread t takes column t >> 1 over rows 64g .. 64g + 63
+// (g = t & 1): four 16x1 blocks, as k_nvfp4_colt encodes them, written as 32
+// contiguous bytes of X^T (the lane pair's pieces of a 64-byte segment meet
+// in L2) and one 4-byte word of block codes. R % 128 == 0, C % 128 == 0.
+__global__ __launch_bounds__(kWG) void k_nvfp4_1x16_rowcol(const uint16_t* __restrict__ x, int64_t R, int64_t C,
+                                                           ScaleSrc src, uint8_t* __restrict__ p,
+                                                           uint8_t* __restrict__ codes, uint8_t* __restrict__ pt,
+                                                           uint8_t* __restrict__ ct, float* S_out, float* amax_out)
+{
+    constexpr int TC = 128, E = 8, CPR = TC / E, RPR = kWG / CPR, ROUNDS = 128 / RPR;
+    __shared__ float lds[4];
+    __shared__ float rtab[128];
+    __shared__ __align__(16) uint16_t tile[128][TC];
+    const int64_t ntc = C / TC;
+    const int64_t r0 = (int64_t)(blockIdx.x / ntc) * 128, c0 = (int64_t)(blockIdx.x % ntc) * TC;
+    const int j = threadIdx.x % CPR, rr0 = threadIdx.x / CPR;  // this lane's chunk of its rows; first row
+    // the tile's loads go out before the tensor scale is resolved
+    u32x4 v[ROUNDS];
+#pragma unroll
+    for (int k = 0; k < ROUNDS; ++k)
+        v[k] = ld16_stream(x + (r0 + rr0 + k * RPR) * C + c0 + j * E);
+    float alpha_s, S, A;
+    nvfp4_tensor(src, lds, rtab, alpha_s, S, A);  // includes a workgroup barrier
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (S_out)
+            *S_out = S;
+        if (amax_out)
+            *amax_out = A;
+    }
+    // stage: chunk j of row r at chunk j ^ (4 * ((r >> 6) & 1))
+#pragma unroll
+    for (int k = 0; k < ROUNDS; ++k) {
+        const int r = rr0 + k * RPR;
+        *reinterpret_cast<u32x4*>(&tile[r][(j ^ (4 * ((r >> 6) & 1))) * E]) = v[k];
+    }
+    // rowwise: a 1x16 block is the chunk pair (j, j ^ 1)
+#pragma unroll
+    for (int k = 0; k < ROUNDS; ++k) {
+        const int64_t row = r0 + rr0 + k * RPR;
+        float f[E];
+        In<uint16_t>::unpack(v[k], f);
+        const float a = max_lanes2(absmax<E>(f));
+        uint32_t code;
+        float r;
+        nvfp4_block(a, alpha_s, rtab, code, r);
+        Fp4Store<E>::store(p + row * (C / 2) + (c0 + j * E) / 2, f, r);
+        if ((j & 1) == 0)
+            codes[row * (C / 16) + (c0 + j * E) / 16] = (uint8_t)code;
+    }
+    lds_barrier();
+    // colwise: column c, rows 64g .. 64g + 63 (column c's place in them: its
+    // chunk XOR 4g)
+    const int c = threadIdx.x >> 1, g = threadIdx.x & 1;
+    const int col = ((c / E) ^ (4 * g)) * E + (c % E);
+    u32x4 w0, w1;
+    uint32_t cw = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        float f[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            f[k] = In<uint16_t>::load1(&tile[64 * g + 16 * b + k][0], col);
+        uint32_t code;
+        float r;
+        nvfp4_block(absmax<16>(f), alpha_s, rtab, code, r);
+        const uint32_t lo = enc8_e2m1(f, r), hi = enc8_e2m1(f + 8, r);
+        if (b < 2) {
+            w0[2 * b] = lo;
+            w0[2 * b + 1] = hi;
+        } else {
+            w1[2 * b - 4] = lo;
+            w1[2 * b - 3] = hi;
+        }
+        cw |= code << (8 * b);
+    }
+    uint8_t* out = pt + (c0 + c) * (R / 2) + (r0 + 64 * g) / 2;  // 16-byte aligned: R % 128 == 0
+    *reinterpret_cast<u32x4*>(out) = w0;
+    *reinterpret_cast<u32x4*>(out + 16) = w1;
+    *reinterpret_cast<uint32_t*>(ct + (c0 + c) * (R / 16) + (r0 + 64 * g) / 16) = cw;
+}
+
 // Colwise copy of 16x16 blocks (BR = 16; the 1x16 copy is k_nvfp4_colt):
 // the same blocks as rowwise, so the colwise nibbles are the rowwise ones
 // transposed. Slab of 32 rows x 256 columns in LDS.
@@ -664,6 +751,14 @@ void launch_t(const void* xv, int64_t R, int64_t C, int br, ScaleSrc src, uint8_
 {
     const T* x = (const T*)xv;
     constexpr int E = In<T>::kE;
+    if constexpr (std::is_same<T, uint16_t>::value) {
+        if (p && pt && br == 1 && !sr.on && !rht.on && R > 0 && C > 0 && R % 128 == 0 && C % 128 == 0) {
+            // both planes of 1x16 blocks from one read
+            const unsigned grid = (unsigned)((R / 128) * (C / 128));
+            k_nvfp4_1x16_rowcol<<<grid, kWG, 0, stream>>>(x, R, C, src, p, codes, pt, codest, S_out, amax_out);
+            return;
+        }
+    }
     if (p && pt && br == 16 && R > 0 && C > 0) {
         // both planes of 16x16 blocks from one read
         const int64_t grid = std::min<int64_t>(cdiv(R, 32) * cdiv(C, 256), kMaxSlabGrid);

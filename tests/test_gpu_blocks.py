@@ -172,8 +172,10 @@ def check_nvfp4(x, block, outputs, amax_in=None, dq=False):
         dequant_check(d, out, want_fn)
 
 
+# (128, 128) and (256, 384) take the one-read both-planes pass for 1x16 blocks
+# (bf16, R and C multiples of 128)
 @pytest.mark.parametrize("block", [(1, 16), (16, 16)])
-@pytest.mark.parametrize("shape", [(16, 16), (32, 64), (48, 80), (64, 4096 + 16), (16, 2064)])
+@pytest.mark.parametrize("shape", [(16, 16), (32, 64), (48, 80), (64, 4096 + 16), (16, 2064), (128, 128), (256, 384)])
 @pytest.mark.parametrize("dt", [W.BF16, W.F32])
 def test_nvfp4_small(block, shape, dt):
     x = W.normal(shape, 1.0, shape[0] * 5 + shape[1], dt)
@@ -183,9 +185,10 @@ def test_nvfp4_small(block, shape, dt):
 
 
 @pytest.mark.parametrize("block", [(1, 16), (16, 16)])
-def test_nvfp4_with_amax(block):
+@pytest.mark.parametrize("shape", [(64, 128), (128, 256)])
+def test_nvfp4_with_amax(block, shape):
     """The block pass at a given tensor amax (e.g. reduced across shards)."""
-    x = W.normal((64, 128), 1.0, 21, W.BF16)
+    x = W.normal(shape, 1.0, 21, W.BF16)
     a = float(np.abs(W.bf16_bits_to_f32(x)).max())
     for amax_in in (a, 2.5 * a, 0.5 * a):
         check_nvfp4(x, block, BOTH, amax_in=amax_in)
@@ -199,6 +202,9 @@ def test_nvfp4_wide_range_and_zero():
     x = W.uniform_bits_bf16((64, 256), 9, max_abs=1e6)
     check_nvfp4(x, (1, 16), BOTH)
     check_nvfp4(x, (16, 16), BOTH)
+    x = W.uniform_bits_bf16((128, 256), 10, max_abs=1e6)
+    check_nvfp4(x, (1, 16), BOTH)
+    check_nvfp4(np.zeros((128, 128), np.uint16), (1, 16), BOTH)
     check_nvfp4(np.zeros((32, 32), np.uint16), (16, 16), BOTH)
     check_nvfp4(np.zeros((32, 32), np.float32), (1, 16), BOTH)
 
@@ -206,6 +212,12 @@ def test_nvfp4_wide_range_and_zero():
 @pytest.mark.parametrize("w", [w for w in W.LARGE if w.recipe == "nvfp4"], ids=lambda w: w.name)
 def test_full_size_nvfp4(w):
     check_nvfp4(w.make(), w.block, fq.FQ_ROWWISE)
+
+
+def test_full_size_nvfp4_1x16_both_planes():
+    """The activation workload with its colwise copy too (one block pass for both)."""
+    w = W.BY_NAME["nvfp4_1x16_act_8192x14336"]
+    check_nvfp4(w.make(), w.block, BOTH)
 
 
 def test_full_size_nvfp4_16x16_both_planes():

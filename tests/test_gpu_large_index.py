@@ -124,6 +124,22 @@ def test_large_nvfp4(big):
     del out
 
 
+def test_large_nvfp4_1x16_both_planes(big):
+    """Both planes of 1x16 blocks from one block pass: sampled rows of X and
+    sampled rows of X^T, past element 2^31 in each plane."""
+    d = fq.desc(fq.FQ_NVFP4, fq.FQ_IN_BF16, fq.FQ_E2M1, R, C, (1, 16), fq.FQ_ROWWISE | fq.FQ_COLWISE)
+    out = quantize(d, big)
+    same_bytes(host(out.amax), f32(AMAX), "tensor amax")
+    want_r = orc.quantize_nvfp4(sample(None), (1, 16), amax=AMAX)
+    same_bytes(host(out.tensor_scale), f32(want_r["S"]), "tensor scale")
+    same_bytes(host(out.row_data[SAMPLE_ROWS]), want_r["p_row"], "packed FP4 rows")
+    same_bytes(host(out.row_scale.view(R, C // 16)[SAMPLE_ROWS]), want_r["c_row"], "E4M3 block scales of rows")
+    want_c = orc.quantize_nvfp4(sample_cols(), (1, 16), amax=AMAX)
+    same_bytes(host(out.col_data[SAMPLE_COLS]), want_c["p_row"], "packed FP4 of X^T rows")
+    same_bytes(host(out.col_scale.view(C, R // 16)[SAMPLE_COLS]), want_c["c_row"], "E4M3 block scales of X^T rows")
+    del out
+
+
 def test_large_nvfp4_16x16_both_planes(big):
     """Both planes of 16x16 blocks from one block pass: the last block row of
     X and the last block column (the last 16 rows of X^T), past element 2^31
