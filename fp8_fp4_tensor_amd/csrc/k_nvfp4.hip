@@ -548,20 +548,25 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_colt(const T* __restrict__ x, int
     }
 }
 
-// Both planes of 1x16 blocks from one block pass (bf16, round to nearest,
-// no transform): a 128x128 tile per workgroup. Rowwise from registers as in
-// k_nvfp4_1x16 (a block is the 16-byte chunks of a lane pair; a tile row
+// The colwise copy of 1x16 blocks, with the rowwise copy from the same read
+// (ROW), from bf16: a 128x128 tile per workgroup. Rowwise from registers as
+// in k_nvfp4_1x16 (a block is the 16-byte chunks of a lane pair; a tile row
 // leaves as 64 contiguous bytes of nibbles). The tile is staged in LDS with
 // its 16-byte chunks XOR-swizzled by the row's 64-row half, and after one
 // LDS-only barrier thread t takes column t >> 1 over rows 64g .. 64g + 63
-// (g = t & 1): four 16x1 blocks, as k_nvfp4_colt encodes them, written as 32
-// contiguous bytes of X^T (the lane pair's pieces of a 64-byte segment meet
-// in L2) and one 4-byte word of block codes. R % 128 == 0, C % 128 == 0.
+// (g = t & 1): four 16x1 blocks, as k_nvfp4_colt encodes them (with its
+// random Hadamard transform and stochastic rounding when asked), written as
+// 32 contiguous bytes of X^T (the lane pair's pieces of a 64-byte segment
+// meet in L2) and one 4-byte word of block codes. R % 128 == 0,
+// C % 128 == 0. ROW only with round to nearest and no transform.
+template <bool ROW, bool SR, bool RHT>
 __global__ __launch_bounds__(kWG) void k_nvfp4_1x16_rowcol(const uint16_t* __restrict__ x, int64_t R, int64_t C,
                                                            ScaleSrc src, uint8_t* __restrict__ p,
                                                            uint8_t* __restrict__ codes, uint8_t* __restrict__ pt,
-                                                           uint8_t* __restrict__ ct, float* S_out, float* amax_out)
+                                                           uint8_t* __restrict__ ct, float* S_out, float* amax_out,
+                                                           uint64_t seed, uint64_t offset, uint32_t signs)
 {
+    static_assert(!(ROW && (SR || RHT)), "the fused rowwise copy rounds to nearest, untransformed");
     constexpr int TC = 128, E = 8, CPR = TC / E, RPR = kWG / CPR, ROUNDS = 128 / RPR;
     __shared__ float lds[4];
     __shared__ float rtab[128];
@@ -589,18 +594,20 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_1x16_rowcol(const uint16_t* __res
         *reinterpret_cast<u32x4*>(&tile[r][(j ^ (4 * ((r >> 6) & 1))) * E]) = v[k];
     }
     // rowwise: a 1x16 block is the chunk pair (j, j ^ 1)
+    if constexpr (ROW) {
 #pragma unroll
-    for (int k = 0; k < ROUNDS; ++k) {
-        const int64_t row = r0 + rr0 + k * RPR;
-        float f[E];
-        In<uint16_t>::unpack(v[k], f);
-        const float a = max_lanes2(absmax<E>(f));
-        uint32_t code;
-        float r;
-        nvfp4_block(a, alpha_s, rtab, code, r);
-        Fp4Store<E>::store(p + row * (C / 2) + (c0 + j * E) / 2, f, r);
-        if ((j & 1) == 0)
-            codes[row * (C / 16) + (c0 + j * E) / 16] = (uint8_t)code;
+        for (int k = 0; k < ROUNDS; ++k) {
+            const int64_t row = r0 + rr0 + k * RPR;
+            float f[E];
+            In<uint16_t>::unpack(v[k], f);
+            const float a = max_lanes2(absmax<E>(f));
+            uint32_t code;
+            float r;
+            nvfp4_block(a, alpha_s, rtab, code, r);
+            Fp4Store<E>::store(p + row * (C / 2) + (c0 + j * E) / 2, f, r);
+            if ((j & 1) == 0)
+                codes[row * (C / 16) + (c0 + j * E) / 16] = (uint8_t)code;
+        }
     }
     lds_barrier();
     // colwise: column c, rows 64g .. 64g + 63 (column c's place in them: its
@@ -615,10 +622,21 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_1x16_rowcol(const uint16_t* __res
 #pragma unroll
         for (int k = 0; k < 16; ++k)
             f[k] = In<uint16_t>::load1(&tile[64 * g + 16 * b + k][0], col);
+        if constexpr (RHT)
+            rht16(f, signs);
         uint32_t code;
         float r;
         nvfp4_block(absmax<16>(f), alpha_s, rtab, code, r);
-        const uint32_t lo = enc8_e2m1(f, r), hi = enc8_e2m1(f + 8, r);
+        uint32_t lo, hi;
+        if constexpr (SR) {
+            // the block's first element in X^T (flat) and the colwise plane's stream
+            const uint64_t e0 = (uint64_t)((c0 + c) * R + r0 + 64 * g + 16 * b), st = 2 * offset + 1;
+            lo = enc8_e2m1_sr(f, r, sr_group(e0 / 8, st, seed));
+            hi = enc8_e2m1_sr(f + 8, r, sr_group(e0 / 8 + 1, st, seed));
+        } else {
+            lo = enc8_e2m1(f, r);
+            hi = enc8_e2m1(f + 8, r);
+        }
         if (b < 2) {
             w0[2 * b] = lo;
             w0[2 * b + 1] = hi;
@@ -752,10 +770,27 @@ void launch_t(const void* xv, int64_t R, int64_t C, int br, ScaleSrc src, uint8_
     const T* x = (const T*)xv;
     constexpr int E = In<T>::kE;
     if constexpr (std::is_same<T, uint16_t>::value) {
-        if (p && pt && br == 1 && !sr.on && !rht.on && R > 0 && C > 0 && R % 128 == 0 && C % 128 == 0) {
-            // both planes of 1x16 blocks from one read
+        if (pt && br == 1 && R > 0 && C > 0 && R % 128 == 0 && C % 128 == 0 && (!p || (!sr.on && !rht.on))) {
+            // the colwise 1x16 copy in 128x128 tiles, and the rowwise one
+            // from the same read when both are asked for
             const unsigned grid = (unsigned)((R / 128) * (C / 128));
-            k_nvfp4_1x16_rowcol<<<grid, kWG, 0, stream>>>(x, R, C, src, p, codes, pt, codest, S_out, amax_out);
+            const uint64_t sd = sr.seed, of = sr.offset;
+            const uint32_t sg = rht.signs;
+            if (p)
+                k_nvfp4_1x16_rowcol<true, false, false><<<grid, kWG, 0, stream>>>(x, R, C, src, p, codes, pt, codest,
+                                                                                 S_out, amax_out, sd, of, sg);
+            else if (rht.on && sr.on)
+                k_nvfp4_1x16_rowcol<false, true, true><<<grid, kWG, 0, stream>>>(x, R, C, src, p, codes, pt, codest,
+                                                                                S_out, amax_out, sd, of, sg);
+            else if (rht.on)
+                k_nvfp4_1x16_rowcol<false, false, true><<<grid, kWG, 0, stream>>>(x, R, C, src, p, codes, pt, codest,
+                                                                                 S_out, amax_out, sd, of, sg);
+            else if (sr.on)
+                k_nvfp4_1x16_rowcol<false, true, false><<<grid, kWG, 0, stream>>>(x, R, C, src, p, codes, pt, codest,
+                                                                                 S_out, amax_out, sd, of, sg);
+            else
+                k_nvfp4_1x16_rowcol<false, false, false><<<grid, kWG, 0, stream>>>(x, R, C, src, p, codes, pt,
+                                                                                  codest, S_out, amax_out, sd, of, sg);
             return;
         }
     }

@@ -50,7 +50,9 @@ def check_rht(x, signs, sr=None, amax_in=None, dq=False):
     return d
 
 
-@pytest.mark.parametrize("shape", [(16, 16), (32, 64), (48, 80), (64, 4096 + 16), (16, 2064), (96, 272)])
+# (128, 128) and (256, 384) in bf16 take the 128x128-tile colwise pass
+@pytest.mark.parametrize("shape", [(16, 16), (32, 64), (48, 80), (64, 4096 + 16), (16, 2064), (96, 272), (128, 128),
+                                   (256, 384)])
 @pytest.mark.parametrize("dt", [W.BF16, W.F32])
 def test_rht_small(shape, dt):
     x = W.normal(shape, 1.0, shape[0] * 11 + shape[1], dt)
@@ -75,6 +77,9 @@ def test_rht_given_amax_and_fq_amax():
 def test_rht_wide_range_and_zero():
     x = W.uniform_bits_bf16((64, 256), 29, max_abs=1e30)
     check_rht(x, 0xBEEF)
+    x = W.uniform_bits_bf16((128, 256), 30, max_abs=1e30)
+    check_rht(x, 0xBEEF)
+    check_rht(x, 0x00FF, sr=(3, 4), amax_in=float(orc.quantize_nvfp4_rht(x, 0x00FF)["amax"]) * 2.0)
     check_rht(np.zeros((32, 32), np.uint16), 0xBEEF)
     check_rht(np.zeros((32, 32), np.float32), 0x0001, sr=(1, 1))
 
