@@ -384,17 +384,13 @@ fq_status fq_quantize(const fq_desc* d, const void* x, const fq_quantized* o, vo
             return FQ_OK;
         const int pow2 = d->scale_mode == FQ_SCALE_POW2;
         if (d->block_rows == 1) {
-            if (row && col)  // both planes from one read (R % 128 == 0 for the colwise tiles)
-                return hip_status(launch_block_1x128_rowcol(x, bf, pow2, R, C, (uint8_t*)o->rowwise.data,
-                                                            (float*)o->rowwise.scale, (uint8_t*)o->colwise.data,
-                                                            (float*)o->colwise.scale, st));
-            if (row && (s = hip_status(launch_block_1x128(x, bf, pow2, R, C, (uint8_t*)o->rowwise.data,
-                                                          (float*)o->rowwise.scale, st))) != FQ_OK)
-                return s;
+            // a colwise plane: 128x128 tiles (R % 128 == 0), the rowwise plane from the same read
             if (col)
-                return hip_status(launch_block_1x128_colwise(x, bf, pow2, R, C, (uint8_t*)o->colwise.data,
-                                                             (float*)o->colwise.scale, st));
-            return FQ_OK;
+                return hip_status(launch_block_1x128_rowcol(
+                    x, bf, pow2, R, C, row ? (uint8_t*)o->rowwise.data : nullptr,
+                    row ? (float*)o->rowwise.scale : nullptr, (uint8_t*)o->colwise.data, (float*)o->colwise.scale, st));
+            return hip_status(launch_block_1x128(x, bf, pow2, R, C, (uint8_t*)o->rowwise.data,
+                                                 (float*)o->rowwise.scale, st));
         }
         return hip_status(launch_block_128x128(x, bf, pow2, R, C, row ? (uint8_t*)o->rowwise.data : nullptr,
                                                row ? (float*)o->rowwise.scale : nullptr,

@@ -20,13 +20,13 @@
 //                      scale division for load i and the quad shares the
 //                      results by DPP, a quarter of the division work. One
 //                      read, no LDS.
-//   k_block_1x128_col  the colwise copy: 1x128 tiles of X^T, i.e. 128-row
-//                      runs down each column. A 128-row x 64-column tile is
-//                      staged in LDS (swizzled); four lanes share a column
-//                      (DPP max) and write its 128 codes, one line of X^T.
-//   k_block_1x128_rowcol  both planes from one read: a 128x128 tile per
-//                      workgroup, rowwise from registers as k_block_1x128,
-//                      colwise from the tile staged in LDS as k_block_1x128_col.
+//   k_block_1x128_rowcol  the colwise copy (1x128 tiles of X^T, i.e. 128-row
+//                      runs down each column) and, when asked, the rowwise
+//                      one from the same read: a 128x128 tile per workgroup,
+//                      rowwise from registers as k_block_1x128, colwise from
+//                      the tile staged in LDS (swizzled), four lanes sharing a
+//                      column (DPP max) and writing its 128 codes, one line
+//                      of X^T.
 //   k_block_128x128    one workgroup per tile, kept in registers between the
 //                      tile max and the cast; the colwise copy is the byte
 //                      transpose of the same codes, through LDS.
@@ -107,62 +107,20 @@ __global__ __launch_bounds__(kWG) void k_block_1x128(const T* __restrict__ x, in
     }
 }
 
-// Colwise 1x128: tiles of X^T (128 rows of one column of X). One 128-row x
-// 64-column tile per workgroup, staged in LDS with its 16-byte chunks
-// XOR-swizzled by 32-row group. Thread t takes column c = t >> 2 and rows
-// 32q .. 32q + 31, q = t & 3: the column max is a quad of lanes (two DPP
-// steps), and each lane writes 32 contiguous bytes of the 128-byte line of
-// X^T (ordinary stores: the four lanes' pieces of a line meet in L2).
-template <typename T, bool POW2>
-__global__ __launch_bounds__(kWG) void k_block_1x128_col(const T* __restrict__ x, int64_t R, int64_t C,
-                                                         uint8_t* __restrict__ qt, float* __restrict__ st)
-{
-    constexpr int TC = 64, E = In<T>::kE, CPR = TC / E, SW = 16 / E;  // chunks per row; swizzle step
-    __shared__ __align__(16) T tile[128][TC];
-    const int64_t ntc = C / TC;  // C % 128 == 0
-    const int64_t r0 = (int64_t)(blockIdx.x / ntc) * 128, c0 = (int64_t)(blockIdx.x % ntc) * TC;
-    for (int i = threadIdx.x; i < 128 * CPR; i += kWG) {
-        const int r = i / CPR, j = i % CPR;
-        const u32x4 v = ld16_stream(x + (r0 + r) * C + c0 + j * E);
-        *reinterpret_cast<u32x4*>(&tile[r][(j ^ (SW * ((r >> 5) & 3))) * E]) = v;
-    }
-    __syncthreads();
-    const int c = threadIdx.x >> 2, q = threadIdx.x & 3;
-    const int col = ((c / E) ^ (SW * q)) * E + (c % E);  // column c's place in rows 32q .. 32q + 31
-    float f[32];
-#pragma unroll
-    for (int k = 0; k < 32; ++k)
-        f[k] = In<T>::load1(&tile[32 * q + k][0], col);
-    const float a = max_lanes4(absmax<32>(f));
-    float alpha, s;
-    tile_scales<POW2>(a, alpha, s);
-    u32x4 w0, w1;
-    w0[0] = enc4<kE4M3>(f[0], f[1], f[2], f[3], alpha);
-    w0[1] = enc4<kE4M3>(f[4], f[5], f[6], f[7], alpha);
-    w0[2] = enc4<kE4M3>(f[8], f[9], f[10], f[11], alpha);
-    w0[3] = enc4<kE4M3>(f[12], f[13], f[14], f[15], alpha);
-    w1[0] = enc4<kE4M3>(f[16], f[17], f[18], f[19], alpha);
-    w1[1] = enc4<kE4M3>(f[20], f[21], f[22], f[23], alpha);
-    w1[2] = enc4<kE4M3>(f[24], f[25], f[26], f[27], alpha);
-    w1[3] = enc4<kE4M3>(f[28], f[29], f[30], f[31], alpha);
-    uint8_t* out = qt + (c0 + c) * R + r0 + 32 * q;
-    *reinterpret_cast<u32x4*>(out) = w0;
-    *reinterpret_cast<u32x4*>(out + 16) = w1;
-    if (q == 0)
-        st[(c0 + c) * (R / 128) + r0 / 128] = s;
-}
-
-// Both planes of 1x128 tiles from one read: a 128x128 tile of X per
-// workgroup. The LPR lanes that load a tile row hold one 1x128 tile of X:
-// the rowwise codes and scale come straight from registers, as in
-// k_block_1x128 (a row's max by DPP; lane j of a row does the scale
-// arithmetic of round j and the others read it with a lane permute). The
-// tile is also staged in LDS, swizzled as in k_block_1x128_col, and after one
-// barrier (LDS only, so the rowwise stores drain meanwhile) quads of lanes
-// take the colwise tiles (128 rows of one column: a 1x128 tile of X^T), 64
-// columns per pass, exactly as k_block_1x128_col does. R % 128 == 0,
-// C % 128 == 0; LDS: 128 rows x 128 elements.
-template <typename T, bool POW2>
+// The colwise copy of 1x128 tiles and, with ROW, the rowwise copy from the
+// same read: a 128x128 tile of X per workgroup. The LPR lanes that load a
+// tile row hold one 1x128 tile of X: the rowwise codes and scale come
+// straight from registers, as in k_block_1x128 (a row's max by DPP; lane j
+// of a row does the scale arithmetic of round j and the others read it with
+// a lane permute). The tile is staged in LDS with its 16-byte chunks
+// XOR-swizzled by 32-row group, and after one barrier (LDS only, so the
+// rowwise stores drain meanwhile) quads of lanes take the colwise tiles (128
+// rows of one column: a 1x128 tile of X^T), 64 columns per pass: lane q of a
+// quad reads rows 32q .. 32q + 31 of its column (distinct banks), the quad's
+// max is two DPP steps, and each lane writes 32 contiguous bytes of the
+// 128-byte line of X^T (ordinary stores: the four pieces meet in L2).
+// R % 128 == 0, C % 128 == 0; LDS: 128 rows x 128 elements.
+template <typename T, bool POW2, bool ROW = true>
 __global__ __launch_bounds__(kWG) void k_block_1x128_rowcol(const T* __restrict__ x, int64_t R, int64_t C,
                                                             uint8_t* __restrict__ q, float* __restrict__ s_out,
                                                             uint8_t* __restrict__ qt, float* __restrict__ st)
@@ -188,6 +146,7 @@ __global__ __launch_bounds__(kWG) void k_block_1x128_rowcol(const T* __restrict_
     }
     // rowwise: round k's row max in every lane of the row; lane j computes
     // the scales of round j % ROUNDS and lends them to the row's other lanes
+    if constexpr (ROW) {
     float a[ROUNDS];
 #pragma unroll
     for (int k = 0; k < ROUNDS; ++k)
@@ -208,6 +167,7 @@ __global__ __launch_bounds__(kWG) void k_block_1x128_rowcol(const T* __restrict_
         Enc8<kE4M3, E>::store(q + row * C + c0 + j * E, f, alpha);
         if (j == k)
             s_out[row * ntc + c0 / 128] = s_sel;
+    }
     }
     lds_barrier();
     // colwise: thread t takes column c = (t >> 2) + 64h and rows 32cq .. 32cq + 31
@@ -358,30 +318,16 @@ hipError_t launch_block_1x128(const void* x, int in_bf16, int pow2, int64_t R, i
     return hipGetLastError();
 }
 
-hipError_t launch_block_1x128_colwise(const void* x, int in_bf16, int pow2, int64_t R, int64_t C, uint8_t* qt,
-                                      float* st, hipStream_t stream)
-{
-    const unsigned grid = (unsigned)((C / 64) * (R / 128));
-    const uint16_t* xb = (const uint16_t*)x;
-    const float* xf = (const float*)x;
-    if (in_bf16 && pow2)
-        k_block_1x128_col<uint16_t, true><<<grid, kWG, 0, stream>>>(xb, R, C, qt, st);
-    else if (in_bf16)
-        k_block_1x128_col<uint16_t, false><<<grid, kWG, 0, stream>>>(xb, R, C, qt, st);
-    else if (pow2)
-        k_block_1x128_col<float, true><<<grid, kWG, 0, stream>>>(xf, R, C, qt, st);
-    else
-        k_block_1x128_col<float, false><<<grid, kWG, 0, stream>>>(xf, R, C, qt, st);
-    return hipGetLastError();
-}
-
 template <typename T, bool POW2>
 static void block_1x128_rowcol_t(const T* x, int64_t R, int64_t C, uint8_t* q, float* s, uint8_t* qt, float* st,
                                  hipStream_t stream)
 {
     const unsigned grid = (unsigned)((R / 128) * (C / 128));
     const size_t lds = 128 * 128 * sizeof(T);
-    k_block_1x128_rowcol<T, POW2><<<grid, kWG, lds, stream>>>(x, R, C, q, s, qt, st);
+    if (q)
+        k_block_1x128_rowcol<T, POW2, true><<<grid, kWG, lds, stream>>>(x, R, C, q, s, qt, st);
+    else
+        k_block_1x128_rowcol<T, POW2, false><<<grid, kWG, lds, stream>>>(x, R, C, q, s, qt, st);
 }
 
 hipError_t launch_block_1x128_rowcol(const void* x, int in_bf16, int pow2, int64_t R, int64_t C, uint8_t* q,

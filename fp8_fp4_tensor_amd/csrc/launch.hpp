@@ -117,9 +117,8 @@ hipError_t launch_delayed_finish(const float* rec, uint32_t tag_lo, uint32_t tag
 // pow2 = 1: tile scales rounded to the MX power of two 2^(floor(log2 a) - 8).
 hipError_t launch_block_1x128(const void* x, int in_bf16, int pow2, int64_t R, int64_t C, uint8_t* q, float* s,
                               hipStream_t stream);
-hipError_t launch_block_1x128_colwise(const void* x, int in_bf16, int pow2, int64_t R, int64_t C, uint8_t* qt,
-                                      float* st, hipStream_t stream);
-// Both planes of 1x128 tiles from one read. R % 128 == 0, C % 128 == 0.
+// The colwise copy of 1x128 tiles, and the rowwise one from the same read
+// if q is not null. R % 128 == 0, C % 128 == 0.
 hipError_t launch_block_1x128_rowcol(const void* x, int in_bf16, int pow2, int64_t R, int64_t C, uint8_t* q,
                                      float* s, uint8_t* qt, float* st, hipStream_t stream);
 hipError_t launch_block_128x128(const void* x, int in_bf16, int pow2, int64_t R, int64_t C, uint8_t* q, float* s,
