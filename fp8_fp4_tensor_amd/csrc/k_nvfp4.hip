@@ -652,6 +652,111 @@ __global__ __launch_bounds__(kWG) void k_nvfp4_1x16_rowcol(const uint16_t* __res
     *reinterpret_cast<uint32_t*>(ct + (c0 + c) * (R / 16) + (r0 + 64 * g) / 16) = cw;
 }
 
+// The colwise copy of 16x16 blocks and, with ROW, the rowwise copy from the
+// same read (bf16): a 128x128 tile per workgroup, loaded as in
+// k_nvfp4_1x16_rowcol (16 lanes per tile row, 16 rows per round), so round k
+// covers block row k of the tile and the lane pair (j, j ^ 1) block column
+// j >> 1. A block's max: the pair's, then the wave's four row groups (two
+// lane shuffles), then the four waves (LDS); 64 threads turn the tile's 64
+// block maxima into codes and multipliers, shared in LDS. The rowwise codes
+// come from registers (the rowwise pass's packing), the colwise ones from
+// the tile staged in LDS (two lanes per column, four blocks each, as in
+// k_nvfp4_1x16_rowcol). R % 128 == 0, C % 128 == 0.
+template <bool ROW>
+__global__ __launch_bounds__(kWG) void k_nvfp4_16x16_tile(const uint16_t* __restrict__ x, int64_t R, int64_t C,
+                                                          ScaleSrc src, uint8_t* __restrict__ p,
+                                                          uint8_t* __restrict__ codes, uint8_t* __restrict__ pt,
+                                                          uint8_t* __restrict__ ct, float* S_out, float* amax_out)
+{
+    constexpr int TC = 128, E = 8, CPR = TC / E, RPR = kWG / CPR, ROUNDS = 128 / RPR, NBC = TC / 16;
+    static_assert(RPR == 16, "a round is one 16-row block row");
+    __shared__ float lds[4];
+    __shared__ float rtab[128];
+    __shared__ __align__(16) uint16_t tile[128][TC];
+    __shared__ float wmax[4][ROUNDS][NBC];  // each wave's block maxima over its four rows of a round
+    __shared__ float bmul[ROUNDS][NBC];     // the tile's block multipliers
+    const int64_t ntc = C / TC;
+    const int64_t r0 = (int64_t)(blockIdx.x / ntc) * 128, c0 = (int64_t)(blockIdx.x % ntc) * TC;
+    const int j = threadIdx.x % CPR, rr0 = threadIdx.x / CPR;  // this lane's chunk of its rows; first row
+    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // the tile's loads go out before the tensor scale is resolved
+    u32x4 v[ROUNDS];
+#pragma unroll
+    for (int k = 0; k < ROUNDS; ++k)
+        v[k] = ld16_stream(x + (r0 + rr0 + k * RPR) * C + c0 + j * E);
+    float alpha_s, S, A;
+    nvfp4_tensor(src, lds, rtab, alpha_s, S, A);  // includes a workgroup barrier
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (S_out)
+            *S_out = S;
+        if (amax_out)
+            *amax_out = A;
+    }
+    // stage for the colwise pass: chunk j of row r at chunk j ^ (4 * ((r >> 6) & 1))
+#pragma unroll
+    for (int k = 0; k < ROUNDS; ++k) {
+        const int r = rr0 + k * RPR;
+        *reinterpret_cast<u32x4*>(&tile[r][(j ^ (4 * ((r >> 6) & 1))) * E]) = v[k];
+    }
+    // block maxima of block row k: the lane pair, the wave's four row groups
+    // (lanes 16 and 32 apart), then the waves
+#pragma unroll
+    for (int k = 0; k < ROUNDS; ++k) {
+        float f[E];
+        In<uint16_t>::unpack(v[k], f);
+        float m = max_lanes2(absmax<E>(f));
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        if (lane < 16 && (j & 1) == 0)
+            wmax[wv][k][j >> 1] = m;
+    }
+    lds_barrier();
+    if (threadIdx.x < ROUNDS * NBC) {
+        const int k = threadIdx.x / NBC, cb = threadIdx.x % NBC;
+        const float a = fmaxf(fmaxf(wmax[0][k][cb], wmax[1][k][cb]), fmaxf(wmax[2][k][cb], wmax[3][k][cb]));
+        uint32_t code;
+        float r;
+        nvfp4_block(a, alpha_s, rtab, code, r);
+        bmul[k][cb] = r;
+        const int64_t br = r0 / 16 + k, bc = c0 / 16 + cb;  // the block's row and column in the block grid
+        if constexpr (ROW)
+            codes[br * (C / 16) + bc] = (uint8_t)code;
+        ct[bc * (R / 16) + br] = (uint8_t)code;
+    }
+    lds_barrier();
+    if constexpr (ROW) {
+#pragma unroll
+        for (int k = 0; k < ROUNDS; ++k) {
+            float f[E];
+            In<uint16_t>::unpack(v[k], f);
+            Fp4Store<E>::store(p + (r0 + rr0 + k * RPR) * (C / 2) + (c0 + j * E) / 2, f, bmul[k][j >> 1]);
+        }
+    }
+    // colwise: column c, rows 64g .. 64g + 63 (block rows 4g .. 4g + 3)
+    const int c = threadIdx.x >> 1, g = threadIdx.x & 1;
+    const int col = ((c / E) ^ (4 * g)) * E + (c % E);
+    u32x4 w0, w1;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        float f[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            f[k] = In<uint16_t>::load1(&tile[64 * g + 16 * b + k][0], col);
+        const float r = bmul[4 * g + b][c >> 4];
+        const uint32_t lo = enc8_e2m1(f, r), hi = enc8_e2m1(f + 8, r);
+        if (b < 2) {
+            w0[2 * b] = lo;
+            w0[2 * b + 1] = hi;
+        } else {
+            w1[2 * b - 4] = lo;
+            w1[2 * b - 3] = hi;
+        }
+    }
+    uint8_t* out = pt + (c0 + c) * (R / 2) + (r0 + 64 * g) / 2;  // 16-byte aligned: R % 128 == 0
+    *reinterpret_cast<u32x4*>(out) = w0;
+    *reinterpret_cast<u32x4*>(out + 16) = w1;
+}
+
 // Colwise copy of 16x16 blocks (BR = 16; the 1x16 copy is k_nvfp4_colt):
 // the same blocks as rowwise, so the colwise nibbles are the rowwise ones
 // transposed. Slab of 32 rows x 256 columns in LDS.
@@ -791,6 +896,19 @@ void launch_t(const void* xv, int64_t R, int64_t C, int br, ScaleSrc src, uint8_
             else
                 k_nvfp4_1x16_rowcol<false, false, false><<<grid, kWG, 0, stream>>>(x, R, C, src, p, codes, pt,
                                                                                   codest, S_out, amax_out, sd, of, sg);
+            return;
+        }
+    }
+    if constexpr (std::is_same<T, uint16_t>::value) {
+        if (pt && br == 16 && R > 0 && C > 0 && R % 128 == 0 && C % 128 == 0) {
+            // the colwise copy of 16x16 blocks in 128x128 tiles, and the
+            // rowwise one from the same read when both are asked for
+            const unsigned grid = (unsigned)((R / 128) * (C / 128));
+            if (p)
+                k_nvfp4_16x16_tile<true><<<grid, kWG, 0, stream>>>(x, R, C, src, p, codes, pt, codest, S_out, amax_out);
+            else
+                k_nvfp4_16x16_tile<false><<<grid, kWG, 0, stream>>>(x, R, C, src, p, codes, pt, codest, S_out,
+                                                                     amax_out);
             return;
         }
     }

@@ -203,8 +203,10 @@ def test_nvfp4_wide_range_and_zero():
     check_nvfp4(x, (1, 16), BOTH)
     check_nvfp4(x, (16, 16), BOTH)
     x = W.uniform_bits_bf16((128, 256), 10, max_abs=1e6)
-    check_nvfp4(x, (1, 16), BOTH)
-    check_nvfp4(np.zeros((128, 128), np.uint16), (1, 16), BOTH)
+    for block in ((1, 16), (16, 16)):
+        check_nvfp4(x, block, BOTH)
+        check_nvfp4(x, block, fq.FQ_COLWISE)
+        check_nvfp4(np.zeros((128, 128), np.uint16), block, BOTH)
     check_nvfp4(np.zeros((32, 32), np.uint16), (16, 16), BOTH)
     check_nvfp4(np.zeros((32, 32), np.float32), (1, 16), BOTH)
 
