@@ -875,27 +875,40 @@ void launch_t(const void* xv, int64_t R, int64_t C, int br, ScaleSrc src, uint8_
     const T* x = (const T*)xv;
     constexpr int E = In<T>::kE;
     if constexpr (std::is_same<T, uint16_t>::value) {
-        if (pt && br == 1 && R > 0 && C > 0 && R % 128 == 0 && C % 128 == 0 && (!p || (!sr.on && !rht.on))) {
-            // the colwise 1x16 copy in 128x128 tiles, and the rowwise one
-            // from the same read when both are asked for
+        if (pt && br == 1 && R > 0 && C > 0 && R % 128 == 0 && C % 128 == 0) {
+            // the colwise 1x16 copy in 128x128 tiles, with the rowwise one
+            // from the same read when both are asked for (a transform is
+            // never asked with a rowwise plane)
             const unsigned grid = (unsigned)((R / 128) * (C / 128));
             const uint64_t sd = sr.seed, of = sr.offset;
             const uint32_t sg = rht.signs;
-            if (p)
+            if (p && !sr.on) {
                 k_nvfp4_1x16_rowcol<true, false, false><<<grid, kWG, 0, stream>>>(x, R, C, src, p, codes, pt, codest,
                                                                                  S_out, amax_out, sd, of, sg);
-            else if (rht.on && sr.on)
+                return;
+            }
+            float* s2 = S_out;
+            float* a2 = amax_out;
+            if (p) {
+                // stochastic rounding on both planes: the rowwise pass first
+                const int64_t nblk = R * C / 16;
+                const int g1 = (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(nblk, kWG), kMaxGrid1x16));
+                k_nvfp4_1x16_sr<T><<<g1, kWG, 0, stream>>>(x, nblk, src, sd, of, p, codes, S_out, amax_out);
+                s2 = nullptr;
+                a2 = nullptr;
+            }
+            if (rht.on && sr.on)
                 k_nvfp4_1x16_rowcol<false, true, true><<<grid, kWG, 0, stream>>>(x, R, C, src, p, codes, pt, codest,
-                                                                                S_out, amax_out, sd, of, sg);
+                                                                                s2, a2, sd, of, sg);
             else if (rht.on)
                 k_nvfp4_1x16_rowcol<false, false, true><<<grid, kWG, 0, stream>>>(x, R, C, src, p, codes, pt, codest,
-                                                                                 S_out, amax_out, sd, of, sg);
+                                                                                 s2, a2, sd, of, sg);
             else if (sr.on)
                 k_nvfp4_1x16_rowcol<false, true, false><<<grid, kWG, 0, stream>>>(x, R, C, src, p, codes, pt, codest,
-                                                                                 S_out, amax_out, sd, of, sg);
+                                                                                 s2, a2, sd, of, sg);
             else
                 k_nvfp4_1x16_rowcol<false, false, false><<<grid, kWG, 0, stream>>>(x, R, C, src, p, codes, pt,
-                                                                                  codest, S_out, amax_out, sd, of, sg);
+                                                                                  codest, s2, a2, sd, of, sg);
             return;
         }
     }

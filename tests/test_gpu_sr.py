@@ -56,12 +56,15 @@ def test_nvfp4_sr_small(shape, dt):
 
 @pytest.mark.parametrize("shape", [(128, 128), (256, 384)])
 def test_nvfp4_sr_colwise_tiles(shape):
-    """The colwise copy alone, bf16, R and C multiples of 128: the
-    128x128-tile colwise pass with stochastic rounding."""
+    """bf16, R and C multiples of 128: the 128x128-tile colwise pass with
+    stochastic rounding, alone and after the rowwise SR pass (both planes)."""
     x = W.normal(shape, 1.0, shape[0] * 7 + shape[1], W.BF16)
     for seed, offset in SEEDS:
         check_sr(x, fq.FQ_COLWISE, seed, offset)
-    check_sr(x, fq.FQ_COLWISE, 11, 12, amax_in=3.0 * float(np.abs(W.bf16_bits_to_f32(x)).max()))
+        check_sr(x, BOTH, seed, offset)
+    a = 3.0 * float(np.abs(W.bf16_bits_to_f32(x)).max())
+    check_sr(x, fq.FQ_COLWISE, 11, 12, amax_in=a)
+    check_sr(x, BOTH, 11, 12, amax_in=a)
 
 
 def test_nvfp4_sr_with_amax_and_special_values():
