@@ -640,11 +640,12 @@ void launch_mx_t(const void* x, int in_bf16, int64_t R, int64_t C, uint8_t* q, u
         return;
     }
     if (in_bf16) {
+        // one region per workgroup: the hardware starts each workgroup as
+        // another finishes (54.5 against 56.8 us per kernel at 8192x8192 for
+        // a resident grid striding over the regions)
         const size_t lds = qt ? 128 * (128 * kMxTiles + 8) * 2 : 0;
-        static ResidentGrid cache;
         const int64_t nregions = cdiv(C, 128 * kMxTiles) * cdiv(R, 128);
-        const int64_t grid = std::min<int64_t>(nregions, cache.get(k_mx_bf16<FMT>, kMxTiles * kWG, lds));
-        k_mx_bf16<FMT><<<(unsigned)grid, kMxTiles * kWG, lds, stream>>>((const uint16_t*)x, R, C, q, e, qt, et);
+        k_mx_bf16<FMT><<<(unsigned)nregions, kMxTiles * kWG, lds, stream>>>((const uint16_t*)x, R, C, q, e, qt, et);
     } else {
         const size_t lds = qt ? 128 * tile_pitch<float>() * 4 : 0;
         static ResidentGrid cache;
