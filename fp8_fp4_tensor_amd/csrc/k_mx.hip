@@ -298,7 +298,8 @@ __global__ __launch_bounds__(kMxTiles * kWG) void k_mx_bf16(const uint16_t* __re
         // whole u32 E8M0 words for this lane's 128-column tile
         const bool full_row_codes = c0 + (cc & ~127) + 128 <= C && (nbc & 3) == 0;
         if (qt)
-            __syncthreads();  // the previous tile's LDS reads are done
+            lds_barrier();  // the previous region's LDS reads are done (LDS-only barriers
+                            // throughout: the rowwise stores drain during the colwise half)
         {
             uint8_t* dst = q ? q + (r0 + rr0) * C + c0 + cc : nullptr;
             uint8_t* edst = q ? e + (r0 + rr0) * nbc + c0 / 32 : nullptr;
@@ -341,7 +342,7 @@ __global__ __launch_bounds__(kMxTiles * kWG) void k_mx_bf16(const uint16_t* __re
         }
         if (!qt)
             continue;
-        __syncthreads();
+        lds_barrier();
         // colwise: thread (p, rb) takes tile columns 2p, 2p+1, rows 32rb..+31
         const int pc = threadIdx.x & (64 * W - 1), rb = threadIdx.x / (64 * W);
         u32x4 w[4];
@@ -373,7 +374,7 @@ __global__ __launch_bounds__(kMxTiles * kWG) void k_mx_bf16(const uint16_t* __re
                 w[2 + (d >> 2)][d & 3] = cvt4_scaled<FMT>(a1, b1, s1);
             }
         }
-        __syncthreads();
+        lds_barrier();
         uint8_t* otile = smem;             // [TW][kOP] codes of X^T
         uint8_t* ocode = smem + TW * kOP;  // [TW][4] E8M0 codes of X^T
 #pragma unroll
@@ -383,7 +384,7 @@ __global__ __launch_bounds__(kMxTiles * kWG) void k_mx_bf16(const uint16_t* __re
         }
         ocode[(2 * pc) * 4 + rb] = (uint8_t)code0;
         ocode[(2 * pc + 1) * 4 + rb] = (uint8_t)code1;
-        __syncthreads();
+        lds_barrier();
         const int64_t nrows = min((int64_t)TW, C - c0), nbytes = min((int64_t)128, R - r0);
         {
             const int row0 = threadIdx.x >> 3, seg = (threadIdx.x & 7) * 16;
