@@ -82,6 +82,18 @@ CASES = [
     ("nvfp4_rht_sr", fq.FQ_NVFP4, fq.FQ_E2M1, (1, 16), fq.FQ_COLWISE, (48, 80),
      {"rounding": fq.FQ_ROUND_STOCHASTIC, "seed": 3, "offset": 9, "transform": fq.FQ_TRANSFORM_RHT16,
       "rht_signs": 0x3C5A}),
+    # shapes of whole 128x128 tiles: the one-read tile kernels (bf16 input)
+    ("block_1x128_cols_tiles", fq.FQ_BLOCK_FP32, fq.FQ_E4M3, (1, 128), fq.FQ_COLWISE, (256, 384), {}),
+    ("nvfp4_1x16_tiles", fq.FQ_NVFP4, fq.FQ_E2M1, (1, 16), BOTH, (256, 384), {}),
+    ("nvfp4_1x16_cols_tiles", fq.FQ_NVFP4, fq.FQ_E2M1, (1, 16), fq.FQ_COLWISE, (256, 384), {}),
+    ("nvfp4_16x16_tiles", fq.FQ_NVFP4, fq.FQ_E2M1, (16, 16), BOTH, (256, 384), {}),
+    ("nvfp4_16x16_cols_tiles", fq.FQ_NVFP4, fq.FQ_E2M1, (16, 16), fq.FQ_COLWISE, (256, 384), {}),
+    ("nvfp4_sr_tiles", fq.FQ_NVFP4, fq.FQ_E2M1, (1, 16), BOTH, (256, 384),
+     {"rounding": fq.FQ_ROUND_STOCHASTIC, "seed": 3, "offset": 9}),
+    ("nvfp4_rht_sr_tiles", fq.FQ_NVFP4, fq.FQ_E2M1, (1, 16), fq.FQ_COLWISE, (256, 384),
+     {"rounding": fq.FQ_ROUND_STOCHASTIC, "seed": 3, "offset": 9, "transform": fq.FQ_TRANSFORM_RHT16,
+      "rht_signs": 0x3C5A}),
+    ("mxfp8_regions", fq.FQ_MX, fq.FQ_E4M3, (1, 32), BOTH, (256, 512), {}),
 ]
 
 
