@@ -332,9 +332,9 @@ def time_extras(torch, fq, L, stream_p, jobs, steps, flush):
     rowwise-to-colwise requantize, NVFP4 1x16 with stochastic rounding, the NVFP4 colwise copy with the RHT and
     stochastic rounding, MX with E5M2 and E2M1 elements, blockwise with
     power-of-two scales, and the rowwise-only recipes with both planes
-    (rowcol), at the large workloads' shapes, each call bracketed by events
-    and started cold (flush() runs before it, outside the events); not part
-    of the step."""
+    (rowcol) or the colwise plane alone (colwise), at the large workloads'
+    shapes, each call bracketed by events and started cold (flush() runs
+    before it, outside the events); not part of the step."""
     out = {}
 
     def time_requant(d_src, c_src, d_dst, nbytes, name, ev):
@@ -420,6 +420,9 @@ def time_extras(torch, fq, L, stream_p, jobs, steps, flush):
             two_pass = w.recipe in ("current", "nvfp4")
             variants.append(("rowcol", drc, (2 if two_pass else 1) * 2 * R * C + z.row_data + z.row_scale
                              + z.col_data + z.col_scale + (4 if two_pass else 0)))
+            dco = fq.desc(d.recipe, d.in_dtype, d.format, R, C, w.block or (0, 0), fq.FQ_COLWISE)
+            variants.append(("colwise", dco, (2 if two_pass else 1) * 2 * R * C + z.col_data + z.col_scale
+                             + (4 if two_pass else 0)))
         for vname, dv, nbytes in variants:
             ov = fq.alloc_quantized(dv)
             cov = ov.c()
