@@ -458,11 +458,13 @@ __global__ __launch_bounds__(kWG) void k_mx_row_bf16(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------- MXFP4 from bf16
-// MXFP4 (E2M1 elements, two per byte) with the same tile walk as k_mx_bf16:
-// both planes from one read. Magnitudes are clamped as bf16 patterns to
-// 6 * 2^e (exact), then v_cvt_scalef32_pk_fp4_bf16 divides each pair by the
-// power-of-two scale and rounds to nearest even. A row of X^T gets 64 bytes
-// per tile (128 rows of 4-bit codes), written by four lanes.
+// MXFP4 (E2M1 elements, two per byte) with the region walk of k_mx_bf16:
+// both planes from one read of a 128-row x 256-column region per 512-thread
+// workgroup. Magnitudes are clamped as bf16 patterns to 6 * 2^e (exact),
+// then v_cvt_scalef32_pk_fp4_bf16 divides each pair by the power-of-two
+// scale and rounds to nearest even. A row of X gets 128 bytes of codes per
+// region (one line, from 32 lanes); a row of X^T gets 64 bytes (128 rows of
+// 4-bit codes), written by four lanes.
 constexpr int kOP4 = 64 + 16;  // pitch of the LDS tile of transposed FP4 codes
 
 // four clamped bf16 pairs (elements 2i, 2i+1 in pair i) -> one dword of E2M1, element k in bits 4k..4k+3
@@ -476,46 +478,37 @@ __device__ __forceinline__ uint32_t cvt8_fp4_scaled(uint32_t p0, uint32_t p1, ui
     return w;
 }
 
-__global__ __launch_bounds__(kWG) void k_mxfp4_bf16(const uint16_t* __restrict__ x, int64_t R, int64_t C,
-                                                    uint8_t* __restrict__ q, uint8_t* __restrict__ e,
-                                                    uint8_t* __restrict__ qt, uint8_t* __restrict__ et)
+__global__ __launch_bounds__(kMxTiles * kWG) void k_mxfp4_bf16(const uint16_t* __restrict__ x, int64_t R, int64_t C,
+                                                            uint8_t* __restrict__ q, uint8_t* __restrict__ e,
+                                                            uint8_t* __restrict__ qt, uint8_t* __restrict__ et)
 {
-    constexpr int ROUNDS = 8, P = 128 + 8;
-    static_assert(128 * kOP4 + 128 * 4 <= 128 * P * 2, "the code tile must fit in the input tile it reuses");
+    constexpr int W = kMxTiles, NT = W * kWG, TW = 128 * W, ROUNDS = 8, P = TW + 8;
+    static_assert(TW * kOP4 + TW * 4 <= 128 * P * 2, "the code tile must fit in the input region it reuses");
     extern __shared__ __align__(16) unsigned char smem[];
     uint16_t* tile = reinterpret_cast<uint16_t*>(smem);
     const int lane = threadIdx.x & 63;
-    const int64_t ntc = cdiv(C, 128), ntiles = ntc * cdiv(R, 128);
-    const int cc = (threadIdx.x & 15) * 8, rr0 = threadIdx.x >> 4;
+    const int64_t ntc = cdiv(C, TW), ntiles = ntc * cdiv(R, 128);
+    const int cc = (threadIdx.x & (16 * W - 1)) * 8, rr0 = threadIdx.x / (16 * W);
     const int64_t nbc = C / 32, nbr = R / 32;
-    // Tile t's loads are issued one iteration early, as soon as the previous
-    // tile's registers are free, so they fly while that tile's colwise half
-    // runs (measured 57.5 -> 54 us at 8192x8192, although the extra live
-    // registers cost one resident workgroup per CU).
-    u32x4 v[ROUNDS];
-    auto load_tile = [&](int64_t t) {
-        int64_t tr, tc;
-        tile_coords(t, ntc, tr, tc);
-        const int64_t r0 = tr * 128, c0 = tc * 128;
-        const bool col_in = c0 + cc < C;
-        const uint16_t* src = x + (r0 + rr0) * C + c0 + cc;
-        const int64_t step = 16 * C;
-#pragma unroll
-        for (int k = 0; k < ROUNDS; ++k) {
-            v[k] = (col_in && r0 + rr0 + 16 * k < R) ? ld16_stream(src) : u32x4{0u, 0u, 0u, 0u};
-            src += step;
-        }
-    };
-    if ((int64_t)blockIdx.x < ntiles)
-        load_tile(blockIdx.x);
     for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
         int64_t tr, tc;
         tile_coords(t, ntc, tr, tc);
-        const int64_t r0 = tr * 128, c0 = tc * 128;
+        const int64_t r0 = tr * 128, c0 = tc * TW;
         const bool col_in = c0 + cc < C;
-        const bool full_row_codes = c0 + 128 <= C && (nbc & 3) == 0;
+        u32x4 v[ROUNDS];
+        {
+            const uint16_t* src = x + (r0 + rr0) * C + c0 + cc;
+            const int64_t step = 16 * C;
+#pragma unroll
+            for (int k = 0; k < ROUNDS; ++k) {
+                v[k] = (col_in && r0 + rr0 + 16 * k < R) ? ld16_stream(src) : u32x4{0u, 0u, 0u, 0u};
+                src += step;
+            }
+        }
+        // whole u32 E8M0 words for this lane's 128-column tile
+        const bool full_row_codes = c0 + (cc & ~127) + 128 <= C && (nbc & 3) == 0;
         if (qt)
-            __syncthreads();  // the previous tile's LDS reads are done
+            lds_barrier();  // the previous region's LDS reads are done
         {
             uint8_t* dst = q ? q + (r0 + rr0) * (C / 2) + (c0 + cc) / 2 : nullptr;
             uint8_t* edst = q ? e + (r0 + rr0) * nbc + c0 / 32 : nullptr;
@@ -542,7 +535,7 @@ __global__ __launch_bounds__(kWG) void k_mxfp4_bf16(const uint16_t* __restrict__
                         st4_stream(dst, w);
                         if (full_row_codes) {
                             if (lane == rbase)
-                                *reinterpret_cast<uint32_t*>(edst) = word;
+                                *reinterpret_cast<uint32_t*>(edst + (cc & ~127) / 32) = word;
                         } else if ((lane & 3) == 0) {
                             edst[cc / 32] = (uint8_t)code;
                         }
@@ -552,13 +545,11 @@ __global__ __launch_bounds__(kWG) void k_mxfp4_bf16(const uint16_t* __restrict__
                 }
             }
         }
-        if (t + gridDim.x < ntiles)
-            load_tile(t + gridDim.x);
         if (!qt)
             continue;
-        __syncthreads();
-        // colwise: thread (p, rb) takes tile columns 2p, 2p+1, rows 32rb..+31
-        const int pc = threadIdx.x & 63, rb = threadIdx.x >> 6;
+        lds_barrier();
+        // colwise: thread (p, rb) takes region columns 2p, 2p+1, rows 32rb..+31
+        const int pc = threadIdx.x & (64 * W - 1), rb = threadIdx.x / (64 * W);
         u32x4 w0, w1;
         uint32_t code0, code1;
         {
@@ -590,25 +581,24 @@ __global__ __launch_bounds__(kWG) void k_mxfp4_bf16(const uint16_t* __restrict__
                 w1[d] = cvt8_fp4_scaled(hi[0], hi[1], hi[2], hi[3], s1);
             }
         }
-        __syncthreads();
-        uint8_t* otile = smem;               // [128][kOP4] FP4 codes of X^T (64 bytes per row)
-        uint8_t* ocode = smem + 128 * kOP4;  // [128][4] E8M0 codes of X^T
+        lds_barrier();
+        uint8_t* otile = smem;              // [TW][kOP4] FP4 codes of X^T (64 bytes per row)
+        uint8_t* ocode = smem + TW * kOP4;  // [TW][4] E8M0 codes of X^T
         *reinterpret_cast<u32x4*>(otile + (2 * pc) * kOP4 + 16 * rb) = w0;
         *reinterpret_cast<u32x4*>(otile + (2 * pc + 1) * kOP4 + 16 * rb) = w1;
         ocode[(2 * pc) * 4 + rb] = (uint8_t)code0;
         ocode[(2 * pc + 1) * 4 + rb] = (uint8_t)code1;
-        __syncthreads();
-        const int64_t nrows = min((int64_t)128, C - c0), nbytes = min((int64_t)128, R - r0) / 2;
+        lds_barrier();
+        const int64_t nrows = min((int64_t)TW, C - c0), nbytes = min((int64_t)128, R - r0) / 2;
         {
-            // 64 bytes of each X^T row per tile: ordinary stores, so the two
-            // halves of a line (from vertically adjacent tiles) can meet in L2
-            // (54.4 us at 8192x8192 against 55.9 us with streaming stores)
+            // 64 bytes of each X^T row per region: ordinary stores, so the two
+            // halves of a line (from vertically adjacent regions) can meet in L2
             const int row0 = threadIdx.x >> 2, seg = (threadIdx.x & 3) * 16;
             uint8_t* dst = qt + (c0 + row0) * (R / 2) + r0 / 2 + seg;
-            const int64_t step = 64 * (R / 2);
+            const int64_t step = (NT / 4) * (R / 2);
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const int row = row0 + 64 * k;
+            for (int k = 0; k < TW / (NT / 4); ++k) {
+                const int row = row0 + (NT / 4) * k;
                 if (row < nrows && seg < nbytes)
                     *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(otile + row * kOP4 + seg);
                 dst += step;
@@ -658,11 +648,10 @@ void launch_mx_t(const void* x, int in_bf16, int64_t R, int64_t C, uint8_t* q, u
 hipError_t launch_mxfp4_bf16(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, uint8_t* e, uint8_t* qt,
                              uint8_t* et, hipStream_t stream)
 {
-    const int64_t ntiles = cdiv(C, 128) * cdiv(R, 128);
-    const size_t lds = qt ? 128 * (128 + 8) * 2 : 0;
-    static ResidentGrid cache;
-    const int64_t grid = std::min<int64_t>(ntiles, cache.get(k_mxfp4_bf16, kWG, lds));
-    k_mxfp4_bf16<<<(unsigned)grid, kWG, lds, stream>>>(x, R, C, q, e, qt, et);
+    // one region per workgroup, as for MXFP8
+    const size_t lds = qt ? 128 * (128 * kMxTiles + 8) * 2 : 0;
+    const int64_t nregions = cdiv(C, 128 * kMxTiles) * cdiv(R, 128);
+    k_mxfp4_bf16<<<(unsigned)nregions, kMxTiles * kWG, lds, stream>>>(x, R, C, q, e, qt, et);
     return hipGetLastError();
 }
 
