@@ -1,7 +1,8 @@
 // k_mx.hip -- MX: E4M3 (MXFP8) or E5M2 elements in 32-element blocks that
 // share one E8M0 (power-of-two) scale, rowwise (1x32 along a row) and colwise
 // (32x1 down a column, stored transposed), both from a single read of the
-// input. (MXFP4 elements: k_mxfp4.hip.)
+// input. MXFP4 (E2M1 elements) from bf16 takes the same region walk
+// (k_mxfp4_bf16, below); fp32 MXFP4 input takes k_mxfp4.hip.
 //
 // Source: [MP] "混合精度训练：fp16 到 fp8" (garden.houmin.site), section
 // "MXFP8" (32-element blocks, one E8M0 scale each, value = element x scale;
