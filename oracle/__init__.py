@@ -46,8 +46,12 @@ What pins each function (tests/test_oracle_*.py):
                        pow2 blockwise against closed forms, brute force and
                        MX blocks sharing the tile exponent.
   sr, rht              Philox against torch's engine; the rounding rule
-                       against a bit-level add-and-truncate on the fp32
-                       significand and its defining properties; the
+                       (E2M1, and E4M3 / E5M2 for the per-tensor, blockwise
+                       1x128 and MX recipes) against a bit-level
+                       add-and-truncate on the fp32 significand and its
+                       defining properties, each SR recipe's elements
+                       recomputed by the test from their scaled values and
+                       their plane's random bits; the
                        transform against a Hadamard matrix built by
                        Kronecker products, and its fp32 rounding against
                        those factors applied as float32 matrix products
@@ -130,6 +134,14 @@ def _load():
         "orc_sr_bits": (_u32, [ctypes.c_uint64, ctypes.c_uint64, _u32, _i64]),
         "orc_encode_e2m1_sr": (_u32, [_f32, _u32]),
         "orc_encode_e2m1_sr_array": (None, [_p, _p, _i64, _p]),
+        "orc_encode_sr": (_u32, [ctypes.c_int, _f32, _u32]),
+        "orc_encode_sr_array": (None, [ctypes.c_int, _p, _p, _i64, _p]),
+        "orc_quantize_with_amax_sr": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, ctypes.c_int, _u32, _f32,
+                                                     ctypes.c_uint64, ctypes.c_uint64, _p, _p, _fp]),
+        "orc_quantize_block_sr": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, ctypes.c_int, _u32,
+                                                 ctypes.c_uint64, ctypes.c_uint64, _p, _p, _p, _p]),
+        "orc_quantize_mx_sr": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, ctypes.c_int, _u32, ctypes.c_uint64,
+                                              ctypes.c_uint64, _p, _p, _p, _p]),
         "orc_f32_to_bf16_array": (None, [_p, _i64, _p]),
         "orc_requant_mx_colwise": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p]),
         "orc_requant_block_colwise": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p]),
@@ -225,10 +237,16 @@ def amax(x):
 
 
 # ---------------------------------------------------------------- recipes
-def quantize_current(x, fmt, outputs=ROWWISE, shape=None):
-    """Per-tensor current scaling. Returns dict(q_row, q_col, s, amax)."""
+def quantize_current(x, fmt, outputs=ROWWISE, shape=None, sr=None):
+    """Per-tensor current scaling. Returns dict(q_row, q_col, s, amax).
+    `sr` = (seed, offset) rounds the elements stochastically."""
     p, dt, keep = _in(x)
     R, C = _shape2(keep, shape)
+    if sr is not None:
+        a = np.float32(_load().orc_amax(p, dt, R * C))
+        out = quantize_with_amax(x, fmt, a, outputs=outputs, shape=shape, sr=sr)
+        out["amax"] = a
+        return out
     q_row = np.empty(R * C, np.uint8)
     q_col = np.empty(R * C, np.uint8) if outputs & COLWISE else None
     s, a = ctypes.c_float(), ctypes.c_float()
@@ -238,15 +256,22 @@ def quantize_current(x, fmt, outputs=ROWWISE, shape=None):
                 s=np.float32(s.value), amax=np.float32(a.value))
 
 
-def quantize_with_amax(x, fmt, amax_value, outputs=ROWWISE, shape=None):
-    """Per-tensor scaling with a given (e.g. all-reduced) amax."""
+def quantize_with_amax(x, fmt, amax_value, outputs=ROWWISE, shape=None, sr=None):
+    """Per-tensor scaling with a given (e.g. all-reduced) amax.
+    `sr` = (seed, offset) rounds the elements stochastically (each plane with
+    its own random bits: the colwise copy is then not the rowwise one transposed)."""
     p, dt, keep = _in(x)
     R, C = _shape2(keep, shape)
     q_row = np.empty(R * C, np.uint8)
     q_col = np.empty(R * C, np.uint8) if outputs & COLWISE else None
     s = ctypes.c_float()
-    _check(_load().orc_quantize_with_amax(p, dt, R, C, fmt, outputs, float(np.float32(amax_value)),
-                                          _ptr(q_row), _ptr(q_col), ctypes.byref(s)), "quantize_with_amax")
+    if sr is None:
+        rc = _load().orc_quantize_with_amax(p, dt, R, C, fmt, outputs, float(np.float32(amax_value)),
+                                            _ptr(q_row), _ptr(q_col), ctypes.byref(s))
+    else:
+        rc = _load().orc_quantize_with_amax_sr(p, dt, R, C, fmt, outputs, float(np.float32(amax_value)),
+                                               int(sr[0]), int(sr[1]), _ptr(q_row), _ptr(q_col), ctypes.byref(s))
+    _check(rc, "quantize_with_amax")
     return dict(q_row=q_row.reshape(R, C), q_col=None if q_col is None else q_col.reshape(C, R),
                 s=np.float32(s.value))
 
@@ -283,9 +308,10 @@ def quantize_delayed(x, fmt, state, outputs=ROWWISE, shape=None):
                 amax=np.float32(a.value))
 
 
-def quantize_block(x, block, outputs=ROWWISE, shape=None, pow2=False):
+def quantize_block(x, block, outputs=ROWWISE, shape=None, pow2=False, sr=None):
     """Blockwise E4M3 with fp32 tile scales; block is (1,128) or (128,128);
-    pow2=True rounds each tile scale to the MX power of two."""
+    pow2=True rounds each tile scale to the MX power of two;
+    `sr` = (seed, offset) rounds the elements stochastically (1x128 only)."""
     p, dt, keep = _in(x)
     R, C = _shape2(keep, shape)
     br, bc = block
@@ -296,8 +322,15 @@ def quantize_block(x, block, outputs=ROWWISE, shape=None, pow2=False):
     s_col = None
     if outputs & COLWISE:
         s_col = np.empty(C * (R // bc) if br == 1 else (C // bc) * (R // br), np.float32)
-    _check(_load().orc_quantize_block_mode(p, dt, R, C, br, bc, 1 if pow2 else 0, outputs, _ptr(q_row),
-                                           _ptr(s_row), _ptr(q_col), _ptr(s_col)), "quantize_block")
+    if sr is None:
+        rc = _load().orc_quantize_block_mode(p, dt, R, C, br, bc, 1 if pow2 else 0, outputs, _ptr(q_row),
+                                             _ptr(s_row), _ptr(q_col), _ptr(s_col))
+    else:
+        if block != (1, 128):
+            raise ValueError("stochastic rounding is offered for 1x128 tiles")
+        rc = _load().orc_quantize_block_sr(p, dt, R, C, 1 if pow2 else 0, outputs, int(sr[0]), int(sr[1]),
+                                           _ptr(q_row), _ptr(s_row), _ptr(q_col), _ptr(s_col))
+    _check(rc, "quantize_block")
     out["q_row"] = None if q_row is None else q_row.reshape(R, C)
     out["s_row"] = None if s_row is None else s_row.reshape(R // br, C // bc)
     out["q_col"] = None if q_col is None else q_col.reshape(C, R)
@@ -308,9 +341,10 @@ def quantize_block(x, block, outputs=ROWWISE, shape=None, pow2=False):
     return out
 
 
-def quantize_mx(x, outputs=ROWWISE | COLWISE, shape=None, fmt=None):
+def quantize_mx(x, outputs=ROWWISE | COLWISE, shape=None, fmt=None, sr=None):
     """MX with E8M0 codes; rowwise 1x32 and colwise 32x1 (transposed).
-    fmt: E4M3 (default, MXFP8), E5M2, or E2M1 (MXFP4, codes packed two per byte)."""
+    fmt: E4M3 (default, MXFP8), E5M2, or E2M1 (MXFP4, codes packed two per byte);
+    `sr` = (seed, offset) rounds E4M3 / E5M2 elements stochastically."""
     p, dt, keep = _in(x)
     R, C = _shape2(keep, shape)
     fmt = E4M3 if fmt is None else fmt
@@ -319,8 +353,13 @@ def quantize_mx(x, outputs=ROWWISE | COLWISE, shape=None, fmt=None):
     e_row = np.empty(R * (C // 32), np.uint8) if outputs & ROWWISE else None
     q_col = np.empty(R * C // k, np.uint8) if outputs & COLWISE else None
     e_col = np.empty(C * (R // 32), np.uint8) if outputs & COLWISE else None
-    _check(_load().orc_quantize_mx_fmt(p, dt, R, C, fmt, outputs, _ptr(q_row), _ptr(e_row), _ptr(q_col),
-                                       _ptr(e_col)), "quantize_mx")
+    if sr is None:
+        rc = _load().orc_quantize_mx_fmt(p, dt, R, C, fmt, outputs, _ptr(q_row), _ptr(e_row), _ptr(q_col),
+                                         _ptr(e_col))
+    else:
+        rc = _load().orc_quantize_mx_sr(p, dt, R, C, fmt, outputs, int(sr[0]), int(sr[1]), _ptr(q_row),
+                                        _ptr(e_row), _ptr(q_col), _ptr(e_col))
+    _check(rc, "quantize_mx")
     return dict(q_row=None if q_row is None else q_row.reshape(R, C // k),
                 e_row=None if e_row is None else e_row.reshape(R, C // 32),
                 q_col=None if q_col is None else q_col.reshape(C, R // k),
@@ -389,6 +428,17 @@ def encode_e2m1_sr(y, u):
     assert y.shape == u.shape
     q = np.empty(y.size, np.uint8)
     _load().orc_encode_e2m1_sr_array(y.ctypes.data, u.ctypes.data, y.size, q.ctypes.data)
+    return q.reshape(y.shape)
+
+
+def encode_sr(fmt, y, u):
+    """Stochastically rounded codes of format fmt (E4M3, E5M2 or E2M1) of fp32
+    values y with 16-bit randoms u."""
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    u = np.ascontiguousarray(u, dtype=np.uint16)
+    assert y.shape == u.shape
+    q = np.empty(y.size, np.uint8)
+    _load().orc_encode_sr_array(int(fmt), y.ctypes.data, u.ctypes.data, y.size, q.ctypes.data)
     return q.reshape(y.shape)
 
 

@@ -238,6 +238,28 @@ static void transpose_f32(const float *s, int64_t R, int64_t C, float *st)
 }
 
 /* ------------------------------------------------------------------ */
+/* Stochastic rounding of one output plane (defined with the generator  */
+/* further down): on = 0 means round to nearest even.                  */
+/* ------------------------------------------------------------------ */
+typedef struct {
+    int on;
+    uint64_t seed, offset;
+    unsigned plane;
+} sr_ctx;
+
+static const sr_ctx kNoSR = {0, 0, 0, 0};
+
+unsigned orc_sr_bits(uint64_t seed, uint64_t offset, unsigned plane, int64_t e);
+unsigned orc_encode_sr(int fmt, float y, unsigned u);
+
+/* Element e of a plane: Q_fmt(y) to nearest, or stochastically with the
+ * plane's random bits for e. */
+static unsigned encode_plane(int fmt, float y, sr_ctx sr, int64_t e)
+{
+    return sr.on ? orc_encode_sr(fmt, y, orc_sr_bits(sr.seed, sr.offset, sr.plane, e)) : orc_encode(fmt, y);
+}
+
+/* ------------------------------------------------------------------ */
 /* Per-tensor scaling                                                  */
 /* ------------------------------------------------------------------ */
 
@@ -283,13 +305,14 @@ void orc_tensor_scales(float a, float fmax, float *alpha, float *s)
     *s = a / fmax;
 }
 
-/* q_i = Q(fp32(alpha * x_i)) over n elements ([CS] "Current Scaling"). */
-static void cast_run(const void *x, int dt, int64_t n, float alpha, int fmt, uint8_t *q)
+/* q_i = Q(fp32(alpha * x_i)) over n elements ([CS] "Current Scaling"),
+ * rounded to nearest or (sr.on) stochastically. */
+static void cast_run(const void *x, int dt, int64_t n, float alpha, int fmt, sr_ctx sr, uint8_t *q)
 {
     int64_t i;
     for (i = 0; i < n; i++) {
         float y = load_x(x, dt, i) * alpha;
-        q[i] = (uint8_t)orc_encode(fmt, y);
+        q[i] = (uint8_t)encode_plane(fmt, y, sr, i);
     }
 }
 
@@ -302,8 +325,8 @@ static void cast_run(const void *x, int dt, int64_t n, float alpha, int fmt, uin
  * made with the same scale ([MP] section "Per-tensor Current Scaling",
  * cast + cast_transpose).
  */
-int orc_quantize_with_amax(const void *x, int dt, int64_t R, int64_t C, int fmt, unsigned outputs,
-                           float amax, uint8_t *q_row, uint8_t *q_col, float *s_out)
+static int with_amax_core(const void *x, int dt, int64_t R, int64_t C, int fmt, unsigned outputs, float amax,
+                          int sr_on, uint64_t seed, uint64_t offset, uint8_t *q_row, uint8_t *q_col, float *s_out)
 {
     float alpha, s;
     uint8_t *q;
@@ -314,15 +337,51 @@ int orc_quantize_with_amax(const void *x, int dt, int64_t R, int64_t C, int fmt,
     if (check_finite(x, dt, R * C))
         return -1;
     orc_tensor_scales(amax, orc_fmax(fmt), &alpha, &s);
-    q = q_row ? q_row : (uint8_t *)malloc((size_t)(R * C));
-    cast_run(x, dt, R * C, alpha, fmt, q);
-    if ((outputs & ORC_COLWISE) && q_col)
-        orc_transpose_u8(q, R, C, q_col);
-    if (!q_row)
-        free(q);
+    if (sr_on) {
+        /* each plane rounded with its own random bits: the colwise copy is
+         * the recipe applied to X^T, not the transposed rowwise bytes */
+        sr_ctx sr_row = {1, seed, offset, 0}, sr_col = {1, seed, offset, 1};
+        if ((outputs & ORC_ROWWISE) && q_row)
+            cast_run(x, dt, R * C, alpha, fmt, sr_row, q_row);
+        if ((outputs & ORC_COLWISE) && q_col) {
+            void *xt = transpose_input(x, dt, R, C);
+            if (!xt)
+                return -4;
+            cast_run(xt, dt, R * C, alpha, fmt, sr_col, q_col);
+            free(xt);
+        }
+    } else {
+        q = q_row ? q_row : (uint8_t *)malloc((size_t)(R * C));
+        cast_run(x, dt, R * C, alpha, fmt, kNoSR, q);
+        if ((outputs & ORC_COLWISE) && q_col)
+            orc_transpose_u8(q, R, C, q_col);
+        if (!q_row)
+            free(q);
+    }
     if (s_out)
         *s_out = s;
     return 0;
+}
+
+int orc_quantize_with_amax(const void *x, int dt, int64_t R, int64_t C, int fmt, unsigned outputs,
+                           float amax, uint8_t *q_row, uint8_t *q_col, float *s_out)
+{
+    return with_amax_core(x, dt, R, C, fmt, outputs, amax, 0, 0, 0, q_row, q_col, s_out);
+}
+
+/*
+ * Per-tensor scaling with stochastically rounded elements ([MP] section
+ * "FP8 数据格式", rounding: round-to-nearest-even by default, stochastic
+ * rounding as an option for training stability; [LP] section 2.4 item 5: on
+ * gradients).  The scales are those of round-to-nearest; each element's
+ * fp32(alpha x) is rounded by orc_encode_sr with the random bits of its
+ * plane (orc_sr_bits, plane 0 rowwise, 1 colwise).
+ */
+int orc_quantize_with_amax_sr(const void *x, int dt, int64_t R, int64_t C, int fmt, unsigned outputs,
+                              float amax, uint64_t seed, uint64_t offset, uint8_t *q_row, uint8_t *q_col,
+                              float *s_out)
+{
+    return with_amax_core(x, dt, R, C, fmt, outputs, amax, 1, seed, offset, q_row, q_col, s_out);
 }
 
 /* Per-tensor current scaling: amax of this tensor, then scale and cast
@@ -363,7 +422,7 @@ int orc_quantize_delayed(const void *x, int dt, int64_t R, int64_t C, int fmt, u
     if (check_finite(x, dt, R * C))
         return -1;
     q = q_row ? q_row : (uint8_t *)malloc((size_t)(R * C));
-    cast_run(x, dt, R * C, *alpha, fmt, q);
+    cast_run(x, dt, R * C, *alpha, fmt, kNoSR, q);
     if ((outputs & ORC_COLWISE) && q_col)
         orc_transpose_u8(q, R, C, q_col);
     if (!q_row)
@@ -402,8 +461,8 @@ unsigned orc_mx_code_fmt(float a, int fmt);
  * s_B = 2^(floor(log2 a_B) - 8) (orc_mx_code_fmt), stored as its fp32 value,
  * and the elements are Q_E4M3(x * 2^-e) (exact scaling, saturating).
  */
-static void block_rowwise(const void *x, int dt, int64_t R, int64_t C, int br, int bc, int pow2, uint8_t *q,
-                          float *sc)
+static void block_rowwise(const void *x, int dt, int64_t R, int64_t C, int br, int bc, int pow2, sr_ctx sr,
+                          uint8_t *q, float *sc)
 {
     int64_t tr, tc, r, c;
     int64_t nbc = C / bc;
@@ -423,7 +482,7 @@ static void block_rowwise(const void *x, int dt, int64_t R, int64_t C, int br, i
             for (r = tr * br; r < (tr + 1) * br; r++)
                 for (c = tc * bc; c < (tc + 1) * bc; c++) {
                     float v = load_x(x, dt, r * C + c);
-                    q[r * C + c] = (uint8_t)orc_encode(ORC_E4M3, pow2 ? ldexpf(v, -e) : v * alpha);
+                    q[r * C + c] = (uint8_t)encode_plane(ORC_E4M3, pow2 ? ldexpf(v, -e) : v * alpha, sr, r * C + c);
                 }
         }
 }
@@ -436,12 +495,16 @@ static void block_rowwise(const void *x, int dt, int64_t R, int64_t C, int br, i
  *     scales, since a square tile quantizes to the same values either way
  *     ([MP] "Blockwise scaling", the closing remark on 2-D tiles).
  */
-int orc_quantize_block_mode(const void *x, int dt, int64_t R, int64_t C, int br, int bc, int pow2,
-                            unsigned outputs, uint8_t *q_row, float *s_row, uint8_t *q_col, float *s_col)
+static int block_core(const void *x, int dt, int64_t R, int64_t C, int br, int bc, int pow2, unsigned outputs,
+                      int sr_on, uint64_t seed, uint64_t offset, uint8_t *q_row, float *s_row, uint8_t *q_col,
+                      float *s_col)
 {
+    sr_ctx sr_row = {sr_on, seed, offset, 0}, sr_col = {sr_on, seed, offset, 1};
     if (R <= 0 || C <= 0)
         return -3;
     if (!((br == 1 && bc == 128) || (br == 128 && bc == 128)))
+        return -2;
+    if (sr_on && br != 1)
         return -2;
     if (R % br || C % bc)
         return -3;
@@ -449,18 +512,18 @@ int orc_quantize_block_mode(const void *x, int dt, int64_t R, int64_t C, int br,
         return -1;
     if (br == 1) {
         if (outputs & ORC_ROWWISE)
-            block_rowwise(x, dt, R, C, 1, bc, pow2, q_row, s_row);
+            block_rowwise(x, dt, R, C, 1, bc, pow2, sr_row, q_row, s_row);
         if (outputs & ORC_COLWISE) {
             if (R % bc)
                 return -3;
             void *xt = transpose_input(x, dt, R, C);
-            block_rowwise(xt, dt, C, R, 1, bc, pow2, q_col, s_col);
+            block_rowwise(xt, dt, C, R, 1, bc, pow2, sr_col, q_col, s_col);
             free(xt);
         }
     } else {
         uint8_t *q = q_row ? q_row : (uint8_t *)malloc((size_t)(R * C));
         float *s = s_row ? s_row : (float *)malloc(sizeof(float) * (size_t)((R / br) * (C / bc)));
-        block_rowwise(x, dt, R, C, br, bc, pow2, q, s);
+        block_rowwise(x, dt, R, C, br, bc, pow2, kNoSR, q, s);
         if (outputs & ORC_COLWISE) {
             orc_transpose_u8(q, R, C, q_col);
             transpose_f32(s, R / br, C / bc, s_col);
@@ -473,10 +536,29 @@ int orc_quantize_block_mode(const void *x, int dt, int64_t R, int64_t C, int br,
     return 0;
 }
 
+int orc_quantize_block_mode(const void *x, int dt, int64_t R, int64_t C, int br, int bc, int pow2,
+                            unsigned outputs, uint8_t *q_row, float *s_row, uint8_t *q_col, float *s_col)
+{
+    return block_core(x, dt, R, C, br, bc, pow2, outputs, 0, 0, 0, q_row, s_row, q_col, s_col);
+}
+
 int orc_quantize_block(const void *x, int dt, int64_t R, int64_t C, int br, int bc, unsigned outputs,
                        uint8_t *q_row, float *s_row, uint8_t *q_col, float *s_col)
 {
     return orc_quantize_block_mode(x, dt, R, C, br, bc, 0, outputs, q_row, s_row, q_col, s_col);
+}
+
+/*
+ * Blockwise 1x128 with stochastically rounded elements (gradients, [MP]
+ * "FP8 数据格式" rounding options; the tiles of the blockwise recipe for
+ * inputs and gradients).  Tile scales as in round-to-nearest (fp32 or
+ * power-of-two); elements by orc_encode_sr, plane 0 rowwise, 1 colwise
+ * (the recipe on X^T).  The 128x128 weight tiles stay round-to-nearest.
+ */
+int orc_quantize_block_sr(const void *x, int dt, int64_t R, int64_t C, int pow2, unsigned outputs, uint64_t seed,
+                          uint64_t offset, uint8_t *q_row, float *s_row, uint8_t *q_col, float *s_col)
+{
+    return block_core(x, dt, R, C, 1, 128, pow2, outputs, 1, seed, offset, q_row, s_row, q_col, s_col);
 }
 
 /* ------------------------------------------------------------------ */
@@ -526,7 +608,8 @@ static void pack_nibbles(const uint8_t *nib, int64_t R, int64_t C, uint8_t *p);
 
 /* Rowwise 1x32 MX blocks of a row-major [R,C] input: q = Q_fmt(x * 2^-e);
  * E2M1 codes are packed two per byte. */
-static void mx_rowwise(const void *x, int dt, int64_t R, int64_t C, int fmt, uint8_t *q, uint8_t *codes)
+static void mx_rowwise(const void *x, int dt, int64_t R, int64_t C, int fmt, sr_ctx sr, uint8_t *q,
+                       uint8_t *codes)
 {
     int64_t r, b, c, nb = C / 32;
     uint8_t *nib = fmt == ORC_E2M1 ? (uint8_t *)malloc((size_t)(R * C)) : q;
@@ -537,7 +620,7 @@ static void mx_rowwise(const void *x, int dt, int64_t R, int64_t C, int fmt, uin
             int e = (int)code - 127;
             codes[r * nb + b] = (uint8_t)code;
             for (c = b * 32; c < b * 32 + 32; c++)
-                nib[r * C + c] = (uint8_t)orc_encode(fmt, ldexpf(load_x(x, dt, r * C + c), -e));
+                nib[r * C + c] = (uint8_t)encode_plane(fmt, ldexpf(load_x(x, dt, r * C + c), -e), sr, r * C + c);
         }
     if (fmt == ORC_E2M1) {
         pack_nibbles(nib, R, C, q);
@@ -552,12 +635,15 @@ static void mx_rowwise(const void *x, int dt, int64_t R, int64_t C, int fmt, uin
  * ([MP] section "MXFP8 recipe": rowwise and colwise copies of the same
  * tensor, 1x32 and 32x1).
  */
-int orc_quantize_mx_fmt(const void *x, int dt, int64_t R, int64_t C, int fmt, unsigned outputs,
-                        uint8_t *q_row, uint8_t *e_row, uint8_t *q_col, uint8_t *e_col)
+static int mx_core(const void *x, int dt, int64_t R, int64_t C, int fmt, unsigned outputs, int sr_on,
+                   uint64_t seed, uint64_t offset, uint8_t *q_row, uint8_t *e_row, uint8_t *q_col, uint8_t *e_col)
 {
+    sr_ctx sr_row = {sr_on, seed, offset, 0}, sr_col = {sr_on, seed, offset, 1};
     if (R <= 0 || C <= 0)
         return -3;
     if (fmt != ORC_E4M3 && fmt != ORC_E5M2 && fmt != ORC_E2M1)
+        return -2;
+    if (sr_on && fmt == ORC_E2M1)
         return -2;
     if (C % 32)
         return -3;
@@ -566,13 +652,31 @@ int orc_quantize_mx_fmt(const void *x, int dt, int64_t R, int64_t C, int fmt, un
     if (check_finite(x, dt, R * C))
         return -1;
     if (outputs & ORC_ROWWISE)
-        mx_rowwise(x, dt, R, C, fmt, q_row, e_row);
+        mx_rowwise(x, dt, R, C, fmt, sr_row, q_row, e_row);
     if (outputs & ORC_COLWISE) {
         void *xt = transpose_input(x, dt, R, C);
-        mx_rowwise(xt, dt, C, R, fmt, q_col, e_col);
+        mx_rowwise(xt, dt, C, R, fmt, sr_col, q_col, e_col);
         free(xt);
     }
     return 0;
+}
+
+int orc_quantize_mx_fmt(const void *x, int dt, int64_t R, int64_t C, int fmt, unsigned outputs,
+                        uint8_t *q_row, uint8_t *e_row, uint8_t *q_col, uint8_t *e_col)
+{
+    return mx_core(x, dt, R, C, fmt, outputs, 0, 0, 0, q_row, e_row, q_col, e_col);
+}
+
+/*
+ * MX with E4M3 or E5M2 elements rounded stochastically ([MP] "FP8 数据格式"
+ * rounding options, "MXFP8 recipe" blocks).  E8M0 block scales as in
+ * round-to-nearest; elements x * 2^-e (exact) by orc_encode_sr, plane 0
+ * rowwise, 1 colwise.
+ */
+int orc_quantize_mx_sr(const void *x, int dt, int64_t R, int64_t C, int fmt, unsigned outputs, uint64_t seed,
+                       uint64_t offset, uint8_t *q_row, uint8_t *e_row, uint8_t *q_col, uint8_t *e_col)
+{
+    return mx_core(x, dt, R, C, fmt, outputs, 1, seed, offset, q_row, e_row, q_col, e_col);
 }
 
 int orc_quantize_mx(const void *x, int dt, int64_t R, int64_t C, unsigned outputs,
@@ -709,14 +813,43 @@ void orc_encode_e2m1_sr_array(const float *y, const uint16_t *u, int64_t n, uint
         q[i] = (uint8_t)orc_encode_e2m1_sr(y[i], u[i]);
 }
 
-/* Stochastic rounding of one plane: on = 0 means round to nearest even. */
-typedef struct {
-    int on;
-    uint64_t seed, offset;
-    unsigned plane;
-} sr_ctx;
+/*
+ * Stochastic rounding to any element format (E4M3, E5M2 or E2M1), the
+ * reading of orc_encode_e2m1_sr carried to the 8-bit grids: for |y| between
+ * the neighbouring representable magnitudes lo <= |y| < hi of the format
+ * (subnormals included), round up iff u + g * 2^16 >= 2^16 with
+ * g = (|y| - lo) / (hi - lo); magnitudes at or above the largest finite
+ * value give it; the sign is kept, also on zero.  Every quantity is exact
+ * in binary64 (|y| - lo and the division by a power of two).
+ */
+unsigned orc_encode_sr(int fmt, float y, unsigned u)
+{
+    const double *v = value_table(fmt);
+    unsigned top = orc_max_code(fmt);
+    unsigned sign = signbit(y) ? (1u << (FMT[fmt].bits - 1)) : 0u;
+    double a = fabs((double)y), g;
+    unsigned lo = 0, hi = top;
+    if (a >= v[top])
+        return sign | top;
+    while (hi - lo > 1) {
+        unsigned mid = (lo + hi) / 2;
+        if (v[mid] <= a)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    /* v[lo] <= a < v[hi], hi = lo + 1 */
+    g = (a - v[lo]) / (v[hi] - v[lo]);
+    return sign | (g * 65536.0 >= (double)(65536u - (u & 0xFFFFu)) ? hi : lo);
+}
 
-static const sr_ctx kNoSR = {0, 0, 0, 0};
+void orc_encode_sr_array(int fmt, const float *y, const uint16_t *u, int64_t n, uint8_t *q)
+{
+    int64_t i;
+    for (i = 0; i < n; i++)
+        q[i] = (uint8_t)orc_encode_sr(fmt, y[i], u[i]);
+}
+
 
 /* One block of NVFP4: returns the E4M3 scale code and writes the nibbles
  * (0..15) of its elements.  Only the elements are rounded stochastically
@@ -1047,7 +1180,7 @@ int orc_requant_mx_colwise(const uint8_t *q_row, const uint8_t *e_row, int64_t R
     orc_dequant_mx(q_row, e_row, R, C, xhat);
     xt = (float *)malloc(sizeof(float) * (size_t)(R * C));
     transpose_f32(xhat, R, C, xt);
-    mx_rowwise(xt, ORC_IN_F32, C, R, ORC_E4M3, q_col, e_col);
+    mx_rowwise(xt, ORC_IN_F32, C, R, ORC_E4M3, kNoSR, q_col, e_col);
     free(xt);
     free(xhat);
     return 0;
@@ -1075,7 +1208,7 @@ int orc_requant_block_colwise(const uint8_t *q_row, const float *s_row, int64_t 
     orc_dequant_block(q_row, s_row, R, C, 1, 128, xhat);
     xt = (float *)malloc(sizeof(float) * (size_t)(R * C));
     transpose_f32(xhat, R, C, xt);
-    block_rowwise(xt, ORC_IN_F32, C, R, 1, 128, 1, q_col, s_col);
+    block_rowwise(xt, ORC_IN_F32, C, R, 1, 128, 1, kNoSR, q_col, s_col);
     free(xt);
     free(xhat);
     return 0;
