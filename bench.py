@@ -330,8 +330,10 @@ def plane_bytes(w, which):
 def time_extras(torch, fq, L, stream_p, jobs, steps, flush):
     """Dequantize (rowwise plane to bf16), MXFP8 and pow2 blockwise 1x128
     rowwise-to-colwise requantize, NVFP4 1x16 with stochastic rounding, the NVFP4 colwise copy with the RHT and
-    stochastic rounding, MX with E5M2 and E2M1 elements, blockwise with
-    power-of-two scales, and the rowwise-only recipes with both planes
+    stochastic rounding, stochastic rounding of the 8-bit elements (the E5M2
+    gradient, blockwise 1x128 and MXFP8 workloads, `sr8`), MX with E5M2 and
+    E2M1 elements, blockwise with power-of-two scales, and the rowwise-only
+    recipes with both planes
     (rowcol) or the colwise plane alone (colwise), at the large workloads'
     shapes, each call bracketed by events and started cold (flush() runs
     before it, outside the events); not part of the step."""
@@ -411,6 +413,12 @@ def time_extras(torch, fq, L, stream_p, jobs, steps, flush):
                                  rounding=fq.FQ_ROUND_STOCHASTIC, seed=2024, offset=1,
                                  transform=fq.FQ_TRANSFORM_RHT16, rht_signs=0xA5C3),
                          2 * 2 * R * C + R * C // 2 + R * C // 16 + 4)]
+        d0 = j["d"]
+        if ((w.recipe == "current" and d0.format == fq.FQ_E5M2) or (w.recipe == "block" and tuple(w.block) == (1, 128))
+                or w.recipe == "mx"):
+            # the same workload with stochastically rounded 8-bit elements
+            variants.append(("sr8", fq.desc(d0.recipe, d0.in_dtype, d0.format, R, C, w.block or (0, 0), w.outputs,
+                                            rounding=fq.FQ_ROUND_STOCHASTIC, seed=2024, offset=3), j["bytes"]))
         if w.recipe in ("current", "block", "nvfp4") and w.outputs == fq.FQ_ROWWISE:
             # the same recipe with both planes (the colwise copy for the
             # backward GEMMs): bytes from the library's own plane sizes

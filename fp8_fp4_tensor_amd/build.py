@@ -28,7 +28,7 @@ FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=
          "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
 
 SOURCES = ["api.cpp", "k_tensor.hip", "k_block.hip", "k_mx.hip", "k_mxfp4.hip", "k_nvfp4.hip", "k_dequant.hip", "k_requant.hip",
-           "noalloc.hip"]
+           "k_sr8.hip", "noalloc.hip"]
 
 
 def _compile(src: str, verbose: bool) -> str:

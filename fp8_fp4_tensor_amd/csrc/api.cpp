@@ -49,8 +49,13 @@ fq_status check_desc(const fq_desc* d)
         return FQ_E_INVALID;
     if (d->scale_mode == FQ_SCALE_POW2 && d->recipe != FQ_BLOCK_FP32)
         return FQ_E_UNSUPPORTED;
+    // stochastic rounding: NVFP4 1x16, and the 8-bit elements of per-tensor
+    // current scaling, blockwise 1x128 and MX (E4M3 / E5M2)
     if (d->rounding == FQ_ROUND_STOCHASTIC &&
-        !(d->recipe == FQ_NVFP4 && d->block_rows == 1 && d->block_cols == 16))
+        !(d->recipe == FQ_NVFP4 && d->block_rows == 1 && d->block_cols == 16) &&
+        !(d->recipe == FQ_PER_TENSOR_CURRENT) &&
+        !(d->recipe == FQ_BLOCK_FP32 && d->block_rows == 1 && d->block_cols == 128) &&
+        !(d->recipe == FQ_MX && d->format != FQ_E2M1))
         return FQ_E_UNSUPPORTED;
     if (d->transform != FQ_TRANSFORM_NONE && d->transform != FQ_TRANSFORM_RHT16)
         return FQ_E_INVALID;
@@ -220,9 +225,24 @@ fq_status hip_status(hipError_t e) { return e == hipSuccess ? FQ_OK : FQ_E_HIP; 
 
 int elem_bytes(const fq_desc* d) { return d->in_dtype == FQ_IN_BF16 ? 2 : 4; }
 
+// Stochastically rounded 8-bit elements of a validated desc (per-tensor with
+// src, blockwise 1x128, MX E4M3 / E5M2).
+fq_status run_sr8(const fq_desc* d, const void* x, ScaleSrc src, const fq_quantized* o, hipStream_t st)
+{
+    const bool row = d->outputs & FQ_ROWWISE, col = d->outputs & FQ_COLWISE;
+    const int kind = d->recipe == FQ_PER_TENSOR_CURRENT ? 0 : d->recipe == FQ_BLOCK_FP32 ? 1 : 2;
+    return hip_status(launch_sr8(x, d->in_dtype == FQ_IN_BF16, d->format, kind, d->scale_mode == FQ_SCALE_POW2,
+                                 d->rows, d->cols, src, sr_of(d), row ? (uint8_t*)o->rowwise.data : nullptr,
+                                 row ? o->rowwise.scale : nullptr, col ? (uint8_t*)o->colwise.data : nullptr,
+                                 col ? o->colwise.scale : nullptr, kind == 0 ? o->tensor_scale : nullptr,
+                                 kind == 0 ? o->amax : nullptr, st));
+}
+
 // Per-tensor current-scaling cast (amax from partials or given) of a validated desc.
 fq_status run_per_tensor_cast(const fq_desc* d, const void* x, ScaleSrc src, const fq_quantized* o, hipStream_t st)
 {
+    if (d->rounding == FQ_ROUND_STOCHASTIC)
+        return run_sr8(d, x, src, o, st);
     const int bf = d->in_dtype == FQ_IN_BF16;
     const int64_t n = d->rows * d->cols;
     uint8_t* q = (d->outputs & FQ_ROWWISE) ? (uint8_t*)o->rowwise.data : nullptr;
@@ -382,6 +402,8 @@ fq_status fq_quantize(const fq_desc* d, const void* x, const fq_quantized* o, vo
     case FQ_BLOCK_FP32: {
         if (n == 0)
             return FQ_OK;
+        if (d->rounding == FQ_ROUND_STOCHASTIC)
+            return run_sr8(d, x, ScaleSrc(), o, st);
         const int pow2 = d->scale_mode == FQ_SCALE_POW2;
         if (d->block_rows == 1) {
             // a colwise plane: 128x128 tiles (R % 128 == 0), the rowwise plane from the same read
@@ -400,6 +422,8 @@ fq_status fq_quantize(const fq_desc* d, const void* x, const fq_quantized* o, vo
     case FQ_MX:
         if (n == 0)
             return FQ_OK;
+        if (d->rounding == FQ_ROUND_STOCHASTIC)
+            return run_sr8(d, x, ScaleSrc(), o, st);
         if (d->format == FQ_E2M1)
             return hip_status(launch_mxfp4(x, bf, R, C, row ? (uint8_t*)o->rowwise.data : nullptr,
                                            row ? (uint8_t*)o->rowwise.scale : nullptr,

@@ -362,4 +362,63 @@ __device__ __forceinline__ uint8_t enc1(float v, float alpha)
     return (uint8_t)(cvt2<FMT, false>(clampf(v * alpha, Fmt<FMT>::kMax), 0.0f, 0u) & 0xFFu);
 }
 
+// ---------------------------------------------------------------- stochastic rounding
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC 2011): the published multipliers and Weyl constants.
+// Each round's two 32 x 32 -> 64-bit products are one v_mad_u64_u32 each,
+// and each three-way xor one v_bitop3_b32 (truth table 0x96 = a ^ b ^ c).
+constexpr uint32_t kPhM0 = 0xD2511F53u, kPhM1 = 0xCD9E8D57u;
+constexpr uint32_t kPhW0 = 0x9E3779B9u, kPhW1 = 0xBB67AE85u;
+
+struct Philox4 {
+    uint32_t w[4];
+};
+
+__device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                                 uint32_t k1)
+{
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+        const uint64_t p0 = (uint64_t)kPhM0 * c0, p1 = (uint64_t)kPhM1 * c2;
+        c0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96);
+        c1 = (uint32_t)p1;
+        c2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
+        c3 = (uint32_t)p0;
+        k0 += kPhW0;
+        k1 += kPhW1;
+    }
+    return Philox4{{c0, c1, c2, c3}};
+}
+
+// The random bits of elements 8h .. 8h+7 of a plane: one call with counter
+// (h, s) as 32-bit words and key = seed, s = 2 * offset + plane.
+__device__ __forceinline__ Philox4 sr_group(uint64_t h, uint64_t s, uint64_t seed)
+{
+    return philox4x32_10((uint32_t)h, (uint32_t)(h >> 32), (uint32_t)s, (uint32_t)(s >> 32), (uint32_t)seed,
+                         (uint32_t)(seed >> 32));
+}
+
+// Stochastic rounding of one clamped fp32 value y to E4M3 / E5M2 with the
+// 16 random bits u16 (bits 15..0): gfx950's v_cvt_scalef32_sr_fp8_f32 /
+// _bf8_f32 at unit scale add the bits of their random word below the last
+// kept bit and truncate, so a word whose bits 31..16 are u16 (15..0 zero)
+// rounds up iff u16 + g * 2^16 >= 2^16 (g the position between the two
+// neighbours), the add-and-truncate rounding with 16 random bits. Only
+// byte 0 of the result is used.
+template <int FMT>
+__device__ __forceinline__ uint32_t sr8_byte0(float y, uint32_t u16)
+{
+    if constexpr (FMT == kE4M3)
+        return (uint32_t)__builtin_amdgcn_cvt_scalef32_sr_fp8_f32(0, y, u16 << 16, 1.0f, 0);
+    else
+        return (uint32_t)__builtin_amdgcn_cvt_scalef32_sr_bf8_f32(0, y, u16 << 16, 1.0f, 0);
+}
+
+// Byte 0 of each of four words -> one dword, word k in byte k.
+__device__ __forceinline__ uint32_t gather_byte0(uint32_t t0, uint32_t t1, uint32_t t2, uint32_t t3)
+{
+    // v_perm_b32(a, b, sel): selector byte i picks byte sel_i of {a:b} (0..3 from b, 4..7 from a), 0x0c gives 0
+    return __builtin_amdgcn_perm(t1, t0, 0x0c0c0400u) | __builtin_amdgcn_perm(t3, t2, 0x04000c0cu);
+}
+
 }  // namespace fq

@@ -132,41 +132,6 @@ struct Fp4Store<4> {
 };
 
 // ---------------------------------------------------------------- stochastic rounding
-// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
-// easy as 1, 2, 3", SC 2011): the published multipliers and Weyl constants.
-// Each round's two 32 x 32 -> 64-bit products are one v_mad_u64_u32 each,
-// and each three-way xor one v_bitop3_b32 (truth table 0x96 = a ^ b ^ c).
-constexpr uint32_t kPhM0 = 0xD2511F53u, kPhM1 = 0xCD9E8D57u;
-constexpr uint32_t kPhW0 = 0x9E3779B9u, kPhW1 = 0xBB67AE85u;
-
-struct Philox4 {
-    uint32_t w[4];
-};
-
-__device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
-                                                 uint32_t k1)
-{
-#pragma unroll
-    for (int i = 0; i < 10; ++i) {
-        const uint64_t p0 = (uint64_t)kPhM0 * c0, p1 = (uint64_t)kPhM1 * c2;
-        c0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96);
-        c1 = (uint32_t)p1;
-        c2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
-        c3 = (uint32_t)p0;
-        k0 += kPhW0;
-        k1 += kPhW1;
-    }
-    return Philox4{{c0, c1, c2, c3}};
-}
-
-// The random bits of elements 8h .. 8h+7 of a plane: one call with counter
-// (h, s) as 32-bit words and key = seed, s = 2 * offset + plane.
-__device__ __forceinline__ Philox4 sr_group(uint64_t h, uint64_t s, uint64_t seed)
-{
-    return philox4x32_10((uint32_t)h, (uint32_t)(h >> 32), (uint32_t)s, (uint32_t)(s >> 32), (uint32_t)seed,
-                         (uint32_t)(seed >> 32));
-}
-
 // Stochastic rounding to E2M1 with gfx950's v_cvt_scalef32_sr_pk_fp4_f32 at
 // unit scale. For its first value the converter adds bits 31..10 of its
 // random word below the last kept bit and truncates (saturating at 6, sign

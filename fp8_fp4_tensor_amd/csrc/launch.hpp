@@ -142,6 +142,15 @@ struct SrArgs {
     uint64_t seed = 0, offset = 0;
 };
 
+// Stochastic rounding of the elements to E4M3 / E5M2 (fmt 0 / 1): kind 0
+// per-tensor (scale from src), 1 blockwise 1x128 (E4M3; pow2: power-of-two
+// scales), 2 MX 1x32. Rowwise codes q (+ scales sq) and/or the colwise copy
+// qt (+ sqt) of the [R, C] tensor; s_out / amax_out for per-tensor. Each
+// plane draws its own random bits (plane 0 rowwise, 1 colwise).
+hipError_t launch_sr8(const void* x, int in_bf16, int fmt, int kind, int pow2, int64_t R, int64_t C, ScaleSrc src,
+                      SrArgs sr, uint8_t* q, void* sq, uint8_t* qt, void* sqt, float* s_out, float* amax_out,
+                      hipStream_t stream);
+
 // Random Hadamard transform of 16-element chunks along the rows of X^T.
 struct RhtArgs {
     int on = 0;

@@ -106,17 +106,26 @@ enum { FQ_ROWWISE = 1, FQ_COLWISE = 2 };
 /*
  * Element rounding.
  *   FQ_ROUND_NEAREST_EVEN  every recipe (the default).
- *   FQ_ROUND_STOCHASTIC    NVFP4 with 1x16 blocks only ([MP] "NVFP4": an
- *                          option for FP4 values; [LP] section 2.4 item 5:
- *                          applied to gradients). A scaled value of
- *                          magnitude v < 6 between neighbouring E2M1 values
- *                          lo <= v < hi, with g = (v - lo) / (hi - lo) and u
- *                          a 16-bit random number, rounds to hi iff
+ *   FQ_ROUND_STOCHASTIC    the elements of NVFP4 with 1x16 blocks ([MP]
+ *                          "NVFP4": an option for FP4 values; [LP] section
+ *                          2.4 item 5: applied to gradients), and the E4M3 /
+ *                          E5M2 elements of CURRENT, BLOCK_FP32 with 1x128
+ *                          tiles and MX ([MP] "FP8 数据格式": stochastic
+ *                          rounding beside round-to-nearest-even). A scaled
+ *                          value of magnitude v below the format's largest
+ *                          value Fmax, between neighbouring representable
+ *                          magnitudes lo <= v < hi (subnormals included),
+ *                          with g = (v - lo) / (hi - lo) and u a 16-bit
+ *                          random number, rounds to hi iff
  *                          u + g * 2^16 >= 2^16: the random bits are added
  *                          below the last kept bit and the sum truncated, so
  *                          it rounds up with probability floor(g * 2^16) /
- *                          2^16. v >= 6 saturates; the sign is kept, also on
- *                          zero; block scales stay round-to-nearest-even.
+ *                          2^16. v >= Fmax saturates; the sign is kept, also
+ *                          on zero; every scale (tensor, tile, block) is
+ *                          that of round-to-nearest-even. Each output plane
+ *                          draws its own bits, so the colwise copy of a
+ *                          CURRENT call is the recipe applied to X^T, not
+ *                          the transposed rowwise bytes.
  *                          u comes from Philox4x32-10 (Salmon et al., SC
  *                          2011) with key = seed (low word first): the
  *                          element at index e of an output plane
@@ -180,7 +189,8 @@ typedef enum { FQ_SCALE_DEFAULT = 0, FQ_SCALE_POW2 = 1 } fq_scale_mode;
  *   MX                E4M3, E5M2 or E2M1, cols % 32 == 0; colwise needs
  *                     rows % 32 == 0
  *   scale_mode POW2   BLOCK_FP32 only
- *   rounding STOCHASTIC  NVFP4 with 1x16 blocks only
+ *   rounding STOCHASTIC  NVFP4 with 1x16 blocks; CURRENT; BLOCK_FP32
+ *                     with 1x128 tiles; MX with E4M3 or E5M2 elements
  *   transform RHT16   NVFP4 with 1x16 blocks, outputs == FQ_COLWISE
  *   NVFP4             E2M1, rows % br == 0, cols % 16 == 0;
  *                     colwise needs rows % 16 == 0

@@ -107,9 +107,15 @@ def test_desc_validation(L, recipe, fmt, R, C, block, outputs, want):
 @pytest.mark.parametrize("recipe,fmt,block,rounding,scale_mode,want", [
     (fq.FQ_NVFP4, fq.FQ_E2M1, (1, 16), fq.FQ_ROUND_STOCHASTIC, 0, fq.FQ_OK),
     (fq.FQ_NVFP4, fq.FQ_E2M1, (16, 16), fq.FQ_ROUND_STOCHASTIC, 0, fq.FQ_E_UNSUPPORTED),
-    (fq.FQ_PER_TENSOR_CURRENT, fq.FQ_E4M3, (0, 0), fq.FQ_ROUND_STOCHASTIC, 0, fq.FQ_E_UNSUPPORTED),
-    (fq.FQ_BLOCK_FP32, fq.FQ_E4M3, (1, 128), fq.FQ_ROUND_STOCHASTIC, 0, fq.FQ_E_UNSUPPORTED),
-    (fq.FQ_MX, fq.FQ_E4M3, (1, 32), fq.FQ_ROUND_STOCHASTIC, 0, fq.FQ_E_UNSUPPORTED),
+    (fq.FQ_PER_TENSOR_CURRENT, fq.FQ_E4M3, (0, 0), fq.FQ_ROUND_STOCHASTIC, 0, fq.FQ_OK),
+    (fq.FQ_PER_TENSOR_CURRENT, fq.FQ_E5M2, (0, 0), fq.FQ_ROUND_STOCHASTIC, 0, fq.FQ_OK),
+    (fq.FQ_PER_TENSOR_DELAYED, fq.FQ_E5M2, (0, 0), fq.FQ_ROUND_STOCHASTIC, 0, fq.FQ_E_UNSUPPORTED),
+    (fq.FQ_BLOCK_FP32, fq.FQ_E4M3, (1, 128), fq.FQ_ROUND_STOCHASTIC, 0, fq.FQ_OK),
+    (fq.FQ_BLOCK_FP32, fq.FQ_E4M3, (1, 128), fq.FQ_ROUND_STOCHASTIC, fq.FQ_SCALE_POW2, fq.FQ_OK),
+    (fq.FQ_BLOCK_FP32, fq.FQ_E4M3, (128, 128), fq.FQ_ROUND_STOCHASTIC, 0, fq.FQ_E_UNSUPPORTED),
+    (fq.FQ_MX, fq.FQ_E4M3, (1, 32), fq.FQ_ROUND_STOCHASTIC, 0, fq.FQ_OK),
+    (fq.FQ_MX, fq.FQ_E5M2, (1, 32), fq.FQ_ROUND_STOCHASTIC, 0, fq.FQ_OK),
+    (fq.FQ_MX, fq.FQ_E2M1, (1, 32), fq.FQ_ROUND_STOCHASTIC, 0, fq.FQ_E_UNSUPPORTED),
     (fq.FQ_NVFP4, fq.FQ_E2M1, (1, 16), 2, 0, fq.FQ_E_INVALID),
     (fq.FQ_NVFP4, fq.FQ_E2M1, (1, 16), -1, 0, fq.FQ_E_INVALID),
     (fq.FQ_NVFP4, fq.FQ_E2M1, (1, 16), 0, 7, fq.FQ_E_INVALID),

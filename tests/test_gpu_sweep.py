@@ -1,5 +1,6 @@
 """GPU parity over a seeded sweep: every recipe, format, plane selection,
-rounding, transform and input dtype, at random shapes (whole 128x128 tiles,
+rounding (stochastic rounding of FP4 and FP8 elements included), transform
+and input dtype, at random shapes (whole 128x128 tiles,
 which take the one-read tile kernels for bf16, and ragged multiples of each
 recipe's block), with random value scales and distributions; each case
 compared byte for byte with the oracle. The cases are drawn once from a
@@ -37,6 +38,12 @@ KINDS = {
     "nvfp4_1x16_sr": (fq.FQ_NVFP4, fq.FQ_E2M1, (1, 16), 1, 16, 16, (ROW, COL, BOTH)),
     "nvfp4_1x16_rht": (fq.FQ_NVFP4, fq.FQ_E2M1, (1, 16), 16, 16, 16, (COL,)),
     "nvfp4_1x16_rht_sr": (fq.FQ_NVFP4, fq.FQ_E2M1, (1, 16), 16, 16, 16, (COL,)),
+    "current_e4m3_sr": (fq.FQ_PER_TENSOR_CURRENT, fq.FQ_E4M3, (0, 0), 1, 1, 1, (ROW, COL, BOTH)),
+    "current_e5m2_sr": (fq.FQ_PER_TENSOR_CURRENT, fq.FQ_E5M2, (0, 0), 1, 1, 1, (ROW, COL, BOTH)),
+    "block_1x128_sr": (fq.FQ_BLOCK_FP32, fq.FQ_E4M3, (1, 128), 1, 128, 128, (ROW, COL, BOTH)),
+    "block_1x128_pow2_sr": (fq.FQ_BLOCK_FP32, fq.FQ_E4M3, (1, 128), 1, 128, 128, (ROW, COL, BOTH)),
+    "mx_e4m3_sr": (fq.FQ_MX, fq.FQ_E4M3, (1, 32), 1, 32, 32, (ROW, COL, BOTH)),
+    "mx_e5m2_sr": (fq.FQ_MX, fq.FQ_E5M2, (1, 32), 1, 32, 32, (ROW, COL, BOTH)),
 }
 OFMT = {fq.FQ_E4M3: orc.E4M3, fq.FQ_E5M2: orc.E5M2, fq.FQ_E2M1: orc.E2M1}
 N_CASES = 600
@@ -115,7 +122,7 @@ def test_sweep(c):
     tag = case_id(c)
     sr = "_sr" in c["kind"]
     rht = "_rht" in c["kind"]
-    pow2 = c["kind"].endswith("_pow2")
+    pow2 = "_pow2" in c["kind"]
     d = fq.desc(recipe, in_dtype(x), fmt, R, C, block, outputs,
                 rounding=fq.FQ_ROUND_STOCHASTIC if sr else fq.FQ_ROUND_NEAREST_EVEN,
                 seed=c["sr"][0] if sr else 0, offset=c["sr"][1] if sr else 0,
@@ -152,22 +159,23 @@ def test_sweep(c):
     torch.cuda.synchronize()
 
     if recipe == fq.FQ_PER_TENSOR_CURRENT:
+        srp = c["sr"] if sr else None
         if amax_in is None:
-            want = orc.quantize_current(x, OFMT[fmt], outputs=outputs)
+            want = orc.quantize_current(x, OFMT[fmt], outputs=outputs, sr=srp)
             same_bytes(host(out.amax), f32(want["amax"]), f"{tag}: amax")
         else:
-            want = orc.quantize_with_amax(x, OFMT[fmt], amax_in, outputs=outputs)
+            want = orc.quantize_with_amax(x, OFMT[fmt], amax_in, outputs=outputs, sr=srp)
         compare_planes(out, outputs, {ROW: [(out.row_data, want["q_row"], "codes")],
                                       COL: [(out.col_data, want["q_col"], "colwise codes")]}, tag)
         same_bytes(host(out.tensor_scale), f32(want["s"]), f"{tag}: s")
     elif recipe == fq.FQ_BLOCK_FP32:
-        want = orc.quantize_block(x, block, outputs=outputs, pow2=pow2)
+        want = orc.quantize_block(x, block, outputs=outputs, pow2=pow2, sr=c["sr"] if sr else None)
         compare_planes(out, outputs, {ROW: [(out.row_data, want["q_row"], "codes"),
                                             (out.row_scale, want["s_row"], "tile scales")],
                                       COL: [(out.col_data, want["q_col"], "colwise codes"),
                                             (out.col_scale, want["s_col"], "colwise tile scales")]}, tag)
     elif recipe == fq.FQ_MX:
-        want = orc.quantize_mx(x, outputs=outputs, fmt=OFMT[fmt])
+        want = orc.quantize_mx(x, outputs=outputs, fmt=OFMT[fmt], sr=c["sr"] if sr else None)
         compare_planes(out, outputs, {ROW: [(out.row_data, want["q_row"], "codes"),
                                             (out.row_scale, want["e_row"], "E8M0")],
                                       COL: [(out.col_data, want["q_col"], "colwise codes"),
