@@ -59,6 +59,10 @@ CASES = [
      [(1024, 4096), (64, 128)], lambda s, seed: W.normal(s, 0.02, seed, W.BF16)),
     ("block 1x128", lambda R, C: fq.desc(fq.FQ_BLOCK_FP32, fq.FQ_IN_BF16, fq.FQ_E4M3, R, C, (1, 128)),
      [(512, 1024), (128, 256)], lambda s, seed: W.normal(s, 1.0, seed, W.BF16)),
+    ("current e5m2 bf16 stochastic both planes",
+     lambda R, C: fq.desc(fq.FQ_PER_TENSOR_CURRENT, fq.FQ_IN_BF16, fq.FQ_E5M2, R, C,
+                          outputs=fq.FQ_ROWWISE | fq.FQ_COLWISE, rounding=fq.FQ_ROUND_STOCHASTIC, seed=3, offset=4),
+     [(1024, 2048), (130, 70)], lambda s, seed: W.normal(s, 1e-3, seed, W.BF16)),
 ]
 
 
