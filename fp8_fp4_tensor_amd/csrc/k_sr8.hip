@@ -28,7 +28,10 @@
 //              XOR-swizzled by 32-row quarter); thread (c, q) takes column
 //              c, rows 32q..32q+31: one MX block, a quarter of a 1x128 block
 //              (the four quarters of a column are a quad of lanes: DPP max),
-//              and writes 32 consecutive bytes of row c of X^T.
+//              and writes 32 consecutive bytes of row c of X^T. For
+//              per-tensor and MX calls with both planes it also writes the
+//              rowwise plane from the same tile (thread (r, h): 32 columns
+//              of row r), so the input is read once.
 #include <algorithm>
 
 #include "codec.hpp"
@@ -171,17 +174,49 @@ __global__ __launch_bounds__(kWG) void k_sr8_row(const T* __restrict__ x, int64_
 // LDS offset (floats) of element (r, c) of the 128 x 64 tile: 32-row quarter
 // q of a row XOR-swizzles the column by 16 q, so the four quarters a quad of
 // lanes reads at once fall in different banks.
-__device__ __forceinline__ int col_tile_off(int r, int c) { return r * kColCols + (c ^ (((r >> 5) & 3) << 4)); }
+// 32 consecutive elements of a plane (element index e0, n of them valid)
+// from fp32 values y times mult: with n == 32 and e0 a multiple of 16, four
+// Philox groups and two 16-byte stores; otherwise element by element.
+template <int FMT>
+__device__ __forceinline__ void sr_run32(const float* y, float mult, uint8_t* dst, int64_t e0, int64_t n,
+                                         bool aligned16, uint64_t stream_s, uint64_t seed)
+{
+    if (aligned16 && n == 32) {
+        u32x4 w[2];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const Philox4 ph = sr_group((uint64_t)(e0 >> 3) + g, stream_s, seed);
+            w[g >> 1][2 * (g & 1)] = sr4<FMT>(y + 8 * g, mult, ph.w[0], ph.w[1]);
+            w[g >> 1][2 * (g & 1) + 1] = sr4<FMT>(y + 8 * g + 4, mult, ph.w[2], ph.w[3]);
+        }
+        *reinterpret_cast<u32x4*>(dst) = w[0];
+        *reinterpret_cast<u32x4*>(dst + 16) = w[1];
+    } else {
+        for (int k = 0; k < 32 && k < n; ++k)
+            dst[k] = (uint8_t)sr8_byte0<FMT>(clampf(y[k] * mult, Fmt<FMT>::kMax), sr_bits_of(e0 + k, stream_s, seed));
+    }
+}
+
+// The pitch P is kColCols, or kColCols + 4 floats when the tile's rows are
+// also read along the row (16-byte reads, rows of a wave 272 bytes apart).
+template <int P>
+__device__ __forceinline__ int col_tile_off(int r, int c) { return r * P + (c ^ (((r >> 5) & 3) << 4)); }
 
 // Colwise plane (X^T): per-tensor (src), 1x128 blocks (R % 128 == 0) or 1x32
 // blocks (R % 32 == 0) down the columns of X. VEC: rows of X are 16-byte
-// aligned and 16-byte multiples (C % (16 / sizeof(T)) == 0).
-template <typename T, int FMT, int KIND, bool POW2, bool VEC>
+// aligned and 16-byte multiples (C % (16 / sizeof(T)) == 0). ROW (per-tensor
+// and MX): the rowwise plane too, from the same staged tile: thread (r, h)
+// rounds columns 32h .. 32h+31 of tile row r (one MX block) with the rowwise
+// random bits (stream_row).
+template <typename T, int FMT, int KIND, bool POW2, bool VEC, bool ROW>
 __global__ __launch_bounds__(kWG) void k_sr8_col(const T* __restrict__ x, int64_t R, int64_t C, ScaleSrc src,
                                                  uint64_t seed, uint64_t stream_s, uint8_t* __restrict__ qt,
-                                                 void* __restrict__ sct, float* s_out, float* amax_out)
+                                                 void* __restrict__ sct, float* s_out, float* amax_out,
+                                                 uint64_t stream_row, uint8_t* __restrict__ q, void* __restrict__ sq)
 {
-    __shared__ __align__(16) float tile[kColRows * kColCols];
+    static_assert(!ROW || KIND != kSrBlock128, "a 1x128 block is wider than the tile");
+    constexpr int P = ROW ? kColCols + 4 : kColCols;
+    __shared__ __align__(16) float tile[kColRows * P];
     __shared__ float lds[4];
     const int64_t ntc = cdiv(C, kColCols);
     int64_t tr, tc;
@@ -210,7 +245,7 @@ __global__ __launch_bounds__(kWG) void k_sr8_col(const T* __restrict__ x, int64_
             In<T>::unpack(v, f);
 #pragma unroll
             for (int j = 0; j < E; j += 4)
-                *reinterpret_cast<float4*>(tile + col_tile_off(row, col + j)) = make_float4(f[j], f[j + 1], f[j + 2],
+                *reinterpret_cast<float4*>(tile + col_tile_off<P>(row, col + j)) = make_float4(f[j], f[j + 1], f[j + 2],
                                                                                             f[j + 3]);
         }
     } else {
@@ -219,7 +254,7 @@ __global__ __launch_bounds__(kWG) void k_sr8_col(const T* __restrict__ x, int64_
         for (int k = 0; k < NL; ++k) {
             const int i = k * kWG + (int)threadIdx.x, row = i / kColCols, col = i % kColCols;
             const bool in = r0 + row < R && c0 + col < C;
-            tile[col_tile_off(row, col)] = in ? In<T>::load1(x, (r0 + row) * C + c0 + col) : 0.0f;
+            tile[col_tile_off<P>(row, col)] = in ? In<T>::load1(x, (r0 + row) * C + c0 + col) : 0.0f;
         }
     }
     __syncthreads();
@@ -227,7 +262,7 @@ __global__ __launch_bounds__(kWG) void k_sr8_col(const T* __restrict__ x, int64_
     float y[32];
 #pragma unroll
     for (int k = 0; k < 32; ++k)
-        y[k] = tile[col_tile_off(32 * qr + k, c)];
+        y[k] = tile[col_tile_off<P>(32 * qr + k, c)];
     float mult = alpha;
     const bool col_in = c0 + c < C;
     if constexpr (KIND == kSrBlock128) {
@@ -241,27 +276,45 @@ __global__ __launch_bounds__(kWG) void k_sr8_col(const T* __restrict__ x, int64_
         if (col_in && r0 + 32 * qr < R)
             reinterpret_cast<uint8_t*>(sct)[(c0 + c) * (R / 32) + r0 / 32 + qr] = (uint8_t)code;
     }
-    if (!col_in)
-        return;
-    const int64_t rb = r0 + 32 * qr;                  // first row of this thread's run
-    const int64_t e0 = (c0 + c) * R + rb;             // its first element of X^T
-    uint8_t* dst = qt + e0;
-    if ((R & 15) == 0 && rb + 32 <= R) {
-        // whole, aligned run: four Philox groups, two 16-byte stores
-        u32x4 w[2];
+    if (col_in)
+        sr_run32<FMT>(y, mult, qt + (c0 + c) * R + r0 + 32 * qr, (c0 + c) * R + r0 + 32 * qr,
+                      min((int64_t)32, R - r0 - 32 * qr), (R & 15) == 0, stream_s, seed);
+    if constexpr (ROW) {
+        const int row = (int)threadIdx.x >> 1, h = (int)threadIdx.x & 1;
+        const int64_t gr = r0 + row, gc = c0 + 32 * h;
+        if (gr < R && gc < C) {
+            float z[32];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const Philox4 ph = sr_group((uint64_t)(e0 >> 3) + g, stream_s, seed);
-            w[g >> 1][2 * (g & 1)] = sr4<FMT>(y + 8 * g, mult, ph.w[0], ph.w[1]);
-            w[g >> 1][2 * (g & 1) + 1] = sr4<FMT>(y + 8 * g + 4, mult, ph.w[2], ph.w[3]);
+            for (int k = 0; k < 8; ++k) {
+                const float4 v = *reinterpret_cast<const float4*>(tile + col_tile_off<P>(row, 32 * h + 4 * k));
+                z[4 * k] = v.x;
+                z[4 * k + 1] = v.y;
+                z[4 * k + 2] = v.z;
+                z[4 * k + 3] = v.w;
+            }
+            float rmult = alpha;
+            if constexpr (KIND == kSrMx32) {
+                const uint32_t code = mx_code<FMT>(absmax<32>(z));
+                rmult = mx_multiplier(code);
+                reinterpret_cast<uint8_t*>(sq)[gr * (C / 32) + gc / 32] = (uint8_t)code;
+            }
+            sr_run32<FMT>(z, rmult, q + gr * C + gc, gr * C + gc, min((int64_t)32, C - gc), (C & 15) == 0,
+                          stream_row, seed);
         }
-        *reinterpret_cast<u32x4*>(dst) = w[0];
-        *reinterpret_cast<u32x4*>(dst + 16) = w[1];
-    } else {
-        // ragged rows (per-tensor only): element by element
-        for (int k = 0; k < 32 && rb + k < R; ++k)
-            dst[k] = (uint8_t)sr8_byte0<FMT>(clampf(y[k] * mult, Fmt<FMT>::kMax), sr_bits_of(e0 + k, stream_s, seed));
     }
+}
+
+template <typename T, int FMT, int KIND, bool POW2, bool ROW>
+void launch_col(const T* x, int64_t R, int64_t C, ScaleSrc src, SrArgs sr, uint8_t* qt, void* sqt, float* s_out,
+                float* amax_out, uint8_t* q, void* sq, hipStream_t stream)
+{
+    const unsigned grid = (unsigned)(cdiv(R, kColRows) * cdiv(C, kColCols));
+    if (C % In<T>::kE == 0)
+        k_sr8_col<T, FMT, KIND, POW2, true, ROW><<<grid, kWG, 0, stream>>>(
+            x, R, C, src, sr.seed, 2 * sr.offset + 1, qt, sqt, s_out, amax_out, 2 * sr.offset, q, sq);
+    else
+        k_sr8_col<T, FMT, KIND, POW2, false, ROW><<<grid, kWG, 0, stream>>>(
+            x, R, C, src, sr.seed, 2 * sr.offset + 1, qt, sqt, s_out, amax_out, 2 * sr.offset, q, sq);
 }
 
 template <typename T, int FMT, int KIND, bool POW2>
@@ -270,6 +323,13 @@ void launch_t(const void* xv, int64_t R, int64_t C, ScaleSrc src, SrArgs sr, uin
 {
     const T* x = reinterpret_cast<const T*>(xv);
     const int64_t n = R * C;
+    // both planes of per-tensor and MX calls: one kernel, one read
+    if constexpr (KIND != kSrBlock128) {
+        if (q && qt && n > 0) {
+            launch_col<T, FMT, KIND, POW2, true>(x, R, C, src, sr, qt, sqt, s_out, amax_out, q, sq, stream);
+            return;
+        }
+    }
     // an empty per-tensor call still writes s and the amax (1 and 0)
     if (q || (n == 0 && KIND == kSrTensor)) {
         // per-tensor: at most 2048 workgroups, since each re-reduces the amax partials
@@ -279,17 +339,9 @@ void launch_t(const void* xv, int64_t R, int64_t C, ScaleSrc src, SrArgs sr, uin
         k_sr8_row<T, FMT, KIND, POW2, kRowLoads><<<grid, kWG, 0, stream>>>(x, n, src, sr.seed, 2 * sr.offset, q, sq,
                                                                            s_out, amax_out);
     }
-    if (qt && n > 0) {
-        const unsigned grid = (unsigned)(cdiv(R, kColRows) * cdiv(C, kColCols));
-        float* so = q ? nullptr : s_out;  // written once, by the rowwise pass if there is one
-        float* ao = q ? nullptr : amax_out;
-        if (C % In<T>::kE == 0)
-            k_sr8_col<T, FMT, KIND, POW2, true><<<grid, kWG, 0, stream>>>(x, R, C, src, sr.seed, 2 * sr.offset + 1,
-                                                                          qt, sqt, so, ao);
-        else
-            k_sr8_col<T, FMT, KIND, POW2, false><<<grid, kWG, 0, stream>>>(x, R, C, src, sr.seed, 2 * sr.offset + 1,
-                                                                           qt, sqt, so, ao);
-    }
+    if (qt && n > 0)  // s and the amax are written once, by the rowwise pass if there is one
+        launch_col<T, FMT, KIND, POW2, false>(x, R, C, src, sr, qt, sqt, q ? nullptr : s_out,
+                                              q ? nullptr : amax_out, nullptr, nullptr, stream);
 }
 
 template <typename T, int KIND, bool POW2>
