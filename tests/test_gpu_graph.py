@@ -3,9 +3,9 @@
 The library enqueues kernels only (no allocation, no memset, no
 synchronization), so a sequence of calls can be captured once and replayed.
 Per-tensor current scaling (two kernels and a workspace), blockwise (both
-tile shapes, power-of-two scales), MX (E4M3, E5M2, E2M1 elements) and NVFP4
-(both block shapes, stochastic rounding, the Hadamard transform) are captured
-together; every replay follows eager work on the same
+tile shapes, power-of-two scales), MX (E4M3, E5M2, E2M1 elements), NVFP4
+(both block shapes, stochastic rounding, the Hadamard transform) and the
+stochastic rounding of 8-bit elements are captured together; every replay follows eager work on the same
 buffers (outputs cleared, a new input copied in) and a synchronization, and
 each replay's bytes are checked against an eager call on that input."""
 import numpy as np
@@ -37,6 +37,12 @@ DESCS = [
             rounding=fq.FQ_ROUND_STOCHASTIC, seed=77, offset=5),
     fq.desc(fq.FQ_NVFP4, fq.FQ_IN_BF16, fq.FQ_E2M1, R, C, (1, 16), fq.FQ_COLWISE,
             rounding=fq.FQ_ROUND_STOCHASTIC, seed=78, offset=6, transform=fq.FQ_TRANSFORM_RHT16, rht_signs=0xA5C3),
+    fq.desc(fq.FQ_PER_TENSOR_CURRENT, fq.FQ_IN_BF16, fq.FQ_E5M2, R, C, (0, 0), BOTH,
+            rounding=fq.FQ_ROUND_STOCHASTIC, seed=79, offset=7),
+    fq.desc(fq.FQ_BLOCK_FP32, fq.FQ_IN_BF16, fq.FQ_E4M3, R, C, (1, 128), BOTH,
+            rounding=fq.FQ_ROUND_STOCHASTIC, seed=80, offset=8),
+    fq.desc(fq.FQ_MX, fq.FQ_IN_BF16, fq.FQ_E4M3, R, C, (1, 32), BOTH,
+            rounding=fq.FQ_ROUND_STOCHASTIC, seed=81, offset=9),
 ]
 
 
