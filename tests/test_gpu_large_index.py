@@ -6,8 +6,9 @@ bf16: x[r, c] = (((1103 r + 2221 c) mod 256) - 128) / 64 * 2^((r + c // 128) mod
 The oracle regenerates sampled rows (and columns) exactly in numpy and checks
 them bit for bit, including rows whose elements lie past index 2^31, and
 colwise planes (rows of X^T) past that index: per-tensor, blockwise, MXFP8,
-MXFP4, NVFP4 (with and without the RHT), dequantization and the MX and
-power-of-two blockwise requantizations. The tensor amax is 256 by
+MXFP4, NVFP4 (with and without the RHT), dequantization, the MX and
+power-of-two blockwise requantizations, and stochastic rounding of 8-bit
+elements (per-tensor, MX and blockwise 1x128, both planes). The tensor amax is 256 by
 construction (k = -128 at scale 2^7 occurs)."""
 import numpy as np
 import pytest
@@ -277,3 +278,70 @@ def test_large_block_pow2_requantize(big):
     same_bytes(host(dst.col_data[SAMPLE_COLS]), want["q_col"][pos], "requantized colwise codes")
     same_bytes(host(dst.col_scale.view(C, R // 128)[SAMPLE_COLS]), want["s_col"][pos], "requantized colwise scales")
     del src, dst
+
+
+# ---------------------------------------------------------------- stochastic rounding of 8-bit elements
+SR = (31337, 12)
+
+
+def sr_codes(fmt, y, plane, e0):
+    """Stochastic codes of consecutive plane elements e0, e0+1, ... with scaled
+    fp32 values y, from the oracle's generator and rounding."""
+    u = np.array([orc.sr_bits(SR[0], SR[1], plane, e0 + i) for i in range(y.size)], np.uint16)
+    return orc.encode_sr(fmt, np.ascontiguousarray(y, np.float32), u)
+
+
+def sr_desc(recipe, fmt, block, outputs):
+    return fq.desc(recipe, fq.FQ_IN_BF16, fmt, R, C, block, outputs, rounding=fq.FQ_ROUND_STOCHASTIC, seed=SR[0],
+                   offset=SR[1])
+
+
+def test_large_current_sr_both_planes(big):
+    """Per-tensor E5M2 with stochastic rounding, both planes from one read;
+    sampled rows and rows of X^T past element 2^31."""
+    out = quantize(sr_desc(fq.FQ_PER_TENSOR_CURRENT, fq.FQ_E5M2, (0, 0), fq.FQ_ROWWISE | fq.FQ_COLWISE), big)
+    alpha = np.float32(57344.0) / np.float32(AMAX)
+    same_bytes(host(out.amax), f32(AMAX), "tensor amax")
+    same_bytes(host(out.tensor_scale), f32(np.float32(AMAX) / np.float32(57344.0)), "s")
+    rows = host(out.row_data[SAMPLE_ROWS])
+    for i, r in enumerate(SAMPLE_ROWS):
+        y = values(np.array([r]), np.arange(C)).ravel() * alpha
+        same_bytes(rows[i], sr_codes(orc.E5M2, y, 0, int(r) * C), f"rowwise row {r}")
+    cols = host(out.col_data[SAMPLE_COLS])
+    for i, c in enumerate(SAMPLE_COLS):
+        y = values(np.arange(R), np.array([c])).ravel() * alpha
+        same_bytes(cols[i], sr_codes(orc.E5M2, y, 1, int(c) * R), f"colwise row {c}")
+    del out
+
+
+def test_large_mx_sr_both_planes(big):
+    out = quantize(sr_desc(fq.FQ_MX, fq.FQ_E4M3, (1, 32), fq.FQ_ROWWISE | fq.FQ_COLWISE), big)
+    for plane, idx, data, scale in ((0, SAMPLE_ROWS, out.row_data, out.row_scale.view(R, C // 32)),
+                                    (1, SAMPLE_COLS, out.col_data, out.col_scale.view(C, R // 32))):
+        got, got_e = host(data[idx]), host(scale[idx])
+        n = C if plane == 0 else R
+        for i, k in enumerate(idx):
+            v = (values(np.array([k]), np.arange(C)) if plane == 0 else values(np.arange(R), np.array([k]))).ravel()
+            a = np.abs(v).reshape(-1, 32).max(1)
+            codes = np.array([orc.mx_code(x) for x in a], np.uint8)
+            same_bytes(got_e[i], codes, f"plane {plane} E8M0 {k}")
+            y = (v.reshape(-1, 32).astype(np.float64) * np.exp2(127.0 - codes.astype(np.float64))[:, None])
+            same_bytes(got[i], sr_codes(orc.E4M3, y.astype(np.float32).ravel(), plane, int(k) * n),
+                       f"plane {plane} codes {k}")
+    del out
+
+
+def test_large_block_1x128_sr_both_planes(big):
+    out = quantize(sr_desc(fq.FQ_BLOCK_FP32, fq.FQ_E4M3, (1, 128), fq.FQ_ROWWISE | fq.FQ_COLWISE), big)
+    for plane, idx, data, scale in ((0, SAMPLE_ROWS, out.row_data, out.row_scale.view(R, C // 128)),
+                                    (1, SAMPLE_COLS, out.col_data, out.col_scale.view(C, R // 128))):
+        got, got_s = host(data[idx]), host(scale[idx])
+        n = C if plane == 0 else R
+        for i, k in enumerate(idx):
+            v = (values(np.array([k]), np.arange(C)) if plane == 0 else values(np.arange(R), np.array([k]))).ravel()
+            a = np.abs(v).reshape(-1, 128).max(1).astype(np.float32)
+            alpha = (np.float32(448.0) / a).astype(np.float32)          # every tile amax is nonzero here
+            same_bytes(got_s[i], (a / np.float32(448.0)).astype(np.float32), f"plane {plane} scales {k}")
+            y = (v.reshape(-1, 128) * alpha[:, None]).astype(np.float32).ravel()
+            same_bytes(got[i], sr_codes(orc.E4M3, y, plane, int(k) * n), f"plane {plane} codes {k}")
+    del out
