@@ -31,6 +31,11 @@ CASES = [
      {"rounding": fq.FQ_ROUND_STOCHASTIC, "seed": 7, "offset": 1}),
     ("nvfp4_rht", fq.FQ_NVFP4, fq.FQ_E2M1, (1, 16), fq.FQ_COLWISE,
      {"transform": fq.FQ_TRANSFORM_RHT16, "rht_signs": 0x5A3C}),
+    ("current_sr", fq.FQ_PER_TENSOR_CURRENT, fq.FQ_E5M2, (0, 0), BOTH,
+     {"rounding": fq.FQ_ROUND_STOCHASTIC, "seed": 7, "offset": 1}),
+    ("block_1x128_sr", fq.FQ_BLOCK_FP32, fq.FQ_E4M3, (1, 128), BOTH,
+     {"rounding": fq.FQ_ROUND_STOCHASTIC, "seed": 7, "offset": 1}),
+    ("mx_sr", fq.FQ_MX, fq.FQ_E4M3, (1, 32), BOTH, {"rounding": fq.FQ_ROUND_STOCHASTIC, "seed": 7, "offset": 1}),
 ]
 
 SENTINEL = -7.0
@@ -73,7 +78,7 @@ def test_empty_quantize_and_dequantize(case, shape, dt):
         if d.outputs & which:
             for ydt in (torch.float32, torch.bfloat16):
                 fq.fq_dequantize(d, out, which, torch.empty(16, dtype=ydt, device="cuda"))
-    if recipe == fq.FQ_MX and fmt == fq.FQ_E4M3:
+    if recipe == fq.FQ_MX and fmt == fq.FQ_E4M3 and not extra.get("rounding"):
         fq.fq_requantize_transpose(d, out, fq.alloc_quantized(d))
     torch.cuda.synchronize()
 

@@ -94,6 +94,22 @@ CASES = [
      {"rounding": fq.FQ_ROUND_STOCHASTIC, "seed": 3, "offset": 9, "transform": fq.FQ_TRANSFORM_RHT16,
       "rht_signs": 0x3C5A}),
     ("mxfp8_regions", fq.FQ_MX, fq.FQ_E4M3, (1, 32), BOTH, (256, 512), {}),
+    # stochastic rounding of 8-bit elements: ragged per-tensor planes, the
+    # one-read both-planes tile, 1x128 and MX
+    ("current_sr_ragged", fq.FQ_PER_TENSOR_CURRENT, fq.FQ_E5M2, (0, 0), BOTH, (37, 61),
+     {"rounding": fq.FQ_ROUND_STOCHASTIC, "seed": 5, "offset": 2}),
+    ("current_sr_cols", fq.FQ_PER_TENSOR_CURRENT, fq.FQ_E4M3, (0, 0), fq.FQ_COLWISE, (130, 70),
+     {"rounding": fq.FQ_ROUND_STOCHASTIC, "seed": 5, "offset": 2}),
+    ("current_sr_tiles", fq.FQ_PER_TENSOR_CURRENT, fq.FQ_E4M3, (0, 0), BOTH, (256, 384),
+     {"rounding": fq.FQ_ROUND_STOCHASTIC, "seed": 5, "offset": 2}),
+    ("block_1x128_sr", fq.FQ_BLOCK_FP32, fq.FQ_E4M3, (1, 128), BOTH, (256, 384),
+     {"rounding": fq.FQ_ROUND_STOCHASTIC, "seed": 5, "offset": 2}),
+    ("block_1x128_sr_rows", fq.FQ_BLOCK_FP32, fq.FQ_E4M3, (1, 128), fq.FQ_ROWWISE, (3, 384),
+     {"rounding": fq.FQ_ROUND_STOCHASTIC, "seed": 5, "offset": 2, "scale_mode": fq.FQ_SCALE_POW2}),
+    ("mx_sr", fq.FQ_MX, fq.FQ_E4M3, (1, 32), BOTH, (96, 160),
+     {"rounding": fq.FQ_ROUND_STOCHASTIC, "seed": 5, "offset": 2}),
+    ("mx_e5m2_sr_rows", fq.FQ_MX, fq.FQ_E5M2, (1, 32), fq.FQ_ROWWISE, (33, 64),
+     {"rounding": fq.FQ_ROUND_STOCHASTIC, "seed": 5, "offset": 2}),
 ]
 
 
@@ -120,8 +136,9 @@ def run_case(case, x, g):
                 y = g.alloc(R * C * es, ydt)
                 fq.fq_dequantize(d, q, which, y)
             g.check(name + " dequantize")
-    requant = (recipe == fq.FQ_MX and fmt == fq.FQ_E4M3 and R % 32 == 0) or \
-              (recipe == fq.FQ_BLOCK_FP32 and block == (1, 128) and extra.get("scale_mode") and R % 128 == 0)
+    requant = ((recipe == fq.FQ_MX and fmt == fq.FQ_E4M3 and R % 32 == 0) or
+               (recipe == fq.FQ_BLOCK_FP32 and block == (1, 128) and extra.get("scale_mode") and R % 128 == 0)) \
+        and not extra.get("rounding")   # requantization is offered for round-to-nearest copies
     if requant:
         dc = fq.desc(recipe, d.in_dtype, fmt, R, C, block, fq.FQ_COLWISE, **extra)
         dst, _ = guarded_quantized(g, dc)
