@@ -76,7 +76,9 @@ IN_F32, IN_BF16 = 0, 1
 ROWWISE, COLWISE = 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liborc.so")
+# ORC_LIB names another build of orc.c (the pin-strength tests load copies
+# with planted mistakes this way); by default the one built here.
+_LIB_PATH = os.environ.get("ORC_LIB") or os.path.join(_HERE, "liborc.so")
 _lib = None
 
 _p = ctypes.c_void_p

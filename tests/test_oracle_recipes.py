@@ -203,6 +203,9 @@ def test_delayed_ring_matches_window_max(orc):
         m = max(amaxes[-H:])
         assert (st.alpha, st.s) == orc.tensor_scales(m, 57344.0)
         assert sorted(st.hist.tolist()) == sorted(amaxes[-H:] + [0.0] * (H - len(amaxes[-H:])))
+        # ring order (the state layout a checkpoint holds): step t's amax in slot t mod H
+        assert st.hist[t % H] == amaxes[-1]
+        assert all(st.hist[(t - k) % H] == amaxes[-1 - k] for k in range(min(H, t + 1)))
 
 
 def test_delayed_zero_window_keeps_scale(orc):
@@ -210,6 +213,15 @@ def test_delayed_zero_window_keeps_scale(orc):
     for _ in range(3):
         r = orc.quantize_delayed(np.zeros((2, 8), np.float32), E4M3, st)
         assert st.alpha == 1.0 and st.s == 1.0 and not r["q_row"].any()
+    # a window that empties after a nonzero step keeps the last scale (it is
+    # not reset to 1): H = 2, one step of amax 3, then zeros
+    st = orc.DelayedState(2)
+    orc.quantize_delayed(np.full((2, 8), 3.0, np.float32), E4M3, st)
+    kept = orc.tensor_scales(3.0, 448.0)
+    for t in range(3):
+        orc.quantize_delayed(np.zeros((2, 8), np.float32), E4M3, st)
+        assert (st.alpha, st.s) == kept, t
+    assert not st.hist.any()
 
 
 # ------------------------------------------------------------ blockwise
