@@ -5,6 +5,8 @@ which take the one-read tile kernels for bf16, and ragged multiples of each
 recipe's block), with random value scales and distributions; each case
 compared byte for byte with the oracle. The cases are drawn once from a
 fixed seed, and each case's id names everything needed to repeat it."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -46,10 +48,12 @@ KINDS = {
     "mx_e5m2_sr": (fq.FQ_MX, fq.FQ_E5M2, (1, 32), 1, 32, 32, (ROW, COL, BOTH)),
 }
 OFMT = {fq.FQ_E4M3: orc.E4M3, fq.FQ_E5M2: orc.E5M2, fq.FQ_E2M1: orc.E2M1}
-N_CASES = 600
+# FQ_SWEEP_CASES / FQ_SWEEP_SEED draw a larger or another sweep
+N_CASES = int(os.environ.get("FQ_SWEEP_CASES", "600"))
+SEED = int(os.environ.get("FQ_SWEEP_SEED", "20261203"))
 
 
-def draw_cases(n, seed=20261203):
+def draw_cases(n, seed=SEED):
     rng = np.random.default_rng(seed)
     names = sorted(KINDS)
     cases = []
