@@ -16,9 +16,10 @@ namespace {
 using namespace fq;
 
 // At most 2^36 elements (128 GiB of bf16). Kernels whose work units can be
-// small at narrow shapes (16x16 strips, 32-row slabs) stride over them with
-// a capped grid; every other tiled kernel's grid stays below 2^32
-// work-items at this size (the widest, 128x64 tiles, needs 2^31).
+// small at narrow shapes (16x16 strips, 32-row slabs, 128-row tiles or
+// regions cut by a narrow last column) stride over them with a capped grid;
+// every other tiled kernel takes whole 128x128 tiles (both sides multiples
+// of 128), at most 2^22 workgroups at this size.
 constexpr int64_t kMaxElems = int64_t(1) << 36;
 static_assert(kPendingBytes == FQ_DELAYED_PENDING_BYTES, "the pending records' size is part of the ABI");
 constexpr int32_t kMaxHistory = 1 << 24;

@@ -37,6 +37,10 @@ static_assert(128 * kOP + 128 * 4 <= 128 * 128 * 2, "the code tile must fit in t
 // 256-column region, 512 threads): rows are read as 512-byte segments and
 // the rowwise E8M0 codes of a row leave as 8 contiguous bytes
 constexpr int kMxTiles = 2;
+// the region walk's grid: one region per workgroup up to this many regions,
+// beyond it each workgroup strides over several (a tall, narrow tensor would
+// otherwise pass 2^32 work-items)
+constexpr int64_t kMaxRegionGrid = 16384;
 static_assert(kMxTiles * 128 * kOP + kMxTiles * 128 * 4 <= 128 * (128 * kMxTiles + 8) * 2,
               "the transposed code tile must fit in the input region it reuses");
 
@@ -637,7 +641,8 @@ void launch_mx_t(const void* x, int in_bf16, int64_t R, int64_t C, uint8_t* q, u
         // a resident grid striding over the regions)
         const size_t lds = qt ? 128 * (128 * kMxTiles + 8) * 2 : 0;
         const int64_t nregions = cdiv(C, 128 * kMxTiles) * cdiv(R, 128);
-        k_mx_bf16<FMT><<<(unsigned)nregions, kMxTiles * kWG, lds, stream>>>((const uint16_t*)x, R, C, q, e, qt, et);
+        const unsigned grid = (unsigned)std::min<int64_t>(nregions, kMaxRegionGrid);
+        k_mx_bf16<FMT><<<grid, kMxTiles * kWG, lds, stream>>>((const uint16_t*)x, R, C, q, e, qt, et);
     } else {
         const size_t lds = qt ? 128 * tile_pitch<float>() * 4 : 0;
         static ResidentGrid cache;
@@ -652,7 +657,8 @@ hipError_t launch_mxfp4_bf16(const uint16_t* x, int64_t R, int64_t C, uint8_t* q
     // one region per workgroup, as for MXFP8
     const size_t lds = qt ? 128 * (128 * kMxTiles + 8) * 2 : 0;
     const int64_t nregions = cdiv(C, 128 * kMxTiles) * cdiv(R, 128);
-    k_mxfp4_bf16<<<(unsigned)nregions, kMxTiles * kWG, lds, stream>>>(x, R, C, q, e, qt, et);
+    const unsigned grid = (unsigned)std::min<int64_t>(nregions, kMaxRegionGrid);
+    k_mxfp4_bf16<<<grid, kMxTiles * kWG, lds, stream>>>(x, R, C, q, e, qt, et);
     return hipGetLastError();
 }
 

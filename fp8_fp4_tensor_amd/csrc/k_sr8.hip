@@ -31,7 +31,8 @@
 //              and writes 32 consecutive bytes of row c of X^T. For
 //              per-tensor and MX calls with both planes it also writes the
 //              rowwise plane from the same tile (thread (r, h): 32 columns
-//              of row r), so the input is read once.
+//              of row r), so the input is read once. One tile per
+//              workgroup, or several in turn beyond 16384 tiles.
 #include <algorithm>
 
 #include "codec.hpp"
@@ -44,6 +45,10 @@ enum { kSrTensor = 0, kSrBlock128 = 1, kSrMx32 = 2 };
 
 constexpr int kRowMaxGrid = 16384, kRowTensorMaxGrid = 2048, kRowLoads = 2;
 constexpr int kColRows = 128, kColCols = 64;
+// k_sr8_col: one tile per workgroup up to this many tiles, beyond it each
+// workgroup strides over several (a tall, narrow tensor would otherwise pass
+// 2^32 work-items)
+constexpr int64_t kColMaxGrid = 16384;
 
 // alpha, s and the amax of a per-tensor cast from its scale source
 // (every workgroup re-reduces the amax partials). Uniform control flow.
@@ -218,10 +223,7 @@ __global__ __launch_bounds__(kWG) void k_sr8_col(const T* __restrict__ x, int64_
     constexpr int P = ROW ? kColCols + 4 : kColCols;
     __shared__ __align__(16) float tile[kColRows * P];
     __shared__ float lds[4];
-    const int64_t ntc = cdiv(C, kColCols);
-    int64_t tr, tc;
-    tile_coords(blockIdx.x, ntc, tr, tc);
-    const int64_t r0 = tr * kColRows, c0 = tc * kColCols;
+    const int64_t ntc = cdiv(C, kColCols), ntiles = ntc * cdiv(R, kColRows);
     float alpha = 1.0f;
     if constexpr (KIND == kSrTensor) {
         float s, a;
@@ -233,74 +235,80 @@ __global__ __launch_bounds__(kWG) void k_sr8_col(const T* __restrict__ x, int64_
                 *amax_out = a;
         }
     }
-    // stage the tile as fp32 (zeros outside the tensor)
-    if constexpr (VEC) {
-        constexpr int E = In<T>::kE, SEGS = kColCols / E, NL = kColRows * SEGS / kWG;
+    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        int64_t tr, tc;
+        tile_coords(t, ntc, tr, tc);
+        const int64_t r0 = tr * kColRows, c0 = tc * kColCols;
+        // stage the tile as fp32 (zeros outside the tensor)
+        if constexpr (VEC) {
+            constexpr int E = In<T>::kE, SEGS = kColCols / E, NL = kColRows * SEGS / kWG;
 #pragma unroll
-        for (int k = 0; k < NL; ++k) {
-            const int i = k * kWG + (int)threadIdx.x, row = i / SEGS, col = (i % SEGS) * E;
-            const bool in = r0 + row < R && c0 + col < C;
-            const u32x4 v = in ? ld16_stream(x + (r0 + row) * C + c0 + col) : u32x4{0u, 0u, 0u, 0u};
-            float f[E];
-            In<T>::unpack(v, f);
+            for (int k = 0; k < NL; ++k) {
+                const int i = k * kWG + (int)threadIdx.x, row = i / SEGS, col = (i % SEGS) * E;
+                const bool in = r0 + row < R && c0 + col < C;
+                const u32x4 v = in ? ld16_stream(x + (r0 + row) * C + c0 + col) : u32x4{0u, 0u, 0u, 0u};
+                float f[E];
+                In<T>::unpack(v, f);
 #pragma unroll
-            for (int j = 0; j < E; j += 4)
-                *reinterpret_cast<float4*>(tile + col_tile_off<P>(row, col + j)) = make_float4(f[j], f[j + 1], f[j + 2],
-                                                                                            f[j + 3]);
-        }
-    } else {
-        constexpr int NL = kColRows * kColCols / kWG;
+                for (int j = 0; j < E; j += 4)
+                    *reinterpret_cast<float4*>(tile + col_tile_off<P>(row, col + j)) =
+                        make_float4(f[j], f[j + 1], f[j + 2], f[j + 3]);
+            }
+        } else {
+            constexpr int NL = kColRows * kColCols / kWG;
 #pragma unroll 8
-        for (int k = 0; k < NL; ++k) {
-            const int i = k * kWG + (int)threadIdx.x, row = i / kColCols, col = i % kColCols;
-            const bool in = r0 + row < R && c0 + col < C;
-            tile[col_tile_off<P>(row, col)] = in ? In<T>::load1(x, (r0 + row) * C + c0 + col) : 0.0f;
-        }
-    }
-    __syncthreads();
-    const int c = (int)threadIdx.x >> 2, qr = (int)threadIdx.x & 3;
-    float y[32];
-#pragma unroll
-    for (int k = 0; k < 32; ++k)
-        y[k] = tile[col_tile_off<P>(32 * qr + k, c)];
-    float mult = alpha;
-    const bool col_in = c0 + c < C;
-    if constexpr (KIND == kSrBlock128) {
-        float s;
-        block_scale<POW2>(max_lanes4(absmax<32>(y)), mult, s);
-        if (col_in && qr == 0)
-            reinterpret_cast<float*>(sct)[(c0 + c) * (R / 128) + r0 / 128] = s;
-    } else if constexpr (KIND == kSrMx32) {
-        const uint32_t code = mx_code<FMT>(absmax<32>(y));
-        mult = mx_multiplier(code);
-        if (col_in && r0 + 32 * qr < R)
-            reinterpret_cast<uint8_t*>(sct)[(c0 + c) * (R / 32) + r0 / 32 + qr] = (uint8_t)code;
-    }
-    if (col_in)
-        sr_run32<FMT>(y, mult, qt + (c0 + c) * R + r0 + 32 * qr, (c0 + c) * R + r0 + 32 * qr,
-                      min((int64_t)32, R - r0 - 32 * qr), (R & 15) == 0, stream_s, seed);
-    if constexpr (ROW) {
-        const int row = (int)threadIdx.x >> 1, h = (int)threadIdx.x & 1;
-        const int64_t gr = r0 + row, gc = c0 + 32 * h;
-        if (gr < R && gc < C) {
-            float z[32];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const float4 v = *reinterpret_cast<const float4*>(tile + col_tile_off<P>(row, 32 * h + 4 * k));
-                z[4 * k] = v.x;
-                z[4 * k + 1] = v.y;
-                z[4 * k + 2] = v.z;
-                z[4 * k + 3] = v.w;
+            for (int k = 0; k < NL; ++k) {
+                const int i = k * kWG + (int)threadIdx.x, row = i / kColCols, col = i % kColCols;
+                const bool in = r0 + row < R && c0 + col < C;
+                tile[col_tile_off<P>(row, col)] = in ? In<T>::load1(x, (r0 + row) * C + c0 + col) : 0.0f;
             }
-            float rmult = alpha;
-            if constexpr (KIND == kSrMx32) {
-                const uint32_t code = mx_code<FMT>(absmax<32>(z));
-                rmult = mx_multiplier(code);
-                reinterpret_cast<uint8_t*>(sq)[gr * (C / 32) + gc / 32] = (uint8_t)code;
-            }
-            sr_run32<FMT>(z, rmult, q + gr * C + gc, gr * C + gc, min((int64_t)32, C - gc), (C & 15) == 0,
-                          stream_row, seed);
         }
+        __syncthreads();
+        const int c = (int)threadIdx.x >> 2, qr = (int)threadIdx.x & 3;
+        float y[32];
+#pragma unroll
+        for (int k = 0; k < 32; ++k)
+            y[k] = tile[col_tile_off<P>(32 * qr + k, c)];
+        float mult = alpha;
+        const bool col_in = c0 + c < C;
+        if constexpr (KIND == kSrBlock128) {
+            float s;
+            block_scale<POW2>(max_lanes4(absmax<32>(y)), mult, s);
+            if (col_in && qr == 0)
+                reinterpret_cast<float*>(sct)[(c0 + c) * (R / 128) + r0 / 128] = s;
+        } else if constexpr (KIND == kSrMx32) {
+            const uint32_t code = mx_code<FMT>(absmax<32>(y));
+            mult = mx_multiplier(code);
+            if (col_in && r0 + 32 * qr < R)
+                reinterpret_cast<uint8_t*>(sct)[(c0 + c) * (R / 32) + r0 / 32 + qr] = (uint8_t)code;
+        }
+        if (col_in)
+            sr_run32<FMT>(y, mult, qt + (c0 + c) * R + r0 + 32 * qr, (c0 + c) * R + r0 + 32 * qr,
+                          min((int64_t)32, R - r0 - 32 * qr), (R & 15) == 0, stream_s, seed);
+        if constexpr (ROW) {
+            const int row = (int)threadIdx.x >> 1, h = (int)threadIdx.x & 1;
+            const int64_t gr = r0 + row, gc = c0 + 32 * h;
+            if (gr < R && gc < C) {
+                float z[32];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const float4 v = *reinterpret_cast<const float4*>(tile + col_tile_off<P>(row, 32 * h + 4 * k));
+                    z[4 * k] = v.x;
+                    z[4 * k + 1] = v.y;
+                    z[4 * k + 2] = v.z;
+                    z[4 * k + 3] = v.w;
+                }
+                float rmult = alpha;
+                if constexpr (KIND == kSrMx32) {
+                    const uint32_t code = mx_code<FMT>(absmax<32>(z));
+                    rmult = mx_multiplier(code);
+                    reinterpret_cast<uint8_t*>(sq)[gr * (C / 32) + gc / 32] = (uint8_t)code;
+                }
+                sr_run32<FMT>(z, rmult, q + gr * C + gc, gr * C + gc, min((int64_t)32, C - gc), (C & 15) == 0,
+                              stream_row, seed);
+            }
+        }
+        __syncthreads();  // the tile's LDS reads are done before the next tile is staged
     }
 }
 
@@ -308,7 +316,7 @@ template <typename T, int FMT, int KIND, bool POW2, bool ROW>
 void launch_col(const T* x, int64_t R, int64_t C, ScaleSrc src, SrArgs sr, uint8_t* qt, void* sqt, float* s_out,
                 float* amax_out, uint8_t* q, void* sq, hipStream_t stream)
 {
-    const unsigned grid = (unsigned)(cdiv(R, kColRows) * cdiv(C, kColCols));
+    const unsigned grid = (unsigned)std::min<int64_t>(cdiv(R, kColRows) * cdiv(C, kColCols), kColMaxGrid);
     if (C % In<T>::kE == 0)
         k_sr8_col<T, FMT, KIND, POW2, true, ROW><<<grid, kWG, 0, stream>>>(
             x, R, C, src, sr.seed, 2 * sr.offset + 1, qt, sqt, s_out, amax_out, 2 * sr.offset, q, sq);
