@@ -31,8 +31,11 @@
 //              and writes 32 consecutive bytes of row c of X^T. For
 //              per-tensor and MX calls with both planes it also writes the
 //              rowwise plane from the same tile (thread (r, h): 32 columns
-//              of row r), so the input is read once. One tile per
-//              workgroup, or several in turn beyond 16384 tiles.
+//              of row r), so the input is read once. With 16-byte rows a
+//              resident grid takes the tiles in turn, each workgroup
+//              issuing the next tile's loads once the current one is in
+//              LDS (the rounding is long enough to hide them); otherwise
+//              one tile per workgroup, or several beyond 16384 tiles.
 #include <algorithm>
 
 #include "codec.hpp"
@@ -213,8 +216,9 @@ __device__ __forceinline__ int col_tile_off(int r, int c) { return r * P + (c ^ 
 // and MX): the rowwise plane too, from the same staged tile: thread (r, h)
 // rounds columns 32h .. 32h+31 of tile row r (one MX block) with the rowwise
 // random bits (stream_row).
+// At most 128 registers, so that four workgroups fit on a CU as the LDS tile allows.
 template <typename T, int FMT, int KIND, bool POW2, bool VEC, bool ROW>
-__global__ __launch_bounds__(kWG) void k_sr8_col(const T* __restrict__ x, int64_t R, int64_t C, ScaleSrc src,
+__global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(4))) void k_sr8_col(const T* __restrict__ x, int64_t R, int64_t C, ScaleSrc src,
                                                  uint64_t seed, uint64_t stream_s, uint8_t* __restrict__ qt,
                                                  void* __restrict__ sct, float* s_out, float* amax_out,
                                                  uint64_t stream_row, uint8_t* __restrict__ q, void* __restrict__ sq)
@@ -235,20 +239,37 @@ __global__ __launch_bounds__(kWG) void k_sr8_col(const T* __restrict__ x, int64_
                 *amax_out = a;
         }
     }
-    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    // VEC: 16-byte loads, the next tile's issued into registers once this
+    // one is in LDS, so they are in flight while this tile is rounded
+    constexpr int E = In<T>::kE, SEGS = kColCols / E, NLV = kColRows * SEGS / kWG;
+    u32x4 v[NLV];
+    auto load_vec = [&](int64_t t) {
+        int64_t tr, tc;
+        tile_coords(t, ntc, tr, tc);
+        const int64_t r0 = tr * kColRows, c0 = tc * kColCols;
+#pragma unroll
+        for (int k = 0; k < NLV; ++k) {
+            const int i = k * kWG + (int)threadIdx.x, row = i / SEGS, col = (i % SEGS) * E;
+            const bool in = r0 + row < R && c0 + col < C;
+            v[k] = in ? ld16_stream(x + (r0 + row) * C + c0 + col) : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    int64_t t = blockIdx.x;
+    if constexpr (VEC) {
+        if (t < ntiles)
+            load_vec(t);
+    }
+    for (; t < ntiles; t += gridDim.x) {
         int64_t tr, tc;
         tile_coords(t, ntc, tr, tc);
         const int64_t r0 = tr * kColRows, c0 = tc * kColCols;
         // stage the tile as fp32 (zeros outside the tensor)
         if constexpr (VEC) {
-            constexpr int E = In<T>::kE, SEGS = kColCols / E, NL = kColRows * SEGS / kWG;
 #pragma unroll
-            for (int k = 0; k < NL; ++k) {
+            for (int k = 0; k < NLV; ++k) {
                 const int i = k * kWG + (int)threadIdx.x, row = i / SEGS, col = (i % SEGS) * E;
-                const bool in = r0 + row < R && c0 + col < C;
-                const u32x4 v = in ? ld16_stream(x + (r0 + row) * C + c0 + col) : u32x4{0u, 0u, 0u, 0u};
                 float f[E];
-                In<T>::unpack(v, f);
+                In<T>::unpack(v[k], f);
 #pragma unroll
                 for (int j = 0; j < E; j += 4)
                     *reinterpret_cast<float4*>(tile + col_tile_off<P>(row, col + j)) =
@@ -263,7 +284,11 @@ __global__ __launch_bounds__(kWG) void k_sr8_col(const T* __restrict__ x, int64_
                 tile[col_tile_off<P>(row, col)] = in ? In<T>::load1(x, (r0 + row) * C + c0 + col) : 0.0f;
             }
         }
-        __syncthreads();
+        lds_barrier();  // LDS only: the previous tile's stores and the loads below stay in flight
+        if constexpr (VEC) {
+            if (t + gridDim.x < ntiles)
+                load_vec(t + gridDim.x);
+        }
         const int c = (int)threadIdx.x >> 2, qr = (int)threadIdx.x & 3;
         float y[32];
 #pragma unroll
@@ -308,7 +333,7 @@ __global__ __launch_bounds__(kWG) void k_sr8_col(const T* __restrict__ x, int64_
                               stream_row, seed);
             }
         }
-        __syncthreads();  // the tile's LDS reads are done before the next tile is staged
+        lds_barrier();  // the tile's LDS reads are done before the next tile is staged
     }
 }
 
@@ -316,13 +341,19 @@ template <typename T, int FMT, int KIND, bool POW2, bool ROW>
 void launch_col(const T* x, int64_t R, int64_t C, ScaleSrc src, SrArgs sr, uint8_t* qt, void* sqt, float* s_out,
                 float* amax_out, uint8_t* q, void* sq, hipStream_t stream)
 {
-    const unsigned grid = (unsigned)std::min<int64_t>(cdiv(R, kColRows) * cdiv(C, kColCols), kColMaxGrid);
-    if (C % In<T>::kE == 0)
+    const int64_t ntiles = cdiv(R, kColRows) * cdiv(C, kColCols);
+    if (C % In<T>::kE == 0) {
+        // a resident grid: each workgroup rounds several tiles, loading the next during each
+        static ResidentGrid cache;
+        const unsigned grid = (unsigned)std::min<int64_t>(
+            ntiles, std::min<int64_t>(kColMaxGrid, cache.get(k_sr8_col<T, FMT, KIND, POW2, true, ROW>, kWG, 0)));
         k_sr8_col<T, FMT, KIND, POW2, true, ROW><<<grid, kWG, 0, stream>>>(
             x, R, C, src, sr.seed, 2 * sr.offset + 1, qt, sqt, s_out, amax_out, 2 * sr.offset, q, sq);
-    else
+    } else {
+        const unsigned grid = (unsigned)std::min<int64_t>(ntiles, kColMaxGrid);
         k_sr8_col<T, FMT, KIND, POW2, false, ROW><<<grid, kWG, 0, stream>>>(
             x, R, C, src, sr.seed, 2 * sr.offset + 1, qt, sqt, s_out, amax_out, 2 * sr.offset, q, sq);
+    }
 }
 
 template <typename T, int FMT, int KIND, bool POW2>
