@@ -199,7 +199,8 @@ __global__ __launch_bounds__(kWG) void k_cast_tensor(const T* __restrict__ x, in
 // One delayed-scaling step over a flat tensor: finish step t-1 (prologue),
 // q = Q(fp32(alpha * x)) and the amax in the same read, this step's record
 // (epilogue). The first loads go out before the prologue's loads, so its
-// round trip overlaps them.
+// round trip overlaps them, and each step's loads go out before the step
+// before it is converted.
 template <typename T, int FMT, int L>
 __global__ __launch_bounds__(kWG) void k_cast_delayed(const T* __restrict__ x, int64_t n, DelayedArgs dl,
                                                       uint8_t* __restrict__ q)
@@ -219,10 +220,12 @@ __global__ __launch_bounds__(kWG) void k_cast_delayed(const T* __restrict__ x, i
     delayed_prologue(dl, lds, alpha, s);
     float m = 0.0f;
     for (; u0 < nunits; u0 += nwaves * L) {
-        if (u0 != wave * L) {
+        const int64_t un = u0 + nwaves * L;
+        u32x4 nx[L];
+        if (un < nunits) {
 #pragma unroll
             for (int j = 0; j < L; ++j)
-                v[j] = (u0 + j < nunits) ? ld16_stream(x + (u0 + j) * U + lane * E) : u32x4{0u, 0u, 0u, 0u};
+                nx[j] = (un + j < nunits) ? ld16_stream(x + (un + j) * U + lane * E) : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int j = 0; j < L; ++j) {
@@ -232,6 +235,11 @@ __global__ __launch_bounds__(kWG) void k_cast_delayed(const T* __restrict__ x, i
                 m = fmaxf(m, absmax<E>(f));
                 Enc8<FMT, E>::store(q + (u0 + j) * U + lane * E, f, alpha);
             }
+        }
+        if (un < nunits) {
+#pragma unroll
+            for (int j = 0; j < L; ++j)
+                v[j] = nx[j];
         }
     }
     for (int64_t i = nunits * U + (int64_t)blockIdx.x * kWG + threadIdx.x; i < n; i += (int64_t)gridDim.x * kWG) {
