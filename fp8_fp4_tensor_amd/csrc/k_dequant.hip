@@ -127,13 +127,15 @@ __device__ __forceinline__ void store1(void* y, int64_t i, float v)
         reinterpret_cast<float*>(y)[i] = v;
 }
 
-// Per-tensor: flat codes, one scale; kChunks chunks per lane per round, the
-// round's loads issued before any decode.
+// Per-tensor: flat codes, one scale; kTensorChunks chunks per lane per
+// round, the round's loads issued before any decode.
+constexpr int kTensorChunks = 8;
+
 template <int CODE, bool BF16>
 __global__ __launch_bounds__(kWG) void k_dq_tensor(const uint8_t* __restrict__ q, int64_t n, const float* s,
                                                    void* __restrict__ y)
 {
-    constexpr int G = chunk_elems<BF16>();
+    constexpr int G = chunk_elems<BF16>(), kChunks = kTensorChunks;
     const float sc = *s;
     const int64_t nch = n / G, nthreads = (int64_t)gridDim.x * kWG;
     const int64_t t = (int64_t)blockIdx.x * kWG + threadIdx.x;
@@ -223,7 +225,10 @@ void rows_t(const uint8_t* q, const void* s, const float* S, int64_t R, int64_t 
 hipError_t launch_dequant_tensor(const uint8_t* q, int fmt, int64_t n, const float* s, void* y, int bf,
                                  hipStream_t stream)
 {
-    const int grid = grid_for(cdiv(n / 4, kChunks) + 1);
+    // a grid that gives every lane kTensorChunks chunks of G elements (8192 x
+    // 4096 to bf16: 23.1 -> 22.2 us per cold call against 4 chunks of half
+    // the intended count)
+    const int grid = grid_for(cdiv(n / (bf ? chunk_elems<true>() : chunk_elems<false>()), kTensorChunks) + 1);
     if (fmt == kE4M3) {
         if (bf)
             k_dq_tensor<kDqE4M3, true><<<grid, kWG, 0, stream>>>(q, n, s, y);
