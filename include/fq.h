@@ -257,7 +257,14 @@ typedef struct {
  *   pending       FQ_DELAYED_PENDING_BYTES, 16-byte aligned, zero-filled
  *                 before step 0: carries a step's amax (as per-workgroup
  *                 partial maxima, tagged with the step) to the next call,
- *                 which records it in the window.
+ *                 which records it in the window. A tensor split by rows
+ *                 across ranks ([CS] "成本与多 GPU 使用": local amaxes
+ *                 reduced with max; history_len <= 1024): after each call,
+ *                 an all-reduce with max over `pending` viewed as
+ *                 FQ_DELAYED_PENDING_BYTES / 4 32-bit integers (each word
+ *                 is a non-negative float or the same on every rank at one
+ *                 step) gives every rank the whole tensor's record, so the
+ *                 next call's window update and scale are the global ones.
  *   step          host counter t; the caller advances it after each call.
  * See fq_quantize_delayed for when the window and scales are up to date, and
  * fq_delayed_flush for checkpointing.

@@ -121,3 +121,41 @@ def test_sharded_block_local(name, recipe, fmt, block, outputs, sizes):
     # colwise scale planes: [C/128, R/128] for 128x128 tiles, [C, R/32] for MX
     check_planes(ranges, outs, ref, name, rows_per_scale_row=block[0],
                  col_scale_rows=128 if block == (128, 128) else 1)
+
+
+@pytest.mark.parametrize("sizes", [[1024] * 8, [1000, 1048, 2000, 96, 1, 4047]], ids=["even", "ragged"])
+def test_sharded_delayed(sizes):
+    """Delayed scaling across shards: after each step, an all-reduce with max
+    over the shards' pending records (viewed as 32-bit integers: every word
+    is a non-negative float or the same on every shard) gives every shard the
+    whole tensor's record, so its next step scales with the global window."""
+    w = W.BY_NAME["delayed_e4m3_act_8192x4096"]
+    R, C = w.shape
+    H = w.extra["history_len"]
+    # steps of different magnitude (power-of-two factors keep bf16 exact)
+    xs = [dev(w.make(w.seed + t)) * f for t, f in enumerate([1.0, 4.0, 0.25, 2.0, 0.5])]
+    d = fq.desc(fq.FQ_PER_TENSOR_DELAYED, fq.FQ_IN_BF16, fq.FQ_E4M3, R, C)
+    st, out = fq.DelayedState(H), fq.alloc_quantized(d)
+    ranges = split_rows(R, sizes)
+    ds = [fq.desc(fq.FQ_PER_TENSOR_DELAYED, fq.FQ_IN_BF16, fq.FQ_E4M3, b - a, C) for a, b in ranges]
+    sts = [fq.DelayedState(H) for _ in ranges]
+    outs = [fq.alloc_quantized(dd) for dd in ds]
+    for t, x in enumerate(xs):
+        fq.fq_quantize_delayed(d, x, st, out)
+        for (a, b), dd, s, o in zip(ranges, ds, sts, outs):
+            fq.fq_quantize_delayed(dd, x[a:b], s, o)
+        red = torch.stack([s.pending for s in sts]).view(torch.int32).amax(0).view(torch.float32)
+        for s in sts:
+            s.pending.copy_(red)
+        torch.cuda.synchronize()
+        same_bytes(np.concatenate([host(o.row_data) for o in outs]), host(out.row_data), f"step {t} codes")
+        for o in outs:
+            same_bytes(host(o.tensor_scale), host(out.tensor_scale), f"step {t} s used")
+    fq.fq_delayed_flush(d, st)
+    for dd, s in zip(ds, sts):
+        fq.fq_delayed_flush(dd, s)
+    torch.cuda.synchronize()
+    for s in sts:
+        same_bytes(host(s.amax_history), host(st.amax_history), "window")
+        same_bytes(host(s.scale), host(st.scale), "scale")
+        same_bytes(host(s.scale_inv), host(st.scale_inv), "scale_inv")
